@@ -1,0 +1,231 @@
+"""CPU reference for one DSA layer step: TEST INFRASTRUCTURE, not the product.
+
+Only the test-suite, the smoke check and the benchmark's CPU-baseline leg import
+this package.  It wraps ``liboracle.so`` (built from ``dsa_oracle.c`` by
+:func:`build`) with ctypes and numpy; every number it returns comes from that plain
+C code, written from the pages' definitions (see the header comment of
+``dsa_oracle.c`` for the citations).  It shares nothing with the HIP library.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "dsa_oracle.c")
+_LIB_PATH = os.path.join(_HERE, "liboracle.so")
+
+F32, BF16, F64 = 0, 1, 2
+_OK, _ERR_SHAPE, _ERR_INDEX = 0, 1, 2
+
+
+class OracleError(RuntimeError):
+    pass
+
+
+def build(force: bool = True) -> str:
+    """Compile liboracle.so with gcc (OpenMP over independent query rows)."""
+    if force or not os.path.exists(_LIB_PATH):
+        tmp = _LIB_PATH + ".tmp"
+        cmd = ["gcc", "-O2", "-std=c11", "-fopenmp", "-fPIC", "-shared", "-Wall", "-Wextra",
+               "-o", tmp, _SRC, "-lm"]
+        subprocess.run(cmd, check=True, cwd=_HERE)
+        os.replace(tmp, _LIB_PATH)
+    return _LIB_PATH
+
+
+_lib = None
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB_PATH):
+            build()
+        lib = ctypes.CDLL(_LIB_PATH)
+        P = ctypes.c_void_p
+        I = ctypes.c_int
+        D = ctypes.c_double
+        lib.orc_e4m3fn_value.argtypes = [ctypes.c_uint8]
+        lib.orc_e4m3fn_value.restype = D
+        lib.orc_bf16_value.argtypes = [ctypes.c_uint16]
+        lib.orc_bf16_value.restype = D
+        lib.orc_index_scores.argtypes = [P, P, P, P, P, P, I, I, I, I, I, D, P]
+        lib.orc_topk.argtypes = [P, P, I, I, I, I, P]
+        lib.orc_sparse_mla_decode.argtypes = [P, P, P, P, I, I, I, I, I, I, I, I, D, P, P]
+        lib.orc_sparse_mha_prefill.argtypes = [P, P, P, P, I, I, I, I, I, I, I, D, P, P]
+        lib.orc_sparse_mha_prefill_dense.argtypes = [P, P, P, P, I, I, I, I, I, I, I, D, P, P]
+        lib.orc_layer_step_latent.argtypes = [P, P, P, P, P, P, I, I, I, I, I, D, I,
+                                              P, P, I, I, I, I, D, P, P, P, P]
+        lib.orc_layer_step_mha.argtypes = [P, P, P, P, P, I, I, I, I, D, I,
+                                           P, P, P, I, I, I, I, D, P, P, P, P]
+        lib.orc_max_threads.argtypes = []
+        for fn in (lib.orc_index_scores, lib.orc_topk, lib.orc_sparse_mla_decode,
+                   lib.orc_sparse_mha_prefill, lib.orc_sparse_mha_prefill_dense,
+                   lib.orc_layer_step_latent, lib.orc_layer_step_mha, lib.orc_max_threads):
+            fn.restype = I
+        _lib = lib
+    return _lib
+
+
+def _c(a, dtype):
+    a = np.ascontiguousarray(a, dtype=dtype)
+    return a, a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _attn_array(x):
+    """Return (contiguous array, dtype code).  bf16 travels as raw uint16 words."""
+    if x.dtype == np.float32:
+        return np.ascontiguousarray(x), F32
+    if x.dtype == np.uint16:
+        return np.ascontiguousarray(x), BF16
+    if x.dtype == np.float64:
+        return np.ascontiguousarray(x), F64
+    raise TypeError(f"attention inputs must be float32, float64 or bf16 bits (uint16), got {x.dtype}")
+
+
+def _check(rc, what):
+    if rc != _OK:
+        raise OracleError(f"{what}: oracle returned {rc}")
+
+
+def max_threads() -> int:
+    return _load().orc_max_threads()
+
+
+def e4m3fn_value(code: int) -> float:
+    return _load().orc_e4m3fn_value(code)
+
+
+def bf16_value(bits: int) -> float:
+    return _load().orc_bf16_value(bits)
+
+
+def index_scores(q_fp8, q_scale, w, k_fp8, k_scale, lens, sm_scale_i):
+    """scores[B,T,Lmax] f32 = sum_h w*q_scale*sm_scale_i * ReLU(q.k) * k_scale, -inf if invisible."""
+    B, T, H, D = q_fp8.shape
+    Lmax = k_fp8.shape[1]
+    lib = _load()
+    q_fp8, pq = _c(q_fp8, np.uint8)
+    q_scale, pqs = _c(q_scale, np.float32)
+    w, pw = _c(w, np.float32)
+    k_fp8, pk = _c(k_fp8, np.uint8)
+    k_scale, pks = _c(k_scale, np.float32)
+    lens, pl = _c(lens, np.int32)
+    out = np.empty((B, T, Lmax), np.float32)
+    _check(lib.orc_index_scores(pq, pqs, pw, pk, pks, pl, B, T, H, D, Lmax, float(sm_scale_i),
+                                out.ctypes.data_as(ctypes.c_void_p)), "index_scores")
+    return out
+
+
+def topk(scores, lens, k):
+    """idx[B,T,k] i32: the min(k, pos+1) best visible positions ascending, then -1."""
+    B, T, Lmax = scores.shape
+    lib = _load()
+    scores, ps = _c(scores, np.float32)
+    lens, pl = _c(lens, np.int32)
+    out = np.empty((B, T, k), np.int32)
+    _check(lib.orc_topk(ps, pl, B, T, Lmax, k, out.ctypes.data_as(ctypes.c_void_p)), "topk")
+    return out
+
+
+def sparse_mla_decode(q, latent, idx, lens, Dv, sm_scale):
+    """Absorbed-form sparse attention.  Returns (out[B,T,H,Dv] f64, lse[B,T,H] f64)."""
+    B, T, H, Dq = q.shape
+    Lmax = latent.shape[1]
+    k = idx.shape[-1]
+    lib = _load()
+    q, dt = _attn_array(q)
+    latent, dt2 = _attn_array(latent)
+    assert dt == dt2 and latent.shape[-1] == Dq
+    idx, pi = _c(idx, np.int32)
+    lens, pl = _c(lens, np.int32)
+    out = np.empty((B, T, H, Dv), np.float64)
+    lse = np.empty((B, T, H), np.float64)
+    _check(lib.orc_sparse_mla_decode(q.ctypes.data_as(ctypes.c_void_p),
+                                     latent.ctypes.data_as(ctypes.c_void_p), pi, pl, dt,
+                                     B, T, H, Dv, Dq - Dv, Lmax, k, float(sm_scale),
+                                     out.ctypes.data_as(ctypes.c_void_p),
+                                     lse.ctypes.data_as(ctypes.c_void_p)), "sparse_mla_decode")
+    return out, lse
+
+
+def _mha(fn, q, k_, v, idx, sm_scale):
+    B, T, H, Dqk = q.shape
+    Dv = v.shape[-1]
+    topk_ = idx.shape[-1]
+    q, dt = _attn_array(q)
+    k_, dt2 = _attn_array(k_)
+    v, dt3 = _attn_array(v)
+    assert dt == dt2 == dt3
+    idx, pi = _c(idx, np.int32)
+    out = np.empty((B, T, H, Dv), np.float64)
+    lse = np.empty((B, T, H), np.float64)
+    _check(fn(q.ctypes.data_as(ctypes.c_void_p), k_.ctypes.data_as(ctypes.c_void_p),
+              v.ctypes.data_as(ctypes.c_void_p), pi, dt, B, T, H, Dqk, Dv, topk_,
+              float(sm_scale), out.ctypes.data_as(ctypes.c_void_p),
+              lse.ctypes.data_as(ctypes.c_void_p)), "sparse_mha_prefill")
+    return out, lse
+
+
+def sparse_mha_prefill(q, k_, v, idx, sm_scale):
+    """Gather-form sparse MHA over selected and causally visible keys."""
+    return _mha(_load().orc_sparse_mha_prefill, q, k_, v, idx, sm_scale)
+
+
+def sparse_mha_prefill_dense(q, k_, v, idx, sm_scale):
+    """The same result computed as dense scores + index mask + causal mask."""
+    return _mha(_load().orc_sparse_mha_prefill_dense, q, k_, v, idx, sm_scale)
+
+
+def layer_step_latent(q_fp8, q_scale, w, k_fp8, k_scale, lens, sm_scale_i, k, q, latent, Dv,
+                      sm_scale, want_scores=False):
+    """Index scores -> top-k -> sparse latent attention.  Returns (out, lse, idx[, scores])."""
+    B, T, H_I, D_I = q_fp8.shape
+    Lmax = k_fp8.shape[1]
+    H, Dq = q.shape[2], q.shape[3]
+    lib = _load()
+    arrs = [_c(q_fp8, np.uint8), _c(q_scale, np.float32), _c(w, np.float32),
+            _c(k_fp8, np.uint8), _c(k_scale, np.float32), _c(lens, np.int32)]
+    qa, dt = _attn_array(q)
+    la, dt2 = _attn_array(latent)
+    assert dt == dt2
+    out = np.empty((B, T, H, Dv), np.float64)
+    lse = np.empty((B, T, H), np.float64)
+    idx = np.empty((B, T, k), np.int32)
+    scores = np.empty((B, T, Lmax), np.float32) if want_scores else None
+    _check(lib.orc_layer_step_latent(*[p for _, p in arrs], B, T, H_I, D_I, Lmax,
+                                     float(sm_scale_i), k, qa.ctypes.data_as(ctypes.c_void_p),
+                                     la.ctypes.data_as(ctypes.c_void_p), dt, H, Dv, Dq - Dv,
+                                     float(sm_scale), out.ctypes.data_as(ctypes.c_void_p),
+                                     lse.ctypes.data_as(ctypes.c_void_p),
+                                     scores.ctypes.data_as(ctypes.c_void_p) if want_scores else None,
+                                     idx.ctypes.data_as(ctypes.c_void_p)), "layer_step_latent")
+    return (out, lse, idx, scores) if want_scores else (out, lse, idx)
+
+
+def layer_step_mha(q_fp8, q_scale, w, k_fp8, k_scale, sm_scale_i, k, q, k_, v, sm_scale):
+    """Index scores -> top-k -> sparse MHA prefill (chunk from position 0)."""
+    B, T, H_I, D_I = q_fp8.shape
+    H, Dqk = q.shape[2], q.shape[3]
+    Dv = v.shape[-1]
+    lib = _load()
+    arrs = [_c(q_fp8, np.uint8), _c(q_scale, np.float32), _c(w, np.float32),
+            _c(k_fp8, np.uint8), _c(k_scale, np.float32)]
+    qa, dt = _attn_array(q)
+    ka, _ = _attn_array(k_)
+    va, _ = _attn_array(v)
+    out = np.empty((B, T, H, Dv), np.float64)
+    lse = np.empty((B, T, H), np.float64)
+    idx = np.empty((B, T, k), np.int32)
+    _check(lib.orc_layer_step_mha(*[p for _, p in arrs], B, T, H_I, D_I, float(sm_scale_i), k,
+                                  qa.ctypes.data_as(ctypes.c_void_p),
+                                  ka.ctypes.data_as(ctypes.c_void_p),
+                                  va.ctypes.data_as(ctypes.c_void_p), dt, H, Dqk, Dv,
+                                  float(sm_scale), out.ctypes.data_as(ctypes.c_void_p),
+                                  lse.ctypes.data_as(ctypes.c_void_p), None,
+                                  idx.ctypes.data_as(ctypes.c_void_p)), "layer_step_mha")
+    return out, lse, idx

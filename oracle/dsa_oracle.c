@@ -1,0 +1,394 @@
+/*
+ * dsa_oracle.c -- plain, slow CPU reference for one DeepSeek Sparse Attention (DSA)
+ * layer step.  TEST INFRASTRUCTURE ONLY: it is loaded by the test-suite, by the
+ * smoke check and by the benchmark's CPU-baseline leg, never by the GPU product
+ * path.  It shares no code, header, table or constant with the HIP library.
+ *
+ * Everything is computed in double precision straight from the definitions on the
+ * pages; the only stored-precision step is the fp32 index score, which is what the
+ * method itself ranks (the score tensor is fp32 on the pages).
+ *
+ * Sources (web pages, cited by title and section):
+ *   [IDX]  "DeepSeek-V3.2-Exp - Split indexer heads", Indexer.forward excerpt:
+ *          FP8 q/k with per-block scales, the weight fold (weights_proj * n_heads^-0.5,
+ *          then * q_scale * softmax_scale), fp8_index, "+= mask", topk(min(k, end_pos)).
+ *   [DIAG] "dsa-indexer.excalidraw" (one DSA decode step in one layer, V3.2 sizes):
+ *          score formula I(t,s) = sum_j w_j ReLU(q_j . k_s); top-k selector k = 2048;
+ *          gather of the selected latents; MQA core attention in which each latent row
+ *          is both key and value; cost-per-token box.
+ *   [MASK] "DeepSeek-V3.2-Exp - Causal mask", Transformer.forward excerpt: additive
+ *          mask full(-inf).triu_(1) for seqlen > 1, none for decode.
+ *   [MLA]  same page, MLA init / prefill excerpts: softmax_scale = qk_head_dim^-0.5,
+ *          the MHA prefill form (scores = einsum * scale, index_mask scatter of the
+ *          top-k, + causal mask, softmax, einsum with v).
+ *   [V4]   "visualize_attention_masks.py" (DeepSeek-V4 mask visualiser): the -1
+ *          warm-up sentinel for unused top-k slots.
+ *
+ * Conventions (the readings where the pages are silent are listed in the design
+ * notes of the repository):
+ *   len[b]        valid keys of sequence b;  T query rows are the LAST T positions,
+ *                 pos(b,t) = len[b] - T + t  (end_pos = start_pos + seqlen in [IDX]);
+ *   key s is visible to row (b,t) iff 0 <= s <= pos(b,t)   ([MASK] triu_(1)).
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#include "dsa_oracle.h"
+
+/* ------------------------------------------------------------------ element codecs */
+
+/* OCP FP8 E4M3 ("e4m3fn"): 1 sign bit, 4 exponent bits (bias 7), 3 mantissa bits.
+ * exponent field 0 is subnormal (m/8 * 2^-6); exponent 15 with mantissa 7 is NaN;
+ * there is no infinity, so the largest finite magnitude is 1.75 * 2^8 = 448. */
+double orc_e4m3fn_value(uint8_t code)
+{
+    int sign = code >> 7;
+    int e = (code >> 3) & 15;
+    int m = code & 7;
+    double mag;
+    if (e == 15 && m == 7) return NAN;
+    if (e == 0)
+        mag = ldexp((double)m / 8.0, 1 - 7);
+    else
+        mag = ldexp(1.0 + (double)m / 8.0, e - 7);
+    return sign ? -mag : mag;
+}
+
+/* bfloat16 is the upper half of an IEEE binary32 word. */
+double orc_bf16_value(uint16_t bits)
+{
+    uint32_t u = (uint32_t)bits << 16;
+    float f;
+    memcpy(&f, &u, sizeof f);
+    return (double)f;
+}
+
+static double load_elem(const void* p, int dtype, size_t i)
+{
+    switch (dtype) {
+    case ORC_F32: return (double)((const float*)p)[i];
+    case ORC_BF16: return orc_bf16_value(((const uint16_t*)p)[i]);
+    default: return ((const double*)p)[i];
+    }
+}
+
+/* ------------------------------------------------------------------ O2: index scores */
+
+/* For every row (b,t) and cache position s:
+ *   w'_h   = w[b,t,h] * q_scale[b,t,h] * sm_scale            (weight fold, [IDX])
+ *   D_h    = sum_d deq(q[b,t,h,d]) * deq(k[b,s,d])            (FP8 query-key product)
+ *   I      = k_scale[b,s] * sum_h w'_h * max(D_h, 0)          ([DIAG] score with ReLU)
+ * and -inf where s is not visible ([MASK], "+= mask" in [IDX]).
+ * The e4m3 products are exact in double and their 128-term sums stay far below 2^53
+ * units of 2^-18, so D_h is exact; the head sum is one double rounding per term. */
+int orc_index_scores(const uint8_t* q, const float* q_scale, const float* w,
+                     const uint8_t* k, const float* k_scale, const int32_t* len,
+                     int B, int T, int H, int D, int Lmax, double sm_scale, float* scores)
+{
+    double table[256];
+    int b;
+    for (int c = 0; c < 256; ++c) table[c] = orc_e4m3fn_value((uint8_t)c);
+    for (b = 0; b < B; ++b)
+        if (len[b] < T || len[b] > Lmax) return ORC_ERR_SHAPE;
+
+#pragma omp parallel for collapse(2) schedule(dynamic)
+    for (b = 0; b < B; ++b) {
+        for (int t = 0; t < T; ++t) {
+            const int pos = len[b] - T + t;
+            const size_t row = (size_t)b * T + t;
+            float* out = scores + row * (size_t)Lmax;
+            for (int s = 0; s < Lmax; ++s) {
+                if (s > pos) { out[s] = -INFINITY; continue; }
+                const uint8_t* ks = k + ((size_t)b * Lmax + s) * D;
+                double acc = 0.0;
+                for (int h = 0; h < H; ++h) {
+                    const uint8_t* qh = q + (row * H + h) * D;
+                    double dot = 0.0;
+                    for (int d = 0; d < D; ++d) dot += table[qh[d]] * table[ks[d]];
+                    double wf = (double)w[row * H + h] * (double)q_scale[row * H + h] * sm_scale;
+                    acc += wf * (dot > 0.0 ? dot : 0.0);
+                }
+                out[s] = (float)(acc * (double)k_scale[(size_t)b * Lmax + s]);
+            }
+        }
+    }
+    return ORC_OK;
+}
+
+/* ------------------------------------------------------------------ O3: top-k */
+
+typedef struct { float score; int32_t pos; } scored_pos;
+
+/* larger score first; equal scores by smaller position first */
+static int by_score_desc(const void* a, const void* b)
+{
+    const scored_pos* x = (const scored_pos*)a;
+    const scored_pos* y = (const scored_pos*)b;
+    if (x->score > y->score) return -1;
+    if (x->score < y->score) return 1;
+    return (x->pos > y->pos) - (x->pos < y->pos);
+}
+
+static int by_pos_asc(const void* a, const void* b)
+{
+    int32_t x = *(const int32_t*)a, y = *(const int32_t*)b;
+    return (x > y) - (x < y);
+}
+
+/* Per row: the min(k, pos+1) visible positions with the largest scores (a full sort,
+ * ties by smaller position), written in ascending position order and padded with -1
+ * up to k slots ([IDX] topk(min(index_topk, end_pos)); [V4] -1 sentinel). */
+int orc_topk(const float* scores, const int32_t* len, int B, int T, int Lmax, int k,
+             int32_t* idx)
+{
+    int b;
+    if (k <= 0) return ORC_ERR_SHAPE;
+    for (b = 0; b < B; ++b)
+        if (len[b] < T || len[b] > Lmax) return ORC_ERR_SHAPE;
+
+#pragma omp parallel for collapse(2) schedule(dynamic)
+    for (b = 0; b < B; ++b) {
+        for (int t = 0; t < T; ++t) {
+            const size_t row = (size_t)b * T + t;
+            const int n = len[b] - T + t + 1;
+            const int kk = n < k ? n : k;
+            const float* sc = scores + row * (size_t)Lmax;
+            int32_t* out = idx + row * (size_t)k;
+            scored_pos* v = (scored_pos*)malloc(sizeof(scored_pos) * (size_t)n);
+            for (int s = 0; s < n; ++s) { v[s].score = sc[s]; v[s].pos = s; }
+            qsort(v, (size_t)n, sizeof *v, by_score_desc);
+            for (int j = 0; j < kk; ++j) out[j] = v[j].pos;
+            qsort(out, (size_t)kk, sizeof *out, by_pos_asc);
+            for (int j = kk; j < k; ++j) out[j] = -1;
+            free(v);
+        }
+    }
+    return ORC_OK;
+}
+
+/* ------------------------------------------------------------------ O4: sparse latent attention */
+
+/* Absorbed (MQA) form of the diagram's core attention: every query head h of row
+ * (b,t) attends over the selected latent rows C[b, s] (s = idx[b,t,j] >= 0 and
+ * visible), each row serving as key (all Dv+Dr columns) and value (first Dv columns):
+ *   l_j = sm_scale * sum_{d < Dv+Dr} q[b,t,h,d] * C[b,s_j,d]
+ *   p   = softmax(l),  out[b,t,h,:] = sum_j p_j C[b,s_j,0:Dv],  lse = log sum_j e^{l_j}
+ * A row with no usable index gets out = 0 and lse = -inf. */
+int orc_sparse_mla_decode(const void* q, const void* latent, const int32_t* idx,
+                          const int32_t* len, int dtype, int B, int T, int H, int Dv, int Dr,
+                          int Lmax, int k, double sm_scale, double* out, double* lse)
+{
+    const int Dq = Dv + Dr;
+    int b;
+    for (b = 0; b < B; ++b)
+        if (len[b] < T || len[b] > Lmax) return ORC_ERR_SHAPE;
+    for (size_t i = 0; i < (size_t)B * T * k; ++i)
+        if (idx[i] < -1 || idx[i] >= Lmax) return ORC_ERR_INDEX;
+
+#pragma omp parallel for collapse(2) schedule(dynamic)
+    for (b = 0; b < B; ++b) {
+        for (int t = 0; t < T; ++t) {
+            const size_t row = (size_t)b * T + t;
+            const int pos = len[b] - T + t;
+            const int32_t* sel = idx + row * (size_t)k;
+            double* logit = (double*)malloc(sizeof(double) * (size_t)k);
+            int32_t* keys = (int32_t*)malloc(sizeof(int32_t) * (size_t)k);
+            int n = 0;
+            for (int j = 0; j < k; ++j)
+                if (sel[j] >= 0 && sel[j] <= pos) keys[n++] = sel[j];
+            for (int h = 0; h < H; ++h) {
+                const size_t qoff = (row * H + h) * (size_t)Dq;
+                double* o = out + (row * H + h) * (size_t)Dv;
+                double m = -INFINITY, sum = 0.0;
+                for (int j = 0; j < n; ++j) {
+                    const size_t coff = ((size_t)b * Lmax + keys[j]) * (size_t)Dq;
+                    double dot = 0.0;
+                    for (int d = 0; d < Dq; ++d)
+                        dot += load_elem(q, dtype, qoff + d) * load_elem(latent, dtype, coff + d);
+                    logit[j] = sm_scale * dot;
+                    if (logit[j] > m) m = logit[j];
+                }
+                for (int d = 0; d < Dv; ++d) o[d] = 0.0;
+                if (n == 0) { if (lse) lse[row * H + h] = -INFINITY; continue; }
+                for (int j = 0; j < n; ++j) sum += exp(logit[j] - m);
+                for (int j = 0; j < n; ++j) {
+                    const double p = exp(logit[j] - m) / sum;
+                    const size_t coff = ((size_t)b * Lmax + keys[j]) * (size_t)Dq;
+                    for (int d = 0; d < Dv; ++d) o[d] += p * load_elem(latent, dtype, coff + d);
+                }
+                if (lse) lse[row * H + h] = m + log(sum);
+            }
+            free(logit);
+            free(keys);
+        }
+    }
+    return ORC_OK;
+}
+
+/* ------------------------------------------------------------------ O5: sparse MHA prefill */
+
+/* MHA prefill form ([MLA] prefill excerpt) over a chunk that starts at position 0:
+ * keys and values are the chunk's own T positions, per head.  Row t attends over
+ * the selected positions that are also causally visible (s <= t):
+ *   l_s = sm_scale * q[b,t,h,:] . k[b,s,h,:],  out = sum_s softmax(l)_s v[b,s,h,:].
+ * Gather form: loop over the selected list only. */
+int orc_sparse_mha_prefill(const void* q, const void* kk, const void* v, const int32_t* idx,
+                           int dtype, int B, int T, int H, int Dqk, int Dv, int k,
+                           double sm_scale, double* out, double* lse)
+{
+    int b;
+    for (size_t i = 0; i < (size_t)B * T * k; ++i)
+        if (idx[i] < -1 || idx[i] >= T) return ORC_ERR_INDEX;
+
+#pragma omp parallel for collapse(2) schedule(dynamic)
+    for (b = 0; b < B; ++b) {
+        for (int t = 0; t < T; ++t) {
+            const size_t row = (size_t)b * T + t;
+            const int32_t* sel = idx + row * (size_t)k;
+            double* logit = (double*)malloc(sizeof(double) * (size_t)k);
+            int32_t* keys = (int32_t*)malloc(sizeof(int32_t) * (size_t)k);
+            int n = 0;
+            for (int j = 0; j < k; ++j)
+                if (sel[j] >= 0 && sel[j] <= t) keys[n++] = sel[j];
+            for (int h = 0; h < H; ++h) {
+                const size_t qoff = (row * H + h) * (size_t)Dqk;
+                double* o = out + (row * H + h) * (size_t)Dv;
+                double m = -INFINITY, sum = 0.0;
+                for (int j = 0; j < n; ++j) {
+                    const size_t koff = (((size_t)b * T + keys[j]) * H + h) * (size_t)Dqk;
+                    double dot = 0.0;
+                    for (int d = 0; d < Dqk; ++d)
+                        dot += load_elem(q, dtype, qoff + d) * load_elem(kk, dtype, koff + d);
+                    logit[j] = sm_scale * dot;
+                    if (logit[j] > m) m = logit[j];
+                }
+                for (int d = 0; d < Dv; ++d) o[d] = 0.0;
+                if (n == 0) { if (lse) lse[row * H + h] = -INFINITY; continue; }
+                for (int j = 0; j < n; ++j) sum += exp(logit[j] - m);
+                for (int j = 0; j < n; ++j) {
+                    const double p = exp(logit[j] - m) / sum;
+                    const size_t voff = (((size_t)b * T + keys[j]) * H + h) * (size_t)Dv;
+                    for (int d = 0; d < Dv; ++d) o[d] += p * load_elem(v, dtype, voff + d);
+                }
+                if (lse) lse[row * H + h] = m + log(sum);
+            }
+            free(logit);
+            free(keys);
+        }
+    }
+    return ORC_OK;
+}
+
+/* The same attention computed the way the MLA prefill excerpt writes it: dense scores
+ * over all T keys, plus an additive index mask that is -inf everywhere except 0 at the
+ * selected positions, plus the causal mask, then a softmax over all T keys and a mix
+ * of all values.  Kept as a second, independently structured form for cross-checks. */
+int orc_sparse_mha_prefill_dense(const void* q, const void* kk, const void* v,
+                                 const int32_t* idx, int dtype, int B, int T, int H, int Dqk,
+                                 int Dv, int k, double sm_scale, double* out, double* lse)
+{
+    int b;
+    for (size_t i = 0; i < (size_t)B * T * k; ++i)
+        if (idx[i] < -1 || idx[i] >= T) return ORC_ERR_INDEX;
+
+#pragma omp parallel for collapse(2) schedule(dynamic)
+    for (b = 0; b < B; ++b) {
+        for (int t = 0; t < T; ++t) {
+            const size_t row = (size_t)b * T + t;
+            double* mask = (double*)malloc(sizeof(double) * (size_t)T);
+            double* sc = (double*)malloc(sizeof(double) * (size_t)T);
+            for (int s = 0; s < T; ++s) mask[s] = -INFINITY;           /* full(-inf)      */
+            for (int j = 0; j < k; ++j)
+                if (idx[row * k + j] >= 0) mask[idx[row * k + j]] = 0.0; /* scatter_(.., 0) */
+            for (int s = t + 1; s < T; ++s) mask[s] += -INFINITY;       /* += causal mask  */
+            for (int h = 0; h < H; ++h) {
+                const size_t qoff = (row * H + h) * (size_t)Dqk;
+                double* o = out + (row * H + h) * (size_t)Dv;
+                double m = -INFINITY, sum = 0.0;
+                for (int s = 0; s < T; ++s) {
+                    const size_t koff = (((size_t)b * T + s) * H + h) * (size_t)Dqk;
+                    double dot = 0.0;
+                    for (int d = 0; d < Dqk; ++d)
+                        dot += load_elem(q, dtype, qoff + d) * load_elem(kk, dtype, koff + d);
+                    sc[s] = dot * sm_scale + mask[s];
+                    if (sc[s] > m) m = sc[s];
+                }
+                for (int d = 0; d < Dv; ++d) o[d] = 0.0;
+                if (m == -INFINITY) { if (lse) lse[row * H + h] = -INFINITY; continue; }
+                for (int s = 0; s < T; ++s) sum += exp(sc[s] - m);
+                for (int s = 0; s < T; ++s) {
+                    const double p = exp(sc[s] - m) / sum;
+                    if (p == 0.0) continue;
+                    const size_t voff = (((size_t)b * T + s) * H + h) * (size_t)Dv;
+                    for (int d = 0; d < Dv; ++d) o[d] += p * load_elem(v, dtype, voff + d);
+                }
+                if (lse) lse[row * H + h] = m + log(sum);
+            }
+            free(mask);
+            free(sc);
+        }
+    }
+    return ORC_OK;
+}
+
+/* ------------------------------------------------------------------ O6: layer step */
+
+/* Index scores -> top-k -> sparse latent attention ([DIAG], one layer).  Scores and
+ * indices are optionally returned (NULL to discard). */
+int orc_layer_step_latent(const uint8_t* q_i, const float* q_scale, const float* w,
+                          const uint8_t* k_i, const float* k_scale, const int32_t* len,
+                          int B, int T, int H_I, int D_I, int Lmax, double sm_scale_i, int k,
+                          const void* q, const void* latent, int dtype, int H, int Dv, int Dr,
+                          double sm_scale, double* out, double* lse, float* scores_out,
+                          int32_t* idx_out)
+{
+    float* scores = scores_out ? scores_out
+                               : (float*)malloc(sizeof(float) * (size_t)B * T * Lmax);
+    int32_t* idx = idx_out ? idx_out : (int32_t*)malloc(sizeof(int32_t) * (size_t)B * T * k);
+    int rc = orc_index_scores(q_i, q_scale, w, k_i, k_scale, len, B, T, H_I, D_I, Lmax,
+                              sm_scale_i, scores);
+    if (rc == ORC_OK) rc = orc_topk(scores, len, B, T, Lmax, k, idx);
+    if (rc == ORC_OK)
+        rc = orc_sparse_mla_decode(q, latent, idx, len, dtype, B, T, H, Dv, Dr, Lmax, k,
+                                   sm_scale, out, lse);
+    if (!scores_out) free(scores);
+    if (!idx_out) free(idx);
+    return rc;
+}
+
+/* Index scores -> top-k -> sparse MHA prefill ([IDX] + [MLA] prefill), chunk from 0. */
+int orc_layer_step_mha(const uint8_t* q_i, const float* q_scale, const float* w,
+                       const uint8_t* k_i, const float* k_scale, int B, int T, int H_I, int D_I,
+                       double sm_scale_i, int k, const void* q, const void* kk, const void* v,
+                       int dtype, int H, int Dqk, int Dv, double sm_scale, double* out,
+                       double* lse, float* scores_out, int32_t* idx_out)
+{
+    int32_t* len = (int32_t*)malloc(sizeof(int32_t) * (size_t)B);
+    float* scores = scores_out ? scores_out
+                               : (float*)malloc(sizeof(float) * (size_t)B * T * T);
+    int32_t* idx = idx_out ? idx_out : (int32_t*)malloc(sizeof(int32_t) * (size_t)B * T * k);
+    int rc;
+    for (int b = 0; b < B; ++b) len[b] = T;
+    rc = orc_index_scores(q_i, q_scale, w, k_i, k_scale, len, B, T, H_I, D_I, T, sm_scale_i,
+                          scores);
+    if (rc == ORC_OK) rc = orc_topk(scores, len, B, T, T, k, idx);
+    if (rc == ORC_OK)
+        rc = orc_sparse_mha_prefill(q, kk, v, idx, dtype, B, T, H, Dqk, Dv, k, sm_scale, out,
+                                    lse);
+    if (!scores_out) free(scores);
+    if (!idx_out) free(idx);
+    free(len);
+    return rc;
+}
+
+int orc_max_threads(void)
+{
+#ifdef _OPENMP
+    extern int omp_get_max_threads(void);
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}

@@ -1,0 +1,382 @@
+"""Pins of the CPU reference against facts that do not come from the reference itself.
+
+Each ``pin_*`` function takes the oracle module and raises AssertionError on a
+mismatch.  They are collected by ``test_oracle_pins.py`` and re-run by
+``test_oracle_mutations.py`` against deliberately broken builds of the oracle, to
+show that a plausible mistake (a dropped term, a wrong sign or index, a transposed
+operand) fails at least one of them.
+
+What pins what:
+  * e4m3fn decoding        -> torch's float8_e4m3fn decoding of all 256 codes;
+  * index scores           -> closed forms (all products positive: the score is a
+                              plain matrix product, computed by torch.matmul; all
+                              products negative: exactly zero; one head positive),
+                              the causal pattern, and invariances (head order,
+                              column order, scale linearity);
+  * top-k                  -> torch.topk / numpy's stable argsort, cardinality and
+                              ordering invariants;
+  * sparse attention       -> torch's scaled_dot_product_attention with a boolean
+                              mask of the selected and visible keys (k >= n is
+                              plain dense causal attention), k = 1, equal values;
+  * MHA prefill            -> the same library routine per head, and the pages'
+                              dense "scores + index mask + causal mask" form;
+  * layer step             -> with k >= len the result is dense attention whatever
+                              the indexer does; a planted dominant key is picked.
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+import torch
+import torch.nn.functional as F
+
+
+def _fp8_values(codes: np.ndarray) -> np.ndarray:
+    return torch.from_numpy(np.ascontiguousarray(codes)).view(torch.float8_e4m3fn).double().numpy()
+
+
+def _rand_codes(rng, shape, positive=False, negative=False):
+    # finite e4m3fn codes: exclude 0x7F / 0xFF (NaN)
+    c = rng.integers(0, 0x7F, size=shape).astype(np.uint8)   # 0x00..0x7E, all >= 0
+    if negative:
+        c = c | 0x80
+    elif not positive:
+        c = c | (rng.integers(0, 2, size=shape).astype(np.uint8) << 7)
+    return c
+
+
+def _nonzero_pos_codes(rng, shape):
+    # strictly positive normal codes 0x08..0x7E (values 2^-6 .. 448)
+    return rng.integers(0x08, 0x7F, size=shape).astype(np.uint8)
+
+
+# ----------------------------------------------------------------------------- codec
+
+def pin_e4m3fn_codec(o):
+    codes = np.arange(256, dtype=np.uint8)
+    ref = _fp8_values(codes)
+    got = np.array([o.e4m3fn_value(int(c)) for c in codes])
+    nan_ref = np.isnan(ref)
+    assert np.array_equal(nan_ref, np.isnan(got)), "NaN codes differ"
+    assert set(np.flatnonzero(nan_ref)) == {0x7F, 0xFF}
+    assert np.array_equal(ref[~nan_ref], got[~nan_ref]), "finite e4m3fn values differ"
+    assert o.e4m3fn_value(0x7E) == 448.0 and o.e4m3fn_value(0x01) == 2.0 ** -9
+
+
+def pin_bf16_codec(o):
+    rng = np.random.default_rng(11)
+    bits = rng.integers(0, 1 << 16, size=512).astype(np.uint16)
+    ref = torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).double().numpy()
+    got = np.array([o.bf16_value(int(b)) for b in bits])
+    fin = np.isfinite(ref)
+    assert np.array_equal(ref[fin], got[fin])
+
+
+# ----------------------------------------------------------------------------- index scores
+
+def _idx_case(rng, B, T, H, D, Lmax, lens, qpos=False, kpos=False, qneg=False):
+    q = _nonzero_pos_codes(rng, (B, T, H, D)) if qpos else _rand_codes(rng, (B, T, H, D), negative=qneg)
+    k = _nonzero_pos_codes(rng, (B, Lmax, D)) if kpos else _rand_codes(rng, (B, Lmax, D))
+    qs = rng.uniform(0.5, 2.0, (B, T, H)).astype(np.float32)
+    w = rng.standard_normal((B, T, H)).astype(np.float32)
+    ks = rng.uniform(0.5, 2.0, (B, Lmax)).astype(np.float32)
+    return q, qs, w, k, ks, np.asarray(lens, np.int32)
+
+
+def pin_index_scores_positive_closed_form(o):
+    """All q and k codes positive -> every product is positive, ReLU is the identity and
+    the score is k_scale[s] * ((w*q_scale*sm) @ Q) . K[s]: one matrix product."""
+    rng = np.random.default_rng(21)
+    B, T, H, D, Lmax = 2, 3, 5, 32, 40
+    lens = [40, 37]
+    q, qs, w, k, ks, lens = _idx_case(rng, B, T, H, D, Lmax, lens, qpos=True, kpos=True)
+    sm = D ** -0.5
+    got = o.index_scores(q, qs, w, k, ks, lens, sm)
+    Q = torch.from_numpy(_fp8_values(q))
+    K = torch.from_numpy(_fp8_values(k))
+    wf = torch.from_numpy(w.astype(np.float64) * qs.astype(np.float64) * sm)
+    for b in range(B):
+        for t in range(T):
+            pos = int(lens[b]) - T + t
+            u = wf[b, t] @ Q[b, t]                        # [D]
+            ref = torch.matmul(K[b, : pos + 1], u) * torch.from_numpy(ks[b, : pos + 1].astype(np.float64))
+            np.testing.assert_allclose(got[b, t, : pos + 1], ref.numpy(), rtol=2e-7, atol=0)
+            assert np.all(np.isneginf(got[b, t, pos + 1:]))
+
+
+def pin_index_scores_relu_zero(o):
+    """All q codes negative, all k codes positive -> every product < 0 -> score exactly 0."""
+    rng = np.random.default_rng(22)
+    q, qs, w, k, ks, lens = _idx_case(rng, 1, 1, 4, 32, 16, [16], qneg=True, kpos=True)
+    q = q | 0x80
+    q[q == 0x80] = 0x88          # no negative zero: strictly negative values
+    got = o.index_scores(q, qs, w, k, ks, lens, 1.0)
+    assert np.all(got == 0.0)
+
+
+def pin_index_scores_one_head(o):
+    """Head 0 has positive products and a NEGATIVE weight; heads 1.. have negative
+    products.  ReLU then weight: the score is w0*qs0*sm*dot0*ks (negative)."""
+    rng = np.random.default_rng(23)
+    H, D, L = 4, 32, 24
+    q = np.empty((1, 1, H, D), np.uint8)
+    q[0, 0, 0] = _nonzero_pos_codes(rng, D)
+    q[0, 0, 1:] = _nonzero_pos_codes(rng, (H - 1, D)) | 0x80
+    k = _nonzero_pos_codes(rng, (1, L, D))
+    qs = rng.uniform(0.5, 2.0, (1, 1, H)).astype(np.float32)
+    w = -np.abs(rng.standard_normal((1, 1, H))).astype(np.float32) - 0.1
+    ks = rng.uniform(0.5, 2.0, (1, L)).astype(np.float32)
+    sm = 0.25
+    got = o.index_scores(q, qs, w, k, ks, np.array([L], np.int32), sm)
+    K = torch.from_numpy(_fp8_values(k[0]))
+    dot0 = torch.matmul(K, torch.from_numpy(_fp8_values(q[0, 0, 0])))
+    ref = float(w[0, 0, 0]) * float(qs[0, 0, 0]) * sm * dot0.numpy() * ks[0].astype(np.float64)
+    assert np.all(ref < 0)
+    np.testing.assert_allclose(got[0, 0], ref, rtol=2e-7)
+
+
+def pin_index_scores_invariances(o):
+    """Mixed signs: permuting heads (with their weights) or permuting the d columns of q and
+    k together leaves the scores unchanged; doubling k_scale doubles them; the visible
+    pattern is s <= len - T + t."""
+    rng = np.random.default_rng(24)
+    B, T, H, D, Lmax = 2, 4, 6, 64, 30
+    q, qs, w, k, ks, lens = _idx_case(rng, B, T, H, D, Lmax, [30, 19])
+    sm = D ** -0.5
+    base = o.index_scores(q, qs, w, k, ks, lens, sm)
+    perm_h = rng.permutation(H)
+    g = o.index_scores(q[:, :, perm_h], qs[:, :, perm_h], w[:, :, perm_h], k, ks, lens, sm)
+    np.testing.assert_allclose(g, base, rtol=1e-6, atol=1e-30)
+    perm_d = rng.permutation(D)
+    g = o.index_scores(q[..., perm_d], qs, w, k[..., perm_d], ks, lens, sm)
+    np.testing.assert_array_equal(g, base)
+    g = o.index_scores(q, qs, w, k, ks * 2, lens, sm)
+    np.testing.assert_array_equal(g, base * 2)
+    for b in range(B):
+        for t in range(T):
+            pos = int(lens[b]) - T + t
+            assert np.all(np.isfinite(base[b, t, : pos + 1]))
+            assert np.all(np.isneginf(base[b, t, pos + 1:]))
+    # a non-trivial mix of positive and zero contributions
+    assert np.any(base[np.isfinite(base)] > 0) and np.any(base[np.isfinite(base)] < 0)
+
+
+# ----------------------------------------------------------------------------- top-k
+
+def pin_topk_library(o):
+    """Distinct scores: the chosen set equals torch.topk's; order ascending; -1 tail."""
+    rng = np.random.default_rng(31)
+    B, T, Lmax, k = 3, 5, 50, 12
+    lens = np.array([50, 20, 9], np.int32)
+    scores = rng.standard_normal((B, T, Lmax)).astype(np.float32)
+    for b in range(B):
+        for t in range(T):
+            scores[b, t, int(lens[b]) - T + t + 1:] = -np.inf
+    idx = o.topk(scores, lens, k)
+    for b in range(B):
+        for t in range(T):
+            n = int(lens[b]) - T + t + 1
+            kk = min(k, n)
+            ref = torch.topk(torch.from_numpy(scores[b, t, :n]), kk).indices.numpy()
+            row = idx[b, t]
+            assert set(row[:kk].tolist()) == set(ref.tolist())
+            assert np.all(np.diff(row[:kk]) > 0)
+            assert np.all(row[kk:] == -1)
+            assert row[:kk].max() <= n - 1
+
+
+def pin_topk_ties(o):
+    """Heavy ties: the chosen set is the first k of a stable descending sort (equal scores
+    keep the smaller position); every chosen score >= every unchosen visible score."""
+    rng = np.random.default_rng(32)
+    B, T, Lmax, k = 2, 3, 64, 10
+    lens = np.array([64, 40], np.int32)
+    scores = rng.integers(-3, 4, size=(B, T, Lmax)).astype(np.float32)
+    idx = o.topk(scores, lens, k)
+    for b in range(B):
+        for t in range(T):
+            n = int(lens[b]) - T + t + 1
+            order = np.argsort(-scores[b, t, :n], kind="stable")[:k]
+            assert sorted(idx[b, t, :k].tolist()) == sorted(order.tolist())
+            chosen = scores[b, t, idx[b, t, :k]]
+            rest = np.delete(scores[b, t, :n], idx[b, t, :k])
+            assert chosen.min() >= rest.max()
+
+
+def pin_topk_short_rows(o):
+    """n <= k: every visible position is returned, padded with -1."""
+    scores = np.random.default_rng(33).standard_normal((1, 4, 8)).astype(np.float32)
+    lens = np.array([6], np.int32)
+    idx = o.topk(scores, lens, 8)
+    for t in range(4):
+        n = 6 - 4 + t + 1
+        assert idx[0, t, :n].tolist() == list(range(n))
+        assert np.all(idx[0, t, n:] == -1)
+
+
+# ----------------------------------------------------------------------------- attention
+
+def _sdpa_rows(q, keys, vals, mask, scale):
+    """torch SDPA in float64: q [H,E], keys [S,E], vals [S,Ev], mask [S] bool."""
+    out = F.scaled_dot_product_attention(q[None], keys[None], vals[None],
+                                         attn_mask=mask[None, None, :].expand(1, q.shape[0], -1),
+                                         scale=scale)
+    return out[0]
+
+
+def pin_latent_attention_library(o):
+    """Sparse latent attention == SDPA over a boolean mask of the selected and visible
+    positions (with k >= n this is plain dense causal attention)."""
+    rng = np.random.default_rng(41)
+    B, T, H, Dv, Dr, Lmax = 2, 3, 4, 24, 8, 40
+    lens = np.array([40, 21], np.int32)
+    q = rng.standard_normal((B, T, H, Dv + Dr))
+    lat = rng.standard_normal((B, Lmax, Dv + Dr))
+    sm = (Dv + Dr) ** -0.5
+    for k in (7, 64):
+        idx = np.full((B, T, k), -1, np.int32)
+        for b in range(B):
+            for t in range(T):
+                n = int(lens[b]) - T + t + 1
+                m = min(k, n)
+                idx[b, t, :m] = rng.choice(n, size=m, replace=False)
+        if k == 7:
+            # one selected slot per row points past the row's position: it must be ignored
+            for b in range(B):
+                for t in range(T):
+                    pos = int(lens[b]) - T + t
+                    idx[b, t, -1] = rng.integers(pos + 1, Lmax) if pos + 1 < Lmax else -1
+        out, lse = o.sparse_mla_decode(q, lat, idx, lens, Dv, sm)
+        for b in range(B):
+            for t in range(T):
+                pos = int(lens[b]) - T + t
+                mask = torch.zeros(Lmax, dtype=torch.bool)
+                sel = idx[b, t][(idx[b, t] >= 0) & (idx[b, t] <= pos)]
+                mask[torch.from_numpy(sel.astype(np.int64))] = True
+                C = torch.from_numpy(lat[b])
+                ref = _sdpa_rows(torch.from_numpy(q[b, t]), C, C[:, :Dv], mask, sm)
+                np.testing.assert_allclose(out[b, t], ref.numpy(), rtol=1e-10, atol=1e-12)
+                logits = torch.from_numpy(q[b, t]) @ C[mask].T * sm
+                np.testing.assert_allclose(lse[b, t], torch.logsumexp(logits, -1).numpy(), rtol=1e-12)
+
+
+def pin_latent_attention_special(o):
+    """k = 1 -> the selected value row exactly; all value rows equal -> that row."""
+    rng = np.random.default_rng(42)
+    H, Dv, Dr, L = 3, 16, 4, 12
+    q = rng.standard_normal((1, 1, H, Dv + Dr))
+    lat = rng.standard_normal((1, L, Dv + Dr))
+    idx = np.array([[[5]]], np.int32)
+    out, lse = o.sparse_mla_decode(q, lat, idx, np.array([L], np.int32), Dv, 0.3)
+    for h in range(H):
+        np.testing.assert_array_equal(out[0, 0, h], lat[0, 5, :Dv])
+        np.testing.assert_allclose(lse[0, 0, h], 0.3 * q[0, 0, h] @ lat[0, 5], rtol=1e-13)
+    lat2 = lat.copy()
+    lat2[0, :, :Dv] = lat[0, 0, :Dv]
+    idx = np.array([[[0, 3, 7, -1]]], np.int32)
+    out, _ = o.sparse_mla_decode(q, lat2, idx, np.array([L], np.int32), Dv, 0.3)
+    for h in range(H):
+        np.testing.assert_allclose(out[0, 0, h], lat[0, 0, :Dv], rtol=1e-13)
+
+
+def pin_mha_prefill_library(o):
+    """Per head, sparse MHA == SDPA with mask = selected & (s <= t); the pages' dense
+    index-mask form agrees."""
+    rng = np.random.default_rng(43)
+    B, T, H, Dqk, Dv, k = 1, 12, 3, 20, 10, 5
+    q = rng.standard_normal((B, T, H, Dqk))
+    kk = rng.standard_normal((B, T, H, Dqk))
+    v = rng.standard_normal((B, T, H, Dv))
+    idx = np.full((B, T, k), -1, np.int32)
+    for t in range(T):
+        m = min(k, T)
+        idx[0, t, :m] = rng.choice(T, size=m, replace=False)   # may include s > t
+    idx[0, 0, 0] = 0                                            # every row sees >= 1 key
+    for t in range(1, T):
+        if not np.any((idx[0, t] >= 0) & (idx[0, t] <= t)):
+            idx[0, t, 0] = t
+    sm = Dqk ** -0.5
+    out, lse = o.sparse_mha_prefill(q, kk, v, idx, sm)
+    out_d, lse_d = o.sparse_mha_prefill_dense(q, kk, v, idx, sm)
+    np.testing.assert_allclose(out, out_d, rtol=1e-12, atol=1e-14)
+    np.testing.assert_allclose(lse, lse_d, rtol=1e-12)
+    for t in range(T):
+        mask = torch.zeros(T, dtype=torch.bool)
+        sel = idx[0, t][(idx[0, t] >= 0) & (idx[0, t] <= t)]
+        mask[torch.from_numpy(sel.astype(np.int64))] = True
+        for h in range(H):
+            ref = _sdpa_rows(torch.from_numpy(q[0, t, h][None]), torch.from_numpy(kk[0, :, h]),
+                             torch.from_numpy(v[0, :, h]), mask, sm)
+            np.testing.assert_allclose(out[0, t, h], ref[0].numpy(), rtol=1e-10, atol=1e-12)
+
+
+# ----------------------------------------------------------------------------- layer step
+
+def pin_layer_step_dense_limit(o):
+    """k >= len: the selection keeps every visible key, so the step is dense causal
+    attention (SDPA with is_causal-style mask) whatever the index scores are."""
+    rng = np.random.default_rng(51)
+    B, T, H_I, D_I, Lmax = 1, 16, 4, 32, 16
+    H, Dv, Dr = 2, 16, 8
+    q_i = _rand_codes(rng, (B, T, H_I, D_I))
+    k_i = _rand_codes(rng, (B, Lmax, D_I))
+    qs = np.ones((B, T, H_I), np.float32)
+    w = rng.standard_normal((B, T, H_I)).astype(np.float32)
+    ks = np.ones((B, Lmax), np.float32)
+    lens = np.array([Lmax], np.int32)
+    q = rng.standard_normal((B, T, H, Dv + Dr))
+    lat = rng.standard_normal((B, Lmax, Dv + Dr))
+    sm = 0.2
+    out, lse, idx = o.layer_step_latent(q_i, qs, w, k_i, ks, lens, D_I ** -0.5, 16, q, lat, Dv, sm)
+    C = torch.from_numpy(lat[0])
+    for t in range(T):
+        mask = torch.arange(Lmax) <= t
+        ref = _sdpa_rows(torch.from_numpy(q[0, t]), C, C[:, :Dv], mask, sm)
+        np.testing.assert_allclose(out[0, t], ref.numpy(), rtol=1e-10, atol=1e-12)
+
+
+def pin_layer_step_planted_key(o):
+    """k = 1 with one key whose index score dominates: the output is that key's value
+    row for every head (decode, T = 1)."""
+    rng = np.random.default_rng(52)
+    H_I, D_I, L = 4, 32, 20
+    H, Dv, Dr = 3, 16, 8
+    q_i = _nonzero_pos_codes(rng, (1, 1, H_I, D_I))
+    q_i[..., :] = 0x38                                   # 1.0 everywhere
+    k_i = _rand_codes(rng, (1, L, D_I))
+    k_i[0, :] = k_i[0, :] | 0x80                         # all keys negative ...
+    k_i[0, 13] = 0x40                                    # ... except key 13 (= 2.0)
+    qs = np.ones((1, 1, H_I), np.float32)
+    w = np.ones((1, 1, H_I), np.float32)
+    ks = np.ones((1, L), np.float32)
+    q = rng.standard_normal((1, 1, H, Dv + Dr))
+    lat = rng.standard_normal((1, L, Dv + Dr))
+    out, lse, idx = o.layer_step_latent(q_i, qs, w, k_i, ks, np.array([L], np.int32),
+                                        D_I ** -0.5, 1, q, lat, Dv, 0.1)
+    assert idx[0, 0, 0] == 13
+    for h in range(H):
+        np.testing.assert_array_equal(out[0, 0, h], lat[0, 13, :Dv])
+
+
+def pin_layer_step_mha_dense_limit(o):
+    """MHA form with k >= T equals per-head dense causal attention (SDPA is_causal)."""
+    rng = np.random.default_rng(53)
+    B, T, H_I, D_I, H, Dqk, Dv = 1, 10, 4, 32, 2, 12, 6
+    q_i = _rand_codes(rng, (B, T, H_I, D_I))
+    k_i = _rand_codes(rng, (B, T, D_I))
+    qs = np.ones((B, T, H_I), np.float32)
+    w = rng.standard_normal((B, T, H_I)).astype(np.float32)
+    ks = np.ones((B, T), np.float32)
+    q = rng.standard_normal((B, T, H, Dqk))
+    kk = rng.standard_normal((B, T, H, Dqk))
+    v = rng.standard_normal((B, T, H, Dv))
+    out, lse, idx = o.layer_step_mha(q_i, qs, w, k_i, ks, D_I ** -0.5, T, q, kk, v, 0.3)
+    qt = torch.from_numpy(q[0]).transpose(0, 1)      # [H,T,D]
+    kt = torch.from_numpy(kk[0]).transpose(0, 1)
+    vt = torch.from_numpy(v[0]).transpose(0, 1)
+    ref = F.scaled_dot_product_attention(qt, kt, vt, is_causal=True, scale=0.3).transpose(0, 1)
+    np.testing.assert_allclose(out[0], ref.numpy(), rtol=1e-10, atol=1e-12)
+
+
+ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

@@ -1,0 +1,84 @@
+"""Plant a mistake in the CPU reference (on the CPU, in a private build) and check that
+at least one pin of oracle_pins.py fails.  This shows the pins would catch a dropped
+term, a wrong sign, a wrong index or a transposed operand in the reference."""
+import contextlib
+import ctypes
+import os
+import subprocess
+
+import pytest
+
+from oracle_pins import ALL_PINS
+
+MUTATIONS = [
+    ("drop ReLU", "acc += wf * (dot > 0.0 ? dot : 0.0);", "acc += wf * dot;"),
+    ("ReLU after weighting", "acc += wf * (dot > 0.0 ? dot : 0.0);",
+     "acc += (wf * dot > 0.0 ? wf * dot : 0.0);"),
+    ("drop q_scale", "(double)w[row * H + h] * (double)q_scale[row * H + h] * sm_scale",
+     "(double)w[row * H + h] * sm_scale"),
+    ("drop indexer scale", "(double)w[row * H + h] * (double)q_scale[row * H + h] * sm_scale",
+     "(double)w[row * H + h] * (double)q_scale[row * H + h]"),
+    ("k_scale indexed by row", "(double)k_scale[(size_t)b * Lmax + s]",
+     "(double)k_scale[(size_t)b * Lmax + t]"),
+    ("causal off by one", "if (s > pos) { out[s] = -INFINITY; continue; }",
+     "if (s >= pos) { out[s] = -INFINITY; continue; }"),
+    ("query head ignored", "const uint8_t* qh = q + (row * H + h) * D;",
+     "const uint8_t* qh = q + (row * H) * D;"),
+    ("decode e4m3 bias 8", "mag = ldexp(1.0 + (double)m / 8.0, e - 7);",
+     "mag = ldexp(1.0 + (double)m / 8.0, e - 8);"),
+    ("top-k takes smallest", "for (int j = 0; j < kk; ++j) out[j] = v[j].pos;",
+     "for (int j = 0; j < kk; ++j) out[j] = v[n - 1 - j].pos;"),
+    ("top-k ties prefer larger position", "return (x->pos > y->pos) - (x->pos < y->pos);",
+     "return (x->pos < y->pos) - (x->pos > y->pos);"),
+    ("top-k drops current position", "const int n = len[b] - T + t + 1;",
+     "const int n = len[b] - T + t;"),
+    ("attention scale dropped", "logit[j] = sm_scale * dot;", "logit[j] = dot;"),
+    ("latent key drops rope part", "for (int d = 0; d < Dq; ++d)\n", "for (int d = 0; d < Dv; ++d)\n"),
+    ("latent value offset", "o[d] += p * load_elem(latent, dtype, coff + d);",
+     "o[d] += p * load_elem(latent, dtype, coff + Dr + d);"),
+    ("latent ignores visibility", "if (sel[j] >= 0 && sel[j] <= pos) keys[n++] = sel[j];",
+     "if (sel[j] >= 0) keys[n++] = sel[j];"),
+    ("lse without max", "lse[row * H + h] = m + log(sum);", "lse[row * H + h] = log(sum);"),
+    ("MHA ignores causality", "if (sel[j] >= 0 && sel[j] <= t) keys[n++] = sel[j];",
+     "if (sel[j] >= 0) keys[n++] = sel[j];"),
+    ("MHA key head fixed", "const size_t koff = (((size_t)b * T + keys[j]) * H + h) * (size_t)Dqk;",
+     "const size_t koff = (((size_t)b * T + keys[j]) * H + 0) * (size_t)Dqk;"),
+    ("MHA value from the query row", "const size_t voff = (((size_t)b * T + keys[j]) * H + h) * (size_t)Dv;",
+     "const size_t voff = (((size_t)b * T + t) * H + h) * (size_t)Dv;"),
+]
+
+
+@contextlib.contextmanager
+def _variant(orc, path):
+    saved = orc._load()
+    lib = ctypes.CDLL(path)
+    for fn in ("orc_e4m3fn_value", "orc_bf16_value", "orc_index_scores", "orc_topk",
+               "orc_sparse_mla_decode", "orc_sparse_mha_prefill", "orc_sparse_mha_prefill_dense",
+               "orc_layer_step_latent", "orc_layer_step_mha", "orc_max_threads"):
+        getattr(lib, fn).argtypes = getattr(saved, fn).argtypes
+        getattr(lib, fn).restype = getattr(saved, fn).restype
+    orc._lib = lib
+    try:
+        yield
+    finally:
+        orc._lib = saved
+
+
+@pytest.mark.parametrize("name,old,new", MUTATIONS, ids=[m[0] for m in MUTATIONS])
+def test_planted_mistake_is_caught(orc, tmp_path, name, old, new):
+    src = open(os.path.join(os.path.dirname(orc.__file__), "dsa_oracle.c")).read()
+    assert old in src, f"mutation anchor missing: {old!r}"
+    (tmp_path / "dsa_oracle.h").write_text(
+        open(os.path.join(os.path.dirname(orc.__file__), "dsa_oracle.h")).read())
+    (tmp_path / "m.c").write_text(src.replace(old, new))
+    so = str(tmp_path / "libm.so")
+    subprocess.run(["gcc", "-O1", "-std=c11", "-fopenmp", "-fPIC", "-shared", "-o", so,
+                    str(tmp_path / "m.c"), "-lm"], check=True)
+    failed = []
+    with _variant(orc, so):
+        for pin in ALL_PINS:
+            try:
+                pin(orc)
+            except Exception:
+                failed.append(pin.__name__)
+    assert failed, f"no pin caught the planted mistake '{name}'"
