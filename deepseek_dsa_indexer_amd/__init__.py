@@ -1,0 +1,18 @@
+"""MI355X (gfx950) DeepSeek Sparse Attention layer step.
+
+The computation lives in ``libdsa_amd.so`` (HIP kernels behind the C ABI of
+``include/dsa.h``); this package is its Python binding:
+
+    index_scores(q_fp8, q_scale, w, k_fp8, k_scale, lens, sm_scale_i)  -> scores
+    topk(scores, lens, k)                                                -> idx
+    sparse_mla_decode(q, latent, idx, lens, Dv, sm_scale)                -> (out, lse)
+    sparse_mla_prefill(q, k, v, idx, sm_scale)                           -> (out, lse)
+    LayerStep(...)()                                                     -> (out, lse)
+
+Build the library with ``python -m deepseek_dsa_indexer_amd.build``.
+"""
+from ._native import (DSAError, LayerStep, index_scores, library_path, load, sparse_mla_decode,
+                      sparse_mla_prefill, topk)
+
+__all__ = ["DSAError", "LayerStep", "index_scores", "library_path", "load", "sparse_mla_decode",
+           "sparse_mla_prefill", "topk"]

@@ -1,0 +1,305 @@
+// dsa_abi.cpp -- the extern "C" entry points of libdsa_amd: argument validation,
+// workspace carving and kernel launches on the caller's stream.  See include/dsa.h for
+// the contract of each call.
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+
+#include "../../include/dsa.h"
+#include "dsa_internal.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+dsa_status fail(dsa_status st, const char* fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_last_error = buf;
+    return st;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+size_t round_up(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
+
+dsa_status hip_status(hipError_t e, const char* what) {
+    if (e != hipSuccess) return fail(DSA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+    return DSA_OK;
+}
+
+#define DSA_REQUIRE(cond, st, ...) \
+    do {                           \
+        if (!(cond)) return fail(st, __VA_ARGS__); \
+    } while (0)
+
+constexpr long long kMaxRows = 1LL << 30;
+
+dsa_status check_index_args(const uint8_t* q_fp8, const float* q_scale, const float* w,
+                            const uint8_t* k_fp8, const float* k_scale, const int32_t* len,
+                            int B, int T, int H_I, int d_I, int Lmax) {
+    DSA_REQUIRE(q_fp8 && q_scale && w && k_fp8 && k_scale && len, DSA_ERR_NULL,
+                "index scores: NULL input pointer");
+    DSA_REQUIRE(B >= 1 && T >= 1 && Lmax >= 1 && T <= Lmax, DSA_ERR_SHAPE,
+                "index scores: need B >= 1 and 1 <= T <= Lmax (B=%d T=%d Lmax=%d)", B, T, Lmax);
+    DSA_REQUIRE(static_cast<long long>(B) * T <= kMaxRows, DSA_ERR_SHAPE, "index scores: B*T too large");
+    DSA_REQUIRE(H_I >= 1 && H_I <= 64, DSA_ERR_SHAPE, "index scores: H_I=%d not in [1, 64]", H_I);
+    DSA_REQUIRE(d_I == 32 || d_I == 64 || d_I == 128, DSA_ERR_SHAPE,
+                "index scores: d_I=%d not in {32, 64, 128}", d_I);
+    DSA_REQUIRE(aligned16(q_fp8) && aligned16(q_scale) && aligned16(w) && aligned16(k_fp8) &&
+                    aligned16(k_scale) && aligned16(len),
+                DSA_ERR_ALIGN, "index scores: inputs must be 16-byte aligned");
+    return DSA_OK;
+}
+
+dsa_status check_topk_args(const float* scores, const int32_t* len, int B, int T, int Lmax, int k,
+                           const int32_t* idx) {
+    DSA_REQUIRE(scores && len && idx, DSA_ERR_NULL, "topk: NULL pointer");
+    DSA_REQUIRE(B >= 1 && T >= 1 && Lmax >= 1 && T <= Lmax && k >= 1, DSA_ERR_SHAPE,
+                "topk: need B, T, k >= 1 and T <= Lmax (B=%d T=%d Lmax=%d k=%d)", B, T, Lmax, k);
+    DSA_REQUIRE(static_cast<long long>(B) * T <= kMaxRows, DSA_ERR_SHAPE, "topk: B*T too large");
+    DSA_REQUIRE(aligned16(scores) && aligned16(len) && aligned16(idx), DSA_ERR_ALIGN,
+                "topk: pointers must be 16-byte aligned");
+    return DSA_OK;
+}
+
+constexpr size_t kGenericLdsLimit = 64 * 1024;
+
+dsa_status check_latent_args(const void* q, const void* latent, const int32_t* idx,
+                             const int32_t* len, int B, int T, int H, int Dv, int Dr, int Lmax,
+                             int k, dsa_dtype dt, const void* out) {
+    DSA_REQUIRE(q && latent && idx && len && out, DSA_ERR_NULL, "sparse_mla_decode: NULL pointer");
+    DSA_REQUIRE(dt == DSA_F32 || dt == DSA_BF16, DSA_ERR_DTYPE, "sparse_mla_decode: bad dtype %d",
+                static_cast<int>(dt));
+    DSA_REQUIRE(B >= 1 && T >= 1 && Lmax >= 1 && T <= Lmax && H >= 1 && Dv >= 1 && Dr >= 0 &&
+                    Dv + Dr <= 1024 && k >= 1,
+                DSA_ERR_SHAPE, "sparse_mla_decode: bad shape (B=%d T=%d H=%d Dv=%d Dr=%d Lmax=%d k=%d)",
+                B, T, H, Dv, Dr, Lmax, k);
+    DSA_REQUIRE(static_cast<long long>(B) * T * H <= kMaxRows, DSA_ERR_SHAPE,
+                "sparse_mla_decode: B*T*H too large");
+    DSA_REQUIRE(aligned16(q) && aligned16(latent) && aligned16(idx) && aligned16(len) && aligned16(out),
+                DSA_ERR_ALIGN, "sparse_mla_decode: pointers must be 16-byte aligned");
+    if (!dsa::mla_decode_mfma_supported(H, Dv, Dr, dt == DSA_BF16))
+        DSA_REQUIRE(sizeof(float) * (static_cast<size_t>(Dv + Dr) + k) <= kGenericLdsLimit, DSA_ERR_SHAPE,
+                    "sparse_mla_decode: k=%d too large for this shape", k);
+    return DSA_OK;
+}
+
+dsa_status launch_latent(const void* q, const void* latent, const int32_t* idx, const int32_t* len,
+                         int B, int T, int H, int Dv, int Dr, int Lmax, int k, float sm_scale,
+                         dsa_dtype dt, void* out, float* lse, void* ws, hipStream_t stream) {
+    if (dsa::mla_decode_mfma_supported(H, Dv, Dr, dt == DSA_BF16))
+        return hip_status(dsa::launch_mla_decode_mfma(q, latent, idx, len, B, T, H, Lmax, k, sm_scale,
+                                                      out, lse, ws, stream),
+                          "sparse_mla_decode");
+    dsa::SparseAttnArgs a{};
+    a.q = q;
+    a.kbase = latent;
+    a.vbase = latent;
+    a.idx = idx;
+    a.len = len;
+    a.B = B; a.T = T; a.H = H; a.Dk = Dv + Dr; a.Dv = Dv; a.k = k; a.kv_rows = Lmax;
+    a.row_stride = static_cast<size_t>(Dv + Dr);
+    a.head_stride = 0;
+    a.row_stride_v = static_cast<size_t>(Dv + Dr);
+    a.head_stride_v = 0;
+    a.sm_scale = sm_scale;
+    a.bf16 = dt == DSA_BF16;
+    a.out = out;
+    a.lse = lse;
+    return hip_status(dsa::launch_sparse_attn_generic(a, stream), "sparse_mla_decode");
+}
+
+size_t latent_ws(int B, int T, int H, int Dv, int Dr, int k, dsa_dtype dt) {
+    if (dsa::mla_decode_mfma_supported(H, Dv, Dr, dt == DSA_BF16))
+        return dsa::mla_decode_workspace_bytes(B, T, H, Dv, k);
+    return 0;
+}
+
+dsa_status check_mha_args(const void* q, const void* k, const void* v, const int32_t* idx, int B,
+                          int T, int H, int Dqk, int Dv, int topk, dsa_dtype dt, const void* out) {
+    DSA_REQUIRE(q && k && v && idx && out, DSA_ERR_NULL, "sparse_mla_prefill: NULL pointer");
+    DSA_REQUIRE(dt == DSA_F32 || dt == DSA_BF16, DSA_ERR_DTYPE, "sparse_mla_prefill: bad dtype %d",
+                static_cast<int>(dt));
+    DSA_REQUIRE(B >= 1 && T >= 1 && H >= 1 && Dqk >= 1 && Dqk <= 1024 && Dv >= 1 && Dv <= 1024 &&
+                    topk >= 1,
+                DSA_ERR_SHAPE, "sparse_mla_prefill: bad shape (B=%d T=%d H=%d Dqk=%d Dv=%d k=%d)", B, T,
+                H, Dqk, Dv, topk);
+    DSA_REQUIRE(static_cast<long long>(B) * T * H <= kMaxRows, DSA_ERR_SHAPE,
+                "sparse_mla_prefill: B*T*H too large");
+    DSA_REQUIRE(aligned16(q) && aligned16(k) && aligned16(v) && aligned16(idx) && aligned16(out),
+                DSA_ERR_ALIGN, "sparse_mla_prefill: pointers must be 16-byte aligned");
+    DSA_REQUIRE(sizeof(float) * (static_cast<size_t>(Dqk) + topk) <= kGenericLdsLimit, DSA_ERR_SHAPE,
+                "sparse_mla_prefill: k=%d too large for this shape", topk);
+    return DSA_OK;
+}
+
+dsa_status launch_mha(const void* q, const void* k, const void* v, const int32_t* idx, int B, int T,
+                      int H, int Dqk, int Dv, int topk, float sm_scale, dsa_dtype dt, void* out,
+                      float* lse, void*, hipStream_t stream) {
+    dsa::SparseAttnArgs a{};
+    a.q = q;
+    a.kbase = k;
+    a.vbase = v;
+    a.idx = idx;
+    a.len = nullptr;
+    a.B = B; a.T = T; a.H = H; a.Dk = Dqk; a.Dv = Dv; a.k = topk; a.kv_rows = T;
+    a.row_stride = static_cast<size_t>(H) * Dqk;
+    a.head_stride = static_cast<size_t>(Dqk);
+    a.row_stride_v = static_cast<size_t>(H) * Dv;
+    a.head_stride_v = static_cast<size_t>(Dv);
+    a.sm_scale = sm_scale;
+    a.bf16 = dt == DSA_BF16;
+    a.out = out;
+    a.lse = lse;
+    return hip_status(dsa::launch_sparse_attn_generic(a, stream), "sparse_mla_prefill");
+}
+
+size_t mha_ws(int, int, int, int, int, int, dsa_dtype) { return 0; }
+
+}  // namespace
+
+extern "C" {
+
+const char* dsa_last_error(void) { return g_last_error.c_str(); }
+
+int dsa_version(void) { return 100; }
+
+dsa_status dsa_index_scores(const uint8_t* q_fp8, const float* q_scale, const float* w,
+                            const uint8_t* k_fp8, const float* k_scale, const int32_t* len, int B,
+                            int T, int H_I, int d_I, int Lmax, float sm_scale_I, float* scores,
+                            hipStream_t stream) {
+    dsa_status st = check_index_args(q_fp8, q_scale, w, k_fp8, k_scale, len, B, T, H_I, d_I, Lmax);
+    if (st != DSA_OK) return st;
+    DSA_REQUIRE(scores, DSA_ERR_NULL, "index scores: NULL output");
+    DSA_REQUIRE(aligned16(scores), DSA_ERR_ALIGN, "index scores: output must be 16-byte aligned");
+    dsa::IndexScoresArgs a{q_fp8, q_scale, w, k_fp8, k_scale, len, B, T, H_I, d_I, Lmax, sm_scale_I,
+                           scores, 1};
+    return hip_status(dsa::launch_index_scores(a, stream), "index scores");
+}
+
+size_t dsa_topk_workspace_bytes(int B, int T, int Lmax, int k) {
+    return dsa::topk_workspace_bytes(B, T, Lmax, k);
+}
+
+dsa_status dsa_topk(const float* scores, const int32_t* len, int B, int T, int Lmax, int k,
+                    int32_t* idx, void* ws, size_t ws_bytes, hipStream_t stream) {
+    dsa_status st = check_topk_args(scores, len, B, T, Lmax, k, idx);
+    if (st != DSA_OK) return st;
+    const size_t need = dsa::topk_workspace_bytes(B, T, Lmax, k);
+    DSA_REQUIRE(need == 0 || (ws && ws_bytes >= need), DSA_ERR_WORKSPACE,
+                "topk: workspace of %zu bytes required", need);
+    dsa::TopkArgs a{scores, len, B, T, Lmax, k, idx};
+    return hip_status(dsa::launch_topk(a, ws, stream), "topk");
+}
+
+size_t dsa_sparse_mla_decode_workspace_bytes(int B, int T, int H, int Dv, int Dr, int k, dsa_dtype dt) {
+    if (B < 1 || T < 1 || H < 1 || Dv < 1 || Dr < 0 || k < 1) return 0;
+    return latent_ws(B, T, H, Dv, Dr, k, dt);
+}
+
+dsa_status dsa_sparse_mla_decode(const void* q, const void* latent, const int32_t* idx,
+                                 const int32_t* len, int B, int T, int H, int Dv, int Dr, int Lmax,
+                                 int k, float sm_scale, dsa_dtype dt, void* out, float* lse, void* ws,
+                                 size_t ws_bytes, hipStream_t stream) {
+    dsa_status st = check_latent_args(q, latent, idx, len, B, T, H, Dv, Dr, Lmax, k, dt, out);
+    if (st != DSA_OK) return st;
+    DSA_REQUIRE(lse == nullptr || aligned16(lse), DSA_ERR_ALIGN, "sparse_mla_decode: lse alignment");
+    const size_t need = latent_ws(B, T, H, Dv, Dr, k, dt);
+    DSA_REQUIRE(need == 0 || (ws && ws_bytes >= need && aligned16(ws)), DSA_ERR_WORKSPACE,
+                "sparse_mla_decode: workspace of %zu bytes required (got %zu)", need, ws_bytes);
+    return launch_latent(q, latent, idx, len, B, T, H, Dv, Dr, Lmax, k, sm_scale, dt, out, lse, ws,
+                         stream);
+}
+
+size_t dsa_sparse_mla_prefill_workspace_bytes(int B, int T, int H, int Dqk, int Dv, int topk,
+                                              dsa_dtype dt) {
+    return mha_ws(B, T, H, Dqk, Dv, topk, dt);
+}
+
+dsa_status dsa_sparse_mla_prefill(const void* q, const void* k, const void* v, const int32_t* idx,
+                                  int B, int T, int H, int Dqk, int Dv, int topk, float sm_scale,
+                                  dsa_dtype dt, void* out, float* lse, void* ws, size_t ws_bytes,
+                                  hipStream_t stream) {
+    dsa_status st = check_mha_args(q, k, v, idx, B, T, H, Dqk, Dv, topk, dt, out);
+    if (st != DSA_OK) return st;
+    DSA_REQUIRE(lse == nullptr || aligned16(lse), DSA_ERR_ALIGN, "sparse_mla_prefill: lse alignment");
+    const size_t need = mha_ws(B, T, H, Dqk, Dv, topk, dt);
+    DSA_REQUIRE(need == 0 || (ws && ws_bytes >= need && aligned16(ws)), DSA_ERR_WORKSPACE,
+                "sparse_mla_prefill: workspace of %zu bytes required (got %zu)", need, ws_bytes);
+    return launch_mha(q, k, v, idx, B, T, H, Dqk, Dv, topk, sm_scale, dt, out, lse, ws, stream);
+}
+
+// Workspace layout of the layer step: [scores][idx][attention scratch], 256-byte aligned.
+static void layer_ws_parts(const dsa_layer_args* a, size_t* s_bytes, size_t* i_bytes, size_t* att) {
+    const size_t rows = static_cast<size_t>(a->B) * a->T;
+    *s_bytes = a->scores_out ? 0 : round_up(rows * a->Lmax * sizeof(float));
+    *i_bytes = a->idx_out ? 0 : round_up(rows * a->topk * sizeof(int32_t));
+    if (a->form == DSA_ATTN_LATENT)
+        *att = round_up(latent_ws(a->B, a->T, a->H, a->Dv, a->Dr, a->topk, a->dtype));
+    else
+        *att = round_up(mha_ws(a->B, a->T, a->H, a->Dqk, a->Dv, a->topk, a->dtype));
+}
+
+size_t dsa_layer_step_workspace_bytes(const dsa_layer_args* a) {
+    if (!a || a->B < 1 || a->T < 1 || a->Lmax < 1 || a->topk < 1) return 0;
+    size_t s, i, t;
+    layer_ws_parts(a, &s, &i, &t);
+    return s + i + t;
+}
+
+dsa_status dsa_layer_step(const dsa_layer_args* a, void* ws, size_t ws_bytes, hipStream_t stream) {
+    DSA_REQUIRE(a, DSA_ERR_NULL, "layer step: NULL args");
+    dsa_status st = check_index_args(a->q_fp8, a->q_scale, a->w, a->k_fp8, a->k_scale, a->len, a->B,
+                                     a->T, a->H_I, a->d_I, a->Lmax);
+    if (st != DSA_OK) return st;
+    DSA_REQUIRE(a->topk >= 1, DSA_ERR_SHAPE, "layer step: topk=%d", a->topk);
+    DSA_REQUIRE(a->form == DSA_ATTN_LATENT || a->form == DSA_ATTN_MHA, DSA_ERR_DTYPE,
+                "layer step: bad attention form %d", static_cast<int>(a->form));
+    if (a->form == DSA_ATTN_LATENT) {
+        st = check_latent_args(a->q, a->latent, a->len, a->len, a->B, a->T, a->H, a->Dv, a->Dr,
+                               a->Lmax, a->topk, a->dtype, a->out);
+    } else {
+        DSA_REQUIRE(a->Lmax == a->T, DSA_ERR_SHAPE,
+                    "layer step (MHA form): the chunk starts at 0, so Lmax must equal T");
+        st = check_mha_args(a->q, a->k, a->v, a->len, a->B, a->T, a->H, a->Dqk, a->Dv, a->topk,
+                            a->dtype, a->out);
+    }
+    if (st != DSA_OK) return st;
+    DSA_REQUIRE(a->lse == nullptr || aligned16(a->lse), DSA_ERR_ALIGN, "layer step: lse alignment");
+    DSA_REQUIRE(!a->idx_out || aligned16(a->idx_out), DSA_ERR_ALIGN, "layer step: idx_out alignment");
+    DSA_REQUIRE(!a->scores_out || aligned16(a->scores_out), DSA_ERR_ALIGN,
+                "layer step: scores_out alignment");
+    size_t s_bytes, i_bytes, att_bytes;
+    layer_ws_parts(a, &s_bytes, &i_bytes, &att_bytes);
+    const size_t need = s_bytes + i_bytes + att_bytes;
+    DSA_REQUIRE(need == 0 || (ws && ws_bytes >= need), DSA_ERR_WORKSPACE,
+                "layer step: workspace of %zu bytes required (got %zu)", need, ws_bytes);
+    DSA_REQUIRE(need == 0 || (reinterpret_cast<uintptr_t>(ws) & 255u) == 0, DSA_ERR_ALIGN,
+                "layer step: workspace must be 256-byte aligned");
+    uint8_t* p = static_cast<uint8_t*>(ws);
+    float* scores = a->scores_out ? a->scores_out : reinterpret_cast<float*>(p);
+    p += s_bytes;
+    int32_t* idx = a->idx_out ? a->idx_out : reinterpret_cast<int32_t*>(p);
+    p += i_bytes;
+    void* att_ws = att_bytes ? p : nullptr;
+
+    dsa::IndexScoresArgs ia{a->q_fp8, a->q_scale, a->w, a->k_fp8, a->k_scale, a->len, a->B, a->T,
+                            a->H_I, a->d_I, a->Lmax, a->sm_scale_I, scores, a->scores_out ? 1 : 0};
+    st = hip_status(dsa::launch_index_scores(ia, stream), "layer step: index scores");
+    if (st != DSA_OK) return st;
+    dsa::TopkArgs ta{scores, a->len, a->B, a->T, a->Lmax, a->topk, idx};
+    st = hip_status(dsa::launch_topk(ta, nullptr, stream), "layer step: topk");
+    if (st != DSA_OK) return st;
+    if (a->form == DSA_ATTN_LATENT)
+        return launch_latent(a->q, a->latent, idx, a->len, a->B, a->T, a->H, a->Dv, a->Dr, a->Lmax,
+                             a->topk, a->sm_scale, a->dtype, a->out, a->lse, att_ws, stream);
+    return launch_mha(a->q, a->k, a->v, idx, a->B, a->T, a->H, a->Dqk, a->Dv, a->topk, a->sm_scale,
+                      a->dtype, a->out, a->lse, att_ws, stream);
+}
+
+}  // extern "C"

@@ -1,0 +1,62 @@
+// dsa_internal.h -- host-side launch interface between the C ABI (dsa_abi.cpp) and the
+// kernel translation units.  Arguments are validated by the caller.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace dsa {
+
+struct IndexScoresArgs {
+    const uint8_t* q;
+    const float* q_scale;
+    const float* w;
+    const uint8_t* k;
+    const float* k_scale;
+    const int32_t* len;
+    int B, T, H, D, Lmax;
+    float sm_scale;
+    float* scores;
+    int fill_invisible;   // write -inf into every invisible position (else only near pos)
+};
+hipError_t launch_index_scores(const IndexScoresArgs& a, hipStream_t stream);
+
+struct TopkArgs {
+    const float* scores;
+    const int32_t* len;
+    int B, T, Lmax, k;
+    int32_t* idx;
+};
+size_t topk_workspace_bytes(int B, int T, int Lmax, int k);
+hipError_t launch_topk(const TopkArgs& a, void* ws, hipStream_t stream);
+
+// Sparse attention over gathered rows.  Keys of row (b,t) for head h are read at
+//   kbase + (b * kv_rows + s) * row_stride + h * head_stride   (Dk values)
+// and values at
+//   vbase + (b * kv_rows + s) * row_stride_v + h * head_stride_v (Dv values).
+struct SparseAttnArgs {
+    const void* q;          // [B,T,H,Dk]
+    const void* kbase;
+    const void* vbase;
+    const int32_t* idx;     // [B,T,k]
+    const int32_t* len;     // [B] (latent form) or NULL (MHA chunk from 0: pos = t)
+    int B, T, H, Dk, Dv, k, kv_rows;
+    size_t row_stride, head_stride, row_stride_v, head_stride_v;   // in elements
+    float sm_scale;
+    int bf16;               // element type: 1 bf16, 0 f32
+    void* out;              // [B,T,H,Dv]
+    float* lse;             // [B,T,H] or NULL
+};
+hipError_t launch_sparse_attn_generic(const SparseAttnArgs& a, hipStream_t stream);
+
+// Matrix-core path of the absorbed latent form (bf16, Dv = 512, Dr = 64, H % 16 == 0,
+// H <= 128).
+bool mla_decode_mfma_supported(int H, int Dv, int Dr, int bf16);
+size_t mla_decode_workspace_bytes(int B, int T, int H, int Dv, int k);
+hipError_t launch_mla_decode_mfma(const void* q, const void* latent, const int32_t* idx,
+                                  const int32_t* len, int B, int T, int H, int Lmax, int k,
+                                  float sm_scale, void* out, float* lse, void* ws,
+                                  hipStream_t stream);
+
+}  // namespace dsa

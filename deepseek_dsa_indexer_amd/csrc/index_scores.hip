@@ -1,0 +1,219 @@
+// index_scores.hip -- lightning-indexer scores on gfx950 matrix cores.
+//
+// Computes, for every query row (b,t) and cache position s < Lmax,
+//   I[b,t,s] = k_scale[b,s] * sum_h w'[b,t,h] * max(0, q[b,t,h,:] . k[b,s,:]),
+//   w' = w * q_scale * sm_scale,
+// with -inf where s > pos(b,t) = len[b] - T + t.  The weight fold follows the
+// Indexer.forward excerpt ("DeepSeek-V3.2-Exp - Split indexer heads"); the per-head
+// ReLU and weighted head sum follow the score box of "dsa-indexer.excalidraw"; the
+// mask follows full(-inf).triu_(1) of the "Causal mask" page.
+//
+// Storage and arithmetic.  q and the key cache stay FP8 (e4m3fn) in memory, so the
+// stream is 128 + 4 bytes per key.  In registers every FP8 byte is widened to bf16
+// (exact: e4m3fn values are a subset of bf16) and the 128-wide products run on the
+// bf16 MFMA, whose products and fp32 sums are exact to fp32 rounding.  The FP8 MFMA
+// was measured on gfx950 to align its in-instruction products to about 13 significant
+// bits (error up to 1.6e-4 of sum |q_d k_d|), which shows up as 1e-3-level relative
+// errors on scores whose head terms cancel.
+//
+// Mapping.  One wave owns QR query rows and streams 64-key chunks of the key cache.
+// The 64 heads of each query row stay in registers as A operands (4 head tiles x 4
+// K-steps of 32).  A chunk is four 16-key B tiles read with 16-byte loads: lane l takes
+// the 32 contiguous bytes [32 g, 32 g + 32) of key (l % 16), g = l / 16, and K-step j
+// uses bytes [8 j, 8 j + 8) of them (q uses the same byte -> K-slot assignment, so the
+// four K-steps cover each of the 128 dims once).  Each MFMA leaves lane l with 4
+// heads x 1 key; ReLU and the head weights are applied in registers and three
+// cross-lane exchanges finish the head sum, so lane l ends with the score of key
+// (chunk + l): one coalesced 256-byte store per row and chunk.  Heads beyond H_I and
+// columns beyond d_I are zero (weight 0), which covers the small test shapes.
+#include "dsa_device.h"
+#include "dsa_internal.h"
+
+namespace dsa {
+
+namespace {
+
+constexpr int kThreads = 256;       // 4 waves
+constexpr int kChunk = 64;          // keys per wave iteration (4 MFMA column tiles)
+
+typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ v8i load32(const uint8_t* p, bool ok) {
+    // 32 contiguous bytes (two 16-byte loads), or zeros when !ok
+    v8i r = {0, 0, 0, 0, 0, 0, 0, 0};
+    if (ok) {
+        const uint4* s = reinterpret_cast<const uint4*>(p);
+        uint4 a = s[0];
+        uint4 b = s[1];
+        r[0] = a.x; r[1] = a.y; r[2] = a.z; r[3] = a.w;
+        r[4] = b.x; r[5] = b.y; r[6] = b.z; r[7] = b.w;
+    }
+    return r;
+}
+
+// 8 FP8 bytes (two dwords) -> 8 bf16, exactly.
+__device__ __forceinline__ v8bf fp8x8_to_bf16(int d0, int d1) {
+    const v2bf a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(d0, 1.0f, false);
+    const v2bf b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(d0, 1.0f, true);
+    const v2bf c = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(d1, 1.0f, false);
+    const v2bf d = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(d1, 1.0f, true);
+    return v8bf{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
+}
+
+// Lane (g, n) holds s[c] = partial score (heads of group g) of key 16c + n.  Returns,
+// in every lane, the full head sum for key 16g + n, i.e. for chunk offset == lane.
+__device__ __forceinline__ float head_sum_transpose(const float s[4], int g) {
+    const bool lo = g < 2;
+    float send0 = lo ? s[2] : s[0];
+    float send1 = lo ? s[3] : s[1];
+    float r0 = __shfl_xor(send0, 32, kWave);
+    float r1 = __shfl_xor(send1, 32, kWave);
+    float a0 = (lo ? s[0] : s[2]) + r0;     // tile 0 (g < 2) or tile 2
+    float a1 = (lo ? s[1] : s[3]) + r1;     // tile 1 (g < 2) or tile 3
+    const bool odd = g & 1;
+    float send = odd ? a0 : a1;
+    float r = __shfl_xor(send, 16, kWave);
+    return (odd ? a1 : a0) + r;
+}
+
+template <int D, int QR, int CHUNKS>
+__global__ __launch_bounds__(kThreads)
+void index_scores_kernel(const uint8_t* __restrict__ q, const float* __restrict__ q_scale,
+                         const float* __restrict__ w, const uint8_t* __restrict__ k,
+                         const float* __restrict__ k_scale, const int32_t* __restrict__ len,
+                         int T, int H, int Lmax, float sm_scale, float* __restrict__ scores,
+                         int fill_invisible)
+{
+    constexpr int kKeysPerBlock = kThreads / kWave * kChunk * CHUNKS;
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wave = threadIdx.x / kWave;
+    const int g = lane >> 4;
+    const int n = lane & 15;
+
+    const int row_groups = (T + QR - 1) / QR;
+    const int b = blockIdx.x / row_groups;
+    const int t0 = (blockIdx.x - b * row_groups) * QR;
+    const int nrows = min(QR, T - t0);
+    const int pos0 = min(len[b], Lmax) - T + t0;   // position of row t0
+    const int pos_hi = pos0 + nrows - 1;
+
+    const int key_blk = blockIdx.y * kKeysPerBlock;
+    float* out = scores + (static_cast<size_t>(b) * T + t0) * Lmax;
+
+    if (key_blk > pos_hi) {                     // the whole block is masked
+        if (fill_invisible) {
+            for (int key = key_blk + threadIdx.x; key < min(key_blk + kKeysPerBlock, Lmax); key += kThreads)
+                for (int r = 0; r < nrows; ++r) out[static_cast<size_t>(r) * Lmax + key] = -INFINITY;
+        }
+        return;
+    }
+
+    // ---- issue the key-chunk loads of this wave first
+    const uint8_t* kb_ptr = k + static_cast<size_t>(b) * Lmax * D;
+    const float* ks_ptr = k_scale + static_cast<size_t>(b) * Lmax;
+    v8i kt[CHUNKS][4];
+    float ks[CHUNKS];
+#pragma unroll
+    for (int c = 0; c < CHUNKS; ++c) {
+        const int kb = key_blk + (c * (kThreads / kWave) + wave) * kChunk;
+        const bool live = kb <= pos_hi;
+#pragma unroll
+        for (int tile = 0; tile < 4; ++tile) {
+            const int key = kb + 16 * tile + n;
+            kt[c][tile] = load32(kb_ptr + static_cast<size_t>(key) * D + g * 32,
+                                 live && key < Lmax && g * 32 < D);
+        }
+        const int key = kb + lane;
+        ks[c] = (live && key < Lmax) ? ks_ptr[key] : 0.f;
+    }
+
+    // ---- query operands (bf16) and folded head weights, kept in registers
+    v8bf qa[QR][4][4];
+    float wf[QR][4][4];
+#pragma unroll
+    for (int r = 0; r < QR; ++r) {
+        const size_t qrow = static_cast<size_t>(b) * T + t0 + r;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int head = 16 * j + n;
+            const bool ok = r < nrows && head < H && g * 32 < D;
+            const v8i raw = load32(q + (qrow * H + head) * D + g * 32, ok);
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk) qa[r][j][kk] = fp8x8_to_bf16(raw[2 * kk], raw[2 * kk + 1]);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int hh = 16 * j + 4 * g + i;
+                float v = 0.f;
+                if (r < nrows && hh < H) v = w[qrow * H + hh] * q_scale[qrow * H + hh] * sm_scale;
+                wf[r][j][i] = v;
+            }
+        }
+    }
+
+#pragma unroll
+    for (int c = 0; c < CHUNKS; ++c) {
+        const int kb = key_blk + (c * (kThreads / kWave) + wave) * kChunk;
+        const int key = kb + lane;
+        if (kb > pos_hi) {
+            if (fill_invisible && key < Lmax)
+                for (int r = 0; r < nrows; ++r) out[static_cast<size_t>(r) * Lmax + key] = -INFINITY;
+            continue;
+        }
+        float s[QR][4];
+#pragma unroll
+        for (int tile = 0; tile < 4; ++tile) {
+            v8bf kbf[4];
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk)
+                kbf[kk] = fp8x8_to_bf16(kt[c][tile][2 * kk], kt[c][tile][2 * kk + 1]);
+#pragma unroll
+            for (int r = 0; r < QR; ++r) {
+                float acc = 0.f;
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    v4f d = v4f{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                    for (int kk = 0; kk < 4; ++kk) d = mfma_bf16_16x16x32(qa[r][j][kk], kbf[kk], d);
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) acc += wf[r][j][i] * fmaxf(d[i], 0.f);
+                }
+                s[r][tile] = acc;
+            }
+        }
+#pragma unroll
+        for (int r = 0; r < QR; ++r) {
+            const float total = head_sum_transpose(s[r], g);
+            if (r < nrows && key < Lmax)
+                out[static_cast<size_t>(r) * Lmax + key] = (key <= pos0 + r) ? total * ks[c] : -INFINITY;
+        }
+    }
+}
+
+template <int D, int QR, int CHUNKS>
+hipError_t launch_d(const IndexScoresArgs& a, hipStream_t stream) {
+    constexpr int kKeysPerBlock = kThreads / kWave * kChunk * CHUNKS;
+    const int row_groups = (a.T + QR - 1) / QR;
+    dim3 grid(a.B * row_groups, (a.Lmax + kKeysPerBlock - 1) / kKeysPerBlock);
+    hipLaunchKernelGGL((index_scores_kernel<D, QR, CHUNKS>), grid, dim3(kThreads), 0, stream,
+                       a.q, a.q_scale, a.w, a.k, a.k_scale, a.len, a.T, a.H, a.Lmax, a.sm_scale,
+                       a.scores, a.fill_invisible);
+    return hipGetLastError();
+}
+
+template <int D>
+hipError_t launch_rows(const IndexScoresArgs& a, hipStream_t stream) {
+    if (a.T >= 2) return launch_d<D, 2, 1>(a, stream);
+    return launch_d<D, 1, 2>(a, stream);
+}
+
+}  // namespace
+
+hipError_t launch_index_scores(const IndexScoresArgs& a, hipStream_t stream) {
+    switch (a.D) {
+    case 32: return launch_rows<32>(a, stream);
+    case 64: return launch_rows<64>(a, stream);
+    default: return launch_rows<128>(a, stream);
+    }
+}
+
+}  // namespace dsa

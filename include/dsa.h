@@ -1,0 +1,174 @@
+/*
+ * dsa.h -- C ABI of the MI355X (gfx950) DeepSeek Sparse Attention layer-step library
+ * (libdsa_amd.so).
+ *
+ * One DSA layer step, as the pages describe it:
+ *   1. lightning-indexer scores     ("DeepSeek-V3.2-Exp - Split indexer heads", Indexer.forward
+ *                                     excerpt: weight fold, fp8_index; "dsa-indexer.excalidraw",
+ *                                     score box I(t,s) = sum_j w_j ReLU(q_j . k_s));
+ *   2. causal mask                   ("DeepSeek-V3.2-Exp - Causal mask", full(-inf).triu_(1));
+ *   3. per-row top-k                 (Indexer.forward excerpt, topk(min(index_topk, end_pos));
+ *                                     excalidraw "top-k selector, k = 2048");
+ *   4. sparse attention over the k selected positions, either in the absorbed latent
+ *      (MQA) form of the excalidraw diagram ("core attention, MQA mode ... each latent is
+ *      key and value") or in the MHA prefill form of the MLA prefill excerpt ("Causal
+ *      mask" page, Multi-head latent attention, prefill).
+ *
+ * Conventions shared by every entry point
+ *   - All tensor pointers are DEVICE pointers to dense row-major arrays, 16-byte aligned.
+ *   - len[b] is the number of valid cache positions of sequence b.  The T query rows of
+ *     a call are the LAST T positions: pos(b,t) = len[b] - T + t.  Cache position s is
+ *     visible to row (b,t) iff 0 <= s <= pos(b,t).  Preconditions checked on the device
+ *     side only by construction (the host cannot read device memory without a sync):
+ *     T <= len[b] <= Lmax.
+ *   - Every call only enqueues work on `stream` and returns; outputs are valid once the
+ *     caller synchronises the stream.  The library never allocates, frees or
+ *     synchronises; scratch memory comes from the caller as (ws, ws_bytes), sized by
+ *     the matching *_workspace_bytes() query.  Inputs must stay alive until the stream
+ *     reaches the call; outputs must not alias inputs or the workspace.
+ *   - Errors are reported by the returned status; nothing aborts.  dsa_last_error()
+ *     returns a thread-local description of the last non-OK status.  Arguments are
+ *     validated before anything is enqueued; DSA_ERR_HIP means a launch failed.
+ *   - FP8 is OCP e4m3fn (max 448), one fp32 scale per row of d_I values (128-wide
+ *     blocks at the V3.2 sizes).  bf16 is IEEE binary32 truncated to 16 bits.
+ */
+#ifndef DSA_H
+#define DSA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    DSA_OK = 0,
+    DSA_ERR_NULL = 1,       /* a required pointer is NULL                          */
+    DSA_ERR_SHAPE = 2,      /* a size is out of the supported range                */
+    DSA_ERR_DTYPE = 3,      /* dtype / form / shape combination not supported      */
+    DSA_ERR_ALIGN = 4,      /* a pointer is not 16-byte aligned                    */
+    DSA_ERR_WORKSPACE = 5,  /* ws is NULL or ws_bytes is below the queried size    */
+    DSA_ERR_HIP = 6         /* a HIP launch or runtime call failed                 */
+} dsa_status;
+
+typedef enum { DSA_F32 = 0, DSA_BF16 = 1 } dsa_dtype;           /* attention element type */
+typedef enum { DSA_ATTN_LATENT = 0, DSA_ATTN_MHA = 1 } dsa_attn_form;
+
+/* Thread-local text for the last non-OK status of this thread ("" if none). */
+const char* dsa_last_error(void);
+/* Library version, major * 10000 + minor * 100 + patch. */
+int dsa_version(void);
+
+/*
+ * dsa_index_scores -- lightning-indexer scores with the causal mask applied.
+ *   scores[b,t,s] = k_scale[b,s] * sum_h (w[b,t,h] * q_scale[b,t,h] * sm_scale_I)
+ *                                     * max(0, sum_d q[b,t,h,d] * k[b,s,d])
+ *   for visible s, and -inf for every other s < Lmax.
+ * ("Split indexer heads": weights = weights_proj(x) * n_heads^-0.5 is the caller's `w`;
+ *  the library folds q_scale and softmax_scale as the excerpt does; the ReLU is the one
+ *  in the excalidraw score box.)
+ *   q_fp8   [B,T,H_I,d_I] u8 e4m3fn     q_scale [B,T,H_I] f32     w [B,T,H_I] f32
+ *   k_fp8   [B,Lmax,d_I]  u8 e4m3fn     k_scale [B,Lmax] f32      len [B] i32
+ *   scores  [B,T,Lmax] f32 (output)
+ * Supported: 1 <= H_I <= 64, d_I in {32, 64, 128}, 1 <= T <= Lmax.
+ */
+dsa_status dsa_index_scores(const uint8_t* q_fp8, const float* q_scale, const float* w,
+                            const uint8_t* k_fp8, const float* k_scale, const int32_t* len,
+                            int B, int T, int H_I, int d_I, int Lmax, float sm_scale_I,
+                            float* scores, hipStream_t stream);
+
+/*
+ * dsa_topk -- per query row, the positions of the min(k, pos+1) largest visible scores.
+ * (Indexer.forward: index_score.topk(min(index_topk, end_pos)); unused slots hold -1 as
+ *  the DeepSeek-V4 mask visualiser's warm-up sentinel does.)
+ *   scores [B,T,Lmax] f32 (only positions 0..pos(b,t) are read)   len [B] i32
+ *   idx    [B,T,k] i32 (output): the selected positions in ascending order, then -1.
+ * Equal scores at the threshold are resolved in favour of the smaller position, so the
+ * result is deterministic.  Scores must not be NaN.  Supported: 1 <= k, T <= Lmax.
+ */
+size_t dsa_topk_workspace_bytes(int B, int T, int Lmax, int k);
+dsa_status dsa_topk(const float* scores, const int32_t* len, int B, int T, int Lmax, int k,
+                    int32_t* idx, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * dsa_sparse_mla_decode -- absorbed (MQA) sparse attention over selected latent rows.
+ * (excalidraw "core attention, MQA mode: q (128 heads) over the 2048 selected latents,
+ *  each latent is key and value"; softmax and value mix as in the MLA prefill excerpt.)
+ *   q      [B,T,H,Dv+Dr]   (absorbed query: Dv latent columns, then Dr rope columns)
+ *   latent [B,Lmax,Dv+Dr]  (cache row: latent Dv, then rope Dr)
+ *   idx    [B,T,k] i32     (slots < 0 and positions > pos(b,t) are ignored)
+ *   out    [B,T,H,Dv]      (same dtype as q), lse [B,T,H] f32 natural-log sum-exp of the
+ *                          scaled logits, or NULL.
+ *   logit_j = sm_scale * q[b,t,h,:] . latent[b,s_j,:]; out = softmax(logit) @ latent[.,:Dv]
+ * A row with no usable slot gets out = 0 and lse = -inf.  Entries of idx must be unique
+ * per row.  Any H, Dv, Dr with Dv+Dr <= 1024 and dtype F32 or BF16; the bf16 shape
+ * H % 16 == 0, H <= 128, Dv = 512, Dr = 64 runs on the matrix-core path.
+ */
+size_t dsa_sparse_mla_decode_workspace_bytes(int B, int T, int H, int Dv, int Dr, int k,
+                                             dsa_dtype dt);
+dsa_status dsa_sparse_mla_decode(const void* q, const void* latent, const int32_t* idx,
+                                 const int32_t* len, int B, int T, int H, int Dv, int Dr,
+                                 int Lmax, int k, float sm_scale, dsa_dtype dt, void* out,
+                                 float* lse, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * dsa_sparse_mla_prefill -- MHA-form sparse attention over a chunk that starts at
+ * position 0 (keys and values are the chunk's own T positions, per head).
+ * (MLA prefill excerpt: q = [q_nope | q_pe], k = [k_nope | k_pe], scores * softmax_scale
+ *  + index_mask (0 at the top-k positions, -inf elsewhere) + causal mask, softmax,
+ *  einsum with v.)
+ *   q, k [B,T,H,Dqk]   v [B,T,H,Dv]   idx [B,T,topk] i32 (slots < 0 or > t are ignored)
+ *   out  [B,T,H,Dv] (same dtype), lse [B,T,H] f32 or NULL.
+ * Supported: dtype F32 or BF16, Dqk <= 1024, Dv <= 1024; the bf16 shape Dqk = 192,
+ * Dv = 128 runs on the matrix-core path.
+ */
+size_t dsa_sparse_mla_prefill_workspace_bytes(int B, int T, int H, int Dqk, int Dv, int topk,
+                                              dsa_dtype dt);
+dsa_status dsa_sparse_mla_prefill(const void* q, const void* k, const void* v,
+                                  const int32_t* idx, int B, int T, int H, int Dqk, int Dv,
+                                  int topk, float sm_scale, dsa_dtype dt, void* out, float* lse,
+                                  void* ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * dsa_layer_step -- the whole step: index scores -> causal mask -> top-k -> sparse
+ * attention, in the latent form (len[] per sequence, T rows at the end) or the MHA
+ * prefill form (len[b] = T for every b, Lmax = T).
+ */
+typedef struct dsa_layer_args {
+    /* indexer */
+    const uint8_t* q_fp8;     /* [B,T,H_I,d_I] e4m3fn                                */
+    const float* q_scale;     /* [B,T,H_I]                                           */
+    const float* w;           /* [B,T,H_I]                                           */
+    const uint8_t* k_fp8;     /* [B,Lmax,d_I] e4m3fn                                 */
+    const float* k_scale;     /* [B,Lmax]                                            */
+    const int32_t* len;       /* [B]                                                 */
+    int B, T, H_I, d_I, Lmax, topk;
+    float sm_scale_I;
+    /* attention */
+    dsa_attn_form form;
+    dsa_dtype dtype;
+    const void* q;            /* latent: [B,T,H,Dv+Dr]    MHA: [B,T,H,Dqk]           */
+    const void* latent;       /* latent: [B,Lmax,Dv+Dr]   MHA: unused                */
+    const void* k;            /* MHA: [B,T,H,Dqk]         latent: unused             */
+    const void* v;            /* MHA: [B,T,H,Dv]          latent: unused             */
+    int H, Dv, Dr, Dqk;
+    float sm_scale;
+    void* out;                /* [B,T,H,Dv]                                          */
+    float* lse;               /* [B,T,H] or NULL                                     */
+    /* optional intermediate outputs (NULL: kept in the workspace) */
+    int32_t* idx_out;         /* [B,T,topk]                                          */
+    float* scores_out;        /* [B,T,Lmax]; when NULL, scores of invisible positions
+                                 are not materialised                               */
+} dsa_layer_args;
+
+size_t dsa_layer_step_workspace_bytes(const dsa_layer_args* a);
+dsa_status dsa_layer_step(const dsa_layer_args* a, void* ws, size_t ws_bytes,
+                          hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* DSA_H */

@@ -1,0 +1,92 @@
+"""Comparison rules between the GPU library and the CPU oracle.
+
+  * index scores: |g - o| <= 1e-3 * max(|o|, 1e-3 * max_row |o|) at visible positions
+    (the row floor guards cancellation: head weights are signed), identical -inf
+    pattern elsewhere (only where the library materialises it);
+  * top-k on identical scores: identical output (both resolve equal scores towards the
+    smaller position and list positions in ascending order);
+  * top-k after scoring on both sides: same cardinality min(k, n), unique, visible,
+    ascending, -1 tail; positions in the symmetric difference of the two sets must
+    have oracle scores within 1e-3 (relative, same row floor) of the oracle's k-th
+    largest score tau;
+  * attention outputs: |g - o| <= 2e-2 (bf16 inputs/outputs) or 1e-4 (fp32), lse
+    within 1e-3 (bf16) or 1e-5 (fp32) absolute, compared on the same indices.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+SCORE_RTOL = 1e-3
+ATTN_ATOL = {"bf16": 2e-2, "f32": 1e-4}
+LSE_ATOL = {"bf16": 1e-3, "f32": 1e-5}
+
+
+def check_scores(gpu: np.ndarray, orc: np.ndarray, lens, T: int, full_mask: bool = True, rows=None):
+    """gpu/orc: [R, Lmax] rows (b,t) given by `rows` (list of (b, t)) or all of [B,T,Lmax]."""
+    if rows is None:
+        B = gpu.shape[0]
+        rows = [(b, t) for b in range(B) for t in range(T)]
+        gpu = gpu.reshape(B * T, -1)
+        orc = orc.reshape(B * T, -1)
+    worst = 0.0
+    for r, (b, t) in enumerate(rows):
+        pos = int(lens[b]) - T + t
+        g, o = gpu[r, : pos + 1].astype(np.float64), orc[r, : pos + 1].astype(np.float64)
+        assert np.all(np.isfinite(g)), f"row {(b, t)}: non-finite GPU score at a visible position"
+        floor = 1e-3 * np.abs(o).max()
+        tol = SCORE_RTOL * np.maximum(np.abs(o), floor)
+        err = np.abs(g - o)
+        bad = np.flatnonzero(err > tol)
+        assert bad.size == 0, (f"row {(b, t)}: {bad.size} scores off, first at s={bad[0]}: "
+                               f"gpu={g[bad[0]]} oracle={o[bad[0]]}")
+        worst = max(worst, float((err / np.maximum(tol, 1e-300)).max()) * SCORE_RTOL)
+        if full_mask:
+            assert np.all(np.isneginf(gpu[r, pos + 1:])), f"row {(b, t)}: invisible score not -inf"
+    return worst
+
+
+def check_topk(gpu_idx: np.ndarray, orc_scores: np.ndarray, orc_idx: np.ndarray, lens, T: int,
+               k: int, rows=None):
+    """gpu_idx/orc_idx: [R, k]; orc_scores: [R, Lmax]; rows: list of (b, t)."""
+    if rows is None:
+        B = gpu_idx.shape[0]
+        rows = [(b, t) for b in range(B) for t in range(T)]
+        gpu_idx = gpu_idx.reshape(B * T, k)
+        orc_idx = orc_idx.reshape(B * T, k)
+        orc_scores = orc_scores.reshape(B * T, -1)
+    swaps = 0
+    for r, (b, t) in enumerate(rows):
+        n = int(lens[b]) - T + t + 1
+        kk = min(k, n)
+        g = gpu_idx[r]
+        assert np.all(g[kk:] == -1), f"row {(b, t)}: tail is not -1"
+        gv = g[:kk]
+        assert np.all(gv >= 0) and np.all(gv < n), f"row {(b, t)}: index out of the visible range"
+        assert np.all(np.diff(gv) > 0), f"row {(b, t)}: not strictly ascending / duplicates"
+        ov = orc_idx[r, :kk]
+        diff = np.setxor1d(gv, ov)
+        if diff.size:
+            sc = orc_scores[r, :n].astype(np.float64)
+            tau = np.sort(sc)[::-1][kk - 1]
+            floor = 1e-3 * np.abs(sc).max()
+            tol = SCORE_RTOL * max(abs(tau), floor)
+            off = diff[np.abs(sc[diff] - tau) > tol]
+            assert off.size == 0, (f"row {(b, t)}: selection differs beyond the tie band at "
+                                   f"{off[:5]} (scores {sc[off[:5]]}, tau {tau})")
+            swaps += diff.size // 2
+    return swaps
+
+
+def check_attention(out_g, lse_g, out_o, lse_o, dtype: str):
+    out_g = np.asarray(out_g, np.float64)
+    err = np.abs(out_g - out_o)
+    assert np.all(np.isfinite(out_g)), "non-finite attention output"
+    i = np.unravel_index(np.argmax(err), err.shape)
+    assert err.max() <= ATTN_ATOL[dtype], f"attention max abs err {err.max()} at {i}"
+    if lse_g is not None:
+        lerr = np.abs(np.asarray(lse_g, np.float64) - lse_o)
+        fin = np.isfinite(lse_o)
+        assert np.array_equal(fin, np.isfinite(lse_g)), "lse -inf pattern differs"
+        if fin.any():
+            assert lerr[fin].max() <= LSE_ATOL[dtype], f"lse max abs err {lerr[fin].max()}"
+    return float(err.max())

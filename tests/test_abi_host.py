@@ -1,0 +1,94 @@
+"""The C-ABI library on the host (no GPU needed): it loads, it exports every entry point
+that include/dsa.h declares, and its argument validation rejects bad calls before any
+work is enqueued (these paths return before touching the device)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from deepseek_dsa_indexer_amd import _native as N
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared():
+    src = open(os.path.join(ROOT, "include", "dsa.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(dsa_[a-z_0-9]+)\s*\(", src)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(N.library_path()):
+        pytest.fail("libdsa_amd.so is not built (python -m deepseek_dsa_indexer_amd.build)")
+    return N.load()
+
+
+def test_exports_match_header(lib):
+    declared = _declared()
+    assert sorted(N.EXPORTED) == declared
+    for name in declared:
+        assert hasattr(lib, name), name
+    assert lib.dsa_version() >= 100
+
+
+def _fake(addr=0x10000):
+    return ctypes.c_void_p(addr)
+
+
+def test_index_scores_validation(lib):
+    p = _fake()
+    st = lib.dsa_index_scores(None, p, p, p, p, p, 1, 1, 64, 128, 16, 1.0, p, None)
+    assert st == 1 and b"NULL" in lib.dsa_last_error()
+    assert lib.dsa_index_scores(p, p, p, p, p, p, 1, 1, 65, 128, 16, 1.0, p, None) == 2
+    assert lib.dsa_index_scores(p, p, p, p, p, p, 1, 1, 64, 96, 16, 1.0, p, None) == 2
+    assert lib.dsa_index_scores(p, p, p, p, p, p, 1, 17, 64, 128, 16, 1.0, p, None) == 2
+    assert lib.dsa_index_scores(p, p, p, p, p, p, 0, 1, 64, 128, 16, 1.0, p, None) == 2
+    q = _fake(0x10004)
+    assert lib.dsa_index_scores(q, p, p, p, p, p, 1, 1, 64, 128, 16, 1.0, p, None) == 4
+
+
+def test_topk_validation(lib):
+    p = _fake()
+    assert lib.dsa_topk(p, p, 1, 1, 16, 0, p, None, 0, None) == 2
+    assert lib.dsa_topk(None, p, 1, 1, 16, 4, p, None, 0, None) == 1
+    assert lib.dsa_topk(p, p, 1, 2, 1, 4, p, None, 0, None) == 2
+
+
+def test_attention_validation_and_workspace(lib):
+    p = _fake()
+    # the matrix-core shape needs a workspace once the rows are split
+    need = lib.dsa_sparse_mla_decode_workspace_bytes(2, 1, 128, 512, 64, 2048, N.DSA_BF16)
+    assert need > 0
+    st = lib.dsa_sparse_mla_decode(p, p, p, p, 2, 1, 128, 512, 64, 4096, 2048, 0.1, N.DSA_BF16,
+                                   p, None, None, 0, None)
+    assert st == 5 and b"workspace" in lib.dsa_last_error()
+    st = lib.dsa_sparse_mla_decode(p, p, p, p, 2, 1, 128, 512, 64, 4096, 2048, 0.1, 7, p, None,
+                                   None, 0, None)
+    assert st == 3
+    assert lib.dsa_sparse_mla_decode_workspace_bytes(256, 1, 128, 512, 64, 2048, N.DSA_BF16) == 0
+    # generic path: logits of all k slots must fit in LDS
+    st = lib.dsa_sparse_mla_prefill(p, p, p, p, 1, 8, 2, 192, 128, 1 << 15, 0.1, N.DSA_BF16, p,
+                                    None, None, 0, None)
+    assert st == 2
+
+
+def test_layer_step_validation(lib):
+    a = N.LayerArgs()
+    assert lib.dsa_layer_step(None, None, 0, None) == 1
+    assert lib.dsa_layer_step(ctypes.byref(a), None, 0, None) == 1
+    p = 0x10000
+    a.q_fp8 = a.q_scale = a.w = a.k_fp8 = a.k_scale = a.len = p
+    a.B, a.T, a.H_I, a.d_I, a.Lmax, a.topk = 32, 1, 64, 128, 8192, 2048
+    a.form, a.dtype = N.DSA_ATTN_LATENT, N.DSA_BF16
+    a.q = a.latent = a.out = p
+    a.H, a.Dv, a.Dr = 128, 512, 64
+    need = lib.dsa_layer_step_workspace_bytes(ctypes.byref(a))
+    assert need >= 32 * 8192 * 4 + 32 * 2048 * 4
+    assert lib.dsa_layer_step(ctypes.byref(a), None, 0, None) == 5
+    assert lib.dsa_layer_step(ctypes.byref(a), ctypes.c_void_p(p + 16), need, None) == 4
+    a.form = N.DSA_ATTN_MHA
+    a.k = a.v = p
+    a.Dqk = 192
+    assert lib.dsa_layer_step(ctypes.byref(a), ctypes.c_void_p(p), need, None) == 2  # Lmax != T

@@ -1,0 +1,267 @@
+"""GPU library vs CPU oracle, element by element, on seeded inputs (needs an MI355X).
+
+Sizes are chosen so that the oracle finishes in seconds while the kernels still run
+several tiles, ragged tails, padded heads/columns, causal rows and short rows."""
+import dataclasses
+import sys
+import zlib
+
+import numpy as np
+import pytest
+import torch
+
+import dsa_synth as S
+from parity import check_attention, check_scores, check_topk
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def dsa():
+    if not torch.cuda.is_available():
+        pytest.fail("no GPU visible")
+    import deepseek_dsa_indexer_amd as D
+    D.load()
+    return D
+
+
+def _small(base: str, **kw) -> S.Config:
+    return dataclasses.replace(S.CONFIGS[base], **kw)
+
+
+def _dev(case):
+    return S.to_device(case, "cuda")
+
+
+def _np_out(t):
+    if t.dtype == torch.bfloat16:
+        return t.float().cpu().numpy()
+    return t.cpu().numpy()
+
+
+def _say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+# ----------------------------------------------------------------------------- index scores
+
+INDEX_CASES = [
+    ("tiny", _small("tiny")),
+    ("decode_ragged_small", _small("decode_ragged", name="drs", B=3, Lmax=1100,
+                                   lens="ragged:37:1100", seed=105)),
+    ("decode_normal_small", _small("decode_v32", name="dns", B=2, Lmax=777, seed=102)),
+    ("prefill_small", _small("prefill_chunk", name="ps", T=70, Lmax=300, lens="ragged:70:300",
+                             B=2, H_I=48, D_I=64, seed=104)),
+]
+
+
+@pytest.mark.parametrize("name,cfg", INDEX_CASES, ids=[c[0] for c in INDEX_CASES])
+def test_index_scores(dsa, orc, name, cfg):
+    _say(f"[index_scores] {name}")
+    c = S.make_case(cfg)
+    d = _dev(c)
+    got = dsa.index_scores(d["q_i"], d["q_scale"], d["w"], d["k_i"], d["k_scale"], d["lens"],
+                           cfg.sm_scale_i)
+    torch.cuda.synchronize()
+    ref = orc.index_scores(c["q_i"], c["q_scale"], c["w"], c["k_i"], c["k_scale"], c["lens"],
+                           cfg.sm_scale_i)
+    check_scores(got.cpu().numpy(), ref, c["lens"], cfg.T)
+
+
+# ----------------------------------------------------------------------------- top-k
+
+def _scores_case(kind, B, T, Lmax, lens, seed):
+    rng = np.random.default_rng(seed)
+    if kind == "normal":
+        sc = rng.standard_normal((B, T, Lmax)).astype(np.float32)
+    elif kind == "ties":
+        sc = rng.integers(-20, 21, size=(B, T, Lmax)).astype(np.float32) * 0.25
+    elif kind == "heavy":
+        x = rng.standard_t(3, size=(B, T, Lmax)).astype(np.float32)
+        # keep 8 mantissa bits so that exact ties appear in the tail
+        sc = (x.view(np.uint32) & np.uint32(0xFFFF8000)).view(np.float32)
+    else:   # signed zeros and a constant row
+        sc = np.where(rng.random((B, T, Lmax)) < 0.5, np.float32(0.0), np.float32(-0.0))
+    return sc, np.asarray(lens, np.int32)
+
+
+TOPK_CASES = [
+    ("normal_decode", "normal", 4, 1, 8192, [8192, 3000, 2049, 100], 2048),
+    ("ties_decode", "ties", 3, 1, 5000, [5000, 4097, 2500], 2048),
+    ("heavy_long", "heavy", 2, 1, 40000, [40000, 17001], 2048),
+    ("zeros", "zeros", 2, 1, 3000, [3000, 2100], 2048),
+    ("causal_rows", "normal", 2, 37, 1001, [1001, 37], 64),
+    ("k1", "ties", 2, 3, 500, [500, 300], 1),
+    ("k_gt_n", "normal", 2, 2, 64, [64, 10], 100),
+]
+
+
+@pytest.mark.parametrize("name,kind,B,T,Lmax,lens,k", TOPK_CASES, ids=[c[0] for c in TOPK_CASES])
+def test_topk_exact(dsa, orc, name, kind, B, T, Lmax, lens, k):
+    _say(f"[topk] {name}")
+    sc, lens = _scores_case(kind, B, T, Lmax, lens, seed=zlib.crc32(name.encode()) % 1000)
+    got = dsa.topk(torch.from_numpy(sc).cuda(), torch.from_numpy(lens).cuda(), k)
+    torch.cuda.synchronize()
+    ref = orc.topk(sc, lens, k)
+    np.testing.assert_array_equal(got.cpu().numpy(), ref)
+
+
+def test_topk_deterministic(dsa):
+    sc, lens = _scores_case("ties", 4, 1, 9000, [9000] * 4, seed=3)
+    s, l = torch.from_numpy(sc).cuda(), torch.from_numpy(lens).cuda()
+    a = dsa.topk(s, l, 2048)
+    b = dsa.topk(s, l, 2048)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
+
+
+# ----------------------------------------------------------------------------- sparse attention
+
+def _random_idx(rng, B, T, k, lens, invisible=False):
+    idx = np.full((B, T, k), -1, np.int32)
+    for b in range(B):
+        for t in range(T):
+            n = int(lens[b]) - T + t + 1
+            m = min(k, n)
+            idx[b, t, :m] = np.sort(rng.choice(n, size=m, replace=False))
+            if invisible and m < k and n < int(lens[b]):
+                idx[b, t, m] = rng.integers(n, int(lens[b]))      # must be ignored
+    return idx
+
+
+MLA_CASES = [
+    # name, B, T, Lmax, lens, k, H
+    ("decode_k2048", 2, 1, 3000, [3000, 1500], 2048, 128),
+    ("decode_ragged_k", 3, 1, 700, [700, 650, 90], 100, 128),
+    ("two_rows_causal", 1, 2, 2100, [2100], 2048, 128),
+    ("heads64", 2, 1, 900, [900, 513], 512, 64),
+    ("many_rows_nosplit", 260, 1, 160, [160] * 260, 64, 128),
+]
+
+
+@pytest.mark.parametrize("name,B,T,Lmax,lens,k,H", MLA_CASES, ids=[c[0] for c in MLA_CASES])
+def test_sparse_mla_decode_mfma(dsa, orc, name, B, T, Lmax, lens, k, H):
+    _say(f"[sparse_mla_decode bf16] {name}")
+    rng = np.random.default_rng(zlib.crc32(name.encode()) % 10000)
+    lens = np.asarray(lens, np.int32)
+    q = S.to_bf16_bits(rng.standard_normal((B, T, H, 576), dtype=np.float32))
+    lat = S.to_bf16_bits(rng.standard_normal((B, Lmax, 576), dtype=np.float32))
+    idx = _random_idx(rng, B, T, k, lens, invisible=True)
+    sm = 192 ** -0.5
+    tq = torch.from_numpy(q.view(np.int16)).view(torch.bfloat16).cuda()
+    tl = torch.from_numpy(lat.view(np.int16)).view(torch.bfloat16).cuda()
+    out, lse = dsa.sparse_mla_decode(tq, tl, torch.from_numpy(idx).cuda(),
+                                     torch.from_numpy(lens).cuda(), 512, sm)
+    torch.cuda.synchronize()
+    ro, rl = orc.sparse_mla_decode(q, lat, idx, lens, 512, sm)
+    check_attention(_np_out(out), lse.cpu().numpy(), ro, rl, "bf16")
+
+
+def test_sparse_mla_decode_generic_f32(dsa, orc):
+    _say("[sparse_mla_decode f32 generic]")
+    rng = np.random.default_rng(7)
+    B, T, H, Dv, Dr, Lmax, k = 2, 5, 4, 64, 16, 40, 8
+    lens = np.array([40, 9], np.int32)
+    q = rng.standard_normal((B, T, H, Dv + Dr)).astype(np.float32)
+    lat = rng.standard_normal((B, Lmax, Dv + Dr)).astype(np.float32)
+    idx = _random_idx(rng, B, T, k, lens, invisible=True)
+    out, lse = dsa.sparse_mla_decode(torch.from_numpy(q).cuda(), torch.from_numpy(lat).cuda(),
+                                     torch.from_numpy(idx).cuda(), torch.from_numpy(lens).cuda(),
+                                     Dv, 0.11)
+    torch.cuda.synchronize()
+    ro, rl = orc.sparse_mla_decode(q, lat, idx, lens, Dv, 0.11)
+    check_attention(out.cpu().numpy(), lse.cpu().numpy(), ro, rl, "f32")
+
+
+@pytest.mark.parametrize("dt", ["bf16", "f32"])
+def test_sparse_mla_prefill(dsa, orc, dt):
+    _say(f"[sparse_mla_prefill {dt}]")
+    rng = np.random.default_rng(9)
+    B, T, H, Dqk, Dv, k = 2, 40, 3, 192, 128, 16
+    mk = (lambda a: S.to_bf16_bits(a)) if dt == "bf16" else (lambda a: a)
+    q = mk(rng.standard_normal((B, T, H, Dqk), dtype=np.float32))
+    kk = mk(rng.standard_normal((B, T, H, Dqk), dtype=np.float32))
+    v = mk(rng.standard_normal((B, T, H, Dv), dtype=np.float32))
+    idx = np.full((B, T, k), -1, np.int32)
+    for b in range(B):
+        for t in range(T):
+            m = min(k, T)
+            idx[b, t, :m] = rng.choice(T, size=m, replace=False)   # includes s > t: ignored
+    def tt(a):
+        if dt == "bf16":
+            return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).cuda()
+        return torch.from_numpy(a).cuda()
+    out, lse = dsa.sparse_mla_prefill(tt(q), tt(kk), tt(v), torch.from_numpy(idx).cuda(), 0.07)
+    torch.cuda.synchronize()
+    ro, rl = orc.sparse_mha_prefill(q, kk, v, idx, 0.07)
+    check_attention(_np_out(out), lse.cpu().numpy(), ro, rl, dt)
+
+
+# ----------------------------------------------------------------------------- layer step
+
+LAYER_CASES = [
+    ("tiny", _small("tiny")),
+    ("decode_small", _small("decode_v32", name="ds", B=3, Lmax=4100, seed=202)),
+    ("ragged_small_t3", _small("decode_ragged", name="rs", B=5, Lmax=6000,
+                               lens="ragged:1024:6000", seed=205)),
+]
+
+
+def _layer_step_latent(dsa, cfg, c):
+    d = _dev(c)
+    step = dsa.LayerStep(d["q_i"], d["q_scale"], d["w"], d["k_i"], d["k_scale"], d["lens"],
+                         cfg.sm_scale_i, cfg.k, d["q"], cfg.sm_scale, latent=d["latent"],
+                         Dv=cfg.Dv, want_idx=True, want_scores=True)
+    out, lse = step()
+    torch.cuda.synchronize()
+    return step, out, lse
+
+
+@pytest.mark.parametrize("name,cfg", LAYER_CASES, ids=[c[0] for c in LAYER_CASES])
+def test_layer_step_latent(dsa, orc, name, cfg):
+    _say(f"[layer_step latent] {name}")
+    c = S.make_case(cfg)
+    step, out, lse = _layer_step_latent(dsa, cfg, c)
+    ro, rl, ridx, rsc = orc.layer_step_latent(c["q_i"], c["q_scale"], c["w"], c["k_i"],
+                                              c["k_scale"], c["lens"], cfg.sm_scale_i, cfg.k,
+                                              c["q"], c["latent"], cfg.Dv, cfg.sm_scale,
+                                              want_scores=True)
+    check_scores(step.scores.cpu().numpy(), rsc, c["lens"], cfg.T)
+    gidx = step.idx.cpu().numpy()
+    check_topk(gidx, rsc, ridx, c["lens"], cfg.T, cfg.k)
+    # attention on the GPU's own selection
+    ro2, rl2 = orc.sparse_mla_decode(c["q"], c["latent"], gidx, c["lens"], cfg.Dv, cfg.sm_scale)
+    check_attention(_np_out(out), lse.cpu().numpy(), ro2, rl2, cfg.attn_dtype)
+
+
+def test_layer_step_mha_small(dsa, orc):
+    _say("[layer_step mha] small")
+    cfg = _small("prefill_chunk", name="pm", T=96, Lmax=96, H=4, k=24, seed=404)
+    c = S.make_case(cfg)
+    d = _dev(c)
+    step = dsa.LayerStep(d["q_i"], d["q_scale"], d["w"], d["k_i"], d["k_scale"], d["lens"],
+                         cfg.sm_scale_i, cfg.k, d["q"], cfg.sm_scale, k=d["k"], v=d["v"],
+                         want_idx=True, want_scores=True)
+    out, lse = step()
+    torch.cuda.synchronize()
+    rsc = orc.index_scores(c["q_i"], c["q_scale"], c["w"], c["k_i"], c["k_scale"], c["lens"],
+                           cfg.sm_scale_i)
+    ridx = orc.topk(rsc, c["lens"], cfg.k)
+    check_scores(step.scores.cpu().numpy(), rsc, c["lens"], cfg.T)
+    gidx = step.idx.cpu().numpy()
+    check_topk(gidx, rsc, ridx, c["lens"], cfg.T, cfg.k)
+    ro, rl = orc.sparse_mha_prefill(c["q"], c["k"], c["v"], gidx, cfg.sm_scale)
+    check_attention(_np_out(out), lse.cpu().numpy(), ro, rl, "bf16")
+
+
+def test_layer_step_deterministic(dsa):
+    cfg = _small("decode_v32", name="det", B=4, Lmax=5000, seed=303)
+    c = S.make_case(cfg)
+    s1, o1, l1 = _layer_step_latent(dsa, cfg, c)
+    i1 = s1.idx.clone()
+    o1 = o1.clone()
+    o2, l2 = s1()
+    torch.cuda.synchronize()
+    assert torch.equal(i1, s1.idx)
+    assert torch.equal(o1, o2)
