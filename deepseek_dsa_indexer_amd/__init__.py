@@ -11,8 +11,8 @@ The computation lives in ``libdsa_amd.so`` (HIP kernels behind the C ABI of
 
 Build the library with ``python -m deepseek_dsa_indexer_amd.build``.
 """
-from ._native import (DSAError, LayerStep, index_scores, library_path, load, sparse_mla_decode,
-                      sparse_mla_prefill, topk)
+from ._native import (DSAError, LayerStep, index_scores, library_path, load, profile_begin,
+                      profile_end, sparse_mla_decode, sparse_mla_prefill, topk)
 
-__all__ = ["DSAError", "LayerStep", "index_scores", "library_path", "load", "sparse_mla_decode",
-           "sparse_mla_prefill", "topk"]
+__all__ = ["DSAError", "LayerStep", "index_scores", "library_path", "load", "profile_begin",
+           "profile_end", "sparse_mla_decode", "sparse_mla_prefill", "topk"]

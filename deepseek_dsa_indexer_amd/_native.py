@@ -23,7 +23,9 @@ STATUS_NAMES = {0: "DSA_OK", 1: "DSA_ERR_NULL", 2: "DSA_ERR_SHAPE", 3: "DSA_ERR_
 EXPORTED = ["dsa_last_error", "dsa_version", "dsa_index_scores", "dsa_topk_workspace_bytes",
             "dsa_topk", "dsa_sparse_mla_decode_workspace_bytes", "dsa_sparse_mla_decode",
             "dsa_sparse_mla_prefill_workspace_bytes", "dsa_sparse_mla_prefill",
-            "dsa_layer_step_workspace_bytes", "dsa_layer_step"]
+            "dsa_layer_step_workspace_bytes", "dsa_layer_step", "dsa_profile_begin",
+            "dsa_profile_end"]
+PHASES = ("index_scores", "topk", "attention", "combine")
 
 
 class DSAError(RuntimeError):
@@ -83,8 +85,10 @@ def load():
     lib.dsa_layer_step_workspace_bytes.argtypes = [ctypes.POINTER(LayerArgs)]
     lib.dsa_layer_step_workspace_bytes.restype = Z
     lib.dsa_layer_step.argtypes = [ctypes.POINTER(LayerArgs), P, Z, P]
+    lib.dsa_profile_begin.argtypes = [I]
+    lib.dsa_profile_end.argtypes = [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(I)]
     for fn in ("dsa_index_scores", "dsa_topk", "dsa_sparse_mla_decode", "dsa_sparse_mla_prefill",
-               "dsa_layer_step"):
+               "dsa_layer_step", "dsa_profile_begin", "dsa_profile_end"):
         getattr(lib, fn).restype = I
     _lib = lib
     return lib
@@ -208,6 +212,19 @@ def sparse_mla_prefill(q, k, v, idx, sm_scale, out=None, lse=None, want_lse=True
                                       topk_, float(sm_scale), dt, _ptr(out), _ptr(lse), _ptr(ws),
                                       ws_bytes, _stream(q.device)))
     return out, lse
+
+
+def profile_begin(max_steps: int):
+    """Start HIP-event timing of the phases of every following layer step."""
+    _check(load().dsa_profile_begin(int(max_steps)))
+
+
+def profile_end() -> dict:
+    """Stop timing; returns {phase: (total_ms, count)} for the recorded steps."""
+    ms = (ctypes.c_double * 4)()
+    cnt = (ctypes.c_int * 4)()
+    _check(load().dsa_profile_end(ms, cnt))
+    return {name: (ms[i], cnt[i]) for i, name in enumerate(PHASES)}
 
 
 class LayerStep:

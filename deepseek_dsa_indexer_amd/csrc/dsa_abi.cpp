@@ -5,6 +5,7 @@
 #include <cstdio>
 #include <cstring>
 #include <string>
+#include <vector>
 
 #include "../../include/dsa.h"
 #include "dsa_internal.h"
@@ -31,6 +32,8 @@ dsa_status hip_status(hipError_t e, const char* what) {
     if (e != hipSuccess) return fail(DSA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
     return DSA_OK;
 }
+
+constexpr size_t kPhaseCountMarks = dsa::kPhaseCount + 1;   // events per layer step
 
 #define DSA_REQUIRE(cond, st, ...) \
     do {                           \
@@ -161,9 +164,70 @@ dsa_status launch_mha(const void* q, const void* k, const void* v, const int32_t
 
 size_t mha_ws(int, int, int, int, int, int, dsa_dtype) { return 0; }
 
+// Event timing of dsa_layer_step phases (dsa_profile_begin / dsa_profile_end).
+struct Profiler {
+    bool on = false;
+    std::vector<hipEvent_t> pool;
+    std::vector<int> label;     // phase started by each recorded event (kPhaseNone: none)
+    size_t used = 0;
+};
+Profiler g_prof;
+
 }  // namespace
 
+void dsa::prof_mark(hipStream_t stream, int next) {
+    if (!g_prof.on || g_prof.used >= g_prof.pool.size()) return;
+    if (hipEventRecord(g_prof.pool[g_prof.used], stream) != hipSuccess) return;
+    g_prof.label[g_prof.used] = next;
+    ++g_prof.used;
+}
+
 extern "C" {
+
+dsa_status dsa_profile_begin(int max_steps) {
+    DSA_REQUIRE(max_steps >= 1 && max_steps <= (1 << 20), DSA_ERR_SHAPE,
+                "profile: max_steps=%d out of range", max_steps);
+    DSA_REQUIRE(!g_prof.on, DSA_ERR_SHAPE, "profile: already running");
+    const size_t n = static_cast<size_t>(max_steps) * (kPhaseCountMarks);
+    g_prof.pool.resize(n);
+    g_prof.label.assign(n, dsa::kPhaseNone);
+    for (size_t i = 0; i < n; ++i) {
+        hipError_t e = hipEventCreate(&g_prof.pool[i]);
+        if (e != hipSuccess) {
+            for (size_t j = 0; j < i; ++j) (void)hipEventDestroy(g_prof.pool[j]);
+            g_prof.pool.clear();
+            return hip_status(e, "profile: hipEventCreate");
+        }
+    }
+    g_prof.used = 0;
+    g_prof.on = true;
+    return DSA_OK;
+}
+
+dsa_status dsa_profile_end(double* ms_total, int* counts) {
+    DSA_REQUIRE(ms_total && counts, DSA_ERR_NULL, "profile: NULL output");
+    DSA_REQUIRE(g_prof.on, DSA_ERR_SHAPE, "profile: not running");
+    for (int p = 0; p < dsa::kPhaseCount; ++p) { ms_total[p] = 0.0; counts[p] = 0; }
+    dsa_status st = DSA_OK;
+    if (g_prof.used > 0) {
+        st = hip_status(hipEventSynchronize(g_prof.pool[g_prof.used - 1]), "profile: sync");
+        for (size_t i = 0; st == DSA_OK && i + 1 < g_prof.used; ++i) {
+            const int p = g_prof.label[i];
+            if (p < 0) continue;
+            float ms = 0.f;
+            st = hip_status(hipEventElapsedTime(&ms, g_prof.pool[i], g_prof.pool[i + 1]),
+                            "profile: elapsed time");
+            ms_total[p] += ms;
+            counts[p] += 1;
+        }
+    }
+    for (hipEvent_t e : g_prof.pool) (void)hipEventDestroy(e);
+    g_prof.pool.clear();
+    g_prof.label.clear();
+    g_prof.used = 0;
+    g_prof.on = false;
+    return st;
+}
 
 const char* dsa_last_error(void) { return g_last_error.c_str(); }
 
@@ -290,16 +354,22 @@ dsa_status dsa_layer_step(const dsa_layer_args* a, void* ws, size_t ws_bytes, hi
 
     dsa::IndexScoresArgs ia{a->q_fp8, a->q_scale, a->w, a->k_fp8, a->k_scale, a->len, a->B, a->T,
                             a->H_I, a->d_I, a->Lmax, a->sm_scale_I, scores, a->scores_out ? 1 : 0};
+    dsa::prof_mark(stream, dsa::kPhaseIndex);
     st = hip_status(dsa::launch_index_scores(ia, stream), "layer step: index scores");
     if (st != DSA_OK) return st;
+    dsa::prof_mark(stream, dsa::kPhaseTopk);
     dsa::TopkArgs ta{scores, a->len, a->B, a->T, a->Lmax, a->topk, idx};
     st = hip_status(dsa::launch_topk(ta, nullptr, stream), "layer step: topk");
     if (st != DSA_OK) return st;
+    dsa::prof_mark(stream, dsa::kPhaseAttention);
     if (a->form == DSA_ATTN_LATENT)
-        return launch_latent(a->q, a->latent, idx, a->len, a->B, a->T, a->H, a->Dv, a->Dr, a->Lmax,
-                             a->topk, a->sm_scale, a->dtype, a->out, a->lse, att_ws, stream);
-    return launch_mha(a->q, a->k, a->v, idx, a->B, a->T, a->H, a->Dqk, a->Dv, a->topk, a->sm_scale,
-                      a->dtype, a->out, a->lse, att_ws, stream);
+        st = launch_latent(a->q, a->latent, idx, a->len, a->B, a->T, a->H, a->Dv, a->Dr, a->Lmax,
+                           a->topk, a->sm_scale, a->dtype, a->out, a->lse, att_ws, stream);
+    else
+        st = launch_mha(a->q, a->k, a->v, idx, a->B, a->T, a->H, a->Dqk, a->Dv, a->topk,
+                        a->sm_scale, a->dtype, a->out, a->lse, att_ws, stream);
+    dsa::prof_mark(stream, dsa::kPhaseNone);
+    return st;
 }
 
 }  // extern "C"

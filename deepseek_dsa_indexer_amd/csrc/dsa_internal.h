@@ -8,6 +8,13 @@
 
 namespace dsa {
 
+// Phases of one layer step, for the optional event timing of dsa_profile_begin/_end.
+enum Phase { kPhaseIndex = 0, kPhaseTopk = 1, kPhaseAttention = 2, kPhaseCombine = 3,
+             kPhaseCount = 4, kPhaseNone = -1 };
+// Records a HIP event on `stream` that ends the running phase and starts `next`
+// (kPhaseNone: nothing starts).  A no-op unless profiling is on.
+void prof_mark(hipStream_t stream, int next);
+
 struct IndexScoresArgs {
     const uint8_t* q;
     const float* q_scale;

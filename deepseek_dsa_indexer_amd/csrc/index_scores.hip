@@ -38,17 +38,17 @@ constexpr int kChunk = 64;          // keys per wave iteration (4 MFMA column ti
 
 typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
 
+// 32 contiguous bytes (two 16-byte loads) of `p`, zeroed when !ok.  The load is issued
+// unconditionally (callers pass a clamped, in-bounds address): a load inside a divergent
+// branch makes the compiler drain every outstanding load at the branch join.
 __device__ __forceinline__ v8i load32(const uint8_t* p, bool ok) {
-    // 32 contiguous bytes (two 16-byte loads), or zeros when !ok
-    v8i r = {0, 0, 0, 0, 0, 0, 0, 0};
-    if (ok) {
-        const uint4* s = reinterpret_cast<const uint4*>(p);
-        uint4 a = s[0];
-        uint4 b = s[1];
-        r[0] = a.x; r[1] = a.y; r[2] = a.z; r[3] = a.w;
-        r[4] = b.x; r[5] = b.y; r[6] = b.z; r[7] = b.w;
-    }
-    return r;
+    const uint4* s = reinterpret_cast<const uint4*>(p);
+    const uint4 a = s[0];
+    const uint4 b = s[1];
+    const int m = ok ? -1 : 0;
+    return v8i{static_cast<int>(a.x) & m, static_cast<int>(a.y) & m, static_cast<int>(a.z) & m,
+               static_cast<int>(a.w) & m, static_cast<int>(b.x) & m, static_cast<int>(b.y) & m,
+               static_cast<int>(b.z) & m, static_cast<int>(b.w) & m};
 }
 
 // 8 FP8 bytes (two dwords) -> 8 bf16, exactly.
@@ -108,84 +108,112 @@ void index_scores_kernel(const uint8_t* __restrict__ q, const float* __restrict_
         return;
     }
 
-    // ---- issue the key-chunk loads of this wave first
     const uint8_t* kb_ptr = k + static_cast<size_t>(b) * Lmax * D;
     const float* ks_ptr = k_scale + static_cast<size_t>(b) * Lmax;
-    v8i kt[CHUNKS][4];
-    float ks[CHUNKS];
-#pragma unroll
-    for (int c = 0; c < CHUNKS; ++c) {
-        const int kb = key_blk + (c * (kThreads / kWave) + wave) * kChunk;
-        const bool live = kb <= pos_hi;
+    // chunk c of this wave starts at key_blk + (4 c + wave) * 64
+    auto chunk_key = [&](int c) { return key_blk + (c * (kThreads / kWave) + wave) * kChunk; };
+    auto load_chunk = [&](int c, v8i (&dst)[4], float& ks) {
+        const int kb = chunk_key(c);
+        const bool live = c < CHUNKS && kb <= pos_hi;
 #pragma unroll
         for (int tile = 0; tile < 4; ++tile) {
             const int key = kb + 16 * tile + n;
-            kt[c][tile] = load32(kb_ptr + static_cast<size_t>(key) * D + g * 32,
-                                 live && key < Lmax && g * 32 < D);
+            const bool ok = live && key < Lmax && g * 32 < D;
+            const int kc = min(key, Lmax - 1);
+            const int bc = g * 32 < D ? g * 32 : 0;
+            dst[tile] = load32(kb_ptr + static_cast<size_t>(kc) * D + bc, ok);
         }
-        const int key = kb + lane;
-        ks[c] = (live && key < Lmax) ? ks_ptr[key] : 0.f;
-    }
+        // positions at or beyond Lmax are never stored, so the clamped scale needs no mask
+        ks = ks_ptr[min(kb + lane, Lmax - 1)];
+    };
 
-    // ---- query operands (bf16) and folded head weights, kept in registers
+    // ---- query operands (bf16) and folded head weights, kept in registers.  Their loads
+    // are issued before the key loads, so waiting for them leaves the keys in flight.
     v8bf qa[QR][4][4];
     float wf[QR][4][4];
+    {
+        v8i raw[QR][4];
+        float wv[QR][4][4], qsv[QR][4][4];
 #pragma unroll
-    for (int r = 0; r < QR; ++r) {
-        const size_t qrow = static_cast<size_t>(b) * T + t0 + r;
+        for (int r = 0; r < QR; ++r) {
+            const size_t qrow = static_cast<size_t>(b) * T + t0 + min(r, nrows - 1);
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int head = 16 * j + n;
-            const bool ok = r < nrows && head < H && g * 32 < D;
-            const v8i raw = load32(q + (qrow * H + head) * D + g * 32, ok);
+            for (int j = 0; j < 4; ++j) {
+                const int head = 16 * j + n;
+                const bool ok = r < nrows && head < H && g * 32 < D;
+                raw[r][j] = load32(q + (qrow * H + min(head, H - 1)) * D + (g * 32 < D ? g * 32 : 0), ok);
 #pragma unroll
-            for (int kk = 0; kk < 4; ++kk) qa[r][j][kk] = fp8x8_to_bf16(raw[2 * kk], raw[2 * kk + 1]);
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int hh = 16 * j + 4 * g + i;
-                float v = 0.f;
-                if (r < nrows && hh < H) v = w[qrow * H + hh] * q_scale[qrow * H + hh] * sm_scale;
-                wf[r][j][i] = v;
+                for (int i = 0; i < 4; ++i) {
+                    const int hh = min(16 * j + 4 * g + i, H - 1);
+                    wv[r][j][i] = w[qrow * H + hh];
+                    qsv[r][j][i] = q_scale[qrow * H + hh];
+                }
             }
         }
+#pragma unroll
+        for (int r = 0; r < QR; ++r)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+#pragma unroll
+                for (int kk = 0; kk < 4; ++kk)
+                    qa[r][j][kk] = fp8x8_to_bf16(raw[r][j][2 * kk], raw[r][j][2 * kk + 1]);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    // arithmetic mask (no branch): padded heads and rows get weight 0
+                    const float ok = (r < nrows && 16 * j + 4 * g + i < H) ? 1.f : 0.f;
+                    wf[r][j][i] = wv[r][j][i] * qsv[r][j][i] * sm_scale * ok;
+                }
+            }
     }
 
-#pragma unroll
+    // ---- two chunks of keys in flight ahead of the arithmetic
+    v8i cur[4], nxt[4];
+    float ks_cur, ks_nxt;
+    load_chunk(0, cur, ks_cur);
+    load_chunk(1, nxt, ks_nxt);
+
     for (int c = 0; c < CHUNKS; ++c) {
-        const int kb = key_blk + (c * (kThreads / kWave) + wave) * kChunk;
+        const int kb = chunk_key(c);
         const int key = kb + lane;
         if (kb > pos_hi) {
             if (fill_invisible && key < Lmax)
                 for (int r = 0; r < nrows; ++r) out[static_cast<size_t>(r) * Lmax + key] = -INFINITY;
-            continue;
-        }
-        float s[QR][4];
+        } else {
+            float s[QR][4];
 #pragma unroll
-        for (int tile = 0; tile < 4; ++tile) {
-            v8bf kbf[4];
+            for (int tile = 0; tile < 4; ++tile) {
+                v8bf kbf[4];
 #pragma unroll
-            for (int kk = 0; kk < 4; ++kk)
-                kbf[kk] = fp8x8_to_bf16(kt[c][tile][2 * kk], kt[c][tile][2 * kk + 1]);
+                for (int kk = 0; kk < 4; ++kk) kbf[kk] = fp8x8_to_bf16(cur[tile][2 * kk], cur[tile][2 * kk + 1]);
+#pragma unroll
+                for (int r = 0; r < QR; ++r) {
+                    // the four head tiles are independent accumulation chains: interleave them
+                    v4f d[4];
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) d[j] = v4f{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                    for (int kk = 0; kk < 4; ++kk)
+#pragma unroll
+                        for (int j = 0; j < 4; ++j) d[j] = mfma_bf16_16x16x32(qa[r][j][kk], kbf[kk], d[j]);
+                    float acc = 0.f;
+#pragma unroll
+                    for (int j = 0; j < 4; ++j)
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) acc += wf[r][j][i] * fmaxf(d[j][i], 0.f);
+                    s[r][tile] = acc;
+                }
+            }
 #pragma unroll
             for (int r = 0; r < QR; ++r) {
-                float acc = 0.f;
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    v4f d = v4f{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                    for (int kk = 0; kk < 4; ++kk) d = mfma_bf16_16x16x32(qa[r][j][kk], kbf[kk], d);
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) acc += wf[r][j][i] * fmaxf(d[i], 0.f);
-                }
-                s[r][tile] = acc;
+                const float total = head_sum_transpose(s[r], g);
+                if (r < nrows && key < Lmax)
+                    out[static_cast<size_t>(r) * Lmax + key] = (key <= pos0 + r) ? total * ks_cur : -INFINITY;
             }
         }
 #pragma unroll
-        for (int r = 0; r < QR; ++r) {
-            const float total = head_sum_transpose(s[r], g);
-            if (r < nrows && key < Lmax)
-                out[static_cast<size_t>(r) * Lmax + key] = (key <= pos0 + r) ? total * ks[c] : -INFINITY;
-        }
+        for (int tile = 0; tile < 4; ++tile) cur[tile] = nxt[tile];
+        ks_cur = ks_nxt;
+        if (c + 2 < CHUNKS) load_chunk(c + 2, nxt, ks_nxt);
     }
 }
 

@@ -114,26 +114,27 @@ void sparse_attn_generic_kernel(SparseAttnArgs a)
 
 // ------------------------------------------------------------------ matrix-core latent path
 //
-// One workgroup (4 waves, one wave per SIMD) owns one query row (b,t), one split of its
-// k slots and one group of 64 heads.  Per tile of 32 selected positions:
-//   gather   32 rows -> LDS with direct global->LDS 16-byte loads, double buffered; the
-//            16-byte chunks of each row are XOR-swizzled inside 128-byte groups so the
-//            matrix-core operand reads spread over the LDS banks;
-//   QK       wave w computes S^T = K . Q^T for heads 16w..16w+15 of the group (keys as
-//            MFMA rows; the wave's queries stay in registers as 18 B operands);
-//   softmax  online, per head, with lazy rescaling: the running maximum only moves when
-//            a tile exceeds it by more than 2^8, so the accumulators are rarely touched;
-//            bf16 probabilities go to LDS already in MFMA operand layout;
-//   PV       wave w owns output columns 128w..128w+127 for the group's 64 heads:
-//            O += P . V with V read from the same LDS tile (the value is the first 512
+// One workgroup (8 waves, two per SIMD) owns one query row (b,t), one split of its k
+// slots and all heads (64 or 128), so every selected latent row is gathered from memory
+// once per row and split.  Per tile of 32 selected positions:
+//   gather   32 latent rows -> LDS with direct global->LDS 16-byte loads.  Four tile
+//            buffers are distinct LDS objects; three tiles stay in flight while one is
+//            consumed.  The 16-byte chunks of each row are XOR-swizzled inside 128-byte
+//            groups so the matrix-core operand reads spread over the LDS banks;
+//   QK       wave w computes S^T = K . Q^T for head tile w (16 heads) and all 32 keys of
+//            the tile (keys as MFMA rows; the wave's queries stay in registers as 18 B
+//            operands);
+//   softmax  online, per head, entirely inside the owning wave, with lazy rescaling: the
+//            running maximum only moves when a tile exceeds it by more than 2^8; the bf16
+//            probabilities go to LDS in MFMA operand layout;
+//   PV       wave w owns output columns 64w..64w+63 for all heads: O += P . V with V read
+//            from the same LDS tile by transpose reads (the value is the first 512
 //            columns of the latent row).
-// The two head groups of a (row, split) are given block ids 8 apart, which the
-// dispatcher places on the same XCD, so the second gather of each latent row is
-// served by that XCD's L2.  Splits of one row are merged by a log-sum-exp combine.
-constexpr int kMlaThreads = 256;
-constexpr int kMlaWaves = 4;
-constexpr int kHeadsPerGroup = 64;
-constexpr int kNht = kHeadsPerGroup / 16;          // head tiles per workgroup
+// Two workgroup barriers per tile.  Splits of one row are merged by a log-sum-exp
+// combine kernel.
+constexpr int kMlaThreads = 512;
+constexpr int kMlaWaves = 8;
+constexpr int kMaxHt = 8;                          // up to 128 heads per workgroup
 constexpr int kDq = 576;
 constexpr int kDv = 512;
 constexpr int kRowBytes = kDq * 2;                 // 1152
@@ -141,54 +142,252 @@ constexpr int kRowChunks = kRowBytes / 16;         // 72
 constexpr int kKt = 32;                            // selected positions per tile
 constexpr int kTileBytes = kKt * kRowBytes;        // 36864
 constexpr int kTileLoads = kTileBytes / (kWave * 16);   // 36 wave-wide 1 KB loads
-constexpr int kMaxSlots = 2048;                    // slots per split held in LDS
+constexpr int kMaxSlots = 1024;                    // slots per split held in LDS
 constexpr int kDs = kDq / 32;                      // 18 K-steps of the QK product
-constexpr int kDt = kDv / kMlaWaves / 16;          // 8 output column tiles per wave
-constexpr int kXcds = 8;
+constexpr int kDtW = kDv / kMlaWaves / 16;         // 4 output column tiles per wave
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kLazyRescale = 8.0f;               // log2 units
 
+__shared__ __attribute__((aligned(16))) uint8_t g_kbuf0[kTileBytes];
+__shared__ __attribute__((aligned(16))) uint8_t g_kbuf1[kTileBytes];
+__shared__ __attribute__((aligned(16))) uint8_t g_kbuf2[kTileBytes];
+__shared__ __attribute__((aligned(16))) uint8_t g_kbuf3[kTileBytes];
+__shared__ __attribute__((aligned(16))) uint8_t g_pbuf[kMaxHt][kWave][16];
+__shared__ __attribute__((aligned(16))) float g_alpha[kMaxHt * 16];
+__shared__ int32_t g_rescale[kMaxHt];
+__shared__ float g_l[kMaxHt * 16];
+__shared__ float g_m[kMaxHt * 16];
+__shared__ int32_t g_keys[kMaxSlots];
+
+template <int I>
+__device__ __forceinline__ uint8_t* kbuf() {
+    if constexpr (I == 0) return g_kbuf0;
+    else if constexpr (I == 1) return g_kbuf1;
+    else if constexpr (I == 2) return g_kbuf2;
+    else return g_kbuf3;
+}
+
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() { asm volatile("s_waitcnt vmcnt(%0)" :: "n"(N) : "memory"); }
+
 __device__ __forceinline__ int swz_chunk(int key, int chunk) { return chunk ^ (key & 7); }
 
-__global__ __launch_bounds__(kMlaThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
+// Workgroup barrier for LDS data only: waits for this wave's LDS operations, not for
+// its global loads, so tile prefetches stay in flight across it (__syncthreads() would
+// also drain every outstanding global->LDS load).
+__device__ __forceinline__ void lds_barrier() {
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+// Wait until this wave's gathers of the current tile have landed, leaving the `later`
+// tiles issued after it in flight (waves 0..3 issue 5 loads per tile, waves 4..7 four).
+__device__ __forceinline__ void wait_tile(int later, bool five) {
+    if (five) {
+        if (later >= 2) wait_vmcnt<10>(); else if (later == 1) wait_vmcnt<5>(); else wait_vmcnt<0>();
+    } else {
+        if (later >= 2) wait_vmcnt<8>(); else if (later == 1) wait_vmcnt<4>(); else wait_vmcnt<0>();
+    }
+}
+
+// Issue the direct global->LDS loads of tile `ti` into `dst`: wave w issues the
+// wave-wide 1 KB loads ci = w, w + 8, ... < 36 (five for waves 0..3, four for waves
+// 4..7); lane l of load ci fetches the 16-byte chunk c = 64 ci + l of the tile, i.e.
+// chunk c % 72 of selected row c / 72, stored at the swizzled chunk position of that row.
+// The per-lane offsets are recomputed from an opaque copy of the lane id on every call
+// (kept live across the loop they would cost registers, and spill reloads would drain
+// the loads in flight).  The loads are written as inline assembly so that the compiler,
+// which cannot tell the four tile buffers apart through a runtime tile index, does not
+// drain them before every LDS read; completion is tracked explicitly with wait_tile()
+// and made visible to the other waves by lds_barrier().  M0 carries the wave-uniform LDS
+// destination; no other instruction of this kernel uses M0.
+constexpr int kGatherMax = (kTileLoads + kMlaWaves - 1) / kMlaWaves;   // 5
+__device__ __forceinline__ void gather_tile(const uint8_t* lat_b, int ti, uint8_t* dst, int wave,
+                                            int lane) {
+    asm volatile("" : "+v"(lane));
+    const uint32_t lds_base = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(
+        (__attribute__((address_space(3))) uint8_t*)(dst)));
+    int s[kGatherMax], key[kGatherMax];
+#pragma unroll
+    for (int i = 0; i < kGatherMax; ++i) {
+        const int c = (wave + kMlaWaves * i) * kWave + lane;
+        key[i] = min(c / kRowChunks, kKt - 1);
+        s[i] = g_keys[ti * kKt + key[i]];
+    }
+#pragma unroll
+    for (int i = 0; i < kGatherMax; ++i) {
+        const int ci = wave + kMlaWaves * i;
+        if (ci < kTileLoads) {
+            const int c = ci * kWave + lane;
+            const int row = s[i] < 0 ? 0 : s[i];     // unused slots read row 0 (masked later)
+            const uint32_t off = static_cast<uint32_t>(row) * kRowBytes +
+                                 swz_chunk(key[i], c - key[i] * kRowChunks) * 16;
+            const uint8_t* src = lat_b + off;
+            const uint32_t m0v = __builtin_amdgcn_readfirstlane(lds_base + ci * kWave * 16);
+            asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off"
+                         :: "s"(m0v), "v"(src) : "memory");
+        }
+    }
+}
+
+template <int NHT>
+struct MlaState {
+    v8bf qreg[kDs];
+    v4f o[NHT][kDtW];
+    float m_run;
+    float l_run;
+};
+
+typedef __bf16 v4bf_t __attribute__((ext_vector_type(4)));
+
+// One tile: wait for its gather, prefetch tile ti + 3 into buffer PREF, QK, softmax, PV.
+template <int NHT, int CUR, int PREF>
+__device__ __forceinline__ void mla_tile(MlaState<NHT>& st, const uint8_t* lat_b, int ti,
+                                         int n_tiles, float scale_log2, int wave, int lane) {
+    wait_tile(min(2, n_tiles - 1 - ti), wave < 4);
+    lds_barrier();                                 // tile ti visible; tile ti-1 released
+    if (ti + 3 < n_tiles) gather_tile(lat_b, ti + 3, kbuf<PREF>(), wave, lane);
+    const uint8_t* kb = kbuf<CUR>();
+
+    // Per-lane LDS offsets are recomputed in every tile step from an opaque copy of the
+    // lane id: hoisted out of the loop they would be kept live once per buffer copy.
+    int lane_o = lane;
+    asm volatile("" : "+v"(lane_o));
+    const int go = lane_o >> 4;
+    const int no = lane_o & 15;
+
+    if (wave < NHT) {
+        // ---- QK: 32 keys x 16 heads (tile `wave`), two MFMA chains (key halves).
+        // Logical chunk 4 ds + g of key row 16 kt + n sits at chunk (4 ds + g) ^ (n & 7)
+        //   = 8 (ds / 2) + ((4 (ds & 1) + g) ^ (n & 7)),
+        // so two base offsets per key half plus an immediate cover all 18 K-steps.
+        v4f sacc[2] = {v4f{0.f, 0.f, 0.f, 0.f}, v4f{0.f, 0.f, 0.f, 0.f}};
+        {
+            const uint8_t* base[2][2];
+#pragma unroll
+            for (int kt = 0; kt < 2; ++kt) {
+                const uint8_t* krow = kb + (16 * kt + no) * kRowBytes;
+                base[kt][0] = krow + ((go) ^ (no & 7)) * 16;
+                base[kt][1] = krow + ((4 + go) ^ (no & 7)) * 16;
+            }
+            constexpr int kPre = 2;               // K-steps of operand reads in flight
+            v8bf a[kPre][2];
+#pragma unroll
+            for (int ds = 0; ds < kPre; ++ds)
+#pragma unroll
+                for (int kt = 0; kt < 2; ++kt)
+                    a[ds][kt] = *reinterpret_cast<const v8bf*>(base[kt][ds & 1] + (ds >> 1) * 128);
+#pragma unroll
+            for (int ds = 0; ds < kDs; ++ds) {
+#pragma unroll
+                for (int kt = 0; kt < 2; ++kt)
+                    sacc[kt] = mfma_bf16_16x16x32(a[ds % kPre][kt], st.qreg[ds], sacc[kt]);
+                if (ds + kPre < kDs) {
+                    const int dn = ds + kPre;
+#pragma unroll
+                    for (int kt = 0; kt < 2; ++kt)
+                        a[ds % kPre][kt] = *reinterpret_cast<const v8bf*>(base[kt][dn & 1] + (dn >> 1) * 128);
+                }
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        }
+        // ---- online softmax of the wave's 16 heads over the 32 keys of this tile.
+        // Lane (g, n) holds head n, keys 16 kt + 4 g + i, which is exactly K-slot
+        // j = 4 kt + i of the P operand of the PV product.
+        float sv[8];
+        float mx = -INFINITY;
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const bool valid = g_keys[ti * kKt + 16 * kt + 4 * go + i] >= 0;
+                const float v = valid ? sacc[kt][i] * scale_log2 : -INFINITY;
+                sv[4 * kt + i] = v;
+                mx = fmaxf(mx, v);
+            }
+        mx = fmaxf(mx, __shfl_xor(mx, 16, kWave));
+        mx = fmaxf(mx, __shfl_xor(mx, 32, kWave));
+        float alpha = 1.f;
+        if (mx > st.m_run + kLazyRescale) {
+            alpha = (st.m_run == -INFINITY) ? 0.f : exp2f(st.m_run - mx);
+            st.m_run = mx;
+        }
+        float psum = 0.f;
+        v8s pk;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const float p = (sv[j] == -INFINITY) ? 0.f : exp2f(sv[j] - st.m_run);
+            psum += p;
+            pk[j] = static_cast<short>(f32_to_bf16(p));
+        }
+        psum += __shfl_xor(psum, 16, kWave);
+        psum += __shfl_xor(psum, 32, kWave);
+        st.l_run = st.l_run * alpha + psum;
+        *reinterpret_cast<v8s*>(&g_pbuf[wave][lane][0]) = pk;
+        if (go == 0) g_alpha[16 * wave + no] = alpha;
+        const unsigned long long any = __ballot(alpha != 1.f);
+        if (lane == 0) g_rescale[wave] = any != 0ull;
+    }
+    lds_barrier();
+
+    // ---- PV: output columns 64 wave .. + 63 for all heads.  V operands come from LDS
+    // transpose reads: for K-slots j = 4 kt + r the lane needs V[16 kt + 4 g + r][d],
+    // d = 64 wave + 16 dt + n; within each 16-lane group a transpose read hands lane n
+    // the element at (address of lane 4 r + n / 4) + n % 4, so lane m supplies row
+    // 16 kt + 4 g + m / 4, columns d0 + 4 (m % 4) .. + 3.
+    v8bf vb[kDtW];
+#pragma unroll
+    for (int dt = 0; dt < kDtW; ++dt) {
+        const int d0 = 64 * wave + 16 * dt;
+        v4bf_t half[2];
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt) {
+            const int key = 16 * kt + 4 * go + (no >> 2);
+            const int chunk = (d0 >> 3) + ((no & 3) >> 1);
+            const int off = key * kRowBytes + (chunk ^ (key & 7)) * 16 + (no & 1) * 8;
+            half[kt] = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+                (__attribute__((address_space(3))) v4bf_t*)(kb + off));
+        }
+        vb[dt] = v8bf{half[0][0], half[0][1], half[0][2], half[0][3],
+                      half[1][0], half[1][1], half[1][2], half[1][3]};
+    }
+#pragma unroll
+    for (int h = 0; h < NHT; ++h) {
+        __builtin_amdgcn_sched_barrier(0);
+        if (g_rescale[h]) {
+            const float4 al = *reinterpret_cast<const float4*>(&g_alpha[16 * h + 4 * go]);
+#pragma unroll
+            for (int dt = 0; dt < kDtW; ++dt) {
+                st.o[h][dt][0] *= al.x; st.o[h][dt][1] *= al.y;
+                st.o[h][dt][2] *= al.z; st.o[h][dt][3] *= al.w;
+            }
+        }
+        const v8bf pa = *reinterpret_cast<const v8bf*>(&g_pbuf[h][lane][0]);
+#pragma unroll
+        for (int dt = 0; dt < kDtW; ++dt) st.o[h][dt] = mfma_bf16_16x16x32(pa, vb[dt], st.o[h][dt]);
+    }
+}
+
+template <int NHT>
+__global__ __launch_bounds__(kMlaThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void mla_decode_mfma_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ latent,
                             const int32_t* __restrict__ idx, const int32_t* __restrict__ len,
-                            int T, int H, int Lmax, int k, int tiles_per_split, int n_splits,
-                            int n_units, float scale_log2, uint16_t* __restrict__ out,
-                            float* __restrict__ lse, float* __restrict__ part_o,
+                            int T, int Lmax, int k, int tiles_per_split, int n_splits,
+                            float scale_log2, uint16_t* __restrict__ out,
+                            float* __restrict__ lse, uint16_t* __restrict__ part_o,
                             float* __restrict__ part_lse)
 {
-    __shared__ __attribute__((aligned(16))) uint8_t kbuf[2 * kTileBytes];
-    __shared__ __attribute__((aligned(16))) uint8_t pbuf[kNht][kWave][16];
-    __shared__ __attribute__((aligned(16))) float alpha_s[kHeadsPerGroup];
-    __shared__ int32_t rescale_s[kNht];
-    __shared__ float m_s[kHeadsPerGroup];
-    __shared__ float l_s[kHeadsPerGroup];
-    __shared__ int32_t keys_s[kMaxSlots];
-
+    constexpr int H = NHT * 16;
     const int lane = threadIdx.x & (kWave - 1);
-    const int wave = threadIdx.x / kWave;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);   // wave-uniform: SGPR
     const int g = lane >> 4;
     const int n = lane & 15;
 
-    // block id -> (unit = row * n_splits + split, head group); groups of a unit share an XCD
-    const int n_groups = H / kHeadsPerGroup;
-    int unit, hg;
-    {
-        const int x = blockIdx.x;
-        const int xcd = x % kXcds;
-        const int local = x / kXcds;
-        hg = local % n_groups;
-        unit = (local / n_groups) * kXcds + xcd;
-    }
-    if (unit >= n_units) return;
-    const int row = unit / n_splits;
-    const int split = unit - row * n_splits;
+    const int row = blockIdx.x / n_splits;
+    const int split = blockIdx.x - row * n_splits;
     const int b = row / T;
     const int t = row - b * T;
     const int pos = min(len[b], Lmax) - T + t;
-    const int head0 = hg * kHeadsPerGroup;
 
     const int n_tiles_total = (k + kKt - 1) / kKt;
     const int tile0 = split * tiles_per_split;
@@ -200,170 +399,70 @@ void mla_decode_mfma_kernel(const uint16_t* __restrict__ q, const uint16_t* __re
     for (int j = threadIdx.x; j < nslots; j += kMlaThreads) {
         const int slot = tile0 * kKt + j;
         const int s = slot < k ? sel[slot] : -1;
-        keys_s[j] = (s >= 0 && s <= pos) ? s : -1;
+        g_keys[j] = (s >= 0 && s <= pos) ? s : -1;
     }
 
-    // this wave's queries as MFMA B operands: head head0 + 16*wave + n, dims 32*ds + 8*g ..
-    v8bf qreg[kDs];
+    MlaState<NHT> st;
     {
-        const uint16_t* qrow = q + (static_cast<size_t>(row) * H + head0 + 16 * wave + n) * kDq + 8 * g;
+        // queries of head tile `wave` as MFMA B operands: head 16 wave + n, dims 32 ds + 8 g
+        const int head = wave < NHT ? 16 * wave + n : n;
+        const uint16_t* qrow = q + (static_cast<size_t>(row) * H + head) * kDq + 8 * g;
 #pragma unroll
-        for (int ds = 0; ds < kDs; ++ds) qreg[ds] = *reinterpret_cast<const v8bf*>(qrow + 32 * ds);
+        for (int ds = 0; ds < kDs; ++ds) st.qreg[ds] = *reinterpret_cast<const v8bf*>(qrow + 32 * ds);
     }
-
-    v4f o[kNht][kDt];
 #pragma unroll
-    for (int ht = 0; ht < kNht; ++ht)
+    for (int h = 0; h < NHT; ++h)
 #pragma unroll
-        for (int dt = 0; dt < kDt; ++dt) o[ht][dt] = v4f{0.f, 0.f, 0.f, 0.f};
-    float m_run = -INFINITY, l_run = 0.f;
+        for (int dt = 0; dt < kDtW; ++dt) st.o[h][dt] = v4f{0.f, 0.f, 0.f, 0.f};
+    st.m_run = -INFINITY;
+    st.l_run = 0.f;
 
     const uint8_t* lat_b = reinterpret_cast<const uint8_t*>(latent) +
                            static_cast<size_t>(b) * Lmax * kRowBytes;
-    __syncthreads();     // keys_s ready
+    // consume the query registers here, so the compiler's own wait for their loads
+    // happens before the tile gathers are in flight rather than at the first MFMA
+#pragma unroll
+    for (int ds = 0; ds < kDs; ++ds) asm volatile("" :: "v"(st.qreg[ds]));
+    __syncthreads();      // g_keys ready
+    if (n_tiles > 0) gather_tile(lat_b, 0, kbuf<0>(), wave, lane);
+    if (n_tiles > 1) gather_tile(lat_b, 1, kbuf<1>(), wave, lane);
+    if (n_tiles > 2) gather_tile(lat_b, 2, kbuf<2>(), wave, lane);
 
-    auto gather = [&](int ti, uint8_t* dst) {
-        for (int ci = wave; ci < kTileLoads; ci += kMlaWaves) {
-            const int c = ci * kWave + lane;
-            const int key = c / kRowChunks;
-            const int phys = c - key * kRowChunks;
-            int s = keys_s[ti * kKt + key];
-            s = s < 0 ? 0 : s;                       // unused slots read row 0 (masked later)
-            const uint8_t* src = lat_b + static_cast<size_t>(s) * kRowBytes +
-                                 swz_chunk(key, phys) * 16;
-            __builtin_amdgcn_global_load_lds(
-                (const __attribute__((address_space(1))) void*)(src),
-                (__attribute__((address_space(3))) void*)(dst + ci * kWave * 16),
-                16, 0, 0);
-        }
-    };
-
-    if (n_tiles > 0) gather(0, kbuf);
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
-
-    for (int ti = 0; ti < n_tiles; ++ti) {
-        const uint8_t* kb = kbuf + (ti & 1) * kTileBytes;
-        if (ti + 1 < n_tiles) gather(ti + 1, kbuf + ((ti + 1) & 1) * kTileBytes);
-
-        // ---- QK for this wave's 16 heads (keys as rows) + online softmax
-        {
-            v4f sacc[2] = {v4f{0.f, 0.f, 0.f, 0.f}, v4f{0.f, 0.f, 0.f, 0.f}};
-#pragma unroll
-            for (int ds = 0; ds < kDs; ++ds) {
-#pragma unroll
-                for (int kt = 0; kt < 2; ++kt) {
-                    const int key = kt * 16 + n;
-                    const v8bf a = *reinterpret_cast<const v8bf*>(
-                        kb + key * kRowBytes + swz_chunk(key, ds * 4 + g) * 16);
-                    sacc[kt] = mfma_bf16_16x16x32(a, qreg[ds], sacc[kt]);
-                }
-            }
-            float sv[8];
-            float mx = -INFINITY;
-#pragma unroll
-            for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const bool valid = keys_s[ti * kKt + kt * 16 + 4 * g + i] >= 0;
-                    const float v = valid ? sacc[kt][i] * scale_log2 : -INFINITY;
-                    sv[kt * 4 + i] = v;
-                    mx = fmaxf(mx, v);
-                }
-            mx = fmaxf(mx, __shfl_xor(mx, 16, kWave));
-            mx = fmaxf(mx, __shfl_xor(mx, 32, kWave));
-            // move the running maximum only when this tile exceeds it by > 2^8
-            float alpha = 1.f;
-            if (mx > m_run + kLazyRescale) {
-                alpha = (m_run == -INFINITY) ? 0.f : exp2f(m_run - mx);
-                m_run = mx;
-            }
-            float psum = 0.f;
-            v8s pk;
-#pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                const float p = (sv[j] == -INFINITY) ? 0.f : exp2f(sv[j] - m_run);
-                psum += p;
-                pk[j] = static_cast<short>(f32_to_bf16(p));
-            }
-            psum += __shfl_xor(psum, 16, kWave);
-            psum += __shfl_xor(psum, 32, kWave);
-            l_run = l_run * alpha + psum;
-            *reinterpret_cast<v8s*>(&pbuf[wave][lane][0]) = pk;
-            if (g == 0) alpha_s[16 * wave + n] = alpha;
-            // the head tile's accumulators need rescaling when any alpha != 1
-            const unsigned long long any = __ballot(alpha != 1.f);
-            if (lane == 0) rescale_s[wave] = any != 0ull;
-        }
-        __syncthreads();
-
-        // ---- PV: this wave's 128 output columns for the group's heads
-        {
-#pragma unroll
-            for (int ht = 0; ht < kNht; ++ht) {
-                if (rescale_s[ht]) {
-                    const float4 al = *reinterpret_cast<const float4*>(&alpha_s[16 * ht + 4 * g]);
-#pragma unroll
-                    for (int dt = 0; dt < kDt; ++dt) {
-                        o[ht][dt][0] *= al.x; o[ht][dt][1] *= al.y;
-                        o[ht][dt][2] *= al.z; o[ht][dt][3] *= al.w;
-                    }
-                }
-            }
-            v8bf pa[kNht];
-#pragma unroll
-            for (int ht = 0; ht < kNht; ++ht) pa[ht] = *reinterpret_cast<const v8bf*>(&pbuf[ht][lane][0]);
-#pragma unroll
-            for (int dt = 0; dt < kDt; ++dt) {
-                const int d = 128 * wave + 16 * dt + n;
-                const int chunk = d >> 3;
-                const int sub = (d & 7) * 2;
-                v8s tmp;
-#pragma unroll
-                for (int j = 0; j < 8; ++j) {
-                    const int key = (j >> 2) * 16 + 4 * g + (j & 3);
-                    tmp[j] = *reinterpret_cast<const short*>(
-                        kb + key * kRowBytes + swz_chunk(key, chunk) * 16 + sub);
-                }
-                const v8bf vb = __builtin_bit_cast(v8bf, tmp);
-#pragma unroll
-                for (int ht = 0; ht < kNht; ++ht) o[ht][dt] = mfma_bf16_16x16x32(pa[ht], vb, o[ht][dt]);
-            }
-        }
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-        __syncthreads();
+    for (int t4 = 0; t4 < n_tiles; t4 += 4) {
+        mla_tile<NHT, 0, 3>(st, lat_b, t4, n_tiles, scale_log2, wave, lane);
+        if (t4 + 1 < n_tiles) mla_tile<NHT, 1, 0>(st, lat_b, t4 + 1, n_tiles, scale_log2, wave, lane);
+        if (t4 + 2 < n_tiles) mla_tile<NHT, 2, 1>(st, lat_b, t4 + 2, n_tiles, scale_log2, wave, lane);
+        if (t4 + 3 < n_tiles) mla_tile<NHT, 3, 2>(st, lat_b, t4 + 3, n_tiles, scale_log2, wave, lane);
     }
 
     // ---- epilogue: normalise, then write the final row or this split's partial
-    if (g == 0) {
-        m_s[16 * wave + n] = m_run;
-        l_s[16 * wave + n] = l_run;
+    if (wave < NHT && g == 0) {
+        g_l[16 * wave + n] = st.l_run;
+        g_m[16 * wave + n] = st.m_run;
     }
     __syncthreads();
 #pragma unroll
-    for (int ht = 0; ht < kNht; ++ht) {
+    for (int h = 0; h < NHT; ++h) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            const int hl = 16 * ht + 4 * g + i;
-            const int head = head0 + hl;
-            const float l = l_s[hl];
+            const int head = 16 * h + 4 * g + i;
+            const float l = g_l[head];
             const float inv = l > 0.f ? 1.f / l : 0.f;
 #pragma unroll
-            for (int dt = 0; dt < kDt; ++dt) {
-                const int d = 128 * wave + 16 * dt + n;
-                const float v = o[ht][dt][i] * inv;
+            for (int dt = 0; dt < kDtW; ++dt) {
+                const int d = 64 * wave + 16 * dt + n;
+                const uint16_t v = f32_to_bf16(st.o[h][dt][i] * inv);
                 if (n_splits == 1)
-                    out[(static_cast<size_t>(row) * H + head) * kDv + d] = f32_to_bf16(v);
+                    out[(static_cast<size_t>(row) * H + head) * kDv + d] = v;
                 else
                     part_o[((static_cast<size_t>(row) * n_splits + split) * H + head) * kDv + d] = v;
             }
         }
     }
-    if (threadIdx.x < kHeadsPerGroup) {
-        const int hl = threadIdx.x;
-        const int head = head0 + hl;
-        const float l = l_s[hl];
-        const float lse2 = l > 0.f ? m_s[hl] + log2f(l) : -INFINITY;
+    if (threadIdx.x < H) {
+        const int head = threadIdx.x;
+        const float l = g_l[head];
+        const float lse2 = l > 0.f ? g_m[head] + log2f(l) : -INFINITY;
         if (n_splits == 1) {
             if (lse) lse[static_cast<size_t>(row) * H + head] = lse2 * kLn2;
         } else {
@@ -372,9 +471,10 @@ void mla_decode_mfma_kernel(const uint16_t* __restrict__ q, const uint16_t* __re
     }
 }
 
-// Merge the splits of each (row, head): weights 2^(lse_s - max), output in bf16.
+// Merge the splits of each (row, head): split s holds its own normalised output (bf16)
+// and its log2-sum-exp; weights are 2^(lse_s - max).  One thread owns 4 columns.
 __global__ __launch_bounds__(256)
-void mla_combine_kernel(const float* __restrict__ part_o, const float* __restrict__ part_lse,
+void mla_combine_kernel(const uint16_t* __restrict__ part_o, const float* __restrict__ part_lse,
                         int rows, int H, int n_splits, uint16_t* __restrict__ out,
                         float* __restrict__ lse)
 {
@@ -385,37 +485,41 @@ void mla_combine_kernel(const float* __restrict__ part_o, const float* __restric
     const size_t rh = gid / (kDv / 4);
     const int h = static_cast<int>(rh % H);
     const size_t row = rh / H;
+    float ls[8];
     float M = -INFINITY;
-    for (int s = 0; s < n_splits; ++s) M = fmaxf(M, part_lse[(row * n_splits + s) * H + h]);
+    for (int s = 0; s < n_splits; ++s) {
+        ls[s] = part_lse[(row * n_splits + s) * H + h];
+        M = fmaxf(M, ls[s]);
+    }
     float W = 0.f;
-    float4 acc = {0.f, 0.f, 0.f, 0.f};
+    float acc[4] = {0.f, 0.f, 0.f, 0.f};
     if (M != -INFINITY) {
         for (int s = 0; s < n_splits; ++s) {
-            const float ls = part_lse[(row * n_splits + s) * H + h];
-            if (ls == -INFINITY) continue;
-            const float wgt = exp2f(ls - M);
+            if (ls[s] == -INFINITY) continue;
+            const float wgt = exp2f(ls[s] - M);
             W += wgt;
-            const float4 v = *reinterpret_cast<const float4*>(
+            const uint2 v = *reinterpret_cast<const uint2*>(
                 part_o + ((row * n_splits + s) * H + h) * kDv + 4 * d4);
-            acc.x += wgt * v.x; acc.y += wgt * v.y; acc.z += wgt * v.z; acc.w += wgt * v.w;
+            acc[0] += wgt * bf16_to_f32(static_cast<uint16_t>(v.x & 0xffffu));
+            acc[1] += wgt * bf16_to_f32(static_cast<uint16_t>(v.x >> 16));
+            acc[2] += wgt * bf16_to_f32(static_cast<uint16_t>(v.y & 0xffffu));
+            acc[3] += wgt * bf16_to_f32(static_cast<uint16_t>(v.y >> 16));
         }
     }
     const float inv = W > 0.f ? 1.f / W : 0.f;
-    uint16_t* o = out + (row * H + h) * kDv + 4 * d4;
-    o[0] = f32_to_bf16(acc.x * inv);
-    o[1] = f32_to_bf16(acc.y * inv);
-    o[2] = f32_to_bf16(acc.z * inv);
-    o[3] = f32_to_bf16(acc.w * inv);
+    uint2 o;
+    o.x = f32_to_bf16(acc[0] * inv) | (static_cast<uint32_t>(f32_to_bf16(acc[1] * inv)) << 16);
+    o.y = f32_to_bf16(acc[2] * inv) | (static_cast<uint32_t>(f32_to_bf16(acc[3] * inv)) << 16);
+    *reinterpret_cast<uint2*>(out + (row * H + h) * kDv + 4 * d4) = o;
     if (lse && d4 == 0) lse[row * H + h] = W > 0.f ? (M + log2f(W)) * kLn2 : -INFINITY;
 }
 
-int mla_splits(int rows, int H, int k) {
-    // enough (row, split, head group) blocks to give every CU one workgroup
+int mla_splits(int rows, int k) {
+    // enough (row, split) workgroups to give every CU one, within the LDS slot limit
     const int n_tiles = (k + kKt - 1) / kKt;
-    const int per_split = rows * (H / kHeadsPerGroup);
-    int s = per_split >= 256 ? 1 : (256 + per_split - 1) / per_split;
+    int s = rows >= 256 ? 1 : (256 + rows - 1) / rows;
     s = min(s, 8);
-    const int min_s = (n_tiles * kKt + kMaxSlots - 1) / kMaxSlots;   // slots per split fit LDS
+    const int min_s = (n_tiles * kKt + kMaxSlots - 1) / kMaxSlots;
     s = max(s, min_s);
     s = min(s, n_tiles);
     return max(s, 1);
@@ -431,14 +535,14 @@ hipError_t launch_sparse_attn_generic(const SparseAttnArgs& a, hipStream_t strea
 }
 
 bool mla_decode_mfma_supported(int H, int Dv, int Dr, int bf16) {
-    return bf16 && Dv == kDv && Dv + Dr == kDq && H >= kHeadsPerGroup && H % kHeadsPerGroup == 0;
+    return bf16 && Dv == kDv && Dv + Dr == kDq && (H == 64 || H == 128);
 }
 
 size_t mla_decode_workspace_bytes(int B, int T, int H, int, int k) {
     const int rows = B * T;
-    const int s = mla_splits(rows, H, k);
+    const int s = mla_splits(rows, k);
     if (s == 1) return 0;
-    return static_cast<size_t>(rows) * s * H * (kDv + 1) * sizeof(float) + 256;
+    return static_cast<size_t>(rows) * s * H * (kDv * sizeof(uint16_t) + sizeof(float)) + 256;
 }
 
 hipError_t launch_mla_decode_mfma(const void* q, const void* latent, const int32_t* idx,
@@ -446,26 +550,28 @@ hipError_t launch_mla_decode_mfma(const void* q, const void* latent, const int32
                                   float sm_scale, void* out, float* lse, void* ws,
                                   hipStream_t stream) {
     const int rows = B * T;
-    const int s = mla_splits(rows, H, k);
+    const int s = mla_splits(rows, k);
     const int n_tiles = (k + kKt - 1) / kKt;
     const int tps = (n_tiles + s - 1) / s;
-    const int n_units = rows * s;
-    const int n_groups = H / kHeadsPerGroup;
-    // units are dealt to the 8 XCD slots; pad so every slot has the same block count
-    const int units_per_xcd = (n_units + kXcds - 1) / kXcds;
-    const int blocks = units_per_xcd * n_groups * kXcds;
-    float* part_o = static_cast<float*>(ws);
-    float* part_lse = s > 1 ? part_o + static_cast<size_t>(rows) * s * H * kDv : nullptr;
+    uint16_t* part_o = static_cast<uint16_t*>(ws);
+    float* part_lse = s > 1 ? reinterpret_cast<float*>(part_o + static_cast<size_t>(rows) * s * H * kDv)
+                            : nullptr;
     const float scale_log2 = sm_scale * kLog2e;
-    hipLaunchKernelGGL(mla_decode_mfma_kernel, dim3(blocks), dim3(kMlaThreads), 0, stream,
-                       static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(latent), idx,
-                       len, T, H, Lmax, k, tps, s, n_units, scale_log2,
-                       static_cast<uint16_t*>(out), lse, part_o, part_lse);
+    auto qp = static_cast<const uint16_t*>(q);
+    auto lp = static_cast<const uint16_t*>(latent);
+    auto op = static_cast<uint16_t*>(out);
+    if (H == 128)
+        hipLaunchKernelGGL(mla_decode_mfma_kernel<8>, dim3(rows * s), dim3(kMlaThreads), 0, stream,
+                           qp, lp, idx, len, T, Lmax, k, tps, s, scale_log2, op, lse, part_o, part_lse);
+    else
+        hipLaunchKernelGGL(mla_decode_mfma_kernel<4>, dim3(rows * s), dim3(kMlaThreads), 0, stream,
+                           qp, lp, idx, len, T, Lmax, k, tps, s, scale_log2, op, lse, part_o, part_lse);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || s == 1) return e;
     const size_t total = static_cast<size_t>(rows) * H * (kDv / 4);
+    prof_mark(stream, kPhaseCombine);
     hipLaunchKernelGGL(mla_combine_kernel, dim3((total + 255) / 256), dim3(256), 0, stream,
-                       part_o, part_lse, rows, H, s, static_cast<uint16_t*>(out), lse);
+                       part_o, part_lse, rows, H, s, op, lse);
     return hipGetLastError();
 }
 

@@ -168,6 +168,21 @@ size_t dsa_layer_step_workspace_bytes(const dsa_layer_args* a);
 dsa_status dsa_layer_step(const dsa_layer_args* a, void* ws, size_t ws_bytes,
                           hipStream_t stream);
 
+/*
+ * Tracing aid: HIP-event timing of the phases of dsa_layer_step.
+ *   dsa_profile_begin(max_steps) creates (max_steps * 5) HIP events (host-side objects,
+ *   no device memory) and makes every following dsa_layer_step record an event on its
+ *   stream before each phase and one at its end.  Phases: 0 index scores, 1 top-k,
+ *   2 sparse attention (main kernel), 3 split combine (only when the attention splits
+ *   its k slots).  Steps beyond max_steps are not recorded.
+ *   dsa_profile_end(ms_total[4], counts[4]) waits for the last recorded event, returns
+ *   the summed elapsed milliseconds and the number of timed instances of each phase,
+ *   and destroys the events.  Process-wide state: not for concurrent use from several
+ *   threads or streams.
+ */
+dsa_status dsa_profile_begin(int max_steps);
+dsa_status dsa_profile_end(double* ms_total, int* counts);
+
 #ifdef __cplusplus
 }
 #endif
