@@ -136,14 +136,19 @@ dsa_status check_mha_args(const void* q, const void* k, const void* v, const int
                 "sparse_mla_prefill: B*T*H too large");
     DSA_REQUIRE(aligned16(q) && aligned16(k) && aligned16(v) && aligned16(idx) && aligned16(out),
                 DSA_ERR_ALIGN, "sparse_mla_prefill: pointers must be 16-byte aligned");
-    DSA_REQUIRE(sizeof(float) * (static_cast<size_t>(Dqk) + topk) <= kGenericLdsLimit, DSA_ERR_SHAPE,
-                "sparse_mla_prefill: k=%d too large for this shape", topk);
+    if (!dsa::mha_prefill_mfma_supported(Dqk, Dv, dt == DSA_BF16))
+        DSA_REQUIRE(sizeof(float) * (static_cast<size_t>(Dqk) + topk) <= kGenericLdsLimit, DSA_ERR_SHAPE,
+                    "sparse_mla_prefill: k=%d too large for this shape", topk);
     return DSA_OK;
 }
 
 dsa_status launch_mha(const void* q, const void* k, const void* v, const int32_t* idx, int B, int T,
                       int H, int Dqk, int Dv, int topk, float sm_scale, dsa_dtype dt, void* out,
-                      float* lse, void*, hipStream_t stream) {
+                      float* lse, void* ws, hipStream_t stream) {
+    if (dsa::mha_prefill_mfma_supported(Dqk, Dv, dt == DSA_BF16))
+        return hip_status(dsa::launch_mha_prefill_mfma(q, k, v, idx, B, T, H, topk, sm_scale, out, lse,
+                                                       ws, stream),
+                          "sparse_mla_prefill");
     dsa::SparseAttnArgs a{};
     a.q = q;
     a.kbase = k;
@@ -162,7 +167,10 @@ dsa_status launch_mha(const void* q, const void* k, const void* v, const int32_t
     return hip_status(dsa::launch_sparse_attn_generic(a, stream), "sparse_mla_prefill");
 }
 
-size_t mha_ws(int, int, int, int, int, int, dsa_dtype) { return 0; }
+size_t mha_ws(int B, int T, int, int Dqk, int Dv, int, dsa_dtype dt) {
+    if (dsa::mha_prefill_mfma_supported(Dqk, Dv, dt == DSA_BF16)) return dsa::mha_prefill_workspace_bytes(B, T);
+    return 0;
+}
 
 // Event timing of dsa_layer_step phases (dsa_profile_begin / dsa_profile_end).
 struct Profiler {

@@ -66,4 +66,11 @@ hipError_t launch_mla_decode_mfma(const void* q, const void* latent, const int32
                                   float sm_scale, void* out, float* lse, void* ws,
                                   hipStream_t stream);
 
+// Matrix-core path of the MHA prefill form (bf16, Dqk = 192, Dv = 128).
+bool mha_prefill_mfma_supported(int Dqk, int Dv, int bf16);
+size_t mha_prefill_workspace_bytes(int B, int T);
+hipError_t launch_mha_prefill_mfma(const void* q, const void* k, const void* v, const int32_t* idx,
+                                   int B, int T, int H, int topk, float sm_scale, void* out,
+                                   float* lse, void* ws, hipStream_t stream);
+
 }  // namespace dsa

@@ -58,6 +58,7 @@ def _load():
         lib.orc_sparse_mla_decode.argtypes = [P, P, P, P, I, I, I, I, I, I, I, I, D, P, P]
         lib.orc_sparse_mha_prefill.argtypes = [P, P, P, P, I, I, I, I, I, I, I, D, P, P]
         lib.orc_sparse_mha_prefill_dense.argtypes = [P, P, P, P, I, I, I, I, I, I, I, D, P, P]
+        lib.orc_sparse_mha_prefill_rows.argtypes = [P, P, P, P, I, I, I, I, I, I, I, D, P, P, I, P, P]
         lib.orc_layer_step_latent.argtypes = [P, P, P, P, P, P, I, I, I, I, I, D, I,
                                               P, P, I, I, I, I, D, P, P, P, P]
         lib.orc_layer_step_mha.argtypes = [P, P, P, P, P, I, I, I, I, D, I,
@@ -65,6 +66,7 @@ def _load():
         lib.orc_max_threads.argtypes = []
         for fn in (lib.orc_index_scores, lib.orc_topk, lib.orc_sparse_mla_decode,
                    lib.orc_sparse_mha_prefill, lib.orc_sparse_mha_prefill_dense,
+                   lib.orc_sparse_mha_prefill_rows,
                    lib.orc_layer_step_latent, lib.orc_layer_step_mha, lib.orc_max_threads):
             fn.restype = I
         _lib = lib
@@ -174,6 +176,29 @@ def _mha(fn, q, k_, v, idx, sm_scale):
 def sparse_mha_prefill(q, k_, v, idx, sm_scale):
     """Gather-form sparse MHA over selected and causally visible keys."""
     return _mha(_load().orc_sparse_mha_prefill, q, k_, v, idx, sm_scale)
+
+
+def sparse_mha_prefill_rows(q, k_, v, idx, sm_scale, rows):
+    """Gather-form sparse MHA for the listed query rows [(b, t), ...] only.
+    Returns (out[R,H,Dv] f64, lse[R,H] f64)."""
+    B, T, H, Dqk = q.shape
+    Dv = v.shape[-1]
+    topk_ = idx.shape[-1]
+    q, dt = _attn_array(q)
+    k_, dt2 = _attn_array(k_)
+    v, dt3 = _attn_array(v)
+    assert dt == dt2 == dt3
+    idx, pi = _c(idx, np.int32)
+    rb, prb = _c(np.array([r[0] for r in rows]), np.int32)
+    rt, prt = _c(np.array([r[1] for r in rows]), np.int32)
+    out = np.empty((len(rows), H, Dv), np.float64)
+    lse = np.empty((len(rows), H), np.float64)
+    _check(_load().orc_sparse_mha_prefill_rows(
+        q.ctypes.data_as(ctypes.c_void_p), k_.ctypes.data_as(ctypes.c_void_p),
+        v.ctypes.data_as(ctypes.c_void_p), pi, dt, B, T, H, Dqk, Dv, topk_, float(sm_scale),
+        prb, prt, len(rows), out.ctypes.data_as(ctypes.c_void_p),
+        lse.ctypes.data_as(ctypes.c_void_p)), "sparse_mha_prefill_rows")
+    return out, lse
 
 
 def sparse_mha_prefill_dense(q, k_, v, idx, sm_scale):

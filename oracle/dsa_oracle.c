@@ -233,7 +233,45 @@ int orc_sparse_mla_decode(const void* q, const void* latent, const int32_t* idx,
  * keys and values are the chunk's own T positions, per head.  Row t attends over
  * the selected positions that are also causally visible (s <= t):
  *   l_s = sm_scale * q[b,t,h,:] . k[b,s,h,:],  out = sum_s softmax(l)_s v[b,s,h,:].
- * Gather form: loop over the selected list only. */
+ * Gather form: loop over the selected list only.  One query row (b,t), all heads;
+ * out points at that row's [H,Dv] block, lse at its [H] block (may be NULL). */
+static void mha_row(const void* q, const void* kk, const void* v, const int32_t* idx, int dtype,
+                    int b, int t, int T, int H, int Dqk, int Dv, int k, double sm_scale,
+                    double* out_row, double* lse_row)
+{
+    const size_t row = (size_t)b * T + t;
+    const int32_t* sel = idx + row * (size_t)k;
+    double* logit = (double*)malloc(sizeof(double) * (size_t)k);
+    int32_t* keys = (int32_t*)malloc(sizeof(int32_t) * (size_t)k);
+    int n = 0;
+    for (int j = 0; j < k; ++j)
+        if (sel[j] >= 0 && sel[j] <= t) keys[n++] = sel[j];
+    for (int h = 0; h < H; ++h) {
+        const size_t qoff = (row * H + h) * (size_t)Dqk;
+        double* o = out_row + (size_t)h * Dv;
+        double m = -INFINITY, sum = 0.0;
+        for (int j = 0; j < n; ++j) {
+            const size_t koff = (((size_t)b * T + keys[j]) * H + h) * (size_t)Dqk;
+            double dot = 0.0;
+            for (int d = 0; d < Dqk; ++d)
+                dot += load_elem(q, dtype, qoff + d) * load_elem(kk, dtype, koff + d);
+            logit[j] = sm_scale * dot;
+            if (logit[j] > m) m = logit[j];
+        }
+        for (int d = 0; d < Dv; ++d) o[d] = 0.0;
+        if (n == 0) { if (lse_row) lse_row[h] = -INFINITY; continue; }
+        for (int j = 0; j < n; ++j) sum += exp(logit[j] - m);
+        for (int j = 0; j < n; ++j) {
+            const double p = exp(logit[j] - m) / sum;
+            const size_t voff = (((size_t)b * T + keys[j]) * H + h) * (size_t)Dv;
+            for (int d = 0; d < Dv; ++d) o[d] += p * load_elem(v, dtype, voff + d);
+        }
+        if (lse_row) lse_row[h] = m + log(sum);
+    }
+    free(logit);
+    free(keys);
+}
+
 int orc_sparse_mha_prefill(const void* q, const void* kk, const void* v, const int32_t* idx,
                            int dtype, int B, int T, int H, int Dqk, int Dv, int k,
                            double sm_scale, double* out, double* lse)
@@ -246,38 +284,32 @@ int orc_sparse_mha_prefill(const void* q, const void* kk, const void* v, const i
     for (b = 0; b < B; ++b) {
         for (int t = 0; t < T; ++t) {
             const size_t row = (size_t)b * T + t;
-            const int32_t* sel = idx + row * (size_t)k;
-            double* logit = (double*)malloc(sizeof(double) * (size_t)k);
-            int32_t* keys = (int32_t*)malloc(sizeof(int32_t) * (size_t)k);
-            int n = 0;
-            for (int j = 0; j < k; ++j)
-                if (sel[j] >= 0 && sel[j] <= t) keys[n++] = sel[j];
-            for (int h = 0; h < H; ++h) {
-                const size_t qoff = (row * H + h) * (size_t)Dqk;
-                double* o = out + (row * H + h) * (size_t)Dv;
-                double m = -INFINITY, sum = 0.0;
-                for (int j = 0; j < n; ++j) {
-                    const size_t koff = (((size_t)b * T + keys[j]) * H + h) * (size_t)Dqk;
-                    double dot = 0.0;
-                    for (int d = 0; d < Dqk; ++d)
-                        dot += load_elem(q, dtype, qoff + d) * load_elem(kk, dtype, koff + d);
-                    logit[j] = sm_scale * dot;
-                    if (logit[j] > m) m = logit[j];
-                }
-                for (int d = 0; d < Dv; ++d) o[d] = 0.0;
-                if (n == 0) { if (lse) lse[row * H + h] = -INFINITY; continue; }
-                for (int j = 0; j < n; ++j) sum += exp(logit[j] - m);
-                for (int j = 0; j < n; ++j) {
-                    const double p = exp(logit[j] - m) / sum;
-                    const size_t voff = (((size_t)b * T + keys[j]) * H + h) * (size_t)Dv;
-                    for (int d = 0; d < Dv; ++d) o[d] += p * load_elem(v, dtype, voff + d);
-                }
-                if (lse) lse[row * H + h] = m + log(sum);
-            }
-            free(logit);
-            free(keys);
+            mha_row(q, kk, v, idx, dtype, b, t, T, H, Dqk, Dv, k, sm_scale,
+                    out + row * H * (size_t)Dv, lse ? lse + row * H : NULL);
         }
     }
+    return ORC_OK;
+}
+
+/* The same gather form for a list of query rows (b, t) = (rows_b[r], rows_t[r]) only;
+ * out [n_rows,H,Dv], lse [n_rows,H].  Lets large chunks be checked on sampled rows. */
+int orc_sparse_mha_prefill_rows(const void* q, const void* kk, const void* v, const int32_t* idx,
+                                int dtype, int B, int T, int H, int Dqk, int Dv, int k,
+                                double sm_scale, const int32_t* rows_b, const int32_t* rows_t,
+                                int n_rows, double* out, double* lse)
+{
+    int r;
+    for (r = 0; r < n_rows; ++r)
+        if (rows_b[r] < 0 || rows_b[r] >= B || rows_t[r] < 0 || rows_t[r] >= T) return ORC_ERR_SHAPE;
+    for (r = 0; r < n_rows; ++r) {
+        const int32_t* sel = idx + ((size_t)rows_b[r] * T + rows_t[r]) * k;
+        for (int j = 0; j < k; ++j)
+            if (sel[j] < -1 || sel[j] >= T) return ORC_ERR_INDEX;
+    }
+#pragma omp parallel for schedule(dynamic)
+    for (r = 0; r < n_rows; ++r)
+        mha_row(q, kk, v, idx, dtype, rows_b[r], rows_t[r], T, H, Dqk, Dv, k, sm_scale,
+                out + (size_t)r * H * Dv, lse ? lse + (size_t)r * H : NULL);
     return ORC_OK;
 }
 

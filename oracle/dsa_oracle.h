@@ -35,6 +35,11 @@ int orc_sparse_mha_prefill(const void* q, const void* kk, const void* v, const i
                            int dtype, int B, int T, int H, int Dqk, int Dv, int k,
                            double sm_scale, double* out, double* lse);
 
+int orc_sparse_mha_prefill_rows(const void* q, const void* kk, const void* v, const int32_t* idx,
+                                int dtype, int B, int T, int H, int Dqk, int Dv, int k,
+                                double sm_scale, const int32_t* rows_b, const int32_t* rows_t,
+                                int n_rows, double* out, double* lse);
+
 int orc_sparse_mha_prefill_dense(const void* q, const void* kk, const void* v,
                                  const int32_t* idx, int dtype, int B, int T, int H, int Dqk,
                                  int Dv, int k, double sm_scale, double* out, double* lse);

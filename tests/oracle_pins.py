@@ -299,6 +299,11 @@ def pin_mha_prefill_library(o):
     sm = Dqk ** -0.5
     out, lse = o.sparse_mha_prefill(q, kk, v, idx, sm)
     out_d, lse_d = o.sparse_mha_prefill_dense(q, kk, v, idx, sm)
+    rows = [(0, 11), (0, 0), (0, 5)]
+    out_r, lse_r = o.sparse_mha_prefill_rows(q, kk, v, idx, sm, rows)
+    for i, (b, t) in enumerate(rows):
+        np.testing.assert_array_equal(out_r[i], out[b, t])
+        np.testing.assert_array_equal(lse_r[i], lse[b, t])
     np.testing.assert_allclose(out, out_d, rtol=1e-12, atol=1e-14)
     np.testing.assert_allclose(lse, lse_d, rtol=1e-12)
     for t in range(T):

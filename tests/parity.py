@@ -84,9 +84,10 @@ def check_attention(out_g, lse_g, out_o, lse_o, dtype: str):
     i = np.unravel_index(np.argmax(err), err.shape)
     assert err.max() <= ATTN_ATOL[dtype], f"attention max abs err {err.max()} at {i}"
     if lse_g is not None:
-        lerr = np.abs(np.asarray(lse_g, np.float64) - lse_o)
+        lse_g = np.asarray(lse_g, np.float64)
         fin = np.isfinite(lse_o)
         assert np.array_equal(fin, np.isfinite(lse_g)), "lse -inf pattern differs"
         if fin.any():
-            assert lerr[fin].max() <= LSE_ATOL[dtype], f"lse max abs err {lerr[fin].max()}"
+            lerr = np.abs(lse_g[fin] - lse_o[fin])
+            assert lerr.max() <= LSE_ATOL[dtype], f"lse max abs err {lerr.max()}"
     return float(err.max())

@@ -67,11 +67,16 @@ def test_attention_validation_and_workspace(lib):
     st = lib.dsa_sparse_mla_decode(p, p, p, p, 2, 1, 128, 512, 64, 4096, 2048, 0.1, 7, p, None,
                                    None, 0, None)
     assert st == 3
-    assert lib.dsa_sparse_mla_decode_workspace_bytes(256, 1, 128, 512, 64, 2048, N.DSA_BF16) == 0
-    # generic path: logits of all k slots must fit in LDS
-    st = lib.dsa_sparse_mla_prefill(p, p, p, p, 1, 8, 2, 192, 128, 1 << 15, 0.1, N.DSA_BF16, p,
+    assert lib.dsa_sparse_mla_decode_workspace_bytes(256, 1, 128, 512, 64, 1024, N.DSA_BF16) == 0
+    # generic (f32) path: logits of all k slots must fit in LDS
+    st = lib.dsa_sparse_mla_prefill(p, p, p, p, 1, 8, 2, 192, 128, 1 << 15, 0.1, N.DSA_F32, p,
                                     None, None, 0, None)
     assert st == 2
+    # matrix-core (bf16 192/128) path: needs the selection-mask workspace
+    assert lib.dsa_sparse_mla_prefill_workspace_bytes(1, 8192, 128, 192, 128, 2048, N.DSA_BF16) >= 8192 * 256 * 4
+    st = lib.dsa_sparse_mla_prefill(p, p, p, p, 1, 8, 2, 192, 128, 1 << 15, 0.1, N.DSA_BF16, p,
+                                    None, None, 0, None)
+    assert st == 5
 
 
 def test_layer_step_validation(lib):

@@ -265,3 +265,25 @@ def test_layer_step_deterministic(dsa):
     torch.cuda.synchronize()
     assert torch.equal(i1, s1.idx)
     assert torch.equal(o1, o2)
+
+
+@pytest.mark.parametrize("T,H,k", [(200, 2, 48), (130, 3, 130), (64, 1, 1)])
+def test_sparse_mla_prefill_blocks(dsa, orc, T, H, k):
+    """Several 64-row query blocks and key blocks, a ragged tail, k >= T (dense causal)
+    and k = 1."""
+    _say(f"[sparse_mla_prefill bf16 blocks] T={T} H={H} k={k}")
+    rng = np.random.default_rng(T * 7 + H)
+    B, Dqk, Dv = 2, 192, 128
+    q = S.to_bf16_bits(rng.standard_normal((B, T, H, Dqk), dtype=np.float32))
+    kk = S.to_bf16_bits(rng.standard_normal((B, T, H, Dqk), dtype=np.float32))
+    v = S.to_bf16_bits(rng.standard_normal((B, T, H, Dv), dtype=np.float32))
+    idx = np.full((B, T, k), -1, np.int32)
+    for b in range(B):
+        for t in range(T):
+            m = min(k, t + 1)
+            idx[b, t, :m] = rng.choice(t + 1, size=m, replace=False)
+    tt = lambda a: torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).cuda()
+    out, lse = dsa.sparse_mla_prefill(tt(q), tt(kk), tt(v), torch.from_numpy(idx).cuda(), Dqk ** -0.5)
+    torch.cuda.synchronize()
+    ro, rl = orc.sparse_mha_prefill(q, kk, v, idx, Dqk ** -0.5)
+    check_attention(_np_out(out), lse.cpu().numpy(), ro, rl, "bf16")

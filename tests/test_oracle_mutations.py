@@ -54,6 +54,7 @@ def _variant(orc, path):
     lib = ctypes.CDLL(path)
     for fn in ("orc_e4m3fn_value", "orc_bf16_value", "orc_index_scores", "orc_topk",
                "orc_sparse_mla_decode", "orc_sparse_mha_prefill", "orc_sparse_mha_prefill_dense",
+               "orc_sparse_mha_prefill_rows",
                "orc_layer_step_latent", "orc_layer_step_mha", "orc_max_threads"):
         getattr(lib, fn).argtypes = getattr(saved, fn).argtypes
         getattr(lib, fn).restype = getattr(saved, fn).restype
