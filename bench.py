@@ -31,6 +31,7 @@ BF16_PEAK_TFLOPS = 2500.0        # MI355X dense bf16 MFMA, published
 METRIC = "DSA decode layer-steps/s and indexer keys scored/s; % of HBM/MFMA roofline"
 ATTN_SOURCE = os.path.join(ROOT, "deepseek_dsa_indexer_amd", "csrc", "sparse_attn.hip")
 INDEX_SOURCE = os.path.join(ROOT, "deepseek_dsa_indexer_amd", "csrc", "index_scores.hip")
+PREFILL_SOURCE = os.path.join(ROOT, "deepseek_dsa_indexer_amd", "csrc", "sparse_mha_prefill.hip")
 
 
 def _sha(path: str) -> str:
@@ -41,10 +42,13 @@ def _sha(path: str) -> str:
 def algorithmic_costs(cfg, lens):
     """Bytes and flops the method must move / execute per step, per phase.
 
-    Indexer: 132 B (128 FP8 + 4 B scale) and 2*H_I*d_I flops per visible (row, key),
-    plus the row's q (H_I*d_I B), weights and q scales (8*H_I B).  Attention: 1152 B
-    (576 bf16) per selected latent row, shared by all heads, 2*H*(576+512) flops per
-    (head, selected row), plus the row's q (H*576*2 B) and output (H*512*2 B)."""
+    Indexer: every sequence's K-cache once, 132 B (128 FP8 + 4 B scale) per cached key,
+    plus each row's q (H_I*d_I B), weights and q scales (8*H_I B); 2*H_I*d_I flops per
+    visible (row, key).  Latent attention: 1152 B (576 bf16) per selected latent row,
+    shared by all heads, 2*H*(576+512) flops per (head, selected row), plus the row's
+    q (H*576*2 B) and output (H*512*2 B).  MHA attention: the chunk's K and V once
+    (H*(Dqk+Dv)*2 B per key), q and output, and 2*H*(Dqk+Dv) flops per (head,
+    selected row)."""
     import dsa_synth as S
     T = cfg.T
     keys = S.visible_keys(cfg, lens)
@@ -53,11 +57,15 @@ def algorithmic_costs(cfg, lens):
     for L in lens:
         for t in range(T):
             sel += min(cfg.k, int(L) - T + t + 1)
-    idx_bytes = keys * (cfg.D_I + 4) + rows * (cfg.H_I * cfg.D_I + 8 * cfg.H_I)
+    cached = int(sum(min(int(L), cfg.Lmax) for L in lens))
+    idx_bytes = cached * (cfg.D_I + 4) + rows * (cfg.H_I * cfg.D_I + 8 * cfg.H_I)
     idx_flops = keys * 2 * cfg.H_I * cfg.D_I
-    row_bytes = cfg.Dq * 2
-    att_bytes = sel * row_bytes + rows * (cfg.H * cfg.Dq * 2 + cfg.H * cfg.Dv * 2)
-    att_flops = sel * 2 * cfg.H * (cfg.Dq + cfg.Dv)
+    if cfg.form == "latent":
+        att_bytes = sel * cfg.Dq * 2 + rows * (cfg.H * cfg.Dq * 2 + cfg.H * cfg.Dv * 2)
+        att_flops = sel * 2 * cfg.H * (cfg.Dq + cfg.Dv)
+    else:
+        att_bytes = rows * cfg.H * (cfg.Dqk + cfg.Dv) * 2 + rows * cfg.H * (cfg.Dqk + cfg.Dv) * 2
+        att_flops = sel * 2 * cfg.H * (cfg.Dqk + cfg.Dv)
     return dict(keys=keys, selected=sel, index_bytes=idx_bytes, index_flops=idx_flops,
                 attention_bytes=att_bytes, attention_flops=att_flops)
 
@@ -82,30 +90,63 @@ def read_traffic(kernel: str, workload: str, source: str):
         return None
 
 
-def cpu_baseline(cfg, n_seqs: int):
+def cpu_baseline(cfg, n_seqs: int, min_seconds: float = 10.0):
+    """The oracle, untuned, on a bounded sample of the same workload, scaled to a step.
+
+    Decode: the whole layer step for the first ``n_seqs`` sequences.  Chunked prefill
+    (one sequence): ``4 * n_seqs`` query rows spread evenly over the chunk, each scored
+    against its causal keys, selected and attended; the step is T rows.  The sample is
+    repeated until ``min_seconds`` of wall time have accumulated."""
     import numpy as np
 
     import dsa_synth as S
     import oracle as orc
     orc.build(force=False)
-    seqs = list(range(min(n_seqs, cfg.B)))
-    c = S.make_case(cfg, seqs=seqs)
-    t0 = time.perf_counter()
     if cfg.form == "latent":
-        orc.layer_step_latent(c["q_i"], c["q_scale"], c["w"], c["k_i"], c["k_scale"], c["lens"],
-                              cfg.sm_scale_i, cfg.k, c["q"], c["latent"], cfg.Dv, cfg.sm_scale)
+        seqs = list(range(min(n_seqs, cfg.B)))
+        c = S.make_case(cfg, seqs=seqs)
+
+        def once():
+            orc.layer_step_latent(c["q_i"], c["q_scale"], c["w"], c["k_i"], c["k_scale"],
+                                  c["lens"], cfg.sm_scale_i, cfg.k, c["q"], c["latent"], cfg.Dv,
+                                  cfg.sm_scale)
+        frac = len(seqs) / cfg.B
+        keys = float(np.sum(c["lens"]))
+        threads = min(orc.max_threads(), len(seqs) * cfg.T)
+        sample = (f"{len(seqs)} of {cfg.B} sequences of the same workload (full index scan, "
+                  f"top-k and attention per sequence), scaled by {cfg.B}/{len(seqs)}")
     else:
-        orc.layer_step_mha(c["q_i"], c["q_scale"], c["w"], c["k_i"], c["k_scale"], cfg.sm_scale_i,
-                           cfg.k, c["q"], c["k"], c["v"], cfg.sm_scale)
-    dt = time.perf_counter() - t0
-    frac = len(seqs) / cfg.B
-    rows = len(seqs) * cfg.T
-    return {"value": frac / dt, "unit": "layer-steps/s", "cores": min(orc.max_threads(), rows),
-            "kind": "oracle",
-            "sample": f"{len(seqs)} of {cfg.B} sequences of the same workload (full index scan, "
-                      f"top-k and attention per sequence), {dt:.2f} s wall, scaled by "
-                      f"{cfg.B}/{len(seqs)}; threads available {orc.max_threads()}",
-            "keys_scored_per_s": float(np.sum(c["lens"])) / dt}
+        c = S.make_case(cfg)
+        n_rows = min(4 * n_seqs, cfg.T)
+        rows = [int(t) for t in np.linspace(0, cfg.T - 1, n_rows)]
+        idx = np.full((cfg.B, cfg.T, cfg.k), -1, np.int32)
+
+        def once():
+            for t in rows:
+                sc = orc.index_scores(c["q_i"][:, t:t + 1], c["q_scale"][:, t:t + 1],
+                                      c["w"][:, t:t + 1], c["k_i"], c["k_scale"],
+                                      np.array([t + 1], np.int32), cfg.sm_scale_i)
+                idx[:, t] = orc.topk(sc, np.array([t + 1], np.int32), cfg.k)[:, 0]
+            orc.sparse_mha_prefill_rows(c["q"], c["k"], c["v"], idx, cfg.sm_scale,
+                                        [(0, t) for t in rows])
+        frac = n_rows / cfg.T
+        keys = float(sum(t + 1 for t in rows))
+        threads = orc.max_threads()
+        sample = (f"{n_rows} of {cfg.T} query rows spread evenly over the chunk (index "
+                  f"scores, top-k and attention per row), scaled by {cfg.T}/{n_rows}")
+    reps = 0
+    t0 = time.perf_counter()
+    while True:
+        once()
+        reps += 1
+        dt = time.perf_counter() - t0
+        if dt >= min_seconds:
+            break
+    keys *= reps
+    sample += f"; {reps} repetitions in {dt:.1f} s wall"
+    return {"value": reps * frac / dt, "unit": "layer-steps/s", "cores": threads, "kind": "oracle",
+            "sample": sample + f"; threads available {orc.max_threads()}",
+            "keys_scored_per_s": keys / dt}
 
 
 def main():
@@ -116,7 +157,10 @@ def main():
     ap.add_argument("--config", default="decode_v32")
     ap.add_argument("--sets", type=int, default=4, help="independent input sets cycled")
     ap.add_argument("--graph", action="store_true", help="replay each step from a HIP graph")
-    ap.add_argument("--cpu-seqs", type=int, default=16, help="sequences in the CPU-oracle sample")
+    ap.add_argument("--cpu-seqs", type=int, default=32,
+                    help="sequences (decode) or rows / 4 (prefill) in the CPU-oracle sample")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0,
+                    help="the CPU-oracle sample repeats until this much wall time has passed")
     ap.add_argument("--no-cpu", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1:
@@ -195,15 +239,35 @@ def main():
     att_ms = phase_ms["attention"]
     idx_ms = phase_ms["index_scores"]
     att_gbs = costs["attention_bytes"] / (att_ms * 1e-3) / 1e9
+    att_tfs = costs["attention_flops"] / (att_ms * 1e-3) / 1e12
     idx_gbs = costs["index_bytes"] / (idx_ms * 1e-3) / 1e9
-    traffic = read_traffic("sparse_mla_decode", cfg.name, ATTN_SOURCE)
-    roofline = {"bound": "hbm", "achieved": round(att_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(att_gbs / HBM_PEAK_GBS, 4), "traffic": traffic,
-                "kernel": "mla_decode_mfma_kernel",
-                "algorithmic_bytes_per_launch": costs["attention_bytes"],
-                "avg_launch_ms": round(att_ms, 5),
-                "mfma_frac": round(costs["attention_flops"] / (att_ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4)}
-    t_roof = (costs["index_bytes"] + costs["attention_bytes"]) / (HBM_PEAK_GBS * 1e9)
+    idx_tfs = costs["index_flops"] / (idx_ms * 1e-3) / 1e12
+    if cfg.form == "latent":
+        kernel, tkey, src = "mla_decode_mfma_kernel", "sparse_mla_decode", ATTN_SOURCE
+    else:
+        kernel, tkey, src = "mha_prefill_mfma_kernel", "sparse_mha_prefill", PREFILL_SOURCE
+    traffic = read_traffic(tkey, cfg.name, src)
+    # the attention kernel's bound: whichever of its bytes or its flops takes longer at peak
+    mfma_bound = costs["attention_flops"] / (BF16_PEAK_TFLOPS * 1e12) > \
+        costs["attention_bytes"] / (HBM_PEAK_GBS * 1e9)
+    if mfma_bound:
+        roofline = {"bound": "mfma", "achieved": round(att_tfs, 1), "peak": BF16_PEAK_TFLOPS,
+                    "unit": "TFLOP/s", "frac": round(att_tfs / BF16_PEAK_TFLOPS, 4),
+                    "algorithmic_flops_per_launch": costs["attention_flops"],
+                    "hbm_frac": round(att_gbs / HBM_PEAK_GBS, 4)}
+    else:
+        roofline = {"bound": "hbm", "achieved": round(att_gbs, 1), "peak": HBM_PEAK_GBS,
+                    "unit": "GB/s", "frac": round(att_gbs / HBM_PEAK_GBS, 4),
+                    "algorithmic_bytes_per_launch": costs["attention_bytes"],
+                    "mfma_frac": round(att_tfs / BF16_PEAK_TFLOPS, 4)}
+    roofline.update({"traffic": traffic, "kernel": kernel, "avg_launch_ms": round(att_ms, 5)})
+    # the step's floor: each phase at the larger of its HBM time and its MFMA time at peak
+    t_roof = sum(max(costs[f"{p}_bytes"] / (HBM_PEAK_GBS * 1e9),
+                     costs[f"{p}_flops"] / (BF16_PEAK_TFLOPS * 1e12)) for p in ("index", "attention"))
+    if cfg.form == "latent":
+        attn_desc = f"MLA {cfg.H} heads over bf16 latent {cfg.Dv}+{cfg.Dr}"
+    else:
+        attn_desc = f"MHA {cfg.H} heads, bf16 qk {cfg.Dqk} / v {cfg.Dv}"
     result = {
         "metric": METRIC,
         "value": round(value, 2),
@@ -218,19 +282,20 @@ def main():
         "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": f"{cfg.name}: B={cfg.B}, context {cfg.Lmax} per sequence, T={cfg.T}, "
-                               f"indexer {cfg.H_I}x{cfg.D_I} FP8, top-{cfg.k}, MLA {cfg.H} heads over "
-                               f"bf16 latent {cfg.Dv}+{cfg.Dr}",
+                               f"indexer {cfg.H_I}x{cfg.D_I} FP8, top-{cfg.k}, {attn_desc}",
                    "B": cfg.B, "context": cfg.Lmax, "T": cfg.T, "topk": cfg.k, "H_I": cfg.H_I,
-                   "d_I": cfg.D_I, "H": cfg.H, "latent": cfg.Dq, "input_sets": args.sets,
+                   "d_I": cfg.D_I, "H": cfg.H, "q_width": cfg.Dq, "input_sets": args.sets,
                    "hip_graph": bool(args.graph)},
         "keys_scored_per_s": round(costs["keys"] * value, 1),
         "keys_per_step": costs["keys"],
-        "step_hbm_roofline_frac": round(t_roof / (ms_per_step * 1e-3), 4),
+        "step_roofline_frac": round(t_roof / (ms_per_step * 1e-3), 4),
         "phases_avg_ms": {k: (round(v, 5) if v is not None else None) for k, v in phase_ms.items()},
-        "index_scores": {"achieved_GBs": round(idx_gbs, 1), "frac": round(idx_gbs / HBM_PEAK_GBS, 4),
+        "index_scores": {"achieved_GBs": round(idx_gbs, 1), "hbm_frac": round(idx_gbs / HBM_PEAK_GBS, 4),
+                         "achieved_TFLOPs": round(idx_tfs, 1),
+                         "mfma_frac": round(idx_tfs / BF16_PEAK_TFLOPS, 4),
                          "keys_per_s": round(costs["keys"] / (idx_ms * 1e-3), 1)},
         "roofline": roofline,
-        "cpu_baseline": None if args.no_cpu else cpu_baseline(cfg, args.cpu_seqs),
+        "cpu_baseline": None if args.no_cpu else cpu_baseline(cfg, args.cpu_seqs, args.cpu_seconds),
     }
     print(json.dumps(result))
 
