@@ -86,7 +86,7 @@ dsa_status check_latent_args(const void* q, const void* latent, const int32_t* i
                 "sparse_mla_decode: B*T*H too large");
     DSA_REQUIRE(aligned16(q) && aligned16(latent) && aligned16(idx) && aligned16(len) && aligned16(out),
                 DSA_ERR_ALIGN, "sparse_mla_decode: pointers must be 16-byte aligned");
-    if (!dsa::mla_decode_mfma_supported(H, Dv, Dr, dt == DSA_BF16))
+    if (!dsa::mla_decode_mfma_supported(H, Dv, Dr, k, dt == DSA_BF16))
         DSA_REQUIRE(sizeof(float) * (static_cast<size_t>(Dv + Dr) + k) <= kGenericLdsLimit, DSA_ERR_SHAPE,
                     "sparse_mla_decode: k=%d too large for this shape", k);
     return DSA_OK;
@@ -95,7 +95,7 @@ dsa_status check_latent_args(const void* q, const void* latent, const int32_t* i
 dsa_status launch_latent(const void* q, const void* latent, const int32_t* idx, const int32_t* len,
                          int B, int T, int H, int Dv, int Dr, int Lmax, int k, float sm_scale,
                          dsa_dtype dt, void* out, float* lse, void* ws, hipStream_t stream) {
-    if (dsa::mla_decode_mfma_supported(H, Dv, Dr, dt == DSA_BF16))
+    if (dsa::mla_decode_mfma_supported(H, Dv, Dr, k, dt == DSA_BF16))
         return hip_status(dsa::launch_mla_decode_mfma(q, latent, idx, len, B, T, H, Lmax, k, sm_scale,
                                                       out, lse, ws, stream),
                           "sparse_mla_decode");
@@ -118,7 +118,7 @@ dsa_status launch_latent(const void* q, const void* latent, const int32_t* idx, 
 }
 
 size_t latent_ws(int B, int T, int H, int Dv, int Dr, int k, dsa_dtype dt) {
-    if (dsa::mla_decode_mfma_supported(H, Dv, Dr, dt == DSA_BF16))
+    if (dsa::mla_decode_mfma_supported(H, Dv, Dr, k, dt == DSA_BF16))
         return dsa::mla_decode_workspace_bytes(B, T, H, Dv, k);
     return 0;
 }

@@ -59,7 +59,7 @@ hipError_t launch_sparse_attn_generic(const SparseAttnArgs& a, hipStream_t strea
 
 // Matrix-core path of the absorbed latent form (bf16, Dv = 512, Dr = 64, H % 16 == 0,
 // H <= 128).
-bool mla_decode_mfma_supported(int H, int Dv, int Dr, int bf16);
+bool mla_decode_mfma_supported(int H, int Dv, int Dr, int k, int bf16);
 size_t mla_decode_workspace_bytes(int B, int T, int H, int Dv, int k);
 hipError_t launch_mla_decode_mfma(const void* q, const void* latent, const int32_t* idx,
                                   const int32_t* len, int B, int T, int H, int Lmax, int k,

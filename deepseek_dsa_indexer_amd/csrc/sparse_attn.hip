@@ -383,8 +383,12 @@ void mla_decode_mfma_kernel(const uint16_t* __restrict__ q, const uint16_t* __re
     const int g = lane >> 4;
     const int n = lane & 15;
 
-    const int row = blockIdx.x / n_splits;
-    const int split = blockIdx.x - row * n_splits;
+    // Consecutive workgroups go to different XCDs (round robin over 8), so block
+    // split * rows + row puts every split of a row on the same XCD whenever rows is a
+    // multiple of 8: the row's queries are then fetched into one L2 and shared.
+    const int rows = gridDim.x / n_splits;
+    const int row = blockIdx.x % rows;
+    const int split = blockIdx.x / rows;
     const int b = row / T;
     const int t = row - b * T;
     const int pos = min(len[b], Lmax) - T + t;
@@ -472,53 +476,61 @@ void mla_decode_mfma_kernel(const uint16_t* __restrict__ q, const uint16_t* __re
 }
 
 // Merge the splits of each (row, head): split s holds its own normalised output (bf16)
-// and its log2-sum-exp; weights are 2^(lse_s - max).  One thread owns 4 columns.
+// and its log2-sum-exp; weights are 2^(lse_s - max).  One thread owns 8 columns.
+constexpr int kCombCols = 8;
+constexpr int kMaxSplits = 8;
 __global__ __launch_bounds__(256)
 void mla_combine_kernel(const uint16_t* __restrict__ part_o, const float* __restrict__ part_lse,
                         int rows, int H, int n_splits, uint16_t* __restrict__ out,
                         float* __restrict__ lse)
 {
     const size_t gid = static_cast<size_t>(blockIdx.x) * blockDim.x + threadIdx.x;
-    const size_t total = static_cast<size_t>(rows) * H * (kDv / 4);
+    const size_t total = static_cast<size_t>(rows) * H * (kDv / kCombCols);
     if (gid >= total) return;
-    const int d4 = static_cast<int>(gid % (kDv / 4));
-    const size_t rh = gid / (kDv / 4);
+    const int d8 = static_cast<int>(gid % (kDv / kCombCols));
+    const size_t rh = gid / (kDv / kCombCols);
     const int h = static_cast<int>(rh % H);
     const size_t row = rh / H;
-    float ls[8];
+    float ls[kMaxSplits];
     float M = -INFINITY;
-    for (int s = 0; s < n_splits; ++s) {
-        ls[s] = part_lse[(row * n_splits + s) * H + h];
+#pragma unroll
+    for (int s = 0; s < kMaxSplits; ++s) {
+        ls[s] = s < n_splits ? part_lse[(row * n_splits + s) * H + h] : -INFINITY;
         M = fmaxf(M, ls[s]);
     }
     float W = 0.f;
-    float acc[4] = {0.f, 0.f, 0.f, 0.f};
+    float acc[kCombCols] = {};
     if (M != -INFINITY) {
-        for (int s = 0; s < n_splits; ++s) {
+#pragma unroll
+        for (int s = 0; s < kMaxSplits; ++s) {
             if (ls[s] == -INFINITY) continue;
             const float wgt = exp2f(ls[s] - M);
             W += wgt;
-            const uint2 v = *reinterpret_cast<const uint2*>(
-                part_o + ((row * n_splits + s) * H + h) * kDv + 4 * d4);
-            acc[0] += wgt * bf16_to_f32(static_cast<uint16_t>(v.x & 0xffffu));
-            acc[1] += wgt * bf16_to_f32(static_cast<uint16_t>(v.x >> 16));
-            acc[2] += wgt * bf16_to_f32(static_cast<uint16_t>(v.y & 0xffffu));
-            acc[3] += wgt * bf16_to_f32(static_cast<uint16_t>(v.y >> 16));
+            const uint4 v = *reinterpret_cast<const uint4*>(
+                part_o + ((row * n_splits + s) * H + h) * kDv + kCombCols * d8);
+            const uint32_t wv[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                acc[2 * i] += wgt * bf16_to_f32(static_cast<uint16_t>(wv[i] & 0xffffu));
+                acc[2 * i + 1] += wgt * bf16_to_f32(static_cast<uint16_t>(wv[i] >> 16));
+            }
         }
     }
     const float inv = W > 0.f ? 1.f / W : 0.f;
-    uint2 o;
-    o.x = f32_to_bf16(acc[0] * inv) | (static_cast<uint32_t>(f32_to_bf16(acc[1] * inv)) << 16);
-    o.y = f32_to_bf16(acc[2] * inv) | (static_cast<uint32_t>(f32_to_bf16(acc[3] * inv)) << 16);
-    *reinterpret_cast<uint2*>(out + (row * H + h) * kDv + 4 * d4) = o;
-    if (lse && d4 == 0) lse[row * H + h] = W > 0.f ? (M + log2f(W)) * kLn2 : -INFINITY;
+    uint32_t o[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+        o[i] = f32_to_bf16(acc[2 * i] * inv) |
+               (static_cast<uint32_t>(f32_to_bf16(acc[2 * i + 1] * inv)) << 16);
+    *reinterpret_cast<uint4*>(out + (row * H + h) * kDv + kCombCols * d8) = uint4{o[0], o[1], o[2], o[3]};
+    if (lse && d8 == 0) lse[row * H + h] = W > 0.f ? (M + log2f(W)) * kLn2 : -INFINITY;
 }
 
 int mla_splits(int rows, int k) {
     // enough (row, split) workgroups to give every CU one, within the LDS slot limit
     const int n_tiles = (k + kKt - 1) / kKt;
     int s = rows >= 256 ? 1 : (256 + rows - 1) / rows;
-    s = min(s, 8);
+    s = min(s, kMaxSplits);
     const int min_s = (n_tiles * kKt + kMaxSlots - 1) / kMaxSlots;
     s = max(s, min_s);
     s = min(s, n_tiles);
@@ -534,8 +546,10 @@ hipError_t launch_sparse_attn_generic(const SparseAttnArgs& a, hipStream_t strea
     return hipGetLastError();
 }
 
-bool mla_decode_mfma_supported(int H, int Dv, int Dr, int bf16) {
-    return bf16 && Dv == kDv && Dv + Dr == kDq && (H == 64 || H == 128);
+bool mla_decode_mfma_supported(int H, int Dv, int Dr, int k, int bf16) {
+    // every split holds at most kMaxSlots selected positions in LDS
+    return bf16 && Dv == kDv && Dv + Dr == kDq && (H == 64 || H == 128) &&
+           k <= kMaxSplits * kMaxSlots;
 }
 
 size_t mla_decode_workspace_bytes(int B, int T, int H, int, int k) {
@@ -568,7 +582,7 @@ hipError_t launch_mla_decode_mfma(const void* q, const void* latent, const int32
                            qp, lp, idx, len, T, Lmax, k, tps, s, scale_log2, op, lse, part_o, part_lse);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || s == 1) return e;
-    const size_t total = static_cast<size_t>(rows) * H * (kDv / 4);
+    const size_t total = static_cast<size_t>(rows) * H * (kDv / kCombCols);
     prof_mark(stream, kPhaseCombine);
     hipLaunchKernelGGL(mla_combine_kernel, dim3((total + 255) / 256), dim3(256), 0, stream,
                        part_o, part_lse, rows, H, s, op, lse);
