@@ -118,9 +118,10 @@ void sparse_attn_generic_kernel(SparseAttnArgs a)
 // slots and all heads (64 or 128), so every selected latent row is gathered from memory
 // once per row and split.  Per tile of 32 selected positions:
 //   gather   32 latent rows -> LDS with direct global->LDS 16-byte loads.  Four tile
-//            buffers are distinct LDS objects; three tiles stay in flight while one is
-//            consumed.  The 16-byte chunks of each row are XOR-swizzled inside 128-byte
-//            groups so the matrix-core operand reads spread over the LDS banks;
+//            buffers are distinct LDS objects; two tiles stay in flight while one is
+//            multiplied against Q and the previous one against P.  The 16-byte chunks
+//            of each row are XOR-swizzled inside 128-byte groups so the matrix-core
+//            operand reads spread over the LDS banks;
 //   QK       wave w computes S^T = K . Q^T for head tile w (16 heads) and all 32 keys of
 //            the tile (keys as MFMA rows; the wave's queries stay in registers as 18 B
 //            operands);
@@ -130,8 +131,13 @@ void sparse_attn_generic_kernel(SparseAttnArgs a)
 //   PV       wave w owns output columns 64w..64w+63 for all heads: O += P . V with V read
 //            from the same LDS tile by transpose reads (the value is the first 512
 //            columns of the latent row).
-// Two workgroup barriers per tile.  Splits of one row are merged by a log-sum-exp
-// combine kernel.
+// Software pipeline: step i runs PV of tile i-1 and QK + softmax of tile i between two
+// workgroup barriers, then publishes P and the rescale factors of tile i, so a tile
+// costs two barriers but the matrix-core work of both products sits in one phase.
+// Waves 0-3 run at a raised issue priority over waves 4-7 (they pair up on the four
+// SIMDs), so within a step the pair drifts apart and one wave's softmax overlaps the
+// other's matrix-core work.  Splits of one row are merged by a log-sum-exp combine
+// kernel.
 constexpr int kMlaThreads = 512;
 constexpr int kMlaWaves = 8;
 constexpr int kMaxHt = 8;                          // up to 128 heads per workgroup
@@ -149,10 +155,8 @@ constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kLazyRescale = 8.0f;               // log2 units
 
-__shared__ __attribute__((aligned(16))) uint8_t g_kbuf0[kTileBytes];
-__shared__ __attribute__((aligned(16))) uint8_t g_kbuf1[kTileBytes];
-__shared__ __attribute__((aligned(16))) uint8_t g_kbuf2[kTileBytes];
-__shared__ __attribute__((aligned(16))) uint8_t g_kbuf3[kTileBytes];
+constexpr int kBufs = 4;                          // tile ring
+__shared__ __attribute__((aligned(16))) uint8_t g_kbuf[kBufs * kTileBytes];
 __shared__ __attribute__((aligned(16))) uint8_t g_pbuf[kMaxHt][kWave][16];
 __shared__ __attribute__((aligned(16))) float g_alpha[kMaxHt * 16];
 __shared__ int32_t g_rescale[kMaxHt];
@@ -160,13 +164,7 @@ __shared__ float g_l[kMaxHt * 16];
 __shared__ float g_m[kMaxHt * 16];
 __shared__ int32_t g_keys[kMaxSlots];
 
-template <int I>
-__device__ __forceinline__ uint8_t* kbuf() {
-    if constexpr (I == 0) return g_kbuf0;
-    else if constexpr (I == 1) return g_kbuf1;
-    else if constexpr (I == 2) return g_kbuf2;
-    else return g_kbuf3;
-}
+__device__ __forceinline__ uint8_t* kbuf(int ti) { return g_kbuf + (ti & (kBufs - 1)) * kTileBytes; }
 
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() { asm volatile("s_waitcnt vmcnt(%0)" :: "n"(N) : "memory"); }
@@ -180,14 +178,12 @@ __device__ __forceinline__ void lds_barrier() {
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
-// Wait until this wave's gathers of the current tile have landed, leaving the `later`
-// tiles issued after it in flight (waves 0..3 issue 5 loads per tile, waves 4..7 four).
-__device__ __forceinline__ void wait_tile(int later, bool five) {
-    if (five) {
-        if (later >= 2) wait_vmcnt<10>(); else if (later == 1) wait_vmcnt<5>(); else wait_vmcnt<0>();
-    } else {
-        if (later >= 2) wait_vmcnt<8>(); else if (later == 1) wait_vmcnt<4>(); else wait_vmcnt<0>();
-    }
+// Wait until this wave's gathers of the current tile have landed, leaving the tile
+// issued after it in flight (waves 0..3 issue 5 loads per tile, waves 4..7 four).
+__device__ __forceinline__ void wait_tile(bool later, bool five) {
+    if (!later) wait_vmcnt<0>();
+    else if (five) wait_vmcnt<5>();
+    else wait_vmcnt<4>();
 }
 
 // Issue the direct global->LDS loads of tile `ti` into `dst`: wave w issues the
@@ -240,15 +236,12 @@ struct MlaState {
 
 typedef __bf16 v4bf_t __attribute__((ext_vector_type(4)));
 
-// One tile: wait for its gather, prefetch tile ti + 3 into buffer PREF, QK, softmax, PV.
-template <int NHT, int CUR, int PREF>
-__device__ __forceinline__ void mla_tile(MlaState<NHT>& st, const uint8_t* lat_b, int ti,
-                                         int n_tiles, float scale_log2, int wave, int lane) {
-    wait_tile(min(2, n_tiles - 1 - ti), wave < 4);
-    lds_barrier();                                 // tile ti visible; tile ti-1 released
-    if (ti + 3 < n_tiles) gather_tile(lat_b, ti + 3, kbuf<PREF>(), wave, lane);
-    const uint8_t* kb = kbuf<CUR>();
-
+// QK and online softmax of tile ti (buffer kb) for head tile `wave` (< NHT).  Returns
+// the bf16 probabilities in PV A-operand layout and the head's rescale factor; they are
+// published after the step's second barrier.
+template <int NHT>
+__device__ __forceinline__ void mla_qk_softmax(MlaState<NHT>& st, const uint8_t* kb, int ti,
+                                               float scale_log2, int lane, v8s& pk, float& alpha) {
     // Per-lane LDS offsets are recomputed in every tile step from an opaque copy of the
     // lane id: hoisted out of the loop they would be kept live once per buffer copy.
     int lane_o = lane;
@@ -256,85 +249,86 @@ __device__ __forceinline__ void mla_tile(MlaState<NHT>& st, const uint8_t* lat_b
     const int go = lane_o >> 4;
     const int no = lane_o & 15;
 
-    if (wave < NHT) {
-        // ---- QK: 32 keys x 16 heads (tile `wave`), two MFMA chains (key halves).
-        // Logical chunk 4 ds + g of key row 16 kt + n sits at chunk (4 ds + g) ^ (n & 7)
-        //   = 8 (ds / 2) + ((4 (ds & 1) + g) ^ (n & 7)),
-        // so two base offsets per key half plus an immediate cover all 18 K-steps.
-        v4f sacc[2] = {v4f{0.f, 0.f, 0.f, 0.f}, v4f{0.f, 0.f, 0.f, 0.f}};
-        {
-            const uint8_t* base[2][2];
+    // ---- QK: 32 keys x 16 heads, two MFMA chains (key halves).
+    // Logical chunk 4 ds + g of key row 16 kt + n sits at chunk (4 ds + g) ^ (n & 7)
+    //   = 8 (ds / 2) + ((4 (ds & 1) + g) ^ (n & 7)),
+    // so two base offsets per key half plus an immediate cover all 18 K-steps.
+    v4f sacc[2] = {v4f{0.f, 0.f, 0.f, 0.f}, v4f{0.f, 0.f, 0.f, 0.f}};
+    {
+        const uint8_t* base[2][2];
 #pragma unroll
-            for (int kt = 0; kt < 2; ++kt) {
-                const uint8_t* krow = kb + (16 * kt + no) * kRowBytes;
-                base[kt][0] = krow + ((go) ^ (no & 7)) * 16;
-                base[kt][1] = krow + ((4 + go) ^ (no & 7)) * 16;
-            }
-            constexpr int kPre = 2;               // K-steps of operand reads in flight
-            v8bf a[kPre][2];
+        for (int kt = 0; kt < 2; ++kt) {
+            const uint8_t* krow = kb + (16 * kt + no) * kRowBytes;
+            base[kt][0] = krow + ((go) ^ (no & 7)) * 16;
+            base[kt][1] = krow + ((4 + go) ^ (no & 7)) * 16;
+        }
+        constexpr int kPre = 2;               // K-steps of operand reads in flight
+        v8bf a[kPre][2];
 #pragma unroll
-            for (int ds = 0; ds < kPre; ++ds)
+        for (int ds = 0; ds < kPre; ++ds)
+#pragma unroll
+            for (int kt = 0; kt < 2; ++kt)
+                a[ds][kt] = *reinterpret_cast<const v8bf*>(base[kt][ds & 1] + (ds >> 1) * 128);
+#pragma unroll
+        for (int ds = 0; ds < kDs; ++ds) {
+#pragma unroll
+            for (int kt = 0; kt < 2; ++kt)
+                sacc[kt] = mfma_bf16_16x16x32(a[ds % kPre][kt], st.qreg[ds], sacc[kt]);
+            if (ds + kPre < kDs) {
+                const int dn = ds + kPre;
 #pragma unroll
                 for (int kt = 0; kt < 2; ++kt)
-                    a[ds][kt] = *reinterpret_cast<const v8bf*>(base[kt][ds & 1] + (ds >> 1) * 128);
-#pragma unroll
-            for (int ds = 0; ds < kDs; ++ds) {
-#pragma unroll
-                for (int kt = 0; kt < 2; ++kt)
-                    sacc[kt] = mfma_bf16_16x16x32(a[ds % kPre][kt], st.qreg[ds], sacc[kt]);
-                if (ds + kPre < kDs) {
-                    const int dn = ds + kPre;
-#pragma unroll
-                    for (int kt = 0; kt < 2; ++kt)
-                        a[ds % kPre][kt] = *reinterpret_cast<const v8bf*>(base[kt][dn & 1] + (dn >> 1) * 128);
-                }
-                __builtin_amdgcn_sched_barrier(0);
+                    a[ds % kPre][kt] = *reinterpret_cast<const v8bf*>(base[kt][dn & 1] + (dn >> 1) * 128);
             }
+            __builtin_amdgcn_sched_barrier(0);
         }
-        // ---- online softmax of the wave's 16 heads over the 32 keys of this tile.
-        // Lane (g, n) holds head n, keys 16 kt + 4 g + i, which is exactly K-slot
-        // j = 4 kt + i of the P operand of the PV product.
-        float sv[8];
-        float mx = -INFINITY;
-#pragma unroll
-        for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const bool valid = g_keys[ti * kKt + 16 * kt + 4 * go + i] >= 0;
-                const float v = valid ? sacc[kt][i] * scale_log2 : -INFINITY;
-                sv[4 * kt + i] = v;
-                mx = fmaxf(mx, v);
-            }
-        mx = fmaxf(mx, __shfl_xor(mx, 16, kWave));
-        mx = fmaxf(mx, __shfl_xor(mx, 32, kWave));
-        float alpha = 1.f;
-        if (mx > st.m_run + kLazyRescale) {
-            alpha = (st.m_run == -INFINITY) ? 0.f : exp2f(st.m_run - mx);
-            st.m_run = mx;
-        }
-        float psum = 0.f;
-        v8s pk;
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            const float p = (sv[j] == -INFINITY) ? 0.f : exp2f(sv[j] - st.m_run);
-            psum += p;
-            pk[j] = static_cast<short>(f32_to_bf16(p));
-        }
-        psum += __shfl_xor(psum, 16, kWave);
-        psum += __shfl_xor(psum, 32, kWave);
-        st.l_run = st.l_run * alpha + psum;
-        *reinterpret_cast<v8s*>(&g_pbuf[wave][lane][0]) = pk;
-        if (go == 0) g_alpha[16 * wave + no] = alpha;
-        const unsigned long long any = __ballot(alpha != 1.f);
-        if (lane == 0) g_rescale[wave] = any != 0ull;
     }
-    lds_barrier();
+    // ---- online softmax of the wave's 16 heads over the 32 keys of this tile.
+    // Lane (g, n) holds head n, keys 16 kt + 4 g + i, which is exactly K-slot
+    // j = 4 kt + i of the P operand of the PV product.
+    float sv[8];
+    float mx = -INFINITY;
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const bool valid = g_keys[ti * kKt + 16 * kt + 4 * go + i] >= 0;
+            const float v = valid ? sacc[kt][i] * scale_log2 : -INFINITY;
+            sv[4 * kt + i] = v;
+            mx = fmaxf(mx, v);
+        }
+    mx = fmaxf(mx, __shfl_xor(mx, 16, kWave));
+    mx = fmaxf(mx, __shfl_xor(mx, 32, kWave));
+    alpha = 1.f;
+    if (mx > st.m_run + kLazyRescale) {
+        // nothing accumulated yet (O = 0, l = 0): no rescale needed
+        alpha = (st.m_run == -INFINITY) ? 1.f : exp2f(st.m_run - mx);
+        st.m_run = mx;
+    }
+    float psum = 0.f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        const float p = (sv[j] == -INFINITY) ? 0.f : exp2f(sv[j] - st.m_run);
+        psum += p;
+        pk[j] = static_cast<short>(f32_to_bf16(p));
+    }
+    psum += __shfl_xor(psum, 16, kWave);
+    psum += __shfl_xor(psum, 32, kWave);
+    st.l_run = st.l_run * alpha + psum;
+}
 
-    // ---- PV: output columns 64 wave .. + 63 for all heads.  V operands come from LDS
-    // transpose reads: for K-slots j = 4 kt + r the lane needs V[16 kt + 4 g + r][d],
-    // d = 64 wave + 16 dt + n; within each 16-lane group a transpose read hands lane n
-    // the element at (address of lane 4 r + n / 4) + n % 4, so lane m supplies row
-    // 16 kt + 4 g + m / 4, columns d0 + 4 (m % 4) .. + 3.
+// PV of the previous tile (buffer kb, probabilities and rescale factors in g_pbuf,
+// g_alpha, g_rescale): output columns 64 wave .. + 63 for all heads.  V operands come
+// from LDS transpose reads: for K-slots j = 4 kt + r the lane needs V[16 kt + 4 g + r][d],
+// d = 64 wave + 16 dt + n; within each 16-lane group a transpose read hands lane n the
+// element at (address of lane 4 r + n / 4) + n % 4, so lane m supplies row
+// 16 kt + 4 g + m / 4, columns d0 + 4 (m % 4) .. + 3.
+template <int NHT>
+__device__ __forceinline__ void mla_pv(MlaState<NHT>& st, const uint8_t* kb, int wave, int lane) {
+    int lane_o = lane;
+    asm volatile("" : "+v"(lane_o));
+    const int go = lane_o >> 4;
+    const int no = lane_o & 15;
     v8bf vb[kDtW];
 #pragma unroll
     for (int dt = 0; dt < kDtW; ++dt) {
@@ -368,6 +362,17 @@ __device__ __forceinline__ void mla_tile(MlaState<NHT>& st, const uint8_t* lat_b
     }
 }
 
+// Publish P and the rescale factors of the wave's head tile (after the step's second
+// barrier: every wave is then done reading the previous tile's).
+__device__ __forceinline__ void mla_publish(const v8s& pk, float alpha, int wave, int lane) {
+    const int go = lane >> 4;
+    const int no = lane & 15;
+    *reinterpret_cast<v8s*>(&g_pbuf[wave][lane][0]) = pk;
+    if (go == 0) g_alpha[16 * wave + no] = alpha;
+    const unsigned long long any = __ballot(alpha != 1.f);
+    if (lane == 0) g_rescale[wave] = any != 0ull;
+}
+
 template <int NHT>
 __global__ __launch_bounds__(kMlaThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void mla_decode_mfma_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ latent,
@@ -382,6 +387,7 @@ void mla_decode_mfma_kernel(const uint16_t* __restrict__ q, const uint16_t* __re
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);   // wave-uniform: SGPR
     const int g = lane >> 4;
     const int n = lane & 15;
+    if (wave < 4) __builtin_amdgcn_s_setprio(1);
 
     // Consecutive workgroups go to different XCDs (round robin over 8), so block
     // split * rows + row puts every split of a row on the same XCD whenever rows is a
@@ -423,20 +429,48 @@ void mla_decode_mfma_kernel(const uint16_t* __restrict__ q, const uint16_t* __re
 
     const uint8_t* lat_b = reinterpret_cast<const uint8_t*>(latent) +
                            static_cast<size_t>(b) * Lmax * kRowBytes;
-    // consume the query registers here, so the compiler's own wait for their loads
-    // happens before the tile gathers are in flight rather than at the first MFMA
+    lds_barrier();        // g_keys ready (its stores waited for the idx loads)
+    // Tile 0 goes out together with the queries; wait for both, then put tile 1 in
+    // flight.  The compiler's own wait for the query registers (it does not see the
+    // gathers) then falls here, where nothing else is outstanding.
+    if (n_tiles > 0) gather_tile(lat_b, 0, kbuf(0), wave, lane);
+    wait_vmcnt<0>();
 #pragma unroll
     for (int ds = 0; ds < kDs; ++ds) asm volatile("" :: "v"(st.qreg[ds]));
-    __syncthreads();      // g_keys ready
-    if (n_tiles > 0) gather_tile(lat_b, 0, kbuf<0>(), wave, lane);
-    if (n_tiles > 1) gather_tile(lat_b, 1, kbuf<1>(), wave, lane);
-    if (n_tiles > 2) gather_tile(lat_b, 2, kbuf<2>(), wave, lane);
+    if (n_tiles > 1) gather_tile(lat_b, 1, kbuf(1), wave, lane);
 
-    for (int t4 = 0; t4 < n_tiles; t4 += 4) {
-        mla_tile<NHT, 0, 3>(st, lat_b, t4, n_tiles, scale_log2, wave, lane);
-        if (t4 + 1 < n_tiles) mla_tile<NHT, 1, 0>(st, lat_b, t4 + 1, n_tiles, scale_log2, wave, lane);
-        if (t4 + 2 < n_tiles) mla_tile<NHT, 2, 1>(st, lat_b, t4 + 2, n_tiles, scale_log2, wave, lane);
-        if (t4 + 3 < n_tiles) mla_tile<NHT, 3, 2>(st, lat_b, t4 + 3, n_tiles, scale_log2, wave, lane);
+    // Step 0: QK + softmax of tile 0.  Steps 1 .. n_tiles-1: PV of tile i-1 and QK +
+    // softmax of tile i.  Last: PV of tile n_tiles-1.  Every step waits for its tile,
+    // passes a barrier (tile i and P(i-1) visible; the buffer of tile i-2 released) and
+    // prefetches tile i+2; a second barrier separates the reads of P(i-1) from the
+    // publication of P(i).  The loop body has no data-dependent branch around the
+    // accumulators, so they keep their registers across iterations.
+    const bool qk_wave = wave < NHT;
+    if (n_tiles > 0) {
+        wait_tile(1 < n_tiles, wave < 4);
+        lds_barrier();
+        if (2 < n_tiles) gather_tile(lat_b, 2, kbuf(2), wave, lane);
+        v8s pk;
+        float alpha = 1.f;
+        if (qk_wave) mla_qk_softmax<NHT>(st, kbuf(0), 0, scale_log2, lane, pk, alpha);
+        lds_barrier();
+        if (qk_wave) mla_publish(pk, alpha, wave, lane);
+    }
+    for (int ti = 1; ti < n_tiles; ++ti) {
+        wait_tile(ti + 1 < n_tiles, wave < 4);
+        lds_barrier();
+        if (ti + 2 < n_tiles) gather_tile(lat_b, ti + 2, kbuf(ti + 2), wave, lane);
+        mla_pv<NHT>(st, kbuf(ti - 1), wave, lane);
+        __builtin_amdgcn_sched_barrier(0);
+        v8s pk;
+        float alpha = 1.f;
+        if (qk_wave) mla_qk_softmax<NHT>(st, kbuf(ti), ti, scale_log2, lane, pk, alpha);
+        lds_barrier();
+        if (qk_wave) mla_publish(pk, alpha, wave, lane);
+    }
+    if (n_tiles > 0) {
+        lds_barrier();
+        mla_pv<NHT>(st, kbuf(n_tiles - 1), wave, lane);
     }
 
     // ---- epilogue: normalise, then write the final row or this split's partial
