@@ -1,6 +1,7 @@
 // dsa_abi.cpp -- the extern "C" entry points of libdsa_amd: argument validation,
 // workspace carving and kernel launches on the caller's stream.  See include/dsa.h for
 // the contract of each call.
+#include <algorithm>
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
@@ -306,15 +307,18 @@ dsa_status dsa_sparse_mla_prefill(const void* q, const void* k, const void* v, c
     return launch_mha(q, k, v, idx, B, T, H, Dqk, Dv, topk, sm_scale, dt, out, lse, ws, stream);
 }
 
-// Workspace layout of the layer step: [scores][idx][attention scratch], 256-byte aligned.
+// Workspace layout of the layer step: [scores][idx][scratch], 256-byte aligned.  The
+// scratch part serves the top-k candidates first and the attention partials after (the
+// two never overlap in time on the stream).
 static void layer_ws_parts(const dsa_layer_args* a, size_t* s_bytes, size_t* i_bytes, size_t* att) {
     const size_t rows = static_cast<size_t>(a->B) * a->T;
     *s_bytes = a->scores_out ? 0 : round_up(rows * a->Lmax * sizeof(float));
     *i_bytes = a->idx_out ? 0 : round_up(rows * a->topk * sizeof(int32_t));
+    const size_t tk = dsa::topk_workspace_bytes(a->B, a->T, a->Lmax, a->topk);
     if (a->form == DSA_ATTN_LATENT)
-        *att = round_up(latent_ws(a->B, a->T, a->H, a->Dv, a->Dr, a->topk, a->dtype));
+        *att = round_up(std::max(tk, latent_ws(a->B, a->T, a->H, a->Dv, a->Dr, a->topk, a->dtype)));
     else
-        *att = round_up(mha_ws(a->B, a->T, a->H, a->Dqk, a->Dv, a->topk, a->dtype));
+        *att = round_up(std::max(tk, mha_ws(a->B, a->T, a->H, a->Dqk, a->Dv, a->topk, a->dtype)));
 }
 
 size_t dsa_layer_step_workspace_bytes(const dsa_layer_args* a) {
@@ -367,7 +371,7 @@ dsa_status dsa_layer_step(const dsa_layer_args* a, void* ws, size_t ws_bytes, hi
     if (st != DSA_OK) return st;
     dsa::prof_mark(stream, dsa::kPhaseTopk);
     dsa::TopkArgs ta{scores, a->len, a->B, a->T, a->Lmax, a->topk, idx};
-    st = hip_status(dsa::launch_topk(ta, nullptr, stream), "layer step: topk");
+    st = hip_status(dsa::launch_topk(ta, att_ws, stream), "layer step: topk");
     if (st != DSA_OK) return st;
     dsa::prof_mark(stream, dsa::kPhaseAttention);
     if (a->form == DSA_ATTN_LATENT)

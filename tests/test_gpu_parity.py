@@ -90,6 +90,11 @@ TOPK_CASES = [
     ("normal_decode", "normal", 4, 1, 8192, [8192, 3000, 2049, 100], 2048),
     ("ties_decode", "ties", 3, 1, 5000, [5000, 4097, 2500], 2048),
     ("heavy_long", "heavy", 2, 1, 40000, [40000, 17001], 2048),
+    # rows beyond 16384 positions: chunk-local candidates, then a merge
+    ("ties_long", "ties", 2, 1, 70000, [70000, 16500], 2048),
+    ("zeros_long", "zeros", 1, 1, 30000, [30000], 2048),
+    ("causal_long_odd_k", "normal", 1, 3, 20000, [20000], 3001),
+    ("big_k_long", "heavy", 2, 1, 20000, [20000, 9000], 8000),
     ("zeros", "zeros", 2, 1, 3000, [3000, 2100], 2048),
     ("causal_rows", "normal", 2, 37, 1001, [1001, 37], 64),
     ("k1", "ties", 2, 3, 500, [500, 300], 1),
