@@ -21,9 +21,9 @@
 //
 // Rows up to 16384 positions: one workgroup per row.  Longer rows (a workgroup can keep
 // only ~64 KB of loads in flight, far too little for one row of a long context) take
-// two launches: every 8192-position chunk of a row selects its own top-k candidates
-// (key and position) in parallel, then one workgroup per row selects the top-k of the
-// candidates.  The row's top-k is contained in the union of its chunks' top-k under
+// two launches: every 8192- or 16384-position chunk of a row selects its own top-k
+// candidates (key and position) in parallel, then one workgroup per row selects the
+// top-k of the candidates.  The row's top-k is contained in the union of its chunks' top-k under
 // the same (score, position) order, and candidates are stored chunk after chunk in
 // position order, so candidate order is position order and ties still resolve towards
 // the smaller position.
@@ -40,8 +40,7 @@ constexpr int kBins = 2048;
 constexpr int kBinBits = 11;
 constexpr int kPerThread = 4;
 constexpr int kPerIter = kThreads * kPerThread;     // positions per block-wide iteration
-constexpr int kMaxIters = 8;                         // register-held iterations
-constexpr int kChunk = 2 * kPerIter;                 // positions per chunk in the two-stage form
+constexpr int kMaxIters = 4;                         // register-held iterations
 constexpr int kSingleMax = 4 * kPerIter;             // longest row for the one-launch form
 constexpr uint32_t kNoKey = 0u;                      // unused candidate (float bits of -NaN)
 
@@ -90,33 +89,30 @@ __device__ __forceinline__ void block_exclusive_scan_n(const uint32_t (&v)[N], T
     __syncthreads();
 }
 
-// Key sources: four consecutive keys at index i0 and whether each is a live element.
+// Key sources: four consecutive keys at index i0; kNoKey marks an element that does not
+// take part (a position past the visible range, an unused candidate slot).  No score
+// maps to kNoKey except a negative NaN with every mantissa bit set.
 struct ScoreSrc {                       // a row of scores, indices < n visible
     const float* sc;
     int n;
     bool vec4;
-    __device__ __forceinline__ void load4(int i0, uint32_t (&key)[kPerThread], bool (&ok)[kPerThread]) const {
+    __device__ __forceinline__ void load4(int i0, uint32_t (&key)[kPerThread]) const {
         if (vec4 && i0 + kPerThread <= n) {
             const float4 v = *reinterpret_cast<const float4*>(sc + i0);
             key[0] = score_key(v.x); key[1] = score_key(v.y);
             key[2] = score_key(v.z); key[3] = score_key(v.w);
-#pragma unroll
-            for (int j = 0; j < kPerThread; ++j) ok[j] = true;
         } else {
 #pragma unroll
-            for (int j = 0; j < kPerThread; ++j) {
-                ok[j] = i0 + j < n;
-                key[j] = ok[j] ? score_key(sc[i0 + j]) : kNoKey;
-            }
+            for (int j = 0; j < kPerThread; ++j) key[j] = i0 + j < n ? score_key(sc[i0 + j]) : kNoKey;
         }
     }
 };
 
-struct CandSrc {                        // candidate keys of a row, kNoKey = unused slot
+struct CandSrc {                        // candidate keys of a row
     const uint32_t* key;
     int n;
     bool vec4;
-    __device__ __forceinline__ void load4(int i0, uint32_t (&k4)[kPerThread], bool (&ok)[kPerThread]) const {
+    __device__ __forceinline__ void load4(int i0, uint32_t (&k4)[kPerThread]) const {
         if (vec4 && i0 + kPerThread <= n) {
             const uint4 v = *reinterpret_cast<const uint4*>(key + i0);
             k4[0] = v.x; k4[1] = v.y; k4[2] = v.z; k4[3] = v.w;
@@ -124,8 +120,6 @@ struct CandSrc {                        // candidate keys of a row, kNoKey = unu
 #pragma unroll
             for (int j = 0; j < kPerThread; ++j) k4[j] = i0 + j < n ? key[i0 + j] : kNoKey;
         }
-#pragma unroll
-        for (int j = 0; j < kPerThread; ++j) ok[j] = k4[j] != kNoKey;
     }
 };
 
@@ -134,7 +128,6 @@ struct CandSrc {                        // candidate keys of a row, kNoKey = unu
 template <int REG, typename Src>
 struct Keys {
     uint32_t key[REG > 0 ? REG : 1][kPerThread];
-    bool ok[REG > 0 ? REG : 1][kPerThread];
     Src src;
     int iters;
 
@@ -143,7 +136,7 @@ struct Keys {
         iters = (n + kPerIter - 1) / kPerIter;
         if constexpr (REG > 0) {
 #pragma unroll
-            for (int it = 0; it < REG; ++it) src.load4(it * kPerIter + threadIdx.x * kPerThread, key[it], ok[it]);
+            for (int it = 0; it < REG; ++it) src.load4(it * kPerIter + threadIdx.x * kPerThread, key[it]);
         }
     }
     // f(key, index, live) for this thread's elements of block iteration `it`
@@ -152,13 +145,12 @@ struct Keys {
         const int i0 = it * kPerIter + threadIdx.x * kPerThread;
         if constexpr (REG > 0) {
 #pragma unroll
-            for (int j = 0; j < kPerThread; ++j) f(key[it][j], i0 + j, ok[it][j]);
+            for (int j = 0; j < kPerThread; ++j) f(key[it][j], i0 + j, key[it][j] != kNoKey);
         } else {
             uint32_t kk[kPerThread];
-            bool oo[kPerThread];
-            src.load4(i0, kk, oo);
+            src.load4(i0, kk);
 #pragma unroll
-            for (int j = 0; j < kPerThread; ++j) f(kk[j], i0 + j, oo[j]);
+            for (int j = 0; j < kPerThread; ++j) f(kk[j], i0 + j, kk[j] != kNoKey);
         }
     }
     // f for every element held by this thread; the re-reading form keeps four block
@@ -172,15 +164,14 @@ struct Keys {
             constexpr int kBatch = 4;
             for (int it0 = 0; it0 < iters; it0 += kBatch) {
                 uint32_t kk[kBatch][kPerThread];
-                bool oo[kBatch][kPerThread];
 #pragma unroll
                 for (int u = 0; u < kBatch; ++u)
-                    src.load4((it0 + u) * kPerIter + threadIdx.x * kPerThread, kk[u], oo[u]);
+                    src.load4((it0 + u) * kPerIter + threadIdx.x * kPerThread, kk[u]);
 #pragma unroll
                 for (int u = 0; u < kBatch; ++u) {
                     const int i0 = (it0 + u) * kPerIter + threadIdx.x * kPerThread;
 #pragma unroll
-                    for (int j = 0; j < kPerThread; ++j) f(kk[u][j], i0 + j, oo[u][j]);
+                    for (int j = 0; j < kPerThread; ++j) f(kk[u][j], i0 + j, kk[u][j] != kNoKey);
                 }
             }
         }
@@ -324,10 +315,10 @@ void topk_row_kernel(const float* __restrict__ scores, const int32_t* __restrict
     block_select(ks, k, sh, [&](uint32_t slot, int i, uint32_t) { out[slot] = i; });
 }
 
-// Two-stage form, stage 1: chunk c of row r (its visible positions among
-// [8192 c, 8192 c + 8192)) writes its top-min(k, m) keys and positions, in position
-// order, to candidate slots [c k, c k + k) of the row; the remaining slots get
-// kNoKey / -1.
+// Two-stage form, stage 1: chunk c of row r (its visible positions among [C c, C c + C),
+// C = 4096 REG) writes its top-min(k, m) keys and positions, in position order, to
+// candidate slots [c k, c k + k) of the row; the remaining slots get kNoKey / -1.
+template <int REG>
 __global__ __launch_bounds__(kThreads)
 void topk_chunk_kernel(const float* __restrict__ scores, const int32_t* __restrict__ len,
                        int T, int Lmax, int k, int n_chunks, uint32_t* __restrict__ cand_key,
@@ -338,6 +329,7 @@ void topk_chunk_kernel(const float* __restrict__ scores, const int32_t* __restri
     const int c = blockIdx.x - row * n_chunks;
     const int n = visible(len, row, T, Lmax);
     if (n <= k) return;                         // stage 2 fills such rows directly
+    constexpr int kChunk = REG * kPerIter;
     const int base = c * kChunk;
     const int m = max(0, min(kChunk, n - base));
     const size_t slot0 = (static_cast<size_t>(row) * n_chunks + c) * k;
@@ -350,7 +342,7 @@ void topk_chunk_kernel(const float* __restrict__ scores, const int32_t* __restri
         for (int j = threadIdx.x; j < m; j += kThreads) { ck[j] = score_key(sc[j]); cp[j] = base + j; }
         return;
     }
-    Keys<2, ScoreSrc> ks;
+    Keys<REG, ScoreSrc> ks;
     ks.init(ScoreSrc{scores + static_cast<size_t>(row) * Lmax + base, m, ((Lmax | base) & 3) == 0}, m);
     block_select(ks, k, sh, [&](uint32_t slot, int i, uint32_t key) { ck[slot] = key; cp[slot] = base + i; });
 }
@@ -378,14 +370,20 @@ void topk_merge_kernel(const uint32_t* __restrict__ cand_key, const int32_t* __r
     block_select(ks, k, sh, [&](uint32_t slot, int i, uint32_t) { out[slot] = cp[i]; });
 }
 
-int n_chunks_for(int Lmax) { return (Lmax + kChunk - 1) / kChunk; }
-bool two_stage(int Lmax, int k) { return Lmax > kSingleMax && k < kChunk; }
+// Chunk length of the two-stage form: 8192 positions while the candidates of a row fit
+// the register-held merge (16384 keys), else 16384.
+int chunk_for(int Lmax, int k) {
+    const long long c8 = (Lmax + 2 * kPerIter - 1) / (2 * kPerIter);
+    return c8 * k <= kSingleMax ? 2 * kPerIter : 4 * kPerIter;
+}
+int n_chunks_for(int Lmax, int k) { const int c = chunk_for(Lmax, k); return (Lmax + c - 1) / c; }
+bool two_stage(int Lmax, int k) { return Lmax > kSingleMax && k < 2 * kPerIter; }
 
 }  // namespace
 
 size_t topk_workspace_bytes(int B, int T, int Lmax, int k) {
     if (!two_stage(Lmax, k)) return 0;
-    return static_cast<size_t>(B) * T * n_chunks_for(Lmax) * k * (sizeof(uint32_t) + sizeof(int32_t)) + 256;
+    return static_cast<size_t>(B) * T * n_chunks_for(Lmax, k) * k * (sizeof(uint32_t) + sizeof(int32_t)) + 256;
 }
 
 hipError_t launch_topk(const TopkArgs& a, void* ws, hipStream_t stream) {
@@ -400,19 +398,21 @@ hipError_t launch_topk(const TopkArgs& a, void* ws, hipStream_t stream) {
             hipLaunchKernelGGL(topk_row_kernel<0>, dim3(rows), block, 0, stream, a.scores, a.len, a.T, a.Lmax, a.k, a.idx);
         return hipGetLastError();
     }
-    const int nch = n_chunks_for(a.Lmax);
+    const int nch = n_chunks_for(a.Lmax, a.k);
     const size_t ncand = static_cast<size_t>(rows) * nch * a.k;
     uint32_t* ck = static_cast<uint32_t*>(ws);
     int32_t* cp = reinterpret_cast<int32_t*>(ck + ncand);
-    hipLaunchKernelGGL(topk_chunk_kernel, dim3(rows * nch), block, 0, stream, a.scores, a.len, a.T,
-                       a.Lmax, a.k, nch, ck, cp);
+    if (chunk_for(a.Lmax, a.k) == 2 * kPerIter)
+        hipLaunchKernelGGL(topk_chunk_kernel<2>, dim3(rows * nch), block, 0, stream, a.scores, a.len,
+                           a.T, a.Lmax, a.k, nch, ck, cp);
+    else
+        hipLaunchKernelGGL(topk_chunk_kernel<4>, dim3(rows * nch), block, 0, stream, a.scores, a.len,
+                           a.T, a.Lmax, a.k, nch, ck, cp);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const long long nc = static_cast<long long>(nch) * a.k;
-    if (nc <= 4 * kPerIter)
+    if (nc <= kSingleMax)
         hipLaunchKernelGGL(topk_merge_kernel<4>, dim3(rows), block, 0, stream, ck, cp, a.len, a.T, a.Lmax, a.k, nch, a.idx);
-    else if (nc <= kMaxIters * kPerIter)
-        hipLaunchKernelGGL(topk_merge_kernel<kMaxIters>, dim3(rows), block, 0, stream, ck, cp, a.len, a.T, a.Lmax, a.k, nch, a.idx);
     else
         hipLaunchKernelGGL(topk_merge_kernel<0>, dim3(rows), block, 0, stream, ck, cp, a.len, a.T, a.Lmax, a.k, nch, a.idx);
     return hipGetLastError();
