@@ -162,6 +162,9 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="the CPU-oracle sample repeats until this much wall time has passed")
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="only run a plain device copy of MIB MiB (10 times) and exit: the "
+                         "reference point for scaling rocprofv3 FETCH_SIZE / WRITE_SIZE")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only: this build has no multi-GPU path "
@@ -169,6 +172,16 @@ def main():
         sys.exit(2)
 
     import torch
+
+    if args.copy_calibration:
+        n = args.copy_calibration * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(10):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes_per_launch": 4 * n}))
+        return
 
     import deepseek_dsa_indexer_amd as D
     import dsa_synth as S

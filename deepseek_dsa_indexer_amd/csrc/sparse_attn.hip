@@ -478,7 +478,11 @@ void mla_decode_mfma_kernel(const uint16_t* __restrict__ q, const uint16_t* __re
         g_l[16 * wave + n] = st.l_run;
         g_m[16 * wave + n] = st.m_run;
     }
-    __syncthreads();
+    __syncthreads();      // every wave is past its last PV: the tile ring is free
+    // Stage the normalised bf16 rows [head][512] in LDS (16-byte chunks XOR-swizzled by
+    // head & 15 so the four head rows a store instruction touches use different banks),
+    // then write them out as whole 1 KB head rows with 16-byte stores.
+    uint16_t* stage = reinterpret_cast<uint16_t*>(g_kbuf);
 #pragma unroll
     for (int h = 0; h < NHT; ++h) {
 #pragma unroll
@@ -489,13 +493,20 @@ void mla_decode_mfma_kernel(const uint16_t* __restrict__ q, const uint16_t* __re
 #pragma unroll
             for (int dt = 0; dt < kDtW; ++dt) {
                 const int d = 64 * wave + 16 * dt + n;
-                const uint16_t v = f32_to_bf16(st.o[h][dt][i] * inv);
-                if (n_splits == 1)
-                    out[(static_cast<size_t>(row) * H + head) * kDv + d] = v;
-                else
-                    part_o[((static_cast<size_t>(row) * n_splits + split) * H + head) * kDv + d] = v;
+                const int pc = (d >> 3) ^ (head & 15);
+                stage[head * kDv + pc * 8 + (d & 7)] = f32_to_bf16(st.o[h][dt][i] * inv);
             }
         }
+    }
+    __syncthreads();
+    uint16_t* dst = n_splits == 1 ? out + static_cast<size_t>(row) * H * kDv
+                                  : part_o + (static_cast<size_t>(row) * n_splits + split) * H * kDv;
+    for (int c = threadIdx.x; c < H * (kDv / 8); c += kMlaThreads) {
+        const int head = c / (kDv / 8);
+        const int lc = c - head * (kDv / 8);
+        const int pc = lc ^ (head & 15);
+        *reinterpret_cast<uint4*>(dst + head * kDv + lc * 8) =
+            *reinterpret_cast<const uint4*>(stage + head * kDv + pc * 8);
     }
     if (threadIdx.x < H) {
         const int head = threadIdx.x;
@@ -518,13 +529,13 @@ void mla_combine_kernel(const uint16_t* __restrict__ part_o, const float* __rest
                         int rows, int H, int n_splits, uint16_t* __restrict__ out,
                         float* __restrict__ lse)
 {
-    const size_t gid = static_cast<size_t>(blockIdx.x) * blockDim.x + threadIdx.x;
-    const size_t total = static_cast<size_t>(rows) * H * (kDv / kCombCols);
-    if (gid >= total) return;
-    const int d8 = static_cast<int>(gid % (kDv / kCombCols));
-    const size_t rh = gid / (kDv / kCombCols);
-    const int h = static_cast<int>(rh % H);
-    const size_t row = rh / H;
+    // block = part * rows + row: a row's blocks share the XCD (block % 8) that ran its
+    // splits, so the partials are read from that XCD's L2 when rows is a multiple of 8
+    const size_t row = blockIdx.x % rows;
+    const int gid = (blockIdx.x / rows) * blockDim.x + threadIdx.x;
+    if (gid >= H * (kDv / kCombCols)) return;
+    const int d8 = gid % (kDv / kCombCols);
+    const int h = gid / (kDv / kCombCols);
     float ls[kMaxSplits];
     float M = -INFINITY;
 #pragma unroll
@@ -616,9 +627,9 @@ hipError_t launch_mla_decode_mfma(const void* q, const void* latent, const int32
                            qp, lp, idx, len, T, Lmax, k, tps, s, scale_log2, op, lse, part_o, part_lse);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || s == 1) return e;
-    const size_t total = static_cast<size_t>(rows) * H * (kDv / kCombCols);
+    const int parts = (H * (kDv / kCombCols) + 255) / 256;
     prof_mark(stream, kPhaseCombine);
-    hipLaunchKernelGGL(mla_combine_kernel, dim3((total + 255) / 256), dim3(256), 0, stream,
+    hipLaunchKernelGGL(mla_combine_kernel, dim3(rows * parts), dim3(256), 0, stream,
                        part_o, part_lse, rows, H, s, op, lse);
     return hipGetLastError();
 }
