@@ -26,6 +26,8 @@
 // cross-lane exchanges finish the head sum, so lane l ends with the score of key
 // (chunk + l): one coalesced 256-byte store per row and chunk.  Heads beyond H_I and
 // columns beyond d_I are zero (weight 0), which covers the small test shapes.
+#include <algorithm>
+
 #include "dsa_device.h"
 #include "dsa_internal.h"
 
@@ -35,6 +37,7 @@ namespace {
 
 constexpr int kThreads = 256;       // 4 waves
 constexpr int kChunk = 64;          // keys per wave iteration (4 MFMA column tiles)
+constexpr int kMaxHeads = 64;       // indexer heads (4 MFMA row tiles)
 
 typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
 
@@ -76,15 +79,17 @@ __device__ __forceinline__ float head_sum_transpose(const float s[4], int g) {
     return (odd ? a1 : a0) + r;
 }
 
-template <int D, int QR, int CHUNKS>
+template <int D, int QR>
 __global__ __launch_bounds__(kThreads)
 void index_scores_kernel(const uint8_t* __restrict__ q, const float* __restrict__ q_scale,
                          const float* __restrict__ w, const uint8_t* __restrict__ k,
                          const float* __restrict__ k_scale, const int32_t* __restrict__ len,
                          int T, int H, int Lmax, float sm_scale, float* __restrict__ scores,
-                         int fill_invisible)
+                         int fill_invisible, int chunks)
 {
-    constexpr int kKeysPerBlock = kThreads / kWave * kChunk * CHUNKS;
+    __shared__ __attribute__((aligned(16))) uint8_t s_q[QR][kMaxHeads * 128];
+    __shared__ __attribute__((aligned(16))) float s_wf[QR][kMaxHeads];
+    const int keys_per_block = kThreads / kWave * kChunk * chunks;
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = threadIdx.x / kWave;
     const int g = lane >> 4;
@@ -97,12 +102,12 @@ void index_scores_kernel(const uint8_t* __restrict__ q, const float* __restrict_
     const int pos0 = min(len[b], Lmax) - T + t0;   // position of row t0
     const int pos_hi = pos0 + nrows - 1;
 
-    const int key_blk = blockIdx.y * kKeysPerBlock;
+    const int key_blk = blockIdx.y * keys_per_block;
     float* out = scores + (static_cast<size_t>(b) * T + t0) * Lmax;
 
     if (key_blk > pos_hi) {                     // the whole block is masked
         if (fill_invisible) {
-            for (int key = key_blk + threadIdx.x; key < min(key_blk + kKeysPerBlock, Lmax); key += kThreads)
+            for (int key = key_blk + threadIdx.x; key < min(key_blk + keys_per_block, Lmax); key += kThreads)
                 for (int r = 0; r < nrows; ++r) out[static_cast<size_t>(r) * Lmax + key] = -INFINITY;
         }
         return;
@@ -114,7 +119,7 @@ void index_scores_kernel(const uint8_t* __restrict__ q, const float* __restrict_
     auto chunk_key = [&](int c) { return key_blk + (c * (kThreads / kWave) + wave) * kChunk; };
     auto load_chunk = [&](int c, v8i (&dst)[4], float& ks) {
         const int kb = chunk_key(c);
-        const bool live = c < CHUNKS && kb <= pos_hi;
+        const bool live = c < chunks && kb <= pos_hi;
 #pragma unroll
         for (int tile = 0; tile < 4; ++tile) {
             const int key = kb + 16 * tile + n;
@@ -127,52 +132,51 @@ void index_scores_kernel(const uint8_t* __restrict__ q, const float* __restrict_
         ks = ks_ptr[min(kb + lane, Lmax - 1)];
     };
 
-    // ---- query operands (bf16) and folded head weights, kept in registers.  Their loads
-    // are issued before the key loads, so waiting for them leaves the keys in flight.
-    v8bf qa[QR][4][4];
-    float wf[QR][4][4];
-    {
-        v8i raw[QR][4];
-        float wv[QR][4][4], qsv[QR][4][4];
-#pragma unroll
-        for (int r = 0; r < QR; ++r) {
-            const size_t qrow = static_cast<size_t>(b) * T + t0 + min(r, nrows - 1);
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int head = 16 * j + n;
-                const bool ok = r < nrows && head < H && g * 32 < D;
-                raw[r][j] = load32(q + (qrow * H + min(head, H - 1)) * D + (g * 32 < D ? g * 32 : 0), ok);
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int hh = min(16 * j + 4 * g + i, H - 1);
-                    wv[r][j][i] = w[qrow * H + hh];
-                    qsv[r][j][i] = q_scale[qrow * H + hh];
-                }
-            }
-        }
-#pragma unroll
-        for (int r = 0; r < QR; ++r)
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-#pragma unroll
-                for (int kk = 0; kk < 4; ++kk)
-                    qa[r][j][kk] = fp8x8_to_bf16(raw[r][j][2 * kk], raw[r][j][2 * kk + 1]);
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    // arithmetic mask (no branch): padded heads and rows get weight 0
-                    const float ok = (r < nrows && 16 * j + 4 * g + i < H) ? 1.f : 0.f;
-                    wf[r][j][i] = wv[r][j][i] * qsv[r][j][i] * sm_scale * ok;
-                }
-            }
-    }
-
-    // ---- two chunks of keys in flight ahead of the arithmetic
+    // ---- the block's query rows and folded head weights go through LDS once: q as
+    // [64 heads][128 bytes] (zero past H heads and D bytes), w * q_scale * sm_scale
+    // (zero past H heads and for padded rows).  The first two key chunks of every wave
+    // are already in flight meanwhile.
     v8i cur[4], nxt[4];
     float ks_cur, ks_nxt;
     load_chunk(0, cur, ks_cur);
     load_chunk(1, nxt, ks_nxt);
+    for (int i = threadIdx.x; i < QR * kMaxHeads * 8; i += kThreads) {
+        const int r = i / (kMaxHeads * 8);
+        const int h = (i / 8) % kMaxHeads;
+        const int c16 = i % 8;
+        const bool ok = r < nrows && h < H && c16 * 16 < D;
+        const size_t qrow = static_cast<size_t>(b) * T + t0 + min(r, nrows - 1);
+        const uint4 v = *reinterpret_cast<const uint4*>(
+            q + (qrow * H + min(h, H - 1)) * D + (c16 * 16 < D ? c16 * 16 : 0));
+        *reinterpret_cast<uint4*>(&s_q[r][h * 128 + c16 * 16]) = ok ? v : uint4{0u, 0u, 0u, 0u};
+    }
+    for (int i = threadIdx.x; i < QR * kMaxHeads; i += kThreads) {
+        const int r = i / kMaxHeads;
+        const int h = i % kMaxHeads;
+        const size_t qrow = static_cast<size_t>(b) * T + t0 + min(r, nrows - 1);
+        const int hc = min(h, H - 1);
+        const float okf = (r < nrows && h < H) ? 1.f : 0.f;
+        s_wf[r][h] = w[qrow * H + hc] * q_scale[qrow * H + hc] * sm_scale * okf;
+    }
+    __syncthreads();
+    v8bf qa[QR][4][4];
+    float wf[QR][4][4];
+#pragma unroll
+    for (int r = 0; r < QR; ++r)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const uint4* src = reinterpret_cast<const uint4*>(&s_q[r][(16 * j + n) * 128 + 32 * g]);
+            const uint4 lo = src[0], hi = src[1];
+            const int raw[8] = {static_cast<int>(lo.x), static_cast<int>(lo.y), static_cast<int>(lo.z),
+                                static_cast<int>(lo.w), static_cast<int>(hi.x), static_cast<int>(hi.y),
+                                static_cast<int>(hi.z), static_cast<int>(hi.w)};
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk) qa[r][j][kk] = fp8x8_to_bf16(raw[2 * kk], raw[2 * kk + 1]);
+            const float4 wv = *reinterpret_cast<const float4*>(&s_wf[r][16 * j + 4 * g]);
+            wf[r][j][0] = wv.x; wf[r][j][1] = wv.y; wf[r][j][2] = wv.z; wf[r][j][3] = wv.w;
+        }
 
-    for (int c = 0; c < CHUNKS; ++c) {
+    for (int c = 0; c < chunks; ++c) {
         const int kb = chunk_key(c);
         const int key = kb + lane;
         if (kb > pos_hi) {
@@ -213,25 +217,29 @@ void index_scores_kernel(const uint8_t* __restrict__ q, const float* __restrict_
 #pragma unroll
         for (int tile = 0; tile < 4; ++tile) cur[tile] = nxt[tile];
         ks_cur = ks_nxt;
-        if (c + 2 < CHUNKS) load_chunk(c + 2, nxt, ks_nxt);
+        if (c + 2 < chunks) load_chunk(c + 2, nxt, ks_nxt);
     }
 }
 
-template <int D, int QR, int CHUNKS>
-hipError_t launch_d(const IndexScoresArgs& a, hipStream_t stream) {
-    constexpr int kKeysPerBlock = kThreads / kWave * kChunk * CHUNKS;
+template <int D, int QR>
+hipError_t launch_d(const IndexScoresArgs& a, int chunks, hipStream_t stream) {
+    const int keys_per_block = kThreads / kWave * kChunk * chunks;
     const int row_groups = (a.T + QR - 1) / QR;
-    dim3 grid(a.B * row_groups, (a.Lmax + kKeysPerBlock - 1) / kKeysPerBlock);
-    hipLaunchKernelGGL((index_scores_kernel<D, QR, CHUNKS>), grid, dim3(kThreads), 0, stream,
+    dim3 grid(a.B * row_groups, (a.Lmax + keys_per_block - 1) / keys_per_block);
+    hipLaunchKernelGGL((index_scores_kernel<D, QR>), grid, dim3(kThreads), 0, stream,
                        a.q, a.q_scale, a.w, a.k, a.k_scale, a.len, a.T, a.H, a.Lmax, a.sm_scale,
-                       a.scores, a.fill_invisible);
+                       a.scores, a.fill_invisible, chunks);
     return hipGetLastError();
 }
 
+// Key chunks per wave: enough waves to cover every SIMD twice (2048 waves), then longer
+// streams per wave (up to 8 chunks) so the block's query and weight set-up is amortised.
 template <int D>
 hipError_t launch_rows(const IndexScoresArgs& a, hipStream_t stream) {
-    if (a.T >= 2) return launch_d<D, 2, 1>(a, stream);
-    return launch_d<D, 1, 2>(a, stream);
+    if (a.T >= 2) return launch_d<D, 2>(a, 4, stream);
+    const long long total_chunks = static_cast<long long>(a.B) * ((a.Lmax + kChunk - 1) / kChunk);
+    const int chunks = static_cast<int>(std::min<long long>(8, std::max<long long>(2, total_chunks / 2048)));
+    return launch_d<D, 1>(a, chunks, stream);
 }
 
 }  // namespace
