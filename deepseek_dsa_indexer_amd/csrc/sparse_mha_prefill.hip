@@ -10,16 +10,19 @@
 // bit mask built from idx by select_mask_kernel (bit s of row t set iff s is selected
 // and s <= t).  Masked-dense work is about 2.3x the selected pairs at T = 8192, k = 2048.
 //
-// Mapping.  One workgroup (4 waves) owns one head and 64 query rows; wave w owns rows
-// 16w..16w+15.  Per key block of 64 positions:
+// Mapping.  One workgroup (4 waves) owns one head and 128 query rows; wave w owns rows
+// 32w..32w+31 as two 16-row query tiles, so every K and V operand read from LDS feeds
+// two matrix-core products.  Per key block of 64 positions:
 //   load  K [64 x 192] and V [64 x 128] bf16 rows into LDS with direct global->LDS
-//         16-byte loads, double buffered, 16-byte chunks XOR-swizzled per row;
-//   QK    S^T = K . Q^T (keys as MFMA rows, the wave's 16 queries as 6 B operands in
-//         registers), so lane (g, n) holds query row n and keys 16 kt + 4 g + i;
-//   mask  selection bits of row n and the causal bound;
+//         16-byte loads, double buffered, 16-byte chunks XOR-swizzled per row; the
+//         selection-mask words of the next block are fetched with them;
+//   QK    S^T = K . Q^T (keys as MFMA rows, each query tile's 16 queries as 6 B
+//         operands in registers), so lane (g, n) holds query row n of the tile and keys
+//         16 kt + 4 g + i;
+//   mask  selection bits of the row and the causal bound;
 //   softmax online per row, entirely in the wave; the probabilities stay in registers
 //         in the A-operand layout of the PV product;
-//   PV    O [16 x 128] += P . V, V operands by LDS transpose reads.
+//   PV    O [32 x 128] += P . V, V operands by LDS transpose reads.
 #include "dsa_device.h"
 #include "dsa_internal.h"
 
@@ -29,7 +32,8 @@ namespace {
 
 constexpr int kMhaThreads = 256;
 constexpr int kMhaWaves = 4;
-constexpr int kQB = 64;                 // query rows per workgroup
+constexpr int kQT = 2;                  // 16-row query tiles per wave
+constexpr int kQB = 16 * kQT * 4;       // query rows per workgroup (128)
 constexpr int kKB = 64;                 // keys per block
 constexpr int kDqk = 192;
 constexpr int kDvM = 128;
@@ -95,14 +99,15 @@ __device__ __forceinline__ void load_block(const uint8_t* kbase, const uint8_t* 
 __device__ __forceinline__ void lds_sync() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
 struct MhaState {
-    v8bf qreg[kDqk / 32];       // 6 K-steps
-    v4f o[kDvM / 16];           // 8 column tiles
-    float m_run, l_run;
+    v8bf qreg[kQT][kDqk / 32];  // 6 K-steps per query tile
+    v4f o[kQT][kDvM / 16];      // 8 column tiles per query tile
+    float m_run[kQT], l_run[kQT];
 };
 
 template <int BUF>
-__device__ __forceinline__ void mha_block(MhaState& st, const uint32_t* __restrict__ mrow,
-                                          int words, int t_row, int s0, float scale_log2, int lane) {
+__device__ __forceinline__ void mha_block(MhaState& st, const uint32_t (&mw)[kQT][2],
+                                          const int (&t_row)[kQT], int s0, float scale_log2,
+                                          int lane) {
     const uint8_t* kb = BUF ? m_k1 : m_k0;
     const uint8_t* vb = BUF ? m_v1 : m_v0;
     int lo = lane;
@@ -110,65 +115,70 @@ __device__ __forceinline__ void mha_block(MhaState& st, const uint32_t* __restri
     const int g = lo >> 4;
     const int n = lo & 15;
 
-    // ---- S^T = K . Q^T: 4 key tiles x 6 K-steps
-    v4f sacc[4];
+    // ---- S^T = K . Q^T: 4 key tiles x 6 K-steps, each K operand used by both query tiles
+    v4f sacc[kQT][4];
 #pragma unroll
-    for (int kt = 0; kt < 4; ++kt) sacc[kt] = v4f{0.f, 0.f, 0.f, 0.f};
+    for (int qt = 0; qt < kQT; ++qt)
+#pragma unroll
+        for (int kt = 0; kt < 4; ++kt) sacc[qt][kt] = v4f{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int ds = 0; ds < kDqk / 32; ++ds) {
 #pragma unroll
         for (int kt = 0; kt < 4; ++kt) {
             const int key = 16 * kt + n;
             const v8bf a = *reinterpret_cast<const v8bf*>(kb + key * kKRow + swz8(key, ds * 4 + g) * 16);
-            sacc[kt] = mfma_bf16_16x16x32(a, st.qreg[ds], sacc[kt]);
+#pragma unroll
+            for (int qt = 0; qt < kQT; ++qt) sacc[qt][kt] = mfma_bf16_16x16x32(a, st.qreg[qt][ds], sacc[qt][kt]);
         }
         __builtin_amdgcn_sched_barrier(0);
     }
-    // ---- selection bits of query row t_row for keys s0 + 16 kt + 4 g + i
-    const uint32_t w0 = (s0 >> 5) < words ? mrow[s0 >> 5] : 0u;
-    const uint32_t w1 = (s0 >> 5) + 1 < words ? mrow[(s0 >> 5) + 1] : 0u;
-    float sv[16];
-    float mx = -INFINITY;
+    // ---- mask + online softmax per query tile; keys s0 + 16 kt + 4 g + i
+    v8s pk[kQT][2];
 #pragma unroll
-    for (int kt = 0; kt < 4; ++kt)
+    for (int qt = 0; qt < kQT; ++qt) {
+        float sv[16];
+        float mx = -INFINITY;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int kk = 16 * kt + 4 * g + i;              // 0..63
-            const uint32_t word = kk < 32 ? w0 : w1;
-            const bool sel = (word >> (kk & 31)) & 1u;
-            const bool vis = s0 + kk <= t_row;
-            const float v = (sel && vis) ? sacc[kt][i] * scale_log2 : -INFINITY;
-            sv[4 * kt + i] = v;
-            mx = fmaxf(mx, v);
+        for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int kk = 16 * kt + 4 * g + i;              // 0..63
+                const uint32_t word = kk < 32 ? mw[qt][0] : mw[qt][1];
+                const bool sel = (word >> (kk & 31)) & 1u;
+                const bool vis = s0 + kk <= t_row[qt];
+                const float v = (sel && vis) ? sacc[qt][kt][i] * scale_log2 : -INFINITY;
+                sv[4 * kt + i] = v;
+                mx = fmaxf(mx, v);
+            }
+        mx = fmaxf(mx, __shfl_xor(mx, 16, kWave));
+        mx = fmaxf(mx, __shfl_xor(mx, 32, kWave));
+        float alpha = 1.f;
+        if (mx > st.m_run[qt] + kLazy) {
+            // nothing accumulated yet (O = 0, l = 0): no rescale needed
+            alpha = (st.m_run[qt] == -INFINITY) ? 1.f : exp2f(st.m_run[qt] - mx);
+            st.m_run[qt] = mx;
         }
-    mx = fmaxf(mx, __shfl_xor(mx, 16, kWave));
-    mx = fmaxf(mx, __shfl_xor(mx, 32, kWave));
-    float alpha = 1.f;
-    if (mx > st.m_run + kLazy) {
-        alpha = (st.m_run == -INFINITY) ? 0.f : exp2f(st.m_run - mx);
-        st.m_run = mx;
-    }
-    v8s pk[2];
-    float psum = 0.f;
+        float psum = 0.f;
 #pragma unroll
-    for (int j = 0; j < 16; ++j) {
-        const float p = (sv[j] == -INFINITY) ? 0.f : exp2f(sv[j] - st.m_run);
-        psum += p;
-        pk[j >> 3][j & 7] = static_cast<short>(f32_to_bf16(p));
-    }
-    psum += __shfl_xor(psum, 16, kWave);
-    psum += __shfl_xor(psum, 32, kWave);
-    st.l_run = st.l_run * alpha + psum;
-    // alpha is per query row n: the O rows of this lane are rows 4 g + i, held by lanes
-    // n' = 4 g + i; fetch their alphas
-    if (__ballot(alpha != 1.f)) {
-        float a4[4];
+        for (int j = 0; j < 16; ++j) {
+            const float p = (sv[j] == -INFINITY) ? 0.f : exp2f(sv[j] - st.m_run[qt]);
+            psum += p;
+            pk[qt][j >> 3][j & 7] = static_cast<short>(f32_to_bf16(p));
+        }
+        psum += __shfl_xor(psum, 16, kWave);
+        psum += __shfl_xor(psum, 32, kWave);
+        st.l_run[qt] = st.l_run[qt] * alpha + psum;
+        // alpha is per query row n: the O rows of this lane are rows 4 g + i, held by
+        // lanes n' = 4 g + i; fetch their alphas
+        if (__ballot(alpha != 1.f)) {
+            float a4[4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) a4[i] = __shfl(alpha, 4 * g + i, kWave);
+            for (int i = 0; i < 4; ++i) a4[i] = __shfl(alpha, 4 * g + i, kWave);
 #pragma unroll
-        for (int dt = 0; dt < kDvM / 16; ++dt)
+            for (int dt = 0; dt < kDvM / 16; ++dt)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) st.o[dt][i] *= a4[i];
+                for (int i = 0; i < 4; ++i) st.o[qt][dt][i] *= a4[i];
+        }
     }
     // ---- O += P . V: K-step 0 covers keys of tiles 0, 1 (slots j = 4 kt + i), K-step 1
     // tiles 2, 3.  V operand of K-step ks: rows 32 ks + 16 kk + 4 g + r (kk = 0, 1).
@@ -186,12 +196,27 @@ __device__ __forceinline__ void mha_block(MhaState& st, const uint32_t* __restri
             }
             const v8bf vop = v8bf{half[0][0], half[0][1], half[0][2], half[0][3],
                                   half[1][0], half[1][1], half[1][2], half[1][3]};
-            st.o[dt] = mfma_bf16_16x16x32(__builtin_bit_cast(v8bf, pk[ks]), vop, st.o[dt]);
+#pragma unroll
+            for (int qt = 0; qt < kQT; ++qt)
+                st.o[qt][dt] = mfma_bf16_16x16x32(__builtin_bit_cast(v8bf, pk[qt][ks]), vop, st.o[qt][dt]);
         }
     }
 }
 
-__global__ __launch_bounds__(kMhaThreads)
+// Selection-mask words of key block s0 for the wave's query rows (zero past the row).
+__device__ __forceinline__ void load_mask(const uint32_t* const (&mrow)[kQT], int words, int s0,
+                                          uint32_t (&mw)[kQT][2]) {
+#pragma unroll
+    for (int qt = 0; qt < kQT; ++qt) {
+        const int w0 = s0 >> 5;
+        mw[qt][0] = mrow[qt][min(w0, words - 1)];
+        mw[qt][1] = mrow[qt][min(w0 + 1, words - 1)];
+        if (w0 >= words) mw[qt][0] = 0u;
+        if (w0 + 1 >= words) mw[qt][1] = 0u;
+    }
+}
+
+__global__ __launch_bounds__(kMhaThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void mha_prefill_mfma_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
                              const uint16_t* __restrict__ v, const uint32_t* __restrict__ mask,
                              int B, int T, int H, float scale_log2, uint16_t* __restrict__ out,
@@ -202,70 +227,88 @@ void mha_prefill_mfma_kernel(const uint16_t* __restrict__ q, const uint16_t* __r
     const int g = lane >> 4;
     const int n = lane & 15;
     const int qblocks = (T + kQB - 1) / kQB;
-    // heaviest query blocks (most key blocks under the causal bound) first
-    const int qb = qblocks - 1 - (blockIdx.x % qblocks);
-    const int bh = blockIdx.x / qblocks;
+    // Block j * (B H) + bh: heaviest query blocks (most key blocks under the causal
+    // bound) first, and all query blocks of a head on one XCD (workgroups go round robin
+    // over the 8 XCDs, B H being a multiple of 8 at the model's head counts), so the
+    // head's K and V blocks are fetched into one L2 and shared there.
+    const int qb = qblocks - 1 - static_cast<int>(blockIdx.x / (B * H));
+    const int bh = static_cast<int>(blockIdx.x % (B * H));
     const int h = bh % H;
     const int b = bh / H;
     const int t0 = qb * kQB;
     const int words = (T + 31) / 32;
 
-    const int t_row = min(t0 + 16 * wave + n, T - 1);       // query row of this lane
-    const bool row_ok = t0 + 16 * wave + n < T;
-    const uint32_t* mrow = mask + (static_cast<size_t>(b) * T + t_row) * words;
-
+    int t_row[kQT];                         // query row of this lane in each tile
+    const uint32_t* mrow[kQT];
     MhaState st;
-    {
-        const uint16_t* qrow = q + ((static_cast<size_t>(b) * T + t_row) * H + h) * kDqk + 8 * g;
 #pragma unroll
-        for (int ds = 0; ds < kDqk / 32; ++ds) st.qreg[ds] = *reinterpret_cast<const v8bf*>(qrow + 32 * ds);
+    for (int qt = 0; qt < kQT; ++qt) {
+        t_row[qt] = min(t0 + 32 * wave + 16 * qt + n, T - 1);
+        mrow[qt] = mask + (static_cast<size_t>(b) * T + t_row[qt]) * words;
+        const uint16_t* qrow = q + ((static_cast<size_t>(b) * T + t_row[qt]) * H + h) * kDqk + 8 * g;
+#pragma unroll
+        for (int ds = 0; ds < kDqk / 32; ++ds) st.qreg[qt][ds] = *reinterpret_cast<const v8bf*>(qrow + 32 * ds);
+#pragma unroll
+        for (int dt = 0; dt < kDvM / 16; ++dt) st.o[qt][dt] = v4f{0.f, 0.f, 0.f, 0.f};
+        st.m_run[qt] = -INFINITY;
+        st.l_run[qt] = 0.f;
     }
+    uint32_t mcur[kQT][2], mnext[kQT][2];
+    load_mask(mrow, words, 0, mcur);
 #pragma unroll
-    for (int dt = 0; dt < kDvM / 16; ++dt) st.o[dt] = v4f{0.f, 0.f, 0.f, 0.f};
-    st.m_run = -INFINITY;
-    st.l_run = 0.f;
+    for (int qt = 0; qt < kQT; ++qt)
 #pragma unroll
-    for (int ds = 0; ds < kDqk / 32; ++ds) asm volatile("" :: "v"(st.qreg[ds]));
+        for (int ds = 0; ds < kDqk / 32; ++ds) asm volatile("" :: "v"(st.qreg[qt][ds]));
 
     const uint8_t* kbase = reinterpret_cast<const uint8_t*>(k) + static_cast<size_t>(b) * T * H * kKRow;
     const uint8_t* vbase = reinterpret_cast<const uint8_t*>(v) + static_cast<size_t>(b) * T * H * kVRow;
     const int t_last = min(t0 + kQB, T) - 1;
     const int nblocks = t_last / kKB + 1;                    // causal: key blocks up to t_last
 
+    // Step j: wait for block j (and its mask words), put block j + 1 and its mask words
+    // in flight, compute block j.
     load_block(kbase, vbase, T, H, h, 0, m_k0, m_v0, wave, lane);
     for (int kb2 = 0; kb2 < nblocks; kb2 += 2) {
         // block kb2 in buffer 0, block kb2 + 1 in buffer 1
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         lds_sync();
-        if (kb2 + 1 < nblocks) load_block(kbase, vbase, T, H, h, (kb2 + 1) * kKB, m_k1, m_v1, wave, lane);
-        mha_block<0>(st, mrow, words, t_row, kb2 * kKB, scale_log2, lane);
+        if (kb2 + 1 < nblocks) {
+            load_block(kbase, vbase, T, H, h, (kb2 + 1) * kKB, m_k1, m_v1, wave, lane);
+            load_mask(mrow, words, (kb2 + 1) * kKB, mnext);
+        }
+        mha_block<0>(st, mcur, t_row, kb2 * kKB, scale_log2, lane);
         if (kb2 + 1 < nblocks) {
             asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
             lds_sync();
-            if (kb2 + 2 < nblocks) load_block(kbase, vbase, T, H, h, (kb2 + 2) * kKB, m_k0, m_v0, wave, lane);
-            mha_block<1>(st, mrow, words, t_row, (kb2 + 1) * kKB, scale_log2, lane);
+            if (kb2 + 2 < nblocks) {
+                load_block(kbase, vbase, T, H, h, (kb2 + 2) * kKB, m_k0, m_v0, wave, lane);
+                load_mask(mrow, words, (kb2 + 2) * kKB, mcur);
+            }
+            mha_block<1>(st, mnext, t_row, (kb2 + 1) * kKB, scale_log2, lane);
         }
     }
 
-    // ---- epilogue: rows 4 g + i of this wave's tile; l and m of row r sit in lane r
-    float inv4[4], lse4[4];
+    // ---- epilogue: rows 4 g + i of each query tile; l and m of row r sit in lane r
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const float l = __shfl(st.l_run, 4 * g + i, kWave);
-        const float m = __shfl(st.m_run, 4 * g + i, kWave);
-        inv4[i] = l > 0.f ? 1.f / l : 0.f;
-        lse4[i] = l > 0.f ? (m + log2f(l)) * kLn2M : -INFINITY;
+    for (int qt = 0; qt < kQT; ++qt) {
+        float inv4[4], lse4[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const float l = __shfl(st.l_run[qt], 4 * g + i, kWave);
+            const float m = __shfl(st.m_run[qt], 4 * g + i, kWave);
+            inv4[i] = l > 0.f ? 1.f / l : 0.f;
+            lse4[i] = l > 0.f ? (m + log2f(l)) * kLn2M : -INFINITY;
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int t = t0 + 32 * wave + 16 * qt + 4 * g + i;
+            if (t >= T) continue;
+            uint16_t* orow = out + ((static_cast<size_t>(b) * T + t) * H + h) * kDvM;
+#pragma unroll
+            for (int dt = 0; dt < kDvM / 16; ++dt) orow[16 * dt + n] = f32_to_bf16(st.o[qt][dt][i] * inv4[i]);
+            if (lse && n == 0) lse[(static_cast<size_t>(b) * T + t) * H + h] = lse4[i];
+        }
     }
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int t = t0 + 16 * wave + 4 * g + i;
-        if (t >= T) continue;
-        uint16_t* orow = out + ((static_cast<size_t>(b) * T + t) * H + h) * kDvM;
-#pragma unroll
-        for (int dt = 0; dt < kDvM / 16; ++dt) orow[16 * dt + n] = f32_to_bf16(st.o[dt][i] * inv4[i]);
-        if (lse && n == 0) lse[(static_cast<size_t>(b) * T + t) * H + h] = lse4[i];
-    }
-    (void)row_ok;
 }
 
 // Bit s of row (b,t) <- s is among idx[b,t,:] and s <= t.  One workgroup per row.
