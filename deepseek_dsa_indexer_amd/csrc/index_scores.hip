@@ -6,7 +6,7 @@
 // with -inf where s > pos(b,t) = len[b] - T + t.  The weight fold follows the
 // Indexer.forward excerpt ("DeepSeek-V3.2-Exp - Split indexer heads"); the per-head
 // ReLU and weighted head sum follow the score box of "dsa-indexer.excalidraw"; the
-// mask follows full(-inf).triu_(1) of the "Causal mask" page.
+// mask is the -inf-above-the-diagonal mask of the "Causal mask" page.
 //
 // Storage and arithmetic.  q and the key cache stay FP8 (e4m3fn) in memory, so the
 // stream is 128 + 4 bytes per key.  In registers every FP8 byte is widened to bf16

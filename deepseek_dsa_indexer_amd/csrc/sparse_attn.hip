@@ -2,9 +2,9 @@
 //
 // Two paths:
 //  * mla_decode_mfma_kernel: the absorbed (MQA) latent form of "dsa-indexer.excalidraw"
-//    ("core attention, MQA mode: q (128 heads) over the 2048 selected latents, each
-//    latent is key and value") at the V3.2 shape: bf16, 576-wide rows (latent 512 then
-//    rope 64), values = the first 512 columns, up to 128 heads, bf16 matrix cores.
+//    (core-attention box: all query heads share the selected latent rows, each row
+//    serving as key and value) at the V3.2 shape: bf16, 576-wide rows (latent 512 then
+//    rope 64), values = the first 512 columns, 64 or 128 heads, bf16 matrix cores.
 //  * sparse_attn_generic_kernel: any shape and f32/bf16, both the latent form and the
 //    MHA prefill form of the MLA prefill excerpt ("DeepSeek-V3.2-Exp - Causal mask",
 //    Multi-head latent attention), on the vector ALUs.  Used for small or unusual shapes.

@@ -1,8 +1,8 @@
 // topk.hip -- per-row top-k of the index scores by radix select (no sort).
 //
 // For row (b,t) with n = pos(b,t) + 1 visible scores, the kernels return the positions
-// of the min(k, n) largest ones (Indexer.forward excerpt, topk(min(index_topk,
-// end_pos)) on the "DeepSeek-V3.2-Exp - Split indexer heads" page), in ascending
+// of the min(k, n) largest ones (the Indexer.forward excerpt on the "DeepSeek-V3.2-Exp -
+// Split indexer heads" page keeps the index_topk best, capped at the visible count), in ascending
 // position order, followed by -1 in the unused slots (the warm-up sentinel of the
 // DeepSeek-V4 mask visualiser).  Equal scores resolve towards the smaller position, so
 // the output is deterministic.

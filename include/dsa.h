@@ -3,16 +3,20 @@
  * (libdsa_amd.so).
  *
  * One DSA layer step, as the pages describe it:
- *   1. lightning-indexer scores     ("DeepSeek-V3.2-Exp - Split indexer heads", Indexer.forward
- *                                     excerpt: weight fold, fp8_index; "dsa-indexer.excalidraw",
- *                                     score box I(t,s) = sum_j w_j ReLU(q_j . k_s));
- *   2. causal mask                   ("DeepSeek-V3.2-Exp - Causal mask", full(-inf).triu_(1));
- *   3. per-row top-k                 (Indexer.forward excerpt, topk(min(index_topk, end_pos));
- *                                     excalidraw "top-k selector, k = 2048");
+ *   1. lightning-indexer scores      ("DeepSeek-V3.2-Exp - Split indexer heads": the
+ *                                      Indexer.forward excerpt folds the query scales into
+ *                                      the head weights and scores FP8 queries against the
+ *                                      FP8 key cache; "dsa-indexer.excalidraw", score box:
+ *                                      per-head ReLU of q.k, weighted sum over heads);
+ *   2. causal mask                    ("DeepSeek-V3.2-Exp - Causal mask": -inf strictly
+ *                                      above the diagonal);
+ *   3. per-row top-k                  (Indexer.forward excerpt: the index_topk best
+ *                                      positions, never more than are visible; the
+ *                                      excalidraw top-k selector keeps 2048);
  *   4. sparse attention over the k selected positions, either in the absorbed latent
- *      (MQA) form of the excalidraw diagram ("core attention, MQA mode ... each latent is
- *      key and value") or in the MHA prefill form of the MLA prefill excerpt ("Causal
- *      mask" page, Multi-head latent attention, prefill).
+ *      (MQA) form of the excalidraw diagram, where all query heads share the selected
+ *      latent rows and each row serves as key and value, or in the MHA prefill form of
+ *      the MLA prefill excerpt ("Causal mask" page, Multi-head latent attention).
  *
  * Conventions shared by every entry point
  *   - All tensor pointers are DEVICE pointers to dense row-major arrays, 16-byte aligned.
@@ -67,9 +71,10 @@ int dsa_version(void);
  *   scores[b,t,s] = k_scale[b,s] * sum_h (w[b,t,h] * q_scale[b,t,h] * sm_scale_I)
  *                                     * max(0, sum_d q[b,t,h,d] * k[b,s,d])
  *   for visible s, and -inf for every other s < Lmax.
- * ("Split indexer heads": weights = weights_proj(x) * n_heads^-0.5 is the caller's `w`;
- *  the library folds q_scale and softmax_scale as the excerpt does; the ReLU is the one
- *  in the excalidraw score box.)
+ * ("Split indexer heads": the caller's `w` is the projected head weight, already scaled
+ *  by the inverse square root of the head count; the library folds q_scale and the
+ *  indexer softmax scale into it as the excerpt does; the ReLU is the one in the
+ *  excalidraw score box.)
  *   q_fp8   [B,T,H_I,d_I] u8 e4m3fn     q_scale [B,T,H_I] f32     w [B,T,H_I] f32
  *   k_fp8   [B,Lmax,d_I]  u8 e4m3fn     k_scale [B,Lmax] f32      len [B] i32
  *   scores  [B,T,Lmax] f32 (output)
@@ -82,12 +87,14 @@ dsa_status dsa_index_scores(const uint8_t* q_fp8, const float* q_scale, const fl
 
 /*
  * dsa_topk -- per query row, the positions of the min(k, pos+1) largest visible scores.
- * (Indexer.forward: index_score.topk(min(index_topk, end_pos)); unused slots hold -1 as
- *  the DeepSeek-V4 mask visualiser's warm-up sentinel does.)
+ * (Indexer.forward excerpt: the index_topk best positions, capped at the number visible;
+ *  unused slots hold -1, the warm-up sentinel of the DeepSeek-V4 mask visualiser.)
  *   scores [B,T,Lmax] f32 (only positions 0..pos(b,t) are read)   len [B] i32
  *   idx    [B,T,k] i32 (output): the selected positions in ascending order, then -1.
  * Equal scores at the threshold are resolved in favour of the smaller position, so the
  * result is deterministic.  Scores must not be NaN.  Supported: 1 <= k, T <= Lmax.
+ * Rows longer than 16384 positions (Lmax > 16384 and k < 8192) use a workspace of
+ * dsa_topk_workspace_bytes() for per-chunk candidates; otherwise it is 0 bytes.
  */
 size_t dsa_topk_workspace_bytes(int B, int T, int Lmax, int k);
 dsa_status dsa_topk(const float* scores, const int32_t* len, int B, int T, int Lmax, int k,
@@ -95,8 +102,9 @@ dsa_status dsa_topk(const float* scores, const int32_t* len, int B, int T, int L
 
 /*
  * dsa_sparse_mla_decode -- absorbed (MQA) sparse attention over selected latent rows.
- * (excalidraw "core attention, MQA mode: q (128 heads) over the 2048 selected latents,
- *  each latent is key and value"; softmax and value mix as in the MLA prefill excerpt.)
+ * (excalidraw core-attention box: the 128 query heads share the 2048 selected latent
+ *  rows, each of which serves as key and value; softmax and value mix as in the MLA
+ *  prefill excerpt.)
  *   q      [B,T,H,Dv+Dr]   (absorbed query: Dv latent columns, then Dr rope columns)
  *   latent [B,Lmax,Dv+Dr]  (cache row: latent Dv, then rope Dr)
  *   idx    [B,T,k] i32     (slots < 0 and positions > pos(b,t) are ignored)
@@ -104,8 +112,12 @@ dsa_status dsa_topk(const float* scores, const int32_t* len, int B, int T, int L
  *                          scaled logits, or NULL.
  *   logit_j = sm_scale * q[b,t,h,:] . latent[b,s_j,:]; out = softmax(logit) @ latent[.,:Dv]
  * A row with no usable slot gets out = 0 and lse = -inf.  Entries of idx must be unique
- * per row.  Any H, Dv, Dr with Dv+Dr <= 1024 and dtype F32 or BF16; the bf16 shape
- * H % 16 == 0, H <= 128, Dv = 512, Dr = 64 runs on the matrix-core path.
+ * per row.  Any H, Dv, Dr with Dv+Dr <= 1024 and dtype F32 or BF16 (the vector-ALU path
+ * keeps all k logits in LDS: 4 (Dv + Dr + k) <= 65536 bytes); the bf16 shape H in
+ * {64, 128}, Dv = 512, Dr = 64, k <= 8192 runs on the matrix-core path, which splits
+ * each row's slots over up to 8 workgroups and needs a workspace for their partial
+ * results (dsa_sparse_mla_decode_workspace_bytes(); 0 when the rows fill the GPU
+ * without splitting).
  */
 size_t dsa_sparse_mla_decode_workspace_bytes(int B, int T, int H, int Dv, int Dr, int k,
                                              dsa_dtype dt);
@@ -117,13 +129,15 @@ dsa_status dsa_sparse_mla_decode(const void* q, const void* latent, const int32_
 /*
  * dsa_sparse_mla_prefill -- MHA-form sparse attention over a chunk that starts at
  * position 0 (keys and values are the chunk's own T positions, per head).
- * (MLA prefill excerpt: q = [q_nope | q_pe], k = [k_nope | k_pe], scores * softmax_scale
- *  + index_mask (0 at the top-k positions, -inf elsewhere) + causal mask, softmax,
- *  einsum with v.)
+ * (MLA prefill excerpt: query and key rows are the no-rope part followed by the rope
+ *  part; the scaled scores get an index mask, 0 at the selected positions and -inf
+ *  elsewhere, plus the causal mask, then a softmax mixes the value rows.)
  *   q, k [B,T,H,Dqk]   v [B,T,H,Dv]   idx [B,T,topk] i32 (slots < 0 or > t are ignored)
  *   out  [B,T,H,Dv] (same dtype), lse [B,T,H] f32 or NULL.
- * Supported: dtype F32 or BF16, Dqk <= 1024, Dv <= 1024; the bf16 shape Dqk = 192,
- * Dv = 128 runs on the matrix-core path.
+ * Supported: dtype F32 or BF16, Dqk <= 1024, Dv <= 1024 (the vector-ALU path keeps all
+ * topk logits in LDS: 4 (Dqk + topk) <= 65536 bytes); the bf16 shape Dqk = 192, Dv = 128
+ * runs on the matrix-core path, which needs a workspace for the per-row selection bit
+ * mask (B * T * ceil(T / 32) words; dsa_sparse_mla_prefill_workspace_bytes()).
  */
 size_t dsa_sparse_mla_prefill_workspace_bytes(int B, int T, int H, int Dqk, int Dv, int topk,
                                               dsa_dtype dt);
@@ -135,7 +149,11 @@ dsa_status dsa_sparse_mla_prefill(const void* q, const void* k, const void* v,
 /*
  * dsa_layer_step -- the whole step: index scores -> causal mask -> top-k -> sparse
  * attention, in the latent form (len[] per sequence, T rows at the end) or the MHA
- * prefill form (len[b] = T for every b, Lmax = T).
+ * prefill form (len[b] = T for every b, Lmax = T).  The workspace
+ * (dsa_layer_step_workspace_bytes(), 256-byte aligned) holds the scores and indices
+ * that are not requested as outputs, then one scratch region shared by the top-k
+ * candidates and the attention partials.  Errors as for the individual calls; nothing
+ * is enqueued when validation fails.
  */
 typedef struct dsa_layer_args {
     /* indexer */

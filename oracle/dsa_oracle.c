@@ -9,26 +9,31 @@
  * method itself ranks (the score tensor is fp32 on the pages).
  *
  * Sources (web pages, cited by title and section):
- *   [IDX]  "DeepSeek-V3.2-Exp - Split indexer heads", Indexer.forward excerpt:
- *          FP8 q/k with per-block scales, the weight fold (weights_proj * n_heads^-0.5,
- *          then * q_scale * softmax_scale), fp8_index, "+= mask", topk(min(k, end_pos)).
+ *   [IDX]  "DeepSeek-V3.2-Exp - Split indexer heads", Indexer.forward excerpt: FP8
+ *          queries and keys with per-block scales; the projected head weights (scaled
+ *          by the inverse square root of the head count) are multiplied by the query
+ *          scales and the indexer softmax scale; the score call is masked additively
+ *          and the best index_topk positions are kept, never more than are visible.
  *   [DIAG] "dsa-indexer.excalidraw" (one DSA decode step in one layer, V3.2 sizes):
- *          score formula I(t,s) = sum_j w_j ReLU(q_j . k_s); top-k selector k = 2048;
- *          gather of the selected latents; MQA core attention in which each latent row
- *          is both key and value; cost-per-token box.
+ *          the score of key s is the head-weighted sum of per-head ReLU(q . k_s); the
+ *          top-k selector keeps 2048; the selected latent rows are gathered and all
+ *          query heads attend to them (MQA), each row serving as key and value; the
+ *          per-token cost box.
  *   [MASK] "DeepSeek-V3.2-Exp - Causal mask", Transformer.forward excerpt: additive
- *          mask full(-inf).triu_(1) for seqlen > 1, none for decode.
- *   [MLA]  same page, MLA init / prefill excerpts: softmax_scale = qk_head_dim^-0.5,
- *          the MHA prefill form (scores = einsum * scale, index_mask scatter of the
- *          top-k, + causal mask, softmax, einsum with v).
- *   [V4]   "visualize_attention_masks.py" (DeepSeek-V4 mask visualiser): the -1
- *          warm-up sentinel for unused top-k slots.
+ *          -inf mask strictly above the diagonal when more than one row is processed,
+ *          no mask for single-row decode.
+ *   [MLA]  same page, MLA init and prefill excerpts: the softmax scale is the inverse
+ *          square root of the qk head width; the MHA prefill form scales dense scores,
+ *          adds an index mask (0 at the selected positions, -inf elsewhere) and the
+ *          causal mask, takes a softmax and mixes the value rows.
+ *   [V4]   "visualize_attention_masks.py" (DeepSeek-V4 mask visualiser): -1 marks
+ *          unused top-k slots.
  *
- * Conventions (the readings where the pages are silent are listed in the design
- * notes of the repository):
+ * Conventions (where the pages leave a point open, the plainest reading is taken):
  *   len[b]        valid keys of sequence b;  T query rows are the LAST T positions,
- *                 pos(b,t) = len[b] - T + t  (end_pos = start_pos + seqlen in [IDX]);
- *   key s is visible to row (b,t) iff 0 <= s <= pos(b,t)   ([MASK] triu_(1)).
+ *                 pos(b,t) = len[b] - T + t  (the excerpt's end position of a chunk is
+ *                 its start position plus its length, [IDX]);
+ *   key s is visible to row (b,t) iff 0 <= s <= pos(b,t)   ([MASK]).
  */
 #include <math.h>
 #include <stdint.h>
@@ -80,7 +85,7 @@ static double load_elem(const void* p, int dtype, size_t i)
  *   w'_h   = w[b,t,h] * q_scale[b,t,h] * sm_scale            (weight fold, [IDX])
  *   D_h    = sum_d deq(q[b,t,h,d]) * deq(k[b,s,d])            (FP8 query-key product)
  *   I      = k_scale[b,s] * sum_h w'_h * max(D_h, 0)          ([DIAG] score with ReLU)
- * and -inf where s is not visible ([MASK], "+= mask" in [IDX]).
+ * and -inf where s is not visible ([MASK]; the additive mask of [IDX]).
  * The e4m3 products are exact in double and their 128-term sums stay far below 2^53
  * units of 2^-18, so D_h is exact; the head sum is one double rounding per term. */
 int orc_index_scores(const uint8_t* q, const float* q_scale, const float* w,
@@ -139,7 +144,7 @@ static int by_pos_asc(const void* a, const void* b)
 
 /* Per row: the min(k, pos+1) visible positions with the largest scores (a full sort,
  * ties by smaller position), written in ascending position order and padded with -1
- * up to k slots ([IDX] topk(min(index_topk, end_pos)); [V4] -1 sentinel). */
+ * up to k slots ([IDX] top-k capped at the visible count; [V4] -1 sentinel). */
 int orc_topk(const float* scores, const int32_t* len, int B, int T, int Lmax, int k,
              int32_t* idx)
 {
