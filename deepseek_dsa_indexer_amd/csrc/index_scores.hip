@@ -134,30 +134,45 @@ void index_scores_kernel(const uint8_t* __restrict__ q, const float* __restrict_
 
     // ---- the block's query rows and folded head weights go through LDS once: q as
     // [64 heads][128 bytes] (zero past H heads and D bytes), w * q_scale * sm_scale
-    // (zero past H heads and for padded rows).  The first two key chunks of every wave
-    // are already in flight meanwhile.
+    // (zero past H heads and for padded rows).  Their loads are issued before the first
+    // two key chunks of every wave, so waiting for them leaves the chunks in flight, and
+    // each chunk is waited for only when it is used.
+    constexpr int kQLoads = QR * kMaxHeads * 8 / kThreads;     // 16-byte pieces per thread
+    uint4 qv[kQLoads];
+    bool qok[kQLoads];
+#pragma unroll
+    for (int u = 0; u < kQLoads; ++u) {
+        const int i = threadIdx.x + u * kThreads;
+        const int r = i / (kMaxHeads * 8);
+        const int h = (i / 8) % kMaxHeads;
+        const int c16 = i % 8;
+        qok[u] = r < nrows && h < H && c16 * 16 < D;
+        const size_t qrow = static_cast<size_t>(b) * T + t0 + min(r, nrows - 1);
+        qv[u] = *reinterpret_cast<const uint4*>(
+            q + (qrow * H + min(h, H - 1)) * D + (c16 * 16 < D ? c16 * 16 : 0));
+    }
+    float wv = 0.f, qsv = 0.f;
+    const int wr = threadIdx.x / kMaxHeads;           // row of this thread's head weight
+    const int wh = threadIdx.x % kMaxHeads;
+    if (wr < QR) {
+        const size_t qrow = static_cast<size_t>(b) * T + t0 + min(wr, nrows - 1);
+        const int hc = min(wh, H - 1);
+        wv = w[qrow * H + hc];
+        qsv = q_scale[qrow * H + hc];
+    }
     v8i cur[4], nxt[4];
     float ks_cur, ks_nxt;
     load_chunk(0, cur, ks_cur);
     load_chunk(1, nxt, ks_nxt);
-    for (int i = threadIdx.x; i < QR * kMaxHeads * 8; i += kThreads) {
+#pragma unroll
+    for (int u = 0; u < kQLoads; ++u) {
+        const int i = threadIdx.x + u * kThreads;
         const int r = i / (kMaxHeads * 8);
         const int h = (i / 8) % kMaxHeads;
         const int c16 = i % 8;
-        const bool ok = r < nrows && h < H && c16 * 16 < D;
-        const size_t qrow = static_cast<size_t>(b) * T + t0 + min(r, nrows - 1);
-        const uint4 v = *reinterpret_cast<const uint4*>(
-            q + (qrow * H + min(h, H - 1)) * D + (c16 * 16 < D ? c16 * 16 : 0));
-        *reinterpret_cast<uint4*>(&s_q[r][h * 128 + c16 * 16]) = ok ? v : uint4{0u, 0u, 0u, 0u};
+        *reinterpret_cast<uint4*>(&s_q[r][h * 128 + c16 * 16]) = qok[u] ? qv[u] : uint4{0u, 0u, 0u, 0u};
     }
-    for (int i = threadIdx.x; i < QR * kMaxHeads; i += kThreads) {
-        const int r = i / kMaxHeads;
-        const int h = i % kMaxHeads;
-        const size_t qrow = static_cast<size_t>(b) * T + t0 + min(r, nrows - 1);
-        const int hc = min(h, H - 1);
-        const float okf = (r < nrows && h < H) ? 1.f : 0.f;
-        s_wf[r][h] = w[qrow * H + hc] * q_scale[qrow * H + hc] * sm_scale * okf;
-    }
+    if (wr < QR) s_wf[wr][wh] = (wr < nrows && wh < H) ? wv * qsv * sm_scale : 0.f;
     __syncthreads();
     v8bf qa[QR][4][4];
     float wf[QR][4][4];
