@@ -19,9 +19,10 @@
 // Mapping.  One wave owns QR query rows and streams 64-key chunks of the key cache.
 // The 64 heads of each query row stay in registers as A operands (4 head tiles x 4
 // K-steps of 32).  A chunk is four 16-key B tiles read with 16-byte loads: lane l takes
-// the 32 contiguous bytes [32 g, 32 g + 32) of key (l % 16), g = l / 16, and K-step j
-// uses bytes [8 j, 8 j + 8) of them (q uses the same byte -> K-slot assignment, so the
-// four K-steps cover each of the 128 dims once).  Each MFMA leaves lane l with 4
+// the bytes [16 g, 16 g + 16) and [64 + 16 g, 64 + 16 g + 16) of key (l % 16), g = l / 16,
+// so each load instruction reads whole 64-byte halves of 16 key rows; K-steps 0 and 1
+// use the first piece, 2 and 3 the second (q uses the same byte -> K-slot assignment, so
+// the four K-steps cover each of the 128 dims once).  Each MFMA leaves lane l with 4
 // heads x 1 key; ReLU and the head weights are applied in registers and three
 // cross-lane exchanges finish the head sum, so lane l ends with the score of key
 // (chunk + l): one coalesced 256-byte store per row and chunk.  Heads beyond H_I and
@@ -41,17 +42,17 @@ constexpr int kMaxHeads = 64;       // indexer heads (4 MFMA row tiles)
 
 typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
 
-// 32 contiguous bytes (two 16-byte loads) of `p`, zeroed when !ok.  The load is issued
-// unconditionally (callers pass a clamped, in-bounds address): a load inside a divergent
-// branch makes the compiler drain every outstanding load at the branch join.
-__device__ __forceinline__ v8i load32(const uint8_t* p, bool ok) {
-    const uint4* s = reinterpret_cast<const uint4*>(p);
-    const uint4 a = s[0];
-    const uint4 b = s[1];
-    const int m = ok ? -1 : 0;
-    return v8i{static_cast<int>(a.x) & m, static_cast<int>(a.y) & m, static_cast<int>(a.z) & m,
-               static_cast<int>(a.w) & m, static_cast<int>(b.x) & m, static_cast<int>(b.y) & m,
-               static_cast<int>(b.z) & m, static_cast<int>(b.w) & m};
+// Two 16-byte pieces at p0 and p1, each zeroed when its flag is false.  The loads are
+// issued unconditionally (callers pass clamped, in-bounds addresses): a load inside a
+// divergent branch makes the compiler drain every outstanding load at the branch join.
+__device__ __forceinline__ v8i load2x16(const uint8_t* p0, bool ok0, const uint8_t* p1, bool ok1) {
+    const uint4 a = *reinterpret_cast<const uint4*>(p0);
+    const uint4 b = *reinterpret_cast<const uint4*>(p1);
+    const int m0 = ok0 ? -1 : 0;
+    const int m1 = ok1 ? -1 : 0;
+    return v8i{static_cast<int>(a.x) & m0, static_cast<int>(a.y) & m0, static_cast<int>(a.z) & m0,
+               static_cast<int>(a.w) & m0, static_cast<int>(b.x) & m1, static_cast<int>(b.y) & m1,
+               static_cast<int>(b.z) & m1, static_cast<int>(b.w) & m1};
 }
 
 // 8 FP8 bytes (two dwords) -> 8 bf16, exactly.
@@ -123,10 +124,12 @@ void index_scores_kernel(const uint8_t* __restrict__ q, const float* __restrict_
 #pragma unroll
         for (int tile = 0; tile < 4; ++tile) {
             const int key = kb + 16 * tile + n;
-            const bool ok = live && key < Lmax && g * 32 < D;
+            const bool ok = live && key < Lmax;
             const int kc = min(key, Lmax - 1);
-            const int bc = g * 32 < D ? g * 32 : 0;
-            dst[tile] = load32(kb_ptr + static_cast<size_t>(kc) * D + bc, ok);
+            const uint8_t* krow = kb_ptr + static_cast<size_t>(kc) * D;
+            const int b0 = 16 * g, b1 = 64 + 16 * g;     // pieces past d_I read 0 (masked)
+            dst[tile] = load2x16(krow + (b0 < D ? b0 : 0), ok && b0 < D,
+                                 krow + (b1 < D ? b1 : 0), ok && b1 < D);
         }
         // positions at or beyond Lmax are never stored, so the clamped scale needs no mask
         ks = ks_ptr[min(kb + lane, Lmax - 1)];
@@ -180,8 +183,8 @@ void index_scores_kernel(const uint8_t* __restrict__ q, const float* __restrict_
     for (int r = 0; r < QR; ++r)
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-            const uint4* src = reinterpret_cast<const uint4*>(&s_q[r][(16 * j + n) * 128 + 32 * g]);
-            const uint4 lo = src[0], hi = src[1];
+            const uint4 lo = *reinterpret_cast<const uint4*>(&s_q[r][(16 * j + n) * 128 + 16 * g]);
+            const uint4 hi = *reinterpret_cast<const uint4*>(&s_q[r][(16 * j + n) * 128 + 64 + 16 * g]);
             const int raw[8] = {static_cast<int>(lo.x), static_cast<int>(lo.y), static_cast<int>(lo.z),
                                 static_cast<int>(lo.w), static_cast<int>(hi.x), static_cast<int>(hi.y),
                                 static_cast<int>(hi.z), static_cast<int>(hi.w)};
