@@ -260,6 +260,32 @@ def test_layer_step_mha_small(dsa, orc):
     check_attention(_np_out(out), lse.cpu().numpy(), ro, rl, "bf16")
 
 
+def test_layer_step_without_intermediates(dsa, orc):
+    """The production configuration (scores and indices kept in the workspace, invisible
+    scores never written, the top-k candidates of rows beyond 16384 positions sharing the
+    scratch region with the attention partials) gives bit-identical results to the
+    configuration that exposes the intermediates, which is checked against the oracle."""
+    _say("[layer_step] without intermediates, long ragged rows")
+    cfg = _small("decode_ragged", name="ni", B=3, Lmax=20000, lens="ragged:1024:20000", seed=207)
+    c = S.make_case(cfg)
+    d = _dev(c)
+    args = (d["q_i"], d["q_scale"], d["w"], d["k_i"], d["k_scale"], d["lens"], cfg.sm_scale_i,
+            cfg.k, d["q"], cfg.sm_scale)
+    full = dsa.LayerStep(*args, latent=d["latent"], Dv=cfg.Dv, want_idx=True, want_scores=True)
+    bare = dsa.LayerStep(*args, latent=d["latent"], Dv=cfg.Dv)
+    o1, l1 = full()
+    o2, l2 = bare()
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+    rsc = orc.index_scores(c["q_i"], c["q_scale"], c["w"], c["k_i"], c["k_scale"], c["lens"],
+                           cfg.sm_scale_i)
+    ridx = orc.topk(rsc, c["lens"], cfg.k)
+    gidx = full.idx.cpu().numpy()
+    check_topk(gidx, rsc, ridx, c["lens"], cfg.T, cfg.k)
+    ro, rl = orc.sparse_mla_decode(c["q"], c["latent"], gidx, c["lens"], cfg.Dv, cfg.sm_scale)
+    check_attention(_np_out(o2), l2.cpu().numpy(), ro, rl, cfg.attn_dtype)
+
+
 def test_layer_step_deterministic(dsa):
     cfg = _small("decode_v32", name="det", B=4, Lmax=5000, seed=303)
     c = S.make_case(cfg)
@@ -274,7 +300,7 @@ def test_layer_step_deterministic(dsa):
 
 @pytest.mark.parametrize("T,H,k", [(200, 2, 48), (130, 3, 130), (64, 1, 1)])
 def test_sparse_mla_prefill_blocks(dsa, orc, T, H, k):
-    """Several 64-row query blocks and key blocks, a ragged tail, k >= T (dense causal)
+    """Several 128-row query blocks and 64-key blocks, ragged tails, k >= T (dense causal)
     and k = 1."""
     _say(f"[sparse_mla_prefill bf16 blocks] T={T} H={H} k={k}")
     rng = np.random.default_rng(T * 7 + H)
