@@ -5,17 +5,18 @@
 // attention, prefill) forms dense scores, adds an index mask that is 0 at the top-k
 // positions and -inf elsewhere plus the causal mask, and takes a softmax.  Per head the
 // selected keys of neighbouring query rows are unrelated (2048 of up to 8192 each), so
-// a tile of 64 query rows touches nearly every key block anyway; the kernel therefore
+// a tile of query rows touches nearly every key block anyway; the kernel therefore
 // runs a causal flash-attention sweep over key blocks and applies the selection as a
 // bit mask built from idx by select_mask_kernel (bit s of row t set iff s is selected
 // and s <= t).  Masked-dense work is about 2.3x the selected pairs at T = 8192, k = 2048.
 //
-// Mapping.  One workgroup (4 waves) owns one head and 128 query rows; wave w owns rows
-// 32w..32w+31 as two 16-row query tiles, so every K and V operand read from LDS feeds
-// two matrix-core products.  Per key block of 64 positions:
-//   load  K [64 x 192] and V [64 x 128] bf16 rows into LDS with direct global->LDS
-//         16-byte loads, double buffered, 16-byte chunks XOR-swizzled per row; the
-//         selection-mask words of the next block are fetched with them;
+// Mapping.  One workgroup (8 waves, two per SIMD) owns one head and 256 query rows; wave
+// w owns rows 32w..32w+31 as two 16-row query tiles, so every K and V operand read from
+// LDS feeds two matrix-core products.  Per key block of 64 positions:
+//   load  K [64 x 192] and V [64 x 128] bf16 rows and the block's selection-mask words
+//         of the 256 rows into LDS with direct global->LDS loads, in a three-stage
+//         ring (two blocks in flight while one is computed), 16-byte chunks
+//         XOR-swizzled per row;
 //   QK    S^T = K . Q^T (keys as MFMA rows, each query tile's 16 queries as 6 B
 //         operands in registers), so lane (g, n) holds query row n of the tile and keys
 //         16 kt + 4 g + i;
@@ -23,6 +24,8 @@
 //   softmax online per row, entirely in the wave; the probabilities stay in registers
 //         in the A-operand layout of the PV product;
 //   PV    O [32 x 128] += P . V, V operands by LDS transpose reads.
+// Heaviest query blocks go first and all query blocks of a head share an XCD, so the
+// head's K and V blocks are fetched into one L2.
 #include "dsa_device.h"
 #include "dsa_internal.h"
 
@@ -30,10 +33,10 @@ namespace dsa {
 
 namespace {
 
-constexpr int kMhaThreads = 256;
-constexpr int kMhaWaves = 4;
+constexpr int kMhaThreads = 512;
+constexpr int kMhaWaves = 8;
 constexpr int kQT = 2;                  // 16-row query tiles per wave
-constexpr int kQB = 16 * kQT * 4;       // query rows per workgroup (128)
+constexpr int kQB = 16 * kQT * kMhaWaves;   // query rows per workgroup (256)
 constexpr int kKB = 64;                 // keys per block
 constexpr int kDqk = 192;
 constexpr int kDvM = 128;
@@ -45,15 +48,19 @@ constexpr int kKBytes = kKB * kKRow;    // 24576
 constexpr int kVBytes = kKB * kVRow;    // 16384
 constexpr int kKLoads = kKBytes / 1024; // 24 wave-wide 1 KB loads
 constexpr int kVLoads = kVBytes / 1024; // 16
-constexpr int kLoadsPerWave = (kKLoads + kVLoads) / kMhaWaves;   // 10
+constexpr int kLoadsPerWave = (kKLoads + kVLoads) / kMhaWaves;   // 5
+constexpr int kMaskBytes = kQB * 2 * 4;                          // 2 mask words per row
+constexpr int kStageBytes = kKBytes + kVBytes + kMaskBytes;      // 43008
+constexpr int kStages = 3;                                       // blocks i, i+1, i+2
+constexpr int kDmaPerBlock = kLoadsPerWave + 1;                  // per wave, with the mask
+static_assert((kKLoads + kVLoads) % kMhaWaves == 0, "block loads split evenly over the waves");
+static_assert(kMaskBytes == kMhaWaves * kWave * 4, "one mask dword per lane");
 constexpr float kLog2eM = 1.4426950408889634f;
 constexpr float kLn2M = 0.6931471805599453f;
 constexpr float kLazy = 8.0f;
 
-__shared__ __attribute__((aligned(16))) uint8_t m_k0[kKBytes];
-__shared__ __attribute__((aligned(16))) uint8_t m_k1[kKBytes];
-__shared__ __attribute__((aligned(16))) uint8_t m_v0[kVBytes];
-__shared__ __attribute__((aligned(16))) uint8_t m_v1[kVBytes];
+// Stage s: K block [64 x 384 B], V block [64 x 256 B], mask words [256 rows][2].
+__shared__ __attribute__((aligned(16))) uint8_t m_stage[kStages * kStageBytes];
 
 typedef __bf16 v4bf_m __attribute__((ext_vector_type(4)));
 
@@ -64,17 +71,29 @@ __device__ __forceinline__ void dma16(const uint8_t* src, uint32_t lds_addr) {
     asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" :: "s"(m0v), "v"(src) : "memory");
 }
 
+__device__ __forceinline__ void dma4(const uint32_t* src, uint32_t lds_addr) {
+    const uint32_t m0v = __builtin_amdgcn_readfirstlane(lds_addr);
+    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dword %1, off" :: "s"(m0v), "v"(src) : "memory");
+}
+
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
     return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) const uint8_t*)(p)));
 }
 
-// Loads key block [s0, s0 + 64) of head h into (kd, vd): 10 wave-wide loads per wave.
-// Rows past the chunk end read the last row (their scores are masked).
-__device__ __forceinline__ void load_block(const uint8_t* kbase, const uint8_t* vbase, int T, int H,
-                                           int h, int s0, uint8_t* kd, uint8_t* vd, int wave,
-                                           int lane) {
+// Loads key block [s0, s0 + 64) of head h and the selection-mask words of the block's
+// 256 query rows into stage `st`: 5 wave-wide 1 KB loads and one mask dword per lane.
+// Rows past the chunk end read the last row (their scores are masked by causality).
+__device__ __forceinline__ void load_block(const uint8_t* kbase, const uint8_t* vbase,
+                                           const uint32_t* mask_b, int words, int t0, int T,
+                                           int H, int h, int s0, uint8_t* st, int wave, int lane) {
     asm volatile("" : "+v"(lane));
-    const uint32_t kl = lds_addr(kd), vl = lds_addr(vd);
+    const uint32_t kl = lds_addr(st), vl = kl + kKBytes;
+    {
+        const int local = 32 * wave + (lane >> 1);
+        const int row = min(t0 + local, T - 1);
+        const int word = min((s0 >> 5) + (lane & 1), words - 1);
+        dma4(mask_b + static_cast<size_t>(row) * words + word, vl + kVBytes + wave * kWave * 4);
+    }
     for (int i = 0; i < kLoadsPerWave; ++i) {
         const int ci = wave + kMhaWaves * i;                 // 0..39
         if (ci < kKLoads) {
@@ -104,16 +123,22 @@ struct MhaState {
     float m_run[kQT], l_run[kQT];
 };
 
-template <int BUF>
-__device__ __forceinline__ void mha_block(MhaState& st, const uint32_t (&mw)[kQT][2],
-                                          const int (&t_row)[kQT], int s0, float scale_log2,
-                                          int lane) {
-    const uint8_t* kb = BUF ? m_k1 : m_k0;
-    const uint8_t* vb = BUF ? m_v1 : m_v0;
+__device__ __forceinline__ void mha_block(MhaState& st, const uint8_t* stage, const int (&t_row)[kQT],
+                                          int s0, float scale_log2, int wave, int lane) {
+    const uint8_t* kb = stage;
+    const uint8_t* vb = stage + kKBytes;
+    const uint32_t* mk = reinterpret_cast<const uint32_t*>(stage + kKBytes + kVBytes);
     int lo = lane;
     asm volatile("" : "+v"(lo));
     const int g = lo >> 4;
     const int n = lo & 15;
+    uint32_t mw[kQT][2];
+#pragma unroll
+    for (int qt = 0; qt < kQT; ++qt) {
+        const uint2 m2 = *reinterpret_cast<const uint2*>(mk + 2 * (32 * wave + 16 * qt + n));
+        mw[qt][0] = m2.x;
+        mw[qt][1] = m2.y;
+    }
 
     // ---- S^T = K . Q^T: 4 key tiles x 6 K-steps, each K operand used by both query tiles
     v4f sacc[kQT][4];
@@ -203,19 +228,6 @@ __device__ __forceinline__ void mha_block(MhaState& st, const uint32_t (&mw)[kQT
     }
 }
 
-// Selection-mask words of key block s0 for the wave's query rows (zero past the row).
-__device__ __forceinline__ void load_mask(const uint32_t* const (&mrow)[kQT], int words, int s0,
-                                          uint32_t (&mw)[kQT][2]) {
-#pragma unroll
-    for (int qt = 0; qt < kQT; ++qt) {
-        const int w0 = s0 >> 5;
-        mw[qt][0] = mrow[qt][min(w0, words - 1)];
-        mw[qt][1] = mrow[qt][min(w0 + 1, words - 1)];
-        if (w0 >= words) mw[qt][0] = 0u;
-        if (w0 + 1 >= words) mw[qt][1] = 0u;
-    }
-}
-
 __global__ __launch_bounds__(kMhaThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void mha_prefill_mfma_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
                              const uint16_t* __restrict__ v, const uint32_t* __restrict__ mask,
@@ -239,12 +251,10 @@ void mha_prefill_mfma_kernel(const uint16_t* __restrict__ q, const uint16_t* __r
     const int words = (T + 31) / 32;
 
     int t_row[kQT];                         // query row of this lane in each tile
-    const uint32_t* mrow[kQT];
     MhaState st;
 #pragma unroll
     for (int qt = 0; qt < kQT; ++qt) {
         t_row[qt] = min(t0 + 32 * wave + 16 * qt + n, T - 1);
-        mrow[qt] = mask + (static_cast<size_t>(b) * T + t_row[qt]) * words;
         const uint16_t* qrow = q + ((static_cast<size_t>(b) * T + t_row[qt]) * H + h) * kDqk + 8 * g;
 #pragma unroll
         for (int ds = 0; ds < kDqk / 32; ++ds) st.qreg[qt][ds] = *reinterpret_cast<const v8bf*>(qrow + 32 * ds);
@@ -253,39 +263,28 @@ void mha_prefill_mfma_kernel(const uint16_t* __restrict__ q, const uint16_t* __r
         st.m_run[qt] = -INFINITY;
         st.l_run[qt] = 0.f;
     }
-    uint32_t mcur[kQT][2], mnext[kQT][2];
-    load_mask(mrow, words, 0, mcur);
-#pragma unroll
-    for (int qt = 0; qt < kQT; ++qt)
-#pragma unroll
-        for (int ds = 0; ds < kDqk / 32; ++ds) asm volatile("" :: "v"(st.qreg[qt][ds]));
 
     const uint8_t* kbase = reinterpret_cast<const uint8_t*>(k) + static_cast<size_t>(b) * T * H * kKRow;
     const uint8_t* vbase = reinterpret_cast<const uint8_t*>(v) + static_cast<size_t>(b) * T * H * kVRow;
+    const uint32_t* mask_b = mask + static_cast<size_t>(b) * T * words;
     const int t_last = min(t0 + kQB, T) - 1;
     const int nblocks = t_last / kKB + 1;                    // causal: key blocks up to t_last
 
-    // Step j: wait for block j (and its mask words), put block j + 1 and its mask words
-    // in flight, compute block j.
-    load_block(kbase, vbase, T, H, h, 0, m_k0, m_v0, wave, lane);
-    for (int kb2 = 0; kb2 < nblocks; kb2 += 2) {
-        // block kb2 in buffer 0, block kb2 + 1 in buffer 1
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    // Three-stage ring: step j waits for block j (block j + 1 stays in flight), passes
+    // one barrier (block j visible; stage of block j - 1 free), puts block j + 2 in
+    // flight and computes block j.  The queries' own loads were issued first, so the
+    // compiler's wait for them (it cannot see the direct-to-LDS loads) is the only
+    // full drain, at the first block.
+    auto stage = [&](int j) { return m_stage + (j % kStages) * kStageBytes; };
+    load_block(kbase, vbase, mask_b, words, t0, T, H, h, 0, stage(0), wave, lane);
+    if (nblocks > 1) load_block(kbase, vbase, mask_b, words, t0, T, H, h, kKB, stage(1), wave, lane);
+    for (int j = 0; j < nblocks; ++j) {
+        if (j + 1 < nblocks) asm volatile("s_waitcnt vmcnt(%0)" :: "n"(kDmaPerBlock) : "memory");
+        else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         lds_sync();
-        if (kb2 + 1 < nblocks) {
-            load_block(kbase, vbase, T, H, h, (kb2 + 1) * kKB, m_k1, m_v1, wave, lane);
-            load_mask(mrow, words, (kb2 + 1) * kKB, mnext);
-        }
-        mha_block<0>(st, mcur, t_row, kb2 * kKB, scale_log2, lane);
-        if (kb2 + 1 < nblocks) {
-            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-            lds_sync();
-            if (kb2 + 2 < nblocks) {
-                load_block(kbase, vbase, T, H, h, (kb2 + 2) * kKB, m_k0, m_v0, wave, lane);
-                load_mask(mrow, words, (kb2 + 2) * kKB, mcur);
-            }
-            mha_block<1>(st, mnext, t_row, (kb2 + 1) * kKB, scale_log2, lane);
-        }
+        if (j + 2 < nblocks)
+            load_block(kbase, vbase, mask_b, words, t0, T, H, h, (j + 2) * kKB, stage(j + 2), wave, lane);
+        mha_block(st, stage(j), t_row, j * kKB, scale_log2, wave, lane);
     }
 
     // ---- epilogue: rows 4 g + i of each query tile; l and m of row r sit in lane r
