@@ -54,6 +54,16 @@ def test_topk_validation(lib):
     assert lib.dsa_topk(p, p, 1, 1, 16, 0, p, None, 0, None) == 2
     assert lib.dsa_topk(None, p, 1, 1, 16, 4, p, None, 0, None) == 1
     assert lib.dsa_topk(p, p, 1, 2, 1, 4, p, None, 0, None) == 2
+    # rows up to 16384 positions need no workspace; longer rows keep per-chunk candidates
+    assert lib.dsa_topk_workspace_bytes(32, 1, 8192, 2048) == 0
+    assert lib.dsa_topk_workspace_bytes(4, 1, 16384, 2048) == 0
+    need = lib.dsa_topk_workspace_bytes(8, 1, 131072, 2048)
+    assert need >= 8 * 131072 // 16384 * 2048 * 8      # keys + positions of every chunk's top-k
+    assert lib.dsa_topk_workspace_bytes(8, 1, 131072, 8192) == 0   # k >= chunk: one pass
+    st = lib.dsa_topk(p, p, 8, 1, 131072, 2048, p, None, 0, None)
+    assert st == 5 and b"workspace" in lib.dsa_last_error()
+    st = lib.dsa_topk(p, p, 8, 1, 131072, 2048, p, p, need - 1, None)
+    assert st == 5
 
 
 def test_attention_validation_and_workspace(lib):
