@@ -43,8 +43,10 @@ constexpr int kPerIter = kThreads * kPerThread;     // positions per block-wide 
 constexpr int kMaxIters = 4;                         // register-held iterations
 constexpr int kSingleMax = 4 * kPerIter;             // longest row for the one-launch form
 constexpr uint32_t kNoKey = 0u;                      // unused candidate (float bits of -NaN)
+constexpr int kStagedOut = 4096;                     // outputs staged in LDS up to this k
 
 struct TopkShared {
+    int32_t out[kStagedOut];          // selected positions, written out coalesced
     uint32_t hist[2][kBins];
     uint32_t scan[kWaves + 1];
     uint32_t scan2[kMaxIters][kWaves + 1];
@@ -312,7 +314,15 @@ void topk_row_kernel(const float* __restrict__ scores, const int32_t* __restrict
     }
     Keys<REG, ScoreSrc> ks;
     ks.init(ScoreSrc{scores + static_cast<size_t>(row) * Lmax, n, (Lmax & 3) == 0}, n);
-    block_select(ks, k, sh, [&](uint32_t slot, int i, uint32_t) { out[slot] = i; });
+    if (k <= kStagedOut) {
+        // slots arrive scattered; staging them in LDS turns k scattered 4-byte stores
+        // into one coalesced pass
+        block_select(ks, k, sh, [&](uint32_t slot, int i, uint32_t) { sh.out[slot] = i; });
+        __syncthreads();
+        for (int j = threadIdx.x; j < k; j += kThreads) out[j] = sh.out[j];
+    } else {
+        block_select(ks, k, sh, [&](uint32_t slot, int i, uint32_t) { out[slot] = i; });
+    }
 }
 
 // Two-stage form, stage 1: chunk c of row r (its visible positions among [C c, C c + C),
@@ -367,7 +377,13 @@ void topk_merge_kernel(const uint32_t* __restrict__ cand_key, const int32_t* __r
     const int32_t* cp = cand_pos + off;
     Keys<REG, CandSrc> ks;
     ks.init(CandSrc{cand_key + off, nc, (nc & 3) == 0}, nc);
-    block_select(ks, k, sh, [&](uint32_t slot, int i, uint32_t) { out[slot] = cp[i]; });
+    if (k <= kStagedOut) {
+        block_select(ks, k, sh, [&](uint32_t slot, int i, uint32_t) { sh.out[slot] = i; });
+        __syncthreads();
+        for (int j = threadIdx.x; j < k; j += kThreads) out[j] = cp[sh.out[j]];
+    } else {
+        block_select(ks, k, sh, [&](uint32_t slot, int i, uint32_t) { out[slot] = cp[i]; });
+    }
 }
 
 // Chunk length of the two-stage form: 8192 positions while the candidates of a row fit
