@@ -240,7 +240,19 @@ def main():
     ms_per_step = 1e3 * dt / args.steps
     value = args.steps / dt
 
-    # second pass of the same steps with the library's per-phase HIP events
+    # per-step distribution: HIP events around every step (the library enqueues on the
+    # current stream, which is where torch records its events)
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
+    for i in range(args.steps):
+        evs[i][0].record()
+        run[i % len(run)]()
+        evs[i][1].record()
+    torch.cuda.synchronize()
+    step_ms = sorted(a.elapsed_time(b) for a, b in evs)
+    pct = lambda q: step_ms[min(len(step_ms) - 1, int(q * len(step_ms)))]
+
+    # next pass of the same steps with the library's per-phase HIP events
     D.profile_begin(args.steps)
     for i in range(args.steps):
         steps[i % len(steps)]()
@@ -299,6 +311,8 @@ def main():
                    "B": cfg.B, "context": cfg.Lmax, "T": cfg.T, "topk": cfg.k, "H_I": cfg.H_I,
                    "d_I": cfg.D_I, "H": cfg.H, "q_width": cfg.Dq, "input_sets": args.sets,
                    "hip_graph": bool(args.graph)},
+        "step_ms_p10_p50_p90": [round(pct(0.1), 5), round(pct(0.5), 5), round(pct(0.9), 5)],
+        "token_layer_steps_per_s": round(cfg.B * cfg.T * value, 1),
         "keys_scored_per_s": round(costs["keys"] * value, 1),
         "keys_per_step": costs["keys"],
         "step_roofline_frac": round(t_roof / (ms_per_step * 1e-3), 4),
