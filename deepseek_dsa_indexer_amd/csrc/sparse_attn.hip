@@ -523,7 +523,7 @@ void mla_decode_mfma_kernel(const uint16_t* __restrict__ q, const uint16_t* __re
 // Merge the splits of each (row, head): split s holds its own normalised output (bf16)
 // and its log2-sum-exp; weights are 2^(lse_s - max).  One thread owns 8 columns.
 constexpr int kCombCols = 8;
-constexpr int kMaxSplits = 8;
+constexpr int kMaxSplits = 16;
 __global__ __launch_bounds__(256)
 void mla_combine_kernel(const uint16_t* __restrict__ part_o, const float* __restrict__ part_lse,
                         int rows, int H, int n_splits, uint16_t* __restrict__ out,
@@ -572,7 +572,8 @@ void mla_combine_kernel(const uint16_t* __restrict__ part_o, const float* __rest
 }
 
 int mla_splits(int rows, int k) {
-    // enough (row, split) workgroups to give every CU one, within the LDS slot limit
+    // enough (row, split) workgroups to give every CU one (a few rows of a long context
+    // split up to 16 ways), within the LDS slot limit
     const int n_tiles = (k + kKt - 1) / kKt;
     int s = rows >= 256 ? 1 : (256 + rows - 1) / rows;
     s = min(s, kMaxSplits);

@@ -114,8 +114,8 @@ dsa_status dsa_topk(const float* scores, const int32_t* len, int B, int T, int L
  * A row with no usable slot gets out = 0 and lse = -inf.  Entries of idx must be unique
  * per row.  Any H, Dv, Dr with Dv+Dr <= 1024 and dtype F32 or BF16 (the vector-ALU path
  * keeps all k logits in LDS: 4 (Dv + Dr + k) <= 65536 bytes); the bf16 shape H in
- * {64, 128}, Dv = 512, Dr = 64, k <= 8192 runs on the matrix-core path, which splits
- * each row's slots over up to 8 workgroups and needs a workspace for their partial
+ * {64, 128}, Dv = 512, Dr = 64, k <= 16384 runs on the matrix-core path, which splits
+ * each row's slots over up to 16 workgroups and needs a workspace for their partial
  * results (dsa_sparse_mla_decode_workspace_bytes(); 0 when the rows fill the GPU
  * without splitting).
  */

@@ -78,11 +78,11 @@ def test_attention_validation_and_workspace(lib):
                                    None, 0, None)
     assert st == 3
     assert lib.dsa_sparse_mla_decode_workspace_bytes(256, 1, 128, 512, 64, 1024, N.DSA_BF16) == 0
-    # beyond 8 splits of 1024 slots the latent shape leaves the matrix-core path: the
+    # beyond 16 splits of 1024 slots the latent shape leaves the matrix-core path: the
     # generic path needs no workspace but must hold all k logits in LDS
-    assert lib.dsa_sparse_mla_decode_workspace_bytes(2, 1, 128, 512, 64, 8192, N.DSA_BF16) > 0
-    assert lib.dsa_sparse_mla_decode_workspace_bytes(2, 1, 128, 512, 64, 8193, N.DSA_BF16) == 0
-    st = lib.dsa_sparse_mla_decode(p, p, p, p, 2, 1, 128, 512, 64, 1 << 15, 1 << 14, 0.1,
+    assert lib.dsa_sparse_mla_decode_workspace_bytes(2, 1, 128, 512, 64, 16384, N.DSA_BF16) > 0
+    assert lib.dsa_sparse_mla_decode_workspace_bytes(2, 1, 128, 512, 64, 16385, N.DSA_BF16) == 0
+    st = lib.dsa_sparse_mla_decode(p, p, p, p, 2, 1, 128, 512, 64, 1 << 16, 20000, 0.1,
                                    N.DSA_BF16, p, None, None, 0, None)
     assert st == 2 and b"too large" in lib.dsa_last_error()
     # generic (f32) path: logits of all k slots must fit in LDS
