@@ -67,4 +67,52 @@ __device__ __forceinline__ uint32_t wave_inclusive_scan(uint32_t v, int lane) {
     return v;
 }
 
+// Work numbering for launches over the sequences of a batch whose sequences need
+// unequal numbers of blocks (count(b) >= 0 for b < n_seq).  The blocks of sequence b
+// take ids P(b) .. P(b) + count(b) - 1, P the exclusive prefix sum, so consecutive ids
+// walk through one sequence after another.  The dispatcher hands consecutive
+// workgroups to the 8 XCDs in turn, so every XCD gets an equal share of the work
+// however unequal the sequences are, and no workgroup is spent on a block past a
+// sequence's end: ids beyond the total return false (the same in every thread).
+// Every thread of the NT-thread block must call it; thread t counts sequences
+// [t * per, t * per + per), per = ceil(n_seq / NT).  sh: NT / 64 + 2 ints of LDS.
+template <int NT, typename Count>
+__device__ __forceinline__ bool numbered_block(int id, int n_seq, Count count, int* sh, int& seq,
+                                               int& blk) {
+    constexpr int kWaves = NT / kWave;
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wave = threadIdx.x / kWave;
+    const int per = (n_seq + NT - 1) / NT;
+    const int s0 = threadIdx.x * per;
+    int mine = 0;
+    for (int i = 0; i < per; ++i) mine += s0 + i < n_seq ? count(s0 + i) : 0;
+    const int inc = static_cast<int>(wave_inclusive_scan(static_cast<uint32_t>(mine), lane));
+    if (lane == kWave - 1) sh[wave] = inc;
+    __syncthreads();
+    int before = 0, total = 0;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) {
+        const int x = sh[w];
+        before += w < wave ? x : 0;
+        total += x;
+    }
+    int base = before + inc - mine;
+    if (id >= base && id < base + mine) {
+        for (int i = 0; i < per; ++i) {
+            const int c = s0 + i < n_seq ? count(s0 + i) : 0;
+            if (id < base + c) {
+                sh[kWaves] = s0 + i;
+                sh[kWaves + 1] = id - base;
+                break;
+            }
+            base += c;
+        }
+    }
+    __syncthreads();
+    if (id >= total) return false;
+    seq = sh[kWaves];
+    blk = sh[kWaves + 1];
+    return true;
+}
+
 }  // namespace dsa

@@ -27,6 +27,13 @@
 // cross-lane exchanges finish the head sum, so lane l ends with the score of key
 // (chunk + l): one coalesced 256-byte store per row and chunk.  Heads beyond H_I and
 // columns beyond d_I are zero (weight 0), which covers the small test shapes.
+//
+// Blocks.  A block covers QR query rows and 256 * chunks consecutive keys.  With one
+// query row per sequence (decode), only the key blocks that hold visible positions are
+// launched work, numbered sequence after sequence (numbered_block), so a batch of
+// unequal lengths loads the 8 XCDs evenly; a grid laid out as (sequence, key block)
+// would give XCD j the sequences j, j + 8, ... and the longest of them would set the
+// kernel's time.
 #include <algorithm>
 
 #include "dsa_device.h"
@@ -39,6 +46,7 @@ namespace {
 constexpr int kThreads = 256;       // 4 waves
 constexpr int kChunk = 64;          // keys per wave iteration (4 MFMA column tiles)
 constexpr int kMaxHeads = 64;       // indexer heads (4 MFMA row tiles)
+constexpr int kMaxSeqPerThread = 16; // numbered decode launches: up to 4096 sequences
 
 typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
 
@@ -97,13 +105,29 @@ void index_scores_kernel(const uint8_t* __restrict__ q, const float* __restrict_
     const int n = lane & 15;
 
     const int row_groups = (T + QR - 1) / QR;
-    const int b = blockIdx.x / row_groups;
-    const int t0 = (blockIdx.x - b * row_groups) * QR;
+    int b, t0, yblk;
+    if (T == 1 && gridDim.x <= kThreads * kMaxSeqPerThread) {
+        // one query row per sequence: numbered blocks (sequences of unequal length
+        // still spread evenly over the XCDs; no block past a sequence's end is run
+        // unless its positions are to be filled with -inf)
+        __shared__ int s_num[kThreads / kWave + 2];
+        const int nblk = gridDim.y;
+        auto count = [&](int s) {
+            return fill_invisible ? nblk : (min(len[s], Lmax) + keys_per_block - 1) / keys_per_block;
+        };
+        if (!numbered_block<kThreads>(blockIdx.y * gridDim.x + blockIdx.x, gridDim.x, count, s_num, b, yblk))
+            return;
+        t0 = 0;
+    } else {
+        b = blockIdx.x / row_groups;
+        t0 = (blockIdx.x - b * row_groups) * QR;
+        yblk = blockIdx.y;
+    }
     const int nrows = min(QR, T - t0);
     const int pos0 = min(len[b], Lmax) - T + t0;   // position of row t0
     const int pos_hi = pos0 + nrows - 1;
 
-    const int key_blk = blockIdx.y * keys_per_block;
+    const int key_blk = yblk * keys_per_block;
     float* out = scores + (static_cast<size_t>(b) * T + t0) * Lmax;
 
     if (key_blk > pos_hi) {                     // the whole block is masked

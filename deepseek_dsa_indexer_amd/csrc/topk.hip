@@ -33,9 +33,12 @@ constexpr int kPerIter = kThreads * kSelPerThread;  // positions per block-wide 
 constexpr int kSingleMax = 4 * kPerIter;             // longest row for the one-launch form
 constexpr int kStagedOut = 4096;                     // outputs staged in LDS up to this k
 
+constexpr int kMaxSeqPerThread = 16;                 // numbered chunk launches: 16384 rows
+
 struct TopkShared {
     int32_t out[kStagedOut];          // selected positions, written out coalesced
     SelectShared<kThreads> sel;
+    int num[kThreads / kWave + 2];    // block numbering
 };
 
 __device__ __forceinline__ int visible(const int32_t* len, int row, int T, int Lmax) {
@@ -74,6 +77,8 @@ void topk_row_kernel(const float* __restrict__ scores, const int32_t* __restrict
 // Two-stage form, stage 1: chunk c of row r (its visible positions among [C c, C c + C),
 // C = 4096 REG) writes its top-min(k, m) keys and positions, in position order, to
 // candidate slots [c k, c k + k) of the row; the remaining slots get kNoKey / -1.
+// Chunks without a visible position write nothing: stage 2 reads only the candidates
+// of the ceil(n / C) chunks that hold the row's n visible positions.
 template <int REG>
 __global__ __launch_bounds__(kThreads)
 void topk_chunk_kernel(const float* __restrict__ scores, const int32_t* __restrict__ len,
@@ -81,13 +86,27 @@ void topk_chunk_kernel(const float* __restrict__ scores, const int32_t* __restri
                        int32_t* __restrict__ cand_pos)
 {
     __shared__ TopkShared sh;
-    const int row = blockIdx.x / n_chunks;
-    const int c = blockIdx.x - row * n_chunks;
+    constexpr int kChunk = REG * kPerIter;
+    int row, c;
+    if (T == 1 && gridDim.x <= kThreads * kMaxSeqPerThread * n_chunks) {
+        // one query row per sequence: only the chunks of rows that need a selection,
+        // numbered row after row, so unequal lengths still load the XCDs evenly
+        auto count = [&](int r) {
+            const int n = visible(len, r, 1, Lmax);
+            return n > k ? (n + kChunk - 1) / kChunk : 0;
+        };
+        if (!numbered_block<kThreads>(blockIdx.x, gridDim.x / n_chunks, count, sh.num, row, c)) return;
+    } else {
+        // chunk c' of row r runs chunk (c' + r) % n_chunks: a block's XCD follows c', so
+        // every XCD gets chunks from the whole length range of the rows
+        row = blockIdx.x / n_chunks;
+        c = (blockIdx.x - row * n_chunks + row) % n_chunks;
+    }
     const int n = visible(len, row, T, Lmax);
     if (n <= k) return;                         // stage 2 fills such rows directly
-    constexpr int kChunk = REG * kPerIter;
     const int base = c * kChunk;
-    const int m = max(0, min(kChunk, n - base));
+    if (base >= n) return;                      // not read by stage 2
+    const int m = min(kChunk, n - base);
     const size_t slot0 = (static_cast<size_t>(row) * n_chunks + c) * k;
     uint32_t* ck = cand_key + slot0;
     int32_t* cp = cand_pos + slot0;
@@ -103,12 +122,13 @@ void topk_chunk_kernel(const float* __restrict__ scores, const int32_t* __restri
     block_select(ks, k, sh.sel, [&](uint32_t slot, int i, uint32_t key) { ck[slot] = key; cp[slot] = base + i; });
 }
 
-// Two-stage form, stage 2: top-k of a row's candidates (REG = 0: re-read them).
+// Two-stage form, stage 2: top-k of a row's candidates (REG = 0: re-read them), those
+// of the chunks [0, ceil(n / chunk)) that hold visible positions.
 template <int REG>
 __global__ __launch_bounds__(kThreads)
 void topk_merge_kernel(const uint32_t* __restrict__ cand_key, const int32_t* __restrict__ cand_pos,
                        const int32_t* __restrict__ len, int T, int Lmax, int k, int n_chunks,
-                       int32_t* __restrict__ idx)
+                       int chunk, int32_t* __restrict__ idx)
 {
     __shared__ TopkShared sh;
     const int row = blockIdx.x;
@@ -118,11 +138,11 @@ void topk_merge_kernel(const uint32_t* __restrict__ cand_key, const int32_t* __r
         for (int j = threadIdx.x; j < k; j += kThreads) out[j] = j < n ? j : -1;
         return;
     }
-    const int nc = n_chunks * k;
-    const size_t off = static_cast<size_t>(row) * nc;
+    const int nc = (n + chunk - 1) / chunk * k;
+    const size_t off = static_cast<size_t>(row) * n_chunks * k;
     const int32_t* cp = cand_pos + off;
     Keys<kThreads, REG, CandSrc> ks;
-    ks.init(CandSrc{cand_key + off, nc, (nc & 3) == 0}, nc);
+    ks.init(CandSrc{cand_key + off, nc, ((n_chunks * k) & 3) == 0}, nc);   // 16-byte aligned rows
     if (k <= kStagedOut) {
         block_select(ks, k, sh.sel, [&](uint32_t slot, int i, uint32_t) { sh.out[slot] = i; });
         __syncthreads();
@@ -173,10 +193,13 @@ hipError_t launch_topk(const TopkArgs& a, void* ws, hipStream_t stream) {
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const long long nc = static_cast<long long>(nch) * a.k;
+    const int chunk = chunk_for(a.Lmax, a.k);
     if (nc <= kSingleMax)
-        hipLaunchKernelGGL(topk_merge_kernel<4>, dim3(rows), block, 0, stream, ck, cp, a.len, a.T, a.Lmax, a.k, nch, a.idx);
+        hipLaunchKernelGGL(topk_merge_kernel<4>, dim3(rows), block, 0, stream, ck, cp, a.len, a.T, a.Lmax, a.k, nch,
+                           chunk, a.idx);
     else
-        hipLaunchKernelGGL(topk_merge_kernel<0>, dim3(rows), block, 0, stream, ck, cp, a.len, a.T, a.Lmax, a.k, nch, a.idx);
+        hipLaunchKernelGGL(topk_merge_kernel<0>, dim3(rows), block, 0, stream, ck, cp, a.len, a.T, a.Lmax, a.k, nch,
+                           chunk, a.idx);
     return hipGetLastError();
 }
 

@@ -95,6 +95,9 @@ TOPK_CASES = [
     ("zeros_long", "zeros", 1, 1, 30000, [30000], 2048),
     ("causal_long_odd_k", "normal", 1, 3, 20000, [20000], 3001),
     ("big_k_long", "heavy", 2, 1, 20000, [20000, 9000], 8000),
+    # nine rows of unequal length (chunk boundaries, rows needing no selection)
+    ("ragged_long_rows", "heavy", 9, 1, 50000,
+     [50000, 1000, 16384, 16385, 32768, 2049, 2048, 40001, 24000], 2048),
     ("zeros", "zeros", 2, 1, 3000, [3000, 2100], 2048),
     ("causal_rows", "normal", 2, 37, 1001, [1001, 37], 64),
     ("k1", "ties", 2, 3, 500, [500, 300], 1),
@@ -260,13 +263,15 @@ def test_layer_step_mha_small(dsa, orc):
     check_attention(_np_out(out), lse.cpu().numpy(), ro, rl, "bf16")
 
 
-def test_layer_step_without_intermediates(dsa, orc):
+@pytest.mark.parametrize("B,Lmax,lo,seed", [(3, 20000, 1024, 207), (9, 36000, 700, 208)])
+def test_layer_step_without_intermediates(dsa, orc, B, Lmax, lo, seed):
     """The production configuration (scores and indices kept in the workspace, invisible
-    scores never written, the top-k candidates of rows beyond 16384 positions sharing the
-    scratch region with the attention partials) gives bit-identical results to the
-    configuration that exposes the intermediates, which is checked against the oracle."""
-    _say("[layer_step] without intermediates, long ragged rows")
-    cfg = _small("decode_ragged", name="ni", B=3, Lmax=20000, lens="ragged:1024:20000", seed=207)
+    scores never written, key blocks and top-k chunks numbered over the visible range
+    only, the top-k candidates of rows beyond 16384 positions sharing the scratch region
+    with the attention partials) gives bit-identical results to the configuration that
+    exposes the intermediates, which is checked against the oracle."""
+    _say(f"[layer_step] without intermediates, long ragged rows, B={B} Lmax={Lmax}")
+    cfg = _small("decode_ragged", name="ni", B=B, Lmax=Lmax, lens=f"ragged:{lo}:{Lmax}", seed=seed)
     c = S.make_case(cfg)
     d = _dev(c)
     args = (d["q_i"], d["q_scale"], d["w"], d["k_i"], d["k_scale"], d["lens"], cfg.sm_scale_i,
