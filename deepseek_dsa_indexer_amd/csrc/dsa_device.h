@@ -17,13 +17,15 @@ __device__ __forceinline__ float bf16_to_f32(uint16_t h) {
     return __uint_as_float(static_cast<uint32_t>(h) << 16);
 }
 
-// round to nearest even; NaN stays NaN
+// Round to nearest even (NaN stays NaN): the gfx950 conversion instruction
+// (v_cvt_pk_bf16_f32), one VALU operation per pair and no branches.
 __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
-    uint32_t u = __float_as_uint(f);
-    if ((u & 0x7fffffffu) > 0x7f800000u) return static_cast<uint16_t>((u >> 16) | 0x40u);
-    u += 0x7fffu + ((u >> 16) & 1u);
-    return static_cast<uint16_t>(u >> 16);
+    return __builtin_bit_cast(uint16_t, static_cast<__bf16>(f));
 }
+
+// 1 / x for a normalising sum (x > 0): the hardware reciprocal (about 1 ulp), which is
+// far inside the bf16 rounding the results get.
+__device__ __forceinline__ float recip(float x) { return __builtin_amdgcn_rcpf(x); }
 
 // Order-preserving map of a float onto an unsigned key: larger float -> larger key.
 __device__ __forceinline__ uint32_t float_key(float f) {
@@ -43,6 +45,15 @@ __device__ __forceinline__ v4f mfma_fp8_16x16x128(const v8i& a, const v8i& b, co
 // (lane group l / 16 selects the K slice); output layout as above.
 __device__ __forceinline__ v4f mfma_bf16_16x16x32(const v8bf& a, const v8bf& b, const v4f& c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// 32x32x16 bf16 matrix-core product (twice the work of the 16x16x32 form in about the
+// same issue time on gfx950): lane l supplies 8 K-values of row/column l % 32, lane
+// half l / 32 selecting the K slice; output element r of lane l is
+// D[8 (r / 4) + 4 (l / 32) + r % 4][l % 32].
+typedef float v16f __attribute__((ext_vector_type(16)));
+__device__ __forceinline__ v16f mfma_bf16_32x32x16(const v8bf& a, const v8bf& b, const v16f& c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
 __device__ __forceinline__ float wave_sum(float v) {

@@ -397,20 +397,26 @@ void mla_decode_mfma_kernel(const uint16_t* __restrict__ q, const uint16_t* __re
     const int split = blockIdx.x / rows;
     const int b = row / T;
     const int t = row - b * T;
-    const int pos = min(len[b], Lmax) - T + t;
 
     const int n_tiles_total = (k + kKt - 1) / kKt;
     const int tile0 = split * tiles_per_split;
     const int n_tiles = max(0, min(tiles_per_split, n_tiles_total - tile0));
     const int nslots = n_tiles * kKt;
 
-    // selected positions of this split (-1: unused slot or not visible)
+    // The three independent start-up loads go out back to back, in the order they are
+    // needed: this split's selected positions, the sequence length, the queries.  The
+    // positions are checked against pos only when both have arrived (the queries stay
+    // in flight), so the gathers wait for one memory latency instead of three.
     const int32_t* sel = idx + static_cast<size_t>(row) * k;
-    for (int j = threadIdx.x; j < nslots; j += kMlaThreads) {
+    constexpr int kSlotIters = kMaxSlots / kMlaThreads;
+    int sraw[kSlotIters];
+#pragma unroll
+    for (int i = 0; i < kSlotIters; ++i) {
+        const int j = threadIdx.x + i * kMlaThreads;
         const int slot = tile0 * kKt + j;
-        const int s = slot < k ? sel[slot] : -1;
-        g_keys[j] = (s >= 0 && s <= pos) ? s : -1;
+        sraw[i] = (j < nslots && slot < k) ? sel[slot] : -1;
     }
+    const int seq_len = len[b];
 
     MlaState<NHT> st;
     {
@@ -419,6 +425,15 @@ void mla_decode_mfma_kernel(const uint16_t* __restrict__ q, const uint16_t* __re
         const uint16_t* qrow = q + (static_cast<size_t>(row) * H + head) * kDq + 8 * g;
 #pragma unroll
         for (int ds = 0; ds < kDs; ++ds) st.qreg[ds] = *reinterpret_cast<const v8bf*>(qrow + 32 * ds);
+    }
+
+    // selected positions of this split (-1: unused slot or not visible)
+    const int pos = min(seq_len, Lmax) - T + t;
+#pragma unroll
+    for (int i = 0; i < kSlotIters; ++i) {
+        const int j = threadIdx.x + i * kMlaThreads;
+        const int s = sraw[i];
+        if (j < nslots) g_keys[j] = (s >= 0 && s <= pos) ? s : -1;
     }
 #pragma unroll
     for (int h = 0; h < NHT; ++h)
@@ -489,7 +504,7 @@ void mla_decode_mfma_kernel(const uint16_t* __restrict__ q, const uint16_t* __re
         for (int i = 0; i < 4; ++i) {
             const int head = 16 * h + 4 * g + i;
             const float l = g_l[head];
-            const float inv = l > 0.f ? 1.f / l : 0.f;
+            const float inv = l > 0.f ? recip(l) : 0.f;
 #pragma unroll
             for (int dt = 0; dt < kDtW; ++dt) {
                 const int d = 64 * wave + 16 * dt + n;
@@ -536,32 +551,38 @@ void mla_combine_kernel(const uint16_t* __restrict__ part_o, const float* __rest
     if (gid >= H * (kDv / kCombCols)) return;
     const int d8 = gid % (kDv / kCombCols);
     const int h = gid / (kDv / kCombCols);
+    // every load goes out before the first wait (the split count is uniform, so the
+    // guards do not diverge): one memory latency per thread instead of two
     float ls[kMaxSplits];
-    float M = -INFINITY;
+    uint4 v[kMaxSplits];
 #pragma unroll
     for (int s = 0; s < kMaxSplits; ++s) {
-        ls[s] = s < n_splits ? part_lse[(row * n_splits + s) * H + h] : -INFINITY;
-        M = fmaxf(M, ls[s]);
-    }
-    float W = 0.f;
-    float acc[kCombCols] = {};
-    if (M != -INFINITY) {
-#pragma unroll
-        for (int s = 0; s < kMaxSplits; ++s) {
-            if (ls[s] == -INFINITY) continue;
-            const float wgt = exp2f(ls[s] - M);
-            W += wgt;
-            const uint4 v = *reinterpret_cast<const uint4*>(
-                part_o + ((row * n_splits + s) * H + h) * kDv + kCombCols * d8);
-            const uint32_t wv[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                acc[2 * i] += wgt * bf16_to_f32(static_cast<uint16_t>(wv[i] & 0xffffu));
-                acc[2 * i + 1] += wgt * bf16_to_f32(static_cast<uint16_t>(wv[i] >> 16));
-            }
+        if (s < n_splits) {
+            ls[s] = part_lse[(row * n_splits + s) * H + h];
+            v[s] = *reinterpret_cast<const uint4*>(part_o + ((row * n_splits + s) * H + h) * kDv + kCombCols * d8);
+        } else {
+            ls[s] = -INFINITY;
+            v[s] = uint4{0u, 0u, 0u, 0u};
         }
     }
-    const float inv = W > 0.f ? 1.f / W : 0.f;
+    float M = -INFINITY;
+#pragma unroll
+    for (int s = 0; s < kMaxSplits; ++s) M = fmaxf(M, ls[s]);
+    float W = 0.f;
+    float acc[kCombCols] = {};
+#pragma unroll
+    for (int s = 0; s < kMaxSplits; ++s) {
+        // a split with no usable slot (lse -inf) has weight 0 and a zero output
+        const float wgt = ls[s] == -INFINITY ? 0.f : exp2f(ls[s] - M);
+        W += wgt;
+        const uint32_t wv[4] = {v[s].x, v[s].y, v[s].z, v[s].w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            acc[2 * i] += wgt * bf16_to_f32(static_cast<uint16_t>(wv[i] & 0xffffu));
+            acc[2 * i + 1] += wgt * bf16_to_f32(static_cast<uint16_t>(wv[i] >> 16));
+        }
+    }
+    const float inv = W > 0.f ? recip(W) : 0.f;
     uint32_t o[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i)

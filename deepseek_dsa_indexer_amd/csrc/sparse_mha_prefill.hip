@@ -295,7 +295,7 @@ void mha_prefill_mfma_kernel(const uint16_t* __restrict__ q, const uint16_t* __r
         for (int i = 0; i < 4; ++i) {
             const float l = __shfl(st.l_run[qt], 4 * g + i, kWave);
             const float m = __shfl(st.m_run[qt], 4 * g + i, kWave);
-            inv4[i] = l > 0.f ? 1.f / l : 0.f;
+            inv4[i] = l > 0.f ? recip(l) : 0.f;
             lse4[i] = l > 0.f ? (m + log2f(l)) * kLn2M : -INFINITY;
         }
 #pragma unroll
