@@ -68,14 +68,73 @@ __device__ __forceinline__ float wave_max(float v) {
     return v;
 }
 
-// Inclusive prefix sum over the 64 lanes of a wave.
-__device__ __forceinline__ uint32_t wave_inclusive_scan(uint32_t v, int lane) {
-#pragma unroll
-    for (int o = 1; o < kWave; o <<= 1) {
-        uint32_t t = __shfl_up(v, o, kWave);
-        if (lane >= o) v += t;
-    }
+// ---- cross-lane steps on the VALU (DPP and the gfx950 lane-swap instructions) rather
+// than through the LDS crossbar (ds_bpermute, about a hundred cycles per step).
+// DPP controls: row_shr:n = 0x110 + n, row_ror:n = 0x120 + n, row_bcast:15 = 0x142,
+// row_bcast:31 = 0x143 (rows are 16 lanes).
+template <int CTRL, int ROW_MASK = 0xf>
+__device__ __forceinline__ uint32_t dpp(uint32_t v) {
+    // lanes without a source, and rows outside ROW_MASK, read 0
+    return static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(v), CTRL, ROW_MASK, 0xf, false));
+}
+
+// v_permlane16_swap / v_permlane32_swap with the same register on both sides: the pair
+// holds, in some order, this lane's value and that of lane l ^ 16 (l ^ 32), so a
+// commutative operation on the pair gives the same result in both lanes.
+__device__ __forceinline__ void pair16(uint32_t v, uint32_t& a, uint32_t& b) {
+    const auto r = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+    a = r[0]; b = r[1];
+}
+__device__ __forceinline__ void pair32(uint32_t v, uint32_t& a, uint32_t& b) {
+    const auto r = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+    a = r[0]; b = r[1];
+}
+__device__ __forceinline__ float max_xor16(float v) {
+    uint32_t a, b; pair16(__float_as_uint(v), a, b); return fmaxf(__uint_as_float(a), __uint_as_float(b));
+}
+__device__ __forceinline__ float max_xor32(float v) {
+    uint32_t a, b; pair32(__float_as_uint(v), a, b); return fmaxf(__uint_as_float(a), __uint_as_float(b));
+}
+__device__ __forceinline__ float sum_xor16(float v) {
+    uint32_t a, b; pair16(__float_as_uint(v), a, b); return __uint_as_float(a) + __uint_as_float(b);
+}
+__device__ __forceinline__ float sum_xor32(float v) {
+    uint32_t a, b; pair32(__float_as_uint(v), a, b); return __uint_as_float(a) + __uint_as_float(b);
+}
+// The value of lane l ^ 16 (l ^ 32); `lane` is this lane's index in the wave.
+__device__ __forceinline__ float from_xor16(float v, int lane) {
+    uint32_t a, b; pair16(__float_as_uint(v), a, b); return __uint_as_float((lane & 16) ? a : b);
+}
+__device__ __forceinline__ float from_xor32(float v, int lane) {
+    uint32_t a, b; pair32(__float_as_uint(v), a, b); return __uint_as_float((lane & 32) ? a : b);
+}
+
+// Inclusive prefix sum over the 64 lanes of a wave: Hillis-Steele within each 16-lane
+// row, then the row totals carried across rows by broadcasts.
+__device__ __forceinline__ uint32_t wave_inclusive_scan(uint32_t v, int) {
+    v += dpp<0x111>(v);
+    v += dpp<0x112>(v);
+    v += dpp<0x114>(v);
+    v += dpp<0x118>(v);
+    v += dpp<0x142, 0xa>(v);
+    v += dpp<0x143, 0xc>(v);
     return v;
+}
+
+// Minimum / maximum over the wave, in every lane.
+__device__ __forceinline__ uint32_t wave_min_u32(uint32_t v) {
+    v = min(v, dpp<0x128>(v)); v = min(v, dpp<0x124>(v));
+    v = min(v, dpp<0x122>(v)); v = min(v, dpp<0x121>(v));
+    uint32_t a, b;
+    pair16(v, a, b); v = min(a, b);
+    pair32(v, a, b); return min(a, b);
+}
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+    v = max(v, dpp<0x128>(v)); v = max(v, dpp<0x124>(v));
+    v = max(v, dpp<0x122>(v)); v = max(v, dpp<0x121>(v));
+    uint32_t a, b;
+    pair16(v, a, b); v = max(a, b);
+    pair32(v, a, b); return max(a, b);
 }
 
 // Work numbering for launches over the sequences of a batch whose sequences need

@@ -78,13 +78,14 @@ __device__ __forceinline__ float head_sum_transpose(const float s[4], int g) {
     const bool lo = g < 2;
     float send0 = lo ? s[2] : s[0];
     float send1 = lo ? s[3] : s[1];
-    float r0 = __shfl_xor(send0, 32, kWave);
-    float r1 = __shfl_xor(send1, 32, kWave);
+    const int lane = g << 4;                    // bits 4 and 5 of the lane index
+    float r0 = from_xor32(send0, lane);
+    float r1 = from_xor32(send1, lane);
     float a0 = (lo ? s[0] : s[2]) + r0;     // tile 0 (g < 2) or tile 2
     float a1 = (lo ? s[1] : s[3]) + r1;     // tile 1 (g < 2) or tile 3
     const bool odd = g & 1;
     float send = odd ? a0 : a1;
-    float r = __shfl_xor(send, 16, kWave);
+    float r = from_xor16(send, lane);
     return (odd ? a1 : a0) + r;
 }
 

@@ -297,8 +297,7 @@ __device__ __forceinline__ void mla_qk_softmax(MlaState<NHT>& st, const uint8_t*
             sv[4 * kt + i] = v;
             mx = fmaxf(mx, v);
         }
-    mx = fmaxf(mx, __shfl_xor(mx, 16, kWave));
-    mx = fmaxf(mx, __shfl_xor(mx, 32, kWave));
+    mx = max_xor32(max_xor16(mx));
     alpha = 1.f;
     if (mx > st.m_run + kLazyRescale) {
         // nothing accumulated yet (O = 0, l = 0): no rescale needed
@@ -312,8 +311,7 @@ __device__ __forceinline__ void mla_qk_softmax(MlaState<NHT>& st, const uint8_t*
         psum += p;
         pk[j] = static_cast<short>(f32_to_bf16(p));
     }
-    psum += __shfl_xor(psum, 16, kWave);
-    psum += __shfl_xor(psum, 32, kWave);
+    psum = sum_xor32(sum_xor16(psum));
     st.l_run = st.l_run * alpha + psum;
 }
 

@@ -175,8 +175,7 @@ __device__ __forceinline__ void mha_block(MhaState& st, const uint8_t* stage, co
                 sv[4 * kt + i] = v;
                 mx = fmaxf(mx, v);
             }
-        mx = fmaxf(mx, __shfl_xor(mx, 16, kWave));
-        mx = fmaxf(mx, __shfl_xor(mx, 32, kWave));
+        mx = max_xor32(max_xor16(mx));
         float alpha = 1.f;
         if (mx > st.m_run[qt] + kLazy) {
             // nothing accumulated yet (O = 0, l = 0): no rescale needed
@@ -190,8 +189,7 @@ __device__ __forceinline__ void mha_block(MhaState& st, const uint8_t* stage, co
             psum += p;
             pk[qt][j >> 3][j & 7] = static_cast<short>(f32_to_bf16(p));
         }
-        psum += __shfl_xor(psum, 16, kWave);
-        psum += __shfl_xor(psum, 32, kWave);
+        psum = sum_xor32(sum_xor16(psum));
         st.l_run[qt] = st.l_run[qt] * alpha + psum;
         // alpha is per query row n: the O rows of this lane are rows 4 g + i, held by
         // lanes n' = 4 g + i; fetch their alphas

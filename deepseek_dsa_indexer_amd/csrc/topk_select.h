@@ -177,11 +177,8 @@ __device__ __forceinline__ void block_select(Keys<NT, REG, Src>& ks, int k, Sele
     ks.visit_all([&](uint32_t key, int, bool ok) {
         if (ok) { kmin = min(kmin, key); kmax = max(kmax, key); }
     });
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) {
-        kmin = min(kmin, static_cast<uint32_t>(__shfl_xor(static_cast<int>(kmin), o, kWave)));
-        kmax = max(kmax, static_cast<uint32_t>(__shfl_xor(static_cast<int>(kmax), o, kWave)));
-    }
+    kmin = wave_min_u32(kmin);
+    kmax = wave_max_u32(kmax);
     if (lane == 0) { sh.red[0][wave] = kmin; sh.red[1][wave] = kmax; }
     for (int i = threadIdx.x; i < kSelBins; i += NT) sh.hist[0][i] = 0;
     __syncthreads();
