@@ -264,6 +264,197 @@ void index_scores_kernel(const uint8_t* __restrict__ q, const float* __restrict_
     }
 }
 
+// ---------------------------------------------------------------- decode form
+//
+// One query row per block (T = 1).  Each wave streams its chunks global -> LDS with direct
+// loads (global_load_lds) into a ring of two 8.25 KB slots of its own, so two chunks per
+// wave stay in flight without holding registers (the register-staged form above keeps
+// one chunk per wave, 64 KB per CU, in flight).  The query row and the head weights
+// arrive the same way.  Slot layout, in load order: 1 KB piece 2 t + p holds, at lane l,
+// bytes [64 p + 16 (l / 16), + 16) of key 16 t + l % 16 of the chunk -- exactly what lane l
+// reads as its MFMA operand piece, so each operand read is one contiguous 16-byte lane
+// read -- and the 256 bytes after the keys hold their 64 scales.  The loads are inline
+// assembly, invisible to the compiler's wait counting: every wait is an explicit vmcnt
+// over this wave's own loads (they complete in issue order), and no other wave touches a
+// wave's slots, so the ring needs no barrier.
+constexpr int kRing = 2;
+constexpr int kSlotBytes = kChunk * 128 + kChunk * 4;     // 8448
+constexpr int kChunkLoads = 9;                            // 8 x 1 KB of keys + 256 B of scales
+constexpr int kWaves = kThreads / kWave;
+
+template <int N>
+__device__ __forceinline__ void vm_wait() { asm volatile("s_waitcnt vmcnt(%0)" :: "n"(N) : "memory"); }
+
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+    return static_cast<uint32_t>(reinterpret_cast<uintptr_t>(
+        (__attribute__((address_space(3))) const uint8_t*)(p)));
+}
+// Lane l's 16 bytes at src go to LDS byte lds + 16 l (M0 carries the wave-uniform base;
+// no other instruction of these kernels uses M0).
+__device__ __forceinline__ void dma16(uint32_t lds, const void* src) {
+    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off"
+                 :: "s"(__builtin_amdgcn_readfirstlane(lds)), "v"(src) : "memory");
+}
+// Lane l's 4 bytes at src go to LDS byte lds + 4 l.
+__device__ __forceinline__ void dma4(uint32_t lds, const void* src) {
+    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dword %1, off"
+                 :: "s"(__builtin_amdgcn_readfirstlane(lds)), "v"(src) : "memory");
+}
+
+template <int D>
+__global__ __launch_bounds__(kThreads)
+void index_scores_decode_kernel(const uint8_t* __restrict__ q, const float* __restrict__ q_scale,
+                                const float* __restrict__ w, const uint8_t* __restrict__ k,
+                                const float* __restrict__ k_scale, const int32_t* __restrict__ len,
+                                int H, int Lmax, float sm_scale, float* __restrict__ scores,
+                                int fill_invisible, int chunks)
+{
+    __shared__ __attribute__((aligned(16))) uint8_t s_q[kMaxHeads * 128];
+    __shared__ __attribute__((aligned(16))) float s_w[kMaxHeads];
+    __shared__ __attribute__((aligned(16))) float s_qs[kMaxHeads];
+    __shared__ __attribute__((aligned(16))) uint8_t s_ring[kWaves][kRing][kSlotBytes];
+    __shared__ int s_num[kWaves + 2];
+    const int keys_per_block = kWaves * kChunk * chunks;
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+    const int g = lane >> 4;
+    const int n = lane & 15;
+
+    // numbered blocks: sequences of unequal length still spread evenly over the XCDs, and
+    // no block past a sequence's end is run unless its positions are to be filled
+    int b, yblk;
+    {
+        const int nblk = gridDim.y;
+        auto count = [&](int sq) {
+            return fill_invisible ? nblk : (min(len[sq], Lmax) + keys_per_block - 1) / keys_per_block;
+        };
+        if (!numbered_block<kThreads>(blockIdx.y * gridDim.x + blockIdx.x, gridDim.x, count, s_num, b, yblk))
+            return;
+    }
+    const int pos = min(len[b], Lmax) - 1;
+    const int key_blk = yblk * keys_per_block;
+    float* out = scores + static_cast<size_t>(b) * Lmax;
+    if (key_blk > pos) {                        // the whole block is masked
+        for (int key = key_blk + threadIdx.x; key < min(key_blk + keys_per_block, Lmax); key += kThreads)
+            out[key] = -INFINITY;
+        return;
+    }
+
+    const uint8_t* kb_ptr = k + static_cast<size_t>(b) * Lmax * D;
+    const float* ks_ptr = k_scale + static_cast<size_t>(b) * Lmax;
+    // chunk c of this wave starts at key_blk + (4 c + wave) * 64; the chunks holding a
+    // visible position are c < n_live
+    const int first = key_blk + wave * kChunk;
+    const int n_live = pos < first ? 0 : min(chunks, (pos - first) / (kWaves * kChunk) + 1);
+    auto issue = [&](int c) {
+        uint8_t* slot = s_ring[wave][c & 1];
+        const int kb = first + c * kWaves * kChunk;
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            const uint8_t* krow = kb_ptr + static_cast<size_t>(min(kb + 16 * t + n, Lmax - 1)) * D;
+#pragma unroll
+            for (int p = 0; p < 2; ++p) {
+                const int byte = 64 * p + 16 * g;       // pieces past d_I are masked on read
+                dma16(lds_addr(slot + (2 * t + p) * 1024), krow + (byte < D ? byte : 0));
+            }
+        }
+        dma4(lds_addr(slot + kChunk * 128), ks_ptr + min(kb + lane, Lmax - 1));
+    };
+
+    // ---- the query row (wave w brings bytes [2048 w, 2048 w + 2048) of [64 heads][128]),
+    // the head weights (wave 0) and q scales (wave 1), then the first two chunks
+    const uint8_t* qrow = q + static_cast<size_t>(b) * H * D;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        const int o = 2048 * wave + 1024 * i + 16 * lane;
+        const int h = min(o >> 7, H - 1), byte = o & 127;   // heads past H, bytes past D: masked on read
+        dma16(lds_addr(s_q + 2048 * wave + 1024 * i), qrow + h * D + (byte < D ? byte : 0));
+    }
+    if (wave == 0) dma4(lds_addr(s_w), w + static_cast<size_t>(b) * H + min(lane, H - 1));
+    if (wave == 1) dma4(lds_addr(s_qs), q_scale + static_cast<size_t>(b) * H + min(lane, H - 1));
+    if (n_live > 0) issue(0);
+    if (n_live > 1) issue(1);
+    // this wave's query and weight loads are in when at most its chunk loads remain
+    if (n_live > 1) vm_wait<2 * kChunkLoads>();
+    else if (n_live > 0) vm_wait<kChunkLoads>();
+    else vm_wait<0>();
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+
+    v8bf qa[4][4];
+    float wf[4][4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int h = 16 * j + n;
+        const uint4 lo = *reinterpret_cast<const uint4*>(&s_q[h * 128 + 16 * g]);
+        const uint4 hi = *reinterpret_cast<const uint4*>(&s_q[h * 128 + 64 + 16 * g]);
+        const int m0 = (h < H && 16 * g < D) ? -1 : 0;
+        const int m1 = (h < H && 64 + 16 * g < D) ? -1 : 0;
+        const int raw[8] = {static_cast<int>(lo.x) & m0, static_cast<int>(lo.y) & m0,
+                            static_cast<int>(lo.z) & m0, static_cast<int>(lo.w) & m0,
+                            static_cast<int>(hi.x) & m1, static_cast<int>(hi.y) & m1,
+                            static_cast<int>(hi.z) & m1, static_cast<int>(hi.w) & m1};
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) qa[j][kk] = fp8x8_to_bf16(raw[2 * kk], raw[2 * kk + 1]);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int hh = 16 * j + 4 * g + i;
+            wf[j][i] = hh < H ? s_w[hh] * s_qs[hh] * sm_scale : 0.f;
+        }
+    }
+
+    for (int c = 0; c < n_live; ++c) {
+        // chunk c is in when at most chunk c + 1's loads remain
+        if (c + 1 < n_live) vm_wait<kChunkLoads>();
+        else vm_wait<0>();
+        const uint8_t* slot = s_ring[wave][c & 1];
+        v8i cur[4];
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            const uint4 lo = *reinterpret_cast<const uint4*>(slot + (2 * t) * 1024 + 16 * lane);
+            const uint4 hi = *reinterpret_cast<const uint4*>(slot + (2 * t + 1) * 1024 + 16 * lane);
+            const int m0 = 16 * g < D ? -1 : 0;
+            const int m1 = 64 + 16 * g < D ? -1 : 0;
+            cur[t] = v8i{static_cast<int>(lo.x) & m0, static_cast<int>(lo.y) & m0,
+                         static_cast<int>(lo.z) & m0, static_cast<int>(lo.w) & m0,
+                         static_cast<int>(hi.x) & m1, static_cast<int>(hi.y) & m1,
+                         static_cast<int>(hi.z) & m1, static_cast<int>(hi.w) & m1};
+        }
+        const float ks = *reinterpret_cast<const float*>(slot + kChunk * 128 + 4 * lane);
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // slot read before it is refilled
+        if (c + 2 < n_live) issue(c + 2);
+
+        float sc[4];
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            v8bf kbf[4];
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk) kbf[kk] = fp8x8_to_bf16(cur[t][2 * kk], cur[t][2 * kk + 1]);
+            v4f d[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) d[j] = v4f{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) d[j] = mfma_bf16_16x16x32(qa[j][kk], kbf[kk], d[j]);
+            float acc = 0.f;
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) acc += wf[j][i] * fmaxf(d[j][i], 0.f);
+            sc[t] = acc;
+        }
+        const float total = head_sum_transpose(sc, g);
+        const int key = first + c * kWaves * kChunk + lane;
+        if (key < Lmax) out[key] = key <= pos ? total * ks : -INFINITY;
+    }
+    if (fill_invisible) {
+        for (int c = n_live; c < chunks; ++c) {
+            const int key = first + c * kWaves * kChunk + lane;
+            if (key < Lmax) out[key] = -INFINITY;
+        }
+    }
+}
+
 template <int D, int QR>
 hipError_t launch_d(const IndexScoresArgs& a, int chunks, hipStream_t stream) {
     const int keys_per_block = kThreads / kWave * kChunk * chunks;
@@ -282,7 +473,16 @@ hipError_t launch_rows(const IndexScoresArgs& a, hipStream_t stream) {
     if (a.T >= 2) return launch_d<D, 2>(a, 4, stream);
     const long long total_chunks = static_cast<long long>(a.B) * ((a.Lmax + kChunk - 1) / kChunk);
     const int chunks = static_cast<int>(std::min<long long>(8, std::max<long long>(2, total_chunks / 2048)));
-    return launch_d<D, 1>(a, chunks, stream);
+    // short streams (two chunks per wave) gain nothing from the deeper LDS pipeline and
+    // pay its longer issue sequence: measured 12.4 vs 10.9 us at B=32, L=8192; at
+    // B=8, L=131072 (eight chunks per wave) the LDS form is ahead
+    if (a.B > kThreads * kMaxSeqPerThread || chunks < 4) return launch_d<D, 1>(a, chunks, stream);
+    const int keys_per_block = kWaves * kChunk * chunks;
+    dim3 grid(a.B, (a.Lmax + keys_per_block - 1) / keys_per_block);
+    hipLaunchKernelGGL((index_scores_decode_kernel<D>), grid, dim3(kThreads), 0, stream,
+                       a.q, a.q_scale, a.w, a.k, a.k_scale, a.len, a.H, a.Lmax, a.sm_scale,
+                       a.scores, a.fill_invisible, chunks);
+    return hipGetLastError();
 }
 
 }  // namespace

@@ -53,6 +53,11 @@ INDEX_CASES = [
     ("decode_normal_small", _small("decode_v32", name="dns", B=2, Lmax=777, seed=102)),
     ("prefill_small", _small("prefill_chunk", name="ps", T=70, Lmax=300, lens="ragged:70:300",
                              B=2, H_I=48, D_I=64, seed=104)),
+    # long decode rows: the LDS-streamed decode kernel (four or more chunks per wave),
+    # with padded heads and columns and ragged lengths
+    ("decode_long_rows", _small("decode_ragged", name="dlr", B=2, Lmax=270000,
+                                lens="ragged:100000:270000", H_I=48, D_I=64, H=4, Dv=16, Dr=16,
+                                seed=106)),
 ]
 
 
