@@ -125,9 +125,8 @@ void sparse_attn_generic_kernel(SparseAttnArgs a)
 //   QK       wave w computes S^T = K . Q^T for head tile w (16 heads) and all 32 keys of
 //            the tile (keys as MFMA rows; the wave's queries stay in registers as 18 B
 //            operands);
-//   softmax  online, per head, entirely inside the owning wave, with lazy rescaling: the
-//            running maximum only moves when a tile exceeds it by more than 2^8; the bf16
-//            probabilities go to LDS in MFMA operand layout;
+//   softmax  per head, entirely inside the owning wave, relative to a fixed reference
+//            (below); the bf16 numerators go to LDS in MFMA operand layout;
 //   PV       wave w owns output columns 64w..64w+63 for all heads: O += P . V with V read
 //            from the same LDS tile by transpose reads (the value is the first 512
 //            columns of the latent row).
@@ -138,6 +137,14 @@ void sparse_attn_generic_kernel(SparseAttnArgs a)
 // SIMDs), so within a step the pair drifts apart and one wave's softmax overlaps the
 // other's matrix-core work.  Splits of one row are merged by a log-sum-exp combine
 // kernel.
+//
+// No running-maximum rescale of the output accumulators: each head's numerators are
+// exp2(logit - m_ref) with m_ref the maximum of the first tile that has a usable slot,
+// which is exact in floating point while nothing overflows, and keeps a conditional
+// update of all accumulators (and the per-tile rescale factors) out of the loop.  A later
+// logit more than 2^64 above the reference (log2 units) marks the split, and a marked
+// split is recomputed from its first tile with the split's true maximum as the
+// reference, so every numerator is then at most 1.
 constexpr int kMlaThreads = 512;
 constexpr int kMlaWaves = 8;
 constexpr int kMaxHt = 8;                          // up to 128 heads per workgroup
@@ -153,13 +160,12 @@ constexpr int kDs = kDq / 32;                      // 18 K-steps of the QK produ
 constexpr int kDtW = kDv / kMlaWaves / 16;         // 4 output column tiles per wave
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
-constexpr float kLazyRescale = 8.0f;               // log2 units
+constexpr float kRefSpan = 64.0f;                  // log2 units above the reference
 
 constexpr int kBufs = 4;                          // tile ring
 __shared__ __attribute__((aligned(16))) uint8_t g_kbuf[kBufs * kTileBytes];
 __shared__ __attribute__((aligned(16))) uint8_t g_pbuf[kMaxHt][kWave][16];
-__shared__ __attribute__((aligned(16))) float g_alpha[kMaxHt * 16];
-__shared__ int32_t g_rescale[kMaxHt];
+__shared__ int32_t g_rescale[kMlaWaves];          // per-wave "recompute the split" flags
 __shared__ float g_l[kMaxHt * 16];
 __shared__ float g_m[kMaxHt * 16];
 __shared__ int32_t g_keys[kMaxSlots];
@@ -230,18 +236,20 @@ template <int NHT>
 struct MlaState {
     v8bf qreg[kDs];
     v4f o[NHT][kDtW];
-    float m_run;
+    float m_ref;                 // reference logit of this lane's head (log2 units)
+    float m_max;                 // largest logit seen
     float l_run;
+    bool over;                   // a logit exceeded m_ref + kRefSpan
 };
 
 typedef __bf16 v4bf_t __attribute__((ext_vector_type(4)));
 
-// QK and online softmax of tile ti (buffer kb) for head tile `wave` (< NHT).  Returns
-// the bf16 probabilities in PV A-operand layout and the head's rescale factor; they are
-// published after the step's second barrier.
+// QK and softmax numerators of tile ti (buffer kb) for head tile `wave` (< NHT).  Returns
+// the bf16 numerators in PV A-operand layout; they are published after the step's second
+// barrier.  fixed: m_ref is final.
 template <int NHT>
 __device__ __forceinline__ void mla_qk_softmax(MlaState<NHT>& st, const uint8_t* kb, int ti,
-                                               float scale_log2, int lane, v8s& pk, float& alpha) {
+                                               float scale_log2, int lane, v8s& pk, bool fixed) {
     // Per-lane LDS offsets are recomputed in every tile step from an opaque copy of the
     // lane id: hoisted out of the loop they would be kept live once per buffer copy.
     int lane_o = lane;
@@ -298,25 +306,23 @@ __device__ __forceinline__ void mla_qk_softmax(MlaState<NHT>& st, const uint8_t*
             mx = fmaxf(mx, v);
         }
     mx = max_xor32(max_xor16(mx));
-    alpha = 1.f;
-    if (mx > st.m_run + kLazyRescale) {
-        // nothing accumulated yet (O = 0, l = 0): no rescale needed
-        alpha = (st.m_run == -INFINITY) ? 1.f : exp2f(st.m_run - mx);
-        st.m_run = mx;
+    if (!fixed) {
+        if (st.m_ref == -INFINITY) st.m_ref = mx;       // first tile with a usable slot
+        st.m_max = fmaxf(st.m_max, mx);
+        st.over = st.over || mx > st.m_ref + kRefSpan;
     }
     float psum = 0.f;
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-        const float p = (sv[j] == -INFINITY) ? 0.f : exp2f(sv[j] - st.m_run);
+        const float p = (sv[j] == -INFINITY) ? 0.f : exp2f(sv[j] - st.m_ref);
         psum += p;
         pk[j] = static_cast<short>(f32_to_bf16(p));
     }
-    psum = sum_xor32(sum_xor16(psum));
-    st.l_run = st.l_run * alpha + psum;
+    st.l_run += sum_xor32(sum_xor16(psum));
 }
 
-// PV of the previous tile (buffer kb, probabilities and rescale factors in g_pbuf,
-// g_alpha, g_rescale): output columns 64 wave .. + 63 for all heads.  V operands come
+// PV of the previous tile (buffer kb, numerators in g_pbuf): output columns
+// 64 wave .. + 63 for all heads.  V operands come
 // from LDS transpose reads: for K-slots j = 4 kt + r the lane needs V[16 kt + 4 g + r][d],
 // d = 64 wave + 16 dt + n; within each 16-lane group a transpose read hands lane n the
 // element at (address of lane 4 r + n / 4) + n % 4, so lane m supplies row
@@ -346,29 +352,16 @@ __device__ __forceinline__ void mla_pv(MlaState<NHT>& st, const uint8_t* kb, int
 #pragma unroll
     for (int h = 0; h < NHT; ++h) {
         __builtin_amdgcn_sched_barrier(0);
-        if (g_rescale[h]) {
-            const float4 al = *reinterpret_cast<const float4*>(&g_alpha[16 * h + 4 * go]);
-#pragma unroll
-            for (int dt = 0; dt < kDtW; ++dt) {
-                st.o[h][dt][0] *= al.x; st.o[h][dt][1] *= al.y;
-                st.o[h][dt][2] *= al.z; st.o[h][dt][3] *= al.w;
-            }
-        }
         const v8bf pa = *reinterpret_cast<const v8bf*>(&g_pbuf[h][lane][0]);
 #pragma unroll
         for (int dt = 0; dt < kDtW; ++dt) st.o[h][dt] = mfma_bf16_16x16x32(pa, vb[dt], st.o[h][dt]);
     }
 }
 
-// Publish P and the rescale factors of the wave's head tile (after the step's second
-// barrier: every wave is then done reading the previous tile's).
-__device__ __forceinline__ void mla_publish(const v8s& pk, float alpha, int wave, int lane) {
-    const int go = lane >> 4;
-    const int no = lane & 15;
+// Publish P of the wave's head tile (after the step's second barrier: every wave is then
+// done reading the previous tile's).
+__device__ __forceinline__ void mla_publish(const v8s& pk, int wave, int lane) {
     *reinterpret_cast<v8s*>(&g_pbuf[wave][lane][0]) = pk;
-    if (go == 0) g_alpha[16 * wave + no] = alpha;
-    const unsigned long long any = __ballot(alpha != 1.f);
-    if (lane == 0) g_rescale[wave] = any != 0ull;
 }
 
 template <int NHT>
@@ -433,63 +426,79 @@ void mla_decode_mfma_kernel(const uint16_t* __restrict__ q, const uint16_t* __re
         const int s = sraw[i];
         if (j < nslots) g_keys[j] = (s >= 0 && s <= pos) ? s : -1;
     }
-#pragma unroll
-    for (int h = 0; h < NHT; ++h)
-#pragma unroll
-        for (int dt = 0; dt < kDtW; ++dt) st.o[h][dt] = v4f{0.f, 0.f, 0.f, 0.f};
-    st.m_run = -INFINITY;
-    st.l_run = 0.f;
+    st.m_ref = -INFINITY;
+    st.m_max = -INFINITY;
+    st.over = false;
 
     const uint8_t* lat_b = reinterpret_cast<const uint8_t*>(latent) +
                            static_cast<size_t>(b) * Lmax * kRowBytes;
     lds_barrier();        // g_keys ready (its stores waited for the idx loads)
+    const bool qk_wave = wave < NHT;
+    // One pass over the split's tiles; the queries and the selected positions stay in
+    // place between passes.
     // Tile 0 goes out together with the queries; wait for both, then put tile 1 in
     // flight.  The compiler's own wait for the query registers (it does not see the
     // gathers) then falls here, where nothing else is outstanding.
-    if (n_tiles > 0) gather_tile(lat_b, 0, kbuf(0), wave, lane);
-    wait_vmcnt<0>();
-#pragma unroll
-    for (int ds = 0; ds < kDs; ++ds) asm volatile("" :: "v"(st.qreg[ds]));
-    if (n_tiles > 1) gather_tile(lat_b, 1, kbuf(1), wave, lane);
-
     // Step 0: QK + softmax of tile 0.  Steps 1 .. n_tiles-1: PV of tile i-1 and QK +
     // softmax of tile i.  Last: PV of tile n_tiles-1.  Every step waits for its tile,
     // passes a barrier (tile i and P(i-1) visible; the buffer of tile i-2 released) and
     // prefetches tile i+2; a second barrier separates the reads of P(i-1) from the
     // publication of P(i).  The loop body has no data-dependent branch around the
     // accumulators, so they keep their registers across iterations.
-    const bool qk_wave = wave < NHT;
-    if (n_tiles > 0) {
-        wait_tile(1 < n_tiles, wave < 4);
-        lds_barrier();
-        if (2 < n_tiles) gather_tile(lat_b, 2, kbuf(2), wave, lane);
-        v8s pk;
-        float alpha = 1.f;
-        if (qk_wave) mla_qk_softmax<NHT>(st, kbuf(0), 0, scale_log2, lane, pk, alpha);
-        lds_barrier();
-        if (qk_wave) mla_publish(pk, alpha, wave, lane);
-    }
-    for (int ti = 1; ti < n_tiles; ++ti) {
-        wait_tile(ti + 1 < n_tiles, wave < 4);
-        lds_barrier();
-        if (ti + 2 < n_tiles) gather_tile(lat_b, ti + 2, kbuf(ti + 2), wave, lane);
-        mla_pv<NHT>(st, kbuf(ti - 1), wave, lane);
-        __builtin_amdgcn_sched_barrier(0);
-        v8s pk;
-        float alpha = 1.f;
-        if (qk_wave) mla_qk_softmax<NHT>(st, kbuf(ti), ti, scale_log2, lane, pk, alpha);
-        lds_barrier();
-        if (qk_wave) mla_publish(pk, alpha, wave, lane);
-    }
-    if (n_tiles > 0) {
-        lds_barrier();
-        mla_pv<NHT>(st, kbuf(n_tiles - 1), wave, lane);
+    auto pass = [&](bool fixed) {
+#pragma unroll
+        for (int h = 0; h < NHT; ++h)
+#pragma unroll
+            for (int dt = 0; dt < kDtW; ++dt) st.o[h][dt] = v4f{0.f, 0.f, 0.f, 0.f};
+        st.l_run = 0.f;
+        if (n_tiles > 0) gather_tile(lat_b, 0, kbuf(0), wave, lane);
+        wait_vmcnt<0>();
+#pragma unroll
+        for (int ds = 0; ds < kDs; ++ds) asm volatile("" :: "v"(st.qreg[ds]));
+        if (n_tiles > 1) gather_tile(lat_b, 1, kbuf(1), wave, lane);
+        if (n_tiles > 0) {
+            wait_tile(1 < n_tiles, wave < 4);
+            lds_barrier();
+            if (2 < n_tiles) gather_tile(lat_b, 2, kbuf(2), wave, lane);
+            v8s pk;
+            if (qk_wave) mla_qk_softmax<NHT>(st, kbuf(0), 0, scale_log2, lane, pk, fixed);
+            lds_barrier();
+            if (qk_wave) mla_publish(pk, wave, lane);
+        }
+        for (int ti = 1; ti < n_tiles; ++ti) {
+            wait_tile(ti + 1 < n_tiles, wave < 4);
+            lds_barrier();
+            if (ti + 2 < n_tiles) gather_tile(lat_b, ti + 2, kbuf(ti + 2), wave, lane);
+            mla_pv<NHT>(st, kbuf(ti - 1), wave, lane);
+            __builtin_amdgcn_sched_barrier(0);
+            v8s pk;
+            if (qk_wave) mla_qk_softmax<NHT>(st, kbuf(ti), ti, scale_log2, lane, pk, fixed);
+            lds_barrier();
+            if (qk_wave) mla_publish(pk, wave, lane);
+        }
+        if (n_tiles > 0) {
+            lds_barrier();
+            mla_pv<NHT>(st, kbuf(n_tiles - 1), wave, lane);
+        }
+    };
+    pass(false);
+    // a head of the workgroup past its reference span: redo the split from the split's
+    // maximum (a uniform decision: every wave reads the same flags)
+    if (lane == 0) g_rescale[wave] = __ballot(st.over) != 0ull;
+    __syncthreads();
+    int redo = 0;
+#pragma unroll
+    for (int w = 0; w < kMlaWaves; ++w) redo |= g_rescale[w];
+    if (redo) {
+        st.m_ref = st.m_max;
+        __syncthreads();  // every wave has read the flags
+        pass(true);
     }
 
     // ---- epilogue: normalise, then write the final row or this split's partial
     if (wave < NHT && g == 0) {
         g_l[16 * wave + n] = st.l_run;
-        g_m[16 * wave + n] = st.m_run;
+        g_m[16 * wave + n] = st.m_ref;
     }
     __syncthreads();      // every wave is past its last PV: the tile ring is free
     // Stage the normalised bf16 rows [head][512] in LDS (16-byte chunks XOR-swizzled by

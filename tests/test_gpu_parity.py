@@ -171,6 +171,34 @@ def test_sparse_mla_decode_mfma(dsa, orc, name, B, T, Lmax, lens, k, H):
     check_attention(_np_out(out), lse.cpu().numpy(), ro, rl, "bf16")
 
 
+def test_sparse_mla_decode_logit_spread(dsa, orc):
+    """Logits far above the rest of a split: in row 0 one key selected late in a split
+    scores about 100 (log2 units) above everything before it for head 5 (the split is
+    then recomputed from its true maximum); in row 1 such a key comes first, so every
+    later probability of head 9 underflows relative to it.  The boost sits in the rope
+    columns, so the outputs keep the magnitude of ordinary value rows."""
+    _say("[sparse_mla_decode bf16] logit spread")
+    rng = np.random.default_rng(11)
+    B, T, H, Lmax, k = 2, 1, 128, 3000, 2048
+    lens = np.array([3000, 3000], np.int32)
+    qf = rng.standard_normal((B, T, H, 576), dtype=np.float32)
+    latf = rng.standard_normal((B, Lmax, 576), dtype=np.float32)
+    idx = _random_idx(rng, B, T, k, lens, invisible=False)
+    qf = (S.to_bf16_bits(qf).astype(np.uint32) << 16).view(np.float32)   # bf16 values
+    latf[0, idx[0, 0, 200], 512:] = 16.0 * qf[0, 0, 5, 512:]      # exact in bf16
+    latf[1, idx[1, 0, 3], 512:] = 16.0 * qf[1, 0, 9, 512:]
+    q = S.to_bf16_bits(qf)
+    lat = S.to_bf16_bits(latf)
+    sm = 192 ** -0.5
+    tq = torch.from_numpy(q.view(np.int16)).view(torch.bfloat16).cuda()
+    tl = torch.from_numpy(lat.view(np.int16)).view(torch.bfloat16).cuda()
+    out, lse = dsa.sparse_mla_decode(tq, tl, torch.from_numpy(idx).cuda(),
+                                     torch.from_numpy(lens).cuda(), 512, sm)
+    torch.cuda.synchronize()
+    ro, rl = orc.sparse_mla_decode(q, lat, idx, lens, 512, sm)
+    check_attention(_np_out(out), lse.cpu().numpy(), ro, rl, "bf16")
+
+
 def test_sparse_mla_decode_generic_f32(dsa, orc):
     _say("[sparse_mla_decode f32 generic]")
     rng = np.random.default_rng(7)
