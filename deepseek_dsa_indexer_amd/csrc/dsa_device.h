@@ -27,6 +27,11 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
 // far inside the bf16 rounding the results get.
 __device__ __forceinline__ float recip(float x) { return __builtin_amdgcn_rcpf(x); }
 
+// 2^x for softmax numerators: the transcendental unit's v_exp_f32 (about 1 ulp), with no
+// range reduction for subnormal results -- those flush to zero, which a numerator never
+// needs, since each softmax row also holds a numerator of at least 1.  2^-inf = 0.
+__device__ __forceinline__ float exp2_num(float x) { return __builtin_amdgcn_exp2f(x); }
+
 // Order-preserving map of a float onto an unsigned key: larger float -> larger key.
 __device__ __forceinline__ uint32_t float_key(float f) {
     uint32_t u = __float_as_uint(f);

@@ -311,10 +311,12 @@ __device__ __forceinline__ void mla_qk_softmax(MlaState<NHT>& st, const uint8_t*
         st.m_max = fmaxf(st.m_max, mx);
         st.over = st.over || mx > st.m_ref + kRefSpan;
     }
+    // while no usable slot has been seen every logit is -inf: any finite reference gives 0
+    const float mref = st.m_ref == -INFINITY ? 0.f : st.m_ref;
     float psum = 0.f;
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-        const float p = (sv[j] == -INFINITY) ? 0.f : exp2f(sv[j] - st.m_ref);
+        const float p = exp2_num(sv[j] - mref);
         psum += p;
         pk[j] = static_cast<short>(f32_to_bf16(p));
     }

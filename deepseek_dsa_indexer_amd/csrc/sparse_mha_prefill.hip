@@ -11,19 +11,27 @@
 // and s <= t).  Masked-dense work is about 2.3x the selected pairs at T = 8192, k = 2048.
 //
 // Mapping.  One workgroup (8 waves, two per SIMD) owns one head and 256 query rows; wave
-// w owns rows 32w..32w+31 as two 16-row query tiles, so every K and V operand read from
-// LDS feeds two matrix-core products.  Per key block of 64 positions:
+// w owns rows 32w..32w+31, one 32-row tile of the 32x32x16 matrix-core form (on gfx950 it
+// issues in about the time of the 16x16x32 form while doing twice the work).  Per key
+// block of 64 positions:
 //   load  K [64 x 192] and V [64 x 128] bf16 rows and the block's selection-mask words
 //         of the 256 rows into LDS with direct global->LDS loads, in a three-stage
 //         ring (two blocks in flight while one is computed), 16-byte chunks
 //         XOR-swizzled per row;
-//   QK    S^T = K . Q^T (keys as MFMA rows, each query tile's 16 queries as 6 B
-//         operands in registers), so lane (g, n) holds query row n of the tile and keys
-//         16 kt + 4 g + i;
+//   QK    S^T = K . Q^T per 32-key group (keys as MFMA rows, the wave's 32 queries as 12
+//         B operands in registers), so lane l holds query row l % 32 and keys
+//         32 kg + 8 (r / 4) + 4 (l / 32) + r % 4;
 //   mask  selection bits of the row and the causal bound;
-//   softmax online per row, entirely in the wave; the probabilities stay in registers
-//         in the A-operand layout of the PV product;
-//   PV    O [32 x 128] += P . V, V operands by LDS transpose reads.
+//   softmax per row over its 32 + 32 keys in lanes l and l ^ 32, relative to a fixed
+//         reference (below); the numerators stay in registers as the PV A operands:
+//         K-slot e of lane half hf in K-step ks of key group kg is key
+//         32 kg + 8 (2 ks + e / 4) + 4 hf + e % 4, exactly element 8 ks + e of the lane;
+//   PV    O [32 x 128] += P . V in four 32-column groups, V operands by LDS transpose
+//         reads.
+// No running-maximum rescale: each row's numerators are exp2(logit - m_ref), m_ref the
+// maximum of its first key block with a usable key, which is exact in floating point
+// while nothing overflows; a logit more than 2^64 above it (log2 units) marks the
+// workgroup, which then recomputes its rows with their true maxima as references.
 // Heaviest query blocks go first and all query blocks of a head share an XCD, so the
 // head's K and V blocks are fetched into one L2.
 #include "dsa_device.h"
@@ -35,8 +43,7 @@ namespace {
 
 constexpr int kMhaThreads = 512;
 constexpr int kMhaWaves = 8;
-constexpr int kQT = 2;                  // 16-row query tiles per wave
-constexpr int kQB = 16 * kQT * kMhaWaves;   // query rows per workgroup (256)
+constexpr int kQB = 32 * kMhaWaves;     // query rows per workgroup (256)
 constexpr int kKB = 64;                 // keys per block
 constexpr int kDqk = 192;
 constexpr int kDvM = 128;
@@ -57,7 +64,7 @@ static_assert((kKLoads + kVLoads) % kMhaWaves == 0, "block loads split evenly ov
 static_assert(kMaskBytes == kMhaWaves * kWave * 4, "one mask dword per lane");
 constexpr float kLog2eM = 1.4426950408889634f;
 constexpr float kLn2M = 0.6931471805599453f;
-constexpr float kLazy = 8.0f;
+constexpr float kRefSpan = 64.0f;                   // log2 units above the reference
 
 // Stage s: K block [64 x 384 B], V block [64 x 256 B], mask words [256 rows][2].
 __shared__ __attribute__((aligned(16))) uint8_t m_stage[kStages * kStageBytes];
@@ -118,113 +125,106 @@ __device__ __forceinline__ void load_block(const uint8_t* kbase, const uint8_t* 
 __device__ __forceinline__ void lds_sync() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
 struct MhaState {
-    v8bf qreg[kQT][kDqk / 32];  // 6 K-steps per query tile
-    v4f o[kQT][kDvM / 16];      // 8 column tiles per query tile
-    float m_run[kQT], l_run[kQT];
+    v8bf qreg[kDqk / 16];       // 12 K-steps of 16 dims: row l % 32, dims 16 ks + 8 (l / 32)
+    v16f o[kDvM / 32];          // four 32-column groups
+    float m_ref, m_max, l_run;  // of row l % 32 (log2 units)
+    bool over;
 };
 
-__device__ __forceinline__ void mha_block(MhaState& st, const uint8_t* stage, const int (&t_row)[kQT],
-                                          int s0, float scale_log2, int wave, int lane) {
+__device__ __forceinline__ void mha_block(MhaState& st, const uint8_t* stage, int t_row, int s0,
+                                          float scale_log2, int wave, int lane, bool fixed) {
     const uint8_t* kb = stage;
     const uint8_t* vb = stage + kKBytes;
     const uint32_t* mk = reinterpret_cast<const uint32_t*>(stage + kKBytes + kVBytes);
     int lo = lane;
     asm volatile("" : "+v"(lo));
-    const int g = lo >> 4;
-    const int n = lo & 15;
-    uint32_t mw[kQT][2];
-#pragma unroll
-    for (int qt = 0; qt < kQT; ++qt) {
-        const uint2 m2 = *reinterpret_cast<const uint2*>(mk + 2 * (32 * wave + 16 * qt + n));
-        mw[qt][0] = m2.x;
-        mw[qt][1] = m2.y;
-    }
+    const int hf = lo >> 5;
+    const int r32 = lo & 31;
+    const uint2 mw = *reinterpret_cast<const uint2*>(mk + 2 * (32 * wave + r32));
 
-    // ---- S^T = K . Q^T: 4 key tiles x 6 K-steps, each K operand used by both query tiles
-    v4f sacc[kQT][4];
+    // ---- S^T = K . Q^T for the two 32-key groups: independent accumulation chains
+    v16f sacc[2];
 #pragma unroll
-    for (int qt = 0; qt < kQT; ++qt)
+    for (int kg = 0; kg < 2; ++kg)
 #pragma unroll
-        for (int kt = 0; kt < 4; ++kt) sacc[qt][kt] = v4f{0.f, 0.f, 0.f, 0.f};
+        for (int r = 0; r < 16; ++r) sacc[kg][r] = 0.f;
 #pragma unroll
-    for (int ds = 0; ds < kDqk / 32; ++ds) {
+    for (int ks = 0; ks < kDqk / 16; ++ks) {
 #pragma unroll
-        for (int kt = 0; kt < 4; ++kt) {
-            const int key = 16 * kt + n;
-            const v8bf a = *reinterpret_cast<const v8bf*>(kb + key * kKRow + swz8(key, ds * 4 + g) * 16);
-#pragma unroll
-            for (int qt = 0; qt < kQT; ++qt) sacc[qt][kt] = mfma_bf16_16x16x32(a, st.qreg[qt][ds], sacc[qt][kt]);
+        for (int kg = 0; kg < 2; ++kg) {
+            const int key = 32 * kg + r32;
+            const v8bf a = *reinterpret_cast<const v8bf*>(kb + key * kKRow + swz8(key, 2 * ks + hf) * 16);
+            sacc[kg] = mfma_bf16_32x32x16(a, st.qreg[ks], sacc[kg]);
         }
-        __builtin_amdgcn_sched_barrier(0);
     }
-    // ---- mask + online softmax per query tile; keys s0 + 16 kt + 4 g + i
-    v8s pk[kQT][2];
+    // ---- mask + softmax numerators; keys s0 + 32 kg + 8 (r / 4) + 4 hf + r % 4.  The
+    // selection word of each key group is cut to the causal bound once, then shifted so
+    // that the lane's keys sit at the fixed bits 8 (r / 4) + r % 4.
+    float mx = -INFINITY;
 #pragma unroll
-    for (int qt = 0; qt < kQT; ++qt) {
-        float sv[16];
-        float mx = -INFINITY;
+    for (int kg = 0; kg < 2; ++kg) {
+        const int lim = t_row - s0 - 32 * kg;                    // last visible key of the group
+        const uint32_t vis = lim >= 31 ? 0xffffffffu : (lim < 0 ? 0u : (2u << lim) - 1u);
+        const uint32_t word = ((kg ? mw.y : mw.x) & vis) >> (4 * hf);
 #pragma unroll
-        for (int kt = 0; kt < 4; ++kt)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int kk = 16 * kt + 4 * g + i;              // 0..63
-                const uint32_t word = kk < 32 ? mw[qt][0] : mw[qt][1];
-                const bool sel = (word >> (kk & 31)) & 1u;
-                const bool vis = s0 + kk <= t_row[qt];
-                const float v = (sel && vis) ? sacc[qt][kt][i] * scale_log2 : -INFINITY;
-                sv[4 * kt + i] = v;
-                mx = fmaxf(mx, v);
-            }
-        mx = max_xor32(max_xor16(mx));
-        float alpha = 1.f;
-        if (mx > st.m_run[qt] + kLazy) {
-            // nothing accumulated yet (O = 0, l = 0): no rescale needed
-            alpha = (st.m_run[qt] == -INFINITY) ? 1.f : exp2f(st.m_run[qt] - mx);
-            st.m_run[qt] = mx;
+        for (int r = 0; r < 16; ++r) {
+            const bool ok = (word >> (8 * (r >> 2) + (r & 3))) & 1u;
+            const float v = ok ? sacc[kg][r] * scale_log2 : -INFINITY;
+            sacc[kg][r] = v;
+            mx = fmaxf(mx, v);
         }
-        float psum = 0.f;
+    }
+    mx = max_xor32(mx);
+    if (!fixed) {
+        if (st.m_ref == -INFINITY) st.m_ref = mx;       // first block with a usable key
+        st.m_max = fmaxf(st.m_max, mx);
+        st.over = st.over || mx > st.m_ref + kRefSpan;
+    }
+    // while no usable key has been seen every logit is -inf: any finite reference gives 0
+    const float mref = st.m_ref == -INFINITY ? 0.f : st.m_ref;
+    v8s pk[2][2];
+    float psum = 0.f;
 #pragma unroll
-        for (int j = 0; j < 16; ++j) {
-            const float p = (sv[j] == -INFINITY) ? 0.f : exp2f(sv[j] - st.m_run[qt]);
+    for (int kg = 0; kg < 2; ++kg)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const float p = exp2_num(sacc[kg][r] - mref);
             psum += p;
-            pk[qt][j >> 3][j & 7] = static_cast<short>(f32_to_bf16(p));
+            pk[kg][r >> 3][r & 7] = static_cast<short>(f32_to_bf16(p));
         }
-        psum = sum_xor32(sum_xor16(psum));
-        st.l_run[qt] = st.l_run[qt] * alpha + psum;
-        // alpha is per query row n: the O rows of this lane are rows 4 g + i, held by
-        // lanes n' = 4 g + i; fetch their alphas
-        if (__ballot(alpha != 1.f)) {
-            float a4[4];
+    st.l_run += sum_xor32(psum);
+
+    // ---- O += P . V.  V operand of (kg, ks), lane l: column 32 dg + l % 32, keys
+    // 32 kg + 16 ks + 8 e4 + 4 hf + 0..3 (e4 = 0, 1), two transpose reads: lane m of a
+    // 16-lane group supplies row key0 + m / 4, columns d0 + 4 (m % 4) .. + 3.
+    const int ch = (lo >> 4) & 1;
+    const int m = lo & 15;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) a4[i] = __shfl(alpha, 4 * g + i, kWave);
+    for (int dg = 0; dg < kDvM / 32; ++dg) {
+        const int chunk = 4 * dg + 2 * ch + ((m & 3) >> 1);
 #pragma unroll
-            for (int dt = 0; dt < kDvM / 16; ++dt)
+        for (int kg = 0; kg < 2; ++kg)
 #pragma unroll
-                for (int i = 0; i < 4; ++i) st.o[qt][dt][i] *= a4[i];
-        }
-    }
-    // ---- O += P . V: K-step 0 covers keys of tiles 0, 1 (slots j = 4 kt + i), K-step 1
-    // tiles 2, 3.  V operand of K-step ks: rows 32 ks + 16 kk + 4 g + r (kk = 0, 1).
+            for (int ks = 0; ks < 2; ++ks) {
+                v4bf_m half[2];
 #pragma unroll
-    for (int dt = 0; dt < kDvM / 16; ++dt) {
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
-            v4bf_m half[2];
-#pragma unroll
-            for (int kk = 0; kk < 2; ++kk) {
-                const int key = 32 * ks + 16 * kk + 4 * g + (n >> 2);
-                const int chunk = 2 * dt + ((n & 3) >> 1);
-                const int off = key * kVRow + swz8(key, chunk) * 16 + (n & 1) * 8;
-                half[kk] = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((__attribute__((address_space(3))) v4bf_m*)(vb + off));
+                for (int e4 = 0; e4 < 2; ++e4) {
+                    const int key = 32 * kg + 16 * ks + 8 * e4 + 4 * hf + (m >> 2);
+                    const int off = key * kVRow + swz8(key, chunk) * 16 + (m & 1) * 8;
+                    half[e4] = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+                        (__attribute__((address_space(3))) v4bf_m*)(vb + off));
+                }
+                const v8bf vop = v8bf{half[0][0], half[0][1], half[0][2], half[0][3],
+                                      half[1][0], half[1][1], half[1][2], half[1][3]};
+                st.o[dg] = mfma_bf16_32x32x16(__builtin_bit_cast(v8bf, pk[kg][ks]), vop, st.o[dg]);
             }
-            const v8bf vop = v8bf{half[0][0], half[0][1], half[0][2], half[0][3],
-                                  half[1][0], half[1][1], half[1][2], half[1][3]};
-#pragma unroll
-            for (int qt = 0; qt < kQT; ++qt)
-                st.o[qt][dt] = mfma_bf16_16x16x32(__builtin_bit_cast(v8bf, pk[qt][ks]), vop, st.o[qt][dt]);
-        }
     }
 }
+
+// per-wave row statistics for the epilogue and the recompute flags
+__shared__ float m_rowl[kMhaWaves][32];
+__shared__ float m_rowm[kMhaWaves][32];
+__shared__ int32_t m_redo[kMhaWaves];
 
 __global__ __launch_bounds__(kMhaThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void mha_prefill_mfma_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
@@ -234,8 +234,6 @@ void mha_prefill_mfma_kernel(const uint16_t* __restrict__ q, const uint16_t* __r
 {
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
-    const int g = lane >> 4;
-    const int n = lane & 15;
     const int qblocks = (T + kQB - 1) / kQB;
     // Block j * (B H) + bh: heaviest query blocks (most key blocks under the causal
     // bound) first, and all query blocks of a head on one XCD (workgroups go round robin
@@ -248,19 +246,16 @@ void mha_prefill_mfma_kernel(const uint16_t* __restrict__ q, const uint16_t* __r
     const int t0 = qb * kQB;
     const int words = (T + 31) / 32;
 
-    int t_row[kQT];                         // query row of this lane in each tile
+    const int t_row = min(t0 + 32 * wave + (lane & 31), T - 1);   // query row of this lane
     MhaState st;
+    {
+        const uint16_t* qrow = q + ((static_cast<size_t>(b) * T + t_row) * H + h) * kDqk + 8 * (lane >> 5);
 #pragma unroll
-    for (int qt = 0; qt < kQT; ++qt) {
-        t_row[qt] = min(t0 + 32 * wave + 16 * qt + n, T - 1);
-        const uint16_t* qrow = q + ((static_cast<size_t>(b) * T + t_row[qt]) * H + h) * kDqk + 8 * g;
-#pragma unroll
-        for (int ds = 0; ds < kDqk / 32; ++ds) st.qreg[qt][ds] = *reinterpret_cast<const v8bf*>(qrow + 32 * ds);
-#pragma unroll
-        for (int dt = 0; dt < kDvM / 16; ++dt) st.o[qt][dt] = v4f{0.f, 0.f, 0.f, 0.f};
-        st.m_run[qt] = -INFINITY;
-        st.l_run[qt] = 0.f;
+        for (int ks = 0; ks < kDqk / 16; ++ks) st.qreg[ks] = *reinterpret_cast<const v8bf*>(qrow + 16 * ks);
     }
+    st.m_ref = -INFINITY;
+    st.m_max = -INFINITY;
+    st.over = false;
 
     const uint8_t* kbase = reinterpret_cast<const uint8_t*>(k) + static_cast<size_t>(b) * T * H * kKRow;
     const uint8_t* vbase = reinterpret_cast<const uint8_t*>(v) + static_cast<size_t>(b) * T * H * kVRow;
@@ -274,37 +269,61 @@ void mha_prefill_mfma_kernel(const uint16_t* __restrict__ q, const uint16_t* __r
     // compiler's wait for them (it cannot see the direct-to-LDS loads) is the only
     // full drain, at the first block.
     auto stage = [&](int j) { return m_stage + (j % kStages) * kStageBytes; };
-    load_block(kbase, vbase, mask_b, words, t0, T, H, h, 0, stage(0), wave, lane);
-    if (nblocks > 1) load_block(kbase, vbase, mask_b, words, t0, T, H, h, kKB, stage(1), wave, lane);
-    for (int j = 0; j < nblocks; ++j) {
-        if (j + 1 < nblocks) asm volatile("s_waitcnt vmcnt(%0)" :: "n"(kDmaPerBlock) : "memory");
-        else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-        lds_sync();
-        if (j + 2 < nblocks)
-            load_block(kbase, vbase, mask_b, words, t0, T, H, h, (j + 2) * kKB, stage(j + 2), wave, lane);
-        mha_block(st, stage(j), t_row, j * kKB, scale_log2, wave, lane);
+    auto sweep = [&](bool fixed) {
+#pragma unroll
+        for (int dg = 0; dg < kDvM / 32; ++dg)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) st.o[dg][r] = 0.f;
+        st.l_run = 0.f;
+        load_block(kbase, vbase, mask_b, words, t0, T, H, h, 0, stage(0), wave, lane);
+        if (nblocks > 1) load_block(kbase, vbase, mask_b, words, t0, T, H, h, kKB, stage(1), wave, lane);
+        for (int j = 0; j < nblocks; ++j) {
+            if (j + 1 < nblocks) asm volatile("s_waitcnt vmcnt(%0)" :: "n"(kDmaPerBlock) : "memory");
+            else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+            lds_sync();
+            if (j + 2 < nblocks)
+                load_block(kbase, vbase, mask_b, words, t0, T, H, h, (j + 2) * kKB, stage(j + 2), wave, lane);
+            mha_block(st, stage(j), t_row, j * kKB, scale_log2, wave, lane, fixed);
+        }
+    };
+    sweep(false);
+    // a row of the workgroup past its reference span: recompute the workgroup's rows
+    // from their true maxima (a uniform decision: every wave reads the same flags)
+    if (lane == 0) m_redo[wave] = __ballot(st.over) != 0ull;
+    __syncthreads();
+    int redo = 0;
+#pragma unroll
+    for (int w = 0; w < kMhaWaves; ++w) redo |= m_redo[w];
+    if (redo) {
+        st.m_ref = st.m_max;
+        __syncthreads();      // every wave has read the flags and left the ring
+        sweep(true);
     }
 
-    // ---- epilogue: rows 4 g + i of each query tile; l and m of row r sit in lane r
+    // ---- epilogue: element r of lane l in column group dg is row 8 (r / 4) + 4 (l / 32)
+    // + r % 4 of the wave's 32, column 32 dg + l % 32; the rows' sums come from the lanes
+    // that own them through this wave's own LDS slots (no other wave reads them)
+    if (lane < 32) {
+        m_rowl[wave][lane] = st.l_run;
+        m_rowm[wave][lane] = st.m_ref;
+    }
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
 #pragma unroll
-    for (int qt = 0; qt < kQT; ++qt) {
-        float inv4[4], lse4[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const float l = __shfl(st.l_run[qt], 4 * g + i, kWave);
-            const float m = __shfl(st.m_run[qt], 4 * g + i, kWave);
-            inv4[i] = l > 0.f ? recip(l) : 0.f;
-            lse4[i] = l > 0.f ? (m + log2f(l)) * kLn2M : -INFINITY;
-        }
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int t = t0 + 32 * wave + 16 * qt + 4 * g + i;
-            if (t >= T) continue;
+    for (int r = 0; r < 16; ++r) {
+        const int rr = 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+        const int t = t0 + 32 * wave + rr;
+        const float l = m_rowl[wave][rr];
+        const float inv = l > 0.f ? recip(l) : 0.f;
+        if (t < T) {
             uint16_t* orow = out + ((static_cast<size_t>(b) * T + t) * H + h) * kDvM;
 #pragma unroll
-            for (int dt = 0; dt < kDvM / 16; ++dt) orow[16 * dt + n] = f32_to_bf16(st.o[qt][dt][i] * inv4[i]);
-            if (lse && n == 0) lse[(static_cast<size_t>(b) * T + t) * H + h] = lse4[i];
+            for (int dg = 0; dg < kDvM / 32; ++dg) orow[32 * dg + (lane & 31)] = f32_to_bf16(st.o[dg][r] * inv);
         }
+    }
+    if (lse && lane < 32) {
+        const int t = t0 + 32 * wave + lane;
+        const float l = st.l_run;
+        if (t < T) lse[(static_cast<size_t>(b) * T + t) * H + h] = l > 0.f ? (st.m_ref + log2f(l)) * kLn2M : -INFINITY;
     }
 }
 
