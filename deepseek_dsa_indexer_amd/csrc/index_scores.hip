@@ -16,17 +16,18 @@
 // bits (error up to 1.6e-4 of sum |q_d k_d|), which shows up as 1e-3-level relative
 // errors on scores whose head terms cancel.
 //
-// Mapping.  One wave owns QR query rows and streams 64-key chunks of the key cache.
-// The 64 heads of each query row stay in registers as A operands (4 head tiles x 4
-// K-steps of 32).  A chunk is four 16-key B tiles read with 16-byte loads: lane l takes
-// the bytes [16 g, 16 g + 16) and [64 + 16 g, 64 + 16 g + 16) of key (l % 16), g = l / 16,
-// so each load instruction reads whole 64-byte halves of 16 key rows; K-steps 0 and 1
-// use the first piece, 2 and 3 the second (q uses the same byte -> K-slot assignment, so
-// the four K-steps cover each of the 128 dims once).  Each MFMA leaves lane l with 4
-// heads x 1 key; ReLU and the head weights are applied in registers and three
-// cross-lane exchanges finish the head sum, so lane l ends with the score of key
-// (chunk + l): one coalesced 256-byte store per row and chunk.  Heads beyond H_I and
-// columns beyond d_I are zero (weight 0), which covers the small test shapes.
+// Mapping.  One wave owns QR query rows and streams 64-key chunks of the key cache, on
+// the 32x32x16 matrix-core form (on gfx950 it issues in about the time of the 16x16x32
+// form while doing twice the work): S = Q . K^T per (32-head group, 32-key group).  The
+// 64 heads of each query row stay in registers as A operands (2 head groups x 8 K-steps
+// of 16).  Lane l takes the 64 contiguous bytes [64 hf, 64 hf + 64) of key l % 32 of
+// each key group, hf = l / 32, so K-step ks uses dims 64 hf + 8 ks .. + 7 (the queries
+// use the same dim -> K-slot assignment, so the 8 K-steps cover each of the 128 dims
+// once).  Each product leaves lane l with key l % 32 and heads 8 (r / 4) + 4 hf + r % 4;
+// ReLU and the head weights are applied in registers, one exchange with lane l ^ 32
+// finishes the head sum, and lane l ends with the score of key (chunk + l): one
+// coalesced 256-byte store per row and chunk.  Heads beyond H_I and columns beyond d_I
+// are zero (weight 0), which covers the small test shapes.
 //
 // Blocks.  A block covers QR query rows and 256 * chunks consecutive keys.  With one
 // query row per sequence (decode), only the key blocks that hold visible positions are
@@ -50,19 +51,6 @@ constexpr int kMaxSeqPerThread = 16; // numbered decode launches: up to 4096 seq
 
 typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
 
-// Two 16-byte pieces at p0 and p1, each zeroed when its flag is false.  The loads are
-// issued unconditionally (callers pass clamped, in-bounds addresses): a load inside a
-// divergent branch makes the compiler drain every outstanding load at the branch join.
-__device__ __forceinline__ v8i load2x16(const uint8_t* p0, bool ok0, const uint8_t* p1, bool ok1) {
-    const uint4 a = *reinterpret_cast<const uint4*>(p0);
-    const uint4 b = *reinterpret_cast<const uint4*>(p1);
-    const int m0 = ok0 ? -1 : 0;
-    const int m1 = ok1 ? -1 : 0;
-    return v8i{static_cast<int>(a.x) & m0, static_cast<int>(a.y) & m0, static_cast<int>(a.z) & m0,
-               static_cast<int>(a.w) & m0, static_cast<int>(b.x) & m1, static_cast<int>(b.y) & m1,
-               static_cast<int>(b.z) & m1, static_cast<int>(b.w) & m1};
-}
-
 // 8 FP8 bytes (two dwords) -> 8 bf16, exactly.
 __device__ __forceinline__ v8bf fp8x8_to_bf16(int d0, int d1) {
     const v2bf a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(d0, 1.0f, false);
@@ -72,21 +60,63 @@ __device__ __forceinline__ v8bf fp8x8_to_bf16(int d0, int d1) {
     return v8bf{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
 }
 
-// Lane (g, n) holds s[c] = partial score (heads of group g) of key 16c + n.  Returns,
-// in every lane, the full head sum for key 16g + n, i.e. for chunk offset == lane.
-__device__ __forceinline__ float head_sum_transpose(const float s[4], int g) {
-    const bool lo = g < 2;
-    float send0 = lo ? s[2] : s[0];
-    float send1 = lo ? s[3] : s[1];
-    const int lane = g << 4;                    // bits 4 and 5 of the lane index
-    float r0 = from_xor32(send0, lane);
-    float r1 = from_xor32(send1, lane);
-    float a0 = (lo ? s[0] : s[2]) + r0;     // tile 0 (g < 2) or tile 2
-    float a1 = (lo ? s[1] : s[3]) + r1;     // tile 1 (g < 2) or tile 3
-    const bool odd = g & 1;
-    float send = odd ? a0 : a1;
-    float r = from_xor16(send, lane);
-    return (odd ? a1 : a0) + r;
+// Query operands of one row from its [64 heads][128 bytes] LDS copy: lane l, head group
+// hg takes head 32 hg + l % 32, dims 64 hf + 8 ks .. + 7; heads past H and bytes past D
+// are zero.  Weights: element r of head group hg belongs to head 32 hg + 8 (r / 4) +
+// 4 hf + r % 4.
+template <int D>
+__device__ __forceinline__ void load_queries(const uint8_t* sq, const float* swf, int H, int lane,
+                                             v8bf (&qa)[2][8], float (&wf)[2][16]) {
+    const int hf = lane >> 5;
+#pragma unroll
+    for (int hg = 0; hg < 2; ++hg) {
+        const int h = 32 * hg + (lane & 31);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int byte = 64 * hf + 16 * j;
+            const uint4 v = *reinterpret_cast<const uint4*>(sq + h * 128 + byte);
+            const int mk = (h < H && byte < D) ? -1 : 0;
+            qa[hg][2 * j] = fp8x8_to_bf16(static_cast<int>(v.x) & mk, static_cast<int>(v.y) & mk);
+            qa[hg][2 * j + 1] = fp8x8_to_bf16(static_cast<int>(v.z) & mk, static_cast<int>(v.w) & mk);
+        }
+#pragma unroll
+        for (int b4 = 0; b4 < 4; ++b4) {
+            const float4 w4 = *reinterpret_cast<const float4*>(swf + 32 * hg + 8 * b4 + 4 * hf);
+            wf[hg][4 * b4 + 0] = w4.x; wf[hg][4 * b4 + 1] = w4.y;
+            wf[hg][4 * b4 + 2] = w4.z; wf[hg][4 * b4 + 3] = w4.w;
+        }
+    }
+}
+
+// Head sum of one 64-key chunk for one query row: kr[kg][j] is lane l's 16-byte piece j
+// of key 32 kg + l % 32 (bytes 64 hf + 16 j .. + 15).  Returns, in lane l, the score of
+// key (chunk + l) before its key scale.
+__device__ __forceinline__ float chunk_scores(const v8bf (&qa)[2][8], const float (&wf)[2][16],
+                                              const uint4 (&kr)[2][4], int lane) {
+    float tot[2];
+#pragma unroll
+    for (int kg = 0; kg < 2; ++kg) {
+        v16f d[2];
+#pragma unroll
+        for (int hg = 0; hg < 2; ++hg)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) d[hg][r] = 0.f;
+#pragma unroll
+        for (int ks = 0; ks < 8; ++ks) {
+            const uint4 pc = kr[kg][ks >> 1];
+            const v8bf kb = (ks & 1) ? fp8x8_to_bf16(static_cast<int>(pc.z), static_cast<int>(pc.w))
+                                     : fp8x8_to_bf16(static_cast<int>(pc.x), static_cast<int>(pc.y));
+#pragma unroll
+            for (int hg = 0; hg < 2; ++hg) d[hg] = mfma_bf16_32x32x16(qa[hg][ks], kb, d[hg]);
+        }
+        float acc = 0.f;
+#pragma unroll
+        for (int hg = 0; hg < 2; ++hg)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc += wf[hg][r] * fmaxf(d[hg][r], 0.f);
+        tot[kg] = sum_xor32(acc);
+    }
+    return (lane & 32) ? tot[1] : tot[0];
 }
 
 template <int D, int QR>
@@ -102,8 +132,6 @@ void index_scores_kernel(const uint8_t* __restrict__ q, const float* __restrict_
     const int keys_per_block = kThreads / kWave * kChunk * chunks;
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = threadIdx.x / kWave;
-    const int g = lane >> 4;
-    const int n = lane & 15;
 
     const int row_groups = (T + QR - 1) / QR;
     int b, t0, yblk;
@@ -143,18 +171,21 @@ void index_scores_kernel(const uint8_t* __restrict__ q, const float* __restrict_
     const float* ks_ptr = k_scale + static_cast<size_t>(b) * Lmax;
     // chunk c of this wave starts at key_blk + (4 c + wave) * 64
     auto chunk_key = [&](int c) { return key_blk + (c * (kThreads / kWave) + wave) * kChunk; };
-    auto load_chunk = [&](int c, v8i (&dst)[4], float& ks) {
+    auto load_chunk = [&](int c, uint4 (&dst)[2][4], float& ks) {
         const int kb = chunk_key(c);
         const bool live = c < chunks && kb <= pos_hi;
 #pragma unroll
-        for (int tile = 0; tile < 4; ++tile) {
-            const int key = kb + 16 * tile + n;
+        for (int kg = 0; kg < 2; ++kg) {
+            const int key = kb + 32 * kg + (lane & 31);
             const bool ok = live && key < Lmax;
-            const int kc = min(key, Lmax - 1);
-            const uint8_t* krow = kb_ptr + static_cast<size_t>(kc) * D;
-            const int b0 = 16 * g, b1 = 64 + 16 * g;     // pieces past d_I read 0 (masked)
-            dst[tile] = load2x16(krow + (b0 < D ? b0 : 0), ok && b0 < D,
-                                 krow + (b1 < D ? b1 : 0), ok && b1 < D);
+            const uint8_t* krow = kb_ptr + static_cast<size_t>(min(key, Lmax - 1)) * D;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int byte = 64 * (lane >> 5) + 16 * j;      // pieces past d_I read 0
+                const uint4 v = *reinterpret_cast<const uint4*>(krow + (byte < D ? byte : 0));
+                const uint32_t mk = (ok && byte < D) ? 0xffffffffu : 0u;
+                dst[kg][j] = uint4{v.x & mk, v.y & mk, v.z & mk, v.w & mk};
+            }
         }
         // positions at or beyond Lmax are never stored, so the clamped scale needs no mask
         ks = ks_ptr[min(kb + lane, Lmax - 1)];
@@ -188,7 +219,7 @@ void index_scores_kernel(const uint8_t* __restrict__ q, const float* __restrict_
         wv = w[qrow * H + hc];
         qsv = q_scale[qrow * H + hc];
     }
-    v8i cur[4], nxt[4];
+    uint4 cur[2][4], nxt[2][4];
     float ks_cur, ks_nxt;
     load_chunk(0, cur, ks_cur);
     load_chunk(1, nxt, ks_nxt);
@@ -202,22 +233,10 @@ void index_scores_kernel(const uint8_t* __restrict__ q, const float* __restrict_
     }
     if (wr < QR) s_wf[wr][wh] = (wr < nrows && wh < H) ? wv * qsv * sm_scale : 0.f;
     __syncthreads();
-    v8bf qa[QR][4][4];
-    float wf[QR][4][4];
+    v8bf qa[QR][2][8];
+    float wf[QR][2][16];
 #pragma unroll
-    for (int r = 0; r < QR; ++r)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const uint4 lo = *reinterpret_cast<const uint4*>(&s_q[r][(16 * j + n) * 128 + 16 * g]);
-            const uint4 hi = *reinterpret_cast<const uint4*>(&s_q[r][(16 * j + n) * 128 + 64 + 16 * g]);
-            const int raw[8] = {static_cast<int>(lo.x), static_cast<int>(lo.y), static_cast<int>(lo.z),
-                                static_cast<int>(lo.w), static_cast<int>(hi.x), static_cast<int>(hi.y),
-                                static_cast<int>(hi.z), static_cast<int>(hi.w)};
-#pragma unroll
-            for (int kk = 0; kk < 4; ++kk) qa[r][j][kk] = fp8x8_to_bf16(raw[2 * kk], raw[2 * kk + 1]);
-            const float4 wv = *reinterpret_cast<const float4*>(&s_wf[r][16 * j + 4 * g]);
-            wf[r][j][0] = wv.x; wf[r][j][1] = wv.y; wf[r][j][2] = wv.z; wf[r][j][3] = wv.w;
-        }
+    for (int r = 0; r < QR; ++r) load_queries<128>(s_q[r], s_wf[r], kMaxHeads, lane, qa[r], wf[r]);
 
     for (int c = 0; c < chunks; ++c) {
         const int kb = chunk_key(c);
@@ -226,39 +245,17 @@ void index_scores_kernel(const uint8_t* __restrict__ q, const float* __restrict_
             if (fill_invisible && key < Lmax)
                 for (int r = 0; r < nrows; ++r) out[static_cast<size_t>(r) * Lmax + key] = -INFINITY;
         } else {
-            float s[QR][4];
-#pragma unroll
-            for (int tile = 0; tile < 4; ++tile) {
-                v8bf kbf[4];
-#pragma unroll
-                for (int kk = 0; kk < 4; ++kk) kbf[kk] = fp8x8_to_bf16(cur[tile][2 * kk], cur[tile][2 * kk + 1]);
-#pragma unroll
-                for (int r = 0; r < QR; ++r) {
-                    // the four head tiles are independent accumulation chains: interleave them
-                    v4f d[4];
-#pragma unroll
-                    for (int j = 0; j < 4; ++j) d[j] = v4f{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                    for (int kk = 0; kk < 4; ++kk)
-#pragma unroll
-                        for (int j = 0; j < 4; ++j) d[j] = mfma_bf16_16x16x32(qa[r][j][kk], kbf[kk], d[j]);
-                    float acc = 0.f;
-#pragma unroll
-                    for (int j = 0; j < 4; ++j)
-#pragma unroll
-                        for (int i = 0; i < 4; ++i) acc += wf[r][j][i] * fmaxf(d[j][i], 0.f);
-                    s[r][tile] = acc;
-                }
-            }
 #pragma unroll
             for (int r = 0; r < QR; ++r) {
-                const float total = head_sum_transpose(s[r], g);
+                const float total = chunk_scores(qa[r], wf[r], cur, lane);
                 if (r < nrows && key < Lmax)
                     out[static_cast<size_t>(r) * Lmax + key] = (key <= pos0 + r) ? total * ks_cur : -INFINITY;
             }
         }
 #pragma unroll
-        for (int tile = 0; tile < 4; ++tile) cur[tile] = nxt[tile];
+        for (int kg = 0; kg < 2; ++kg)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) cur[kg][j] = nxt[kg][j];
         ks_cur = ks_nxt;
         if (c + 2 < chunks) load_chunk(c + 2, nxt, ks_nxt);
     }
@@ -270,10 +267,10 @@ void index_scores_kernel(const uint8_t* __restrict__ q, const float* __restrict_
 // loads (global_load_lds) into a ring of two 8.25 KB slots of its own, so two chunks per
 // wave stay in flight without holding registers (the register-staged form above keeps
 // one chunk per wave, 64 KB per CU, in flight).  The query row and the head weights
-// arrive the same way.  Slot layout, in load order: 1 KB piece 2 t + p holds, at lane l,
-// bytes [64 p + 16 (l / 16), + 16) of key 16 t + l % 16 of the chunk -- exactly what lane l
-// reads as its MFMA operand piece, so each operand read is one contiguous 16-byte lane
-// read -- and the 256 bytes after the keys hold their 64 scales.  The loads are inline
+// arrive the same way.  Slot layout, in load order: 1 KB piece 4 kg + j holds, at lane l,
+// bytes [64 hf + 16 j, + 16) of key 32 kg + l % 32 of the chunk -- exactly what lane l
+// reads as its operand piece, so each read is one contiguous 16-byte lane read -- and
+// the 256 bytes after the keys hold their 64 scales.  The loads are inline
 // assembly, invisible to the compiler's wait counting: every wait is an explicit vmcnt
 // over this wave's own loads (they complete in issue order), and no other wave touches a
 // wave's slots, so the ring needs no barrier.
@@ -317,8 +314,6 @@ void index_scores_decode_kernel(const uint8_t* __restrict__ q, const float* __re
     const int keys_per_block = kWaves * kChunk * chunks;
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
-    const int g = lane >> 4;
-    const int n = lane & 15;
 
     // numbered blocks: sequences of unequal length still spread evenly over the XCDs, and
     // no block past a sequence's end is run unless its positions are to be filled
@@ -350,12 +345,12 @@ void index_scores_decode_kernel(const uint8_t* __restrict__ q, const float* __re
         uint8_t* slot = s_ring[wave][c & 1];
         const int kb = first + c * kWaves * kChunk;
 #pragma unroll
-        for (int t = 0; t < 4; ++t) {
-            const uint8_t* krow = kb_ptr + static_cast<size_t>(min(kb + 16 * t + n, Lmax - 1)) * D;
+        for (int kg = 0; kg < 2; ++kg) {
+            const uint8_t* krow = kb_ptr + static_cast<size_t>(min(kb + 32 * kg + (lane & 31), Lmax - 1)) * D;
 #pragma unroll
-            for (int p = 0; p < 2; ++p) {
-                const int byte = 64 * p + 16 * g;       // pieces past d_I are masked on read
-                dma16(lds_addr(slot + (2 * t + p) * 1024), krow + (byte < D ? byte : 0));
+            for (int j = 0; j < 4; ++j) {
+                const int byte = 64 * (lane >> 5) + 16 * j;     // pieces past d_I are masked on read
+                dma16(lds_addr(slot + (4 * kg + j) * 1024), krow + (byte < D ? byte : 0));
             }
         }
         dma4(lds_addr(slot + kChunk * 128), ks_ptr + min(kb + lane, Lmax - 1));
@@ -380,70 +375,37 @@ void index_scores_decode_kernel(const uint8_t* __restrict__ q, const float* __re
     else vm_wait<0>();
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 
-    v8bf qa[4][4];
-    float wf[4][4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        const int h = 16 * j + n;
-        const uint4 lo = *reinterpret_cast<const uint4*>(&s_q[h * 128 + 16 * g]);
-        const uint4 hi = *reinterpret_cast<const uint4*>(&s_q[h * 128 + 64 + 16 * g]);
-        const int m0 = (h < H && 16 * g < D) ? -1 : 0;
-        const int m1 = (h < H && 64 + 16 * g < D) ? -1 : 0;
-        const int raw[8] = {static_cast<int>(lo.x) & m0, static_cast<int>(lo.y) & m0,
-                            static_cast<int>(lo.z) & m0, static_cast<int>(lo.w) & m0,
-                            static_cast<int>(hi.x) & m1, static_cast<int>(hi.y) & m1,
-                            static_cast<int>(hi.z) & m1, static_cast<int>(hi.w) & m1};
-#pragma unroll
-        for (int kk = 0; kk < 4; ++kk) qa[j][kk] = fp8x8_to_bf16(raw[2 * kk], raw[2 * kk + 1]);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int hh = 16 * j + 4 * g + i;
-            wf[j][i] = hh < H ? s_w[hh] * s_qs[hh] * sm_scale : 0.f;
-        }
+    // folded weights into s_w (0 past H heads), then the operands
+    if (threadIdx.x < kMaxHeads) {
+        const int hh = threadIdx.x;
+        const float wv = hh < H ? s_w[hh] * s_qs[hh] * sm_scale : 0.f;
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        s_w[hh] = wv;
     }
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    v8bf qa[2][8];
+    float wf[2][16];
+    load_queries<D>(s_q, s_w, H, lane, qa, wf);
 
     for (int c = 0; c < n_live; ++c) {
         // chunk c is in when at most chunk c + 1's loads remain
         if (c + 1 < n_live) vm_wait<kChunkLoads>();
         else vm_wait<0>();
         const uint8_t* slot = s_ring[wave][c & 1];
-        v8i cur[4];
+        uint4 cur[2][4];
 #pragma unroll
-        for (int t = 0; t < 4; ++t) {
-            const uint4 lo = *reinterpret_cast<const uint4*>(slot + (2 * t) * 1024 + 16 * lane);
-            const uint4 hi = *reinterpret_cast<const uint4*>(slot + (2 * t + 1) * 1024 + 16 * lane);
-            const int m0 = 16 * g < D ? -1 : 0;
-            const int m1 = 64 + 16 * g < D ? -1 : 0;
-            cur[t] = v8i{static_cast<int>(lo.x) & m0, static_cast<int>(lo.y) & m0,
-                         static_cast<int>(lo.z) & m0, static_cast<int>(lo.w) & m0,
-                         static_cast<int>(hi.x) & m1, static_cast<int>(hi.y) & m1,
-                         static_cast<int>(hi.z) & m1, static_cast<int>(hi.w) & m1};
-        }
+        for (int kg = 0; kg < 2; ++kg)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const uint4 v = *reinterpret_cast<const uint4*>(slot + (4 * kg + j) * 1024 + 16 * lane);
+                const uint32_t mk = 64 * (lane >> 5) + 16 * j < D ? 0xffffffffu : 0u;
+                cur[kg][j] = uint4{v.x & mk, v.y & mk, v.z & mk, v.w & mk};
+            }
         const float ks = *reinterpret_cast<const float*>(slot + kChunk * 128 + 4 * lane);
         asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // slot read before it is refilled
         if (c + 2 < n_live) issue(c + 2);
 
-        float sc[4];
-#pragma unroll
-        for (int t = 0; t < 4; ++t) {
-            v8bf kbf[4];
-#pragma unroll
-            for (int kk = 0; kk < 4; ++kk) kbf[kk] = fp8x8_to_bf16(cur[t][2 * kk], cur[t][2 * kk + 1]);
-            v4f d[4];
-#pragma unroll
-            for (int j = 0; j < 4; ++j) d[j] = v4f{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int kk = 0; kk < 4; ++kk)
-#pragma unroll
-                for (int j = 0; j < 4; ++j) d[j] = mfma_bf16_16x16x32(qa[j][kk], kbf[kk], d[j]);
-            float acc = 0.f;
-#pragma unroll
-            for (int j = 0; j < 4; ++j)
-#pragma unroll
-                for (int i = 0; i < 4; ++i) acc += wf[j][i] * fmaxf(d[j][i], 0.f);
-            sc[t] = acc;
-        }
-        const float total = head_sum_transpose(sc, g);
+        const float total = chunk_scores(qa, wf, cur, lane);
         const int key = first + c * kWaves * kChunk + lane;
         if (key < Lmax) out[key] = key <= pos ? total * ks : -INFINITY;
     }
