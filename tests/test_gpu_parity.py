@@ -244,8 +244,12 @@ def test_sparse_mla_prefill(dsa, orc, dt):
 LAYER_CASES = [
     ("tiny", _small("tiny")),
     ("decode_small", _small("decode_v32", name="ds", B=3, Lmax=4100, seed=202)),
-    ("ragged_small_t3", _small("decode_ragged", name="rs", B=5, Lmax=6000,
+    ("ragged_small_t3", _small("decode_ragged", name="rs", B=5, T=3, Lmax=6000,
                                lens="ragged:1024:6000", seed=205)),
+    # two query rows per sequence beyond 16384 positions: two-stage top-k with several
+    # rows per sequence, indexer blocks of two rows
+    ("long_t2", _small("decode_long", name="lt2", B=2, T=2, Lmax=40000,
+                       lens="ragged:20000:40000", seed=206)),
 ]
 
 
