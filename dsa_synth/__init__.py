@@ -116,13 +116,41 @@ def to_bf16_bits(x: np.ndarray) -> np.ndarray:
     return t.view(torch.int16).numpy().view(np.uint16)
 
 
-def make_case(cfg: Config, seqs=None) -> dict:
+FP8_LATENT_ROW_BYTES = 656
+FP8_LATENT_DV, FP8_LATENT_DR, FP8_LATENT_BLOCK = 512, 64, 128
+
+
+def pack_latent_fp8(x: np.ndarray) -> np.ndarray:
+    """Store float32 latent rows ``x`` [..., 576] in the 656-byte FP8 form: the 512 latent
+    columns as e4m3fn codes (quantize_e4m3fn, one scale per 128 columns), then the four
+    fp32 scales, then the 64 rope columns as bf16."""
+    assert x.shape[-1] == FP8_LATENT_DV + FP8_LATENT_DR
+    lead = x.shape[:-1]
+    codes, scales = quantize_e4m3fn(x[..., :FP8_LATENT_DV], FP8_LATENT_BLOCK)
+    rope = to_bf16_bits(x[..., FP8_LATENT_DV:])
+    out = np.empty(lead + (FP8_LATENT_ROW_BYTES,), np.uint8)
+    out[..., :FP8_LATENT_DV] = codes
+    out[..., FP8_LATENT_DV:FP8_LATENT_DV + 16] = np.ascontiguousarray(
+        scales, dtype=np.float32).view(np.uint8).reshape(lead + (16,))
+    out[..., FP8_LATENT_DV + 16:] = np.ascontiguousarray(rope).view(np.uint8).reshape(lead + (128,))
+    return out
+
+
+def make_case(cfg: Config, seqs=None, latent_form: str = "bf16") -> dict:
     """All inputs of one layer step as host numpy arrays.
 
     ``seqs`` restricts the batch to the listed sequence ids (same values as in the
     full batch).  Attention tensors are float32 or bf16 bits (uint16) per
     ``cfg.attn_dtype``.  Keys: q_i, q_scale, w, k_i, k_scale, lens, and either
-    (q, latent) or (q, k, v)."""
+    (q, latent) or (q, k, v).  ``latent_form="fp8"`` (bf16 latent configurations with
+    576-wide rows only) stores the latent cache as 656-byte FP8 rows (pack_latent_fp8)
+    drawn from the same float32 values; poisoned rows then hold code 448 with scale
+    1e4 and rope 1e4."""
+    assert latent_form in ("bf16", "fp8")
+    fp8_lat = latent_form == "fp8"
+    if fp8_lat:
+        assert (cfg.form == "latent" and cfg.attn_dtype == "bf16" and cfg.Dv == FP8_LATENT_DV
+                and cfg.Dr == FP8_LATENT_DR), "FP8 latent rows need the 512 + 64 bf16 shape"
     all_lens = lengths(cfg)
     seqs = list(range(cfg.B)) if seqs is None else list(seqs)
     nb = len(seqs)
@@ -142,8 +170,12 @@ def make_case(cfg: Config, seqs=None) -> dict:
     conv = to_bf16_bits if bf16 else (lambda a: a.astype(np.float32))
     if cfg.form == "latent":
         q = np.empty((nb, T, cfg.H, cfg.Dq), adt)
-        latent = np.empty((nb, Lmax, cfg.Dq), adt)
-        latent[...] = conv(np.full((1,), POISON_VALUE, np.float32))[0]
+        if fp8_lat:
+            latent = np.empty((nb, Lmax, FP8_LATENT_ROW_BYTES), np.uint8)
+            latent[...] = _poison_fp8_row()
+        else:
+            latent = np.empty((nb, Lmax, cfg.Dq), adt)
+            latent[...] = conv(np.full((1,), POISON_VALUE, np.float32))[0]
     else:
         q = np.empty((nb, T, cfg.H, cfg.Dqk), adt)
         kk = np.empty((nb, T, cfg.H, cfg.Dqk), adt)
@@ -158,7 +190,8 @@ def make_case(cfg: Config, seqs=None) -> dict:
         w[j] = _rng(cfg, 2, b).standard_normal((T, H_I), dtype=np.float32) / np.float32(math.sqrt(H_I))
         if cfg.form == "latent":
             q[j] = conv(_rng(cfg, 3, b).standard_normal((T, cfg.H, cfg.Dq), dtype=np.float32))
-            latent[j, :L] = conv(_rng(cfg, 4, b).standard_normal((L, cfg.Dq), dtype=np.float32))
+            x = _rng(cfg, 4, b).standard_normal((L, cfg.Dq), dtype=np.float32)
+            latent[j, :L] = pack_latent_fp8(x) if fp8_lat else conv(x)
         else:
             q[j] = conv(_rng(cfg, 3, b).standard_normal((T, cfg.H, cfg.Dqk), dtype=np.float32))
             kk[j] = conv(_rng(cfg, 4, b).standard_normal((T, cfg.H, cfg.Dqk), dtype=np.float32))
@@ -170,6 +203,15 @@ def make_case(cfg: Config, seqs=None) -> dict:
     else:
         case.update(q=q, k=kk, v=v)
     return case
+
+
+def _poison_fp8_row() -> np.ndarray:
+    row = np.empty(FP8_LATENT_ROW_BYTES, np.uint8)
+    row[:FP8_LATENT_DV] = POISON_K_CODE
+    row[FP8_LATENT_DV:FP8_LATENT_DV + 16] = np.full(4, POISON_VALUE, np.float32).view(np.uint8)
+    row[FP8_LATENT_DV + 16:] = np.repeat(
+        to_bf16_bits(np.full((1,), POISON_VALUE, np.float32)), FP8_LATENT_DR).view(np.uint8)
+    return row
 
 
 def to_device(case: dict, device="cuda") -> dict:

@@ -18,7 +18,8 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "dsa_oracle.c")
 _LIB_PATH = os.path.join(_HERE, "liboracle.so")
 
-F32, BF16, F64 = 0, 1, 2
+F32, BF16, F64, FP8_LATENT = 0, 1, 2, 3
+FP8_LATENT_ROW_BYTES = 656      # 512 e4m3fn codes + 4 fp32 scales + 64 bf16 rope values
 _OK, _ERR_SHAPE, _ERR_INDEX = 0, 1, 2
 
 
@@ -53,6 +54,8 @@ def _load():
         lib.orc_e4m3fn_value.restype = D
         lib.orc_bf16_value.argtypes = [ctypes.c_uint16]
         lib.orc_bf16_value.restype = D
+        lib.orc_latent_fp8_value.argtypes = [P, I]
+        lib.orc_latent_fp8_value.restype = D
         lib.orc_index_scores.argtypes = [P, P, P, P, P, P, I, I, I, I, I, D, P]
         lib.orc_topk.argtypes = [P, P, I, I, I, I, P]
         lib.orc_sparse_mla_decode.argtypes = [P, P, P, P, I, I, I, I, I, I, I, I, D, P, P]
@@ -79,7 +82,10 @@ def _c(a, dtype):
 
 
 def _attn_array(x):
-    """Return (contiguous array, dtype code).  bf16 travels as raw uint16 words."""
+    """Return (contiguous array, dtype code).  bf16 travels as raw uint16 words; uint8
+    arrays whose last axis is 656 bytes are latent rows in the FP8 storage form."""
+    if x.dtype == np.uint8 and x.shape[-1] == FP8_LATENT_ROW_BYTES:
+        return np.ascontiguousarray(x), FP8_LATENT
     if x.dtype == np.float32:
         return np.ascontiguousarray(x), F32
     if x.dtype == np.uint16:
@@ -104,6 +110,26 @@ def e4m3fn_value(code: int) -> float:
 
 def bf16_value(bits: int) -> float:
     return _load().orc_bf16_value(bits)
+
+
+def latent_fp8_value(row, d: int) -> float:
+    """Decoded column d of one 656-byte FP8 latent row (uint8 array)."""
+    row = np.ascontiguousarray(row, dtype=np.uint8)
+    assert row.shape == (FP8_LATENT_ROW_BYTES,)
+    return _load().orc_latent_fp8_value(row.ctypes.data_as(ctypes.c_void_p), int(d))
+
+
+def latent_fp8_decode(rows) -> np.ndarray:
+    """Decode FP8 latent rows [..., 656] u8 to float64 [..., 576] column by column."""
+    rows = np.ascontiguousarray(rows, dtype=np.uint8)
+    flat = rows.reshape(-1, FP8_LATENT_ROW_BYTES)
+    out = np.empty((flat.shape[0], 576), np.float64)
+    lib = _load()
+    for i in range(flat.shape[0]):
+        p = flat[i].ctypes.data_as(ctypes.c_void_p)
+        for d in range(576):
+            out[i, d] = lib.orc_latent_fp8_value(p, d)
+    return out.reshape(*rows.shape[:-1], 576)
 
 
 def index_scores(q_fp8, q_scale, w, k_fp8, k_scale, lens, sm_scale_i):
@@ -142,7 +168,11 @@ def sparse_mla_decode(q, latent, idx, lens, Dv, sm_scale):
     lib = _load()
     q, dt = _attn_array(q)
     latent, dt2 = _attn_array(latent)
-    assert dt == dt2 and latent.shape[-1] == Dq
+    if dt2 == FP8_LATENT:
+        assert dt == BF16 and Dq == 576 and Dv == 512
+        dt = FP8_LATENT
+    else:
+        assert dt == dt2 and latent.shape[-1] == Dq
     idx, pi = _c(idx, np.int32)
     lens, pl = _c(lens, np.int32)
     out = np.empty((B, T, H, Dv), np.float64)
@@ -217,7 +247,11 @@ def layer_step_latent(q_fp8, q_scale, w, k_fp8, k_scale, lens, sm_scale_i, k, q,
             _c(k_fp8, np.uint8), _c(k_scale, np.float32), _c(lens, np.int32)]
     qa, dt = _attn_array(q)
     la, dt2 = _attn_array(latent)
-    assert dt == dt2
+    if dt2 == FP8_LATENT:
+        assert dt == BF16 and Dq == 576 and Dv == 512
+        dt = FP8_LATENT
+    else:
+        assert dt == dt2
     out = np.empty((B, T, H, Dv), np.float64)
     lse = np.empty((B, T, H), np.float64)
     idx = np.empty((B, T, k), np.int32)

@@ -79,6 +79,33 @@ static double load_elem(const void* p, int dtype, size_t i)
     }
 }
 
+/* FP8 storage form of one latent cache row ([DIAG]: the latent cache holds FP8 latents
+ * with bf16 rope parts, 656 bytes per token).  Reading taken for the byte order, which
+ * the diagram does not draw: the 512 e4m3fn codes of the latent part, then its four
+ * fp32 scales (one per 128 columns, the block size of the FP8 indexer keys, [IDX]),
+ * then the 64 rope values as bf16; 512 + 4*4 + 64*2 = 656.  Column d < 512 is
+ * code[d] * scale[d / 128]; column 512 + r is the bf16 rope value r. */
+double orc_latent_fp8_value(const uint8_t* row, int d)
+{
+    if (d < ORC_FP8_LATENT_DV) {
+        float scale;
+        memcpy(&scale, row + ORC_FP8_LATENT_DV + 4 * (d / ORC_FP8_LATENT_BLOCK), sizeof scale);
+        return orc_e4m3fn_value(row[d]) * (double)scale;
+    }
+    uint16_t bits;
+    memcpy(&bits, row + ORC_FP8_LATENT_DV + 4 * (ORC_FP8_LATENT_DV / ORC_FP8_LATENT_BLOCK) +
+                      2 * (d - ORC_FP8_LATENT_DV), sizeof bits);
+    return orc_bf16_value(bits);
+}
+
+/* Element d of latent row `row` (of Dq columns) in storage type `dtype`. */
+static double latent_elem(const void* latent, int dtype, size_t row, int Dq, int d)
+{
+    if (dtype == ORC_FP8_LATENT)
+        return orc_latent_fp8_value((const uint8_t*)latent + row * ORC_FP8_LATENT_ROW_BYTES, d);
+    return load_elem(latent, dtype, row * (size_t)Dq + d);
+}
+
 /* ------------------------------------------------------------------ O2: index scores */
 
 /* For every row (b,t) and cache position s:
@@ -180,13 +207,19 @@ int orc_topk(const float* scores, const int32_t* len, int B, int T, int Lmax, in
  * visible), each row serving as key (all Dv+Dr columns) and value (first Dv columns):
  *   l_j = sm_scale * sum_{d < Dv+Dr} q[b,t,h,d] * C[b,s_j,d]
  *   p   = softmax(l),  out[b,t,h,:] = sum_j p_j C[b,s_j,0:Dv],  lse = log sum_j e^{l_j}
- * A row with no usable index gets out = 0 and lse = -inf. */
+ * A row with no usable index gets out = 0 and lse = -inf.  With dtype ORC_FP8_LATENT
+ * the rows are in the FP8 storage form and C[b,s,d] is their decoded value
+ * (orc_latent_fp8_value), the queries bf16. */
 int orc_sparse_mla_decode(const void* q, const void* latent, const int32_t* idx,
                           const int32_t* len, int dtype, int B, int T, int H, int Dv, int Dr,
                           int Lmax, int k, double sm_scale, double* out, double* lse)
 {
     const int Dq = Dv + Dr;
+    /* FP8 latent rows pair with bf16 queries, at the storage form's fixed widths */
+    const int qdt = dtype == ORC_FP8_LATENT ? ORC_BF16 : dtype;
     int b;
+    if (dtype == ORC_FP8_LATENT && (Dv != ORC_FP8_LATENT_DV || Dr != ORC_FP8_LATENT_DR))
+        return ORC_ERR_SHAPE;
     for (b = 0; b < B; ++b)
         if (len[b] < T || len[b] > Lmax) return ORC_ERR_SHAPE;
     for (size_t i = 0; i < (size_t)B * T * k; ++i)
@@ -208,10 +241,10 @@ int orc_sparse_mla_decode(const void* q, const void* latent, const int32_t* idx,
                 double* o = out + (row * H + h) * (size_t)Dv;
                 double m = -INFINITY, sum = 0.0;
                 for (int j = 0; j < n; ++j) {
-                    const size_t coff = ((size_t)b * Lmax + keys[j]) * (size_t)Dq;
+                    const size_t crow = (size_t)b * Lmax + keys[j];
                     double dot = 0.0;
                     for (int d = 0; d < Dq; ++d)
-                        dot += load_elem(q, dtype, qoff + d) * load_elem(latent, dtype, coff + d);
+                        dot += load_elem(q, qdt, qoff + d) * latent_elem(latent, dtype, crow, Dq, d);
                     logit[j] = sm_scale * dot;
                     if (logit[j] > m) m = logit[j];
                 }
@@ -220,8 +253,8 @@ int orc_sparse_mla_decode(const void* q, const void* latent, const int32_t* idx,
                 for (int j = 0; j < n; ++j) sum += exp(logit[j] - m);
                 for (int j = 0; j < n; ++j) {
                     const double p = exp(logit[j] - m) / sum;
-                    const size_t coff = ((size_t)b * Lmax + keys[j]) * (size_t)Dq;
-                    for (int d = 0; d < Dv; ++d) o[d] += p * load_elem(latent, dtype, coff + d);
+                    const size_t crow = (size_t)b * Lmax + keys[j];
+                    for (int d = 0; d < Dv; ++d) o[d] += p * latent_elem(latent, dtype, crow, Dq, d);
                 }
                 if (lse) lse[row * H + h] = m + log(sum);
             }

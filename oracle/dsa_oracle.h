@@ -9,16 +9,22 @@
  *   latent form:  q [B,T,H,Dv+Dr], latent [B,Lmax,Dv+Dr], out [B,T,H,Dv] f64, lse [B,T,H] f64
  *   MHA form:     q, k [B,T,H,Dqk], v [B,T,H,Dv], out [B,T,H,Dv] f64, lse [B,T,H] f64
  * Attention inputs are read as ORC_F32, ORC_BF16 (raw 16-bit words) or ORC_F64.
+ * ORC_FP8_LATENT (latent form only): bf16 queries and 656-byte FP8 latent rows
+ *   [512 e4m3fn codes][4 fp32 scales, one per 128 columns][64 bf16 rope values],
+ *   latent [B,Lmax,656] u8, Dv = 512, Dr = 64.
  */
 #ifndef DSA_ORACLE_H
 #define DSA_ORACLE_H
 #include <stdint.h>
 
 enum { ORC_OK = 0, ORC_ERR_SHAPE = 1, ORC_ERR_INDEX = 2 };
-enum { ORC_F32 = 0, ORC_BF16 = 1, ORC_F64 = 2 };
+enum { ORC_F32 = 0, ORC_BF16 = 1, ORC_F64 = 2, ORC_FP8_LATENT = 3 };
+enum { ORC_FP8_LATENT_DV = 512, ORC_FP8_LATENT_DR = 64, ORC_FP8_LATENT_BLOCK = 128,
+       ORC_FP8_LATENT_ROW_BYTES = 656 };
 
 double orc_e4m3fn_value(uint8_t code);
 double orc_bf16_value(uint16_t bits);
+double orc_latent_fp8_value(const uint8_t* row, int d);
 
 int orc_index_scores(const uint8_t* q, const float* q_scale, const float* w,
                      const uint8_t* k, const float* k_scale, const int32_t* len,

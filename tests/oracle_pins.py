@@ -21,7 +21,11 @@ What pins what:
   * MHA prefill            -> the same library routine per head, and the pages'
                               dense "scores + index mask + causal mask" form;
   * layer step             -> with k >= len the result is dense attention whatever
-                              the indexer does; a planted dominant key is picked.
+                              the indexer does; a planted dominant key is picked;
+  * FP8 latent rows        -> torch's float8_e4m3fn and bfloat16 decoding at the
+                              656-byte layout (512 codes, 4 fp32 block scales, 64
+                              bf16 rope values), and attention over such rows ==
+                              SDPA over the torch-decoded rows.
 """
 from __future__ import annotations
 
@@ -382,6 +386,63 @@ def pin_layer_step_mha_dense_limit(o):
     vt = torch.from_numpy(v[0]).transpose(0, 1)
     ref = F.scaled_dot_product_attention(qt, kt, vt, is_causal=True, scale=0.3).transpose(0, 1)
     np.testing.assert_allclose(out[0], ref.numpy(), rtol=1e-10, atol=1e-12)
+
+
+# ----------------------------------------------------------------------------- FP8 latent rows
+
+def _fp8_latent_rows(rng, n):
+    """n random 656-byte rows: finite codes, fp32 scales over a wide range, finite bf16
+    rope values.  Returns (rows u8 [n,656], torch-decoded float64 [n,576])."""
+    codes = _rand_codes(rng, (n, 512))
+    scales = (2.0 ** rng.uniform(-12, 6, size=(n, 4))).astype(np.float32)
+    rope = torch.from_numpy(rng.standard_normal((n, 64)).astype(np.float32)).to(torch.bfloat16)
+    rows = np.concatenate([codes, scales.view(np.uint8).reshape(n, 16),
+                           rope.view(torch.int16).numpy().view(np.uint8).reshape(n, 128)], axis=1)
+    ref = np.concatenate([_fp8_values(codes) * np.repeat(scales.astype(np.float64), 128, axis=1),
+                          rope.double().numpy()], axis=1)
+    return rows, ref
+
+
+def pin_latent_fp8_decode_library(o):
+    """The 656-byte row (the diagram's per-token latent figure) decodes, column by column,
+    to torch's e4m3fn value times the scale of its 128-column block, then torch's bf16
+    rope values."""
+    assert 512 + 4 * 4 + 64 * 2 == 656 == o.FP8_LATENT_ROW_BYTES
+    rows, ref = _fp8_latent_rows(np.random.default_rng(71), 6)
+    got = o.latent_fp8_decode(rows)
+    np.testing.assert_array_equal(got, ref)
+
+
+def pin_latent_fp8_attention_library(o):
+    """Sparse latent attention over FP8 rows with bf16 queries == SDPA in float64 over the
+    torch-decoded rows (keys: all 576 columns, values: the first 512)."""
+    rng = np.random.default_rng(72)
+    B, T, H, Lmax, k = 2, 2, 3, 20, 6
+    lens = np.array([20, 13], np.int32)
+    rows, ref = _fp8_latent_rows(rng, B * Lmax)
+    rows, ref = rows.reshape(B, Lmax, 656), ref.reshape(B, Lmax, 576)
+    qf = torch.from_numpy(rng.standard_normal((B, T, H, 576)).astype(np.float32)).to(torch.bfloat16)
+    q_bits = qf.view(torch.int16).numpy().view(np.uint16)
+    sm = 192.0 ** -0.5
+    idx = np.full((B, T, k), -1, np.int32)
+    for b in range(B):
+        for t in range(T):
+            n = int(lens[b]) - T + t + 1
+            idx[b, t, :k - 1] = rng.choice(n, size=k - 1, replace=False)
+            idx[b, t, k - 1] = min(n, Lmax - 1) if n < Lmax else -1   # past pos: ignored
+    out, lse = o.sparse_mla_decode(q_bits, rows, idx, lens, 512, sm)
+    for b in range(B):
+        for t in range(T):
+            pos = int(lens[b]) - T + t
+            mask = torch.zeros(Lmax, dtype=torch.bool)
+            sel = idx[b, t][(idx[b, t] >= 0) & (idx[b, t] <= pos)]
+            mask[torch.from_numpy(sel.astype(np.int64))] = True
+            C = torch.from_numpy(ref[b])
+            qd = qf[b, t].double()
+            want = _sdpa_rows(qd, C, C[:, :512], mask, sm)
+            np.testing.assert_allclose(out[b, t], want.numpy(), rtol=1e-9, atol=1e-12)
+            logits = qd @ C[mask].T * sm
+            np.testing.assert_allclose(lse[b, t], torch.logsumexp(logits, -1).numpy(), rtol=1e-12)
 
 
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

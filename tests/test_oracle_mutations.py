@@ -34,8 +34,17 @@ MUTATIONS = [
      "const int n = len[b] - T + t;"),
     ("attention scale dropped", "logit[j] = sm_scale * dot;", "logit[j] = dot;"),
     ("latent key drops rope part", "for (int d = 0; d < Dq; ++d)\n", "for (int d = 0; d < Dv; ++d)\n"),
-    ("latent value offset", "o[d] += p * load_elem(latent, dtype, coff + d);",
-     "o[d] += p * load_elem(latent, dtype, coff + Dr + d);"),
+    ("latent value offset", "o[d] += p * latent_elem(latent, dtype, crow, Dq, d);",
+     "o[d] += p * latent_elem(latent, dtype, crow, Dq, Dr + d);"),
+    ("fp8 latent scale ignored", "return orc_e4m3fn_value(row[d]) * (double)scale;",
+     "return orc_e4m3fn_value(row[d]);"),
+    ("fp8 latent scale per 64 columns", "row + ORC_FP8_LATENT_DV + 4 * (d / ORC_FP8_LATENT_BLOCK)",
+     "row + ORC_FP8_LATENT_DV + 4 * ((d / 64) & 3)"),
+    ("fp8 latent rope read over the scales",
+     "4 * (ORC_FP8_LATENT_DV / ORC_FP8_LATENT_BLOCK) +\n                      2 * (d - ORC_FP8_LATENT_DV)",
+     "2 * (d - ORC_FP8_LATENT_DV)"),
+    ("fp8 latent queries not bf16", "const int qdt = dtype == ORC_FP8_LATENT ? ORC_BF16 : dtype;",
+     "const int qdt = dtype == ORC_FP8_LATENT ? ORC_F32 : dtype;"),
     ("latent ignores visibility", "if (sel[j] >= 0 && sel[j] <= pos) keys[n++] = sel[j];",
      "if (sel[j] >= 0) keys[n++] = sel[j];"),
     ("lse without max", "lse[row * H + h] = m + log(sum);", "lse[row * H + h] = log(sum);"),
@@ -52,7 +61,7 @@ MUTATIONS = [
 def _variant(orc, path):
     saved = orc._load()
     lib = ctypes.CDLL(path)
-    for fn in ("orc_e4m3fn_value", "orc_bf16_value", "orc_index_scores", "orc_topk",
+    for fn in ("orc_e4m3fn_value", "orc_bf16_value", "orc_latent_fp8_value", "orc_index_scores", "orc_topk",
                "orc_sparse_mla_decode", "orc_sparse_mha_prefill", "orc_sparse_mha_prefill_dense",
                "orc_sparse_mha_prefill_rows",
                "orc_layer_step_latent", "orc_layer_step_mha", "orc_max_threads"):

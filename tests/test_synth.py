@@ -64,3 +64,26 @@ def test_ragged_lengths_and_poison():
     sub = S.make_case(small, seqs=[2])
     np.testing.assert_array_equal(sub["k_i"][0], case["k_i"][2])
     np.testing.assert_array_equal(sub["latent"][0], case["latent"][2])
+
+
+def test_fp8_latent_rows():
+    """656-byte rows: codes and scales from the blockwise quantizer of the same float32
+    draws as the bf16 cache, bf16 rope bytes equal to the bf16 cache's, poison beyond len."""
+    import dataclasses
+    cfg = dataclasses.replace(S.CONFIGS["decode_ragged"], B=2, Lmax=96, lens="ragged:40:96")
+    a = S.make_case(cfg, latent_form="fp8")
+    b = S.make_case(cfg)
+    lat8, lat16 = a["latent"], b["latent"]
+    assert lat8.dtype == np.uint8 and lat8.shape == (2, 96, S.FP8_LATENT_ROW_BYTES)
+    np.testing.assert_array_equal(a["q"], b["q"])
+    for j, L in enumerate(a["lens"]):
+        L = int(L)
+        x = np.random.default_rng([cfg.seed, 4, j]).standard_normal((L, 576), dtype=np.float32)
+        codes, scales = S.quantize_e4m3fn(x[:, :512], 128)
+        np.testing.assert_array_equal(lat8[j, :L, :512], codes)
+        np.testing.assert_array_equal(lat8[j, :L, 512:528].view(np.float32), scales)
+        np.testing.assert_array_equal(lat8[j, :L, 528:].view(np.uint16), lat16[j, :L, 512:])
+        assert (lat8[j, L:, :512] == S.POISON_K_CODE).all()
+        assert (lat8[j, L:, 512:528].view(np.float32) == S.POISON_VALUE).all()
+    with pytest.raises(AssertionError):
+        S.make_case(S.CONFIGS["tiny"], latent_form="fp8")
