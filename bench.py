@@ -1,6 +1,6 @@
 """Benchmark of one DSA layer step on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config decode_v32]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config decode_v32] [--latent fp8]
 
 A step is one call of dsa_layer_step over the whole batch: index scores over every
 cached key of every sequence, top-k, sparse attention over the selected latent rows.
@@ -39,14 +39,14 @@ def _sha(path: str) -> str:
         return hashlib.sha256(f.read()).hexdigest()[:16]
 
 
-def algorithmic_costs(cfg, lens):
+def algorithmic_costs(cfg, lens, latent_form="bf16"):
     """Bytes and flops the method must move / execute per step, per phase.
 
     Indexer: every sequence's K-cache once, 132 B (128 FP8 + 4 B scale) per cached key,
     plus each row's q (H_I*d_I B), weights and q scales (8*H_I B); 2*H_I*d_I flops per
-    visible (row, key).  Latent attention: 1152 B (576 bf16) per selected latent row,
-    shared by all heads, 2*H*(576+512) flops per (head, selected row), plus the row's
-    q (H*576*2 B) and output (H*512*2 B).  MHA attention: the chunk's K and V once
+    visible (row, key).  Latent attention: 1152 B (576 bf16) per selected latent row, or
+    656 B in the FP8 row form, shared by all heads, 2*H*(576+512) flops per (head,
+    selected row), plus the row's q (H*576*2 B) and output (H*512*2 B).  MHA attention: the chunk's K and V once
     (H*(Dqk+Dv)*2 B per key), q and output, and 2*H*(Dqk+Dv) flops per (head,
     selected row)."""
     import dsa_synth as S
@@ -61,7 +61,8 @@ def algorithmic_costs(cfg, lens):
     idx_bytes = cached * (cfg.D_I + 4) + rows * (cfg.H_I * cfg.D_I + 8 * cfg.H_I)
     idx_flops = keys * 2 * cfg.H_I * cfg.D_I
     if cfg.form == "latent":
-        att_bytes = sel * cfg.Dq * 2 + rows * (cfg.H * cfg.Dq * 2 + cfg.H * cfg.Dv * 2)
+        row_bytes = S.FP8_LATENT_ROW_BYTES if latent_form == "fp8" else cfg.Dq * 2
+        att_bytes = sel * row_bytes + rows * (cfg.H * cfg.Dq * 2 + cfg.H * cfg.Dv * 2)
         att_flops = sel * 2 * cfg.H * (cfg.Dq + cfg.Dv)
     else:
         att_bytes = rows * cfg.H * (cfg.Dqk + cfg.Dv) * 2 + rows * cfg.H * (cfg.Dqk + cfg.Dv) * 2
@@ -90,7 +91,7 @@ def read_traffic(kernel: str, workload: str, source: str):
         return None
 
 
-def cpu_baseline(cfg, n_seqs: int, min_seconds: float = 10.0):
+def cpu_baseline(cfg, n_seqs: int, min_seconds: float = 10.0, latent_form: str = "bf16"):
     """The oracle, untuned, on a bounded sample of the same workload, scaled to a step.
 
     Decode: the whole layer step for the first ``n_seqs`` sequences.  Chunked prefill
@@ -104,7 +105,7 @@ def cpu_baseline(cfg, n_seqs: int, min_seconds: float = 10.0):
     orc.build(force=False)
     if cfg.form == "latent":
         seqs = list(range(min(n_seqs, cfg.B)))
-        c = S.make_case(cfg, seqs=seqs)
+        c = S.make_case(cfg, seqs=seqs, latent_form=latent_form)
 
         def once():
             orc.layer_step_latent(c["q_i"], c["q_scale"], c["w"], c["k_i"], c["k_scale"],
@@ -156,6 +157,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--config", default="decode_v32")
     ap.add_argument("--sets", type=int, default=4, help="independent input sets cycled")
+    ap.add_argument("--latent", choices=["bf16", "fp8"], default="bf16",
+                    help="latent cache rows: bf16 (1152 B) or the FP8 storage form (656 B: "
+                         "512 e4m3fn codes, four fp32 block scales, 64 bf16 rope values)")
     ap.add_argument("--graph", action="store_true", help="replay each step from a HIP graph")
     ap.add_argument("--cpu-seqs", type=int, default=32,
                     help="sequences (decode) or rows / 4 (prefill) in the CPU-oracle sample")
@@ -191,13 +195,18 @@ def main():
         sys.exit(1)
     D.load()
     cfg = S.CONFIGS[args.config]
+    fp8_lat = args.latent == "fp8"
+    if fp8_lat and cfg.form != "latent":
+        print("--latent fp8 applies to the latent (decode) workloads only", file=sys.stderr)
+        sys.exit(2)
     lens = S.lengths(cfg)
-    costs = algorithmic_costs(cfg, lens)
+    costs = algorithmic_costs(cfg, lens, args.latent)
 
     steps = []
     t_gen = time.perf_counter()
     for i in range(args.sets):
-        c = S.make_case(dataclasses.replace(cfg, seed=cfg.seed + 1000 * i) if i else cfg)
+        c = S.make_case(dataclasses.replace(cfg, seed=cfg.seed + 1000 * i) if i else cfg,
+                        latent_form=args.latent)
         d = S.to_device(c, "cuda")
         del c
         if cfg.form == "latent":
@@ -271,7 +280,7 @@ def main():
         kernel, tkey, src = "mla_decode_mfma_kernel", "sparse_mla_decode", ATTN_SOURCE
     else:
         kernel, tkey, src = "mha_prefill_mfma_kernel", "sparse_mha_prefill", PREFILL_SOURCE
-    traffic = read_traffic(tkey, cfg.name, src)
+    traffic = read_traffic(tkey, cfg.name + ("-fp8" if fp8_lat else ""), src)
     # the attention kernel's bound: whichever of its bytes or its flops takes longer at peak
     mfma_bound = costs["attention_flops"] / (BF16_PEAK_TFLOPS * 1e12) > \
         costs["attention_bytes"] / (HBM_PEAK_GBS * 1e9)
@@ -290,7 +299,9 @@ def main():
     t_roof = sum(max(costs[f"{p}_bytes"] / (HBM_PEAK_GBS * 1e9),
                      costs[f"{p}_flops"] / (BF16_PEAK_TFLOPS * 1e12)) for p in ("index", "attention"))
     if cfg.form == "latent":
-        attn_desc = f"MLA {cfg.H} heads over bf16 latent {cfg.Dv}+{cfg.Dr}"
+        attn_desc = (f"MLA {cfg.H} heads over FP8 latent rows (656 B: {cfg.Dv} e4m3fn + 4 "
+                     f"block scales + {cfg.Dr} bf16 rope)" if fp8_lat else
+                     f"MLA {cfg.H} heads over bf16 latent {cfg.Dv}+{cfg.Dr}")
     else:
         attn_desc = f"MHA {cfg.H} heads, bf16 qk {cfg.Dqk} / v {cfg.Dv}"
     result = {
@@ -310,6 +321,7 @@ def main():
                                f"indexer {cfg.H_I}x{cfg.D_I} FP8, top-{cfg.k}, {attn_desc}",
                    "B": cfg.B, "context": cfg.Lmax, "T": cfg.T, "topk": cfg.k, "H_I": cfg.H_I,
                    "d_I": cfg.D_I, "H": cfg.H, "q_width": cfg.Dq, "input_sets": args.sets,
+                   "latent_cache": args.latent if cfg.form == "latent" else None,
                    "hip_graph": bool(args.graph)},
         "step_ms_p10_p50_p90": [round(pct(0.1), 5), round(pct(0.5), 5), round(pct(0.9), 5)],
         "token_layer_steps_per_s": round(cfg.B * cfg.T * value, 1),
@@ -322,7 +334,8 @@ def main():
                          "mfma_frac": round(idx_tfs / BF16_PEAK_TFLOPS, 4),
                          "keys_per_s": round(costs["keys"] / (idx_ms * 1e-3), 1)},
         "roofline": roofline,
-        "cpu_baseline": None if args.no_cpu else cpu_baseline(cfg, args.cpu_seqs, args.cpu_seconds),
+        "cpu_baseline": None if args.no_cpu else cpu_baseline(cfg, args.cpu_seqs, args.cpu_seconds,
+                                                              args.latent),
     }
     print(json.dumps(result))
 

@@ -6,6 +6,8 @@ The computation lives in ``libdsa_amd.so`` (HIP kernels behind the C ABI of
     index_scores(q_fp8, q_scale, w, k_fp8, k_scale, lens, sm_scale_i)  -> scores
     topk(scores, lens, k)                                                -> idx
     sparse_mla_decode(q, latent, idx, lens, Dv, sm_scale)                -> (out, lse)
+        (latent: q's dtype, or uint8 [B,Lmax,656] rows in the FP8 storage form with
+         bf16 q: 512 e4m3fn codes, four fp32 block scales, 64 bf16 rope values)
     sparse_mla_prefill(q, k, v, idx, sm_scale)                           -> (out, lse)
     LayerStep(...)()                                                     -> (out, lse)
 

@@ -15,7 +15,8 @@ import torch
 _LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libdsa_amd.so")
 
 DSA_OK = 0
-DSA_F32, DSA_BF16 = 0, 1
+DSA_F32, DSA_BF16, DSA_FP8_LATENT = 0, 1, 2
+FP8_LATENT_ROW_BYTES = 656     # 512 e4m3fn codes, four fp32 block scales, 64 bf16 rope values
 DSA_ATTN_LATENT, DSA_ATTN_MHA = 0, 1
 STATUS_NAMES = {0: "DSA_OK", 1: "DSA_ERR_NULL", 2: "DSA_ERR_SHAPE", 3: "DSA_ERR_DTYPE",
                 4: "DSA_ERR_ALIGN", 5: "DSA_ERR_WORKSPACE", 6: "DSA_ERR_HIP"}
@@ -131,6 +132,18 @@ def _attn_dtype(t) -> int:
     raise TypeError(f"attention tensors must be bf16 or f32, got {t.dtype}")
 
 
+def _latent_dtype(q, latent) -> int:
+    """dtype code of a latent-form call: uint8 rows of 656 bytes are the FP8 storage form
+    (bf16 queries), otherwise latent has q's dtype."""
+    if latent.dtype == torch.uint8 and latent.shape[-1] == FP8_LATENT_ROW_BYTES:
+        if q.dtype != torch.bfloat16:
+            raise TypeError("FP8 latent rows take bf16 queries")
+        _need(latent, torch.uint8, "latent")
+        return DSA_FP8_LATENT
+    _need(latent, q.dtype, "latent")
+    return _attn_dtype(q)
+
+
 def _workspace(nbytes: int, device):
     if nbytes == 0:
         return None
@@ -171,9 +184,8 @@ def topk(scores, lens, k, idx=None):
 
 def sparse_mla_decode(q, latent, idx, lens, Dv, sm_scale, out=None, lse=None, want_lse=True):
     """Absorbed-form sparse attention; returns (out[B,T,H,Dv], lse[B,T,H] or None)."""
-    dt = _attn_dtype(q)
     _need(q, q.dtype, "q")
-    _need(latent, q.dtype, "latent")
+    dt = _latent_dtype(q, latent)
     _need(idx, torch.int32, "idx")
     _need(lens, torch.int32, "lens")
     B, T, H, Dq = q.shape
@@ -256,7 +268,7 @@ class LayerStep:
         a.H = H
         a.sm_scale = float(sm_scale)
         if latent is not None:
-            _need(latent, q.dtype, "latent")
+            a.dtype = dt = _latent_dtype(q, latent)
             if Dv is None:
                 raise ValueError("Dv is required for the latent form")
             a.form = DSA_ATTN_LATENT

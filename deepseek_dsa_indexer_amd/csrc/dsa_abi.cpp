@@ -72,13 +72,18 @@ dsa_status check_topk_args(const float* scores, const int32_t* len, int B, int T
 }
 
 constexpr size_t kGenericLdsLimit = 64 * 1024;
+static_assert(static_cast<int>(DSA_F32) == dsa::kLatF32 && static_cast<int>(DSA_BF16) == dsa::kLatBf16 &&
+                  static_cast<int>(DSA_FP8_LATENT) == dsa::kLatFp8,
+              "dsa_dtype values are the kernels' latent types");
 
 dsa_status check_latent_args(const void* q, const void* latent, const int32_t* idx,
                              const int32_t* len, int B, int T, int H, int Dv, int Dr, int Lmax,
                              int k, dsa_dtype dt, const void* out) {
     DSA_REQUIRE(q && latent && idx && len && out, DSA_ERR_NULL, "sparse_mla_decode: NULL pointer");
-    DSA_REQUIRE(dt == DSA_F32 || dt == DSA_BF16, DSA_ERR_DTYPE, "sparse_mla_decode: bad dtype %d",
-                static_cast<int>(dt));
+    DSA_REQUIRE(dt == DSA_F32 || dt == DSA_BF16 || dt == DSA_FP8_LATENT, DSA_ERR_DTYPE,
+                "sparse_mla_decode: bad dtype %d", static_cast<int>(dt));
+    DSA_REQUIRE(dt != DSA_FP8_LATENT || (Dv == dsa::kFp8Dv && Dr == dsa::kFp8Dr), DSA_ERR_DTYPE,
+                "sparse_mla_decode: FP8 latent rows need Dv=512, Dr=64 (got Dv=%d Dr=%d)", Dv, Dr);
     DSA_REQUIRE(B >= 1 && T >= 1 && Lmax >= 1 && T <= Lmax && H >= 1 && Dv >= 1 && Dr >= 0 &&
                     Dv + Dr <= 1024 && k >= 1,
                 DSA_ERR_SHAPE, "sparse_mla_decode: bad shape (B=%d T=%d H=%d Dv=%d Dr=%d Lmax=%d k=%d)",
@@ -87,7 +92,7 @@ dsa_status check_latent_args(const void* q, const void* latent, const int32_t* i
                 "sparse_mla_decode: B*T*H too large");
     DSA_REQUIRE(aligned16(q) && aligned16(latent) && aligned16(idx) && aligned16(len) && aligned16(out),
                 DSA_ERR_ALIGN, "sparse_mla_decode: pointers must be 16-byte aligned");
-    if (!dsa::mla_decode_mfma_supported(H, Dv, Dr, k, dt == DSA_BF16))
+    if (!dsa::mla_decode_mfma_supported(H, Dv, Dr, k, dt))
         DSA_REQUIRE(sizeof(float) * (static_cast<size_t>(Dv + Dr) + k) <= kGenericLdsLimit, DSA_ERR_SHAPE,
                     "sparse_mla_decode: k=%d too large for this shape", k);
     return DSA_OK;
@@ -96,9 +101,9 @@ dsa_status check_latent_args(const void* q, const void* latent, const int32_t* i
 dsa_status launch_latent(const void* q, const void* latent, const int32_t* idx, const int32_t* len,
                          int B, int T, int H, int Dv, int Dr, int Lmax, int k, float sm_scale,
                          dsa_dtype dt, void* out, float* lse, void* ws, hipStream_t stream) {
-    if (dsa::mla_decode_mfma_supported(H, Dv, Dr, k, dt == DSA_BF16))
+    if (dsa::mla_decode_mfma_supported(H, Dv, Dr, k, dt))
         return hip_status(dsa::launch_mla_decode_mfma(q, latent, idx, len, B, T, H, Lmax, k, sm_scale,
-                                                      out, lse, ws, stream),
+                                                      dt, out, lse, ws, stream),
                           "sparse_mla_decode");
     dsa::SparseAttnArgs a{};
     a.q = q;
@@ -112,14 +117,15 @@ dsa_status launch_latent(const void* q, const void* latent, const int32_t* idx, 
     a.row_stride_v = static_cast<size_t>(Dv + Dr);
     a.head_stride_v = 0;
     a.sm_scale = sm_scale;
-    a.bf16 = dt == DSA_BF16;
+    a.bf16 = dt != DSA_F32;
+    a.fp8_latent = dt == DSA_FP8_LATENT;
     a.out = out;
     a.lse = lse;
     return hip_status(dsa::launch_sparse_attn_generic(a, stream), "sparse_mla_decode");
 }
 
 size_t latent_ws(int B, int T, int H, int Dv, int Dr, int k, dsa_dtype dt) {
-    if (dsa::mla_decode_mfma_supported(H, Dv, Dr, k, dt == DSA_BF16))
+    if (dsa::mla_decode_mfma_supported(H, Dv, Dr, k, dt))
         return dsa::mla_decode_workspace_bytes(B, T, H, Dv, k);
     return 0;
 }

@@ -23,6 +23,23 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
     return __builtin_bit_cast(uint16_t, static_cast<__bf16>(f));
 }
 
+typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
+
+// 8 FP8 (OCP e4m3fn) bytes, two dwords, -> 8 bf16, byte order kept.  Exact: every
+// e4m3fn value is a bf16 value (the scale operand of the conversion is 1).
+__device__ __forceinline__ v8bf fp8x8_to_bf16(int d0, int d1) {
+    const v2bf a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(d0, 1.0f, false);
+    const v2bf b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(d0, 1.0f, true);
+    const v2bf c = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(d1, 1.0f, false);
+    const v2bf d = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(d1, 1.0f, true);
+    return v8bf{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
+}
+
+// One FP8 (OCP e4m3fn) byte -> float, exactly.
+__device__ __forceinline__ float fp8_to_f32(uint8_t c) {
+    return static_cast<float>(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(static_cast<int>(c), 1.0f, false)[0]);
+}
+
 // 1 / x for a normalising sum (x > 0): the hardware reciprocal (about 1 ulp), which is
 // far inside the bf16 rounding the results get.
 __device__ __forceinline__ float recip(float x) { return __builtin_amdgcn_rcpf(x); }

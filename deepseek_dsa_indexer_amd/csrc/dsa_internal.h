@@ -38,6 +38,14 @@ struct TopkArgs {
 size_t topk_workspace_bytes(int B, int T, int Lmax, int k);
 hipError_t launch_topk(const TopkArgs& a, void* ws, hipStream_t stream);
 
+// Element types of the latent form (the values of the ABI's dsa_dtype).  kLatFp8: bf16
+// queries and outputs, cache rows of 656 bytes -- 512 e4m3fn codes, four fp32 scales (one
+// per 128 columns), 64 bf16 rope values.
+enum LatentType { kLatF32 = 0, kLatBf16 = 1, kLatFp8 = 2 };
+constexpr int kFp8RowBytes = 656;
+constexpr int kFp8Dv = 512;
+constexpr int kFp8Dr = 64;
+
 // Sparse attention over gathered rows.  Keys of row (b,t) for head h are read at
 //   kbase + (b * kv_rows + s) * row_stride + h * head_stride   (Dk values)
 // and values at
@@ -52,18 +60,20 @@ struct SparseAttnArgs {
     size_t row_stride, head_stride, row_stride_v, head_stride_v;   // in elements
     float sm_scale;
     int bf16;               // element type: 1 bf16, 0 f32
+    int fp8_latent;         // keys and values are 656-byte FP8 latent rows at kbase
+                            // (row = b * kv_rows + s; strides unused); q, out bf16
     void* out;              // [B,T,H,Dv]
     float* lse;             // [B,T,H] or NULL
 };
 hipError_t launch_sparse_attn_generic(const SparseAttnArgs& a, hipStream_t stream);
 
-// Matrix-core path of the absorbed latent form (bf16, Dv = 512, Dr = 64, H % 16 == 0,
-// H <= 128).
-bool mla_decode_mfma_supported(int H, int Dv, int Dr, int k, int bf16);
+// Matrix-core path of the absorbed latent form (bf16 or FP8 rows, Dv = 512, Dr = 64,
+// H = 64 or 128).  `type` is a LatentType.
+bool mla_decode_mfma_supported(int H, int Dv, int Dr, int k, int type);
 size_t mla_decode_workspace_bytes(int B, int T, int H, int Dv, int k);
 hipError_t launch_mla_decode_mfma(const void* q, const void* latent, const int32_t* idx,
                                   const int32_t* len, int B, int T, int H, int Lmax, int k,
-                                  float sm_scale, void* out, float* lse, void* ws,
+                                  float sm_scale, int type, void* out, float* lse, void* ws,
                                   hipStream_t stream);
 
 // Matrix-core path of the MHA prefill form (bf16, Dqk = 192, Dv = 128).

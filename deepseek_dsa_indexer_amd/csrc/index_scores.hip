@@ -49,17 +49,6 @@ constexpr int kChunk = 64;          // keys per wave iteration (4 MFMA column ti
 constexpr int kMaxHeads = 64;       // indexer heads (4 MFMA row tiles)
 constexpr int kMaxSeqPerThread = 16; // numbered decode launches: up to 4096 sequences
 
-typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
-
-// 8 FP8 bytes (two dwords) -> 8 bf16, exactly.
-__device__ __forceinline__ v8bf fp8x8_to_bf16(int d0, int d1) {
-    const v2bf a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(d0, 1.0f, false);
-    const v2bf b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(d0, 1.0f, true);
-    const v2bf c = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(d1, 1.0f, false);
-    const v2bf d = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(d1, 1.0f, true);
-    return v8bf{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
-}
-
 // Query operands of one row from its [64 heads][128 bytes] LDS copy: lane l, head group
 // hg takes head 32 hg + l % 32, dims 64 hf + 8 ks .. + 7; heads past H and bytes past D
 // are zero.  Weights: element r of head group hg belongs to head 32 hg + 8 (r / 4) +

@@ -23,6 +23,12 @@ __device__ __forceinline__ float ld_elem(const void* p, size_t i, int bf16) {
     return bf16 ? bf16_to_f32(static_cast<const uint16_t*>(p)[i]) : static_cast<const float*>(p)[i];
 }
 
+// Column d of a 656-byte FP8 latent row: code * block scale for d < 512, else bf16 rope.
+__device__ __forceinline__ float fp8_latent_elem(const uint8_t* row, int d) {
+    if (d < kFp8Dv) return fp8_to_f32(row[d]) * reinterpret_cast<const float*>(row + kFp8Dv)[d >> 7];
+    return bf16_to_f32(reinterpret_cast<const uint16_t*>(row + kFp8Dv + 16)[d - kFp8Dv]);
+}
+
 constexpr int kGenThreads = 256;
 
 // One workgroup per (b, t, h).  Dynamic LDS: q row (Dk floats) + k logits.
@@ -54,10 +60,16 @@ void sparse_attn_generic_kernel(SparseAttnArgs a)
         const int s = sel[j];
         float l = -INFINITY;
         if (s >= 0 && s <= pos) {
-            const size_t koff = (static_cast<size_t>(b) * a.kv_rows + s) * a.row_stride +
-                                static_cast<size_t>(h) * a.head_stride;
             float acc = 0.f;
-            for (int d = 0; d < a.Dk; ++d) acc += qs[d] * ld_elem(a.kbase, koff + d, a.bf16);
+            if (a.fp8_latent) {
+                const uint8_t* row = static_cast<const uint8_t*>(a.kbase) +
+                                     (static_cast<size_t>(b) * a.kv_rows + s) * kFp8RowBytes;
+                for (int d = 0; d < a.Dk; ++d) acc += qs[d] * fp8_latent_elem(row, d);
+            } else {
+                const size_t koff = (static_cast<size_t>(b) * a.kv_rows + s) * a.row_stride +
+                                    static_cast<size_t>(h) * a.head_stride;
+                for (int d = 0; d < a.Dk; ++d) acc += qs[d] * ld_elem(a.kbase, koff + d, a.bf16);
+            }
             l = acc * a.sm_scale;
         }
         logit[j] = l;
@@ -100,6 +112,12 @@ void sparse_attn_generic_kernel(SparseAttnArgs a)
             const float p = logit[j];
             if (p == 0.f) continue;
             const int s = sel[j];
+            if (a.fp8_latent) {
+                const uint8_t* row = static_cast<const uint8_t*>(a.vbase) +
+                                     (static_cast<size_t>(b) * a.kv_rows + s) * kFp8RowBytes;
+                acc += p * fp8_latent_elem(row, d);
+                continue;
+            }
             const size_t voff = (static_cast<size_t>(b) * a.kv_rows + s) * a.row_stride_v +
                                 static_cast<size_t>(h) * a.head_stride_v;
             acc += p * ld_elem(a.vbase, voff + d, a.bf16);
@@ -366,9 +384,219 @@ __device__ __forceinline__ void mla_publish(const v8s& pk, int wave, int lane) {
     *reinterpret_cast<v8s*>(&g_pbuf[wave][lane][0]) = pk;
 }
 
+// ---- FP8 latent rows (656 bytes: 512 e4m3fn codes, four fp32 block scales, 64 bf16 rope
+// values).  Same pipeline and roles as above; what changes:
+//   tile     32 rows of 656 bytes, unswizzled, with a 128-byte gap between rows 15 and
+//            16 (row r at 656 r, plus 128 from row 16 on) so that the transpose reads of
+//            PV, which touch rows κ and κ + 16 together, fall in different LDS banks;
+//            21 wave-wide 1 KB loads fill 1320 of the 1344 16-byte slots of a 21 KB
+//            buffer (the gap and the tail slots get dummy copies);
+//   QK       the code bytes are widened to bf16 exactly in registers, and each 128-column
+//            block gets its own matrix-core chain, scaled per key afterwards in fp32
+//            (logit = sum_j scale_j . (q_j . code_j) + q_rope . rope), so no product is
+//            rounded beyond the fp32 accumulation;
+//   PV       one 8-byte transpose read hands each lane the eight key codes of its
+//            output column; wave w's columns lie in block w / 2, whose per-key scale is
+//            folded into the wave's copy of P: every QK wave publishes four copies of
+//            its bf16 numerators, p . scale_j for j = 0..3.
+constexpr int kF8Row = kFp8RowBytes;                   // 656
+constexpr int kF8Gap = 128;                            // LDS gap before row 16
+constexpr int kF8Slots = (kKt * kF8Row + kF8Gap) / 16; // 1320 used 16-byte slots
+constexpr int kF8Loads = (kF8Slots + kWave - 1) / kWave;   // 21
+constexpr int kF8TileStride = kF8Loads * kWave * 16;   // 21504
+constexpr int kF8Scale = kFp8Dv;                       // byte offset of the scales
+constexpr int kF8Rope = kFp8Dv + 16;                   // byte offset of the rope values
+constexpr int kF8PbufOff = kBufs * kF8TileStride;      // P copies: [block 4][ht 8][lane][16 B]
+constexpr int kF8GatherMax = (kF8Loads + kMlaWaves - 1) / kMlaWaves;   // 3
+static_assert(kF8PbufOff + 4 * kMaxHt * kWave * 16 <= kBufs * kTileBytes,
+              "FP8 tiles and P copies fit in the tile ring's LDS");
+
+__device__ __forceinline__ uint8_t* kbuf8(int ti) { return g_kbuf + (ti & (kBufs - 1)) * kF8TileStride; }
+__device__ __forceinline__ int f8_row_off(int r) { return r * kF8Row + (r >= 16 ? kF8Gap : 0); }
+
+// Wait for this wave's loads of the current tile (waves 0..4 issue 3 per tile, 5..7 two).
+__device__ __forceinline__ void wait_tile8(bool later, bool three) {
+    if (!later) wait_vmcnt<0>();
+    else if (three) wait_vmcnt<3>();
+    else wait_vmcnt<2>();
+}
+
+// Direct global->LDS loads of FP8 tile `ti`: lane l of wave load ci fills 16-byte slot
+// p = 64 ci + l of the buffer.  Slots 0..655 are rows 0..15 (41 slots a row), 656..663
+// the gap, 664..1319 rows 16..31, 1320..1343 slack; gap and slack lanes copy chunk 0 of
+// the tile's first row (in bounds, never read back).
+__device__ __forceinline__ void gather_tile8(const uint8_t* lat_b, int ti, uint8_t* dst, int wave,
+                                             int lane) {
+    asm volatile("" : "+v"(lane));
+    const uint32_t lds_base = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(
+        (__attribute__((address_space(3))) uint8_t*)(dst)));
+    constexpr int kHalf = 16 * (kF8Row / 16);          // 656 slots per 16 rows
+    constexpr int kHi = kHalf + kF8Gap / 16;           // 664: first slot of row 16
+    int s[kF8GatherMax], chunk[kF8GatherMax];
+#pragma unroll
+    for (int i = 0; i < kF8GatherMax; ++i) {
+        const int p = (wave + kMlaWaves * i) * kWave + lane;
+        const bool lo = p < kHalf;
+        const bool used = lo || (p >= kHi && p < kF8Slots);
+        const int rel = lo ? p : p - kHi;
+        const int r = used ? rel / (kF8Row / 16) : 0;
+        chunk[i] = used ? rel - r * (kF8Row / 16) : 0;
+        s[i] = g_keys[ti * kKt + (used && !lo ? 16 + r : r)];
+    }
+#pragma unroll
+    for (int i = 0; i < kF8GatherMax; ++i) {
+        const int ci = wave + kMlaWaves * i;
+        if (ci < kF8Loads) {
+            const int row = s[i] < 0 ? 0 : s[i];     // unused slots read row 0 (masked later)
+            const uint8_t* src = lat_b + static_cast<uint32_t>(row) * kF8Row + chunk[i] * 16;
+            const uint32_t m0v = __builtin_amdgcn_readfirstlane(lds_base + ci * kWave * 16);
+            asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off"
+                         :: "s"(m0v), "v"(src) : "memory");
+        }
+    }
+}
+
+// QK and softmax numerators of FP8 tile ti for head tile `wave`; returns the four
+// block-scaled bf16 copies of the numerators in PV A-operand layout.
 template <int NHT>
+__device__ __forceinline__ void mla_qk_softmax8(MlaState<NHT>& st, const uint8_t* kb, int ti,
+                                                float scale_log2, int lane, v8s (&pk)[4],
+                                                bool fixed) {
+    int lane_o = lane;
+    asm volatile("" : "+v"(lane_o));
+    const int go = lane_o >> 4;
+    const int no = lane_o & 15;
+    // A operand: key row 16 kt + n, columns 32 ds + 8 g .. + 7
+    const uint8_t* krow[2] = {kb + f8_row_off(no) + 8 * go, kb + f8_row_off(16 + no) + 8 * go};
+    // scales of the keys this lane's results belong to: rows 16 kt + 4 g + i
+    const uint8_t* srow = kb + f8_row_off(4 * go) + kF8Scale;
+    auto scale_of = [&](int kt, int i, int blk) -> float {
+        return *reinterpret_cast<const float*>(srow + kt * (16 * kF8Row + kF8Gap) + i * kF8Row + 4 * blk);
+    };
+    // Register budget: the queries and the output accumulators hold 200 of the wave's 256
+    // registers, so the two key halves run one after the other (one chain each), the block
+    // scales are read in the middle of their block and the rope operands only once the
+    // last code bytes have been widened.
+    v4f tot[2];
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt) {
+        constexpr int kPre = 2;
+        uint2 raw[kPre];
+#pragma unroll
+        for (int ds = 0; ds < kPre; ++ds) raw[ds] = *reinterpret_cast<const uint2*>(krow[kt] + 32 * ds);
+        v8bf rope[2];
+        tot[kt] = v4f{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int blk = 0; blk < 4; ++blk) {
+            v4f acc = v4f{0.f, 0.f, 0.f, 0.f};
+            float sc[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int ds = 4 * blk + j;
+                const v8bf a = fp8x8_to_bf16(static_cast<int>(raw[ds % kPre].x),
+                                             static_cast<int>(raw[ds % kPre].y));
+                if (ds + kPre < 16)
+                    raw[ds % kPre] = *reinterpret_cast<const uint2*>(krow[kt] + 32 * (ds + kPre));
+                if (ds == 15) {
+#pragma unroll
+                    for (int r = 0; r < 2; ++r)
+                        rope[r] = *reinterpret_cast<const v8bf*>(krow[kt] - 8 * go + kF8Rope + 64 * r + 16 * go);
+                }
+                if (j == 1) {
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) sc[i] = scale_of(kt, i, blk);
+                }
+                acc = mfma_bf16_16x16x32(a, st.qreg[ds], acc);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i) tot[kt][i] += acc[i] * sc[i];
+        }
+        v4f acc = v4f{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int r = 0; r < 2; ++r) acc = mfma_bf16_16x16x32(rope[r], st.qreg[16 + r], acc);
+        tot[kt] += acc;
+    }
+    // softmax numerators, as for bf16 rows
+    float sv[8];
+    float mx = -INFINITY;
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const bool valid = g_keys[ti * kKt + 16 * kt + 4 * go + i] >= 0;
+            const float v = valid ? tot[kt][i] * scale_log2 : -INFINITY;
+            sv[4 * kt + i] = v;
+            mx = fmaxf(mx, v);
+        }
+    mx = max_xor32(max_xor16(mx));
+    if (!fixed) {
+        if (st.m_ref == -INFINITY) st.m_ref = mx;
+        st.m_max = fmaxf(st.m_max, mx);
+        st.over = st.over || mx > st.m_ref + kRefSpan;
+    }
+    const float mref = st.m_ref == -INFINITY ? 0.f : st.m_ref;
+    float psum = 0.f;
+    float p[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        p[j] = exp2_num(sv[j] - mref);
+        psum += p[j];
+    }
+    st.l_run += sum_xor32(sum_xor16(psum));
+    // value-block copies: numerator of key 16 kt + 4 g + i times that key's scale j
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const float4 s4 = *reinterpret_cast<const float4*>(srow + kt * (16 * kF8Row + kF8Gap) + i * kF8Row);
+            pk[0][4 * kt + i] = static_cast<short>(f32_to_bf16(p[4 * kt + i] * s4.x));
+            pk[1][4 * kt + i] = static_cast<short>(f32_to_bf16(p[4 * kt + i] * s4.y));
+            pk[2][4 * kt + i] = static_cast<short>(f32_to_bf16(p[4 * kt + i] * s4.z));
+            pk[3][4 * kt + i] = static_cast<short>(f32_to_bf16(p[4 * kt + i] * s4.w));
+        }
+}
+
+// PV of the previous FP8 tile: output columns 64 wave .. + 63 (block wave / 2) for all
+// heads.  Within each 16-lane group an 8-byte transpose read hands lane n byte n % 8 of
+// the address of lane 2 e + n / 8 as element e, so lane m supplies row
+// κ = 16 (e / 4) + 4 g + e % 4 (e = m / 2), columns d0 + 8 (m % 2) .. + 7: lane n then
+// holds column d0 + n of the eight keys of its P operand slots.
+template <int NHT>
+__device__ __forceinline__ void mla_pv8(MlaState<NHT>& st, const uint8_t* kb, int wave, int lane) {
+    typedef int v2i_t __attribute__((ext_vector_type(2)));
+    int lane_o = lane;
+    asm volatile("" : "+v"(lane_o));
+    const int go = lane_o >> 4;
+    const int mo = lane_o & 15;
+    const int e = mo >> 1;
+    const uint8_t* src = kb + f8_row_off(16 * (e >> 2) + 4 * go + (e & 3)) + 8 * (mo & 1) + 64 * wave;
+    v8bf vb[kDtW];
+#pragma unroll
+    for (int dt = 0; dt < kDtW; ++dt) {
+        const v2i_t r = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+            (__attribute__((address_space(3))) v2i_t*)(src + 16 * dt));
+        vb[dt] = fp8x8_to_bf16(r[0], r[1]);
+    }
+    const uint8_t* pb = g_kbuf + kF8PbufOff + ((wave >> 1) * kMaxHt * kWave + lane) * 16;
+#pragma unroll
+    for (int h = 0; h < NHT; ++h) {
+        __builtin_amdgcn_sched_barrier(0);
+        const v8bf pa = *reinterpret_cast<const v8bf*>(pb + h * kWave * 16);
+#pragma unroll
+        for (int dt = 0; dt < kDtW; ++dt) st.o[h][dt] = mfma_bf16_16x16x32(pa, vb[dt], st.o[h][dt]);
+    }
+}
+
+__device__ __forceinline__ void mla_publish8(const v8s (&pk)[4], int wave, int lane) {
+#pragma unroll
+    for (int blk = 0; blk < 4; ++blk)
+        *reinterpret_cast<v8s*>(g_kbuf + kF8PbufOff + ((blk * kMaxHt + wave) * kWave + lane) * 16) = pk[blk];
+}
+
+template <int NHT, bool F8>
 __global__ __launch_bounds__(kMlaThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
-void mla_decode_mfma_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ latent,
+void mla_decode_mfma_kernel(const uint16_t* __restrict__ q, const uint8_t* __restrict__ latent,
                             const int32_t* __restrict__ idx, const int32_t* __restrict__ len,
                             int T, int Lmax, int k, int tiles_per_split, int n_splits,
                             float scale_log2, uint16_t* __restrict__ out,
@@ -432,8 +660,7 @@ void mla_decode_mfma_kernel(const uint16_t* __restrict__ q, const uint16_t* __re
     st.m_max = -INFINITY;
     st.over = false;
 
-    const uint8_t* lat_b = reinterpret_cast<const uint8_t*>(latent) +
-                           static_cast<size_t>(b) * Lmax * kRowBytes;
+    const uint8_t* lat_b = latent + static_cast<size_t>(b) * Lmax * (F8 ? kF8Row : kRowBytes);
     lds_barrier();        // g_keys ready (its stores waited for the idx loads)
     const bool qk_wave = wave < NHT;
     // One pass over the split's tiles; the queries and the selected positions stay in
@@ -447,40 +674,60 @@ void mla_decode_mfma_kernel(const uint16_t* __restrict__ q, const uint16_t* __re
     // prefetches tile i+2; a second barrier separates the reads of P(i-1) from the
     // publication of P(i).  The loop body has no data-dependent branch around the
     // accumulators, so they keep their registers across iterations.
+    // The tile-format specific steps (bf16 rows or FP8 rows).
+    auto gather = [&](int ti) {
+        if constexpr (F8) gather_tile8(lat_b, ti, kbuf8(ti), wave, lane);
+        else gather_tile(lat_b, ti, kbuf(ti), wave, lane);
+    };
+    auto wait_for = [&](bool later) {
+        if constexpr (F8) wait_tile8(later, wave < 5);
+        else wait_tile(later, wave < 4);
+    };
+    auto pv = [&](int ti) {
+        if constexpr (F8) mla_pv8<NHT>(st, kbuf8(ti), wave, lane);
+        else mla_pv<NHT>(st, kbuf(ti), wave, lane);
+    };
+    auto qk_publish = [&](int ti, bool fixed) {
+        if constexpr (F8) {
+            v8s pk[4];
+            if (qk_wave) mla_qk_softmax8<NHT>(st, kbuf8(ti), ti, scale_log2, lane, pk, fixed);
+            lds_barrier();
+            if (qk_wave) mla_publish8(pk, wave, lane);
+        } else {
+            v8s pk;
+            if (qk_wave) mla_qk_softmax<NHT>(st, kbuf(ti), ti, scale_log2, lane, pk, fixed);
+            lds_barrier();
+            if (qk_wave) mla_publish(pk, wave, lane);
+        }
+    };
     auto pass = [&](bool fixed) {
 #pragma unroll
         for (int h = 0; h < NHT; ++h)
 #pragma unroll
             for (int dt = 0; dt < kDtW; ++dt) st.o[h][dt] = v4f{0.f, 0.f, 0.f, 0.f};
         st.l_run = 0.f;
-        if (n_tiles > 0) gather_tile(lat_b, 0, kbuf(0), wave, lane);
+        if (n_tiles > 0) gather(0);
         wait_vmcnt<0>();
 #pragma unroll
         for (int ds = 0; ds < kDs; ++ds) asm volatile("" :: "v"(st.qreg[ds]));
-        if (n_tiles > 1) gather_tile(lat_b, 1, kbuf(1), wave, lane);
+        if (n_tiles > 1) gather(1);
         if (n_tiles > 0) {
-            wait_tile(1 < n_tiles, wave < 4);
+            wait_for(1 < n_tiles);
             lds_barrier();
-            if (2 < n_tiles) gather_tile(lat_b, 2, kbuf(2), wave, lane);
-            v8s pk;
-            if (qk_wave) mla_qk_softmax<NHT>(st, kbuf(0), 0, scale_log2, lane, pk, fixed);
-            lds_barrier();
-            if (qk_wave) mla_publish(pk, wave, lane);
+            if (2 < n_tiles) gather(2);
+            qk_publish(0, fixed);
         }
         for (int ti = 1; ti < n_tiles; ++ti) {
-            wait_tile(ti + 1 < n_tiles, wave < 4);
+            wait_for(ti + 1 < n_tiles);
             lds_barrier();
-            if (ti + 2 < n_tiles) gather_tile(lat_b, ti + 2, kbuf(ti + 2), wave, lane);
-            mla_pv<NHT>(st, kbuf(ti - 1), wave, lane);
+            if (ti + 2 < n_tiles) gather(ti + 2);
+            pv(ti - 1);
             __builtin_amdgcn_sched_barrier(0);
-            v8s pk;
-            if (qk_wave) mla_qk_softmax<NHT>(st, kbuf(ti), ti, scale_log2, lane, pk, fixed);
-            lds_barrier();
-            if (qk_wave) mla_publish(pk, wave, lane);
+            qk_publish(ti, fixed);
         }
         if (n_tiles > 0) {
             lds_barrier();
-            mla_pv<NHT>(st, kbuf(n_tiles - 1), wave, lane);
+            pv(n_tiles - 1);
         }
     };
     pass(false);
@@ -622,10 +869,10 @@ hipError_t launch_sparse_attn_generic(const SparseAttnArgs& a, hipStream_t strea
     return hipGetLastError();
 }
 
-bool mla_decode_mfma_supported(int H, int Dv, int Dr, int k, int bf16) {
+bool mla_decode_mfma_supported(int H, int Dv, int Dr, int k, int type) {
     // every split holds at most kMaxSlots selected positions in LDS
-    return bf16 && Dv == kDv && Dv + Dr == kDq && (H == 64 || H == 128) &&
-           k <= kMaxSplits * kMaxSlots;
+    return (type == kLatBf16 || type == kLatFp8) && Dv == kDv && Dv + Dr == kDq &&
+           (H == 64 || H == 128) && k <= kMaxSplits * kMaxSlots;
 }
 
 size_t mla_decode_workspace_bytes(int B, int T, int H, int, int k) {
@@ -637,7 +884,7 @@ size_t mla_decode_workspace_bytes(int B, int T, int H, int, int k) {
 
 hipError_t launch_mla_decode_mfma(const void* q, const void* latent, const int32_t* idx,
                                   const int32_t* len, int B, int T, int H, int Lmax, int k,
-                                  float sm_scale, void* out, float* lse, void* ws,
+                                  float sm_scale, int type, void* out, float* lse, void* ws,
                                   hipStream_t stream) {
     const int rows = B * T;
     const int s = mla_splits(rows, k);
@@ -648,14 +895,13 @@ hipError_t launch_mla_decode_mfma(const void* q, const void* latent, const int32
                             : nullptr;
     const float scale_log2 = sm_scale * kLog2e;
     auto qp = static_cast<const uint16_t*>(q);
-    auto lp = static_cast<const uint16_t*>(latent);
+    auto lp = static_cast<const uint8_t*>(latent);
     auto op = static_cast<uint16_t*>(out);
-    if (H == 128)
-        hipLaunchKernelGGL(mla_decode_mfma_kernel<8>, dim3(rows * s), dim3(kMlaThreads), 0, stream,
-                           qp, lp, idx, len, T, Lmax, k, tps, s, scale_log2, op, lse, part_o, part_lse);
-    else
-        hipLaunchKernelGGL(mla_decode_mfma_kernel<4>, dim3(rows * s), dim3(kMlaThreads), 0, stream,
-                           qp, lp, idx, len, T, Lmax, k, tps, s, scale_log2, op, lse, part_o, part_lse);
+    const bool f8 = type == kLatFp8;
+    auto kern = H == 128 ? (f8 ? mla_decode_mfma_kernel<8, true> : mla_decode_mfma_kernel<8, false>)
+                         : (f8 ? mla_decode_mfma_kernel<4, true> : mla_decode_mfma_kernel<4, false>);
+    hipLaunchKernelGGL(kern, dim3(rows * s), dim3(kMlaThreads), 0, stream,
+                       qp, lp, idx, len, T, Lmax, k, tps, s, scale_log2, op, lse, part_o, part_lse);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || s == 1) return e;
     const int parts = (H * (kDv / kCombCols) + 255) / 256;

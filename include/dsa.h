@@ -58,7 +58,14 @@ typedef enum {
     DSA_ERR_HIP = 6         /* a HIP launch or runtime call failed                 */
 } dsa_status;
 
-typedef enum { DSA_F32 = 0, DSA_BF16 = 1 } dsa_dtype;           /* attention element type */
+/* Attention element type.  DSA_FP8_LATENT (latent form only: dsa_sparse_mla_decode and
+ * dsa_layer_step with DSA_ATTN_LATENT): q and out are bf16, and each latent cache row is
+ * the 656-byte FP8 storage form of the excalidraw diagram's latent cache box and its
+ * per-token byte figure -- 512 e4m3fn codes, then four fp32 scales (scale j multiplies
+ * columns 128j .. 128j+127), then the 64 rope values as bf16 -- so latent is
+ * [B,Lmax,656] bytes and the shape is fixed at Dv = 512, Dr = 64.  Column d < 512 of a
+ * row is code[d] * scale[d / 128]; column 512 + r is rope value r. */
+typedef enum { DSA_F32 = 0, DSA_BF16 = 1, DSA_FP8_LATENT = 2 } dsa_dtype;
 typedef enum { DSA_ATTN_LATENT = 0, DSA_ATTN_MHA = 1 } dsa_attn_form;
 
 /* Thread-local text for the last non-OK status of this thread ("" if none). */
@@ -106,18 +113,20 @@ dsa_status dsa_topk(const float* scores, const int32_t* len, int B, int T, int L
  *  rows, each of which serves as key and value; softmax and value mix as in the MLA
  *  prefill excerpt.)
  *   q      [B,T,H,Dv+Dr]   (absorbed query: Dv latent columns, then Dr rope columns)
- *   latent [B,Lmax,Dv+Dr]  (cache row: latent Dv, then rope Dr)
+ *   latent [B,Lmax,Dv+Dr]  (cache row: latent Dv, then rope Dr; with DSA_FP8_LATENT
+ *                          [B,Lmax,656] bytes in the FP8 storage form, decoded as above)
  *   idx    [B,T,k] i32     (slots < 0 and positions > pos(b,t) are ignored)
  *   out    [B,T,H,Dv]      (same dtype as q), lse [B,T,H] f32 natural-log sum-exp of the
  *                          scaled logits, or NULL.
  *   logit_j = sm_scale * q[b,t,h,:] . latent[b,s_j,:]; out = softmax(logit) @ latent[.,:Dv]
  * A row with no usable slot gets out = 0 and lse = -inf.  Entries of idx must be unique
- * per row.  Any H, Dv, Dr with Dv+Dr <= 1024 and dtype F32 or BF16 (the vector-ALU path
- * keeps all k logits in LDS: 4 (Dv + Dr + k) <= 65536 bytes); the bf16 shape H in
- * {64, 128}, Dv = 512, Dr = 64, k <= 16384 runs on the matrix-core path, which splits
- * each row's slots over up to 16 workgroups and needs a workspace for their partial
- * results (dsa_sparse_mla_decode_workspace_bytes(); 0 when the rows fill the GPU
- * without splitting).
+ * per row.  Any H, Dv, Dr with Dv+Dr <= 1024 and dtype F32 or BF16, and any H with
+ * DSA_FP8_LATENT (the vector-ALU path keeps all k logits in LDS: 4 (Dv + Dr + k) <= 65536
+ * bytes); the BF16 and FP8_LATENT shape H in {64, 128}, Dv = 512, Dr = 64, k <= 16384
+ * runs on the matrix-core path, which splits each row's slots over up to 16 workgroups
+ * and needs a workspace for their partial results (dsa_sparse_mla_decode_workspace_bytes();
+ * 0 when the rows fill the GPU without splitting).  A DSA_FP8_LATENT dtype with other
+ * widths is DSA_ERR_DTYPE.
  */
 size_t dsa_sparse_mla_decode_workspace_bytes(int B, int T, int H, int Dv, int Dr, int k,
                                              dsa_dtype dt);
@@ -167,7 +176,7 @@ typedef struct dsa_layer_args {
     float sm_scale_I;
     /* attention */
     dsa_attn_form form;
-    dsa_dtype dtype;
+    dsa_dtype dtype;          /* DSA_FP8_LATENT: latent form only                    */
     const void* q;            /* latent: [B,T,H,Dv+Dr]    MHA: [B,T,H,Dqk]           */
     const void* latent;       /* latent: [B,Lmax,Dv+Dr]   MHA: unused                */
     const void* k;            /* MHA: [B,T,H,Dqk]         latent: unused             */

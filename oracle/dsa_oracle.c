@@ -236,15 +236,19 @@ int orc_sparse_mla_decode(const void* q, const void* latent, const int32_t* idx,
             int n = 0;
             for (int j = 0; j < k; ++j)
                 if (sel[j] >= 0 && sel[j] <= pos) keys[n++] = sel[j];
+            /* the selected rows' values, decoded once for all heads: C[j][c] = C[b, s_j, c] */
+            double* C = (double*)malloc(sizeof(double) * (size_t)(n > 0 ? n : 1) * Dq);
+            for (int j = 0; j < n; ++j)
+                for (int c = 0; c < Dq; ++c)
+                    C[(size_t)j * Dq + c] = latent_elem(latent, dtype, (size_t)b * Lmax + keys[j], Dq, c);
             for (int h = 0; h < H; ++h) {
                 const size_t qoff = (row * H + h) * (size_t)Dq;
                 double* o = out + (row * H + h) * (size_t)Dv;
                 double m = -INFINITY, sum = 0.0;
                 for (int j = 0; j < n; ++j) {
-                    const size_t crow = (size_t)b * Lmax + keys[j];
                     double dot = 0.0;
                     for (int d = 0; d < Dq; ++d)
-                        dot += load_elem(q, qdt, qoff + d) * latent_elem(latent, dtype, crow, Dq, d);
+                        dot += load_elem(q, qdt, qoff + d) * C[(size_t)j * Dq + d];
                     logit[j] = sm_scale * dot;
                     if (logit[j] > m) m = logit[j];
                 }
@@ -253,11 +257,11 @@ int orc_sparse_mla_decode(const void* q, const void* latent, const int32_t* idx,
                 for (int j = 0; j < n; ++j) sum += exp(logit[j] - m);
                 for (int j = 0; j < n; ++j) {
                     const double p = exp(logit[j] - m) / sum;
-                    const size_t crow = (size_t)b * Lmax + keys[j];
-                    for (int d = 0; d < Dv; ++d) o[d] += p * latent_elem(latent, dtype, crow, Dq, d);
+                    for (int d = 0; d < Dv; ++d) o[d] += p * C[(size_t)j * Dq + d];
                 }
                 if (lse) lse[row * H + h] = m + log(sum);
             }
+            free(C);
             free(logit);
             free(keys);
         }

@@ -114,3 +114,25 @@ def test_layer_step_validation(lib):
     a.k = a.v = p
     a.Dqk = 192
     assert lib.dsa_layer_step(ctypes.byref(a), ctypes.c_void_p(p), need, None) == 2  # Lmax != T
+
+
+def test_fp8_latent_validation(lib):
+    """FP8 latent rows: the latent form only, at the storage form's 512 + 64 widths; the
+    matrix-core shape takes the same split workspace as bf16 rows."""
+    p = _fake()
+    F8 = N.DSA_FP8_LATENT
+    assert F8 == 2
+    assert (lib.dsa_sparse_mla_decode_workspace_bytes(2, 1, 128, 512, 64, 2048, F8) ==
+            lib.dsa_sparse_mla_decode_workspace_bytes(2, 1, 128, 512, 64, 2048, N.DSA_BF16))
+    st = lib.dsa_sparse_mla_decode(p, p, p, p, 2, 1, 128, 256, 64, 4096, 2048, 0.1, F8, p, None,
+                                   None, 0, None)
+    assert st == 3 and b"FP8" in lib.dsa_last_error()
+    st = lib.dsa_sparse_mla_decode(p, p, p, p, 2, 1, 128, 512, 64, 4096, 2048, 0.1, F8, p, None,
+                                   None, 0, None)
+    assert st == 5
+    # any head count runs on the vector-ALU path (no workspace)
+    assert lib.dsa_sparse_mla_decode_workspace_bytes(2, 1, 16, 512, 64, 2048, F8) == 0
+    # the MHA prefill form has no FP8 variant
+    st = lib.dsa_sparse_mla_prefill(p, p, p, p, 1, 8, 2, 192, 128, 64, 0.1, F8, p, None, None, 0,
+                                    None)
+    assert st == 3

@@ -4,7 +4,8 @@ index-score row, its top-k and its attention output over the GPU's own selection
 
 Shapes: V3.2-size decode (B=32, L=8192), long-context decode (B=8, L=131072), ragged
 decode (B=64, lengths in [1024, 65536], Student-t(3) indexer inputs), chunked prefill
-(T=8192, MHA form, 128 heads, qk 192 / v 128).  Cache padding past each length is
+(T=8192, MHA form, 128 heads, qk 192 / v 128); the V3.2 and ragged decodes also with the
+latent cache in its 656-byte FP8 row form.  Cache padding past each length is
 poisoned, so any read beyond it fails the comparison."""
 import sys
 
@@ -36,11 +37,15 @@ def _np(t):
     return t.float().cpu().numpy() if t.dtype == torch.bfloat16 else t.cpu().numpy()
 
 
-@pytest.mark.parametrize("name", ["decode_v32", "decode_long", "decode_ragged"])
-def test_fullsize_decode(dsa, orc, name):
+@pytest.mark.parametrize("name,latent_form", [("decode_v32", "bf16"), ("decode_long", "bf16"),
+                                               ("decode_ragged", "bf16"), ("decode_v32", "fp8"),
+                                               ("decode_ragged", "fp8")],
+                         ids=["decode_v32", "decode_long", "decode_ragged", "decode_v32-fp8",
+                              "decode_ragged-fp8"])
+def test_fullsize_decode(dsa, orc, name, latent_form):
     cfg = S.CONFIGS[name]
-    _say(f"[fullsize] {name}: generating inputs")
-    c = S.make_case(cfg)
+    _say(f"[fullsize] {name} ({latent_form} latent): generating inputs")
+    c = S.make_case(cfg, latent_form=latent_form)
     d = S.to_device(c, "cuda")
     step = dsa.LayerStep(d["q_i"], d["q_scale"], d["w"], d["k_i"], d["k_scale"], d["lens"],
                          cfg.sm_scale_i, cfg.k, d["q"], cfg.sm_scale, latent=d["latent"],
@@ -63,6 +68,7 @@ def test_fullsize_decode(dsa, orc, name):
         ro, rl = orc.sparse_mla_decode(c["q"][sl], c["latent"][sl], gidx, lens[sl], cfg.Dv,
                                        cfg.sm_scale)
         check_attention(_np(out[sl]), lse[sl].cpu().numpy(), ro, rl, cfg.attn_dtype)
+    _say(f"[fullsize] {name} ({latent_form} latent): done")
 
 
 def test_fullsize_prefill(dsa, orc):

@@ -215,6 +215,44 @@ def test_sparse_mla_decode_generic_f32(dsa, orc):
     check_attention(out.cpu().numpy(), lse.cpu().numpy(), ro, rl, "f32")
 
 
+FP8_MLA_CASES = [
+    # name, B, T, Lmax, lens, k, H   (H 64 / 128: matrix cores; other H: vector ALUs)
+    ("decode_k2048", 2, 1, 3000, [3000, 1500], 2048, 128),
+    ("decode_ragged_k", 3, 1, 700, [700, 650, 90], 100, 128),
+    ("two_rows_causal", 1, 2, 2100, [2100], 2048, 128),
+    ("heads64", 2, 1, 900, [900, 513], 512, 64),
+    ("many_rows_nosplit", 260, 1, 160, [160] * 260, 64, 128),
+    ("long_k_16_splits", 1, 1, 17000, [17000], 16384, 128),
+    ("heads16_generic", 2, 3, 300, [300, 77], 40, 16),
+]
+
+
+def _fp8_rows(rng, shape):
+    """656-byte FP8 latent rows whose 128-column blocks differ in magnitude by up to 32x
+    (so that each block's scale matters), values at most about 3 in magnitude."""
+    x = rng.standard_normal(shape + (576,), dtype=np.float32)
+    f = np.exp2(rng.uniform(-5, 0, size=shape + (4,))).astype(np.float32)
+    x[..., :512] *= np.repeat(f, 128, axis=-1)
+    return S.pack_latent_fp8(x)
+
+
+@pytest.mark.parametrize("name,B,T,Lmax,lens,k,H", FP8_MLA_CASES, ids=[c[0] for c in FP8_MLA_CASES])
+def test_sparse_mla_decode_fp8_latent(dsa, orc, name, B, T, Lmax, lens, k, H):
+    _say(f"[sparse_mla_decode fp8 latent] {name}")
+    rng = np.random.default_rng(zlib.crc32(("fp8" + name).encode()) % 10000)
+    lens = np.asarray(lens, np.int32)
+    q = S.to_bf16_bits(rng.standard_normal((B, T, H, 576), dtype=np.float32))
+    lat = _fp8_rows(rng, (B, Lmax))
+    idx = _random_idx(rng, B, T, k, lens, invisible=True)
+    sm = 192 ** -0.5
+    tq = torch.from_numpy(q.view(np.int16)).view(torch.bfloat16).cuda()
+    out, lse = dsa.sparse_mla_decode(tq, torch.from_numpy(lat).cuda(), torch.from_numpy(idx).cuda(),
+                                     torch.from_numpy(lens).cuda(), 512, sm)
+    torch.cuda.synchronize()
+    ro, rl = orc.sparse_mla_decode(q, lat, idx, lens, 512, sm)
+    check_attention(_np_out(out), lse.cpu().numpy(), ro, rl, "bf16")
+
+
 @pytest.mark.parametrize("dt", ["bf16", "f32"])
 def test_sparse_mla_prefill(dsa, orc, dt):
     _say(f"[sparse_mla_prefill {dt}]")
@@ -253,6 +291,13 @@ LAYER_CASES = [
 ]
 
 
+FP8_LAYER_CASES = [
+    ("decode_small", _small("decode_v32", name="ds8", B=3, Lmax=4100, seed=212)),
+    ("ragged_small_t3", _small("decode_ragged", name="rs8", B=5, T=3, Lmax=6000,
+                               lens="ragged:1024:6000", seed=215)),
+]
+
+
 def _layer_step_latent(dsa, cfg, c):
     d = _dev(c)
     step = dsa.LayerStep(d["q_i"], d["q_scale"], d["w"], d["k_i"], d["k_scale"], d["lens"],
@@ -278,6 +323,22 @@ def test_layer_step_latent(dsa, orc, name, cfg):
     # attention on the GPU's own selection
     ro2, rl2 = orc.sparse_mla_decode(c["q"], c["latent"], gidx, c["lens"], cfg.Dv, cfg.sm_scale)
     check_attention(_np_out(out), lse.cpu().numpy(), ro2, rl2, cfg.attn_dtype)
+
+
+@pytest.mark.parametrize("name,cfg", FP8_LAYER_CASES, ids=[c[0] for c in FP8_LAYER_CASES])
+def test_layer_step_fp8_latent(dsa, orc, name, cfg):
+    _say(f"[layer_step fp8 latent] {name}")
+    c = S.make_case(cfg, latent_form="fp8")
+    step, out, lse = _layer_step_latent(dsa, cfg, c)
+    ro, rl, ridx, rsc = orc.layer_step_latent(c["q_i"], c["q_scale"], c["w"], c["k_i"],
+                                              c["k_scale"], c["lens"], cfg.sm_scale_i, cfg.k,
+                                              c["q"], c["latent"], cfg.Dv, cfg.sm_scale,
+                                              want_scores=True)
+    check_scores(step.scores.cpu().numpy(), rsc, c["lens"], cfg.T)
+    gidx = step.idx.cpu().numpy()
+    check_topk(gidx, rsc, ridx, c["lens"], cfg.T, cfg.k)
+    ro2, rl2 = orc.sparse_mla_decode(c["q"], c["latent"], gidx, c["lens"], cfg.Dv, cfg.sm_scale)
+    check_attention(_np_out(out), lse.cpu().numpy(), ro2, rl2, "bf16")
 
 
 def test_layer_step_mha_small(dsa, orc):

@@ -34,8 +34,8 @@ MUTATIONS = [
      "const int n = len[b] - T + t;"),
     ("attention scale dropped", "logit[j] = sm_scale * dot;", "logit[j] = dot;"),
     ("latent key drops rope part", "for (int d = 0; d < Dq; ++d)\n", "for (int d = 0; d < Dv; ++d)\n"),
-    ("latent value offset", "o[d] += p * latent_elem(latent, dtype, crow, Dq, d);",
-     "o[d] += p * latent_elem(latent, dtype, crow, Dq, Dr + d);"),
+    ("latent value offset", "o[d] += p * C[(size_t)j * Dq + d];",
+     "o[d] += p * C[(size_t)j * Dq + Dr + d];"),
     ("fp8 latent scale ignored", "return orc_e4m3fn_value(row[d]) * (double)scale;",
      "return orc_e4m3fn_value(row[d]);"),
     ("fp8 latent scale per 64 columns", "row + ORC_FP8_LATENT_DV + 4 * (d / ORC_FP8_LATENT_BLOCK)",
