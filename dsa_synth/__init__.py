@@ -7,7 +7,8 @@ arithmetic: both the GPU library and the CPU reference receive its arrays unchan
 
 Seeding: every tensor of sequence ``b`` comes from ``numpy.random.default_rng([seed,
 tensor_id, b])`` (tensor ids: 0 indexer q, 1 indexer K, 2 head weights, 3 attention
-q, 4 latent cache / MHA k, 5 MHA v); the lengths come from ``default_rng([seed, 6])``.
+q, 4 latent cache / MHA k, 5 MHA v, 7 / 8 the new tokens' indexer q / k before their
+preparation); the lengths come from ``default_rng([seed, 6])``.
 Generating a subset of sequences therefore reproduces exactly their slices of the
 full batch.  Cache rows at or beyond ``len[b]`` are poisoned (K code 0x7E = 448,
 K scale 1e4, latent 1e4) so that any read past the valid length shows up.
@@ -43,6 +44,7 @@ class Config:
     attn_dtype: str      # "bf16" or "f32"
     dist: str            # "normal" or "student_t3" for the indexer q/k draws
     seed: int
+    rope_i: int = 64     # rope columns at the front of each indexer q head / key row
 
     @property
     def sm_scale_i(self) -> float:
@@ -62,7 +64,8 @@ class Config:
 
 CONFIGS = {
     "tiny": Config("tiny", "latent", B=1, T=64, Lmax=64, lens="full", H_I=4, D_I=32, k=8,
-                   H=4, Dv=64, Dr=16, Dqk=0, attn_dtype="f32", dist="normal", seed=1),
+                   H=4, Dv=64, Dr=16, Dqk=0, attn_dtype="f32", dist="normal", seed=1,
+                   rope_i=8),
     "decode_v32": Config("decode_v32", "latent", B=32, T=1, Lmax=8192, lens="full", H_I=64,
                          D_I=128, k=2048, H=128, Dv=512, Dr=64, Dqk=0, attn_dtype="bf16",
                          dist="normal", seed=2),
@@ -212,6 +215,32 @@ def _poison_fp8_row() -> np.ndarray:
     row[FP8_LATENT_DV + 16:] = np.repeat(
         to_bf16_bits(np.full((1,), POISON_VALUE, np.float32)), FP8_LATENT_DR).view(np.uint8)
     return row
+
+
+def rope_tables(n_pos: int, rope_dim: int, base: float = 10000.0):
+    """cos and sin [n_pos, rope_dim/2] float32 of the rotary angle pos * base^(-2j/rope_dim)
+    (a standard frequency schedule; the preparation takes the tables as inputs)."""
+    j = np.arange(rope_dim // 2, dtype=np.float64)
+    theta = np.arange(n_pos, dtype=np.float64)[:, None] * base ** (-2.0 * j[None, :] / rope_dim)
+    return np.cos(theta).astype(np.float32), np.sin(theta).astype(np.float32)
+
+
+def make_prep_case(cfg: Config, seqs=None) -> dict:
+    """Inputs of the indexer preparation for the T new tokens of each sequence (the last T
+    positions, start = len - T): q [B,T,H_I,D_I] and k [B,T,D_I] before rope, rotation and
+    quantisation (N(0,1), Student-t(3) for the "student_t3" workloads; bf16 bits, or
+    float32 for f32 workloads), the rope tables over Lmax positions, and the key cache
+    and scales the new keys are appended to (the case's own cache from make_case)."""
+    base = make_case(cfg, seqs)
+    seqs = base["seqs"]
+    lens = base["lens"]
+    T, H_I, D_I = cfg.T, cfg.H_I, cfg.D_I
+    conv = to_bf16_bits if cfg.attn_dtype == "bf16" else (lambda a: a.astype(np.float32))
+    q = np.stack([conv(_draw(_rng(cfg, 7, b), (T, H_I, D_I), cfg.dist)) for b in seqs])
+    k = np.stack([conv(_draw(_rng(cfg, 8, b), (T, D_I), cfg.dist)) for b in seqs])
+    cos, sin = rope_tables(cfg.Lmax, cfg.rope_i)
+    return dict(q=q, k=k, cos=cos, sin=sin, start=(lens - T).astype(np.int32),
+                k_cache=base["k_i"], k_scale=base["k_scale"], lens=lens, seqs=seqs)
 
 
 def to_device(case: dict, device="cuda") -> dict:

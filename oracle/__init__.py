@@ -66,6 +66,11 @@ def _load():
                                               P, P, I, I, I, I, D, P, P, P, P]
         lib.orc_layer_step_mha.argtypes = [P, P, P, P, P, I, I, I, I, D, I,
                                            P, P, P, I, I, I, I, D, P, P, P, P]
+        lib.orc_e4m3fn_encode.argtypes = [D]
+        lib.orc_e4m3fn_encode.restype = ctypes.c_uint8
+        lib.orc_indexer_prep.argtypes = [P, P, I, P, P, I, P, I, I, I, I, I, I,
+                                         P, P, P, P, P, P, P]
+        lib.orc_indexer_prep.restype = I
         lib.orc_max_threads.argtypes = []
         for fn in (lib.orc_index_scores, lib.orc_topk, lib.orc_sparse_mla_decode,
                    lib.orc_sparse_mha_prefill, lib.orc_sparse_mha_prefill_dense,
@@ -130,6 +135,40 @@ def latent_fp8_decode(rows) -> np.ndarray:
         for d in range(576):
             out[i, d] = lib.orc_latent_fp8_value(p, d)
     return out.reshape(*rows.shape[:-1], 576)
+
+
+def e4m3fn_encode(y: float) -> int:
+    """OCP e4m3fn code of y in [-448, 448] (nearest, ties to even)."""
+    return int(_load().orc_e4m3fn_encode(float(y)))
+
+
+def indexer_prep(q, k, cos, sin, start, rope_dim, k_cache, k_scale):
+    """Rope (non-interleaved) + Walsh-Hadamard rotation + blockwise FP8 quantisation of the
+    new indexer queries q [B,T,H,D] and keys k [B,T,D] (float32/float64 or bf16 bits), the
+    keys appended into copies of k_cache [B,Lmax,D] u8 / k_scale [B,Lmax] f32 at positions
+    start[b] + t.  Returns a dict: q_fp8, q_scale (float64), k_cache, k_scale (the updated
+    copies), k_scale64, q_y, k_y (values divided by their scale, before rounding)."""
+    B, T, H, D = q.shape
+    Lmax = k_cache.shape[1]
+    qa, dt = _attn_array(q)
+    ka, dt2 = _attn_array(k)
+    assert dt == dt2 and ka.shape == (B, T, D)
+    cos, pc = _c(cos, np.float32)
+    sin, ps = _c(sin, np.float32)
+    assert cos.shape == sin.shape and cos.shape[1] == rope_dim // 2
+    start, pst = _c(start, np.int32)
+    kc = np.array(k_cache, dtype=np.uint8, copy=True, order="C")
+    ks = np.array(k_scale, dtype=np.float32, copy=True, order="C")
+    out = dict(q_fp8=np.empty((B, T, H, D), np.uint8), q_scale=np.empty((B, T, H), np.float64),
+               k_scale64=np.empty((B, T), np.float64), q_y=np.empty((B, T, H, D), np.float64),
+               k_y=np.empty((B, T, D), np.float64))
+    vp = lambda a: a.ctypes.data_as(ctypes.c_void_p)
+    _check(_load().orc_indexer_prep(vp(qa), vp(ka), dt, pc, ps, cos.shape[0], pst, B, T, H, D,
+                                    rope_dim, Lmax, vp(out["q_fp8"]), vp(out["q_scale"]),
+                                    vp(kc), vp(ks), vp(out["k_scale64"]), vp(out["q_y"]),
+                                    vp(out["k_y"])), "indexer_prep")
+    out.update(k_cache=kc, k_scale=ks)
+    return out
 
 
 def index_scores(q_fp8, q_scale, w, k_fp8, k_scale, lens, sm_scale_i):

@@ -457,6 +457,114 @@ int orc_layer_step_mha(const uint8_t* q_i, const float* q_scale, const float* w,
     return rc;
 }
 
+/* ------------------------------------------------------------------ O7: indexer preparation */
+
+/* [IDX] Indexer.forward, the steps between the projections and the scores: the query
+ * heads and the normalised key are split into a rope part (the first R columns) and the
+ * rest; rope is applied "not interleaved"; both go through rotate_activation; act_quant
+ * turns them into FP8 codes with one scale per block, and the keys are written into the
+ * key cache at the new positions.  Readings taken where the pages name a step without
+ * its body:
+ *   - non-interleaved rope pairs column j with column j + R/2 (j < R/2) and rotates the
+ *     pair by the angle of frequency j at the token's position: (a, b) ->
+ *     (a cos - b sin, a sin + b cos), with the angles' cos and sin given per position;
+ *   - rotate_activation is the orthonormal Walsh-Hadamard rotation of each D-wide row
+ *     (Sylvester order): v'_i = D^-1/2 sum_j (-1)^popcount(i & j) v_j.  The pages give
+ *     only the name, so this reading is not pinned by them;
+ *   - act_quant with block_size = D (one block per head row / key row) and a plain fp32
+ *     scale: scale = max(amax, 1e-12) / 448, code = e4m3fn(clamp(x / scale, +-448)),
+ *     nearest value, ties to the even code. */
+
+/* OCP e4m3fn code of a value in [-448, 448]: nearest representable magnitude, ties to
+ * the even code (the even mantissa); the sign bit is y's sign bit. */
+uint8_t orc_e4m3fn_encode(double y)
+{
+    const int neg = signbit(y) ? 1 : 0;
+    const double a = fabs(y);
+    int mag;
+    if (a < ldexp(1.0, -6)) {
+        mag = (int)nearbyint(ldexp(a, 9));           /* subnormal step 2^-9; 8 = 2^-6 */
+    } else {
+        int e;
+        const double m = 2.0 * frexp(a, &e);         /* a = m 2^(e-1), m in [1, 2) */
+        const int mant = (int)nearbyint((m - 1.0) * 8.0);   /* 8 carries into the exponent */
+        mag = ((e - 1 + 7) << 3) + mant;
+    }
+    return (uint8_t)((neg << 7) | mag);
+}
+
+/* act_quant of one D-wide row: returns the scale, writes the codes and (if y) x / scale. */
+static double quant_row(const double* x, int D, uint8_t* codes, double* y)
+{
+    double amax = 0.0;
+    for (int d = 0; d < D; ++d) amax = fmax(amax, fabs(x[d]));
+    const double scale = fmax(amax, 1e-12) / 448.0;
+    for (int d = 0; d < D; ++d) {
+        double v = x[d] / scale;
+        if (y) y[d] = v;
+        v = fmin(fmax(v, -448.0), 448.0);
+        codes[d] = orc_e4m3fn_encode(v);
+    }
+    return scale;
+}
+
+/* rope (non-interleaved) on the first R columns, then the Walsh-Hadamard rotation */
+static void prep_row(const void* src, int dtype, size_t off, int D, int R, const float* cs,
+                     const float* sn, double* out)
+{
+    double* v = (double*)malloc(sizeof(double) * (size_t)D);
+    for (int d = 0; d < D; ++d) v[d] = load_elem(src, dtype, off + d);
+    for (int j = 0; j < R / 2; ++j) {
+        const double a = v[j], b = v[j + R / 2];
+        v[j] = a * (double)cs[j] - b * (double)sn[j];
+        v[j + R / 2] = a * (double)sn[j] + b * (double)cs[j];
+    }
+    const double norm = 1.0 / sqrt((double)D);
+    for (int i = 0; i < D; ++i) {
+        double acc = 0.0;
+        for (int j = 0; j < D; ++j) acc += (__builtin_popcount((unsigned)(i & j)) & 1) ? -v[j] : v[j];
+        out[i] = acc * norm;
+    }
+    free(v);
+}
+
+/* q [B,T,H,D], k [B,T,D] (dtype), cos/sin [P,R/2] f32, start [B]: token t of sequence b
+ * sits at position start[b] + t.  Outputs: q codes [B,T,H,D] and scales [B,T,H]; the key
+ * codes and scales go to k_cache [B,Lmax,D] / k_scale [B,Lmax] at that position (other
+ * rows untouched); q_y [B,T,H,D] and k_y [B,T,D] (may be NULL) get x / scale before
+ * rounding; q_scale64 [B,T,H] and k_scale64 [B,T] the scales in double. */
+int orc_indexer_prep(const void* q, const void* k, int dtype, const float* cosT, const float* sinT,
+                     int P, const int32_t* start, int B, int T, int H, int D, int R, int Lmax,
+                     uint8_t* q_fp8, double* q_scale64, uint8_t* k_cache, float* k_scale,
+                     double* k_scale64, double* q_y, double* k_y)
+{
+    if (D < 2 || (D & (D - 1)) || R < 0 || R > D || (R & 1)) return ORC_ERR_SHAPE;
+    for (int b = 0; b < B; ++b)
+        if (start[b] < 0 || start[b] + T > Lmax || start[b] + T > P) return ORC_ERR_SHAPE;
+#pragma omp parallel for collapse(2) schedule(dynamic)
+    for (int b = 0; b < B; ++b) {
+        for (int t = 0; t < T; ++t) {
+            const int pos = start[b] + t;
+            const float* cs = cosT + (size_t)pos * (R / 2);
+            const float* sn = sinT + (size_t)pos * (R / 2);
+            const size_t row = (size_t)b * T + t;
+            double* x = (double*)malloc(sizeof(double) * (size_t)D);
+            for (int h = 0; h < H; ++h) {
+                const size_t qr = row * H + h;
+                prep_row(q, dtype, qr * D, D, R, cs, sn, x);
+                q_scale64[qr] = quant_row(x, D, q_fp8 + qr * D, q_y ? q_y + qr * D : NULL);
+            }
+            prep_row(k, dtype, row * D, D, R, cs, sn, x);
+            const size_t kr = (size_t)b * Lmax + pos;
+            const double ks = quant_row(x, D, k_cache + kr * D, k_y ? k_y + row * D : NULL);
+            k_scale[kr] = (float)ks;
+            k_scale64[row] = ks;
+            free(x);
+        }
+    }
+    return ORC_OK;
+}
+
 int orc_max_threads(void)
 {
 #ifdef _OPENMP

@@ -25,6 +25,12 @@ enum { ORC_FP8_LATENT_DV = 512, ORC_FP8_LATENT_DR = 64, ORC_FP8_LATENT_BLOCK = 1
 double orc_e4m3fn_value(uint8_t code);
 double orc_bf16_value(uint16_t bits);
 double orc_latent_fp8_value(const uint8_t* row, int d);
+uint8_t orc_e4m3fn_encode(double y);
+
+int orc_indexer_prep(const void* q, const void* k, int dtype, const float* cosT, const float* sinT,
+                     int P, const int32_t* start, int B, int T, int H, int D, int R, int Lmax,
+                     uint8_t* q_fp8, double* q_scale64, uint8_t* k_cache, float* k_scale,
+                     double* k_scale64, double* q_y, double* k_y);
 
 int orc_index_scores(const uint8_t* q, const float* q_scale, const float* w,
                      const uint8_t* k, const float* k_scale, const int32_t* len,

@@ -22,6 +22,11 @@ What pins what:
                               dense "scores + index mask + causal mask" form;
   * layer step             -> with k >= len the result is dense attention whatever
                               the indexer does; a planted dominant key is picked;
+  * indexer preparation    -> the e4m3fn encoder against torch's float8 cast (all
+                              midpoints, ties, signed zeros), rope against complex
+                              multiplication and the rotation against scipy's Hadamard
+                              matrix (recovered through the returned scales), a
+                              quantisation closed form, the cache append placement;
   * FP8 latent rows        -> torch's float8_e4m3fn and bfloat16 decoding at the
                               656-byte layout (512 codes, 4 fp32 block scales, 64
                               bf16 rope values), and attention over such rows ==
@@ -443,6 +448,116 @@ def pin_latent_fp8_attention_library(o):
             np.testing.assert_allclose(out[b, t], want.numpy(), rtol=1e-9, atol=1e-12)
             logits = qd @ C[mask].T * sm
             np.testing.assert_allclose(lse[b, t], torch.logsumexp(logits, -1).numpy(), rtol=1e-12)
+
+
+# ----------------------------------------------------------------------------- indexer preparation
+
+def _e4m3_grid():
+    v = _fp8_values(np.arange(0, 0x7F, dtype=np.uint8))     # 0 .. 448, ascending
+    return v
+
+
+def pin_e4m3fn_encode_library(o):
+    """Encoder == torch's float8_e4m3fn cast on every representable value, every midpoint
+    (ties to even), points just off the midpoints, signed zeros and random values."""
+    g = _e4m3_grid()
+    mids = (g[:-1] + g[1:]) / 2
+    rng = np.random.default_rng(81)
+    xs = np.concatenate([g, mids, np.nextafter(mids, 0), np.nextafter(mids, 1000),
+                         rng.uniform(-448, 448, 4000), rng.uniform(-0.02, 0.02, 2000)])
+    xs = np.concatenate([xs, -xs]).astype(np.float32)
+    xs = xs[np.abs(xs) <= 448]
+    ref = torch.from_numpy(xs).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    got = np.array([o.e4m3fn_encode(float(x)) for x in xs], np.uint8)
+    bad = np.flatnonzero(ref != got)
+    assert bad.size == 0, f"e4m3fn encode differs at {xs[bad[:5]]}: {got[bad[:5]]} vs {ref[bad[:5]]}"
+    assert o.e4m3fn_encode(-0.0) == 0x80 and o.e4m3fn_encode(0.0) == 0x00
+
+
+def _rope_angles(P, R, base=10000.0):
+    j = np.arange(R // 2)
+    theta = np.arange(P)[:, None] * base ** (-2.0 * j[None, :] / R)
+    return theta, np.cos(theta).astype(np.float32), np.sin(theta).astype(np.float32)
+
+
+def pin_indexer_prep_rope_and_rotation(o):
+    """The pre-rounding values times their scale, rotated back with scipy's Hadamard
+    matrix (its own inverse once normalised), equal the inputs rotated by complex
+    multiplication: (x_j + i x_{j+R/2}) e^{i theta_j} for the rope pairs, x unchanged
+    beyond R."""
+    import scipy.linalg
+    rng = np.random.default_rng(82)
+    B, T, H, D, R, P, Lmax = 2, 3, 2, 32, 8, 40, 40
+    q = rng.standard_normal((B, T, H, D))
+    k = rng.standard_normal((B, T, D))
+    theta, cs, sn = _rope_angles(P, R)
+    start = np.array([5, 30], np.int32)
+    r = o.indexer_prep(q, k, cs, sn, start, R, np.zeros((B, Lmax, D), np.uint8),
+                       np.zeros((B, Lmax), np.float32))
+    Hm = scipy.linalg.hadamard(D) / np.sqrt(D)
+    for b in range(B):
+        for t in range(T):
+            pos = start[b] + t
+            e = np.cos(theta[pos]).astype(np.float32) + 1j * np.sin(theta[pos]).astype(np.float32)
+            for x, y, sc in [(q[b, t, h], r["q_y"][b, t, h], r["q_scale"][b, t, h]) for h in range(H)] + \
+                            [(k[b, t], r["k_y"][b, t], r["k_scale64"][b, t])]:
+                want = x.copy()
+                z = (x[:R // 2] + 1j * x[R // 2:R]) * e
+                want[:R // 2], want[R // 2:R] = z.real, z.imag
+                np.testing.assert_allclose(Hm @ (y * sc), want, rtol=1e-10, atol=1e-12)
+
+
+def pin_indexer_prep_quant_closed_form(o):
+    """No rotation angle (cos 1, sin 0) and a row equal to a scaled column of the
+    Hadamard matrix: after the rotation the row is one spike, so its code is +-448 and
+    every other value decodes to 0; the scale is |spike| / 448."""
+    import scipy.linalg
+    D, R = 32, 8
+    Hm = scipy.linalg.hadamard(D)
+    cs = np.ones((4, R // 2), np.float32)
+    sn = np.zeros((4, R // 2), np.float32)
+    q = np.stack([3.0 * Hm[:, 5] / np.sqrt(D), -0.5 * Hm[:, 17] / np.sqrt(D)])[None, None]
+    k = (2.0 * Hm[:, 0] / np.sqrt(D))[None, None]
+    r = o.indexer_prep(q, k, cs, sn, np.array([1], np.int32), R, np.zeros((1, 4, D), np.uint8),
+                       np.zeros((1, 4), np.float32))
+    for codes, spike, val, sc in [(r["q_fp8"][0, 0, 0], 5, 448.0, r["q_scale"][0, 0, 0]),
+                                  (r["q_fp8"][0, 0, 1], 17, -448.0, r["q_scale"][0, 0, 1]),
+                                  (r["k_cache"][0, 1], 0, 448.0, r["k_scale64"][0, 0])]:
+        dec = _fp8_values(codes)
+        assert dec[spike] == val and np.all(dec[np.arange(D) != spike] == 0.0)
+    np.testing.assert_allclose(r["q_scale"][0, 0], [3.0 / 448, 0.5 / 448], rtol=1e-14)
+    np.testing.assert_allclose(r["k_scale64"][0, 0], 2.0 / 448, rtol=1e-14)
+
+
+def pin_indexer_prep_quant_bound_and_append(o):
+    """Every code is the nearest e4m3fn value of its pre-rounding value (decoded error at
+    most half a step of the e4m3 grid there), the largest magnitude of each row maps to
+    +-448, and the keys land in exactly rows start..start+T-1 of the cache."""
+    rng = np.random.default_rng(83)
+    B, T, H, D, R, P, Lmax = 3, 4, 3, 64, 16, 60, 50
+    q = rng.standard_normal((B, T, H, D)) * rng.uniform(0.01, 10, (B, T, H, 1))
+    k = rng.standard_t(3, (B, T, D))
+    _, cs, sn = _rope_angles(P, R)
+    start = np.array([0, 17, Lmax - T], np.int32)
+    kc0 = rng.integers(0, 256, (B, Lmax, D)).astype(np.uint8)
+    ks0 = rng.standard_normal((B, Lmax)).astype(np.float32)
+    r = o.indexer_prep(q, k, cs, sn, start, R, kc0, ks0)
+    g = _e4m3_grid()
+    for codes, y in [(r["q_fp8"].reshape(-1, D), r["q_y"].reshape(-1, D)),
+                     (np.concatenate([r["k_cache"][b, start[b]:start[b] + T] for b in range(B)]),
+                      r["k_y"].reshape(-1, D))]:
+        dec = _fp8_values(codes)
+        idx = np.clip(np.searchsorted(g, np.abs(y)), 1, len(g) - 1)
+        step = g[idx] - g[idx - 1]
+        assert np.all(np.abs(dec - y) <= step / 2 + 1e-12)
+        am = np.argmax(np.abs(y), axis=1)
+        assert np.all(np.abs(dec[np.arange(len(am)), am]) == 448.0)
+    for b in range(B):
+        keep = np.ones(Lmax, bool)
+        keep[start[b]:start[b] + T] = False
+        assert np.array_equal(r["k_cache"][b, keep], kc0[b, keep])
+        assert np.array_equal(r["k_scale"][b, keep], ks0[b, keep])
+        np.testing.assert_allclose(r["k_scale"][b, start[b]:start[b] + T], r["k_scale64"][b], rtol=1e-7)
 
 
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

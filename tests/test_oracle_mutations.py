@@ -43,6 +43,20 @@ MUTATIONS = [
     ("fp8 latent rope read over the scales",
      "4 * (ORC_FP8_LATENT_DV / ORC_FP8_LATENT_BLOCK) +\n                      2 * (d - ORC_FP8_LATENT_DV)",
      "2 * (d - ORC_FP8_LATENT_DV)"),
+    ("prep rope interleaved pairs", "const double a = v[j], b = v[j + R / 2];",
+     "const double a = v[2 * j], b = v[2 * j + 1];"),
+    ("prep rope sin sign", "v[j] = a * (double)cs[j] - b * (double)sn[j];",
+     "v[j] = a * (double)cs[j] + b * (double)sn[j];"),
+    ("prep rotation unnormalised", "const double norm = 1.0 / sqrt((double)D);",
+     "const double norm = 1.0;"),
+    ("prep rotation wrong sign pattern", "__builtin_popcount((unsigned)(i & j))",
+     "__builtin_popcount((unsigned)(i | j))"),
+    ("prep scale over 240", "const double scale = fmax(amax, 1e-12) / 448.0;",
+     "const double scale = fmax(amax, 1e-12) / 240.0;"),
+    ("prep ties away from zero", "const int mant = (int)nearbyint((m - 1.0) * 8.0);",
+     "const int mant = (int)round((m - 1.0) * 8.0);"),
+    ("prep key row off by one", "const size_t kr = (size_t)b * Lmax + pos;",
+     "const size_t kr = (size_t)b * Lmax + pos - (pos > 0);"),
     ("fp8 latent queries not bf16", "const int qdt = dtype == ORC_FP8_LATENT ? ORC_BF16 : dtype;",
      "const int qdt = dtype == ORC_FP8_LATENT ? ORC_F32 : dtype;"),
     ("latent ignores visibility", "if (sel[j] >= 0 && sel[j] <= pos) keys[n++] = sel[j];",
@@ -61,7 +75,8 @@ MUTATIONS = [
 def _variant(orc, path):
     saved = orc._load()
     lib = ctypes.CDLL(path)
-    for fn in ("orc_e4m3fn_value", "orc_bf16_value", "orc_latent_fp8_value", "orc_index_scores", "orc_topk",
+    for fn in ("orc_e4m3fn_value", "orc_bf16_value", "orc_latent_fp8_value", "orc_e4m3fn_encode",
+               "orc_indexer_prep", "orc_index_scores", "orc_topk",
                "orc_sparse_mla_decode", "orc_sparse_mha_prefill", "orc_sparse_mha_prefill_dense",
                "orc_sparse_mha_prefill_rows",
                "orc_layer_step_latent", "orc_layer_step_mha", "orc_max_threads"):
