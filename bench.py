@@ -150,6 +150,35 @@ def cpu_baseline(cfg, n_seqs: int, min_seconds: float = 10.0, latent_form: str =
             "keys_scored_per_s": keys / dt}
 
 
+def measure_prep(D, S, cfg, n: int):
+    """The indexer preparation of the workload's new tokens (B*T of them: rope, rotation,
+    FP8 quantisation, key-cache append), timed alone with HIP events over n launches on
+    the current stream.  Not part of the layer step; reported beside it.  Algorithmic
+    bytes: the bf16 q and k rows and their rope angles read, the codes and scales written."""
+    import torch
+    c = S.make_prep_case(cfg)
+    d = S.to_device(c, "cuda")
+    R = cfg.rope_i
+    tokens = cfg.B * cfg.T
+    in_b = 2 if cfg.attn_dtype == "bf16" else 4
+    nbytes = tokens * ((cfg.H_I + 1) * cfg.D_I * (in_b + 1) + (cfg.H_I + 1) * 4 + R * 4)
+    run = lambda: D.indexer_prep(d["q"], d["k"], d["cos"], d["sin"], d["start"], R, d["k_cache"],
+                                 d["k_scale"])
+    q_fp8, q_scale = run()
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev0.record()
+    for _ in range(n):
+        D.indexer_prep(d["q"], d["k"], d["cos"], d["sin"], d["start"], R, d["k_cache"],
+                       d["k_scale"], q_fp8, q_scale)
+    ev1.record()
+    torch.cuda.synchronize()
+    ms = ev0.elapsed_time(ev1) / n
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    return {"tokens": tokens, "avg_launch_ms": round(ms, 5), "algorithmic_bytes_per_launch": nbytes,
+            "achieved_GBs": round(gbs, 1), "hbm_frac": round(gbs / HBM_PEAK_GBS, 4)}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -270,6 +299,9 @@ def main():
     phase_ms = {k: (v[0] / v[1] if v[1] else None) for k, v in prof.items()}
     print(f"[bench] phases (avg ms): {phase_ms}", file=sys.stderr, flush=True)
 
+    prep = measure_prep(D, S, cfg, args.steps)
+    print(f"[bench] indexer prep: {prep}", file=sys.stderr, flush=True)
+
     att_ms = phase_ms["attention"]
     idx_ms = phase_ms["index_scores"]
     att_gbs = costs["attention_bytes"] / (att_ms * 1e-3) / 1e9
@@ -334,6 +366,7 @@ def main():
                          "mfma_frac": round(idx_tfs / BF16_PEAK_TFLOPS, 4),
                          "keys_per_s": round(costs["keys"] / (idx_ms * 1e-3), 1)},
         "roofline": roofline,
+        "indexer_prep": prep,
         "cpu_baseline": None if args.no_cpu else cpu_baseline(cfg, args.cpu_seqs, args.cpu_seconds,
                                                               args.latent),
     }

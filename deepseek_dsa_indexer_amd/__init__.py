@@ -3,6 +3,8 @@
 The computation lives in ``libdsa_amd.so`` (HIP kernels behind the C ABI of
 ``include/dsa.h``); this package is its Python binding:
 
+    indexer_prep(q, k, rope_cos, rope_sin, start, rope_dim, k_cache, k_scale)
+                                                                         -> (q_fp8, q_scale)
     index_scores(q_fp8, q_scale, w, k_fp8, k_scale, lens, sm_scale_i)  -> scores
     topk(scores, lens, k)                                                -> idx
     sparse_mla_decode(q, latent, idx, lens, Dv, sm_scale)                -> (out, lse)
@@ -13,8 +15,8 @@ The computation lives in ``libdsa_amd.so`` (HIP kernels behind the C ABI of
 
 Build the library with ``python -m deepseek_dsa_indexer_amd.build``.
 """
-from ._native import (DSAError, LayerStep, index_scores, library_path, load, profile_begin,
-                      profile_end, sparse_mla_decode, sparse_mla_prefill, topk)
+from ._native import (DSAError, LayerStep, index_scores, indexer_prep, library_path, load,
+                      profile_begin, profile_end, sparse_mla_decode, sparse_mla_prefill, topk)
 
-__all__ = ["DSAError", "LayerStep", "index_scores", "library_path", "load", "profile_begin",
-           "profile_end", "sparse_mla_decode", "sparse_mla_prefill", "topk"]
+__all__ = ["DSAError", "LayerStep", "index_scores", "indexer_prep", "library_path", "load",
+           "profile_begin", "profile_end", "sparse_mla_decode", "sparse_mla_prefill", "topk"]

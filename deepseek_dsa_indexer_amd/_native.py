@@ -21,7 +21,8 @@ DSA_ATTN_LATENT, DSA_ATTN_MHA = 0, 1
 STATUS_NAMES = {0: "DSA_OK", 1: "DSA_ERR_NULL", 2: "DSA_ERR_SHAPE", 3: "DSA_ERR_DTYPE",
                 4: "DSA_ERR_ALIGN", 5: "DSA_ERR_WORKSPACE", 6: "DSA_ERR_HIP"}
 
-EXPORTED = ["dsa_last_error", "dsa_version", "dsa_index_scores", "dsa_topk_workspace_bytes",
+EXPORTED = ["dsa_last_error", "dsa_version", "dsa_indexer_prep", "dsa_index_scores",
+            "dsa_topk_workspace_bytes",
             "dsa_topk", "dsa_sparse_mla_decode_workspace_bytes", "dsa_sparse_mla_decode",
             "dsa_sparse_mla_prefill_workspace_bytes", "dsa_sparse_mla_prefill",
             "dsa_layer_step_workspace_bytes", "dsa_layer_step", "dsa_profile_begin",
@@ -73,6 +74,7 @@ def load():
     lib.dsa_last_error.argtypes = []
     lib.dsa_version.restype = I
     lib.dsa_version.argtypes = []
+    lib.dsa_indexer_prep.argtypes = [P, P, I, P, P, I, P, I, I, I, I, I, I, P, P, P, P, P]
     lib.dsa_index_scores.argtypes = [P, P, P, P, P, P, I, I, I, I, I, F, P, P]
     lib.dsa_topk_workspace_bytes.argtypes = [I, I, I, I]
     lib.dsa_topk_workspace_bytes.restype = Z
@@ -88,7 +90,8 @@ def load():
     lib.dsa_layer_step.argtypes = [ctypes.POINTER(LayerArgs), P, Z, P]
     lib.dsa_profile_begin.argtypes = [I]
     lib.dsa_profile_end.argtypes = [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(I)]
-    for fn in ("dsa_index_scores", "dsa_topk", "dsa_sparse_mla_decode", "dsa_sparse_mla_prefill",
+    for fn in ("dsa_indexer_prep", "dsa_index_scores", "dsa_topk", "dsa_sparse_mla_decode",
+               "dsa_sparse_mla_prefill",
                "dsa_layer_step", "dsa_profile_begin", "dsa_profile_end"):
         getattr(lib, fn).restype = I
     _lib = lib
@@ -148,6 +151,37 @@ def _workspace(nbytes: int, device):
     if nbytes == 0:
         return None
     return torch.empty(nbytes, dtype=torch.uint8, device=device)
+
+
+def indexer_prep(q, k, rope_cos, rope_sin, start, rope_dim, k_cache, k_scale, q_fp8=None,
+                 q_scale=None):
+    """Rope + rotation + FP8 quantisation of the new tokens' indexer queries q [B,T,H,D]
+    and keys k [B,T,D] (bf16 or f32); the key codes and scales are written into
+    k_cache [B,Lmax,D] / k_scale [B,Lmax] at positions start[b] + t.  Returns
+    (q_fp8 [B,T,H,D] u8, q_scale [B,T,H] f32)."""
+    dt = _attn_dtype(q)
+    _need(q, q.dtype, "q")
+    _need(k, q.dtype, "k")
+    _need(start, torch.int32, "start")
+    k_cache = _fp8(k_cache, "k_cache")
+    _need(k_scale, torch.float32, "k_scale")
+    if rope_dim:
+        _need(rope_cos, torch.float32, "rope_cos")
+        _need(rope_sin, torch.float32, "rope_sin")
+        P = rope_cos.shape[0]
+    else:
+        P = k_cache.shape[1]
+    B, T, H, D = q.shape
+    Lmax = k_cache.shape[1]
+    if q_fp8 is None:
+        q_fp8 = torch.empty((B, T, H, D), dtype=torch.uint8, device=q.device)
+    if q_scale is None:
+        q_scale = torch.empty((B, T, H), dtype=torch.float32, device=q.device)
+    _check(load().dsa_indexer_prep(_ptr(q), _ptr(k), dt, _ptr(rope_cos) if rope_dim else None,
+                                   _ptr(rope_sin) if rope_dim else None, P, _ptr(start), B, T, H,
+                                   D, int(rope_dim), Lmax, _ptr(q_fp8), _ptr(q_scale),
+                                   _ptr(k_cache), _ptr(k_scale), _stream(q.device)))
+    return q_fp8, q_scale
 
 
 def index_scores(q_fp8, q_scale, w, k_fp8, k_scale, lens, sm_scale_i, scores=None):

@@ -16,8 +16,8 @@ CSRC = os.path.join(PKG, "csrc")
 OUT = os.path.join(PKG, "libdsa_amd.so")
 BUILD_DIR = os.path.join(ROOT, "_build")
 
-SOURCES = ["index_scores.hip", "topk.hip", "sparse_attn.hip", "sparse_mha_prefill.hip",
-           "dsa_abi.cpp"]
+SOURCES = ["indexer_prep.hip", "index_scores.hip", "topk.hip", "sparse_attn.hip",
+           "sparse_mha_prefill.hip", "dsa_abi.cpp"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"

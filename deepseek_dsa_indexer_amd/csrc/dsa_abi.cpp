@@ -248,6 +248,32 @@ const char* dsa_last_error(void) { return g_last_error.c_str(); }
 
 int dsa_version(void) { return 100; }
 
+dsa_status dsa_indexer_prep(const void* q, const void* k, dsa_dtype dt, const float* rope_cos,
+                            const float* rope_sin, int P, const int32_t* start, int B, int T,
+                            int H_I, int d_I, int rope_dim, int Lmax, uint8_t* q_fp8,
+                            float* q_scale, uint8_t* k_cache, float* k_scale, hipStream_t stream) {
+    DSA_REQUIRE(q && k && start && q_fp8 && q_scale && k_cache && k_scale, DSA_ERR_NULL,
+                "indexer prep: NULL pointer");
+    DSA_REQUIRE(rope_dim == 0 || (rope_cos && rope_sin), DSA_ERR_NULL, "indexer prep: NULL rope table");
+    DSA_REQUIRE(dt == DSA_F32 || dt == DSA_BF16, DSA_ERR_DTYPE, "indexer prep: bad dtype %d",
+                static_cast<int>(dt));
+    DSA_REQUIRE(B >= 1 && T >= 1 && Lmax >= 1 && T <= Lmax && P >= 1, DSA_ERR_SHAPE,
+                "indexer prep: need B, T, P >= 1 and T <= Lmax (B=%d T=%d P=%d Lmax=%d)", B, T, P, Lmax);
+    DSA_REQUIRE(static_cast<long long>(B) * T <= kMaxRows, DSA_ERR_SHAPE, "indexer prep: B*T too large");
+    DSA_REQUIRE(H_I >= 1 && H_I <= 64, DSA_ERR_SHAPE, "indexer prep: H_I=%d not in [1, 64]", H_I);
+    DSA_REQUIRE(d_I == 32 || d_I == 64 || d_I == 128, DSA_ERR_SHAPE,
+                "indexer prep: d_I=%d not in {32, 64, 128}", d_I);
+    DSA_REQUIRE(rope_dim >= 0 && rope_dim <= d_I && rope_dim % 4 == 0, DSA_ERR_SHAPE,
+                "indexer prep: rope_dim=%d must be a multiple of 4 in [0, d_I]", rope_dim);
+    DSA_REQUIRE(aligned16(q) && aligned16(k) && aligned16(start) && aligned16(q_fp8) &&
+                    aligned16(q_scale) && aligned16(k_cache) && aligned16(k_scale) &&
+                    (rope_dim == 0 || (aligned16(rope_cos) && aligned16(rope_sin))),
+                DSA_ERR_ALIGN, "indexer prep: pointers must be 16-byte aligned");
+    dsa::IndexerPrepArgs a{q, k, dt == DSA_BF16, rope_cos, rope_sin, P, start, B, T, H_I, d_I,
+                           rope_dim, Lmax, q_fp8, q_scale, k_cache, k_scale};
+    return hip_status(dsa::launch_indexer_prep(a, stream), "indexer prep");
+}
+
 dsa_status dsa_index_scores(const uint8_t* q_fp8, const float* q_scale, const float* w,
                             const uint8_t* k_fp8, const float* k_scale, const int32_t* len, int B,
                             int T, int H_I, int d_I, int Lmax, float sm_scale_I, float* scores,

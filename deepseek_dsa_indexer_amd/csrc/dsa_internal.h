@@ -29,6 +29,24 @@ struct IndexScoresArgs {
 };
 hipError_t launch_index_scores(const IndexScoresArgs& a, hipStream_t stream);
 
+// Indexer preparation of the T new tokens of each sequence (rope, rotation, FP8
+// quantisation, key-cache append); token t of sequence b sits at position start[b] + t.
+struct IndexerPrepArgs {
+    const void* q;          // [B,T,H,D] bf16 or f32
+    const void* k;          // [B,T,D]
+    int bf16;
+    const float* cos;       // [P, R/2]
+    const float* sin;       // [P, R/2]
+    int P;
+    const int32_t* start;   // [B]
+    int B, T, H, D, R, Lmax;
+    uint8_t* q_fp8;         // [B,T,H,D]
+    float* q_scale;         // [B,T,H]
+    uint8_t* k_cache;       // [B,Lmax,D]
+    float* k_scale;         // [B,Lmax]
+};
+hipError_t launch_indexer_prep(const IndexerPrepArgs& a, hipStream_t stream);
+
 struct TopkArgs {
     const float* scores;
     const int32_t* len;

@@ -74,6 +74,35 @@ const char* dsa_last_error(void);
 int dsa_version(void);
 
 /*
+ * dsa_indexer_prep -- the indexer's preparation of T new tokens per sequence, between the
+ * projections and the scores ("Split indexer heads": Indexer.forward applies rope to the
+ * leading rope columns without interleaving, then rotate_activation, then act_quant to
+ * FP8 with one scale per block, and writes the keys into the key cache; the bodies of
+ * those steps are not on the pages, so they are read as follows):
+ *   rope      column j < rope_dim/2 of a row pairs with column j + rope_dim/2 and the pair
+ *             (a, b) becomes (a c - b s, a s + b c), c/s = rope_cos/rope_sin[pos][j];
+ *   rotation  the orthonormal Walsh-Hadamard transform of the d_I-wide row (Sylvester
+ *             order: out_i = d_I^-1/2 sum_j (-1)^popcount(i & j) in_j);
+ *   act_quant scale = max(amax, 1e-12) / 448 per row (fp32), code = e4m3fn nearest to
+ *             clamp(x / scale, +-448), ties to even, sign from x.
+ * All arithmetic is fp32; a value within fp32 rounding of a midpoint between two e4m3fn
+ * values may take either neighbour.
+ *   q        [B,T,H_I,d_I] (dtype F32 or BF16) projected indexer queries, rope columns first
+ *   k        [B,T,d_I] normalised indexer keys of the new tokens, rope columns first
+ *   rope_cos, rope_sin [P, rope_dim/2] f32 (may be NULL when rope_dim = 0)
+ *   start    [B] i32: token t of sequence b sits at position start[b] + t
+ *   q_fp8    [B,T,H_I,d_I] u8, q_scale [B,T,H_I] f32 (outputs: the inputs of dsa_index_scores)
+ *   k_cache  [B,Lmax,d_I] u8, k_scale [B,Lmax] f32: rows start[b] .. start[b]+T-1 are
+ *            written, every other row is left as it is.
+ * Supported: 1 <= H_I <= 64, d_I in {32, 64, 128}, rope_dim a multiple of 4 in [0, d_I].
+ * A token whose position is outside [0, min(P, Lmax)) is skipped (device-side check).
+ */
+dsa_status dsa_indexer_prep(const void* q, const void* k, dsa_dtype dt, const float* rope_cos,
+                            const float* rope_sin, int P, const int32_t* start, int B, int T,
+                            int H_I, int d_I, int rope_dim, int Lmax, uint8_t* q_fp8,
+                            float* q_scale, uint8_t* k_cache, float* k_scale, hipStream_t stream);
+
+/*
  * dsa_index_scores -- lightning-indexer scores with the causal mask applied.
  *   scores[b,t,s] = k_scale[b,s] * sum_h (w[b,t,h] * q_scale[b,t,h] * sm_scale_I)
  *                                     * max(0, sum_d q[b,t,h,d] * k[b,s,d])

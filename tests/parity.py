@@ -10,7 +10,11 @@
     have oracle scores within 1e-3 (relative, same row floor) of the oracle's k-th
     largest score tau;
   * attention outputs: |g - o| <= 2e-2 (bf16 inputs/outputs) or 1e-4 (fp32), lse
-    within 1e-3 (bf16) or 1e-5 (fp32) absolute, compared on the same indices.
+    within 1e-3 (bf16) or 1e-5 (fp32) absolute, compared on the same indices;
+  * indexer preparation: scales within 2e-6 relative; every FP8 code decodes to the
+    oracle's nearest e4m3fn value of its pre-rounding value y, except that where y lies
+    within 2e-3 of the midpoint between two e4m3fn values (the fp32 rotation's error
+    bound, in units of y) the other neighbour is accepted too.
 """
 from __future__ import annotations
 
@@ -91,3 +95,39 @@ def check_attention(out_g, lse_g, out_o, lse_o, dtype: str):
             lerr = np.abs(lse_g[fin] - lse_o[fin])
             assert lerr.max() <= LSE_ATOL[dtype], f"lse max abs err {lerr.max()}"
     return float(err.max())
+
+
+PREP_SCALE_RTOL = 2e-6
+PREP_MID_TOL = 2e-3
+
+
+def _e4m3_decode(codes):
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(codes, dtype=np.uint8)).view(torch.float8_e4m3fn).double().numpy()
+
+
+def check_prep(codes_g, scale_g, y_o, scale_o):
+    """GPU codes/scales of the indexer preparation against the oracle's pre-rounding
+    values y_o (x / scale in float64) and scales; returns the number of codes that took
+    the other neighbour at a midpoint."""
+    scale_g = np.asarray(scale_g, np.float64)
+    rel = np.abs(scale_g - scale_o) / scale_o
+    assert rel.max() <= PREP_SCALE_RTOL, f"prep scale rel err {rel.max()}"
+    grid = _e4m3_decode(np.arange(0, 0x7F, dtype=np.uint8))          # 0 .. 448 ascending
+    y = np.clip(np.asarray(y_o, np.float64), -448.0, 448.0)
+    a = np.abs(y)
+    hi = np.clip(np.searchsorted(grid, a), 1, len(grid) - 1)
+    lo_v, hi_v = grid[hi - 1], grid[hi]
+    mid = (lo_v + hi_v) / 2
+    # nearest, ties to the even code (codes of lo_v and hi_v are hi - 1 and hi)
+    near = np.where(a < mid, lo_v, np.where(a > mid, hi_v, np.where((hi - 1) % 2 == 0, lo_v, hi_v)))
+    other = np.where(near == lo_v, hi_v, lo_v)
+    dec = np.abs(_e4m3_decode(codes_g))
+    sign_ok = (dec == 0) | (np.signbit(_e4m3_decode(codes_g)) == np.signbit(y)) | (near == 0)
+    exact = dec == near
+    at_mid = (np.abs(a - mid) <= PREP_MID_TOL) & (dec == other)
+    ok = (exact | at_mid) & sign_ok
+    bad = np.flatnonzero(~ok.ravel())
+    assert bad.size == 0, (f"prep codes: {bad.size} mismatches, first at flat {bad[:5]}: "
+                           f"y={y.ravel()[bad[:5]]} gpu={dec.ravel()[bad[:5]]} want={near.ravel()[bad[:5]]}")
+    return int(np.count_nonzero(at_mid & ~exact))

@@ -136,3 +136,23 @@ def test_fp8_latent_validation(lib):
     st = lib.dsa_sparse_mla_prefill(p, p, p, p, 1, 8, 2, 192, 128, 64, 0.1, F8, p, None, None, 0,
                                     None)
     assert st == 3
+
+
+def test_indexer_prep_validation(lib):
+    p = _fake()
+    args = lambda **kw: [kw.get("q", p), p, kw.get("dt", N.DSA_BF16), p, p, kw.get("P", 100), p,
+                         kw.get("B", 2), kw.get("T", 1), kw.get("H", 64), kw.get("D", 128),
+                         kw.get("R", 64), kw.get("Lmax", 100), p, p, p, p, None]
+    assert lib.dsa_indexer_prep(*args(q=None)) == 1
+    assert lib.dsa_indexer_prep(*args(dt=N.DSA_FP8_LATENT)) == 3
+    assert lib.dsa_indexer_prep(*args(D=96)) == 2
+    assert lib.dsa_indexer_prep(*args(H=65)) == 2
+    assert lib.dsa_indexer_prep(*args(R=62)) == 2 and b"rope_dim" in lib.dsa_last_error()
+    assert lib.dsa_indexer_prep(*args(R=132)) == 2
+    assert lib.dsa_indexer_prep(*args(T=101)) == 2
+    assert lib.dsa_indexer_prep(*args(q=_fake(0x10008))) == 4
+    # no rope: the tables may be NULL (validation passes through to the alignment checks)
+    a = args(R=0)
+    a[3] = a[4] = None
+    a[0] = _fake(0x10008)
+    assert lib.dsa_indexer_prep(*a) == 4

@@ -11,7 +11,7 @@ import pytest
 import torch
 
 import dsa_synth as S
-from parity import check_attention, check_scores, check_topk
+from parity import check_attention, check_prep, check_scores, check_topk
 
 pytestmark = pytest.mark.gpu
 
@@ -42,6 +42,44 @@ def _np_out(t):
 def _say(msg):
     print(msg, flush=True)
     sys.stdout.flush()
+
+
+# ----------------------------------------------------------------------------- indexer preparation
+
+PREP_CASES = [
+    ("decode_small", _small("decode_v32", name="pds", B=3, Lmax=300, seed=301)),
+    ("ragged_t3_student", _small("decode_ragged", name="prs", B=4, T=3, Lmax=2000,
+                                 lens="ragged:3:2000", seed=302)),
+    ("tiny_f32_d32", _small("tiny")),
+    ("d64_rope16", _small("decode_v32", name="pd64", B=2, T=2, Lmax=90, H_I=16, D_I=64,
+                          rope_i=16, seed=303)),
+    ("no_rope", _small("decode_v32", name="pnr", B=2, Lmax=64, rope_i=0, seed=304)),
+]
+
+
+@pytest.mark.parametrize("name,cfg", PREP_CASES, ids=[c[0] for c in PREP_CASES])
+def test_indexer_prep(dsa, orc, name, cfg):
+    _say(f"[indexer_prep] {name}")
+    c = S.make_prep_case(cfg)
+    d = _dev(c)
+    R = cfg.rope_i
+    q_fp8, q_scale = dsa.indexer_prep(d["q"], d["k"], d["cos"], d["sin"], d["start"], R,
+                                      d["k_cache"], d["k_scale"])
+    torch.cuda.synchronize()
+    r = orc.indexer_prep(c["q"], c["k"], c["cos"], c["sin"], c["start"], R, c["k_cache"],
+                         c["k_scale"])
+    swaps = check_prep(q_fp8.cpu().numpy(), q_scale.cpu().numpy(), r["q_y"], r["q_scale"])
+    kc, ks = d["k_cache"].cpu().numpy(), d["k_scale"].cpu().numpy()
+    st, T = c["start"], cfg.T
+    rows = np.stack([kc[b, st[b]:st[b] + T] for b in range(len(st))])
+    scales = np.stack([ks[b, st[b]:st[b] + T] for b in range(len(st))])
+    swaps += check_prep(rows, scales, r["k_y"], r["k_scale64"])
+    for b in range(len(st)):
+        keep = np.ones(cfg.Lmax, bool)
+        keep[st[b]:st[b] + T] = False
+        assert np.array_equal(kc[b, keep], c["k_cache"][b, keep]), "cache rows outside the new tokens changed"
+        assert np.array_equal(ks[b, keep], c["k_scale"][b, keep])
+    _say(f"[indexer_prep] {name}: {swaps} codes took the other neighbour at a midpoint")
 
 
 # ----------------------------------------------------------------------------- index scores
