@@ -259,7 +259,8 @@ dsa_status dsa_indexer_prep(const void* q, const void* k, dsa_dtype dt, const fl
                 static_cast<int>(dt));
     DSA_REQUIRE(B >= 1 && T >= 1 && Lmax >= 1 && T <= Lmax && P >= 1, DSA_ERR_SHAPE,
                 "indexer prep: need B, T, P >= 1 and T <= Lmax (B=%d T=%d P=%d Lmax=%d)", B, T, P, Lmax);
-    DSA_REQUIRE(static_cast<long long>(B) * T <= kMaxRows, DSA_ERR_SHAPE, "indexer prep: B*T too large");
+    DSA_REQUIRE(static_cast<long long>(B) * T <= (1LL << 26), DSA_ERR_SHAPE,
+                "indexer prep: B*T too large (one wave per row, at most 2^26 tokens)");
     DSA_REQUIRE(H_I >= 1 && H_I <= 64, DSA_ERR_SHAPE, "indexer prep: H_I=%d not in [1, 64]", H_I);
     DSA_REQUIRE(d_I == 32 || d_I == 64 || d_I == 128, DSA_ERR_SHAPE,
                 "indexer prep: d_I=%d not in {32, 64, 128}", d_I);

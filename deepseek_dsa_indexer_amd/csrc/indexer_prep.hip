@@ -7,7 +7,7 @@
 // to the nearest e4m3fn value, ties to even); the key codes and scale are written into
 // the key cache at the token's position.
 //
-// One wave per row (64 query heads + the key at the V3.2 sizes), fp32 throughout.  A
+// One wave per row (64 query heads + the key per token at the V3.2 sizes), fp32.  A
 // lane holds EPL = max(1, D / 64) neighbouring columns, so the Walsh-Hadamard butterflies
 // of distance < EPL stay in the lane and the others pair lane l with lane l ^ (dist /
 // EPL).  HBM-bound and tiny: per token 16 KB of bf16 queries read, 8 KB of codes written.
@@ -116,37 +116,41 @@ __device__ __forceinline__ float prep_row(const void* src, size_t off, int bf16,
     return scale;
 }
 
-// One workgroup per new token (b, t): waves take the H query rows and the key row in turn.
+// One wave per row: the H query rows of token (b, t) and then its key row, so that every
+// row's loads are in flight at once (a row is one memory latency plus a few hundred
+// cycles of shuffles; walking rows one after another per wave made the step latency-bound).
 template <int D>
 __global__ __launch_bounds__(kPrepThreads)
 void indexer_prep_kernel(IndexerPrepArgs a) {
-    const int row = blockIdx.x;                        // b * T + t
-    const int b = row / a.T;
-    const int t = row - b * a.T;
     const int lane = threadIdx.x & (kWave - 1);
-    const int wave = threadIdx.x / kWave;
+    const long long gr = static_cast<long long>(blockIdx.x) * kPrepWaves + threadIdx.x / kWave;
+    const int rows_per_token = a.H + 1;
+    if (gr >= static_cast<long long>(a.B) * a.T * rows_per_token) return;
+    const int token = static_cast<int>(gr / rows_per_token);   // b * T + t
+    const int r = static_cast<int>(gr - static_cast<long long>(token) * rows_per_token);
+    const int b = token / a.T;
+    const int t = token - b * a.T;
     const int pos = a.start[b] + t;
     if (pos < 0 || pos >= a.P || pos >= a.Lmax) return;   // outside the tables or the cache
     const float* cs = a.cos + static_cast<size_t>(pos) * (a.R / 2);
     const float* sn = a.sin + static_cast<size_t>(pos) * (a.R / 2);
-    for (int r = wave; r <= a.H; r += kPrepWaves) {
-        if (r < a.H) {
-            const size_t qr = static_cast<size_t>(row) * a.H + r;
-            const float sc = prep_row<D>(a.q, qr * D, a.bf16, cs, sn, a.R, lane, a.q_fp8 + qr * D);
-            if (lane == 0) a.q_scale[qr] = sc;
-        } else {
-            const size_t kr = static_cast<size_t>(b) * a.Lmax + pos;
-            const float sc = prep_row<D>(a.k, static_cast<size_t>(row) * D, a.bf16, cs, sn, a.R, lane,
-                                         a.k_cache + kr * D);
-            if (lane == 0) a.k_scale[kr] = sc;
-        }
+    if (r < a.H) {
+        const size_t qr = static_cast<size_t>(token) * a.H + r;
+        const float sc = prep_row<D>(a.q, qr * D, a.bf16, cs, sn, a.R, lane, a.q_fp8 + qr * D);
+        if (lane == 0) a.q_scale[qr] = sc;
+    } else {
+        const size_t kr = static_cast<size_t>(b) * a.Lmax + pos;
+        const float sc = prep_row<D>(a.k, static_cast<size_t>(token) * D, a.bf16, cs, sn, a.R, lane,
+                                     a.k_cache + kr * D);
+        if (lane == 0) a.k_scale[kr] = sc;
     }
 }
 
 }  // namespace
 
 hipError_t launch_indexer_prep(const IndexerPrepArgs& a, hipStream_t stream) {
-    const dim3 grid(a.B * a.T), block(kPrepThreads);
+    const long long rows = static_cast<long long>(a.B) * a.T * (a.H + 1);
+    const dim3 grid(static_cast<unsigned>((rows + kPrepWaves - 1) / kPrepWaves)), block(kPrepThreads);
     switch (a.D) {
     case 32: hipLaunchKernelGGL(indexer_prep_kernel<32>, grid, block, 0, stream, a); break;
     case 64: hipLaunchKernelGGL(indexer_prep_kernel<64>, grid, block, 0, stream, a); break;
