@@ -264,8 +264,9 @@ dsa_status dsa_indexer_prep(const void* q, const void* k, dsa_dtype dt, const fl
     DSA_REQUIRE(H_I >= 1 && H_I <= 64, DSA_ERR_SHAPE, "indexer prep: H_I=%d not in [1, 64]", H_I);
     DSA_REQUIRE(d_I == 32 || d_I == 64 || d_I == 128, DSA_ERR_SHAPE,
                 "indexer prep: d_I=%d not in {32, 64, 128}", d_I);
-    DSA_REQUIRE(rope_dim >= 0 && rope_dim <= d_I && rope_dim % 4 == 0, DSA_ERR_SHAPE,
-                "indexer prep: rope_dim=%d must be a multiple of 4 in [0, d_I]", rope_dim);
+    DSA_REQUIRE(rope_dim == 0 || (rope_dim >= 4 && rope_dim <= d_I && (rope_dim & (rope_dim - 1)) == 0),
+                DSA_ERR_SHAPE, "indexer prep: rope_dim=%d must be 0 or a power of two in [4, d_I]",
+                rope_dim);
     DSA_REQUIRE(aligned16(q) && aligned16(k) && aligned16(start) && aligned16(q_fp8) &&
                     aligned16(q_scale) && aligned16(k_cache) && aligned16(k_scale) &&
                     (rope_dim == 0 || (aligned16(rope_cos) && aligned16(rope_sin))),

@@ -7,10 +7,9 @@
 // to the nearest e4m3fn value, ties to even); the key codes and scale are written into
 // the key cache at the token's position.
 //
-// One wave per row (64 query heads + the key per token at the V3.2 sizes), fp32.  A
-// lane holds EPL = max(1, D / 64) neighbouring columns, so the Walsh-Hadamard butterflies
-// of distance < EPL stay in the lane and the others pair lane l with lane l ^ (dist /
-// EPL).  HBM-bound and tiny: per token 16 KB of bf16 queries read, 8 KB of codes written.
+// Rows (64 query heads + the key per token at the V3.2 sizes) go to groups of D / 8 lanes,
+// fp32 throughout; cross-lane steps are DPP moves inside 16-lane rows.  HBM-bound: per
+// token 16 KB of bf16 queries read, 8 KB of codes written.
 #include "dsa_device.h"
 #include "dsa_internal.h"
 
@@ -43,114 +42,166 @@ __device__ __forceinline__ uint32_t e4m3fn_code(float y) {
     return sign | mag;
 }
 
-__device__ __forceinline__ float ld_in(const void* p, size_t i, int bf16) {
-    return bf16 ? bf16_to_f32(static_cast<const uint16_t*>(p)[i]) : static_cast<const float*>(p)[i];
+// Value of lane l ^ M within its row of 16 lanes (M = 1, 2, 4, 8), by DPP moves: quad
+// permutations for 1 and 2; a half-row mirror (l ^ 7) then a quad reversal (l ^ 3) for 4;
+// a row mirror (l ^ 15) then a half-row mirror for 8.
+template <int M>
+__device__ __forceinline__ float xor_lane(float v) {
+    const int x = __float_as_int(v);
+    if constexpr (M == 1) return __int_as_float(__builtin_amdgcn_mov_dpp(x, 0xB1, 0xf, 0xf, false));
+    else if constexpr (M == 2) return __int_as_float(__builtin_amdgcn_mov_dpp(x, 0x4E, 0xf, 0xf, false));
+    else if constexpr (M == 4)
+        return __int_as_float(__builtin_amdgcn_mov_dpp(__builtin_amdgcn_mov_dpp(x, 0x141, 0xf, 0xf, false),
+                                                       0x1B, 0xf, 0xf, false));
+    else
+        return __int_as_float(__builtin_amdgcn_mov_dpp(__builtin_amdgcn_mov_dpp(x, 0x140, 0xf, 0xf, false),
+                                                       0x141, 0xf, 0xf, false));
 }
 
-// One row: rope, rotation, quantisation.  src: D input values (bf16 or f32); codes: D
-// bytes out; returns the scale (every lane).
-template <int D>
-__device__ __forceinline__ float prep_row(const void* src, size_t off, int bf16, const float* cs,
-                                          const float* sn, int R, int lane, uint8_t* codes) {
-    constexpr int EPL = D >= 64 ? D / 64 : 1;
-    constexpr int kLanes = D / EPL;                   // lanes that hold columns
-    const bool holds = lane < kLanes;
-    float v[EPL];
-#pragma unroll
-    for (int i = 0; i < EPL; ++i)
-        v[i] = holds ? ld_in(src, off + EPL * lane + i, bf16) : 0.f;
-    // rope: column e < R/2 pairs with e + R/2 (same slot i in lane (e + R/2) / EPL)
-    const int half = R / 2;
-#pragma unroll
-    for (int i = 0; i < EPL; ++i) {
-        const int e = EPL * lane + i;
-        const bool lo = e < half;
-        const int pe = lo ? e + half : e - half;
-        const float p = __shfl(v[i], (e < R ? pe : e) / EPL);
-        if (holds && e < R) {
-            const int j = lo ? e : pe;
-            const float c = cs[j], s = sn[j];
-            v[i] = lo ? v[i] * c - p * s : p * s + v[i] * c;
-        }
+__device__ __forceinline__ float xor_lane_rt(float v, int m) {
+    switch (m) {
+    case 1: return xor_lane<1>(v);
+    case 2: return xor_lane<2>(v);
+    case 4: return xor_lane<4>(v);
+    default: return xor_lane<8>(v);
     }
-    // Walsh-Hadamard butterflies: the lower column of each pair gets a + b, the upper a - b
+}
+
+// Rows of D values are handled by groups of D / 8 lanes, lane n of a group holding
+// columns 8n .. 8n+7, so a wave prepares 64 / (D / 8) rows at once: butterflies of
+// distance 1, 2, 4 stay in the lane, distance 8m pairs lane n with lane n ^ m.
+template <int D>
+__global__ __launch_bounds__(kPrepThreads)
+void indexer_prep_kernel(IndexerPrepArgs a) {
+    constexpr int LPR = D / 8;                        // lanes per row
+    constexpr int RPW = kWave / LPR;                  // rows per wave
+    const int lane = threadIdx.x & (kWave - 1);
+    const int n = lane % LPR;
+    const long long gr = (static_cast<long long>(blockIdx.x) * kPrepWaves + threadIdx.x / kWave) * RPW +
+                         lane / LPR;
+    const int rows_per_token = a.H + 1;
+    const long long n_rows = static_cast<long long>(a.B) * a.T * rows_per_token;
+    bool live = gr < n_rows;
+    const int token = live ? static_cast<int>(gr / rows_per_token) : 0;   // b * T + t
+    const int r = live ? static_cast<int>(gr - static_cast<long long>(token) * rows_per_token) : 0;
+    const int b = token / a.T;
+    const int t = token - b * a.T;
+    const int pos = a.start[b] + t;
+    live = live && pos >= 0 && pos < a.P && pos < a.Lmax;   // outside the tables or the cache: skip
+    const bool is_key = r == a.H;
+    const void* src = is_key ? a.k : a.q;
+    const size_t off = (is_key ? static_cast<size_t>(token) : static_cast<size_t>(token) * a.H + r) * D + 8 * n;
+
+    float v[8];
+    if (live) {
+        if (a.bf16) {
+            const uint4 w = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(src) + off);
+            const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
 #pragma unroll
-    for (int dist = 1; dist < D; dist <<= 1) {
-        if (dist < EPL) {
-#pragma unroll
-            for (int i = 0; i < EPL; ++i) {
-                if (i & dist) continue;
-                const float a = v[i], b = v[i + dist];
-                v[i] = a + b;
-                v[i + dist] = a - b;
+            for (int i = 0; i < 4; ++i) {
+                v[2 * i] = __uint_as_float(ws[i] << 16);
+                v[2 * i + 1] = __uint_as_float(ws[i] & 0xffff0000u);
             }
         } else {
-            const int ld = dist / EPL;
-            const bool upper = (lane & ld) != 0;
+            const float4 lo = *reinterpret_cast<const float4*>(static_cast<const float*>(src) + off);
+            const float4 hi = *reinterpret_cast<const float4*>(static_cast<const float*>(src) + off + 4);
+            v[0] = lo.x; v[1] = lo.y; v[2] = lo.z; v[3] = lo.w;
+            v[4] = hi.x; v[5] = hi.y; v[6] = hi.z; v[7] = hi.w;
+        }
+    } else {
 #pragma unroll
-            for (int i = 0; i < EPL; ++i) {
-                const float p = __shfl_xor(v[i], ld);
-                v[i] = upper ? p - v[i] : v[i] + p;
+        for (int i = 0; i < 8; ++i) v[i] = 0.f;
+    }
+
+    // rope: column e < R/2 pairs with e + R/2
+    const int R = a.R;
+    const float* cs = a.cos + static_cast<size_t>(pos) * (R / 2);
+    const float* sn = a.sin + static_cast<size_t>(pos) * (R / 2);
+    if (R >= 16) {
+        const int m = R / 16;                         // partner lane distance (power of two)
+        float p[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) p[i] = xor_lane_rt(v[i], m);
+        if (live && 8 * n < R) {
+            const bool lo = 8 * n < R / 2;
+            const int j0 = lo ? 8 * n : 8 * n - R / 2;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const float c = cs[j0 + i], s = sn[j0 + i];
+                v[i] = lo ? v[i] * c - p[i] * s : p[i] * s + v[i] * c;
             }
+        }
+    } else if (R > 0 && live && n == 0) {             // R = 4 or 8: the pairs sit in lane 0
+        const int h = R / 2;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            if (i < h) {
+                const float c = cs[i], s = sn[i];
+                const float x0 = v[i], x1 = v[i + h];
+                v[i] = x0 * c - x1 * s;
+                v[i + h] = x0 * s + x1 * c;
+            }
+        }
+    }
+
+    // Walsh-Hadamard butterflies: the lower column of each pair gets a + b, the upper a - b
+#pragma unroll
+    for (int dist = 1; dist < 8; dist <<= 1)
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            if (i & dist) continue;
+            const float x0 = v[i], x1 = v[i + dist];
+            v[i] = x0 + x1;
+            v[i + dist] = x0 - x1;
+        }
+#pragma unroll
+    for (int m = 1; m < LPR; m <<= 1) {
+        const bool upper = (n & m) != 0;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const float p = xor_lane_rt(v[i], m);
+            v[i] = upper ? p - v[i] : v[i] + p;
         }
     }
     const float norm = 1.0f / __builtin_sqrtf(static_cast<float>(D));
     float amax = 0.f;
 #pragma unroll
-    for (int i = 0; i < EPL; ++i) {
+    for (int i = 0; i < 8; ++i) {
         v[i] *= norm;
         amax = fmaxf(amax, fabsf(v[i]));
     }
-    amax = wave_max(amax);
-    const float scale = __fdiv_rn(fmaxf(amax, 1e-12f), 448.0f);
-    uint32_t packed = 0;
 #pragma unroll
-    for (int i = 0; i < EPL; ++i) {
+    for (int m = 1; m < LPR; m <<= 1) amax = fmaxf(amax, xor_lane_rt(amax, m));
+    const float scale = __fdiv_rn(fmaxf(amax, 1e-12f), 448.0f);
+    uint32_t c0 = 0, c1 = 0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
         const float y = fminf(fmaxf(__fdiv_rn(v[i], scale), -448.0f), 448.0f);
-        packed |= e4m3fn_code(y) << (8 * i);
+        if (i < 4) c0 |= e4m3fn_code(y) << (8 * i);
+        else c1 |= e4m3fn_code(y) << (8 * (i - 4));
     }
-    if (holds) {
-        if constexpr (EPL == 2) reinterpret_cast<uint16_t*>(codes)[lane] = static_cast<uint16_t>(packed);
-        else codes[lane] = static_cast<uint8_t>(packed);
-    }
-    return scale;
-}
-
-// One wave per row: the H query rows of token (b, t) and then its key row, so that every
-// row's loads are in flight at once (a row is one memory latency plus a few hundred
-// cycles of shuffles; walking rows one after another per wave made the step latency-bound).
-template <int D>
-__global__ __launch_bounds__(kPrepThreads)
-void indexer_prep_kernel(IndexerPrepArgs a) {
-    const int lane = threadIdx.x & (kWave - 1);
-    const long long gr = static_cast<long long>(blockIdx.x) * kPrepWaves + threadIdx.x / kWave;
-    const int rows_per_token = a.H + 1;
-    if (gr >= static_cast<long long>(a.B) * a.T * rows_per_token) return;
-    const int token = static_cast<int>(gr / rows_per_token);   // b * T + t
-    const int r = static_cast<int>(gr - static_cast<long long>(token) * rows_per_token);
-    const int b = token / a.T;
-    const int t = token - b * a.T;
-    const int pos = a.start[b] + t;
-    if (pos < 0 || pos >= a.P || pos >= a.Lmax) return;   // outside the tables or the cache
-    const float* cs = a.cos + static_cast<size_t>(pos) * (a.R / 2);
-    const float* sn = a.sin + static_cast<size_t>(pos) * (a.R / 2);
-    if (r < a.H) {
-        const size_t qr = static_cast<size_t>(token) * a.H + r;
-        const float sc = prep_row<D>(a.q, qr * D, a.bf16, cs, sn, a.R, lane, a.q_fp8 + qr * D);
-        if (lane == 0) a.q_scale[qr] = sc;
-    } else {
+    if (!live) return;
+    uint8_t* codes;
+    float* scale_out;
+    if (is_key) {
         const size_t kr = static_cast<size_t>(b) * a.Lmax + pos;
-        const float sc = prep_row<D>(a.k, static_cast<size_t>(token) * D, a.bf16, cs, sn, a.R, lane,
-                                     a.k_cache + kr * D);
-        if (lane == 0) a.k_scale[kr] = sc;
+        codes = a.k_cache + kr * D;
+        scale_out = a.k_scale + kr;
+    } else {
+        const size_t qr = static_cast<size_t>(token) * a.H + r;
+        codes = a.q_fp8 + qr * D;
+        scale_out = a.q_scale + qr;
     }
+    *reinterpret_cast<uint2*>(codes + 8 * n) = uint2{c0, c1};
+    if (n == 0) *scale_out = scale;
 }
 
 }  // namespace
 
 hipError_t launch_indexer_prep(const IndexerPrepArgs& a, hipStream_t stream) {
     const long long rows = static_cast<long long>(a.B) * a.T * (a.H + 1);
-    const dim3 grid(static_cast<unsigned>((rows + kPrepWaves - 1) / kPrepWaves)), block(kPrepThreads);
+    const long long rows_per_block = static_cast<long long>(kPrepWaves) * (kWave / (a.D / 8));
+    const dim3 grid(static_cast<unsigned>((rows + rows_per_block - 1) / rows_per_block)), block(kPrepThreads);
     switch (a.D) {
     case 32: hipLaunchKernelGGL(indexer_prep_kernel<32>, grid, block, 0, stream, a); break;
     case 64: hipLaunchKernelGGL(indexer_prep_kernel<64>, grid, block, 0, stream, a); break;

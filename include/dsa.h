@@ -94,7 +94,8 @@ int dsa_version(void);
  *   q_fp8    [B,T,H_I,d_I] u8, q_scale [B,T,H_I] f32 (outputs: the inputs of dsa_index_scores)
  *   k_cache  [B,Lmax,d_I] u8, k_scale [B,Lmax] f32: rows start[b] .. start[b]+T-1 are
  *            written, every other row is left as it is.
- * Supported: 1 <= H_I <= 64, d_I in {32, 64, 128}, rope_dim a multiple of 4 in [0, d_I].
+ * Supported: 1 <= H_I <= 64, d_I in {32, 64, 128}, rope_dim 0 or a power of two in
+ * [4, d_I].
  * A token whose position is outside [0, min(P, Lmax)) is skipped (device-side check).
  */
 dsa_status dsa_indexer_prep(const void* q, const void* k, dsa_dtype dt, const float* rope_cos,

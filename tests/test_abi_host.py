@@ -148,6 +148,7 @@ def test_indexer_prep_validation(lib):
     assert lib.dsa_indexer_prep(*args(D=96)) == 2
     assert lib.dsa_indexer_prep(*args(H=65)) == 2
     assert lib.dsa_indexer_prep(*args(R=62)) == 2 and b"rope_dim" in lib.dsa_last_error()
+    assert lib.dsa_indexer_prep(*args(R=48)) == 2
     assert lib.dsa_indexer_prep(*args(R=132)) == 2
     assert lib.dsa_indexer_prep(*args(T=101)) == 2
     assert lib.dsa_indexer_prep(*args(q=_fake(0x10008))) == 4
