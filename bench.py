@@ -152,9 +152,11 @@ def cpu_baseline(cfg, n_seqs: int, min_seconds: float = 10.0, latent_form: str =
 
 def measure_prep(D, S, cfg, n: int):
     """The indexer preparation of the workload's new tokens (B*T of them: rope, rotation,
-    FP8 quantisation, key-cache append), timed alone with HIP events over n launches on
-    the current stream.  Not part of the layer step; reported beside it.  Algorithmic
-    bytes: the bf16 q and k rows and their rope angles read, the codes and scales written."""
+    FP8 quantisation, key-cache append), timed alone: n launches captured in one HIP
+    graph and replayed under HIP events, so the host's launch rate does not enter (a
+    decode-sized launch is shorter than a launch from Python).  Not part of the layer
+    step; reported beside it.  Algorithmic bytes: the q and k rows and their rope angles
+    read, the codes and scales written."""
     import torch
     c = S.make_prep_case(cfg)
     d = S.to_device(c, "cuda")
@@ -166,11 +168,16 @@ def measure_prep(D, S, cfg, n: int):
                                  d["k_scale"])
     q_fp8, q_scale = run()
     torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for _ in range(n):
+            D.indexer_prep(d["q"], d["k"], d["cos"], d["sin"], d["start"], R, d["k_cache"],
+                           d["k_scale"], q_fp8, q_scale)
+    g.replay()                                       # warm
+    torch.cuda.synchronize()
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     ev0.record()
-    for _ in range(n):
-        D.indexer_prep(d["q"], d["k"], d["cos"], d["sin"], d["start"], R, d["k_cache"],
-                       d["k_scale"], q_fp8, q_scale)
+    g.replay()
     ev1.record()
     torch.cuda.synchronize()
     ms = ev0.elapsed_time(ev1) / n

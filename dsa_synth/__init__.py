@@ -231,16 +231,23 @@ def make_prep_case(cfg: Config, seqs=None) -> dict:
     quantisation (N(0,1), Student-t(3) for the "student_t3" workloads; bf16 bits, or
     float32 for f32 workloads), the rope tables over Lmax positions, and the key cache
     and scales the new keys are appended to (the case's own cache from make_case)."""
-    base = make_case(cfg, seqs)
-    seqs = base["seqs"]
-    lens = base["lens"]
+    all_lens = lengths(cfg)
+    seqs = list(range(cfg.B)) if seqs is None else list(seqs)
+    lens = all_lens[seqs].copy()
     T, H_I, D_I = cfg.T, cfg.H_I, cfg.D_I
+    # the case's own key cache (same draws as make_case), poisoned past each length
+    k_i = np.full((len(seqs), cfg.Lmax, D_I), POISON_K_CODE, np.uint8)
+    k_scale = np.full((len(seqs), cfg.Lmax), POISON_VALUE, np.float32)
+    for j, b in enumerate(seqs):
+        L = int(lens[j])
+        c, sc = quantize_e4m3fn(_draw(_rng(cfg, 1, b), (L, D_I), cfg.dist), min(128, D_I))
+        k_i[j, :L], k_scale[j, :L] = c, sc[..., 0]
     conv = to_bf16_bits if cfg.attn_dtype == "bf16" else (lambda a: a.astype(np.float32))
     q = np.stack([conv(_draw(_rng(cfg, 7, b), (T, H_I, D_I), cfg.dist)) for b in seqs])
     k = np.stack([conv(_draw(_rng(cfg, 8, b), (T, D_I), cfg.dist)) for b in seqs])
     cos, sin = rope_tables(cfg.Lmax, cfg.rope_i)
     return dict(q=q, k=k, cos=cos, sin=sin, start=(lens - T).astype(np.int32),
-                k_cache=base["k_i"], k_scale=base["k_scale"], lens=lens, seqs=seqs)
+                k_cache=k_i, k_scale=k_scale, lens=lens, seqs=seqs)
 
 
 def to_device(case: dict, device="cuda") -> dict:

@@ -98,3 +98,36 @@ def test_fullsize_prefill(dsa, orc):
     ro, rl = orc.sparse_mha_prefill_rows(c["q"], c["k"], c["v"], gidx_all, cfg.sm_scale,
                                          [(0, t) for t in rows])
     check_attention(out_np[0, rows], lse_np[0, rows], ro, rl, "bf16")
+
+
+@pytest.mark.parametrize("name", ["decode_v32", "prefill_chunk"])
+def test_fullsize_indexer_prep(dsa, orc, name):
+    """The indexer preparation of every new token of the workload (32 decode tokens, or
+    the 8192 tokens of the prefill chunk), checked against the oracle on sampled tokens."""
+    from parity import check_prep
+    cfg = S.CONFIGS[name]
+    _say(f"[fullsize] prep {name}: generating inputs")
+    c = S.make_prep_case(cfg)
+    d = S.to_device(c, "cuda")
+    R = cfg.rope_i
+    q_fp8, q_scale = dsa.indexer_prep(d["q"], d["k"], d["cos"], d["sin"], d["start"], R,
+                                      d["k_cache"], d["k_scale"])
+    torch.cuda.synchronize()
+    q_fp8, q_scale = q_fp8.cpu().numpy(), q_scale.cpu().numpy()
+    kc, ks = d["k_cache"].cpu().numpy(), d["k_scale"].cpu().numpy()
+    if cfg.T == 1:
+        samples = [(b, 0) for b in range(cfg.B)]
+    else:
+        samples = [(0, t) for t in (0, 1, 63, 4095, cfg.T - 2, cfg.T - 1)]
+    for b, t in samples:
+        pos = int(c["start"][b]) + t
+        r = orc.indexer_prep(c["q"][b:b + 1, t:t + 1], c["k"][b:b + 1, t:t + 1], c["cos"], c["sin"],
+                             np.array([pos], np.int32), R, c["k_cache"][b:b + 1], c["k_scale"][b:b + 1])
+        check_prep(q_fp8[b:b + 1, t:t + 1], q_scale[b:b + 1, t:t + 1], r["q_y"], r["q_scale"])
+        check_prep(kc[b:b + 1, pos:pos + 1], ks[b:b + 1, pos:pos + 1], r["k_y"], r["k_scale64"])
+    # rows of the cache outside the new tokens are untouched
+    for b in range(cfg.B):
+        keep = np.ones(cfg.Lmax, bool)
+        keep[int(c["start"][b]):int(c["start"][b]) + cfg.T] = False
+        assert np.array_equal(kc[b, keep], c["k_cache"][b, keep])
+    _say(f"[fullsize] prep {name}: done")
