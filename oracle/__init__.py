@@ -56,14 +56,14 @@ def _load():
         lib.orc_bf16_value.restype = D
         lib.orc_latent_fp8_value.argtypes = [P, I]
         lib.orc_latent_fp8_value.restype = D
-        lib.orc_index_scores.argtypes = [P, P, P, P, P, P, I, I, I, I, I, D, P]
-        lib.orc_topk.argtypes = [P, P, I, I, I, I, P]
-        lib.orc_sparse_mla_decode.argtypes = [P, P, P, P, I, I, I, I, I, I, I, I, D, P, P]
+        lib.orc_index_scores.argtypes = [P, P, P, P, P, P, I, I, I, I, I, D, I, P]
+        lib.orc_topk.argtypes = [P, P, I, I, I, I, I, P]
+        lib.orc_sparse_mla_decode.argtypes = [P, P, P, P, I, I, I, I, I, I, I, I, D, I, P, P]
         lib.orc_sparse_mha_prefill.argtypes = [P, P, P, P, I, I, I, I, I, I, I, D, P, P]
         lib.orc_sparse_mha_prefill_dense.argtypes = [P, P, P, P, I, I, I, I, I, I, I, D, P, P]
         lib.orc_sparse_mha_prefill_rows.argtypes = [P, P, P, P, I, I, I, I, I, I, I, D, P, P, I, P, P]
         lib.orc_layer_step_latent.argtypes = [P, P, P, P, P, P, I, I, I, I, I, D, I,
-                                              P, P, I, I, I, I, D, P, P, P, P]
+                                              P, P, I, I, I, I, D, I, P, P, P, P]
         lib.orc_layer_step_mha.argtypes = [P, P, P, P, P, I, I, I, I, D, I,
                                            P, P, P, I, I, I, I, D, P, P, P, P]
         lib.orc_e4m3fn_encode.argtypes = [D]
@@ -171,8 +171,10 @@ def indexer_prep(q, k, cos, sin, start, rope_dim, k_cache, k_scale):
     return out
 
 
-def index_scores(q_fp8, q_scale, w, k_fp8, k_scale, lens, sm_scale_i):
-    """scores[B,T,Lmax] f32 = sum_h w*q_scale*sm_scale_i * ReLU(q.k) * k_scale, -inf if invisible."""
+def index_scores(q_fp8, q_scale, w, k_fp8, k_scale, lens, sm_scale_i, compress=1):
+    """scores[B,T,Lmax] f32 = sum_h w*q_scale*sm_scale_i * ReLU(q.k) * k_scale, -inf if invisible
+    (compress = m > 1: the cache rows are compressed entries, row (b,t) sees
+    e < (len - T + t + 1) / m)."""
     B, T, H, D = q_fp8.shape
     Lmax = k_fp8.shape[1]
     lib = _load()
@@ -184,22 +186,23 @@ def index_scores(q_fp8, q_scale, w, k_fp8, k_scale, lens, sm_scale_i):
     lens, pl = _c(lens, np.int32)
     out = np.empty((B, T, Lmax), np.float32)
     _check(lib.orc_index_scores(pq, pqs, pw, pk, pks, pl, B, T, H, D, Lmax, float(sm_scale_i),
-                                out.ctypes.data_as(ctypes.c_void_p)), "index_scores")
+                                int(compress), out.ctypes.data_as(ctypes.c_void_p)), "index_scores")
     return out
 
 
-def topk(scores, lens, k):
-    """idx[B,T,k] i32: the min(k, pos+1) best visible positions ascending, then -1."""
+def topk(scores, lens, k, compress=1):
+    """idx[B,T,k] i32: the min(k, n) best visible rows ascending, then -1."""
     B, T, Lmax = scores.shape
     lib = _load()
     scores, ps = _c(scores, np.float32)
     lens, pl = _c(lens, np.int32)
     out = np.empty((B, T, k), np.int32)
-    _check(lib.orc_topk(ps, pl, B, T, Lmax, k, out.ctypes.data_as(ctypes.c_void_p)), "topk")
+    _check(lib.orc_topk(ps, pl, B, T, Lmax, k, int(compress), out.ctypes.data_as(ctypes.c_void_p)),
+           "topk")
     return out
 
 
-def sparse_mla_decode(q, latent, idx, lens, Dv, sm_scale):
+def sparse_mla_decode(q, latent, idx, lens, Dv, sm_scale, compress=1):
     """Absorbed-form sparse attention.  Returns (out[B,T,H,Dv] f64, lse[B,T,H] f64)."""
     B, T, H, Dq = q.shape
     Lmax = latent.shape[1]
@@ -218,7 +221,7 @@ def sparse_mla_decode(q, latent, idx, lens, Dv, sm_scale):
     lse = np.empty((B, T, H), np.float64)
     _check(lib.orc_sparse_mla_decode(q.ctypes.data_as(ctypes.c_void_p),
                                      latent.ctypes.data_as(ctypes.c_void_p), pi, pl, dt,
-                                     B, T, H, Dv, Dq - Dv, Lmax, k, float(sm_scale),
+                                     B, T, H, Dv, Dq - Dv, Lmax, k, float(sm_scale), int(compress),
                                      out.ctypes.data_as(ctypes.c_void_p),
                                      lse.ctypes.data_as(ctypes.c_void_p)), "sparse_mla_decode")
     return out, lse
@@ -276,7 +279,7 @@ def sparse_mha_prefill_dense(q, k_, v, idx, sm_scale):
 
 
 def layer_step_latent(q_fp8, q_scale, w, k_fp8, k_scale, lens, sm_scale_i, k, q, latent, Dv,
-                      sm_scale, want_scores=False):
+                      sm_scale, want_scores=False, compress=1):
     """Index scores -> top-k -> sparse latent attention.  Returns (out, lse, idx[, scores])."""
     B, T, H_I, D_I = q_fp8.shape
     Lmax = k_fp8.shape[1]
@@ -298,7 +301,8 @@ def layer_step_latent(q_fp8, q_scale, w, k_fp8, k_scale, lens, sm_scale_i, k, q,
     _check(lib.orc_layer_step_latent(*[p for _, p in arrs], B, T, H_I, D_I, Lmax,
                                      float(sm_scale_i), k, qa.ctypes.data_as(ctypes.c_void_p),
                                      la.ctypes.data_as(ctypes.c_void_p), dt, H, Dv, Dq - Dv,
-                                     float(sm_scale), out.ctypes.data_as(ctypes.c_void_p),
+                                     float(sm_scale), int(compress),
+                                     out.ctypes.data_as(ctypes.c_void_p),
                                      lse.ctypes.data_as(ctypes.c_void_p),
                                      scores.ctypes.data_as(ctypes.c_void_p) if want_scores else None,
                                      idx.ctypes.data_as(ctypes.c_void_p)), "layer_step_latent")

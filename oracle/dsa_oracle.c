@@ -27,7 +27,9 @@
  *          adds an index mask (0 at the selected positions, -inf elsewhere) and the
  *          causal mask, takes a softmax and mixes the value rows.
  *   [V4]   "visualize_attention_masks.py" (DeepSeek-V4 mask visualiser): -1 marks
- *          unused top-k slots.
+ *          unused top-k slots; in the compressed-sparse layers the indexer ranks
+ *          compressed entries, entry e being available to the query at position p iff
+ *          e < (p + 1) / compress_rate.
  *
  * Conventions (where the pages leave a point open, the plainest reading is taken):
  *   len[b]        valid keys of sequence b;  T query rows are the LAST T positions,
@@ -106,6 +108,29 @@ static double latent_elem(const void* latent, int dtype, size_t row, int Dq, int
     return load_elem(latent, dtype, row * (size_t)Dq + d);
 }
 
+/* ------------------------------------------------------------------ visibility */
+
+/* Cache rows visible to query row t of a call with T rows over a sequence of len
+ * positions.  m = 1: every position is a cache row and row t sits at position
+ * pos = len - T + t, so rows 0 .. pos are visible ([MASK]).  m > 1: the cache holds
+ * compressed entries, each standing for m consecutive positions, and entry e is
+ * available to the query at position pos iff e < (pos + 1) / m (integer division; the
+ * causal threshold of the compressed-sparse layers in [V4]), so the first m - 1
+ * positions see no entry at all. */
+static int visible_rows(int len, int T, int t, int m)
+{
+    return (len - T + t + 1) / m;
+}
+
+/* T <= len[b] and every visible row exists in the cache (len[b] / m <= Lmax) */
+static int check_rows(const int32_t* len, int B, int T, int Lmax, int m)
+{
+    if (m < 1) return ORC_ERR_SHAPE;
+    for (int b = 0; b < B; ++b)
+        if (len[b] < T || visible_rows(len[b], T, T - 1, m) > Lmax) return ORC_ERR_SHAPE;
+    return ORC_OK;
+}
+
 /* ------------------------------------------------------------------ O2: index scores */
 
 /* For every row (b,t) and cache position s:
@@ -117,22 +142,21 @@ static double latent_elem(const void* latent, int dtype, size_t row, int Dq, int
  * units of 2^-18, so D_h is exact; the head sum is one double rounding per term. */
 int orc_index_scores(const uint8_t* q, const float* q_scale, const float* w,
                      const uint8_t* k, const float* k_scale, const int32_t* len,
-                     int B, int T, int H, int D, int Lmax, double sm_scale, float* scores)
+                     int B, int T, int H, int D, int Lmax, double sm_scale, int m, float* scores)
 {
     double table[256];
     int b;
     for (int c = 0; c < 256; ++c) table[c] = orc_e4m3fn_value((uint8_t)c);
-    for (b = 0; b < B; ++b)
-        if (len[b] < T || len[b] > Lmax) return ORC_ERR_SHAPE;
+    if (check_rows(len, B, T, Lmax, m) != ORC_OK) return ORC_ERR_SHAPE;
 
 #pragma omp parallel for collapse(2) schedule(dynamic)
     for (b = 0; b < B; ++b) {
         for (int t = 0; t < T; ++t) {
-            const int pos = len[b] - T + t;
+            const int n = visible_rows(len[b], T, t, m);
             const size_t row = (size_t)b * T + t;
             float* out = scores + row * (size_t)Lmax;
             for (int s = 0; s < Lmax; ++s) {
-                if (s > pos) { out[s] = -INFINITY; continue; }
+                if (s >= n) { out[s] = -INFINITY; continue; }
                 const uint8_t* ks = k + ((size_t)b * Lmax + s) * D;
                 double acc = 0.0;
                 for (int h = 0; h < H; ++h) {
@@ -169,22 +193,21 @@ static int by_pos_asc(const void* a, const void* b)
     return (x > y) - (x < y);
 }
 
-/* Per row: the min(k, pos+1) visible positions with the largest scores (a full sort,
- * ties by smaller position), written in ascending position order and padded with -1
- * up to k slots ([IDX] top-k capped at the visible count; [V4] -1 sentinel). */
-int orc_topk(const float* scores, const int32_t* len, int B, int T, int Lmax, int k,
+/* Per row: the min(k, n) visible rows with the largest scores (n = visible_rows; a full
+ * sort, ties by smaller position), written in ascending position order and padded with
+ * -1 up to k slots ([IDX] top-k capped at the visible count; [V4] -1 sentinel). */
+int orc_topk(const float* scores, const int32_t* len, int B, int T, int Lmax, int k, int m,
              int32_t* idx)
 {
     int b;
     if (k <= 0) return ORC_ERR_SHAPE;
-    for (b = 0; b < B; ++b)
-        if (len[b] < T || len[b] > Lmax) return ORC_ERR_SHAPE;
+    if (check_rows(len, B, T, Lmax, m) != ORC_OK) return ORC_ERR_SHAPE;
 
 #pragma omp parallel for collapse(2) schedule(dynamic)
     for (b = 0; b < B; ++b) {
         for (int t = 0; t < T; ++t) {
             const size_t row = (size_t)b * T + t;
-            const int n = len[b] - T + t + 1;
+            const int n = visible_rows(len[b], T, t, m);
             const int kk = n < k ? n : k;
             const float* sc = scores + row * (size_t)Lmax;
             int32_t* out = idx + row * (size_t)k;
@@ -212,7 +235,7 @@ int orc_topk(const float* scores, const int32_t* len, int B, int T, int Lmax, in
  * (orc_latent_fp8_value), the queries bf16. */
 int orc_sparse_mla_decode(const void* q, const void* latent, const int32_t* idx,
                           const int32_t* len, int dtype, int B, int T, int H, int Dv, int Dr,
-                          int Lmax, int k, double sm_scale, double* out, double* lse)
+                          int Lmax, int k, double sm_scale, int m, double* out, double* lse)
 {
     const int Dq = Dv + Dr;
     /* FP8 latent rows pair with bf16 queries, at the storage form's fixed widths */
@@ -220,8 +243,7 @@ int orc_sparse_mla_decode(const void* q, const void* latent, const int32_t* idx,
     int b;
     if (dtype == ORC_FP8_LATENT && (Dv != ORC_FP8_LATENT_DV || Dr != ORC_FP8_LATENT_DR))
         return ORC_ERR_SHAPE;
-    for (b = 0; b < B; ++b)
-        if (len[b] < T || len[b] > Lmax) return ORC_ERR_SHAPE;
+    if (check_rows(len, B, T, Lmax, m) != ORC_OK) return ORC_ERR_SHAPE;
     for (size_t i = 0; i < (size_t)B * T * k; ++i)
         if (idx[i] < -1 || idx[i] >= Lmax) return ORC_ERR_INDEX;
 
@@ -229,13 +251,13 @@ int orc_sparse_mla_decode(const void* q, const void* latent, const int32_t* idx,
     for (b = 0; b < B; ++b) {
         for (int t = 0; t < T; ++t) {
             const size_t row = (size_t)b * T + t;
-            const int pos = len[b] - T + t;
+            const int nvis = visible_rows(len[b], T, t, m);
             const int32_t* sel = idx + row * (size_t)k;
             double* logit = (double*)malloc(sizeof(double) * (size_t)k);
             int32_t* keys = (int32_t*)malloc(sizeof(int32_t) * (size_t)k);
             int n = 0;
             for (int j = 0; j < k; ++j)
-                if (sel[j] >= 0 && sel[j] <= pos) keys[n++] = sel[j];
+                if (sel[j] >= 0 && sel[j] < nvis) keys[n++] = sel[j];
             /* the selected rows' values, decoded once for all heads: C[j][c] = C[b, s_j, c] */
             double* C = (double*)malloc(sizeof(double) * (size_t)(n > 0 ? n : 1) * Dq);
             for (int j = 0; j < n; ++j)
@@ -415,18 +437,18 @@ int orc_layer_step_latent(const uint8_t* q_i, const float* q_scale, const float*
                           const uint8_t* k_i, const float* k_scale, const int32_t* len,
                           int B, int T, int H_I, int D_I, int Lmax, double sm_scale_i, int k,
                           const void* q, const void* latent, int dtype, int H, int Dv, int Dr,
-                          double sm_scale, double* out, double* lse, float* scores_out,
+                          double sm_scale, int m, double* out, double* lse, float* scores_out,
                           int32_t* idx_out)
 {
     float* scores = scores_out ? scores_out
                                : (float*)malloc(sizeof(float) * (size_t)B * T * Lmax);
     int32_t* idx = idx_out ? idx_out : (int32_t*)malloc(sizeof(int32_t) * (size_t)B * T * k);
     int rc = orc_index_scores(q_i, q_scale, w, k_i, k_scale, len, B, T, H_I, D_I, Lmax,
-                              sm_scale_i, scores);
-    if (rc == ORC_OK) rc = orc_topk(scores, len, B, T, Lmax, k, idx);
+                              sm_scale_i, m, scores);
+    if (rc == ORC_OK) rc = orc_topk(scores, len, B, T, Lmax, k, m, idx);
     if (rc == ORC_OK)
         rc = orc_sparse_mla_decode(q, latent, idx, len, dtype, B, T, H, Dv, Dr, Lmax, k,
-                                   sm_scale, out, lse);
+                                   sm_scale, m, out, lse);
     if (!scores_out) free(scores);
     if (!idx_out) free(idx);
     return rc;
@@ -445,9 +467,9 @@ int orc_layer_step_mha(const uint8_t* q_i, const float* q_scale, const float* w,
     int32_t* idx = idx_out ? idx_out : (int32_t*)malloc(sizeof(int32_t) * (size_t)B * T * k);
     int rc;
     for (int b = 0; b < B; ++b) len[b] = T;
-    rc = orc_index_scores(q_i, q_scale, w, k_i, k_scale, len, B, T, H_I, D_I, T, sm_scale_i,
+    rc = orc_index_scores(q_i, q_scale, w, k_i, k_scale, len, B, T, H_I, D_I, T, sm_scale_i, 1,
                           scores);
-    if (rc == ORC_OK) rc = orc_topk(scores, len, B, T, T, k, idx);
+    if (rc == ORC_OK) rc = orc_topk(scores, len, B, T, T, k, 1, idx);
     if (rc == ORC_OK)
         rc = orc_sparse_mha_prefill(q, kk, v, idx, dtype, B, T, H, Dqk, Dv, k, sm_scale, out,
                                     lse);

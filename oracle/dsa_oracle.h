@@ -8,6 +8,8 @@
  *   scores  [B,T,Lmax] f32              idx        [B,T,k]   i32 (-1 = unused slot)
  *   latent form:  q [B,T,H,Dv+Dr], latent [B,Lmax,Dv+Dr], out [B,T,H,Dv] f64, lse [B,T,H] f64
  *   MHA form:     q, k [B,T,H,Dqk], v [B,T,H,Dv], out [B,T,H,Dv] f64, lse [B,T,H] f64
+ * m (compress rate): 1 = every position is a cache row; m > 1 = the key and latent caches
+ * hold compressed entries and row (b,t) sees entries e < (len[b] - T + t + 1) / m.
  * Attention inputs are read as ORC_F32, ORC_BF16 (raw 16-bit words) or ORC_F64.
  * ORC_FP8_LATENT (latent form only): bf16 queries and 656-byte FP8 latent rows
  *   [512 e4m3fn codes][4 fp32 scales, one per 128 columns][64 bf16 rope values],
@@ -34,14 +36,14 @@ int orc_indexer_prep(const void* q, const void* k, int dtype, const float* cosT,
 
 int orc_index_scores(const uint8_t* q, const float* q_scale, const float* w,
                      const uint8_t* k, const float* k_scale, const int32_t* len,
-                     int B, int T, int H, int D, int Lmax, double sm_scale, float* scores);
+                     int B, int T, int H, int D, int Lmax, double sm_scale, int m, float* scores);
 
-int orc_topk(const float* scores, const int32_t* len, int B, int T, int Lmax, int k,
+int orc_topk(const float* scores, const int32_t* len, int B, int T, int Lmax, int k, int m,
              int32_t* idx);
 
 int orc_sparse_mla_decode(const void* q, const void* latent, const int32_t* idx,
                           const int32_t* len, int dtype, int B, int T, int H, int Dv, int Dr,
-                          int Lmax, int k, double sm_scale, double* out, double* lse);
+                          int Lmax, int k, double sm_scale, int m, double* out, double* lse);
 
 int orc_sparse_mha_prefill(const void* q, const void* kk, const void* v, const int32_t* idx,
                            int dtype, int B, int T, int H, int Dqk, int Dv, int k,
@@ -60,7 +62,7 @@ int orc_layer_step_latent(const uint8_t* q_i, const float* q_scale, const float*
                           const uint8_t* k_i, const float* k_scale, const int32_t* len,
                           int B, int T, int H_I, int D_I, int Lmax, double sm_scale_i, int k,
                           const void* q, const void* latent, int dtype, int H, int Dv, int Dr,
-                          double sm_scale, double* out, double* lse, float* scores_out,
+                          double sm_scale, int m, double* out, double* lse, float* scores_out,
                           int32_t* idx_out);
 
 int orc_layer_step_mha(const uint8_t* q_i, const float* q_scale, const float* w,

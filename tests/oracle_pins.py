@@ -27,6 +27,11 @@ What pins what:
                               multiplication and the rotation against scipy's Hadamard
                               matrix (recovered through the returned scales), a
                               quantisation closed form, the cache append placement;
+  * compressed entries     -> the V4 visualiser's tiny configuration (16 positions,
+                              compress rate 4, top-2): warm-up rows of -1 sentinels,
+                              then one, two, three, four available entries; scores,
+                              top-k and attention under compression equal the
+                              uncompressed ones restricted to the available entries;
   * FP8 latent rows        -> torch's float8_e4m3fn and bfloat16 decoding at the
                               656-byte layout (512 codes, 4 fp32 block scales, 64
                               bf16 rope values), and attention over such rows ==
@@ -448,6 +453,85 @@ def pin_latent_fp8_attention_library(o):
             np.testing.assert_allclose(out[b, t], want.numpy(), rtol=1e-9, atol=1e-12)
             logits = qd @ C[mask].T * sm
             np.testing.assert_allclose(lse[b, t], torch.logsumexp(logits, -1).numpy(), rtol=1e-12)
+
+
+# ----------------------------------------------------------------------------- compressed entries
+
+def pin_compressed_entries_v4_tiny(o):
+    """The V4 mask visualiser's tiny configuration: 16 query positions, compress rate 4,
+    top-2 over the compressed entries.  Positions 0..2 have no entry yet (all slots -1,
+    the warm-up sentinel); positions 3..6 have exactly entry 0; 7..10 entries 0 and 1
+    (both kept); 11..14 three entries, 15 four (two kept).  Scores of unavailable
+    entries are -inf."""
+    rng = np.random.default_rng(91)
+    S_, m, k, H, D = 16, 4, 2, 2, 32
+    L_e = S_ // m
+    qc = _rand_codes(rng, (1, S_, H, D))
+    kc = _rand_codes(rng, (1, L_e, D))
+    qs = rng.uniform(0.5, 2, (1, S_, H)).astype(np.float32)
+    ks = rng.uniform(0.5, 2, (1, L_e)).astype(np.float32)
+    w = rng.standard_normal((1, S_, H)).astype(np.float32)
+    lens = np.array([S_], np.int32)
+    sc = o.index_scores(qc, qs, w, kc, ks, lens, 0.2, compress=m)
+    idx = o.topk(sc, lens, k, compress=m)
+    avail = [0, 0, 0, 1, 1, 1, 1, 2, 2, 2, 2, 3, 3, 3, 3, 4]
+    for t in range(S_):
+        n = avail[t]
+        assert np.all(np.isfinite(sc[0, t, :n])) and np.all(sc[0, t, n:] == -np.inf), t
+        got = idx[0, t]
+        assert np.all(got[min(n, k):] == -1) and np.all(got[:min(n, k)] >= 0), (t, got)
+        assert set(got[:min(n, k)]) <= set(range(n))
+    assert [list(idx[0, t]) for t in (0, 2, 3, 6, 7, 10)] == [[-1, -1], [-1, -1], [0, -1], [0, -1],
+                                                             [0, 1], [0, 1]]
+
+
+def pin_compressed_entries_restriction(o):
+    """Under compression m the scores, top-k and attention are the uncompressed ones
+    restricted to the entries a row may see (e < (pos + 1) / m), over a cache of
+    entries, for several query rows per sequence and ragged lengths."""
+    rng = np.random.default_rng(92)
+    B, T, H, D, m, k = 2, 5, 3, 32, 3, 4
+    lens = np.array([40, 17], np.int32)
+    Lmax = 40 // m + 1
+    qc = _rand_codes(rng, (B, T, H, D))
+    kc = _rand_codes(rng, (B, Lmax, D))
+    qs = rng.uniform(0.5, 2, (B, T, H)).astype(np.float32)
+    ks = rng.uniform(0.5, 2, (B, Lmax)).astype(np.float32)
+    w = rng.standard_normal((B, T, H)).astype(np.float32)
+    sc_m = o.index_scores(qc, qs, w, kc, ks, lens, 0.3, compress=m)
+    # uncompressed reference over the same Lmax entries: a call whose rows all see the
+    # whole entry cache (len = Lmax, one row per call) gives every entry's score
+    for b in range(B):
+        for t in range(T):
+            n = (int(lens[b]) - T + t + 1) // m
+            full = o.index_scores(qc[b:b + 1, t:t + 1], qs[b:b + 1, t:t + 1], w[b:b + 1, t:t + 1],
+                                  kc[b:b + 1], ks[b:b + 1], np.array([Lmax], np.int32), 0.3)
+            np.testing.assert_array_equal(sc_m[b, t, :n], full[0, 0, :n])
+            assert np.all(sc_m[b, t, n:] == -np.inf)
+    idx_m = o.topk(sc_m, lens, k, compress=m)
+    for b in range(B):
+        for t in range(T):
+            n = (int(lens[b]) - T + t + 1) // m
+            order = np.argsort(-sc_m[b, t, :n].astype(np.float64), kind="stable")[:k]
+            assert list(idx_m[b, t, :min(n, k)]) == sorted(order.tolist())
+            assert np.all(idx_m[b, t, min(n, k):] == -1)
+    # attention: the slots of unavailable entries are ignored
+    q = rng.standard_normal((B, T, H, 24))
+    lat = rng.standard_normal((B, Lmax, 24))
+    idx = np.stack([np.stack([rng.permutation(Lmax)[:6] for _ in range(T)]) for _ in range(B)]).astype(np.int32)
+    out_m, lse_m = o.sparse_mla_decode(q, lat, idx, lens, 16, 0.2, compress=m)
+    idx_r = idx.copy()
+    for b in range(B):
+        for t in range(T):
+            n = (int(lens[b]) - T + t + 1) // m
+            idx_r[b, t][idx_r[b, t] >= n] = -1
+    for b in range(B):
+        for t in range(T):
+            # one uncompressed row with len = Lmax sees every entry of the cache
+            o1, l1 = o.sparse_mla_decode(q[b:b + 1, t:t + 1], lat[b:b + 1], idx_r[b:b + 1, t:t + 1],
+                                         np.array([Lmax], np.int32), 16, 0.2)
+            np.testing.assert_allclose(out_m[b, t], o1[0, 0], rtol=1e-12, atol=1e-14)
+            np.testing.assert_allclose(lse_m[b, t], l1[0, 0], rtol=1e-12)
 
 
 # ----------------------------------------------------------------------------- indexer preparation

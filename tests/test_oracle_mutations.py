@@ -20,8 +20,8 @@ MUTATIONS = [
      "(double)w[row * H + h] * (double)q_scale[row * H + h]"),
     ("k_scale indexed by row", "(double)k_scale[(size_t)b * Lmax + s]",
      "(double)k_scale[(size_t)b * Lmax + t]"),
-    ("causal off by one", "if (s > pos) { out[s] = -INFINITY; continue; }",
-     "if (s >= pos) { out[s] = -INFINITY; continue; }"),
+    ("causal off by one", "if (s >= n) { out[s] = -INFINITY; continue; }",
+     "if (s >= n - 1) { out[s] = -INFINITY; continue; }"),
     ("query head ignored", "const uint8_t* qh = q + (row * H + h) * D;",
      "const uint8_t* qh = q + (row * H) * D;"),
     ("decode e4m3 bias 8", "mag = ldexp(1.0 + (double)m / 8.0, e - 7);",
@@ -30,8 +30,8 @@ MUTATIONS = [
      "for (int j = 0; j < kk; ++j) out[j] = v[n - 1 - j].pos;"),
     ("top-k ties prefer larger position", "return (x->pos > y->pos) - (x->pos < y->pos);",
      "return (x->pos < y->pos) - (x->pos > y->pos);"),
-    ("top-k drops current position", "const int n = len[b] - T + t + 1;",
-     "const int n = len[b] - T + t;"),
+    ("top-k drops current position", "const int n = visible_rows(len[b], T, t, m);\n            const int kk",
+     "const int n = visible_rows(len[b] - (len[b] > T), T, t, m);\n            const int kk"),
     ("attention scale dropped", "logit[j] = sm_scale * dot;", "logit[j] = dot;"),
     ("latent key drops rope part", "for (int d = 0; d < Dq; ++d)\n", "for (int d = 0; d < Dv; ++d)\n"),
     ("latent value offset", "o[d] += p * C[(size_t)j * Dq + d];",
@@ -43,6 +43,12 @@ MUTATIONS = [
     ("fp8 latent rope read over the scales",
      "4 * (ORC_FP8_LATENT_DV / ORC_FP8_LATENT_BLOCK) +\n                      2 * (d - ORC_FP8_LATENT_DV)",
      "2 * (d - ORC_FP8_LATENT_DV)"),
+    ("compressed threshold rounded up", "    return (len - T + t + 1) / m;",
+     "    return (len - T + t + m) / m;"),
+    ("top-k ignores compression", "const int n = visible_rows(len[b], T, t, m);\n            const int kk",
+     "const int n = visible_rows(len[b], T, t, 1);\n            const int kk"),
+    ("attention ignores compression", "const int nvis = visible_rows(len[b], T, t, m);",
+     "const int nvis = visible_rows(len[b], T, t, 1);"),
     ("prep rope interleaved pairs", "const double a = v[j], b = v[j + R / 2];",
      "const double a = v[2 * j], b = v[2 * j + 1];"),
     ("prep rope sin sign", "v[j] = a * (double)cs[j] - b * (double)sn[j];",
@@ -59,7 +65,7 @@ MUTATIONS = [
      "const size_t kr = (size_t)b * Lmax + pos - (pos > 0);"),
     ("fp8 latent queries not bf16", "const int qdt = dtype == ORC_FP8_LATENT ? ORC_BF16 : dtype;",
      "const int qdt = dtype == ORC_FP8_LATENT ? ORC_F32 : dtype;"),
-    ("latent ignores visibility", "if (sel[j] >= 0 && sel[j] <= pos) keys[n++] = sel[j];",
+    ("latent ignores visibility", "if (sel[j] >= 0 && sel[j] < nvis) keys[n++] = sel[j];",
      "if (sel[j] >= 0) keys[n++] = sel[j];"),
     ("lse without max", "lse[row * H + h] = m + log(sum);", "lse[row * H + h] = log(sum);"),
     ("MHA ignores causality", "if (sel[j] >= 0 && sel[j] <= t) keys[n++] = sel[j];",
