@@ -50,6 +50,7 @@ class LayerArgs(ctypes.Structure):
         ("sm_scale", ctypes.c_float),
         ("out", ctypes.c_void_p), ("lse", ctypes.c_void_p),
         ("idx_out", ctypes.c_void_p), ("scores_out", ctypes.c_void_p),
+        ("compress_rate", ctypes.c_int),
     ]
 
 
@@ -281,7 +282,7 @@ class LayerStep:
 
     def __init__(self, q_fp8, q_scale, w, k_fp8, k_scale, lens, sm_scale_i, topk, q, sm_scale,
                  latent=None, k=None, v=None, Dv=None, want_lse=True, want_idx=False,
-                 want_scores=False):
+                 want_scores=False, compress_rate=1):
         q_fp8 = _fp8(q_fp8, "q_fp8")
         k_fp8 = _fp8(k_fp8, "k_fp8")
         for t, n in ((q_scale, "q_scale"), (w, "w"), (k_scale, "k_scale")):
@@ -297,6 +298,7 @@ class LayerStep:
         a.k_fp8, a.k_scale, a.len = k_fp8.data_ptr(), k_scale.data_ptr(), lens.data_ptr()
         a.B, a.T, a.H_I, a.d_I, a.Lmax, a.topk = B, T, H_I, D_I, Lmax, topk
         a.sm_scale_I = float(sm_scale_i)
+        a.compress_rate = int(compress_rate)
         a.dtype = dt
         a.q = q.data_ptr()
         a.H = H

@@ -45,10 +45,11 @@ constexpr long long kMaxRows = 1LL << 30;
 
 dsa_status check_index_args(const uint8_t* q_fp8, const float* q_scale, const float* w,
                             const uint8_t* k_fp8, const float* k_scale, const int32_t* len,
-                            int B, int T, int H_I, int d_I, int Lmax) {
+                            int B, int T, int H_I, int d_I, int Lmax, int m = 1) {
     DSA_REQUIRE(q_fp8 && q_scale && w && k_fp8 && k_scale && len, DSA_ERR_NULL,
                 "index scores: NULL input pointer");
-    DSA_REQUIRE(B >= 1 && T >= 1 && Lmax >= 1 && T <= Lmax, DSA_ERR_SHAPE,
+    // with compressed entries (m > 1) the T rows are positions, the Lmax rows entries
+    DSA_REQUIRE(B >= 1 && T >= 1 && Lmax >= 1 && (T <= Lmax || m > 1), DSA_ERR_SHAPE,
                 "index scores: need B >= 1 and 1 <= T <= Lmax (B=%d T=%d Lmax=%d)", B, T, Lmax);
     DSA_REQUIRE(static_cast<long long>(B) * T <= kMaxRows, DSA_ERR_SHAPE, "index scores: B*T too large");
     DSA_REQUIRE(H_I >= 1 && H_I <= 64, DSA_ERR_SHAPE, "index scores: H_I=%d not in [1, 64]", H_I);
@@ -78,14 +79,14 @@ static_assert(static_cast<int>(DSA_F32) == dsa::kLatF32 && static_cast<int>(DSA_
 
 dsa_status check_latent_args(const void* q, const void* latent, const int32_t* idx,
                              const int32_t* len, int B, int T, int H, int Dv, int Dr, int Lmax,
-                             int k, dsa_dtype dt, const void* out) {
+                             int k, dsa_dtype dt, const void* out, int m = 1) {
     DSA_REQUIRE(q && latent && idx && len && out, DSA_ERR_NULL, "sparse_mla_decode: NULL pointer");
     DSA_REQUIRE(dt == DSA_F32 || dt == DSA_BF16 || dt == DSA_FP8_LATENT, DSA_ERR_DTYPE,
                 "sparse_mla_decode: bad dtype %d", static_cast<int>(dt));
     DSA_REQUIRE(dt != DSA_FP8_LATENT || (Dv == dsa::kFp8Dv && Dr == dsa::kFp8Dr), DSA_ERR_DTYPE,
                 "sparse_mla_decode: FP8 latent rows need Dv=512, Dr=64 (got Dv=%d Dr=%d)", Dv, Dr);
-    DSA_REQUIRE(B >= 1 && T >= 1 && Lmax >= 1 && T <= Lmax && H >= 1 && Dv >= 1 && Dr >= 0 &&
-                    Dv + Dr <= 1024 && k >= 1,
+    DSA_REQUIRE(B >= 1 && T >= 1 && Lmax >= 1 && (T <= Lmax || m > 1) && H >= 1 && Dv >= 1 &&
+                    Dr >= 0 && Dv + Dr <= 1024 && k >= 1,
                 DSA_ERR_SHAPE, "sparse_mla_decode: bad shape (B=%d T=%d H=%d Dv=%d Dr=%d Lmax=%d k=%d)",
                 B, T, H, Dv, Dr, Lmax, k);
     DSA_REQUIRE(static_cast<long long>(B) * T * H <= kMaxRows, DSA_ERR_SHAPE,
@@ -100,10 +101,10 @@ dsa_status check_latent_args(const void* q, const void* latent, const int32_t* i
 
 dsa_status launch_latent(const void* q, const void* latent, const int32_t* idx, const int32_t* len,
                          int B, int T, int H, int Dv, int Dr, int Lmax, int k, float sm_scale,
-                         dsa_dtype dt, void* out, float* lse, void* ws, hipStream_t stream) {
+                         dsa_dtype dt, void* out, float* lse, void* ws, hipStream_t stream, int m) {
     if (dsa::mla_decode_mfma_supported(H, Dv, Dr, k, dt))
         return hip_status(dsa::launch_mla_decode_mfma(q, latent, idx, len, B, T, H, Lmax, k, sm_scale,
-                                                      dt, out, lse, ws, stream),
+                                                      dt, m, out, lse, ws, stream),
                           "sparse_mla_decode");
     dsa::SparseAttnArgs a{};
     a.q = q;
@@ -121,6 +122,7 @@ dsa_status launch_latent(const void* q, const void* latent, const int32_t* idx, 
     a.fp8_latent = dt == DSA_FP8_LATENT;
     a.out = out;
     a.lse = lse;
+    a.m = m;
     return hip_status(dsa::launch_sparse_attn_generic(a, stream), "sparse_mla_decode");
 }
 
@@ -171,6 +173,7 @@ dsa_status launch_mha(const void* q, const void* k, const void* v, const int32_t
     a.bf16 = dt == DSA_BF16;
     a.out = out;
     a.lse = lse;
+    a.m = 1;
     return hip_status(dsa::launch_sparse_attn_generic(a, stream), "sparse_mla_prefill");
 }
 
@@ -285,7 +288,7 @@ dsa_status dsa_index_scores(const uint8_t* q_fp8, const float* q_scale, const fl
     DSA_REQUIRE(scores, DSA_ERR_NULL, "index scores: NULL output");
     DSA_REQUIRE(aligned16(scores), DSA_ERR_ALIGN, "index scores: output must be 16-byte aligned");
     dsa::IndexScoresArgs a{q_fp8, q_scale, w, k_fp8, k_scale, len, B, T, H_I, d_I, Lmax, sm_scale_I,
-                           scores, 1};
+                           scores, 1, 1};
     return hip_status(dsa::launch_index_scores(a, stream), "index scores");
 }
 
@@ -300,7 +303,7 @@ dsa_status dsa_topk(const float* scores, const int32_t* len, int B, int T, int L
     const size_t need = dsa::topk_workspace_bytes(B, T, Lmax, k);
     DSA_REQUIRE(need == 0 || (ws && ws_bytes >= need), DSA_ERR_WORKSPACE,
                 "topk: workspace of %zu bytes required", need);
-    dsa::TopkArgs a{scores, len, B, T, Lmax, k, idx};
+    dsa::TopkArgs a{scores, len, B, T, Lmax, k, idx, 1};
     return hip_status(dsa::launch_topk(a, ws, stream), "topk");
 }
 
@@ -320,7 +323,7 @@ dsa_status dsa_sparse_mla_decode(const void* q, const void* latent, const int32_
     DSA_REQUIRE(need == 0 || (ws && ws_bytes >= need && aligned16(ws)), DSA_ERR_WORKSPACE,
                 "sparse_mla_decode: workspace of %zu bytes required (got %zu)", need, ws_bytes);
     return launch_latent(q, latent, idx, len, B, T, H, Dv, Dr, Lmax, k, sm_scale, dt, out, lse, ws,
-                         stream);
+                         stream, 1);
 }
 
 size_t dsa_sparse_mla_prefill_workspace_bytes(int B, int T, int H, int Dqk, int Dv, int topk,
@@ -364,15 +367,19 @@ size_t dsa_layer_step_workspace_bytes(const dsa_layer_args* a) {
 
 dsa_status dsa_layer_step(const dsa_layer_args* a, void* ws, size_t ws_bytes, hipStream_t stream) {
     DSA_REQUIRE(a, DSA_ERR_NULL, "layer step: NULL args");
+    DSA_REQUIRE(a->compress_rate >= 0, DSA_ERR_SHAPE, "layer step: compress_rate=%d", a->compress_rate);
+    const int m = a->compress_rate > 1 ? a->compress_rate : 1;
+    DSA_REQUIRE(m == 1 || a->form == DSA_ATTN_LATENT, DSA_ERR_SHAPE,
+                "layer step: compressed entries (compress_rate > 1) need the latent form");
     dsa_status st = check_index_args(a->q_fp8, a->q_scale, a->w, a->k_fp8, a->k_scale, a->len, a->B,
-                                     a->T, a->H_I, a->d_I, a->Lmax);
+                                     a->T, a->H_I, a->d_I, a->Lmax, m);
     if (st != DSA_OK) return st;
     DSA_REQUIRE(a->topk >= 1, DSA_ERR_SHAPE, "layer step: topk=%d", a->topk);
     DSA_REQUIRE(a->form == DSA_ATTN_LATENT || a->form == DSA_ATTN_MHA, DSA_ERR_DTYPE,
                 "layer step: bad attention form %d", static_cast<int>(a->form));
     if (a->form == DSA_ATTN_LATENT) {
         st = check_latent_args(a->q, a->latent, a->len, a->len, a->B, a->T, a->H, a->Dv, a->Dr,
-                               a->Lmax, a->topk, a->dtype, a->out);
+                               a->Lmax, a->topk, a->dtype, a->out, m);
     } else {
         DSA_REQUIRE(a->Lmax == a->T, DSA_ERR_SHAPE,
                     "layer step (MHA form): the chunk starts at 0, so Lmax must equal T");
@@ -399,18 +406,18 @@ dsa_status dsa_layer_step(const dsa_layer_args* a, void* ws, size_t ws_bytes, hi
     void* att_ws = att_bytes ? p : nullptr;
 
     dsa::IndexScoresArgs ia{a->q_fp8, a->q_scale, a->w, a->k_fp8, a->k_scale, a->len, a->B, a->T,
-                            a->H_I, a->d_I, a->Lmax, a->sm_scale_I, scores, a->scores_out ? 1 : 0};
+                            a->H_I, a->d_I, a->Lmax, a->sm_scale_I, scores, a->scores_out ? 1 : 0, m};
     dsa::prof_mark(stream, dsa::kPhaseIndex);
     st = hip_status(dsa::launch_index_scores(ia, stream), "layer step: index scores");
     if (st != DSA_OK) return st;
     dsa::prof_mark(stream, dsa::kPhaseTopk);
-    dsa::TopkArgs ta{scores, a->len, a->B, a->T, a->Lmax, a->topk, idx};
+    dsa::TopkArgs ta{scores, a->len, a->B, a->T, a->Lmax, a->topk, idx, m};
     st = hip_status(dsa::launch_topk(ta, att_ws, stream), "layer step: topk");
     if (st != DSA_OK) return st;
     dsa::prof_mark(stream, dsa::kPhaseAttention);
     if (a->form == DSA_ATTN_LATENT)
         st = launch_latent(a->q, a->latent, idx, a->len, a->B, a->T, a->H, a->Dv, a->Dr, a->Lmax,
-                           a->topk, a->sm_scale, a->dtype, a->out, a->lse, att_ws, stream);
+                           a->topk, a->sm_scale, a->dtype, a->out, a->lse, att_ws, stream, m);
     else
         st = launch_mha(a->q, a->k, a->v, idx, a->B, a->T, a->H, a->Dqk, a->Dv, a->topk,
                         a->sm_scale, a->dtype, a->out, a->lse, att_ws, stream);

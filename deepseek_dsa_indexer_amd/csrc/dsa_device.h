@@ -49,6 +49,15 @@ __device__ __forceinline__ float recip(float x) { return __builtin_amdgcn_rcpf(x
 // needs, since each softmax row also holds a numerator of at least 1.  2^-inf = 0.
 __device__ __forceinline__ float exp2_num(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Cache rows visible to query row t of a call with T rows over a sequence of len
+// positions, in a cache of Lmax rows.  m = 1: every position is a cache row and row t
+// sits at position min(len, Lmax) - T + t, so that many rows plus one are visible.  m > 1:
+// the cache holds compressed entries, each standing for m consecutive positions, and
+// entry e is available to the query at position p = len - T + t iff e < (p + 1) / m.
+__device__ __forceinline__ int n_visible(int len, int T, int t, int Lmax, int m) {
+    return m == 1 ? min(len, Lmax) - T + t + 1 : min((len - T + t + 1) / m, Lmax);
+}
+
 // Order-preserving map of a float onto an unsigned key: larger float -> larger key.
 __device__ __forceinline__ uint32_t float_key(float f) {
     uint32_t u = __float_as_uint(f);

@@ -26,6 +26,7 @@ struct IndexScoresArgs {
     float sm_scale;
     float* scores;
     int fill_invisible;   // write -inf into every invisible position (else only near pos)
+    int m;                // compress rate (1: every position is a cache row; see n_visible)
 };
 hipError_t launch_index_scores(const IndexScoresArgs& a, hipStream_t stream);
 
@@ -52,6 +53,7 @@ struct TopkArgs {
     const int32_t* len;
     int B, T, Lmax, k;
     int32_t* idx;
+    int m;                // compress rate (see n_visible)
 };
 size_t topk_workspace_bytes(int B, int T, int Lmax, int k);
 hipError_t launch_topk(const TopkArgs& a, void* ws, hipStream_t stream);
@@ -82,6 +84,7 @@ struct SparseAttnArgs {
                             // (row = b * kv_rows + s; strides unused); q, out bf16
     void* out;              // [B,T,H,Dv]
     float* lse;             // [B,T,H] or NULL
+    int m;                  // compress rate (latent form; see n_visible)
 };
 hipError_t launch_sparse_attn_generic(const SparseAttnArgs& a, hipStream_t stream);
 
@@ -91,7 +94,7 @@ bool mla_decode_mfma_supported(int H, int Dv, int Dr, int k, int type);
 size_t mla_decode_workspace_bytes(int B, int T, int H, int Dv, int k);
 hipError_t launch_mla_decode_mfma(const void* q, const void* latent, const int32_t* idx,
                                   const int32_t* len, int B, int T, int H, int Lmax, int k,
-                                  float sm_scale, int type, void* out, float* lse, void* ws,
+                                  float sm_scale, int type, int m, void* out, float* lse, void* ws,
                                   hipStream_t stream);
 
 // Matrix-core path of the MHA prefill form (bf16, Dqk = 192, Dv = 128).

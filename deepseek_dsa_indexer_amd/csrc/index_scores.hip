@@ -3,7 +3,8 @@
 // Computes, for every query row (b,t) and cache position s < Lmax,
 //   I[b,t,s] = k_scale[b,s] * sum_h w'[b,t,h] * max(0, q[b,t,h,:] . k[b,s,:]),
 //   w' = w * q_scale * sm_scale,
-// with -inf where s > pos(b,t) = len[b] - T + t.  The weight fold follows the
+// with -inf where s > pos(b,t) = len[b] - T + t (with compressed entries, m > 1: where
+// s >= (pos + 1) / m; see n_visible).  The weight fold follows the
 // Indexer.forward excerpt ("DeepSeek-V3.2-Exp - Split indexer heads"); the per-head
 // ReLU and weighted head sum follow the score box of "dsa-indexer.excalidraw"; the
 // mask is the -inf-above-the-diagonal mask of the "Causal mask" page.
@@ -114,7 +115,7 @@ void index_scores_kernel(const uint8_t* __restrict__ q, const float* __restrict_
                          const float* __restrict__ w, const uint8_t* __restrict__ k,
                          const float* __restrict__ k_scale, const int32_t* __restrict__ len,
                          int T, int H, int Lmax, float sm_scale, float* __restrict__ scores,
-                         int fill_invisible, int chunks)
+                         int fill_invisible, int chunks, int m)
 {
     __shared__ __attribute__((aligned(16))) uint8_t s_q[QR][kMaxHeads * 128];
     __shared__ __attribute__((aligned(16))) float s_wf[QR][kMaxHeads];
@@ -131,7 +132,7 @@ void index_scores_kernel(const uint8_t* __restrict__ q, const float* __restrict_
         __shared__ int s_num[kThreads / kWave + 2];
         const int nblk = gridDim.y;
         auto count = [&](int s) {
-            return fill_invisible ? nblk : (min(len[s], Lmax) + keys_per_block - 1) / keys_per_block;
+            return fill_invisible ? nblk : (n_visible(len[s], 1, 0, Lmax, m) + keys_per_block - 1) / keys_per_block;
         };
         if (!numbered_block<kThreads>(blockIdx.y * gridDim.x + blockIdx.x, gridDim.x, count, s_num, b, yblk))
             return;
@@ -142,8 +143,11 @@ void index_scores_kernel(const uint8_t* __restrict__ q, const float* __restrict_
         yblk = blockIdx.y;
     }
     const int nrows = min(QR, T - t0);
-    const int pos0 = min(len[b], Lmax) - T + t0;   // position of row t0
-    const int pos_hi = pos0 + nrows - 1;
+    // last visible row of each query row (non-decreasing in t)
+    int last[QR];
+#pragma unroll
+    for (int r = 0; r < QR; ++r) last[r] = n_visible(len[b], T, t0 + min(r, nrows - 1), Lmax, m) - 1;
+    const int pos_hi = last[QR - 1];
 
     const int key_blk = yblk * keys_per_block;
     float* out = scores + (static_cast<size_t>(b) * T + t0) * Lmax;
@@ -238,7 +242,7 @@ void index_scores_kernel(const uint8_t* __restrict__ q, const float* __restrict_
             for (int r = 0; r < QR; ++r) {
                 const float total = chunk_scores(qa[r], wf[r], cur, lane);
                 if (r < nrows && key < Lmax)
-                    out[static_cast<size_t>(r) * Lmax + key] = (key <= pos0 + r) ? total * ks_cur : -INFINITY;
+                    out[static_cast<size_t>(r) * Lmax + key] = (key <= last[r]) ? total * ks_cur : -INFINITY;
             }
         }
 #pragma unroll
@@ -293,7 +297,7 @@ void index_scores_decode_kernel(const uint8_t* __restrict__ q, const float* __re
                                 const float* __restrict__ w, const uint8_t* __restrict__ k,
                                 const float* __restrict__ k_scale, const int32_t* __restrict__ len,
                                 int H, int Lmax, float sm_scale, float* __restrict__ scores,
-                                int fill_invisible, int chunks)
+                                int fill_invisible, int chunks, int m)
 {
     __shared__ __attribute__((aligned(16))) uint8_t s_q[kMaxHeads * 128];
     __shared__ __attribute__((aligned(16))) float s_w[kMaxHeads];
@@ -310,12 +314,12 @@ void index_scores_decode_kernel(const uint8_t* __restrict__ q, const float* __re
     {
         const int nblk = gridDim.y;
         auto count = [&](int sq) {
-            return fill_invisible ? nblk : (min(len[sq], Lmax) + keys_per_block - 1) / keys_per_block;
+            return fill_invisible ? nblk : (n_visible(len[sq], 1, 0, Lmax, m) + keys_per_block - 1) / keys_per_block;
         };
         if (!numbered_block<kThreads>(blockIdx.y * gridDim.x + blockIdx.x, gridDim.x, count, s_num, b, yblk))
             return;
     }
-    const int pos = min(len[b], Lmax) - 1;
+    const int pos = n_visible(len[b], 1, 0, Lmax, m) - 1;
     const int key_blk = yblk * keys_per_block;
     float* out = scores + static_cast<size_t>(b) * Lmax;
     if (key_blk > pos) {                        // the whole block is masked
@@ -413,7 +417,7 @@ hipError_t launch_d(const IndexScoresArgs& a, int chunks, hipStream_t stream) {
     dim3 grid(a.B * row_groups, (a.Lmax + keys_per_block - 1) / keys_per_block);
     hipLaunchKernelGGL((index_scores_kernel<D, QR>), grid, dim3(kThreads), 0, stream,
                        a.q, a.q_scale, a.w, a.k, a.k_scale, a.len, a.T, a.H, a.Lmax, a.sm_scale,
-                       a.scores, a.fill_invisible, chunks);
+                       a.scores, a.fill_invisible, chunks, a.m);
     return hipGetLastError();
 }
 
@@ -432,7 +436,7 @@ hipError_t launch_rows(const IndexScoresArgs& a, hipStream_t stream) {
     dim3 grid(a.B, (a.Lmax + keys_per_block - 1) / keys_per_block);
     hipLaunchKernelGGL((index_scores_decode_kernel<D>), grid, dim3(kThreads), 0, stream,
                        a.q, a.q_scale, a.w, a.k, a.k_scale, a.len, a.H, a.Lmax, a.sm_scale,
-                       a.scores, a.fill_invisible, chunks);
+                       a.scores, a.fill_invisible, chunks, a.m);
     return hipGetLastError();
 }
 

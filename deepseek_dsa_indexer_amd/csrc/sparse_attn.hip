@@ -46,7 +46,7 @@ void sparse_attn_generic_kernel(SparseAttnArgs a)
     const int h = blockIdx.x - row * H;
     const int b = row / a.T;
     const int t = row - b * a.T;
-    const int pos = a.len ? min(a.len[b], a.kv_rows) - a.T + t : t;
+    const int pos = a.len ? n_visible(a.len[b], a.T, t, a.kv_rows, a.m) - 1 : t;   // last visible row
     const int32_t* sel = a.idx + static_cast<size_t>(row) * a.k;
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = threadIdx.x / kWave;
@@ -598,7 +598,7 @@ template <int NHT, bool F8>
 __global__ __launch_bounds__(kMlaThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void mla_decode_mfma_kernel(const uint16_t* __restrict__ q, const uint8_t* __restrict__ latent,
                             const int32_t* __restrict__ idx, const int32_t* __restrict__ len,
-                            int T, int Lmax, int k, int tiles_per_split, int n_splits,
+                            int T, int Lmax, int k, int m, int tiles_per_split, int n_splits,
                             float scale_log2, uint16_t* __restrict__ out,
                             float* __restrict__ lse, uint16_t* __restrict__ part_o,
                             float* __restrict__ part_lse)
@@ -649,7 +649,7 @@ void mla_decode_mfma_kernel(const uint16_t* __restrict__ q, const uint8_t* __res
     }
 
     // selected positions of this split (-1: unused slot or not visible)
-    const int pos = min(seq_len, Lmax) - T + t;
+    const int pos = n_visible(seq_len, T, t, Lmax, m) - 1;   // last visible cache row
 #pragma unroll
     for (int i = 0; i < kSlotIters; ++i) {
         const int j = threadIdx.x + i * kMlaThreads;
@@ -884,7 +884,7 @@ size_t mla_decode_workspace_bytes(int B, int T, int H, int, int k) {
 
 hipError_t launch_mla_decode_mfma(const void* q, const void* latent, const int32_t* idx,
                                   const int32_t* len, int B, int T, int H, int Lmax, int k,
-                                  float sm_scale, int type, void* out, float* lse, void* ws,
+                                  float sm_scale, int type, int m, void* out, float* lse, void* ws,
                                   hipStream_t stream) {
     const int rows = B * T;
     const int s = mla_splits(rows, k);
@@ -901,7 +901,7 @@ hipError_t launch_mla_decode_mfma(const void* q, const void* latent, const int32
     auto kern = H == 128 ? (f8 ? mla_decode_mfma_kernel<8, true> : mla_decode_mfma_kernel<8, false>)
                          : (f8 ? mla_decode_mfma_kernel<4, true> : mla_decode_mfma_kernel<4, false>);
     hipLaunchKernelGGL(kern, dim3(rows * s), dim3(kMlaThreads), 0, stream,
-                       qp, lp, idx, len, T, Lmax, k, tps, s, scale_log2, op, lse, part_o, part_lse);
+                       qp, lp, idx, len, T, Lmax, k, m, tps, s, scale_log2, op, lse, part_o, part_lse);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || s == 1) return e;
     const int parts = (H * (kDv / kCombCols) + 255) / 256;

@@ -1,6 +1,7 @@
 // topk.hip -- per-row top-k of the index scores by radix select (no sort).
 //
-// For row (b,t) with n = pos(b,t) + 1 visible scores, the kernels return the positions
+// For row (b,t) with n = pos(b,t) + 1 visible scores (with compressed entries, m > 1:
+// n = (pos + 1) / m; see n_visible), the kernels return the positions
 // of the min(k, n) largest ones (the Indexer.forward excerpt on the "DeepSeek-V3.2-Exp -
 // Split indexer heads" page keeps the index_topk best, capped at the visible count), in ascending
 // position order, followed by -1 in the unused slots (the warm-up sentinel of the
@@ -41,21 +42,21 @@ struct TopkShared {
     int num[kThreads / kWave + 2];    // block numbering
 };
 
-__device__ __forceinline__ int visible(const int32_t* len, int row, int T, int Lmax) {
+__device__ __forceinline__ int visible(const int32_t* len, int row, int T, int Lmax, int m) {
     const int b = row / T;
     const int t = row - b * T;
-    return min(len[b], Lmax) - T + t + 1;       // clamped: never read past Lmax
+    return n_visible(len[b], T, t, Lmax, m);    // clamped: never read past Lmax
 }
 
 // One workgroup per row (rows of at most 4096 * REG positions when REG > 0).
 template <int REG>
 __global__ __launch_bounds__(kThreads)
 void topk_row_kernel(const float* __restrict__ scores, const int32_t* __restrict__ len,
-                     int T, int Lmax, int k, int32_t* __restrict__ idx)
+                     int T, int Lmax, int k, int m, int32_t* __restrict__ idx)
 {
     __shared__ TopkShared sh;
     const int row = blockIdx.x;
-    const int n = visible(len, row, T, Lmax);
+    const int n = visible(len, row, T, Lmax, m);
     int32_t* out = idx + static_cast<size_t>(row) * k;
     if (n <= k) {                               // every visible position is kept
         for (int j = threadIdx.x; j < k; j += kThreads) out[j] = j < n ? j : -1;
@@ -82,7 +83,7 @@ void topk_row_kernel(const float* __restrict__ scores, const int32_t* __restrict
 template <int REG>
 __global__ __launch_bounds__(kThreads)
 void topk_chunk_kernel(const float* __restrict__ scores, const int32_t* __restrict__ len,
-                       int T, int Lmax, int k, int n_chunks, uint32_t* __restrict__ cand_key,
+                       int T, int Lmax, int k, int m, int n_chunks, uint32_t* __restrict__ cand_key,
                        int32_t* __restrict__ cand_pos)
 {
     __shared__ TopkShared sh;
@@ -92,7 +93,7 @@ void topk_chunk_kernel(const float* __restrict__ scores, const int32_t* __restri
         // one query row per sequence: only the chunks of rows that need a selection,
         // numbered row after row, so unequal lengths still load the XCDs evenly
         auto count = [&](int r) {
-            const int n = visible(len, r, 1, Lmax);
+            const int n = visible(len, r, 1, Lmax, m);
             return n > k ? (n + kChunk - 1) / kChunk : 0;
         };
         if (!numbered_block<kThreads>(blockIdx.x, gridDim.x / n_chunks, count, sh.num, row, c)) return;
@@ -102,23 +103,23 @@ void topk_chunk_kernel(const float* __restrict__ scores, const int32_t* __restri
         row = blockIdx.x / n_chunks;
         c = (blockIdx.x - row * n_chunks + row) % n_chunks;
     }
-    const int n = visible(len, row, T, Lmax);
+    const int n = visible(len, row, T, Lmax, m);
     if (n <= k) return;                         // stage 2 fills such rows directly
     const int base = c * kChunk;
     if (base >= n) return;                      // not read by stage 2
-    const int m = min(kChunk, n - base);
+    const int span = min(kChunk, n - base);
     const size_t slot0 = (static_cast<size_t>(row) * n_chunks + c) * k;
     uint32_t* ck = cand_key + slot0;
     int32_t* cp = cand_pos + slot0;
-    const int kept = min(k, m);
+    const int kept = min(k, span);
     for (int j = kept + threadIdx.x; j < k; j += kThreads) { ck[j] = kNoKey; cp[j] = -1; }
-    if (m <= k) {                               // the whole chunk is a candidate set
+    if (span <= k) {                               // the whole chunk is a candidate set
         const float* sc = scores + static_cast<size_t>(row) * Lmax + base;
-        for (int j = threadIdx.x; j < m; j += kThreads) { ck[j] = score_key(sc[j]); cp[j] = base + j; }
+        for (int j = threadIdx.x; j < span; j += kThreads) { ck[j] = score_key(sc[j]); cp[j] = base + j; }
         return;
     }
     Keys<kThreads, REG, ScoreSrc> ks;
-    ks.init(ScoreSrc{scores + static_cast<size_t>(row) * Lmax + base, m, ((Lmax | base) & 3) == 0}, m);
+    ks.init(ScoreSrc{scores + static_cast<size_t>(row) * Lmax + base, span, ((Lmax | base) & 3) == 0}, span);
     block_select(ks, k, sh.sel, [&](uint32_t slot, int i, uint32_t key) { ck[slot] = key; cp[slot] = base + i; });
 }
 
@@ -127,12 +128,12 @@ void topk_chunk_kernel(const float* __restrict__ scores, const int32_t* __restri
 template <int REG>
 __global__ __launch_bounds__(kThreads)
 void topk_merge_kernel(const uint32_t* __restrict__ cand_key, const int32_t* __restrict__ cand_pos,
-                       const int32_t* __restrict__ len, int T, int Lmax, int k, int n_chunks,
+                       const int32_t* __restrict__ len, int T, int Lmax, int k, int m, int n_chunks,
                        int chunk, int32_t* __restrict__ idx)
 {
     __shared__ TopkShared sh;
     const int row = blockIdx.x;
-    const int n = visible(len, row, T, Lmax);
+    const int n = visible(len, row, T, Lmax, m);
     int32_t* out = idx + static_cast<size_t>(row) * k;
     if (n <= k) {
         for (int j = threadIdx.x; j < k; j += kThreads) out[j] = j < n ? j : -1;
@@ -173,11 +174,11 @@ hipError_t launch_topk(const TopkArgs& a, void* ws, hipStream_t stream) {
     const dim3 block(kThreads);
     if (!two_stage(a.Lmax, a.k)) {
         if (a.Lmax <= 2 * kPerIter)
-            hipLaunchKernelGGL(topk_row_kernel<2>, dim3(rows), block, 0, stream, a.scores, a.len, a.T, a.Lmax, a.k, a.idx);
+            hipLaunchKernelGGL(topk_row_kernel<2>, dim3(rows), block, 0, stream, a.scores, a.len, a.T, a.Lmax, a.k, a.m, a.idx);
         else if (a.Lmax <= kSingleMax)
-            hipLaunchKernelGGL(topk_row_kernel<4>, dim3(rows), block, 0, stream, a.scores, a.len, a.T, a.Lmax, a.k, a.idx);
+            hipLaunchKernelGGL(topk_row_kernel<4>, dim3(rows), block, 0, stream, a.scores, a.len, a.T, a.Lmax, a.k, a.m, a.idx);
         else
-            hipLaunchKernelGGL(topk_row_kernel<0>, dim3(rows), block, 0, stream, a.scores, a.len, a.T, a.Lmax, a.k, a.idx);
+            hipLaunchKernelGGL(topk_row_kernel<0>, dim3(rows), block, 0, stream, a.scores, a.len, a.T, a.Lmax, a.k, a.m, a.idx);
         return hipGetLastError();
     }
     const int nch = n_chunks_for(a.Lmax, a.k);
@@ -186,19 +187,19 @@ hipError_t launch_topk(const TopkArgs& a, void* ws, hipStream_t stream) {
     int32_t* cp = reinterpret_cast<int32_t*>(ck + ncand);
     if (chunk_for(a.Lmax, a.k) == 2 * kPerIter)
         hipLaunchKernelGGL(topk_chunk_kernel<2>, dim3(rows * nch), block, 0, stream, a.scores, a.len,
-                           a.T, a.Lmax, a.k, nch, ck, cp);
+                           a.T, a.Lmax, a.k, a.m, nch, ck, cp);
     else
         hipLaunchKernelGGL(topk_chunk_kernel<4>, dim3(rows * nch), block, 0, stream, a.scores, a.len,
-                           a.T, a.Lmax, a.k, nch, ck, cp);
+                           a.T, a.Lmax, a.k, a.m, nch, ck, cp);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const long long nc = static_cast<long long>(nch) * a.k;
     const int chunk = chunk_for(a.Lmax, a.k);
     if (nc <= kSingleMax)
-        hipLaunchKernelGGL(topk_merge_kernel<4>, dim3(rows), block, 0, stream, ck, cp, a.len, a.T, a.Lmax, a.k, nch,
+        hipLaunchKernelGGL(topk_merge_kernel<4>, dim3(rows), block, 0, stream, ck, cp, a.len, a.T, a.Lmax, a.k, a.m, nch,
                            chunk, a.idx);
     else
-        hipLaunchKernelGGL(topk_merge_kernel<0>, dim3(rows), block, 0, stream, ck, cp, a.len, a.T, a.Lmax, a.k, nch,
+        hipLaunchKernelGGL(topk_merge_kernel<0>, dim3(rows), block, 0, stream, ck, cp, a.len, a.T, a.Lmax, a.k, a.m, nch,
                            chunk, a.idx);
     return hipGetLastError();
 }

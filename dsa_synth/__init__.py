@@ -139,7 +139,7 @@ def pack_latent_fp8(x: np.ndarray) -> np.ndarray:
     return out
 
 
-def make_case(cfg: Config, seqs=None, latent_form: str = "bf16") -> dict:
+def make_case(cfg: Config, seqs=None, latent_form: str = "bf16", compress: int = 1) -> dict:
     """All inputs of one layer step as host numpy arrays.
 
     ``seqs`` restricts the batch to the listed sequence ids (same values as in the
@@ -148,7 +148,9 @@ def make_case(cfg: Config, seqs=None, latent_form: str = "bf16") -> dict:
     (q, latent) or (q, k, v).  ``latent_form="fp8"`` (bf16 latent configurations with
     576-wide rows only) stores the latent cache as 656-byte FP8 rows (pack_latent_fp8)
     drawn from the same float32 values; poisoned rows then hold code 448 with scale
-    1e4 and rope 1e4."""
+    1e4 and rope 1e4.  ``compress = m > 1`` makes the caches compressed entries, each
+    standing for m positions: sequence b (len[b] positions) has len[b] // m valid cache
+    rows, and Lmax counts entries."""
     assert latent_form in ("bf16", "fp8")
     fp8_lat = latent_form == "fp8"
     if fp8_lat:
@@ -185,7 +187,8 @@ def make_case(cfg: Config, seqs=None, latent_form: str = "bf16") -> dict:
         v = np.empty((nb, T, cfg.H, cfg.Dv), adt)
 
     for j, b in enumerate(seqs):
-        L = int(lens[j])
+        L = int(lens[j]) // compress                # valid cache rows
+        assert L <= Lmax, "the cache must hold every valid row"
         c, s = quantize_e4m3fn(_draw(_rng(cfg, 0, b), (T, H_I, D_I), cfg.dist), block)
         q_i[j], q_scale[j] = c, s[..., 0]
         c, s = quantize_e4m3fn(_draw(_rng(cfg, 1, b), (L, D_I), cfg.dist), block)

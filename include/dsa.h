@@ -219,6 +219,14 @@ typedef struct dsa_layer_args {
     int32_t* idx_out;         /* [B,T,topk]                                          */
     float* scores_out;        /* [B,T,Lmax]; when NULL, scores of invisible positions
                                  are not materialised                               */
+    /* Compressed entries (the DeepSeek-V4 mask visualiser's compressed-sparse layers):
+     * 0 or 1 = every position is a cache row (the V3.2 step).  m > 1 = the key cache and
+     * the latent cache hold compressed entries, each standing for m consecutive
+     * positions; len[b] stays the sequence's position count, Lmax is the entry capacity,
+     * and row (b,t) at position p = len[b] - T + t may select entry e iff e < (p + 1) / m
+     * -- rows with no entry get all -1 slots, a zero output and lse = -inf.  Requires
+     * the latent form and len[b] / m <= Lmax (T may then exceed Lmax).                */
+    int compress_rate;
 } dsa_layer_args;
 
 size_t dsa_layer_step_workspace_bytes(const dsa_layer_args* a);

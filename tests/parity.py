@@ -25,7 +25,14 @@ ATTN_ATOL = {"bf16": 2e-2, "f32": 1e-4}
 LSE_ATOL = {"bf16": 1e-3, "f32": 1e-5}
 
 
-def check_scores(gpu: np.ndarray, orc: np.ndarray, lens, T: int, full_mask: bool = True, rows=None):
+def _n_visible(L, T, t, compress):
+    """rows visible to query row t: positions 0..pos, or with compressed entries
+    (compress = m > 1) the entries e < (pos + 1) / m"""
+    return (int(L) - T + t + 1) // compress
+
+
+def check_scores(gpu: np.ndarray, orc: np.ndarray, lens, T: int, full_mask: bool = True, rows=None,
+                 compress: int = 1):
     """gpu/orc: [R, Lmax] rows (b,t) given by `rows` (list of (b, t)) or all of [B,T,Lmax]."""
     if rows is None:
         B = gpu.shape[0]
@@ -34,8 +41,12 @@ def check_scores(gpu: np.ndarray, orc: np.ndarray, lens, T: int, full_mask: bool
         orc = orc.reshape(B * T, -1)
     worst = 0.0
     for r, (b, t) in enumerate(rows):
-        pos = int(lens[b]) - T + t
-        g, o = gpu[r, : pos + 1].astype(np.float64), orc[r, : pos + 1].astype(np.float64)
+        n = _n_visible(lens[b], T, t, compress)
+        if full_mask:
+            assert np.all(np.isneginf(gpu[r, n:])), f"row {(b, t)}: invisible score not -inf"
+        if n == 0:
+            continue
+        g, o = gpu[r, :n].astype(np.float64), orc[r, :n].astype(np.float64)
         assert np.all(np.isfinite(g)), f"row {(b, t)}: non-finite GPU score at a visible position"
         floor = 1e-3 * np.abs(o).max()
         tol = SCORE_RTOL * np.maximum(np.abs(o), floor)
@@ -44,13 +55,11 @@ def check_scores(gpu: np.ndarray, orc: np.ndarray, lens, T: int, full_mask: bool
         assert bad.size == 0, (f"row {(b, t)}: {bad.size} scores off, first at s={bad[0]}: "
                                f"gpu={g[bad[0]]} oracle={o[bad[0]]}")
         worst = max(worst, float((err / np.maximum(tol, 1e-300)).max()) * SCORE_RTOL)
-        if full_mask:
-            assert np.all(np.isneginf(gpu[r, pos + 1:])), f"row {(b, t)}: invisible score not -inf"
     return worst
 
 
 def check_topk(gpu_idx: np.ndarray, orc_scores: np.ndarray, orc_idx: np.ndarray, lens, T: int,
-               k: int, rows=None):
+               k: int, rows=None, compress: int = 1):
     """gpu_idx/orc_idx: [R, k]; orc_scores: [R, Lmax]; rows: list of (b, t)."""
     if rows is None:
         B = gpu_idx.shape[0]
@@ -60,7 +69,7 @@ def check_topk(gpu_idx: np.ndarray, orc_scores: np.ndarray, orc_idx: np.ndarray,
         orc_scores = orc_scores.reshape(B * T, -1)
     swaps = 0
     for r, (b, t) in enumerate(rows):
-        n = int(lens[b]) - T + t + 1
+        n = _n_visible(lens[b], T, t, compress)
         kk = min(k, n)
         g = gpu_idx[r]
         assert np.all(g[kk:] == -1), f"row {(b, t)}: tail is not -1"

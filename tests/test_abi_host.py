@@ -110,9 +110,21 @@ def test_layer_step_validation(lib):
     assert need >= 32 * 8192 * 4 + 32 * 2048 * 4
     assert lib.dsa_layer_step(ctypes.byref(a), None, 0, None) == 5
     assert lib.dsa_layer_step(ctypes.byref(a), ctypes.c_void_p(p + 16), need, None) == 4
+    # compressed entries: T may exceed the entry capacity Lmax; negative rates are rejected
+    a.compress_rate = -1
+    assert lib.dsa_layer_step(ctypes.byref(a), ctypes.c_void_p(p), need, None) == 2
+    a.compress_rate = 4
+    a.T, a.Lmax = 64, 16
+    need_c = lib.dsa_layer_step_workspace_bytes(ctypes.byref(a))
+    assert lib.dsa_layer_step(ctypes.byref(a), None, 0, None) == 5      # validation passed
+    a.T, a.Lmax = 1, 8192
     a.form = N.DSA_ATTN_MHA
     a.k = a.v = p
     a.Dqk = 192
+    assert lib.dsa_layer_step(ctypes.byref(a), ctypes.c_void_p(p), need, None) == 2  # MHA + compression
+    assert b"latent form" in lib.dsa_last_error()
+    a.compress_rate = 0
+    assert need_c > 0
     assert lib.dsa_layer_step(ctypes.byref(a), ctypes.c_void_p(p), need, None) == 2  # Lmax != T
 
 

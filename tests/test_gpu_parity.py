@@ -379,6 +379,48 @@ def test_layer_step_fp8_latent(dsa, orc, name, cfg):
     check_attention(_np_out(out), lse.cpu().numpy(), ro2, rl2, "bf16")
 
 
+COMPRESSED_CASES = [
+    # name, config (lens in positions, Lmax in entries), compress rate
+    ("prefill_t64_m4", _small("decode_v32", name="cp1", B=1, T=64, Lmax=64, k=8, seed=501), 4),
+    ("decode_ragged_m4", _small("decode_ragged", name="cp2", B=5, Lmax=750, lens="ragged:10:3000",
+                                k=64, seed=502), 4),
+    ("ragged_t3_m2", _small("decode_ragged", name="cp3", B=4, T=3, Lmax=3000,
+                            lens="ragged:1024:6000", seed=503), 2),
+    # more than 16384 visible entries: the two-stage top-k, two rows per sequence
+    ("long_t2_m4", _small("decode_long", name="cp4", B=2, T=2, Lmax=20000,
+                          lens="ragged:70000:80000", seed=504), 4),
+]
+
+
+@pytest.mark.parametrize("name,cfg,m", COMPRESSED_CASES, ids=[c[0] for c in COMPRESSED_CASES])
+def test_layer_step_compressed_entries(dsa, orc, name, cfg, m):
+    """Caches of compressed entries (each standing for m positions): row (b,t) may select
+    entry e iff e < (pos + 1) / m; rows with no entry get -1 slots, a zero output and
+    lse = -inf."""
+    _say(f"[layer_step compressed] {name} m={m}")
+    c = S.make_case(cfg, compress=m)
+    d = _dev(c)
+    step = dsa.LayerStep(d["q_i"], d["q_scale"], d["w"], d["k_i"], d["k_scale"], d["lens"],
+                         cfg.sm_scale_i, cfg.k, d["q"], cfg.sm_scale, latent=d["latent"],
+                         Dv=cfg.Dv, want_idx=True, want_scores=True, compress_rate=m)
+    out, lse = step()
+    torch.cuda.synchronize()
+    ro, rl, ridx, rsc = orc.layer_step_latent(c["q_i"], c["q_scale"], c["w"], c["k_i"],
+                                              c["k_scale"], c["lens"], cfg.sm_scale_i, cfg.k,
+                                              c["q"], c["latent"], cfg.Dv, cfg.sm_scale,
+                                              want_scores=True, compress=m)
+    check_scores(step.scores.cpu().numpy(), rsc, c["lens"], cfg.T, compress=m)
+    gidx = step.idx.cpu().numpy()
+    check_topk(gidx, rsc, ridx, c["lens"], cfg.T, cfg.k, compress=m)
+    ro2, rl2 = orc.sparse_mla_decode(c["q"], c["latent"], gidx, c["lens"], cfg.Dv, cfg.sm_scale,
+                                     compress=m)
+    check_attention(_np_out(out), lse.cpu().numpy(), ro2, rl2, cfg.attn_dtype)
+    if name.startswith("prefill"):
+        # the first m - 1 positions have no entry yet: -1 slots, zero rows, lse -inf
+        assert np.all(gidx[0, :m - 1] == -1)
+        assert np.all(_np_out(out)[0, :m - 1] == 0) and np.all(np.isneginf(lse.cpu().numpy()[0, :m - 1]))
+
+
 def test_layer_step_mha_small(dsa, orc):
     _say("[layer_step mha] small")
     cfg = _small("prefill_chunk", name="pm", T=96, Lmax=96, H=4, k=24, seed=404)
