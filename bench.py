@@ -95,15 +95,15 @@ def cpu_baseline(cfg, n_seqs: int, min_seconds: float = 10.0, latent_form: str =
     """The oracle, untuned, on a bounded sample of the same workload, scaled to a step.
 
     Decode: the whole layer step for the first ``n_seqs`` sequences.  Chunked prefill
-    (one sequence): ``4 * n_seqs`` query rows spread evenly over the chunk, each scored
-    against its causal keys, selected and attended; the step is T rows.  The sample is
+    (one sequence, either form): ``4 * n_seqs`` query rows spread evenly over the chunk,
+    each scored against its causal keys, selected and attended; the step is T rows.  The sample is
     repeated until ``min_seconds`` of wall time have accumulated."""
     import numpy as np
 
     import dsa_synth as S
     import oracle as orc
     orc.build(force=False)
-    if cfg.form == "latent":
+    if cfg.form == "latent" and cfg.T == 1:
         seqs = list(range(min(n_seqs, cfg.B)))
         c = S.make_case(cfg, seqs=seqs, latent_form=latent_form)
 
@@ -128,8 +128,12 @@ def cpu_baseline(cfg, n_seqs: int, min_seconds: float = 10.0, latent_form: str =
                                       c["w"][:, t:t + 1], c["k_i"], c["k_scale"],
                                       np.array([t + 1], np.int32), cfg.sm_scale_i)
                 idx[:, t] = orc.topk(sc, np.array([t + 1], np.int32), cfg.k)[:, 0]
-            orc.sparse_mha_prefill_rows(c["q"], c["k"], c["v"], idx, cfg.sm_scale,
-                                        [(0, t) for t in rows])
+                if cfg.form == "latent":
+                    orc.sparse_mla_decode(c["q"][:, t:t + 1], c["latent"], idx[:, t:t + 1],
+                                          np.array([t + 1], np.int32), cfg.Dv, cfg.sm_scale)
+            if cfg.form != "latent":
+                orc.sparse_mha_prefill_rows(c["q"], c["k"], c["v"], idx, cfg.sm_scale,
+                                            [(0, t) for t in rows])
         frac = n_rows / cfg.T
         keys = float(sum(t + 1 for t in rows))
         threads = orc.max_threads()

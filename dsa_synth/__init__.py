@@ -78,6 +78,11 @@ CONFIGS = {
     "decode_ragged": Config("decode_ragged", "latent", B=64, T=1, Lmax=65536,
                             lens="ragged:1024:65536", H_I=64, D_I=128, k=2048, H=128, Dv=512,
                             Dr=64, Dqk=0, attn_dtype="bf16", dist="student_t3", seed=5),
+    # the prefill chunk in the absorbed (latent, MQA) form instead of the MHA form: the
+    # same indexer work, attention of 128 heads over the selected 576-wide latent rows
+    "prefill_chunk_latent": Config("prefill_chunk_latent", "latent", B=1, T=8192, Lmax=8192,
+                                   lens="full", H_I=64, D_I=128, k=2048, H=128, Dv=512, Dr=64,
+                                   Dqk=0, attn_dtype="bf16", dist="normal", seed=6),
 }
 
 

@@ -326,6 +326,9 @@ LAYER_CASES = [
     # rows per sequence, indexer blocks of two rows
     ("long_t2", _small("decode_long", name="lt2", B=2, T=2, Lmax=40000,
                        lens="ragged:20000:40000", seed=206)),
+    # a prefill chunk in the absorbed (latent) form: 256 query rows over their own chunk
+    ("prefill_latent_t256", _small("prefill_chunk_latent", name="pl", T=256, Lmax=256, k=64,
+                                   seed=209)),
 ]
 
 
