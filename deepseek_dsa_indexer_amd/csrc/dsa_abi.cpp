@@ -128,7 +128,7 @@ dsa_status launch_latent(const void* q, const void* latent, const int32_t* idx, 
 
 size_t latent_ws(int B, int T, int H, int Dv, int Dr, int k, dsa_dtype dt) {
     if (dsa::mla_decode_mfma_supported(H, Dv, Dr, k, dt))
-        return dsa::mla_decode_workspace_bytes(B, T, H, Dv, k);
+        return dsa::mla_decode_workspace_bytes(B, T, H, Dv, k, dt);
     return 0;
 }
 

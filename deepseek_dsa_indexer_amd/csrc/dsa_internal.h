@@ -91,7 +91,7 @@ hipError_t launch_sparse_attn_generic(const SparseAttnArgs& a, hipStream_t strea
 // Matrix-core path of the absorbed latent form (bf16 or FP8 rows, Dv = 512, Dr = 64,
 // H = 64 or 128).  `type` is a LatentType.
 bool mla_decode_mfma_supported(int H, int Dv, int Dr, int k, int type);
-size_t mla_decode_workspace_bytes(int B, int T, int H, int Dv, int k);
+size_t mla_decode_workspace_bytes(int B, int T, int H, int Dv, int k, int type);
 hipError_t launch_mla_decode_mfma(const void* q, const void* latent, const int32_t* idx,
                                   const int32_t* len, int B, int T, int H, int Lmax, int k,
                                   float sm_scale, int type, int m, void* out, float* lse, void* ws,

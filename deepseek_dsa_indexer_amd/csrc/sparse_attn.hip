@@ -133,8 +133,9 @@ void sparse_attn_generic_kernel(SparseAttnArgs a)
 // ------------------------------------------------------------------ matrix-core latent path
 //
 // One workgroup (8 waves, two per SIMD) owns one query row (b,t), one split of its k
-// slots and all heads (64 or 128), so every selected latent row is gathered from memory
-// once per row and split.  Per tile of 32 selected positions:
+// slots and 64 or 128 heads (128 heads of few rows go to two 64-head workgroups, which
+// share each gathered tile through their XCD's L2), so every selected latent row is
+// fetched from memory once per row and split.  Per tile of 32 selected positions:
 //   gather   32 latent rows -> LDS with direct global->LDS 16-byte loads.  Four tile
 //            buffers are distinct LDS objects; two tiles stay in flight while one is
 //            multiplied against Q and the previous one against P.  The 16-byte chunks
@@ -599,23 +600,27 @@ __global__ __launch_bounds__(kMlaThreads) __attribute__((amdgpu_waves_per_eu(2, 
 void mla_decode_mfma_kernel(const uint16_t* __restrict__ q, const uint8_t* __restrict__ latent,
                             const int32_t* __restrict__ idx, const int32_t* __restrict__ len,
                             int T, int Lmax, int k, int m, int tiles_per_split, int n_splits,
-                            float scale_log2, uint16_t* __restrict__ out,
+                            int H_total, float scale_log2, uint16_t* __restrict__ out,
                             float* __restrict__ lse, uint16_t* __restrict__ part_o,
                             float* __restrict__ part_lse)
 {
-    constexpr int H = NHT * 16;
+    constexpr int H = NHT * 16;                        // heads of this workgroup
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);   // wave-uniform: SGPR
     const int g = lane >> 4;
     const int n = lane & 15;
     if (wave < 4) __builtin_amdgcn_s_setprio(1);
 
-    // Consecutive workgroups go to different XCDs (round robin over 8), so block
-    // split * rows + row puts every split of a row on the same XCD whenever rows is a
-    // multiple of 8: the row's queries are then fetched into one L2 and shared.
-    const int rows = gridDim.x / n_splits;
+    // Workgroup (row, split, head part): H_total / H parts of H heads each.  Consecutive
+    // workgroups go to different XCDs (round robin over 8), so block
+    // (part * n_splits + split) * rows + row puts every workgroup of a row on the same
+    // XCD whenever rows is a multiple of 8: the row's queries and selected latent rows
+    // are then fetched into one L2 and shared.
+    const int rows = gridDim.x / (n_splits * (H_total / H));
     const int row = blockIdx.x % rows;
-    const int split = blockIdx.x / rows;
+    const int rest = blockIdx.x / rows;
+    const int split = rest % n_splits;
+    const int head0 = (rest / n_splits) * H;
     const int b = row / T;
     const int t = row - b * T;
 
@@ -643,7 +648,7 @@ void mla_decode_mfma_kernel(const uint16_t* __restrict__ q, const uint8_t* __res
     {
         // queries of head tile `wave` as MFMA B operands: head 16 wave + n, dims 32 ds + 8 g
         const int head = wave < NHT ? 16 * wave + n : n;
-        const uint16_t* qrow = q + (static_cast<size_t>(row) * H + head) * kDq + 8 * g;
+        const uint16_t* qrow = q + (static_cast<size_t>(row) * H_total + head0 + head) * kDq + 8 * g;
 #pragma unroll
         for (int ds = 0; ds < kDs; ++ds) st.qreg[ds] = *reinterpret_cast<const v8bf*>(qrow + 32 * ds);
     }
@@ -770,8 +775,8 @@ void mla_decode_mfma_kernel(const uint16_t* __restrict__ q, const uint8_t* __res
         }
     }
     __syncthreads();
-    uint16_t* dst = n_splits == 1 ? out + static_cast<size_t>(row) * H * kDv
-                                  : part_o + (static_cast<size_t>(row) * n_splits + split) * H * kDv;
+    uint16_t* dst = n_splits == 1 ? out + (static_cast<size_t>(row) * H_total + head0) * kDv
+                                  : part_o + ((static_cast<size_t>(row) * n_splits + split) * H_total + head0) * kDv;
     for (int c = threadIdx.x; c < H * (kDv / 8); c += kMlaThreads) {
         const int head = c / (kDv / 8);
         const int lc = c - head * (kDv / 8);
@@ -784,9 +789,9 @@ void mla_decode_mfma_kernel(const uint16_t* __restrict__ q, const uint8_t* __res
         const float l = g_l[head];
         const float lse2 = l > 0.f ? g_m[head] + log2f(l) : -INFINITY;
         if (n_splits == 1) {
-            if (lse) lse[static_cast<size_t>(row) * H + head] = lse2 * kLn2;
+            if (lse) lse[static_cast<size_t>(row) * H_total + head0 + head] = lse2 * kLn2;
         } else {
-            part_lse[(static_cast<size_t>(row) * n_splits + split) * H + head] = lse2;
+            part_lse[(static_cast<size_t>(row) * n_splits + split) * H_total + head0 + head] = lse2;
         }
     }
 }
@@ -875,9 +880,31 @@ bool mla_decode_mfma_supported(int H, int Dv, int Dr, int k, int type) {
            (H == 64 || H == 128) && k <= kMaxSplits * kMaxSlots;
 }
 
-size_t mla_decode_workspace_bytes(int B, int T, int H, int, int k) {
+// Launch shape of the matrix-core path.  128 heads go to two 64-head workgroups per
+// (row, split) -- half the queries per workgroup, half the partial rows written, twice
+// the workgroups for the same key splits -- when the key splits alone leave CUs idle
+// (at most 16 splits: B = 8 decode ran 128 workgroups), and for bf16 rows when a row
+// would need 8 or more splits (measured: decode B = 32 attention + combine 48.2 ->
+// 45.8 us).  Otherwise not: at 64 rows (4 splits) and for FP8 rows, whose QK waves each
+// widen the whole tile whatever their head count, the 64-head form measured slower.
+struct MlaPlan {
+    int nht;          // 16-head tiles per workgroup
+    int parts;        // head parts per row
+    int splits;       // key splits per row
+};
+MlaPlan mla_plan(int rows, int H, int k, int type) {
+    MlaPlan p;
+    const int s1 = mla_splits(rows, k);
+    const bool idle = rows * s1 < 256;
+    p.parts = (H == 128 && rows < 256 && (idle || (type == kLatBf16 && s1 >= 8))) ? 2 : 1;
+    p.nht = H / 16 / p.parts;
+    p.splits = p.parts == 1 ? s1 : mla_splits(rows * p.parts, k);
+    return p;
+}
+
+size_t mla_decode_workspace_bytes(int B, int T, int H, int, int k, int type) {
     const int rows = B * T;
-    const int s = mla_splits(rows, k);
+    const int s = mla_plan(rows, H, k, type).splits;
     if (s == 1) return 0;
     return static_cast<size_t>(rows) * s * H * (kDv * sizeof(uint16_t) + sizeof(float)) + 256;
 }
@@ -887,7 +914,8 @@ hipError_t launch_mla_decode_mfma(const void* q, const void* latent, const int32
                                   float sm_scale, int type, int m, void* out, float* lse, void* ws,
                                   hipStream_t stream) {
     const int rows = B * T;
-    const int s = mla_splits(rows, k);
+    const MlaPlan plan = mla_plan(rows, H, k, type);
+    const int s = plan.splits;
     const int n_tiles = (k + kKt - 1) / kKt;
     const int tps = (n_tiles + s - 1) / s;
     uint16_t* part_o = static_cast<uint16_t*>(ws);
@@ -898,10 +926,11 @@ hipError_t launch_mla_decode_mfma(const void* q, const void* latent, const int32
     auto lp = static_cast<const uint8_t*>(latent);
     auto op = static_cast<uint16_t*>(out);
     const bool f8 = type == kLatFp8;
-    auto kern = H == 128 ? (f8 ? mla_decode_mfma_kernel<8, true> : mla_decode_mfma_kernel<8, false>)
-                         : (f8 ? mla_decode_mfma_kernel<4, true> : mla_decode_mfma_kernel<4, false>);
-    hipLaunchKernelGGL(kern, dim3(rows * s), dim3(kMlaThreads), 0, stream,
-                       qp, lp, idx, len, T, Lmax, k, m, tps, s, scale_log2, op, lse, part_o, part_lse);
+    auto kern = plan.nht == 8 ? (f8 ? mla_decode_mfma_kernel<8, true> : mla_decode_mfma_kernel<8, false>)
+                              : (f8 ? mla_decode_mfma_kernel<4, true> : mla_decode_mfma_kernel<4, false>);
+    hipLaunchKernelGGL(kern, dim3(rows * s * plan.parts), dim3(kMlaThreads), 0, stream,
+                       qp, lp, idx, len, T, Lmax, k, m, tps, s, H, scale_log2, op, lse, part_o,
+                       part_lse);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || s == 1) return e;
     const int parts = (H * (kDv / kCombCols) + 255) / 256;

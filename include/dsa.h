@@ -154,8 +154,9 @@ dsa_status dsa_topk(const float* scores, const int32_t* len, int B, int T, int L
  * DSA_FP8_LATENT (the vector-ALU path keeps all k logits in LDS: 4 (Dv + Dr + k) <= 65536
  * bytes); the BF16 and FP8_LATENT shape H in {64, 128}, Dv = 512, Dr = 64, k <= 16384
  * runs on the matrix-core path, which splits each row's slots over up to 16 workgroups
- * and needs a workspace for their partial results (dsa_sparse_mla_decode_workspace_bytes();
- * 0 when the rows fill the GPU without splitting).  A DSA_FP8_LATENT dtype with other
+ * (and the 128 heads of few rows over two) and needs a workspace for their partial
+ * results (dsa_sparse_mla_decode_workspace_bytes(); 0 when the rows fill the GPU without
+ * splitting the slots).  A DSA_FP8_LATENT dtype with other
  * widths is DSA_ERR_DTYPE.
  */
 size_t dsa_sparse_mla_decode_workspace_bytes(int B, int T, int H, int Dv, int Dr, int k,
