@@ -84,7 +84,7 @@ template <int REG>
 __global__ __launch_bounds__(kThreads)
 void topk_chunk_kernel(const float* __restrict__ scores, const int32_t* __restrict__ len,
                        int T, int Lmax, int k, int m, int n_chunks, uint32_t* __restrict__ cand_key,
-                       int32_t* __restrict__ cand_pos, uint32_t* __restrict__ cand_bound)
+                       int32_t* __restrict__ cand_pos)
 {
     __shared__ TopkShared sh;
     constexpr int kChunk = REG * kPerIter;
@@ -116,20 +116,11 @@ void topk_chunk_kernel(const float* __restrict__ scores, const int32_t* __restri
     if (span <= k) {                               // the whole chunk is a candidate set
         const float* sc = scores + static_cast<size_t>(row) * Lmax + base;
         for (int j = threadIdx.x; j < span; j += kThreads) { ck[j] = score_key(sc[j]); cp[j] = base + j; }
-        if (threadIdx.x == 0) cand_bound[static_cast<size_t>(row) * n_chunks + c] = kNoKey;   // no bound
         return;
     }
-    // The row's k-th largest key is at least the smallest, over its L live chunks, of each
-    // chunk's ceil(k / L)-th largest key (those L * ceil(k / L) >= k keys are all at least
-    // that large), so a lower bound of this chunk's ceil(k / L)-th largest lets stage 2
-    // skip every candidate below the smallest of the chunks' bounds.
-    const int live_chunks = (n + kChunk - 1) / kChunk;
-    const uint32_t kb = static_cast<uint32_t>((k + live_chunks - 1) / live_chunks);
     Keys<kThreads, REG, ScoreSrc> ks;
     ks.init(ScoreSrc{scores + static_cast<size_t>(row) * Lmax + base, span, ((Lmax | base) & 3) == 0}, span);
-    block_select(ks, k, sh.sel, [&](uint32_t slot, int i, uint32_t key) { ck[slot] = key; cp[slot] = base + i; },
-                 kb);
-    if (threadIdx.x == 0) cand_bound[static_cast<size_t>(row) * n_chunks + c] = sh.sel.bound;
+    block_select(ks, k, sh.sel, [&](uint32_t slot, int i, uint32_t key) { ck[slot] = key; cp[slot] = base + i; });
 }
 
 // Two-stage form, stage 2: top-k of a row's candidates (REG = 0: re-read them), those
@@ -137,9 +128,8 @@ void topk_chunk_kernel(const float* __restrict__ scores, const int32_t* __restri
 template <int REG>
 __global__ __launch_bounds__(kThreads)
 void topk_merge_kernel(const uint32_t* __restrict__ cand_key, const int32_t* __restrict__ cand_pos,
-                       const int32_t* __restrict__ len, const uint32_t* __restrict__ cand_bound,
-                       int T, int Lmax, int k, int m, int n_chunks, int chunk,
-                       int32_t* __restrict__ idx)
+                       const int32_t* __restrict__ len, int T, int Lmax, int k, int m, int n_chunks,
+                       int chunk, int32_t* __restrict__ idx)
 {
     __shared__ TopkShared sh;
     const int row = blockIdx.x;
@@ -149,16 +139,11 @@ void topk_merge_kernel(const uint32_t* __restrict__ cand_key, const int32_t* __r
         for (int j = threadIdx.x; j < k; j += kThreads) out[j] = j < n ? j : -1;
         return;
     }
-    const int live_chunks = (n + chunk - 1) / chunk;
-    const int nc = live_chunks * k;
-    // candidates below every chunk's bound cannot be among the row's k largest (stage 1)
-    uint32_t floor_key = 0xffffffffu;
-    for (int c = 0; c < live_chunks; ++c)
-        floor_key = min(floor_key, cand_bound[static_cast<size_t>(row) * n_chunks + c]);
+    const int nc = (n + chunk - 1) / chunk * k;
     const size_t off = static_cast<size_t>(row) * n_chunks * k;
     const int32_t* cp = cand_pos + off;
     Keys<kThreads, REG, CandSrc> ks;
-    ks.init(CandSrc{cand_key + off, nc, ((n_chunks * k) & 3) == 0, floor_key}, nc);   // 16-byte aligned rows
+    ks.init(CandSrc{cand_key + off, nc, ((n_chunks * k) & 3) == 0}, nc);   // 16-byte aligned rows
     if (k <= kStagedOut) {
         block_select(ks, k, sh.sel, [&](uint32_t slot, int i, uint32_t) { sh.out[slot] = i; });
         __syncthreads();
@@ -181,8 +166,7 @@ bool two_stage(int Lmax, int k) { return Lmax > kSingleMax && k < 2 * kPerIter; 
 
 size_t topk_workspace_bytes(int B, int T, int Lmax, int k) {
     if (!two_stage(Lmax, k)) return 0;
-    const size_t slots = static_cast<size_t>(B) * T * n_chunks_for(Lmax, k);
-    return slots * k * (sizeof(uint32_t) + sizeof(int32_t)) + slots * sizeof(uint32_t) + 256;
+    return static_cast<size_t>(B) * T * n_chunks_for(Lmax, k) * k * (sizeof(uint32_t) + sizeof(int32_t)) + 256;
 }
 
 hipError_t launch_topk(const TopkArgs& a, void* ws, hipStream_t stream) {
@@ -201,23 +185,22 @@ hipError_t launch_topk(const TopkArgs& a, void* ws, hipStream_t stream) {
     const size_t ncand = static_cast<size_t>(rows) * nch * a.k;
     uint32_t* ck = static_cast<uint32_t*>(ws);
     int32_t* cp = reinterpret_cast<int32_t*>(ck + ncand);
-    uint32_t* cb = reinterpret_cast<uint32_t*>(cp + ncand);          // one bound per chunk
     if (chunk_for(a.Lmax, a.k) == 2 * kPerIter)
         hipLaunchKernelGGL(topk_chunk_kernel<2>, dim3(rows * nch), block, 0, stream, a.scores, a.len,
-                           a.T, a.Lmax, a.k, a.m, nch, ck, cp, cb);
+                           a.T, a.Lmax, a.k, a.m, nch, ck, cp);
     else
         hipLaunchKernelGGL(topk_chunk_kernel<4>, dim3(rows * nch), block, 0, stream, a.scores, a.len,
-                           a.T, a.Lmax, a.k, a.m, nch, ck, cp, cb);
+                           a.T, a.Lmax, a.k, a.m, nch, ck, cp);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const long long nc = static_cast<long long>(nch) * a.k;
     const int chunk = chunk_for(a.Lmax, a.k);
     if (nc <= kSingleMax)
-        hipLaunchKernelGGL(topk_merge_kernel<4>, dim3(rows), block, 0, stream, ck, cp, a.len, cb, a.T, a.Lmax, a.k, a.m,
-                           nch, chunk, a.idx);
+        hipLaunchKernelGGL(topk_merge_kernel<4>, dim3(rows), block, 0, stream, ck, cp, a.len, a.T, a.Lmax, a.k, a.m, nch,
+                           chunk, a.idx);
     else
-        hipLaunchKernelGGL(topk_merge_kernel<0>, dim3(rows), block, 0, stream, ck, cp, a.len, cb, a.T, a.Lmax, a.k, a.m,
-                           nch, chunk, a.idx);
+        hipLaunchKernelGGL(topk_merge_kernel<0>, dim3(rows), block, 0, stream, ck, cp, a.len, a.T, a.Lmax, a.k, a.m, nch,
+                           chunk, a.idx);
     return hipGetLastError();
 }
 

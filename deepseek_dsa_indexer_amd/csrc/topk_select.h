@@ -33,7 +33,6 @@ struct SelectShared {
     uint32_t bin;
     uint32_t need;
     uint32_t bin_count;
-    uint32_t bound;         // a lower bound of the kb-th largest key (see block_select)
 };
 
 __device__ __forceinline__ uint32_t score_key(float f) {
@@ -91,11 +90,10 @@ struct ScoreSrc {                       // a row of scores, indices < n visible
     }
 };
 
-struct CandSrc {                        // candidate keys of a row; keys below `floor` drop out
+struct CandSrc {                        // candidate keys of a row
     const uint32_t* key;
     int n;
     bool vec4;
-    uint32_t floor;
     __device__ __forceinline__ void load4(int i0, uint32_t (&k4)[kSelPerThread]) const {
         if (vec4 && i0 + kSelPerThread <= n) {
             const uint4 v = *reinterpret_cast<const uint4*>(key + i0);
@@ -104,8 +102,6 @@ struct CandSrc {                        // candidate keys of a row; keys below `
 #pragma unroll
             for (int j = 0; j < kSelPerThread; ++j) k4[j] = i0 + j < n ? key[i0 + j] : kNoKey;
         }
-#pragma unroll
-        for (int j = 0; j < kSelPerThread; ++j) k4[j] = k4[j] >= floor ? k4[j] : kNoKey;
     }
 };
 
@@ -166,11 +162,10 @@ struct Keys {
 };
 
 // Select the k largest live keys (k < number of live keys) of `ks`; store(slot, index,
-// key) receives slots 0..k-1 in ascending index order.  With 0 < kb <= k, sh.bound also
-// gets a lower bound of the kb-th largest key: the lower edge of its first-level bin.
+// key) receives slots 0..k-1 in ascending index order.
 template <int NT, int REG, typename Src, typename Store>
 __device__ __forceinline__ void block_select(Keys<NT, REG, Src>& ks, int k, SelectShared<NT>& sh,
-                                             Store&& store, uint32_t kb = 0) {
+                                             Store&& store) {
     constexpr int kWaves = NT / kWave;
     constexpr int kBpt = kSelBins / NT;             // histogram bins per thread in the scan
     static_assert(kSelBins % NT == 0 && NT % kWave == 0, "bins must split evenly over the block");
@@ -190,7 +185,6 @@ __device__ __forceinline__ void block_select(Keys<NT, REG, Src>& ks, int k, Sele
     uint32_t lo = sh.red[0][0], hi = sh.red[1][0];
 #pragma unroll
     for (int w = 1; w < kWaves; ++w) { lo = min(lo, sh.red[0][w]); hi = max(hi, sh.red[1][w]); }
-    if (threadIdx.x == 0) sh.bound = lo;      // stays if every key is equal
 
     // ---- narrow [lo, hi] to the class of the k-th largest key
     uint32_t need = static_cast<uint32_t>(k);
@@ -231,8 +225,6 @@ __device__ __forceinline__ void block_select(Keys<NT, REG, Src>& ks, int k, Sele
                 sh.need = need - above;
                 sh.bin_count = cb[u];
             }
-            if (level == 0 && above < kb && kb <= above + cb[u])
-                sh.bound = lo + (static_cast<uint32_t>(kSelBins - 1 - kBpt * static_cast<int>(threadIdx.x) - u) << shift);
             above += cb[u];
         }
         __syncthreads();
