@@ -329,6 +329,9 @@ LAYER_CASES = [
     # a prefill chunk in the absorbed (latent) form: 256 query rows over their own chunk
     ("prefill_latent_t256", _small("prefill_chunk_latent", name="pl", T=256, Lmax=256, k=64,
                                    seed=209)),
+    # rows of 8192 positions with k = 2000: the last tile of the selection is partly unused
+    ("k2000_l8192", _small("decode_v32", name="fk", B=2, Lmax=8192, k=2000, lens="ragged:7000:8192",
+                           seed=210)),
 ]
 
 
@@ -444,7 +447,8 @@ def test_layer_step_mha_small(dsa, orc):
     check_attention(_np_out(out), lse.cpu().numpy(), ro, rl, "bf16")
 
 
-@pytest.mark.parametrize("B,Lmax,lo,seed", [(3, 20000, 1024, 207), (9, 36000, 700, 208)])
+@pytest.mark.parametrize("B,Lmax,lo,seed", [(3, 20000, 1024, 207), (9, 36000, 700, 208),
+                                            (3, 8000, 700, 209)])
 def test_layer_step_without_intermediates(dsa, orc, B, Lmax, lo, seed):
     """The production configuration (scores and indices kept in the workspace, invisible
     scores never written, key blocks and top-k chunks numbered over the visible range
