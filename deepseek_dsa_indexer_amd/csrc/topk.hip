@@ -10,8 +10,7 @@
 //
 // Method (topk_select.h): scores map to order-preserving 32-bit keys; range-adaptive
 // LDS histogram levels narrow the range that holds the k-th largest key; one ordered
-// compaction writes the result.  Selected positions are staged in LDS and written out
-// coalesced.
+// compaction writes the result.
 //
 // Rows up to 16384 positions: one workgroup per row.  Longer rows (a workgroup can keep
 // only ~64 KB of loads in flight, far too little for one row of a long context) take
@@ -64,15 +63,10 @@ void topk_row_kernel(const float* __restrict__ scores, const int32_t* __restrict
     }
     Keys<kThreads, REG, ScoreSrc> ks;
     ks.init(ScoreSrc{scores + static_cast<size_t>(row) * Lmax, n, (Lmax & 3) == 0}, n);
-    if (k <= kStagedOut) {
-        // slots arrive scattered; staging them in LDS turns k scattered 4-byte stores
-        // into one coalesced pass
-        block_select(ks, k, sh.sel, [&](uint32_t slot, int i, uint32_t) { sh.out[slot] = i; });
-        __syncthreads();
-        for (int j = threadIdx.x; j < k; j += kThreads) out[j] = sh.out[j];
-    } else {
-        block_select(ks, k, sh.sel, [&](uint32_t slot, int i, uint32_t) { out[slot] = i; });
-    }
+    // Direct stores: the slots of neighbouring lanes lie close together, so a store
+    // instruction touches few cache lines (staging the slots in LDS first measured
+    // 9.9 us against 9.5 us for 32 rows of 8192 keys).
+    block_select(ks, k, sh.sel, [&](uint32_t slot, int i, uint32_t) { out[slot] = i; });
 }
 
 // Two-stage form, stage 1: chunk c of row r (its visible positions among [C c, C c + C),
