@@ -216,4 +216,29 @@ __device__ __forceinline__ bool numbered_block(int id, int n_seq, Count count, i
     return true;
 }
 
+// The same numbering for n_seq <= 64, worked out by every wave on its own: lane l
+// counts sequence l, a wave scan gives each sequence's first id, and the lane whose
+// range holds `id` names the sequence.  No LDS and no block barrier.
+template <typename Count>
+__device__ __forceinline__ bool numbered_block_wave(int id, int n_seq, Count count, int& seq, int& blk) {
+    const int lane = threadIdx.x & (kWave - 1);
+    const int mine = lane < n_seq ? count(lane) : 0;
+    const int inc = static_cast<int>(wave_inclusive_scan(static_cast<uint32_t>(mine), lane));
+    const int total = __builtin_amdgcn_readlane(inc, kWave - 1);
+    if (id >= total) return false;
+    const int first = inc - mine;
+    const unsigned long long own = __ballot(id >= first && id < inc);   // exactly one lane
+    const int s = __builtin_amdgcn_readfirstlane(__ffsll(static_cast<long long>(own)) - 1);
+    seq = s;
+    blk = id - __builtin_amdgcn_readlane(first, s);
+    return true;
+}
+
+// Either form, by batch size (uniform over the block).
+template <int NT, typename Count>
+__device__ __forceinline__ bool number_block(int id, int n_seq, Count count, int* sh, int& seq, int& blk) {
+    if (n_seq <= kWave) return numbered_block_wave(id, n_seq, count, seq, blk);
+    return numbered_block<NT>(id, n_seq, count, sh, seq, blk);
+}
+
 }  // namespace dsa

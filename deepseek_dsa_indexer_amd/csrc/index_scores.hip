@@ -134,7 +134,7 @@ void index_scores_kernel(const uint8_t* __restrict__ q, const float* __restrict_
         auto count = [&](int s) {
             return fill_invisible ? nblk : (n_visible(len[s], 1, 0, Lmax, m) + keys_per_block - 1) / keys_per_block;
         };
-        if (!numbered_block<kThreads>(blockIdx.y * gridDim.x + blockIdx.x, gridDim.x, count, s_num, b, yblk))
+        if (!number_block<kThreads>(blockIdx.y * gridDim.x + blockIdx.x, gridDim.x, count, s_num, b, yblk))
             return;
         t0 = 0;
     } else {
@@ -316,7 +316,7 @@ void index_scores_decode_kernel(const uint8_t* __restrict__ q, const float* __re
         auto count = [&](int sq) {
             return fill_invisible ? nblk : (n_visible(len[sq], 1, 0, Lmax, m) + keys_per_block - 1) / keys_per_block;
         };
-        if (!numbered_block<kThreads>(blockIdx.y * gridDim.x + blockIdx.x, gridDim.x, count, s_num, b, yblk))
+        if (!number_block<kThreads>(blockIdx.y * gridDim.x + blockIdx.x, gridDim.x, count, s_num, b, yblk))
             return;
     }
     const int pos = n_visible(len[b], 1, 0, Lmax, m) - 1;

@@ -90,7 +90,7 @@ void topk_chunk_kernel(const float* __restrict__ scores, const int32_t* __restri
             const int n = visible(len, r, 1, Lmax, m);
             return n > k ? (n + kChunk - 1) / kChunk : 0;
         };
-        if (!numbered_block<kThreads>(blockIdx.x, gridDim.x / n_chunks, count, sh.num, row, c)) return;
+        if (!number_block<kThreads>(blockIdx.x, gridDim.x / n_chunks, count, sh.num, row, c)) return;
     } else {
         // chunk c' of row r runs chunk (c' + r) % n_chunks: a block's XCD follows c', so
         // every XCD gets chunks from the whole length range of the rows

@@ -89,6 +89,9 @@ INDEX_CASES = [
     ("decode_ragged_small", _small("decode_ragged", name="drs", B=3, Lmax=1100,
                                    lens="ragged:37:1100", seed=105)),
     ("decode_normal_small", _small("decode_v32", name="dns", B=2, Lmax=777, seed=102)),
+    # more than 64 sequences: the block-wide block numbering (64 or fewer: one wave's)
+    ("decode_many_seqs", _small("decode_ragged", name="dms", B=80, Lmax=600, lens="ragged:30:600",
+                                seed=107)),
     ("prefill_small", _small("prefill_chunk", name="ps", T=70, Lmax=300, lens="ragged:70:300",
                              B=2, H_I=48, D_I=64, seed=104)),
     # long decode rows: the LDS-streamed decode kernel (four or more chunks per wave),
@@ -141,6 +144,8 @@ TOPK_CASES = [
     # nine rows of unequal length (chunk boundaries, rows needing no selection)
     ("ragged_long_rows", "heavy", 9, 1, 50000,
      [50000, 1000, 16384, 16385, 32768, 2049, 2048, 40001, 24000], 2048),
+    # 70 sequences of up to 17000 positions: two-stage, chunks numbered block-wide
+    ("many_long_rows", "heavy", 70, 1, 17000, [17000 - 97 * i for i in range(70)], 2048),
     ("zeros", "zeros", 2, 1, 3000, [3000, 2100], 2048),
     ("causal_rows", "normal", 2, 37, 1001, [1001, 37], 64),
     ("k1", "ties", 2, 3, 500, [500, 300], 1),
