@@ -647,10 +647,15 @@ void mla_decode_mfma_kernel(const uint16_t* __restrict__ q, const uint8_t* __res
     MlaState<NHT> st;
     {
         // queries of head tile `wave` as MFMA B operands: head 16 wave + n, dims 32 ds + 8 g
-        const int head = wave < NHT ? 16 * wave + n : n;
-        const uint16_t* qrow = q + (static_cast<size_t>(row) * H_total + head0 + head) * kDq + 8 * g;
+        // (only the QK waves hold them; with 64 heads the other four waves load nothing)
+        if (wave < NHT) {
+            const uint16_t* qrow = q + (static_cast<size_t>(row) * H_total + head0 + 16 * wave + n) * kDq + 8 * g;
 #pragma unroll
-        for (int ds = 0; ds < kDs; ++ds) st.qreg[ds] = *reinterpret_cast<const v8bf*>(qrow + 32 * ds);
+            for (int ds = 0; ds < kDs; ++ds) st.qreg[ds] = *reinterpret_cast<const v8bf*>(qrow + 32 * ds);
+        } else {
+#pragma unroll
+            for (int ds = 0; ds < kDs; ++ds) st.qreg[ds] = v8bf{};
+        }
     }
 
     // selected positions of this split (-1: unused slot or not visible)
