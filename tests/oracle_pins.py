@@ -150,6 +150,35 @@ def pin_index_scores_one_head(o):
     np.testing.assert_allclose(got[0, 0], ref, rtol=2e-7)
 
 
+def pin_index_scores_relu_per_head_mixed_signs(o):
+    """The ReLU of the score box acts on each head's whole dot product, not on the single
+    products: two heads whose products have mixed signs, values worked out by hand.
+      head 0: q = [2, -1],  head 1: q = [1, -3]   (other columns 0)
+      key 0 = [ 1,  1]: dots ( 1, -2) -> ReLU ( 1, 0)
+      key 1 = [ 1,  2]: dots ( 0, -5) -> ( 0, 0)
+      key 2 = [ 2,  1]: dots ( 3, -1) -> ( 3, 0)
+      key 3 = [-1, -1]: dots (-1,  2) -> ( 0, 2)
+    With w = [0.5, -0.25], q_scale = [1, 2], sm = 1 and key scales 1 the folded weights
+    are [0.5, -0.5], so the scores are exactly [0.5, 0, 1.5, -1].  Clipping each product
+    at zero instead would give [0.5, 0.5, 1.5, -1]; no ReLU at all [1.5, 2.5, 2, -1.5]."""
+    one, two, three = 0x38, 0x40, 0x44          # e4m3fn codes of 1, 2, 3
+    neg = 0x80
+    D = 32
+    q = np.zeros((1, 1, 2, D), np.uint8)
+    q[0, 0, 0, :2] = [two, one | neg]
+    q[0, 0, 1, :2] = [one, three | neg]
+    k = np.zeros((1, 4, D), np.uint8)
+    k[0, 0, :2] = [one, one]
+    k[0, 1, :2] = [one, two]
+    k[0, 2, :2] = [two, one]
+    k[0, 3, :2] = [one | neg, one | neg]
+    qs = np.array([[[1.0, 2.0]]], np.float32)
+    w = np.array([[[0.5, -0.25]]], np.float32)
+    ks = np.ones((1, 4), np.float32)
+    got = o.index_scores(q, qs, w, k, ks, np.array([4], np.int32), 1.0)
+    np.testing.assert_array_equal(got[0, 0], np.array([0.5, 0.0, 1.5, -1.0], np.float32))
+
+
 def pin_index_scores_invariances(o):
     """Mixed signs: permuting heads (with their weights) or permuting the d columns of q and
     k together leaves the scores unchanged; doubling k_scale doubles them; the visible

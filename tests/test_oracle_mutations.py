@@ -14,6 +14,9 @@ MUTATIONS = [
     ("drop ReLU", "acc += wf * (dot > 0.0 ? dot : 0.0);", "acc += wf * dot;"),
     ("ReLU after weighting", "acc += wf * (dot > 0.0 ? dot : 0.0);",
      "acc += (wf * dot > 0.0 ? wf * dot : 0.0);"),
+    ("ReLU per product", "for (int d = 0; d < D; ++d) dot += table[qh[d]] * table[ks[d]];",
+     "for (int d = 0; d < D; ++d) { const double p_ = table[qh[d]] * table[ks[d]]; "
+     "dot += p_ > 0.0 ? p_ : 0.0; }"),
     ("drop q_scale", "(double)w[row * H + h] * (double)q_scale[row * H + h] * sm_scale",
      "(double)w[row * H + h] * sm_scale"),
     ("drop indexer scale", "(double)w[row * H + h] * (double)q_scale[row * H + h] * sm_scale",
