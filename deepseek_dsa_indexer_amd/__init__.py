@@ -12,11 +12,16 @@ The computation lives in ``libdsa_amd.so`` (HIP kernels behind the C ABI of
          bf16 q: 512 e4m3fn codes, four fp32 block scales, 64 bf16 rope values)
     sparse_mla_prefill(q, k, v, idx, sm_scale)                           -> (out, lse)
     LayerStep(...)()                                                     -> (out, lse)
+    LayerStep(..., workspace=False).call_noalloc()                       -> (out, lse)
+        (the library's fixed per-device scratch instead of a workspace; at most
+         NOALLOC_SCRATCH_BYTES of it)
 
 Build the library with ``python -m deepseek_dsa_indexer_amd.build``.
 """
-from ._native import (DSAError, LayerStep, index_scores, indexer_prep, library_path, load,
-                      profile_begin, profile_end, sparse_mla_decode, sparse_mla_prefill, topk)
+from ._native import (NOALLOC_SCRATCH_BYTES, DSAError, LayerStep, index_scores, indexer_prep,
+                      library_path, load, profile_begin, profile_end, sparse_mla_decode,
+                      sparse_mla_prefill, topk)
 
-__all__ = ["DSAError", "LayerStep", "index_scores", "indexer_prep", "library_path", "load",
-           "profile_begin", "profile_end", "sparse_mla_decode", "sparse_mla_prefill", "topk"]
+__all__ = ["NOALLOC_SCRATCH_BYTES", "DSAError", "LayerStep", "index_scores", "indexer_prep",
+           "library_path", "load", "profile_begin", "profile_end", "sparse_mla_decode",
+           "sparse_mla_prefill", "topk"]

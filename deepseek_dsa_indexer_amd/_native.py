@@ -25,8 +25,9 @@ EXPORTED = ["dsa_last_error", "dsa_version", "dsa_indexer_prep", "dsa_index_scor
             "dsa_topk_workspace_bytes",
             "dsa_topk", "dsa_sparse_mla_decode_workspace_bytes", "dsa_sparse_mla_decode",
             "dsa_sparse_mla_prefill_workspace_bytes", "dsa_sparse_mla_prefill",
-            "dsa_layer_step_workspace_bytes", "dsa_layer_step", "dsa_profile_begin",
-            "dsa_profile_end"]
+            "dsa_layer_step_workspace_bytes", "dsa_layer_step", "dsa_layer_step_noalloc",
+            "dsa_profile_begin", "dsa_profile_end"]
+NOALLOC_SCRATCH_BYTES = 64 << 20     # DSA_NOALLOC_SCRATCH_BYTES
 PHASES = ("index_scores", "topk", "attention", "combine")
 
 
@@ -89,11 +90,12 @@ def load():
     lib.dsa_layer_step_workspace_bytes.argtypes = [ctypes.POINTER(LayerArgs)]
     lib.dsa_layer_step_workspace_bytes.restype = Z
     lib.dsa_layer_step.argtypes = [ctypes.POINTER(LayerArgs), P, Z, P]
+    lib.dsa_layer_step_noalloc.argtypes = [ctypes.POINTER(LayerArgs), P]
     lib.dsa_profile_begin.argtypes = [I]
     lib.dsa_profile_end.argtypes = [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(I)]
     for fn in ("dsa_indexer_prep", "dsa_index_scores", "dsa_topk", "dsa_sparse_mla_decode",
                "dsa_sparse_mla_prefill",
-               "dsa_layer_step", "dsa_profile_begin", "dsa_profile_end"):
+               "dsa_layer_step", "dsa_layer_step_noalloc", "dsa_profile_begin", "dsa_profile_end"):
         getattr(lib, fn).restype = I
     _lib = lib
     return lib
@@ -282,7 +284,7 @@ class LayerStep:
 
     def __init__(self, q_fp8, q_scale, w, k_fp8, k_scale, lens, sm_scale_i, topk, q, sm_scale,
                  latent=None, k=None, v=None, Dv=None, want_lse=True, want_idx=False,
-                 want_scores=False, compress_rate=1):
+                 want_scores=False, compress_rate=1, workspace=True):
         q_fp8 = _fp8(q_fp8, "q_fp8")
         k_fp8 = _fp8(k_fp8, "k_fp8")
         for t, n in ((q_scale, "q_scale"), (w, "w"), (k_scale, "k_scale")):
@@ -330,12 +332,20 @@ class LayerStep:
         self._keep = (q_fp8, q_scale, w, k_fp8, k_scale, lens, q, latent, k, v)
         lib = load()
         self.ws_bytes = lib.dsa_layer_step_workspace_bytes(ctypes.byref(a))
-        # 256-byte aligned workspace (torch's caching allocator aligns to 512 bytes)
-        self.ws = _workspace(self.ws_bytes, dev)
+        # 256-byte aligned workspace (torch's caching allocator aligns to 512 bytes);
+        # workspace=False: none (for call_noalloc only)
+        self.ws = _workspace(self.ws_bytes, dev) if workspace else None
         self._ws_ptr = _ptr(self.ws)
         self.device = dev
 
     def __call__(self, stream=None):
         s = ctypes.c_void_p(stream) if stream is not None else _stream(self.device)
         _check(load().dsa_layer_step(ctypes.byref(self.args), self._ws_ptr, self.ws_bytes, s))
+        return self.out, self.lse
+
+    def call_noalloc(self, stream=None):
+        """The same step through dsa_layer_step_noalloc (the library's own per-device
+        scratch instead of this object's workspace)."""
+        s = ctypes.c_void_p(stream) if stream is not None else _stream(self.device)
+        _check(load().dsa_layer_step_noalloc(ctypes.byref(self.args), s))
         return self.out, self.lse

@@ -5,6 +5,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <string>
 #include <vector>
 
@@ -190,6 +191,36 @@ struct Profiler {
     size_t used = 0;
 };
 Profiler g_prof;
+
+// Library-owned scratch of dsa_layer_step_noalloc: one array per GPU, in the code object's
+// device memory (the loader places it when the library's code is loaded on a device and
+// keeps it until the process ends).  Host code never uses the array's own name as an
+// address: each device's copy is looked up once with hipGetSymbolAddress, with that
+// device current, and only that pointer is passed to kernels.
+constexpr size_t kStaticScratchBytes = static_cast<size_t>(DSA_NOALLOC_SCRATCH_BYTES);
+__device__ __attribute__((aligned(256))) uint8_t scratch[kStaticScratchBytes];
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// This device's copy of `scratch` (looked up on the first call on the device).
+dsa_status device_scratch(void** out) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return fail(DSA_ERR_HIP, "layer step (no alloc): hipGetDevice: %s", hipGetErrorString(e));
+    if (dev < 0 || dev >= kMaxDevices)
+        return fail(DSA_ERR_HIP, "layer step (no alloc): device %d beyond %d", dev, kMaxDevices);
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void* ptr = nullptr;
+        e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || !ptr)
+            return fail(DSA_ERR_HIP, "layer step (no alloc): hipGetSymbolAddress: %s", hipGetErrorString(e));
+        g_scratch_ptr[dev] = ptr;
+    }
+    *out = g_scratch_ptr[dev];
+    return DSA_OK;
+}
 
 }  // namespace
 
@@ -423,6 +454,18 @@ dsa_status dsa_layer_step(const dsa_layer_args* a, void* ws, size_t ws_bytes, hi
                         a->sm_scale, a->dtype, a->out, a->lse, att_ws, stream);
     dsa::prof_mark(stream, dsa::kPhaseNone);
     return st;
+}
+
+dsa_status dsa_layer_step_noalloc(const dsa_layer_args* a, hipStream_t stream) {
+    DSA_REQUIRE(a, DSA_ERR_NULL, "layer step (no alloc): NULL args");
+    const size_t need = dsa_layer_step_workspace_bytes(a);
+    DSA_REQUIRE(need <= kStaticScratchBytes, DSA_ERR_WORKSPACE,
+                "layer step (no alloc): this shape needs %zu bytes of scratch, above the library's "
+                "fixed %zu (use dsa_layer_step with a workspace)", need, kStaticScratchBytes);
+    void* ws = nullptr;
+    dsa_status st = device_scratch(&ws);
+    if (st != DSA_OK) return st;
+    return dsa_layer_step(a, ws, kStaticScratchBytes, stream);
 }
 
 }  // extern "C"

@@ -28,7 +28,8 @@
  *   - Every call only enqueues work on `stream` and returns; outputs are valid once the
  *     caller synchronises the stream.  The library never allocates, frees or
  *     synchronises; scratch memory comes from the caller as (ws, ws_bytes), sized by
- *     the matching *_workspace_bytes() query.  Inputs must stay alive until the stream
+ *     the matching *_workspace_bytes() query (dsa_layer_step_noalloc instead uses a
+ *     fixed scratch array that the library's device code holds on each GPU).  Inputs must stay alive until the stream
  *     reaches the call; outputs must not alias inputs or the workspace.
  *   - Errors are reported by the returned status; nothing aborts.  dsa_last_error()
  *     returns a thread-local description of the last non-OK status.  Arguments are
@@ -233,6 +234,28 @@ typedef struct dsa_layer_args {
 size_t dsa_layer_step_workspace_bytes(const dsa_layer_args* a);
 dsa_status dsa_layer_step(const dsa_layer_args* a, void* ws, size_t ws_bytes,
                           hipStream_t stream);
+
+/*
+ * dsa_layer_step_noalloc -- dsa_layer_step for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid hipMalloc):
+ * the same step and results, with the workspace taken from a scratch array the library
+ * holds in each GPU's memory (DSA_NOALLOC_SCRATCH_BYTES = 64 MiB per device, placed when
+ * the library's device code is loaded and kept until the process ends) instead of a
+ * caller buffer.  The caller still passes every input and output in `a`.
+ *   - A shape whose dsa_layer_step_workspace_bytes() exceeds DSA_NOALLOC_SCRATCH_BYTES is
+ *     rejected with DSA_ERR_WORKSPACE before anything is enqueued (the decode shapes up
+ *     to B=64 x 65536 positions fit; a T=8192 prefill chunk's score matrix does not).
+ *   - The call allocates and frees nothing (no hipMalloc, no torch allocation).  On its
+ *     first use on a device it looks up that device's copy of the array once.
+ *   - Every call on one GPU shares that GPU's array, which keeps the last call's
+ *     contents: calls that overlap on one GPU (concurrent streams, or host threads
+ *     enqueueing on different streams) race on it and must be serialised by the
+ *     caller.  Nothing in the array needs to start at zero: each step writes every
+ *     scratch value before reading it.
+ * Other errors as for dsa_layer_step.
+ */
+#define DSA_NOALLOC_SCRATCH_BYTES (64u << 20)
+dsa_status dsa_layer_step_noalloc(const dsa_layer_args* a, hipStream_t stream);
 
 /*
  * Tracing aid: HIP-event timing of the phases of dsa_layer_step.

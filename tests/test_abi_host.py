@@ -128,6 +128,27 @@ def test_layer_step_validation(lib):
     assert lib.dsa_layer_step(ctypes.byref(a), ctypes.c_void_p(p), need, None) == 2  # Lmax != T
 
 
+def test_layer_step_noalloc_validation(lib):
+    """The allocation-free entry point rejects, before touching the device, any shape
+    whose workspace exceeds its fixed scratch (a T=8192 prefill chunk's scores), and
+    validates like dsa_layer_step otherwise."""
+    a = N.LayerArgs()
+    assert lib.dsa_layer_step_noalloc(None, None) == 1
+    p = 0x10000
+    a.q_fp8 = a.q_scale = a.w = a.k_fp8 = a.k_scale = a.len = p
+    a.B, a.T, a.H_I, a.d_I, a.Lmax, a.topk = 1, 8192, 64, 128, 8192, 2048
+    a.form, a.dtype = N.DSA_ATTN_MHA, N.DSA_BF16
+    a.q = a.k = a.v = a.out = p
+    a.H, a.Dv, a.Dqk = 128, 128, 192
+    assert lib.dsa_layer_step_workspace_bytes(ctypes.byref(a)) > N.NOALLOC_SCRATCH_BYTES
+    assert lib.dsa_layer_step_noalloc(ctypes.byref(a), None) == 5
+    assert b"scratch" in lib.dsa_last_error()
+    # the largest decode workload (64 sequences of up to 65536 positions) fits
+    a.B, a.T, a.Lmax = 64, 1, 65536
+    a.form, a.latent, a.Dv, a.Dr, a.Dqk = N.DSA_ATTN_LATENT, p, 512, 64, 0
+    assert lib.dsa_layer_step_workspace_bytes(ctypes.byref(a)) <= N.NOALLOC_SCRATCH_BYTES
+
+
 def test_fp8_latent_validation(lib):
     """FP8 latent rows: the latent form only, at the storage form's 512 + 64 widths; the
     matrix-core shape takes the same split workspace as bf16 rows."""
