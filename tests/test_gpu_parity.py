@@ -242,6 +242,65 @@ def test_sparse_mla_decode_logit_spread(dsa, orc):
     check_attention(_np_out(out), lse.cpu().numpy(), ro, rl, "bf16")
 
 
+def test_sparse_mla_decode_fp8_logit_spread(dsa, orc):
+    """FP8 latent rows with logits far above the rest of a split: one selected row's bf16
+    rope columns are 16x the query's rope part of one head, so its logit lies about 100
+    log2 units above the others -- late in a split in row 0 (the split is recomputed from
+    its true maximum, with FP8 gathers and block-scaled numerators), first in row 1."""
+    _say("[sparse_mla_decode fp8 latent] logit spread")
+    rng = np.random.default_rng(12)
+    B, T, H, Lmax, k = 2, 1, 128, 3000, 2048
+    lens = np.array([3000, 3000], np.int32)
+    qf = rng.standard_normal((B, T, H, 576), dtype=np.float32)
+    qf = (S.to_bf16_bits(qf).astype(np.uint32) << 16).view(np.float32)   # bf16 values
+    x = rng.standard_normal((B, Lmax, 576), dtype=np.float32)
+    f = np.exp2(rng.uniform(-5, 0, size=(B, Lmax, 4))).astype(np.float32)
+    x[..., :512] *= np.repeat(f, 128, axis=-1)
+    idx = _random_idx(rng, B, T, k, lens, invisible=False)
+    x[0, idx[0, 0, 200], 512:] = 16.0 * qf[0, 0, 5, 512:]      # exact in bf16
+    x[1, idx[1, 0, 3], 512:] = 16.0 * qf[1, 0, 9, 512:]
+    q = S.to_bf16_bits(qf)
+    lat = S.pack_latent_fp8(x)
+    sm = 192 ** -0.5
+    tq = torch.from_numpy(q.view(np.int16)).view(torch.bfloat16).cuda()
+    out, lse = dsa.sparse_mla_decode(tq, torch.from_numpy(lat).cuda(), torch.from_numpy(idx).cuda(),
+                                     torch.from_numpy(lens).cuda(), 512, sm)
+    torch.cuda.synchronize()
+    ro, rl = orc.sparse_mla_decode(q, lat, idx, lens, 512, sm)
+    check_attention(_np_out(out), lse.cpu().numpy(), ro, rl, "bf16")
+
+
+def test_sparse_mla_prefill_logit_spread(dsa, orc):
+    """MHA prefill with a selected key far above the rest of its row: for row 150 of head
+    1, key 130 (third key block) has rope columns 16x the query's, about 100 log2 units
+    above the logits of the first key block (the workgroup is recomputed from the true
+    maximum); for row 40 of head 0 such a key sits in the first block (key 5), so the
+    later numerators of that row underflow relative to it."""
+    _say("[sparse_mla_prefill bf16] logit spread")
+    rng = np.random.default_rng(13)
+    B, T, H, Dqk, Dv, k = 1, 200, 2, 192, 128, 48
+    qf = rng.standard_normal((B, T, H, Dqk), dtype=np.float32)
+    qf = (S.to_bf16_bits(qf).astype(np.uint32) << 16).view(np.float32)
+    kf = rng.standard_normal((B, T, H, Dqk), dtype=np.float32)
+    v = S.to_bf16_bits(rng.standard_normal((B, T, H, Dv), dtype=np.float32))
+    idx = np.full((B, T, k), -1, np.int32)
+    for t in range(T):
+        m = min(k, t + 1)
+        idx[0, t, :m] = rng.choice(t + 1, size=m, replace=False)
+    for t, h, s_key in ((150, 1, 130), (40, 0, 5)):
+        row = idx[0, t]
+        if s_key not in row:
+            row[0] = s_key
+        kf[0, s_key, h, 128:] = 16.0 * qf[0, t, h, 128:]
+    q = S.to_bf16_bits(qf)
+    kk = S.to_bf16_bits(kf)
+    tt = lambda a: torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).cuda()
+    out, lse = dsa.sparse_mla_prefill(tt(q), tt(kk), tt(v), torch.from_numpy(idx).cuda(), Dqk ** -0.5)
+    torch.cuda.synchronize()
+    ro, rl = orc.sparse_mha_prefill(q, kk, v, idx, Dqk ** -0.5)
+    check_attention(_np_out(out), lse.cpu().numpy(), ro, rl, "bf16")
+
+
 def test_sparse_mla_decode_generic_f32(dsa, orc):
     _say("[sparse_mla_decode f32 generic]")
     rng = np.random.default_rng(7)
@@ -453,13 +512,21 @@ def test_layer_step_mha_small(dsa, orc):
 
 
 @pytest.mark.parametrize("B,Lmax,lo,seed", [(3, 20000, 1024, 207), (9, 36000, 700, 208),
-                                            (3, 8000, 700, 209)])
+                                            (3, 8000, 700, 209),
+                                            # four or more key chunks per wave: the
+                                            # LDS-streamed decode index kernel
+                                            (8, 65536, 30000, 217),
+                                            # more than 64 sequences: its block-wide
+                                            # numbering over unequal visible ranges
+                                            (80, 8192, 1024, 218)])
 def test_layer_step_without_intermediates(dsa, orc, B, Lmax, lo, seed):
     """The production configuration (scores and indices kept in the workspace, invisible
     scores never written, key blocks and top-k chunks numbered over the visible range
     only, the top-k candidates of rows beyond 16384 positions sharing the scratch region
     with the attention partials) gives bit-identical results to the configuration that
-    exposes the intermediates, which is checked against the oracle."""
+    exposes the intermediates, which is checked against the oracle.  The shapes cover
+    both index kernels (register-staged short streams; LDS-streamed rows of four or more
+    chunks per wave, with one wave's or the block's numbering)."""
     _say(f"[layer_step] without intermediates, long ragged rows, B={B} Lmax={Lmax}")
     cfg = _small("decode_ragged", name="ni", B=B, Lmax=Lmax, lens=f"ragged:{lo}:{Lmax}", seed=seed)
     c = S.make_case(cfg)
