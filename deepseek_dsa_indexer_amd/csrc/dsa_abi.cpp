@@ -35,7 +35,7 @@ dsa_status hip_status(hipError_t e, const char* what) {
     return DSA_OK;
 }
 
-constexpr size_t kPhaseCountMarks = dsa::kPhaseCount + 1;   // events per layer step
+constexpr size_t kProfPairsPerStep = 6;   // kernels per layer step, at most
 
 #define DSA_REQUIRE(cond, st, ...) \
     do {                           \
@@ -183,12 +183,13 @@ size_t mha_ws(int B, int T, int, int Dqk, int Dv, int, dsa_dtype dt) {
     return 0;
 }
 
-// Event timing of dsa_layer_step phases (dsa_profile_begin / dsa_profile_end).
+// Kernel timing of dsa_layer_step phases (dsa_profile_begin / dsa_profile_end): one
+// start/stop event pair per kernel, recorded by the dispatch itself.
 struct Profiler {
     bool on = false;
-    std::vector<hipEvent_t> pool;
-    std::vector<int> label;     // phase started by each recorded event (kPhaseNone: none)
-    size_t used = 0;
+    std::vector<hipEvent_t> pool;     // pairs: 2 i (start), 2 i + 1 (stop)
+    std::vector<int> label;           // phase of pair i
+    size_t used = 0;                  // pairs handed out
 };
 Profiler g_prof;
 
@@ -224,11 +225,13 @@ dsa_status device_scratch(void** out) {
 
 }  // namespace
 
-void dsa::prof_mark(hipStream_t stream, int next) {
-    if (!g_prof.on || g_prof.used >= g_prof.pool.size()) return;
-    if (hipEventRecord(g_prof.pool[g_prof.used], stream) != hipSuccess) return;
-    g_prof.label[g_prof.used] = next;
+bool dsa::prof_kernel_events(int phase, hipEvent_t* start, hipEvent_t* stop) {
+    if (!g_prof.on || 2 * (g_prof.used + 1) > g_prof.pool.size()) return false;
+    *start = g_prof.pool[2 * g_prof.used];
+    *stop = g_prof.pool[2 * g_prof.used + 1];
+    g_prof.label[g_prof.used] = phase;
     ++g_prof.used;
+    return true;
 }
 
 extern "C" {
@@ -237,9 +240,10 @@ dsa_status dsa_profile_begin(int max_steps) {
     DSA_REQUIRE(max_steps >= 1 && max_steps <= (1 << 20), DSA_ERR_SHAPE,
                 "profile: max_steps=%d out of range", max_steps);
     DSA_REQUIRE(!g_prof.on, DSA_ERR_SHAPE, "profile: already running");
-    const size_t n = static_cast<size_t>(max_steps) * (kPhaseCountMarks);
+    const size_t pairs = static_cast<size_t>(max_steps) * kProfPairsPerStep;
+    const size_t n = 2 * pairs;
     g_prof.pool.resize(n);
-    g_prof.label.assign(n, dsa::kPhaseNone);
+    g_prof.label.assign(pairs, dsa::kPhaseNone);
     for (size_t i = 0; i < n; ++i) {
         hipError_t e = hipEventCreate(&g_prof.pool[i]);
         if (e != hipSuccess) {
@@ -259,12 +263,12 @@ dsa_status dsa_profile_end(double* ms_total, int* counts) {
     for (int p = 0; p < dsa::kPhaseCount; ++p) { ms_total[p] = 0.0; counts[p] = 0; }
     dsa_status st = DSA_OK;
     if (g_prof.used > 0) {
-        st = hip_status(hipEventSynchronize(g_prof.pool[g_prof.used - 1]), "profile: sync");
-        for (size_t i = 0; st == DSA_OK && i + 1 < g_prof.used; ++i) {
+        st = hip_status(hipEventSynchronize(g_prof.pool[2 * g_prof.used - 1]), "profile: sync");
+        for (size_t i = 0; st == DSA_OK && i < g_prof.used; ++i) {
             const int p = g_prof.label[i];
             if (p < 0) continue;
             float ms = 0.f;
-            st = hip_status(hipEventElapsedTime(&ms, g_prof.pool[i], g_prof.pool[i + 1]),
+            st = hip_status(hipEventElapsedTime(&ms, g_prof.pool[2 * i], g_prof.pool[2 * i + 1]),
                             "profile: elapsed time");
             ms_total[p] += ms;
             counts[p] += 1;
@@ -438,21 +442,17 @@ dsa_status dsa_layer_step(const dsa_layer_args* a, void* ws, size_t ws_bytes, hi
 
     dsa::IndexScoresArgs ia{a->q_fp8, a->q_scale, a->w, a->k_fp8, a->k_scale, a->len, a->B, a->T,
                             a->H_I, a->d_I, a->Lmax, a->sm_scale_I, scores, a->scores_out ? 1 : 0, m};
-    dsa::prof_mark(stream, dsa::kPhaseIndex);
     st = hip_status(dsa::launch_index_scores(ia, stream), "layer step: index scores");
     if (st != DSA_OK) return st;
-    dsa::prof_mark(stream, dsa::kPhaseTopk);
     dsa::TopkArgs ta{scores, a->len, a->B, a->T, a->Lmax, a->topk, idx, m};
     st = hip_status(dsa::launch_topk(ta, att_ws, stream), "layer step: topk");
     if (st != DSA_OK) return st;
-    dsa::prof_mark(stream, dsa::kPhaseAttention);
     if (a->form == DSA_ATTN_LATENT)
         st = launch_latent(a->q, a->latent, idx, a->len, a->B, a->T, a->H, a->Dv, a->Dr, a->Lmax,
                            a->topk, a->sm_scale, a->dtype, a->out, a->lse, att_ws, stream, m);
     else
         st = launch_mha(a->q, a->k, a->v, idx, a->B, a->T, a->H, a->Dqk, a->Dv, a->topk,
                         a->sm_scale, a->dtype, a->out, a->lse, att_ws, stream);
-    dsa::prof_mark(stream, dsa::kPhaseNone);
     return st;
 }
 

@@ -2,18 +2,33 @@
 // kernel translation units.  Arguments are validated by the caller.
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stddef.h>
 #include <stdint.h>
 
 namespace dsa {
 
-// Phases of one layer step, for the optional event timing of dsa_profile_begin/_end.
+// Phases of one layer step, for the optional kernel timing of dsa_profile_begin/_end.
 enum Phase { kPhaseIndex = 0, kPhaseTopk = 1, kPhaseAttention = 2, kPhaseCombine = 3,
              kPhaseCount = 4, kPhaseNone = -1 };
-// Records a HIP event on `stream` that ends the running phase and starts `next`
-// (kPhaseNone: nothing starts).  A no-op unless profiling is on.
-void prof_mark(hipStream_t stream, int next);
+// While profiling is on: a fresh start/stop event pair for the next kernel of `phase`
+// (false when profiling is off or the pool is used up).
+bool prof_kernel_events(int phase, hipEvent_t* start, hipEvent_t* stop);
+
+// Launch of a kernel that belongs to `phase`.  While profiling is on, the start and stop
+// events are part of the dispatch itself (hipExtLaunchKernelGGL), so they time the
+// kernel's own execution, without the gaps between kernels.
+template <typename... KArgs, typename... Args>
+hipError_t launch_kernel(int phase, void (*kernel)(KArgs...), dim3 grid, dim3 block, uint32_t shmem,
+                         hipStream_t stream, Args... args) {
+    hipEvent_t e0, e1;
+    if (phase != kPhaseNone && prof_kernel_events(phase, &e0, &e1))
+        hipExtLaunchKernelGGL(kernel, grid, block, shmem, stream, e0, e1, 0u, static_cast<KArgs>(args)...);
+    else
+        hipLaunchKernelGGL(kernel, grid, block, shmem, stream, static_cast<KArgs>(args)...);
+    return hipGetLastError();
+}
 
 struct IndexScoresArgs {
     const uint8_t* q;
@@ -96,6 +111,18 @@ hipError_t launch_mla_decode_mfma(const void* q, const void* latent, const int32
                                   const int32_t* len, int B, int T, int H, int Lmax, int k,
                                   float sm_scale, int type, int m, void* out, float* lse, void* ws,
                                   hipStream_t stream);
+
+// The 32x32x16 matrix-core kernel of the bf16 latent form (sparse_mla_decode32.hip): 64
+// heads per workgroup (H = 64 or 128), at most mla_decode32_max_tiles() tiles of 32 slots
+// per split.  Launches rows * n_splits * (H / 64) workgroups; with n_splits > 1 each split
+// writes its normalised bf16 rows to part_o [rows][n_splits][H][512] and its log2-sum-exp
+// to part_lse [rows][n_splits][H], which mla_combine_kernel merges.
+bool mla_decode32_supported(int H, int k);
+int mla_decode32_max_tiles();
+hipError_t launch_mla_decode32(const void* q, const void* latent, const int32_t* idx,
+                               const int32_t* len, int rows, int T, int H, int Lmax, int k, int m,
+                               int tiles_per_split, int n_splits, float scale_log2, void* out,
+                               float* lse, void* part_o, float* part_lse, hipStream_t stream);
 
 // Matrix-core path of the MHA prefill form (bf16, Dqk = 192, Dv = 128).
 bool mha_prefill_mfma_supported(int Dqk, int Dv, int bf16);

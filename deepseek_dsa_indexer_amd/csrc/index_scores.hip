@@ -415,10 +415,9 @@ hipError_t launch_d(const IndexScoresArgs& a, int chunks, hipStream_t stream) {
     const int keys_per_block = kThreads / kWave * kChunk * chunks;
     const int row_groups = (a.T + QR - 1) / QR;
     dim3 grid(a.B * row_groups, (a.Lmax + keys_per_block - 1) / keys_per_block);
-    hipLaunchKernelGGL((index_scores_kernel<D, QR>), grid, dim3(kThreads), 0, stream,
-                       a.q, a.q_scale, a.w, a.k, a.k_scale, a.len, a.T, a.H, a.Lmax, a.sm_scale,
-                       a.scores, a.fill_invisible, chunks, a.m);
-    return hipGetLastError();
+    return launch_kernel(kPhaseIndex, index_scores_kernel<D, QR>, grid, dim3(kThreads), 0, stream,
+                         a.q, a.q_scale, a.w, a.k, a.k_scale, a.len, a.T, a.H, a.Lmax, a.sm_scale,
+                         a.scores, a.fill_invisible, chunks, a.m);
 }
 
 // Key chunks per wave: enough waves to cover every SIMD twice (2048 waves), then longer
@@ -434,10 +433,9 @@ hipError_t launch_rows(const IndexScoresArgs& a, hipStream_t stream) {
     if (a.B > kThreads * kMaxSeqPerThread || chunks < 4) return launch_d<D, 1>(a, chunks, stream);
     const int keys_per_block = kWaves * kChunk * chunks;
     dim3 grid(a.B, (a.Lmax + keys_per_block - 1) / keys_per_block);
-    hipLaunchKernelGGL((index_scores_decode_kernel<D>), grid, dim3(kThreads), 0, stream,
-                       a.q, a.q_scale, a.w, a.k, a.k_scale, a.len, a.H, a.Lmax, a.sm_scale,
-                       a.scores, a.fill_invisible, chunks, a.m);
-    return hipGetLastError();
+    return launch_kernel(kPhaseIndex, index_scores_decode_kernel<D>, grid, dim3(kThreads), 0, stream,
+                         a.q, a.q_scale, a.w, a.k, a.k_scale, a.len, a.H, a.Lmax, a.sm_scale,
+                         a.scores, a.fill_invisible, chunks, a.m);
 }
 
 }  // namespace

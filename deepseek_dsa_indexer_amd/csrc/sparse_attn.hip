@@ -874,9 +874,8 @@ int mla_splits(int rows, int k) {
 
 hipError_t launch_sparse_attn_generic(const SparseAttnArgs& a, hipStream_t stream) {
     const size_t shmem = sizeof(float) * (static_cast<size_t>(a.Dk) + a.k);
-    hipLaunchKernelGGL(sparse_attn_generic_kernel, dim3(a.B * a.T * a.H), dim3(kGenThreads),
-                       shmem, stream, a);
-    return hipGetLastError();
+    return launch_kernel(kPhaseAttention, sparse_attn_generic_kernel, dim3(a.B * a.T * a.H),
+                         dim3(kGenThreads), static_cast<uint32_t>(shmem), stream, a);
 }
 
 bool mla_decode_mfma_supported(int H, int Dv, int Dr, int k, int type) {
@@ -899,6 +898,20 @@ struct MlaPlan {
 };
 MlaPlan mla_plan(int rows, int H, int k, int type) {
     MlaPlan p;
+    if (type == kLatBf16 && mla_decode32_supported(H, k)) {
+        // the 32x32x16 kernel: 64 heads per workgroup, enough key splits to give every CU
+        // a workgroup, at most mla_decode32_max_tiles() tiles per split
+        p.parts = H / 64;
+        p.nht = 4;
+        const int n_tiles = (k + kKt - 1) / kKt;
+        const int wg = rows * p.parts;
+        int s = wg >= 256 ? 1 : (256 + wg - 1) / wg;
+        s = min(s, kMaxSplits);
+        const int tmax = mla_decode32_max_tiles();
+        s = max(s, (n_tiles + tmax - 1) / tmax);
+        p.splits = max(1, min(s, n_tiles));
+        return p;
+    }
     const int s1 = mla_splits(rows, k);
     const bool idle = rows * s1 < 256;
     p.parts = (H == 128 && rows < 256 && (idle || (type == kLatBf16 && s1 >= 8))) ? 2 : 1;
@@ -931,18 +944,23 @@ hipError_t launch_mla_decode_mfma(const void* q, const void* latent, const int32
     auto lp = static_cast<const uint8_t*>(latent);
     auto op = static_cast<uint16_t*>(out);
     const bool f8 = type == kLatFp8;
+    if (!f8 && mla_decode32_supported(H, k)) {
+        hipError_t e = launch_mla_decode32(q, latent, idx, len, rows, T, H, Lmax, k, m, tps, s,
+                                           scale_log2, out, lse, part_o, part_lse, stream);
+        if (e != hipSuccess || s == 1) return e;
+        const int parts = (H * (kDv / kCombCols) + 255) / 256;
+        return launch_kernel(kPhaseCombine, mla_combine_kernel, dim3(rows * parts), dim3(256), 0, stream,
+                             part_o, part_lse, rows, H, s, op, lse);
+    }
     auto kern = plan.nht == 8 ? (f8 ? mla_decode_mfma_kernel<8, true> : mla_decode_mfma_kernel<8, false>)
                               : (f8 ? mla_decode_mfma_kernel<4, true> : mla_decode_mfma_kernel<4, false>);
-    hipLaunchKernelGGL(kern, dim3(rows * s * plan.parts), dim3(kMlaThreads), 0, stream,
-                       qp, lp, idx, len, T, Lmax, k, m, tps, s, H, scale_log2, op, lse, part_o,
-                       part_lse);
-    hipError_t e = hipGetLastError();
+    hipError_t e = launch_kernel(kPhaseAttention, kern, dim3(rows * s * plan.parts), dim3(kMlaThreads), 0,
+                                 stream, qp, lp, idx, len, T, Lmax, k, m, tps, s, H, scale_log2, op, lse,
+                                 part_o, part_lse);
     if (e != hipSuccess || s == 1) return e;
     const int parts = (H * (kDv / kCombCols) + 255) / 256;
-    prof_mark(stream, kPhaseCombine);
-    hipLaunchKernelGGL(mla_combine_kernel, dim3(rows * parts), dim3(256), 0, stream,
-                       part_o, part_lse, rows, H, s, op, lse);
-    return hipGetLastError();
+    return launch_kernel(kPhaseCombine, mla_combine_kernel, dim3(rows * parts), dim3(256), 0, stream,
+                         part_o, part_lse, rows, H, s, op, lse);
 }
 
 }  // namespace dsa

@@ -359,16 +359,16 @@ hipError_t launch_mha_prefill_mfma(const void* q, const void* k, const void* v, 
                                    float* lse, void* ws, hipStream_t stream) {
     uint32_t* mask = static_cast<uint32_t*>(ws);
     const int words = (T + 31) / 32;
-    hipLaunchKernelGGL(select_mask_kernel, dim3(B * T), dim3(256), words * sizeof(uint32_t), stream,
-                       idx, T, topk, mask);
-    hipError_t e = hipGetLastError();
+    // the selection's bit mask is timed with the top-k (it turns the selection into the
+    // attention's operand form)
+    hipError_t e = launch_kernel(kPhaseTopk, select_mask_kernel, dim3(B * T), dim3(256),
+                                 static_cast<uint32_t>(words * sizeof(uint32_t)), stream, idx, T, topk, mask);
     if (e != hipSuccess) return e;
     const int qblocks = (T + kQB - 1) / kQB;
-    hipLaunchKernelGGL(mha_prefill_mfma_kernel, dim3(B * H * qblocks), dim3(kMhaThreads), 0, stream,
-                       static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
-                       static_cast<const uint16_t*>(v), mask, B, T, H, sm_scale * kLog2eM,
-                       static_cast<uint16_t*>(out), lse);
-    return hipGetLastError();
+    return launch_kernel(kPhaseAttention, mha_prefill_mfma_kernel, dim3(B * H * qblocks), dim3(kMhaThreads), 0,
+                         stream, static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
+                         static_cast<const uint16_t*>(v), mask, B, T, H, sm_scale * kLog2eM,
+                         static_cast<uint16_t*>(out), lse);
 }
 
 }  // namespace dsa

@@ -167,35 +167,25 @@ hipError_t launch_topk(const TopkArgs& a, void* ws, hipStream_t stream) {
     const int rows = a.B * a.T;
     const dim3 block(kThreads);
     if (!two_stage(a.Lmax, a.k)) {
-        if (a.Lmax <= 2 * kPerIter)
-            hipLaunchKernelGGL(topk_row_kernel<2>, dim3(rows), block, 0, stream, a.scores, a.len, a.T, a.Lmax, a.k, a.m, a.idx);
-        else if (a.Lmax <= kSingleMax)
-            hipLaunchKernelGGL(topk_row_kernel<4>, dim3(rows), block, 0, stream, a.scores, a.len, a.T, a.Lmax, a.k, a.m, a.idx);
-        else
-            hipLaunchKernelGGL(topk_row_kernel<0>, dim3(rows), block, 0, stream, a.scores, a.len, a.T, a.Lmax, a.k, a.m, a.idx);
-        return hipGetLastError();
+        auto kern = a.Lmax <= 2 * kPerIter ? topk_row_kernel<2>
+                  : a.Lmax <= kSingleMax   ? topk_row_kernel<4>
+                                           : topk_row_kernel<0>;
+        return launch_kernel(kPhaseTopk, kern, dim3(rows), block, 0, stream, a.scores, a.len, a.T,
+                             a.Lmax, a.k, a.m, a.idx);
     }
     const int nch = n_chunks_for(a.Lmax, a.k);
     const size_t ncand = static_cast<size_t>(rows) * nch * a.k;
     uint32_t* ck = static_cast<uint32_t*>(ws);
     int32_t* cp = reinterpret_cast<int32_t*>(ck + ncand);
-    if (chunk_for(a.Lmax, a.k) == 2 * kPerIter)
-        hipLaunchKernelGGL(topk_chunk_kernel<2>, dim3(rows * nch), block, 0, stream, a.scores, a.len,
-                           a.T, a.Lmax, a.k, a.m, nch, ck, cp);
-    else
-        hipLaunchKernelGGL(topk_chunk_kernel<4>, dim3(rows * nch), block, 0, stream, a.scores, a.len,
-                           a.T, a.Lmax, a.k, a.m, nch, ck, cp);
-    hipError_t e = hipGetLastError();
+    auto chunk_kern = chunk_for(a.Lmax, a.k) == 2 * kPerIter ? topk_chunk_kernel<2> : topk_chunk_kernel<4>;
+    hipError_t e = launch_kernel(kPhaseTopk, chunk_kern, dim3(rows * nch), block, 0, stream, a.scores,
+                                 a.len, a.T, a.Lmax, a.k, a.m, nch, ck, cp);
     if (e != hipSuccess) return e;
     const long long nc = static_cast<long long>(nch) * a.k;
     const int chunk = chunk_for(a.Lmax, a.k);
-    if (nc <= kSingleMax)
-        hipLaunchKernelGGL(topk_merge_kernel<4>, dim3(rows), block, 0, stream, ck, cp, a.len, a.T, a.Lmax, a.k, a.m, nch,
-                           chunk, a.idx);
-    else
-        hipLaunchKernelGGL(topk_merge_kernel<0>, dim3(rows), block, 0, stream, ck, cp, a.len, a.T, a.Lmax, a.k, a.m, nch,
-                           chunk, a.idx);
-    return hipGetLastError();
+    auto merge_kern = nc <= kSingleMax ? topk_merge_kernel<4> : topk_merge_kernel<0>;
+    return launch_kernel(kPhaseTopk, merge_kern, dim3(rows), block, 0, stream, ck, cp, a.len, a.T,
+                         a.Lmax, a.k, a.m, nch, chunk, a.idx);
 }
 
 }  // namespace dsa

@@ -258,15 +258,17 @@ dsa_status dsa_layer_step(const dsa_layer_args* a, void* ws, size_t ws_bytes,
 dsa_status dsa_layer_step_noalloc(const dsa_layer_args* a, hipStream_t stream);
 
 /*
- * Tracing aid: HIP-event timing of the phases of dsa_layer_step.
- *   dsa_profile_begin(max_steps) creates (max_steps * 5) HIP events (host-side objects,
- *   no device memory) and makes every following dsa_layer_step record an event on its
- *   stream before each phase and one at its end.  Phases: 0 index scores, 1 top-k,
- *   2 sparse attention (main kernel), 3 split combine (only when the attention splits
- *   its k slots).  Steps beyond max_steps are not recorded.
+ * Tracing aid: HIP-event timing of the kernels of dsa_layer_step.
+ *   dsa_profile_begin(max_steps) creates (max_steps * 12) HIP events (host-side objects,
+ *   no device memory) and makes every following layer-step call launch each of its
+ *   kernels with a start/stop event pair that the dispatch itself records
+ *   (hipExtLaunchKernel), so each pair spans one kernel's execution alone.  Phases:
+ *   0 index scores, 1 top-k (one or two kernels; for the MHA form also the kernel
+ *   that turns the selection into the attention's bit mask), 2 sparse attention (its
+ *   main kernel), 3 split combine (only when the attention splits its k slots).  Kernels beyond the pool are not timed.
  *   dsa_profile_end(ms_total[4], counts[4]) waits for the last recorded event, returns
- *   the summed elapsed milliseconds and the number of timed instances of each phase,
- *   and destroys the events.  Process-wide state: not for concurrent use from several
+ *   the summed elapsed milliseconds and the number of timed kernels of each phase, and
+ *   destroys the events.  Process-wide state: not for concurrent use from several
  *   threads or streams.
  */
 dsa_status dsa_profile_begin(int max_steps);
