@@ -8,10 +8,13 @@ Inputs are seeded synthetic tensors of the configuration's shapes, resident in H
 before the timed region; several independent input sets are cycled so that the
 256 MB Infinity Cache cannot serve a step from the previous one.
 
-Prints one JSON line: layer-steps/s (value), keys scored/s, the roofline of the
-dominant kernel from HIP events recorded by the library during a second pass of the
-same steps, the HBM traffic measured by rocprofv3 counters (from profiles/, when they
-match the current kernel source), and the CPU oracle timed on a bounded sample.
+Prints one JSON line: layer-steps/s (value) of the headline workload (decode_v32 by
+default), keys scored/s, the roofline of the dominant kernel (the sparse attention)
+from HIP events that the library records as part of each kernel's dispatch during a
+second pass of the same steps (kernel execution only, comparable with a rocprofv3
+kernel trace), the HBM traffic measured by rocprofv3 counters (from profiles/, when
+they match the current kernel source), the CPU oracle timed on a bounded sample, and
+the same measurements for the other workloads as sub-objects (``--only`` skips them).
 """
 from __future__ import annotations
 
@@ -28,8 +31,10 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0            # MI355X HBM3E, published
 BF16_PEAK_TFLOPS = 2500.0        # MI355X dense bf16 MFMA, published
+FP8_PEAK_TFLOPS = 5000.0         # MI355X dense FP8 MFMA, published
 METRIC = "DSA decode layer-steps/s and indexer keys scored/s; % of HBM/MFMA roofline"
-ATTN_SOURCE = os.path.join(ROOT, "deepseek_dsa_indexer_amd", "csrc", "sparse_attn.hip")
+ATTN_SOURCE = os.path.join(ROOT, "deepseek_dsa_indexer_amd", "csrc", "sparse_mla_decode32.hip")
+ATTN_FP8_SOURCE = os.path.join(ROOT, "deepseek_dsa_indexer_amd", "csrc", "sparse_attn.hip")
 INDEX_SOURCE = os.path.join(ROOT, "deepseek_dsa_indexer_amd", "csrc", "index_scores.hip")
 PREFILL_SOURCE = os.path.join(ROOT, "deepseek_dsa_indexer_amd", "csrc", "sparse_mha_prefill.hip")
 
@@ -149,9 +154,41 @@ def cpu_baseline(cfg, n_seqs: int, min_seconds: float = 10.0, latent_form: str =
             break
     keys *= reps
     sample += f"; {reps} repetitions in {dt:.1f} s wall"
-    return {"value": reps * frac / dt, "unit": "layer-steps/s", "cores": threads, "kind": "oracle",
-            "sample": sample + f"; threads available {orc.max_threads()}",
-            "keys_scored_per_s": keys / dt}
+    res = {"value": reps * frac / dt, "unit": "layer-steps/s", "cores": threads, "kind": "oracle",
+           "sample": sample + f"; threads available {orc.max_threads()}",
+           "keys_scored_per_s": keys / dt, "cpu_model": cpu_model()}
+    if cfg.form == "latent" and cfg.T == 1:
+        # the same oracle on one thread, over the first two sequences
+        n1 = min(2, cfg.B)
+        c1 = S.make_case(cfg, seqs=list(range(n1)), latent_form=latent_form)
+        all_threads = orc.max_threads()
+        orc.set_threads(1)
+        try:
+            reps1, t1 = 0, time.perf_counter()
+            while True:
+                orc.layer_step_latent(c1["q_i"], c1["q_scale"], c1["w"], c1["k_i"], c1["k_scale"],
+                                      c1["lens"], cfg.sm_scale_i, cfg.k, c1["q"], c1["latent"], cfg.Dv,
+                                      cfg.sm_scale)
+                reps1 += 1
+                d1 = time.perf_counter() - t1
+                if d1 >= min_seconds / 2:
+                    break
+        finally:
+            orc.set_threads(all_threads)
+        res["single_thread"] = {"value": reps1 * (n1 / cfg.B) / d1, "unit": "layer-steps/s",
+                                "sample": f"{n1} of {cfg.B} sequences, {reps1} repetitions in "
+                                          f"{d1:.1f} s on one thread, scaled by {cfg.B}/{n1}"}
+    return res
+
+
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
 
 def measure_prep(D, S, cfg, n: int):
@@ -190,13 +227,183 @@ def measure_prep(D, S, cfg, n: int):
             "achieved_GBs": round(gbs, 1), "hbm_frac": round(gbs / HBM_PEAK_GBS, 4)}
 
 
+# input sets cycled per workload: enough distinct sets that the bytes one step touches
+# (cache streams and gathered rows) exceed the 256 MB Infinity Cache before a set repeats
+DEFAULT_SETS = {"tiny": 2, "decode_v32": 4, "decode_long": 2, "decode_ragged": 2,
+                "prefill_chunk": 1, "prefill_chunk_latent": 1}
+
+
+def measure(D, S, cfg, steps: int, warmup: int, sets: int, latent: str, graph: bool = False,
+            with_prep: bool = True) -> dict:
+    """Time `steps` layer steps of one workload (inputs resident on the GPU, `sets` input
+    sets cycled), then the same steps again with per-kernel HIP events, and return the
+    figures of one JSON object."""
+    import torch
+    fp8_lat = latent == "fp8"
+    lens = S.lengths(cfg)
+    costs = algorithmic_costs(cfg, lens, latent)
+    step_objs = []
+    t_gen = time.perf_counter()
+    for i in range(sets):
+        c = S.make_case(dataclasses.replace(cfg, seed=cfg.seed + 1000 * i) if i else cfg,
+                        latent_form=latent)
+        d = S.to_device(c, "cuda")
+        del c
+        if cfg.form == "latent":
+            step = D.LayerStep(d["q_i"], d["q_scale"], d["w"], d["k_i"], d["k_scale"], d["lens"],
+                               cfg.sm_scale_i, cfg.k, d["q"], cfg.sm_scale, latent=d["latent"],
+                               Dv=cfg.Dv)
+        else:
+            step = D.LayerStep(d["q_i"], d["q_scale"], d["w"], d["k_i"], d["k_scale"], d["lens"],
+                               cfg.sm_scale_i, cfg.k, d["q"], cfg.sm_scale, k=d["k"], v=d["v"])
+        step_objs.append(step)
+    torch.cuda.synchronize()
+    print(f"[bench] {cfg.name}: {sets} input sets on the GPU in "
+          f"{time.perf_counter() - t_gen:.1f} s", file=sys.stderr, flush=True)
+
+    run = list(step_objs)
+    if graph:
+        graphs = []
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            for s_ in step_objs:
+                s_()                                  # warm the launch path before capture
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        for s_ in step_objs:
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                s_()
+            graphs.append(g)
+        run = [g.replay for g in graphs]
+
+    for i in range(warmup):
+        run[i % len(run)]()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        run[i % len(run)]()
+    torch.cuda.synchronize()
+    dt = time.perf_counter() - t0
+    ms_per_step = 1e3 * dt / steps
+    value = steps / dt
+
+    # per-step distribution: HIP events around every step (the library enqueues on the
+    # current stream, which is where torch records its events)
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(steps)]
+    for i in range(steps):
+        evs[i][0].record()
+        run[i % len(run)]()
+        evs[i][1].record()
+    torch.cuda.synchronize()
+    step_ms = sorted(a.elapsed_time(b) for a, b in evs)
+    pct = lambda q: step_ms[min(len(step_ms) - 1, int(q * len(step_ms)))]
+
+    # the same steps again, every kernel launched with a start/stop event pair recorded
+    # by its own dispatch: kernel execution times without the gaps between kernels
+    D.profile_begin(steps)
+    for i in range(steps):
+        step_objs[i % len(step_objs)]()
+    prof = D.profile_end()
+    torch.cuda.synchronize()
+    phase_ms = {k: (v[0] / steps if v[1] else None) for k, v in prof.items()}
+    att_launch_ms = prof["attention"][0] / prof["attention"][1]
+    idx_launch_ms = prof["index_scores"][0] / prof["index_scores"][1]
+    kernels_ms = sum(v for v in phase_ms.values() if v is not None)
+    print(f"[bench] {cfg.name}: kernel time per step (ms): {phase_ms}", file=sys.stderr, flush=True)
+
+    att_gbs = costs["attention_bytes"] / (att_launch_ms * 1e-3) / 1e9
+    att_tfs = costs["attention_flops"] / (att_launch_ms * 1e-3) / 1e12
+    idx_gbs = costs["index_bytes"] / (idx_launch_ms * 1e-3) / 1e9
+    idx_tfs = costs["index_flops"] / (idx_launch_ms * 1e-3) / 1e12
+    workload = cfg.name + ("-fp8" if fp8_lat else "")
+    if cfg.form == "latent":
+        if fp8_lat:
+            kernel, tkey, src = "mla_decode_mfma_kernel", "sparse_mla_decode", ATTN_FP8_SOURCE
+        else:
+            kernel, tkey, src = "mla_decode32_kernel", "sparse_mla_decode", ATTN_SOURCE
+        if cfg.H not in (64, 128) or cfg.Dv != 512:
+            kernel, src = "sparse_attn_generic_kernel", ATTN_FP8_SOURCE
+    else:
+        kernel, tkey, src = "mha_prefill_mfma_kernel", "sparse_mha_prefill", PREFILL_SOURCE
+    traffic = read_traffic(tkey, workload, src)
+    # the attention kernel's bound: whichever of its bytes or its flops takes longer at peak
+    mfma_bound = costs["attention_flops"] / (BF16_PEAK_TFLOPS * 1e12) > \
+        costs["attention_bytes"] / (HBM_PEAK_GBS * 1e9)
+    if mfma_bound:
+        roofline = {"bound": "mfma", "achieved": round(att_tfs, 1), "peak": BF16_PEAK_TFLOPS,
+                    "unit": "TFLOP/s", "frac": round(att_tfs / BF16_PEAK_TFLOPS, 4),
+                    "algorithmic_flops_per_launch": costs["attention_flops"],
+                    "hbm_frac": round(att_gbs / HBM_PEAK_GBS, 4)}
+    else:
+        roofline = {"bound": "hbm", "achieved": round(att_gbs, 1), "peak": HBM_PEAK_GBS,
+                    "unit": "GB/s", "frac": round(att_gbs / HBM_PEAK_GBS, 4),
+                    "algorithmic_bytes_per_launch": costs["attention_bytes"],
+                    "mfma_frac": round(att_tfs / BF16_PEAK_TFLOPS, 4)}
+    roofline.update({"traffic": traffic, "kernel": kernel, "avg_launch_ms": round(att_launch_ms, 5),
+                     "timing": "HIP start/stop events recorded by each launch's dispatch "
+                               "(hipExtLaunchKernel), averaged over the profiled steps"})
+    # the step's floor: each phase at the larger of its HBM time and its matrix-core time at
+    # the peak of its own data type (the indexer's FP8 products, the attention's bf16)
+    t_roof = (max(costs["index_bytes"] / (HBM_PEAK_GBS * 1e9), costs["index_flops"] / (FP8_PEAK_TFLOPS * 1e12)) +
+              max(costs["attention_bytes"] / (HBM_PEAK_GBS * 1e9),
+                  costs["attention_flops"] / (BF16_PEAK_TFLOPS * 1e12)))
+    if cfg.form == "latent":
+        attn_desc = (f"MLA {cfg.H} heads over FP8 latent rows (656 B: {cfg.Dv} e4m3fn + 4 "
+                     f"block scales + {cfg.Dr} bf16 rope)" if fp8_lat else
+                     f"MLA {cfg.H} heads over {cfg.attn_dtype} latent {cfg.Dv}+{cfg.Dr}")
+    else:
+        attn_desc = f"MHA {cfg.H} heads, bf16 qk {cfg.Dqk} / v {cfg.Dv}"
+    out = {
+        "value": round(value, 2),
+        "unit": "layer-steps/s",
+        "steps": steps,
+        "warmup": warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "dtype": cfg.attn_dtype,
+        "config": {"workload": f"{cfg.name}: B={cfg.B}, context {cfg.Lmax} per sequence"
+                               f"{' (' + cfg.lens + ')' if cfg.lens != 'full' else ''}, T={cfg.T}, "
+                               f"indexer {cfg.H_I}x{cfg.D_I} FP8, top-{cfg.k}, {attn_desc}",
+                   "B": cfg.B, "context": cfg.Lmax, "T": cfg.T, "topk": cfg.k, "H_I": cfg.H_I,
+                   "d_I": cfg.D_I, "H": cfg.H, "q_width": cfg.Dq, "input_sets": sets,
+                   "latent_cache": latent if cfg.form == "latent" else None,
+                   "hip_graph": bool(graph)},
+        "step_ms_p10_p50_p90": [round(pct(0.1), 5), round(pct(0.5), 5), round(pct(0.9), 5)],
+        "token_layer_steps_per_s": round(cfg.B * cfg.T * value, 1),
+        "keys_scored_per_s": round(costs["keys"] * value, 1),
+        "keys_per_step": costs["keys"],
+        "step_roofline_frac": round(t_roof / (ms_per_step * 1e-3), 4),
+        "kernel_ms_per_step": {k: (round(v, 5) if v is not None else None) for k, v in phase_ms.items()},
+        "gaps_ms_per_step": round(ms_per_step - kernels_ms, 5),
+        "index_scores": {"avg_launch_ms": round(idx_launch_ms, 5),
+                         "algorithmic_bytes_per_launch": costs["index_bytes"],
+                         "achieved_GBs": round(idx_gbs, 1), "hbm_frac": round(idx_gbs / HBM_PEAK_GBS, 4),
+                         "achieved_TFLOPs": round(idx_tfs, 1),
+                         "mfma_frac_of_bf16_peak": round(idx_tfs / BF16_PEAK_TFLOPS, 4),
+                         "mfma_frac_of_fp8_peak": round(idx_tfs / FP8_PEAK_TFLOPS, 4),
+                         "keys_per_s": round(costs["keys"] / (idx_launch_ms * 1e-3), 1)},
+        "roofline": roofline,
+    }
+    if with_prep:
+        out["indexer_prep"] = measure_prep(D, S, cfg, steps)
+        print(f"[bench] {cfg.name}: indexer prep {out['indexer_prep']}", file=sys.stderr, flush=True)
+    del step_objs, run
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--config", default="decode_v32")
-    ap.add_argument("--sets", type=int, default=4, help="independent input sets cycled")
+    ap.add_argument("--config", default="decode_v32", help="the headline workload")
+    ap.add_argument("--only", action="store_true", help="measure the headline workload only")
+    ap.add_argument("--sets", type=int, default=0,
+                    help="independent input sets cycled (0: the workload's default)")
     ap.add_argument("--latent", choices=["bf16", "fp8"], default="bf16",
                     help="latent cache rows: bf16 (1152 B) or the FP8 storage form (656 B: "
                          "512 e4m3fn codes, four fp32 block scales, 64 bf16 rope values)")
@@ -235,152 +442,40 @@ def main():
         sys.exit(1)
     D.load()
     cfg = S.CONFIGS[args.config]
-    fp8_lat = args.latent == "fp8"
-    if fp8_lat and cfg.form != "latent":
+    if args.latent == "fp8" and cfg.form != "latent":
         print("--latent fp8 applies to the latent (decode) workloads only", file=sys.stderr)
         sys.exit(2)
-    lens = S.lengths(cfg)
-    costs = algorithmic_costs(cfg, lens, args.latent)
-
-    steps = []
-    t_gen = time.perf_counter()
-    for i in range(args.sets):
-        c = S.make_case(dataclasses.replace(cfg, seed=cfg.seed + 1000 * i) if i else cfg,
-                        latent_form=args.latent)
-        d = S.to_device(c, "cuda")
-        del c
-        if cfg.form == "latent":
-            step = D.LayerStep(d["q_i"], d["q_scale"], d["w"], d["k_i"], d["k_scale"], d["lens"],
-                               cfg.sm_scale_i, cfg.k, d["q"], cfg.sm_scale, latent=d["latent"],
-                               Dv=cfg.Dv)
-        else:
-            step = D.LayerStep(d["q_i"], d["q_scale"], d["w"], d["k_i"], d["k_scale"], d["lens"],
-                               cfg.sm_scale_i, cfg.k, d["q"], cfg.sm_scale, k=d["k"], v=d["v"])
-        steps.append(step)
-    torch.cuda.synchronize()
-    print(f"[bench] {cfg.name}: {args.sets} input sets on the GPU in "
-          f"{time.perf_counter() - t_gen:.1f} s", file=sys.stderr, flush=True)
-
-    run = [s for s in steps]
-    if args.graph:
-        graphs = []
-        side = torch.cuda.Stream()
-        side.wait_stream(torch.cuda.current_stream())
-        with torch.cuda.stream(side):
-            for s in steps:
-                s()                                   # warm the launch path before capture
-        torch.cuda.current_stream().wait_stream(side)
-        torch.cuda.synchronize()
-        for s in steps:
-            g = torch.cuda.CUDAGraph()
-            with torch.cuda.graph(g):
-                s()
-            graphs.append(g)
-        run = [g.replay for g in graphs]
-
-    for i in range(args.warmup):
-        run[i % len(run)]()
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        run[i % len(run)]()
-    torch.cuda.synchronize()
-    dt = time.perf_counter() - t0
-    ms_per_step = 1e3 * dt / args.steps
-    value = args.steps / dt
-
-    # per-step distribution: HIP events around every step (the library enqueues on the
-    # current stream, which is where torch records its events)
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(args.steps)]
-    for i in range(args.steps):
-        evs[i][0].record()
-        run[i % len(run)]()
-        evs[i][1].record()
-    torch.cuda.synchronize()
-    step_ms = sorted(a.elapsed_time(b) for a, b in evs)
-    pct = lambda q: step_ms[min(len(step_ms) - 1, int(q * len(step_ms)))]
-
-    # next pass of the same steps with the library's per-phase HIP events
-    D.profile_begin(args.steps)
-    for i in range(args.steps):
-        steps[i % len(steps)]()
-    prof = D.profile_end()
-    torch.cuda.synchronize()
-    phase_ms = {k: (v[0] / v[1] if v[1] else None) for k, v in prof.items()}
-    print(f"[bench] phases (avg ms): {phase_ms}", file=sys.stderr, flush=True)
-
-    prep = measure_prep(D, S, cfg, args.steps)
-    print(f"[bench] indexer prep: {prep}", file=sys.stderr, flush=True)
-
-    att_ms = phase_ms["attention"]
-    idx_ms = phase_ms["index_scores"]
-    att_gbs = costs["attention_bytes"] / (att_ms * 1e-3) / 1e9
-    att_tfs = costs["attention_flops"] / (att_ms * 1e-3) / 1e12
-    idx_gbs = costs["index_bytes"] / (idx_ms * 1e-3) / 1e9
-    idx_tfs = costs["index_flops"] / (idx_ms * 1e-3) / 1e12
-    if cfg.form == "latent":
-        kernel, tkey, src = "mla_decode_mfma_kernel", "sparse_mla_decode", ATTN_SOURCE
-    else:
-        kernel, tkey, src = "mha_prefill_mfma_kernel", "sparse_mha_prefill", PREFILL_SOURCE
-    traffic = read_traffic(tkey, cfg.name + ("-fp8" if fp8_lat else ""), src)
-    # the attention kernel's bound: whichever of its bytes or its flops takes longer at peak
-    mfma_bound = costs["attention_flops"] / (BF16_PEAK_TFLOPS * 1e12) > \
-        costs["attention_bytes"] / (HBM_PEAK_GBS * 1e9)
-    if mfma_bound:
-        roofline = {"bound": "mfma", "achieved": round(att_tfs, 1), "peak": BF16_PEAK_TFLOPS,
-                    "unit": "TFLOP/s", "frac": round(att_tfs / BF16_PEAK_TFLOPS, 4),
-                    "algorithmic_flops_per_launch": costs["attention_flops"],
-                    "hbm_frac": round(att_gbs / HBM_PEAK_GBS, 4)}
-    else:
-        roofline = {"bound": "hbm", "achieved": round(att_gbs, 1), "peak": HBM_PEAK_GBS,
-                    "unit": "GB/s", "frac": round(att_gbs / HBM_PEAK_GBS, 4),
-                    "algorithmic_bytes_per_launch": costs["attention_bytes"],
-                    "mfma_frac": round(att_tfs / BF16_PEAK_TFLOPS, 4)}
-    roofline.update({"traffic": traffic, "kernel": kernel, "avg_launch_ms": round(att_ms, 5)})
-    # the step's floor: each phase at the larger of its HBM time and its MFMA time at peak
-    t_roof = sum(max(costs[f"{p}_bytes"] / (HBM_PEAK_GBS * 1e9),
-                     costs[f"{p}_flops"] / (BF16_PEAK_TFLOPS * 1e12)) for p in ("index", "attention"))
-    if cfg.form == "latent":
-        attn_desc = (f"MLA {cfg.H} heads over FP8 latent rows (656 B: {cfg.Dv} e4m3fn + 4 "
-                     f"block scales + {cfg.Dr} bf16 rope)" if fp8_lat else
-                     f"MLA {cfg.H} heads over bf16 latent {cfg.Dv}+{cfg.Dr}")
-    else:
-        attn_desc = f"MHA {cfg.H} heads, bf16 qk {cfg.Dqk} / v {cfg.Dv}"
+    sets = args.sets or DEFAULT_SETS.get(cfg.name, 4)
+    head = measure(D, S, cfg, args.steps, args.warmup, sets, args.latent, graph=args.graph)
     result = {
         "metric": METRIC,
-        "value": round(value, 2),
+        "value": head["value"],
         "unit": "layer-steps/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(ms_per_step, 5),
+        "ms_per_step": head["ms_per_step"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": head["dtype"],
         "data": "synthetic",
-        "config": {"workload": f"{cfg.name}: B={cfg.B}, context {cfg.Lmax} per sequence, T={cfg.T}, "
-                               f"indexer {cfg.H_I}x{cfg.D_I} FP8, top-{cfg.k}, {attn_desc}",
-                   "B": cfg.B, "context": cfg.Lmax, "T": cfg.T, "topk": cfg.k, "H_I": cfg.H_I,
-                   "d_I": cfg.D_I, "H": cfg.H, "q_width": cfg.Dq, "input_sets": args.sets,
-                   "latent_cache": args.latent if cfg.form == "latent" else None,
-                   "hip_graph": bool(args.graph)},
-        "step_ms_p10_p50_p90": [round(pct(0.1), 5), round(pct(0.5), 5), round(pct(0.9), 5)],
-        "token_layer_steps_per_s": round(cfg.B * cfg.T * value, 1),
-        "keys_scored_per_s": round(costs["keys"] * value, 1),
-        "keys_per_step": costs["keys"],
-        "step_roofline_frac": round(t_roof / (ms_per_step * 1e-3), 4),
-        "phases_avg_ms": {k: (round(v, 5) if v is not None else None) for k, v in phase_ms.items()},
-        "index_scores": {"achieved_GBs": round(idx_gbs, 1), "hbm_frac": round(idx_gbs / HBM_PEAK_GBS, 4),
-                         "achieved_TFLOPs": round(idx_tfs, 1),
-                         "mfma_frac": round(idx_tfs / BF16_PEAK_TFLOPS, 4),
-                         "keys_per_s": round(costs["keys"] / (idx_ms * 1e-3), 1)},
-        "roofline": roofline,
-        "indexer_prep": prep,
-        "cpu_baseline": None if args.no_cpu else cpu_baseline(cfg, args.cpu_seqs, args.cpu_seconds,
-                                                              args.latent),
     }
+    result.update({k: v for k, v in head.items() if k not in ("value", "unit", "steps", "warmup",
+                                                               "ms_per_step", "dtype")})
+    result["cpu_baseline"] = None if args.no_cpu else cpu_baseline(cfg, args.cpu_seqs, args.cpu_seconds,
+                                                                  args.latent)
+    if not args.only:
+        others = {}
+        for name in S.CONFIGS:
+            if name == cfg.name:
+                continue
+            ocfg = S.CONFIGS[name]
+            lat = args.latent if ocfg.form == "latent" and ocfg.attn_dtype == "bf16" else "bf16"
+            steps = min(args.steps, 50) if ocfg.T == 1 else min(args.steps, 10)
+            warm = min(args.warmup, 5)
+            others[name] = measure(D, S, ocfg, steps, warm, DEFAULT_SETS.get(name, 2), lat, with_prep=False)
+        result["other_workloads"] = others
     print(json.dumps(result))
 
 

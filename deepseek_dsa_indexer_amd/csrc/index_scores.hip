@@ -109,14 +109,17 @@ __device__ __forceinline__ float chunk_scores(const v8bf (&qa)[2][8], const floa
     return (lane & 32) ? tot[1] : tot[0];
 }
 
-template <int D, int QR>
+template <int D, int QR, int CHUNKS>
 __global__ __launch_bounds__(kThreads)
 void index_scores_kernel(const uint8_t* __restrict__ q, const float* __restrict__ q_scale,
                          const float* __restrict__ w, const uint8_t* __restrict__ k,
                          const float* __restrict__ k_scale, const int32_t* __restrict__ len,
                          int T, int H, int Lmax, float sm_scale, float* __restrict__ scores,
-                         int fill_invisible, int chunks, int m)
+                         int fill_invisible, int m)
 {
+    // a compile-time chunk count: the chunk loop unrolls completely, so the compiler's own
+    // waits for the loaded key registers count exactly the loads issued after them
+    constexpr int chunks = CHUNKS;
     __shared__ __attribute__((aligned(16))) uint8_t s_q[QR][kMaxHeads * 128];
     __shared__ __attribute__((aligned(16))) float s_wf[QR][kMaxHeads];
     const int keys_per_block = kThreads / kWave * kChunk * chunks;
@@ -164,24 +167,35 @@ void index_scores_kernel(const uint8_t* __restrict__ q, const float* __restrict_
     const float* ks_ptr = k_scale + static_cast<size_t>(b) * Lmax;
     // chunk c of this wave starts at key_blk + (4 c + wave) * 64
     auto chunk_key = [&](int c) { return key_blk + (c * (kThreads / kWave) + wave) * kChunk; };
-    auto load_chunk = [&](int c, uint4 (&dst)[2][4], float& ks) {
+    // The raw bytes stay as loaded until the chunk is used (masking them here would make
+    // the compiler wait for every load of both chunks before any work starts): okb bit kg
+    // tells whether key group kg holds valid keys, and the pieces past d_I are zeroed at use.
+    auto load_chunk = [&](int c, uint4 (&dst)[2][4], float& ks, uint32_t& okb) {
         const int kb = chunk_key(c);
         const bool live = c < chunks && kb <= pos_hi;
+        okb = 0u;
 #pragma unroll
         for (int kg = 0; kg < 2; ++kg) {
             const int key = kb + 32 * kg + (lane & 31);
-            const bool ok = live && key < Lmax;
+            okb |= (live && key < Lmax) ? (1u << kg) : 0u;
             const uint8_t* krow = kb_ptr + static_cast<size_t>(min(key, Lmax - 1)) * D;
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-                const int byte = 64 * (lane >> 5) + 16 * j;      // pieces past d_I read 0
-                const uint4 v = *reinterpret_cast<const uint4*>(krow + (byte < D ? byte : 0));
-                const uint32_t mk = (ok && byte < D) ? 0xffffffffu : 0u;
-                dst[kg][j] = uint4{v.x & mk, v.y & mk, v.z & mk, v.w & mk};
+                const int byte = 64 * (lane >> 5) + 16 * j;      // pieces past d_I: masked at use
+                dst[kg][j] = *reinterpret_cast<const uint4*>(krow + (byte < D ? byte : 0));
             }
         }
         // positions at or beyond Lmax are never stored, so the clamped scale needs no mask
         ks = ks_ptr[min(kb + lane, Lmax - 1)];
+    };
+    auto masked = [&](const uint4 (&raw)[2][4], uint32_t okb, uint4 (&dst)[2][4]) {
+#pragma unroll
+        for (int kg = 0; kg < 2; ++kg)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const uint32_t mk = (((okb >> kg) & 1u) && 64 * (lane >> 5) + 16 * j < D) ? 0xffffffffu : 0u;
+                dst[kg][j] = uint4{raw[kg][j].x & mk, raw[kg][j].y & mk, raw[kg][j].z & mk, raw[kg][j].w & mk};
+            }
     };
 
     // ---- the block's query rows and folded head weights go through LDS once: q as
@@ -212,10 +226,13 @@ void index_scores_kernel(const uint8_t* __restrict__ q, const float* __restrict_
         wv = w[qrow * H + hc];
         qsv = q_scale[qrow * H + hc];
     }
-    uint4 cur[2][4], nxt[2][4];
-    float ks_cur, ks_nxt;
-    load_chunk(0, cur, ks_cur);
-    load_chunk(1, nxt, ks_nxt);
+    // two register sets, used alternately: chunk c + 2 loads into the set chunk c has used
+    uint4 ra[2][4], rb[2][4];
+    float ks_a, ks_b;
+    uint32_t ok_a, ok_b;
+    load_chunk(0, ra, ks_a, ok_a);
+    __builtin_amdgcn_sched_barrier(0);     // chunk 0's loads all go out before chunk 1's
+    load_chunk(1, rb, ks_b, ok_b);
 #pragma unroll
     for (int u = 0; u < kQLoads; ++u) {
         const int i = threadIdx.x + u * kThreads;
@@ -231,26 +248,35 @@ void index_scores_kernel(const uint8_t* __restrict__ q, const float* __restrict_
 #pragma unroll
     for (int r = 0; r < QR; ++r) load_queries<128>(s_q[r], s_wf[r], kMaxHeads, lane, qa[r], wf[r]);
 
-    for (int c = 0; c < chunks; ++c) {
+    auto process = [&](int c, uint4 (&raw)[2][4], float ks, uint32_t okb) {
         const int kb = chunk_key(c);
         const int key = kb + lane;
         if (kb > pos_hi) {
             if (fill_invisible && key < Lmax)
                 for (int r = 0; r < nrows; ++r) out[static_cast<size_t>(r) * Lmax + key] = -INFINITY;
         } else {
+            uint4 kr[2][4];
+            masked(raw, okb, kr);
 #pragma unroll
             for (int r = 0; r < QR; ++r) {
-                const float total = chunk_scores(qa[r], wf[r], cur, lane);
+                const float total = chunk_scores(qa[r], wf[r], kr, lane);
                 if (r < nrows && key < Lmax)
-                    out[static_cast<size_t>(r) * Lmax + key] = (key <= last[r]) ? total * ks_cur : -INFINITY;
+                    out[static_cast<size_t>(r) * Lmax + key] = (key <= last[r]) ? total * ks : -INFINITY;
             }
         }
+    };
+    // (the scheduling barriers keep each chunk's work, and so its waits, ahead of the next
+    // chunk's: otherwise the interleaved code waits for the later chunk's loads early)
 #pragma unroll
-        for (int kg = 0; kg < 2; ++kg)
-#pragma unroll
-            for (int j = 0; j < 4; ++j) cur[kg][j] = nxt[kg][j];
-        ks_cur = ks_nxt;
-        if (c + 2 < chunks) load_chunk(c + 2, nxt, ks_nxt);
+    for (int c = 0; c < chunks; c += 2) {
+        process(c, ra, ks_a, ok_a);
+        __builtin_amdgcn_sched_barrier(0);
+        if (c + 2 < chunks) load_chunk(c + 2, ra, ks_a, ok_a);
+        if (c + 1 < chunks) {
+            process(c + 1, rb, ks_b, ok_b);
+            __builtin_amdgcn_sched_barrier(0);
+            if (c + 3 < chunks) load_chunk(c + 3, rb, ks_b, ok_b);
+        }
     }
 }
 
@@ -410,27 +436,37 @@ void index_scores_decode_kernel(const uint8_t* __restrict__ q, const float* __re
     }
 }
 
-template <int D, int QR>
-hipError_t launch_d(const IndexScoresArgs& a, int chunks, hipStream_t stream) {
-    const int keys_per_block = kThreads / kWave * kChunk * chunks;
+template <int D, int QR, int CHUNKS>
+hipError_t launch_d(const IndexScoresArgs& a, hipStream_t stream) {
+    const int keys_per_block = kThreads / kWave * kChunk * CHUNKS;
     const int row_groups = (a.T + QR - 1) / QR;
     dim3 grid(a.B * row_groups, (a.Lmax + keys_per_block - 1) / keys_per_block);
-    return launch_kernel(kPhaseIndex, index_scores_kernel<D, QR>, grid, dim3(kThreads), 0, stream,
+    return launch_kernel(kPhaseIndex, index_scores_kernel<D, QR, CHUNKS>, grid, dim3(kThreads), 0, stream,
                          a.q, a.q_scale, a.w, a.k, a.k_scale, a.len, a.T, a.H, a.Lmax, a.sm_scale,
-                         a.scores, a.fill_invisible, chunks, a.m);
+                         a.scores, a.fill_invisible, a.m);
 }
 
 // Key chunks per wave: enough waves to cover every SIMD twice (2048 waves), then longer
 // streams per wave (up to 8 chunks) so the block's query and weight set-up is amortised.
 template <int D>
 hipError_t launch_rows(const IndexScoresArgs& a, hipStream_t stream) {
-    if (a.T >= 2) return launch_d<D, 2>(a, 4, stream);
+    if (a.T >= 2) return launch_d<D, 2, 4>(a, stream);
     const long long total_chunks = static_cast<long long>(a.B) * ((a.Lmax + kChunk - 1) / kChunk);
     const int chunks = static_cast<int>(std::min<long long>(8, std::max<long long>(2, total_chunks / 2048)));
     // short streams (two chunks per wave) gain nothing from the deeper LDS pipeline and
     // pay its longer issue sequence: measured 12.4 vs 10.9 us at B=32, L=8192; at
     // B=8, L=131072 (eight chunks per wave) the LDS form is ahead
-    if (a.B > kThreads * kMaxSeqPerThread || chunks < 4) return launch_d<D, 1>(a, chunks, stream);
+    if (a.B > kThreads * kMaxSeqPerThread || chunks < 4) {
+        switch (chunks) {
+        case 2: return launch_d<D, 1, 2>(a, stream);
+        case 3: return launch_d<D, 1, 3>(a, stream);
+        case 4: return launch_d<D, 1, 4>(a, stream);
+        case 5: return launch_d<D, 1, 5>(a, stream);
+        case 6: return launch_d<D, 1, 6>(a, stream);
+        case 7: return launch_d<D, 1, 7>(a, stream);
+        default: return launch_d<D, 1, 8>(a, stream);
+        }
+    }
     const int keys_per_block = kWaves * kChunk * chunks;
     dim3 grid(a.B, (a.Lmax + keys_per_block - 1) / keys_per_block);
     return launch_kernel(kPhaseIndex, index_scores_decode_kernel<D>, grid, dim3(kThreads), 0, stream,

@@ -25,23 +25,31 @@
 // Per tile of 32 selected rows the four waves of a SIMD issue 34 matrix-core instructions
 // (18 QK + 16 PV) against 68 of the 16x16x32 form.
 //
-// Pipeline (step i, two workgroup barriers):
-//   A(i)   tile i has landed for every wave; P(i-1) is published.  Tile i+2 is issued.
+// Pipeline.  A tile's buffer is released in its own step -- the QK waves read K in phase
+// 1 and the PV waves copy their V operands into registers in the same phase -- so while
+// tile i is in use, tiles i+1 and i+2 are in flight and tile i+3 goes out after step i's
+// second barrier.  (A further tile in flight, which the ring would allow, measured no
+// faster per step and slower overall.)  The PV waves issue all gathers, in phase 2, while
+// the QK waves form the softmax numerators; issued between their PV instructions instead,
+// the loads held back the matrix-core issue and the PV phase grew from 0.5 to 1.25 us.  The queries reach the QK waves through LDS (direct loads
+// into buffers 2 and 3 before those tiles are issued), so the compiler's own waits for
+// register loads never drain the gathers.
+// Step i (two workgroup barriers):
+//   A(i)     tile i has landed for every wave; P(i-1) is published.
 //   phase 1  QK waves: QK(i), then the partner's half of S(i) to LDS.
-//            PV waves: all P(i-1) operands into registers, then half of PV(i-1).
-//   B(i)
-//   phase 2  QK waves: add the partner's half, softmax numerators of S(i), publish P(i)
-//            (the PV waves no longer read P(i-1) from LDS, so one P buffer suffices).
-//            PV waves: the other half of PV(i-1), overlapping the softmax.
+//            PV waves: P(i-1) operands from LDS, PV(i-1) from the V operands held in
+//            registers since step i-1, then the V operands of tile i into registers.
+//   B(i)     tile i's buffer is free.
+//   phase 2  QK waves: add the partner's half, softmax numerators, publish P(i).
+//            PV waves: issue tile i+3 (at step 0: tiles 2 and 3).
 // Softmax without a running rescale: each head's numerators are exp2(logit - m_ref), where
-// m_ref is the largest logit of the split's first tile (its dominant key gets the
-// numerator 1 exactly): at step 0 the two waves of a head half exchange their whole S
-// partials through ring buffer 3, which no gather uses before step 1.  A split whose
-// first tile holds no usable slot takes instead the logit of the first usable key of its
-// first usable tile (both halves of that key's logit travel with S).  A key with a logit
-// more than 2^64 above the reference (log2 units) marks the split, which is then
-// recomputed with the split's maximum as reference; the normalised result is the same
-// softmax.
+// m_ref is the largest logit of the split's first tile, so the tile's dominant key gets the
+// numerator 1 exactly: at step 0 both waves of a head half post the maximum of their 16
+// keys and read the partner's after one extra barrier.  A split whose first tile holds no
+// usable slot takes instead the logit of the first usable key of its first usable tile
+// (both column halves of that key's logit travel with S).  A key with a logit more than
+// 2^64 above the reference (log2 units) marks the split, which is then recomputed with the
+// split's maximum as reference; the normalised result is the same softmax.
 #include "dsa_device.h"
 #include "dsa_internal.h"
 
@@ -59,7 +67,8 @@ constexpr int kRowChunks = kRowBytes / 16;          // 72
 constexpr int kKt = 32;                             // selected rows per tile
 constexpr int kTileBytes = kKt * kRowBytes;         // 36864
 constexpr int kTileLoads = kTileBytes / (kWave * 16);   // 36 wave-wide 1 KB loads
-constexpr int kGatherMax = (kTileLoads + kWaves - 1) / kWaves;   // 5
+constexpr int kGatherWaves = 4;                    // the PV waves issue every tile's loads
+constexpr int kGatherLoads = kTileLoads / kGatherWaves;          // 9 per wave and tile
 constexpr int kBufs = 4;                            // tile ring
 constexpr int kMaxTiles = 16;                       // tiles per split
 constexpr int kMaxSlots = kMaxTiles * kKt;          // 512 slots per split
@@ -71,7 +80,7 @@ constexpr float kRefSpan = 64.0f;                   // log2 units above the refe
 // 2,048 (slots) + small.
 __shared__ __attribute__((aligned(16))) uint8_t s_tile[kBufs * kTileBytes];
 __shared__ __attribute__((aligned(16))) float s_half[2][2][2][kWave][4];   // [hh][owner dh][j][lane][4]
-__shared__ float s_ref[2][2][32];                   // [hh][from dh][head]: partial logit of the reference key
+__shared__ float s_ref[2][2][32];                   // [hh][dh][head]: reference exchange
 __shared__ __attribute__((aligned(16))) uint8_t s_p[2][2][kWave][16];      // [hh][kk][lane][8 bf16]
 __shared__ int32_t s_keys[kMaxSlots];
 __shared__ uint32_t s_tmask[kMaxTiles];             // usable slots of each tile (bit = row)
@@ -88,46 +97,61 @@ __device__ __forceinline__ void wait_vmcnt() { asm volatile("s_waitcnt vmcnt(%0)
 // gathers in flight stay in flight across it.
 __device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
-// Wait until this wave's gathers of the current tile have landed, leaving the next tile's
-// in flight (waves 0..3 issue 5 loads per tile, waves 4..7 four).
-__device__ __forceinline__ void wait_tile(bool later, bool five) {
-    if (!later) wait_vmcnt<0>();
-    else if (five) wait_vmcnt<5>();
-    else wait_vmcnt<4>();
+// Wait until this wave's gathers of the current tile have landed, leaving the `later`
+// tiles issued after it (0..3) in flight: a PV wave issues kGatherLoads loads per tile,
+// and loads complete in issue order.
+__device__ __forceinline__ void wait_tile(int later) {
+    if (later >= 3) wait_vmcnt<3 * kGatherLoads>();
+    else if (later == 2) wait_vmcnt<2 * kGatherLoads>();
+    else if (later == 1) wait_vmcnt<kGatherLoads>();
+    else wait_vmcnt<0>();
 }
 
-// Direct global->LDS loads of tile `ti`: wave w issues the wave-wide 1 KB loads ci = w,
-// w + 8, ... < 36; lane l of load ci fetches 16-byte chunk c = 64 ci + l of the tile,
-// i.e. chunk c % 72 of selected row c / 72, stored at chunk position (c % 72) ^ (row & 7)
-// of that row (the XOR spreads the matrix-core operand reads over the LDS banks).
-// Written as inline assembly so that the compiler, which cannot tell the ring's buffers
-// apart, inserts no drain of these loads before later LDS reads; completion is tracked
-// with wait_tile() and published by lds_barrier().  M0 holds the wave-uniform LDS
-// destination; nothing else in this kernel uses M0.  Unused slots fetch row 0 (masked).
-__device__ __forceinline__ void gather_tile(const uint8_t* lat_b, int ti, int wave, int lane) {
-    asm volatile("" : "+v"(lane));
+// LDS layout of a tile: row r (1152 bytes = 72 chunks of 16 bytes) keeps its chunk c at
+// chunk position c ^ swz(r), swz(r) = (r >> 1) & 7.  Rows are 288 dwords apart, which is 32
+// banks, so rows of one parity share a half of the 64 banks; within it the XOR gives the 8
+// rows of each parity among any 16 consecutive rows distinct 4-bank groups, and 16-lane
+// reads of one chunk over 16 consecutive rows are free of bank conflicts.  (The XOR stays
+// inside each aligned group of 8 chunks, so the rope chunks 64..71 stay in place.)
+__device__ __forceinline__ int swz(int r) { return (r >> 1) & 7; }
+
+// Direct global->LDS loads of tile `ti`, issued by the PV waves (the QK waves' time between
+// their matrix-core chains goes to the softmax): PV wave c issues the wave-wide 1 KB loads
+// ci = c, c + 4, ... < 36; lane l of load ci fetches 16-byte chunk q = 64 ci + l of the tile,
+// i.e. chunk q % 72 of selected row q / 72, stored at its swizzled position.  Written as
+// inline assembly so that the compiler, which cannot tell the ring's buffers apart, inserts
+// no drain of these loads before later LDS reads; completion is tracked with wait_tile()
+// and published by lds_barrier().  M0 holds the wave-uniform LDS destination; nothing else
+// in this kernel uses M0.  Unused slots fetch row 0 (masked).
+struct GatherLane {
+    int key[kGatherLoads];       // tile row of load i for this lane
+    uint32_t off[kGatherLoads];  // byte offset of the lane's source chunk within that row
+};
+__device__ __forceinline__ GatherLane gather_lane(int c, int lane) {
+    GatherLane gl;
+#pragma unroll
+    for (int i = 0; i < kGatherLoads; ++i) {
+        const int q = (c + kGatherWaves * i) * kWave + lane;
+        const int key = q / kRowChunks;
+        gl.key[i] = key;
+        gl.off[i] = static_cast<uint32_t>(((q - key * kRowChunks) ^ swz(key)) * 16);
+    }
+    return gl;
+}
+__device__ __forceinline__ void gather_tile(const uint8_t* lat_b, int ti, int c, const GatherLane& gl) {
     const uint32_t lds_base = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(
         (__attribute__((address_space(3))) uint8_t*)(tile_buf(ti))));
-    int s[kGatherMax], key[kGatherMax];
+    int s[kGatherLoads];
 #pragma unroll
-    for (int i = 0; i < kGatherMax; ++i) {
-        const int c = (wave + kWaves * i) * kWave + lane;
-        key[i] = min(c / kRowChunks, kKt - 1);
-        s[i] = s_keys[ti * kKt + key[i]];
-    }
+    for (int i = 0; i < kGatherLoads; ++i) s[i] = s_keys[ti * kKt + gl.key[i]];
 #pragma unroll
-    for (int i = 0; i < kGatherMax; ++i) {
-        const int ci = wave + kWaves * i;
-        if (ci < kTileLoads) {
-            const int c = ci * kWave + lane;
-            const int row = s[i] < 0 ? 0 : s[i];
-            const uint32_t off = static_cast<uint32_t>(row) * kRowBytes +
-                                 ((c - key[i] * kRowChunks) ^ (key[i] & 7)) * 16;
-            const uint8_t* src = lat_b + off;
-            const uint32_t m0v = __builtin_amdgcn_readfirstlane(lds_base + ci * kWave * 16);
-            asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off"
-                         :: "s"(m0v), "v"(src) : "memory");
-        }
+    for (int i = 0; i < kGatherLoads; ++i) {
+        const int ci = c + kGatherWaves * i;
+        const int row = s[i] < 0 ? 0 : s[i];
+        const uint8_t* src = lat_b + static_cast<size_t>(row) * kRowBytes + gl.off[i];
+        const uint32_t m0v = __builtin_amdgcn_readfirstlane(lds_base + ci * kWave * 16);
+        asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off"
+                     :: "s"(m0v), "v"(src) : "memory");
     }
 }
 
@@ -145,7 +169,7 @@ __device__ __forceinline__ v16f qk_half(const v8bf (&qreg)[kKs], const uint8_t* 
     asm volatile("" : "+v"(lo));
     const int r = lo & 31;
     const int g = lo >> 5;
-    const int x = r & 7;
+    const int x = swz(r);
     const uint8_t* row = kb + r * kRowBytes;
     // chunk 36 DH + 2 ks + g = 8 a + b sits at 16 (8 a + (b ^ x)); b = (C0 & 7) + g with
     // C0 = 36 DH + 2 ks even, so four per-lane offsets cover every K-step
@@ -159,7 +183,7 @@ __device__ __forceinline__ v16f qk_half(const v8bf (&qreg)[kKs], const uint8_t* 
     v16f acc;
 #pragma unroll
     for (int i = 0; i < 16; ++i) acc[i] = 0.f;
-    constexpr int kPre = 3;
+    constexpr int kPre = 9;               // K-steps of operand reads in flight (LDS latency)
     v8bf a[kPre];
 #pragma unroll
     for (int ks = 0; ks < kPre; ++ks) a[ks] = *addr(ks);
@@ -202,77 +226,50 @@ __device__ __forceinline__ void qk_send(const v16f& acc, int hh, int lane, bool 
     }
 }
 
-// Step 0 with usable keys in tile 0: the whole partial (all 32 keys) goes to the partner
-// through ring buffer 3, which no gather touches before step 1, so that both waves of the
-// head half form every logit of the tile and take the tile's maximum as the reference.
-// The dominant key of the tile then gets the numerator 1 exactly.
-__device__ __forceinline__ float* full_exchange(int hh, int dh) {
-    return reinterpret_cast<float*>(s_tile + 3 * kTileBytes) + (2 * hh + dh) * 16 * kWave;
-}
-__device__ __forceinline__ void qk_send_full(const v16f& acc, int hh, int dh, int lane) {
-    float* dst = full_exchange(hh, dh);
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        float4 v;
-        v.x = acc[4 * j + 0];
-        v.y = acc[4 * j + 1];
-        v.z = acc[4 * j + 2];
-        v.w = acc[4 * j + 3];
-        *reinterpret_cast<float4*>(dst + (j * kWave + lane) * 4) = v;
-    }
-}
-// Adds the partner's whole partial and returns the tile's largest usable logit of this
-// lane's head (log2 units; the same value in both waves: the two partials are added in
-// either order, which IEEE addition does not distinguish).
-__device__ __forceinline__ float qk_full_max(v16f& acc, int hh, int dh, int lane, uint32_t tmask,
-                                             float scale_log2) {
-    const float* src = full_exchange(hh, 1 - dh);
-    const int g = lane >> 5;
-    float mx = -INFINITY;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        const float4 v = *reinterpret_cast<const float4*>(src + (j * kWave + lane) * 4);
-        acc[4 * j + 0] += v.x;
-        acc[4 * j + 1] += v.y;
-        acc[4 * j + 2] += v.z;
-        acc[4 * j + 3] += v.w;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int key = 8 * j + 4 * g + i;
-            if ((tmask >> key) & 1u) mx = fmaxf(mx, acc[4 * j + i] * scale_log2);
-        }
-    }
-    return max_xor32(mx);
-}
-
 // Phase 2: this wave's 16 keys of S complete, softmax numerators, P published.  The lane
 // holds keys 16 DH + 8 (s / 4) + 4 (l / 32) + s % 4, s = 0..7, of head l % 32 -- exactly
-// K-slot s of the P operand for K-step DH of the PV product.  want_ref: this tile holds
-// the split's first usable key, whose logit becomes the head's reference (the sum of the
-// two column halves' partials, formed in the same order by both waves of the half).
+// K-slot s of the P operand for K-step DH of the PV product.
+//   first_max  (step 0, tile 0 usable) the reference is the tile's largest logit: each
+//              wave posts the maximum of its 16 keys, and after one extra barrier (which
+//              the PV waves pass as well) takes the larger of the two;
+//   want_ref   (a later first usable tile) the reference is the logit of the tile's first
+//              usable key, the sum of the two halves' partials.
 template <int DH>
 __device__ __forceinline__ void qk_finish(v16f& acc, QkState& st, int hh, int lane, uint32_t tmask,
-                                          bool want_ref, float scale_log2, bool fixed, bool summed) {
-    if (!summed) {
+                                          bool first_max, bool want_ref, float scale_log2, bool fixed) {
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
-            const float4 v = *reinterpret_cast<const float4*>(&s_half[hh][DH][j][lane][0]);
-            acc[8 * DH + 4 * j + 0] += v.x;
-            acc[8 * DH + 4 * j + 1] += v.y;
-            acc[8 * DH + 4 * j + 2] += v.z;
-            acc[8 * DH + 4 * j + 3] += v.w;
-        }
+    for (int j = 0; j < 2; ++j) {
+        const float4 v = *reinterpret_cast<const float4*>(&s_half[hh][DH][j][lane][0]);
+        acc[8 * DH + 4 * j + 0] += v.x;
+        acc[8 * DH + 4 * j + 1] += v.y;
+        acc[8 * DH + 4 * j + 2] += v.z;
+        acc[8 * DH + 4 * j + 3] += v.w;
     }
-    if (want_ref) st.m_ref = (s_ref[hh][0][lane & 31] + s_ref[hh][1][lane & 31]) * scale_log2;
     const int g = lane >> 5;
     float v[8];
     float mx = -INFINITY;
+    if (tmask == 0xffffffffu) {                           // every slot usable (uniform)
 #pragma unroll
-    for (int s = 0; s < 8; ++s) {
-        const int key = 16 * DH + 8 * (s >> 2) + 4 * g + (s & 3);
-        const bool ok = (tmask >> key) & 1u;
-        v[s] = ok ? acc[8 * DH + s] * scale_log2 : -INFINITY;
-        mx = fmaxf(mx, v[s]);
+        for (int s = 0; s < 8; ++s) {
+            v[s] = acc[8 * DH + s] * scale_log2;
+            mx = fmaxf(mx, v[s]);
+        }
+    } else {
+#pragma unroll
+        for (int s = 0; s < 8; ++s) {
+            const int key = 16 * DH + 8 * (s >> 2) + 4 * g + (s & 3);
+            const bool ok = (tmask >> key) & 1u;
+            v[s] = ok ? acc[8 * DH + s] * scale_log2 : -INFINITY;
+            mx = fmaxf(mx, v[s]);
+        }
+    }
+    if (first_max) {
+        const float m2 = max_xor32(mx);
+        if (lane < 32) s_ref[hh][DH][lane] = m2;
+        lds_barrier();                                     // C: the extra step-0 barrier
+        st.m_ref = fmaxf(s_ref[hh][0][lane & 31], s_ref[hh][1][lane & 31]);
+    } else if (want_ref) {
+        st.m_ref = (s_ref[hh][0][lane & 31] + s_ref[hh][1][lane & 31]) * scale_log2;
     }
     if (!fixed) {
         st.m_max = fmaxf(st.m_max, mx);
@@ -290,6 +287,22 @@ __device__ __forceinline__ void qk_finish(v16f& acc, QkState& st, int hh, int la
     }
     st.l_run += psum;
     *reinterpret_cast<v8s*>(&s_p[hh][DH][lane][0]) = pk;
+}
+
+// Query operands of QK wave (hh, dh) through LDS: 18 wave-wide direct loads of 1 KB into
+// ring buffers 2 and 3 (wave w's at 18 KB * w), lane l of load ks fetching head
+// 32 hh + l % 32, columns 288 dh + 16 ks + 8 (l / 32) .. + 7 -- the B-operand layout, so
+// each lane later reads back its own 16 bytes.
+__device__ __forceinline__ uint8_t* q_stage(int wave) { return s_tile + 2 * kTileBytes + wave * kKs * 1024; }
+__device__ __forceinline__ void load_q(const uint16_t* qrow, int wave) {
+    const uint32_t lds_base = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(
+        (__attribute__((address_space(3))) uint8_t*)(q_stage(wave))));
+#pragma unroll
+    for (int ks = 0; ks < kKs; ++ks) {
+        const uint32_t m0v = __builtin_amdgcn_readfirstlane(lds_base + ks * 1024);
+        asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off"
+                     :: "s"(m0v), "v"(qrow + 16 * ks) : "memory");
+    }
 }
 
 // ---- PV waves
@@ -310,7 +323,7 @@ struct PvState {
 // 4 j .. 4 j + 3 of the group's 16.
 struct VAddr {
     int base;      // byte offset of (row 4 g + e, column group) for this lane, minus swizzle
-    int t[2];      // swizzled 16-byte chunk offsets for ct & 1 = 0 / 1
+    int t[2][2];   // swizzled 16-byte chunk offsets [key half q][ct & 1]
 };
 __device__ __forceinline__ VAddr v_addr(int c, int lane) {
     int lo = lane;
@@ -320,34 +333,45 @@ __device__ __forceinline__ VAddr v_addr(int c, int lane) {
     const int e = n >> 2;
     const int j = n & 3;
     const int g = G >> 1;
-    const int x = 4 * g + e;                  // key & 7 of every key this lane points at
     const int low = 2 * (G & 1) + (j >> 1);   // column chunk bits below the tile's 4 ct
     VAddr va;
-    va.base = x * kRowBytes + 8 * (j & 1) + 16 * 16 * c;
-    va.t[0] = 16 * ((0 + low) ^ x);
-    va.t[1] = 16 * ((4 + low) ^ x);
+    va.base = (4 * g + e) * kRowBytes + 8 * (j & 1) + 16 * 16 * c;
+#pragma unroll
+    for (int qh = 0; qh < 2; ++qh) {
+        // the lane's keys 16 kk + 8 qh + 4 g + e share swz = (4 qh + 2 g + e / 2) & 7
+        const int x = swz(8 * qh + 4 * g + e);
+        va.t[qh][0] = 16 * ((0 + low) ^ x);
+        va.t[qh][1] = 16 * ((4 + low) ^ x);
+    }
     return va;
 }
 
 __device__ __forceinline__ v8bf v_operand(const uint8_t* kb, const VAddr& va, int kk, int ct) {
-    const uint8_t* p = kb + va.base + va.t[ct & 1] + 16 * 8 * (ct >> 1) + 16 * kk * kRowBytes;
+    const uint8_t* p = kb + va.base + 16 * 8 * (ct >> 1) + 16 * kk * kRowBytes;
     const v4bf_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
-        (__attribute__((address_space(3))) v4bf_t*)(p));
+        (__attribute__((address_space(3))) v4bf_t*)(p + va.t[0][ct & 1]));
     const v4bf_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
-        (__attribute__((address_space(3))) v4bf_t*)(p + 8 * kRowBytes));
+        (__attribute__((address_space(3))) v4bf_t*)(p + 8 * kRowBytes + va.t[1][ct & 1]));
     return v8bf{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
 }
 
-// PV of K-step kk of the previous tile: 8 instructions (2 head halves x 4 column tiles).
-__device__ __forceinline__ void pv_step(PvState& st, const uint8_t* kb, const VAddr& va, int kk,
-                                        const v8bf (&pop)[2]) {
-    v8bf vop[4];
+// The V operands of one tile for this wave's four column tiles and both K-steps.
+__device__ __forceinline__ void load_v(v8bf (&vop)[2][4], const uint8_t* kb, const VAddr& va) {
 #pragma unroll
-    for (int ct = 0; ct < 4; ++ct) vop[ct] = v_operand(kb, va, kk, ct);
+    for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
-    for (int ct = 0; ct < 4; ++ct)
+        for (int ct = 0; ct < 4; ++ct) vop[kk][ct] = v_operand(kb, va, kk, ct);
+}
+
+// PV of one tile: 16 instructions (2 K-steps x 2 head halves x 4 column tiles).
+__device__ __forceinline__ void pv_tile(PvState& st, const v8bf (&vop)[2][4], const v8bf (&pop)[2][2]) {
 #pragma unroll
-        for (int hh = 0; hh < 2; ++hh) st.acc[hh][ct] = mfma_bf16_32x32x16(vop[ct], pop[hh], st.acc[hh][ct]);
+    for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+        for (int ct = 0; ct < 4; ++ct)
+#pragma unroll
+            for (int hh = 0; hh < 2; ++hh)
+                st.acc[hh][ct] = mfma_bf16_32x32x16(vop[kk][ct], pop[kk][hh], st.acc[hh][ct]);
 }
 
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
@@ -382,8 +406,8 @@ void mla_decode32_kernel(const uint16_t* __restrict__ q, const uint8_t* __restri
     const int n_tiles = max(0, min(tiles_per_split, n_tiles_total - tile0));
     const int nslots = n_tiles * kKt;
 
-    // start-up loads back to back: this split's selected positions, the length, then (QK
-    // waves, below) the queries; the positions are checked against pos once both are in
+    // start-up loads: this split's selected positions and the sequence length; the
+    // positions are checked against pos once both are in
     const int32_t* sel = idx + static_cast<size_t>(row) * k;
     const int j0 = threadIdx.x;               // kMaxSlots == kThreads
     const int slot0 = tile0 * kKt + j0;
@@ -391,7 +415,7 @@ void mla_decode32_kernel(const uint16_t* __restrict__ q, const uint8_t* __restri
     const int seq_len = len[b];
     const uint8_t* lat_b = latent + static_cast<size_t>(b) * Lmax * kRowBytes;
 
-    auto publish_slots = [&]() {
+    {
         const int pos = n_visible(seq_len, T, t, Lmax, m) - 1;     // last visible cache row
         const int sv = (sraw >= 0 && sraw <= pos) ? sraw : -1;
         if (j0 < nslots) s_keys[j0] = sv;
@@ -402,18 +426,7 @@ void mla_decode32_kernel(const uint16_t* __restrict__ q, const uint8_t* __restri
             s_tmask[2 * wave + 1] = static_cast<uint32_t>(bal >> 32);
         }
         lds_barrier();        // s_keys, s_tmask ready
-    };
-    auto start_tiles = [&]() {
-        if (n_tiles > 0) gather_tile(lat_b, 0, wave, lane);
-        wait_vmcnt<0>();                          // tile 0 and (QK waves) the queries
-        if (n_tiles > 1) gather_tile(lat_b, 1, wave, lane);
-    };
-    // A(ti): tile ti has landed for every wave and P(ti - 1) is published; tile ti + 2 goes out
-    auto step_begin = [&](int ti) {
-        if (ti < n_tiles) wait_tile(ti + 1 < n_tiles, wave < 4);
-        lds_barrier();
-        if (ti + 2 < n_tiles) gather_tile(lat_b, ti + 2, wave, lane);
-    };
+    }
     auto redo_flags = [&](bool over) {
         if (lane == 0) s_redo[wave] = __ballot(over) != 0ull;
     };
@@ -423,22 +436,34 @@ void mla_decode32_kernel(const uint16_t* __restrict__ q, const uint8_t* __restri
         for (int w = 0; w < kWaves; ++w) redo |= s_redo[w];
         return redo != 0;
     };
+    // Tiles in flight while tile ti is used: ti + 1 and ti + 2 (at step 0 only tile 1: tiles
+    // 2 and 3 follow the queries through buffers 2 and 3 and go out after barrier B(0)).
+    auto later_tiles = [&](int ti) { return ti == 0 ? min(1, n_tiles - 1) : min(2, n_tiles - 1 - ti); };
+    // A(ti): the PV waves wait for their loads of tile ti (the QK waves load no tiles)
+    auto step_begin = [&](int ti) {
+        if (!qk_wave && ti < n_tiles) wait_tile(later_tiles(ti));
+        lds_barrier();
+    };
+    auto step_gathers = [&](int ti, const GatherLane& gl) {   // PV waves, after B(ti): tile ti's buffer is free
+        if (ti == 0) {
+            for (int tj = 2; tj <= 3; ++tj)
+                if (tj < n_tiles) gather_tile(lat_b, tj, wave - 4, gl);
+        } else if (ti + 3 < n_tiles) {
+            gather_tile(lat_b, ti + 3, wave - 4, gl);
+        }
+    };
+    const bool tile0_usable = n_tiles > 0 && s_tmask[0] != 0u;
 
     // The two roles run separate code with the same barrier sequence (the slot barrier,
-    // A and B per step for n_tiles + 1 steps, the recompute decision, an optional second
-    // pass, the staging barrier), so their registers -- queries and S for the QK waves,
-    // output accumulators for the PV waves -- are never live at the same time.  Every wave
-    // issues and waits for its share of each tile's gathers.
+    // A and B per step for n_tiles + 1 steps plus C at step 0 of a first pass with a usable
+    // first tile, the recompute decision, an optional second pass, the staging barrier),
+    // so their registers -- queries and S for the QK waves, output accumulators and V
+    // operands for the PV waves -- are never live at the same time.  The PV waves issue and
+    // wait for every tile's gathers; the QK waves see the tiles through barrier A.
     if (qk_wave) {
         v8bf qreg[kKs];
-        {
-            // head 32 hh + l % 32, columns 288 dh + 16 ks + 8 (l / 32) .. + 7
-            const uint16_t* qrow = q + (static_cast<size_t>(row) * H_total + head0 + 32 * hh + (lane & 31)) * kDq +
-                                   288 * dh + 8 * (lane >> 5);
-#pragma unroll
-            for (int ks = 0; ks < kKs; ++ks) qreg[ks] = *reinterpret_cast<const v8bf*>(qrow + 16 * ks);
-        }
-        publish_slots();
+        const uint16_t* qrow = q + (static_cast<size_t>(row) * H_total + head0 + 32 * hh + (lane & 31)) * kDq +
+                               288 * dh + 8 * (lane >> 5);
         QkState qs;
         qs.m_ref = -INFINITY;
         qs.m_max = -INFINITY;
@@ -446,37 +471,37 @@ void mla_decode32_kernel(const uint16_t* __restrict__ q, const uint8_t* __restri
         auto qk_pass = [&](bool fixed) {
             bool ref_set = fixed;
             qs.l_run = 0.f;
-            start_tiles();
-#pragma unroll
-            for (int ks = 0; ks < kKs; ++ks) asm volatile("" :: "v"(qreg[ks]));
+            if (!fixed) load_q(qrow, wave);
             for (int ti = 0; ti <= n_tiles; ++ti) {
+                if (ti == 0) wait_vmcnt<0>();                         // this wave's queries
                 step_begin(ti);
+                if (ti == 0 && !fixed) {
+                    // this wave's queries, landed with tile 0 (its own loads: no barrier needed)
+                    const uint8_t* qs_lds = q_stage(wave) + 16 * lane;
+#pragma unroll
+                    for (int ks = 0; ks < kKs; ++ks) qreg[ks] = *reinterpret_cast<const v8bf*>(qs_lds + ks * 1024);
+                }
                 const uint32_t tmask = ti < n_tiles ? s_tmask[ti] : 0u;
-                // reference still unset and this tile usable (uniform over the workgroup):
-                // tile 0 takes its maximum through the full exchange, a later tile the
-                // logit of its first usable key
-                const bool want_ref = !ref_set && tmask != 0u;
-                const bool full = want_ref && ti == 0;
+                // reference still unset and this tile usable (uniform over the workgroup)
+                const bool first_max = !ref_set && ti == 0 && tmask != 0u;
+                const bool want_ref = !ref_set && ti > 0 && tmask != 0u;
                 const int ref_key = want_ref ? __builtin_ctz(tmask) : 0;
                 v16f sacc;
                 if (ti < n_tiles) {
                     if (dh == 0) {
                         sacc = qk_half<0>(qreg, tile_buf(ti), lane);
-                        if (full) qk_send_full(sacc, hh, 0, lane);
-                        else qk_send<0>(sacc, hh, lane, want_ref, ref_key);
+                        qk_send<0>(sacc, hh, lane, want_ref, ref_key);
                     } else {
                         sacc = qk_half<1>(qreg, tile_buf(ti), lane);
-                        if (full) qk_send_full(sacc, hh, 1, lane);
-                        else qk_send<1>(sacc, hh, lane, want_ref, ref_key);
+                        qk_send<1>(sacc, hh, lane, want_ref, ref_key);
                     }
                 }
                 lds_barrier();                                        // B(ti)
                 if (ti < n_tiles) {
-                    if (full) qs.m_ref = qk_full_max(sacc, hh, dh, lane, tmask, scale_log2);
-                    if (dh == 0) qk_finish<0>(sacc, qs, hh, lane, tmask, want_ref && !full, scale_log2, fixed, full);
-                    else qk_finish<1>(sacc, qs, hh, lane, tmask, want_ref && !full, scale_log2, fixed, full);
+                    if (dh == 0) qk_finish<0>(sacc, qs, hh, lane, tmask, first_max, want_ref, scale_log2, fixed);
+                    else qk_finish<1>(sacc, qs, hh, lane, tmask, first_max, want_ref, scale_log2, fixed);
                 }
-                ref_set = ref_set || want_ref;
+                ref_set = ref_set || first_max || want_ref;
             }
         };
         qk_pass(false);
@@ -501,10 +526,9 @@ void mla_decode32_kernel(const uint16_t* __restrict__ q, const uint8_t* __restri
         }
         __syncthreads();          // every wave is past its last PV: the tile ring is free
     } else {
-        publish_slots();
         PvState pv;
         const int c = wave - 4;
-        auto pv_pass = [&]() {
+        auto pv_pass = [&](bool fixed) {
             const VAddr va = v_addr(c, lane);
 #pragma unroll
             for (int h2 = 0; h2 < 2; ++h2)
@@ -512,28 +536,33 @@ void mla_decode32_kernel(const uint16_t* __restrict__ q, const uint8_t* __restri
                 for (int ct = 0; ct < 4; ++ct)
 #pragma unroll
                     for (int i = 0; i < 16; ++i) pv.acc[h2][ct][i] = 0.f;
-            start_tiles();
+            const GatherLane gl = gather_lane(c, lane);
+            if (n_tiles > 0) gather_tile(lat_b, 0, c, gl);
+            if (n_tiles > 1) gather_tile(lat_b, 1, c, gl);
+            v8bf vop[2][4];                                           // V operands of the previous tile
             for (int ti = 0; ti <= n_tiles; ++ti) {
                 step_begin(ti);
-                v8bf pop[2][2];                                       // P(ti - 1) operands [kk][hh]
                 if (ti > 0) {
+                    v8bf pop[2][2];                                   // P(ti - 1) operands [kk][hh]
 #pragma unroll
                     for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
                         for (int h2 = 0; h2 < 2; ++h2)
                             pop[kk][h2] = *reinterpret_cast<const v8bf*>(&s_p[h2][kk][lane][0]);
-                    pv_step(pv, tile_buf(ti - 1), va, 0, pop[0]);
+                    pv_tile(pv, vop, pop);
                 }
+                if (ti < n_tiles) load_v(vop, tile_buf(ti), va);
                 lds_barrier();                                        // B(ti)
-                if (ti > 0) pv_step(pv, tile_buf(ti - 1), va, 1, pop[1]);
+                step_gathers(ti, gl);
+                if (!fixed && ti == 0 && tile0_usable) lds_barrier();  // C
             }
         };
-        pv_pass();
+        pv_pass(false);
         redo_flags(false);
         __syncthreads();
         if (any_redo()) {
             __syncthreads();
-            pv_pass();
+            pv_pass(true);
         }
         __syncthreads();          // the sums are published; the tile ring is free
         // normalised bf16 rows staged in LDS as [64 heads][512] with the 16-byte chunk

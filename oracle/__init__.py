@@ -72,6 +72,8 @@ def _load():
                                          P, P, P, P, P, P, P]
         lib.orc_indexer_prep.restype = I
         lib.orc_max_threads.argtypes = []
+        lib.orc_set_threads.argtypes = [I]
+        lib.orc_set_threads.restype = None
         for fn in (lib.orc_index_scores, lib.orc_topk, lib.orc_sparse_mla_decode,
                    lib.orc_sparse_mha_prefill, lib.orc_sparse_mha_prefill_dense,
                    lib.orc_sparse_mha_prefill_rows,
@@ -107,6 +109,11 @@ def _check(rc, what):
 
 def max_threads() -> int:
     return _load().orc_max_threads()
+
+
+def set_threads(n: int) -> None:
+    """Threads of the oracle's following parallel loops."""
+    _load().orc_set_threads(int(n))
 
 
 def e4m3fn_value(code: int) -> float:

@@ -596,3 +596,14 @@ int orc_max_threads(void)
     return 1;
 #endif
 }
+
+/* Threads of the following parallel loops (n >= 1); for timing the oracle on one core. */
+void orc_set_threads(int n)
+{
+#ifdef _OPENMP
+    extern void omp_set_num_threads(int);
+    omp_set_num_threads(n < 1 ? 1 : n);
+#else
+    (void)n;
+#endif
+}

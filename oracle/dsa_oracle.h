@@ -72,5 +72,6 @@ int orc_layer_step_mha(const uint8_t* q_i, const float* q_scale, const float* w,
                        double* lse, float* scores_out, int32_t* idx_out);
 
 int orc_max_threads(void);
+void orc_set_threads(int n);
 
 #endif

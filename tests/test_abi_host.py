@@ -77,10 +77,8 @@ def test_attention_validation_and_workspace(lib):
     st = lib.dsa_sparse_mla_decode(p, p, p, p, 2, 1, 128, 512, 64, 4096, 2048, 0.1, 7, p, None,
                                    None, 0, None)
     assert st == 3
-    # rows that fill the GPU keep each row in one workgroup per head half (no partials)
-    # while a split holds at most 512 slots
-    assert lib.dsa_sparse_mla_decode_workspace_bytes(256, 1, 128, 512, 64, 512, N.DSA_BF16) == 0
-    assert lib.dsa_sparse_mla_decode_workspace_bytes(256, 1, 128, 512, 64, 1024, N.DSA_BF16) > 0
+    # rows that fill the GPU keep each row in one workgroup (no partials)
+    assert lib.dsa_sparse_mla_decode_workspace_bytes(256, 1, 128, 512, 64, 1024, N.DSA_BF16) == 0
     # beyond 16 splits of 1024 slots the latent shape leaves the matrix-core path: the
     # generic path needs no workspace but must hold all k logits in LDS
     assert lib.dsa_sparse_mla_decode_workspace_bytes(2, 1, 128, 512, 64, 16384, N.DSA_BF16) > 0

@@ -88,7 +88,7 @@ def _variant(orc, path):
                "orc_indexer_prep", "orc_index_scores", "orc_topk",
                "orc_sparse_mla_decode", "orc_sparse_mha_prefill", "orc_sparse_mha_prefill_dense",
                "orc_sparse_mha_prefill_rows",
-               "orc_layer_step_latent", "orc_layer_step_mha", "orc_max_threads"):
+               "orc_layer_step_latent", "orc_layer_step_mha", "orc_max_threads", "orc_set_threads"):
         getattr(lib, fn).argtypes = getattr(saved, fn).argtypes
         getattr(lib, fn).restype = getattr(saved, fn).restype
     orc._lib = lib
