@@ -383,7 +383,8 @@ def measure(D, S, cfg, steps: int, warmup: int, sets: int, latent: str, graph: b
                          "achieved_TFLOPs": round(idx_tfs, 1),
                          "mfma_frac_of_bf16_peak": round(idx_tfs / BF16_PEAK_TFLOPS, 4),
                          "mfma_frac_of_fp8_peak": round(idx_tfs / FP8_PEAK_TFLOPS, 4),
-                         "keys_per_s": round(costs["keys"] / (idx_launch_ms * 1e-3), 1)},
+                         "keys_per_s": round(costs["keys"] / (idx_launch_ms * 1e-3), 1),
+                         "traffic": read_traffic("index_scores", workload, INDEX_SOURCE)},
         "roofline": roofline,
     }
     if with_prep:

@@ -100,6 +100,42 @@ def test_fullsize_prefill(dsa, orc):
     check_attention(out_np[0, rows], lse_np[0, rows], ro, rl, "bf16")
 
 
+def test_fullsize_prefill_latent(dsa, orc):
+    """The latent form of the chunked prefill (T=8192 rows of one sequence, top-2048, 128
+    heads over 512 + 64 latent rows): the step runs whole on the GPU; sampled rows are
+    checked against the oracle, each as a one-row query whose length ends at its own
+    position, so the oracle sees exactly that row's causal keys."""
+    cfg = S.CONFIGS["prefill_chunk_latent"]
+    _say("[fullsize] prefill_chunk_latent: generating inputs")
+    c = S.make_case(cfg)
+    d = S.to_device(c, "cuda")
+    step = dsa.LayerStep(d["q_i"], d["q_scale"], d["w"], d["k_i"], d["k_scale"], d["lens"],
+                         cfg.sm_scale_i, cfg.k, d["q"], cfg.sm_scale, latent=d["latent"],
+                         Dv=cfg.Dv, want_idx=True, want_scores=True)
+    _say("[fullsize] prefill_chunk_latent: layer step on the GPU")
+    out, lse = step()
+    torch.cuda.synchronize()
+    T = cfg.T
+    assert int(c["lens"][0]) == T
+    rows = [0, 1, 2046, 2047, 2048, 4097, 6000, T - 1]
+    lens_full = np.array([T], np.int32)
+    gidx_all = step.idx.cpu().numpy()
+    out_np, lse_np = _np(out), lse.cpu().numpy()
+    for t in rows:
+        _say(f"[fullsize] prefill_chunk_latent: oracle on row {t}")
+        one = np.array([t + 1], np.int32)
+        rsc = orc.index_scores(c["q_i"][:, t:t + 1], c["q_scale"][:, t:t + 1], c["w"][:, t:t + 1],
+                               c["k_i"], c["k_scale"], one, cfg.sm_scale_i)
+        check_scores(step.scores[0, t:t + 1].cpu().numpy(), rsc[0], lens_full, T, rows=[(0, t)])
+        ridx = orc.topk(rsc, one, cfg.k)
+        gidx = gidx_all[:, t:t + 1]
+        check_topk(gidx[0], rsc[0], ridx[0], lens_full, T, cfg.k, rows=[(0, t)])
+        ro, rl = orc.sparse_mla_decode(c["q"][:, t:t + 1], c["latent"], gidx, one, cfg.Dv,
+                                       cfg.sm_scale)
+        check_attention(out_np[:, t:t + 1], lse_np[:, t:t + 1], ro, rl, cfg.attn_dtype)
+    _say("[fullsize] prefill_chunk_latent: done")
+
+
 @pytest.mark.parametrize("name", ["decode_v32", "prefill_chunk"])
 def test_fullsize_indexer_prep(dsa, orc, name):
     """The indexer preparation of every new token of the workload (32 decode tokens, or
