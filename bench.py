@@ -1,12 +1,16 @@
 """Benchmark of one DSA layer step on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config decode_v32] [--latent fp8]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config decode_v32] [--latent fp8] [--graph]
 
 A step is one call of dsa_layer_step over the whole batch: index scores over every
 cached key of every sequence, top-k, sparse attention over the selected latent rows.
 Inputs are seeded synthetic tensors of the configuration's shapes, resident in HBM
 before the timed region; several independent input sets are cycled so that the
 256 MB Infinity Cache cannot serve a step from the previous one.
+
+The timed steps are eager calls of dsa_layer_step (the library enqueueing each kernel);
+the same steps replayed from one HIP graph per input set are timed as well and reported
+as graph_ms_per_step (``--graph`` makes them the headline).
 
 Prints one JSON line: layer-steps/s (value) of the headline workload (decode_v32 by
 default), keys scored/s, the roofline of the dominant kernel (the sparse attention)
@@ -261,31 +265,36 @@ def measure(D, S, cfg, steps: int, warmup: int, sets: int, latent: str, graph: b
     print(f"[bench] {cfg.name}: {sets} input sets on the GPU in "
           f"{time.perf_counter() - t_gen:.1f} s", file=sys.stderr, flush=True)
 
-    run = list(step_objs)
-    if graph:
-        graphs = []
-        side = torch.cuda.Stream()
-        side.wait_stream(torch.cuda.current_stream())
-        with torch.cuda.stream(side):
-            for s_ in step_objs:
-                s_()                                  # warm the launch path before capture
-        torch.cuda.current_stream().wait_stream(side)
+    def timed(run_list):
+        for i in range(warmup):
+            run_list[i % len(run_list)]()
         torch.cuda.synchronize()
-        for s_ in step_objs:
-            g = torch.cuda.CUDAGraph()
-            with torch.cuda.graph(g):
-                s_()
-            graphs.append(g)
-        run = [g.replay for g in graphs]
+        t0 = time.perf_counter()
+        for i in range(steps):
+            run_list[i % len(run_list)]()
+        torch.cuda.synchronize()
+        return time.perf_counter() - t0
 
-    for i in range(warmup):
-        run[i % len(run)]()
+    # eager launches (one C call per step, the library enqueueing each kernel) and the same
+    # steps replayed from one HIP graph per input set (the launch sequence captured once)
+    eager = list(step_objs)
+    dt_eager = timed(eager)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        for s_ in step_objs:
+            s_()                                      # warm the launch path before capture
+    torch.cuda.current_stream().wait_stream(side)
     torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(steps):
-        run[i % len(run)]()
-    torch.cuda.synchronize()
-    dt = time.perf_counter() - t0
+    graphs = []
+    for s_ in step_objs:
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            s_()
+        graphs.append(g)
+    replay = [g.replay for g in graphs]
+    dt_graph = timed(replay)
+    run, dt = (replay, dt_graph) if graph else (eager, dt_eager)
     ms_per_step = 1e3 * dt / steps
     value = steps / dt
 
@@ -362,6 +371,8 @@ def measure(D, S, cfg, steps: int, warmup: int, sets: int, latent: str, graph: b
         "steps": steps,
         "warmup": warmup,
         "ms_per_step": round(ms_per_step, 5),
+        "eager_ms_per_step": round(1e3 * dt_eager / steps, 5),
+        "graph_ms_per_step": round(1e3 * dt_graph / steps, 5),
         "dtype": cfg.attn_dtype,
         "config": {"workload": f"{cfg.name}: B={cfg.B}, context {cfg.Lmax} per sequence"
                                f"{' (' + cfg.lens + ')' if cfg.lens != 'full' else ''}, T={cfg.T}, "
@@ -408,7 +419,9 @@ def main():
     ap.add_argument("--latent", choices=["bf16", "fp8"], default="bf16",
                     help="latent cache rows: bf16 (1152 B) or the FP8 storage form (656 B: "
                          "512 e4m3fn codes, four fp32 block scales, 64 bf16 rope values)")
-    ap.add_argument("--graph", action="store_true", help="replay each step from a HIP graph")
+    ap.add_argument("--graph", action="store_true",
+                    help="headline from the steps replayed from HIP graphs (default: eager calls; "
+                         "both are measured and reported)")
     ap.add_argument("--cpu-seqs", type=int, default=32,
                     help="sequences (decode) or rows / 4 (prefill) in the CPU-oracle sample")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
@@ -475,7 +488,8 @@ def main():
             lat = args.latent if ocfg.form == "latent" and ocfg.attn_dtype == "bf16" else "bf16"
             steps = min(args.steps, 50) if ocfg.T == 1 else min(args.steps, 10)
             warm = min(args.warmup, 5)
-            others[name] = measure(D, S, ocfg, steps, warm, DEFAULT_SETS.get(name, 2), lat, with_prep=False)
+            others[name] = measure(D, S, ocfg, steps, warm, DEFAULT_SETS.get(name, 2), lat,
+                                   graph=args.graph, with_prep=False)
         result["other_workloads"] = others
     print(json.dumps(result))
 

@@ -7,49 +7,48 @@
 // ("DeepSeek-V3.2-Exp - Causal mask", Multi-head latent attention).
 //
 // One workgroup (8 waves, two per SIMD) owns one query row (b,t), 64 of its heads and one
-// split of its selected slots, as the 16x16 kernel of sparse_attn.hip, with the roles
-// of its waves changed so that both products run on the 32x32x16 form (twice the work of
-// 16x16x32 per instruction at about the same issue time):
+// split of its selected slots.  The roles of its waves are split so that both products run
+// on the 32x32x16 form:
 //   QK waves 0..3   wave w computes S = K . Q^T for head half hh = w & 1 (32 heads) over
 //                   the column half dh = w >> 1 (288 of the 576 columns, 18 K-steps): its
 //                   queries stay in registers (72 VGPRs).  The two column halves of a
 //                   head half are summed through LDS: each wave sends the partner the
 //                   16 keys the partner finishes (8 values per lane) and keeps its own;
-//                   it then forms the softmax numerators of its 16 keys and publishes
-//                   them in the P operand layout.  No wave holds output accumulators.
+//                   it forms the softmax numerators of its 16 keys one step later and
+//                   publishes them in the P operand layout.  No wave holds output
+//                   accumulators.
 //   PV waves 4..7   wave 4 + c owns output columns 128 c .. 128 c + 127 of all 64 heads
 //                   and accumulates O^T = V^T . P^T (output columns as MFMA rows, heads as
 //                   MFMA columns: every lane ends with one head and runs of four adjacent
 //                   columns, which go to LDS as 8-byte stores), V read by transpose reads
 //                   straight from the gathered tile.
-// Per tile of 32 selected rows the four waves of a SIMD issue 34 matrix-core instructions
-// (18 QK + 16 PV) against 68 of the 16x16x32 form.
+// Per tile of 32 selected rows the two waves of a SIMD issue 34 matrix-core instructions
+// (18 QK + 16 PV).
 //
-// Pipeline.  A tile's buffer is released in its own step -- the QK waves read K in phase
-// 1 and the PV waves copy their V operands into registers in the same phase -- so while
-// tile i is in use, tiles i+1 and i+2 are in flight and tile i+3 goes out after step i's
-// second barrier.  (A further tile in flight, which the ring would allow, measured no
-// faster per step and slower overall.)  The PV waves issue all gathers, in phase 2, while
-// the QK waves form the softmax numerators; issued between their PV instructions instead,
-// the loads held back the matrix-core issue and the PV phase grew from 0.5 to 1.25 us.  The queries reach the QK waves through LDS (direct loads
-// into buffers 2 and 3 before those tiles are issued), so the compiler's own waits for
-// register loads never drain the gathers.
-// Step i (two workgroup barriers):
-//   A(i)     tile i has landed for every wave; P(i-1) is published.
-//   phase 1  QK waves: QK(i), then the partner's half of S(i) to LDS.
-//            PV waves: P(i-1) operands from LDS, PV(i-1) from the V operands held in
-//            registers since step i-1, then the V operands of tile i into registers.
-//   B(i)     tile i's buffer is free.
-//   phase 2  QK waves: add the partner's half, softmax numerators, publish P(i).
-//            PV waves: issue tile i+3 (at step 0: tiles 2 and 3).
+// Pipeline: step i (two workgroup barriers) --
+//   A(i)     tile i has landed for every wave.
+//   phase 1  QK waves: QK(i), with the numerators of tile i-1 formed between its matrix-
+//            core instructions and published as P(i-1); the partner's half of S(i) out.
+//            PV waves: their share of the gathers of tile i+3, into tile i-1's buffer.
+//   B(i)     P(i-1) and the halves of S(i) are published.
+//   phase 2  QK waves: S(i) completed (the partner's half added); their share of the
+//            gathers of tile i+3.
+//            PV waves: PV(i-1) from P(i-1) and the V operands of tile i-1 held in
+//            registers, then the V operands of tile i into the same registers.
+// The softmax runs one tile behind QK so that its VALU work fills the matrix cores'
+// issue gaps instead of a phase of its own, and the gathers of a tile are split between
+// the two roles (5 and 4 of the 9 wave-wide loads per wave position) so that each role
+// issues them while the other role's matrix-core chain runs.  Four buffers: tile i+3 goes
+// into the buffer of tile i-1 while tiles i+1 and i+2 are in flight.  Step n_tiles forms
+// the last tile's numerators and runs its PV.  The queries reach the QK waves through LDS
+// (direct loads into buffers 2 and 3, read at step 0 before tiles 2 and 3 go out after
+// B(0)), so the compiler's own waits for register loads never drain the gathers.
 // Softmax without a running rescale: each head's numerators are exp2(logit - m_ref), where
-// m_ref is the largest logit of the split's first tile, so the tile's dominant key gets the
-// numerator 1 exactly: at step 0 both waves of a head half post the maximum of their 16
-// keys and read the partner's after one extra barrier.  A split whose first tile holds no
-// usable slot takes instead the logit of the first usable key of its first usable tile
-// (both column halves of that key's logit travel with S).  A key with a logit more than
-// 2^64 above the reference (log2 units) marks the split, which is then recomputed with the
-// split's maximum as reference; the normalised result is the same softmax.
+// m_ref is the largest logit of the split's first tile with a usable slot (posted by both
+// column-half waves in phase 2 of that tile's step, read in the next step), so that tile's
+// dominant key gets the numerator 1 exactly.  A key with a logit more than 2^64 above the
+// reference (log2 units) marks the split, which is then recomputed with the split's
+// maximum as reference; the normalised result is the same softmax.
 #include "dsa_device.h"
 #include "dsa_internal.h"
 
@@ -67,8 +66,10 @@ constexpr int kRowChunks = kRowBytes / 16;          // 72
 constexpr int kKt = 32;                             // selected rows per tile
 constexpr int kTileBytes = kKt * kRowBytes;         // 36864
 constexpr int kTileLoads = kTileBytes / (kWave * 16);   // 36 wave-wide 1 KB loads
-constexpr int kGatherWaves = 4;                    // the PV waves issue every tile's loads
-constexpr int kGatherLoads = kTileLoads / kGatherWaves;          // 9 per wave and tile
+constexpr int kGatherWaves = 4;                    // wave positions sharing a tile's loads
+constexpr int kGatherLoads = kTileLoads / kGatherWaves;          // 9 per wave position and tile
+constexpr int kPvLoads = 5;                         // of them issued by the PV wave (phase 1)
+constexpr int kQkLoads = kGatherLoads - kPvLoads;   // and by the QK wave (phase 2)
 constexpr int kBufs = 4;                            // tile ring
 constexpr int kMaxTiles = 16;                       // tiles per split
 constexpr int kMaxSlots = kMaxTiles * kKt;          // 512 slots per split
@@ -88,6 +89,8 @@ __shared__ float s_l[2][2][32];                     // [hh][dh][head] numerator 
 __shared__ float s_m[2][2][32];                     // [hh][dh][head] reference / split maximum
 __shared__ int32_t s_redo[kWaves];
 
+template <int N> struct IntConst { static constexpr int value = N; };
+
 __device__ __forceinline__ uint8_t* tile_buf(int ti) { return s_tile + (ti & (kBufs - 1)) * kTileBytes; }
 
 template <int N>
@@ -97,13 +100,28 @@ __device__ __forceinline__ void wait_vmcnt() { asm volatile("s_waitcnt vmcnt(%0)
 // gathers in flight stay in flight across it.
 __device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
-// Wait until this wave's gathers of the current tile have landed, leaving the `later`
-// tiles issued after it (0..3) in flight: a PV wave issues kGatherLoads loads per tile,
-// and loads complete in issue order.
-__device__ __forceinline__ void wait_tile(int later) {
-    if (later >= 3) wait_vmcnt<3 * kGatherLoads>();
-    else if (later == 2) wait_vmcnt<2 * kGatherLoads>();
-    else if (later == 1) wait_vmcnt<kGatherLoads>();
+// Waits for this wave's gathers of the tile used at step t (loads complete in issue
+// order).  The PV waves issue all of tiles 0 and 1 (kGatherLoads each) and kPvLoads of
+// every later tile; the QK waves issue the other kQkLoads of tiles 2 onwards.  Tiles in
+// flight behind tile t: t + 1 and t + 2, except at step 0 (tile 1 only: tiles 2 and 3 go
+// out after B(0)).
+__device__ __forceinline__ void wait_tile_pv(int t, int n_tiles) {
+    if (t >= n_tiles) return;
+    if (t == 0) {
+        if (n_tiles > 1) wait_vmcnt<kGatherLoads>();
+        else wait_vmcnt<0>();
+        return;
+    }
+    const int later = min(2, n_tiles - 1 - t);
+    if (later == 2) wait_vmcnt<2 * kPvLoads>();
+    else if (later == 1) wait_vmcnt<kPvLoads>();
+    else wait_vmcnt<0>();
+}
+__device__ __forceinline__ void wait_tile_qk(int t, int n_tiles) {
+    if (t < 2 || t >= n_tiles) return;
+    const int later = min(2, n_tiles - 1 - t);
+    if (later == 2) wait_vmcnt<2 * kQkLoads>();
+    else if (later == 1) wait_vmcnt<kQkLoads>();
     else wait_vmcnt<0>();
 }
 
@@ -115,40 +133,47 @@ __device__ __forceinline__ void wait_tile(int later) {
 // inside each aligned group of 8 chunks, so the rope chunks 64..71 stay in place.)
 __device__ __forceinline__ int swz(int r) { return (r >> 1) & 7; }
 
-// Direct global->LDS loads of tile `ti`, issued by the PV waves (the QK waves' time between
-// their matrix-core chains goes to the softmax): PV wave c issues the wave-wide 1 KB loads
-// ci = c, c + 4, ... < 36; lane l of load ci fetches 16-byte chunk q = 64 ci + l of the tile,
-// i.e. chunk q % 72 of selected row q / 72, stored at its swizzled position.  Written as
-// inline assembly so that the compiler, which cannot tell the ring's buffers apart, inserts
-// no drain of these loads before later LDS reads; completion is tracked with wait_tile()
-// and published by lds_barrier().  M0 holds the wave-uniform LDS destination; nothing else
-// in this kernel uses M0.  Unused slots fetch row 0 (masked).
+// Direct global->LDS loads of a tile: 36 wave-wide 1 KB loads ci = c + 4 i (wave position
+// c = 0..3, i = 0..8); lane l of load ci fetches 16-byte chunk q = 64 ci + l of the tile,
+// i.e. chunk q % 72 of selected row q / 72, stored at its swizzled position.  PV wave c
+// issues loads i < kPvLoads of position c in phase 1 (all nine for tiles 0 and 1), QK wave
+// w the loads i >= kPvLoads of position w in phase 2, so each role's issue time overlaps
+// the other role's matrix-core work.  Written as inline assembly so that the compiler,
+// which cannot tell the ring's buffers apart, inserts no drain of these loads before later
+// LDS reads; completion is tracked with wait_tile_*() and published by lds_barrier().  M0
+// holds the wave-uniform LDS destination; nothing else in this kernel uses M0.  Unused
+// slots fetch row 0 (masked).
+template <int I0, int N>
 struct GatherLane {
-    int key[kGatherLoads];       // tile row of load i for this lane
-    uint32_t off[kGatherLoads];  // byte offset of the lane's source chunk within that row
+    int key[N];         // tile row of load I0 + i for this lane
+    uint32_t off[N];    // byte offset of the lane's source chunk within that row
 };
-__device__ __forceinline__ GatherLane gather_lane(int c, int lane) {
-    GatherLane gl;
+template <int I0, int N>
+__device__ __forceinline__ GatherLane<I0, N> gather_lane(int c, int lane) {
+    GatherLane<I0, N> gl;
 #pragma unroll
-    for (int i = 0; i < kGatherLoads; ++i) {
-        const int q = (c + kGatherWaves * i) * kWave + lane;
+    for (int i = 0; i < N; ++i) {
+        const int q = (c + kGatherWaves * (I0 + i)) * kWave + lane;
         const int key = q / kRowChunks;
         gl.key[i] = key;
         gl.off[i] = static_cast<uint32_t>(((q - key * kRowChunks) ^ swz(key)) * 16);
     }
     return gl;
 }
-__device__ __forceinline__ void gather_tile(const uint8_t* lat_b, int ti, int c, const GatherLane& gl) {
+// Loads I0 + J0 .. I0 + J0 + M - 1 of position c for tile ti.
+template <int J0, int M, int I0, int N>
+__device__ __forceinline__ void gather_tile(const uint8_t* lat_b, int ti, int c, const GatherLane<I0, N>& gl) {
+    static_assert(J0 + M <= N, "loads outside the lane's part");
     const uint32_t lds_base = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(
         (__attribute__((address_space(3))) uint8_t*)(tile_buf(ti))));
-    int s[kGatherLoads];
+    int s[M];
 #pragma unroll
-    for (int i = 0; i < kGatherLoads; ++i) s[i] = s_keys[ti * kKt + gl.key[i]];
+    for (int i = 0; i < M; ++i) s[i] = s_keys[ti * kKt + gl.key[J0 + i]];
 #pragma unroll
-    for (int i = 0; i < kGatherLoads; ++i) {
-        const int ci = c + kGatherWaves * i;
-        const int row = s[i] < 0 ? 0 : s[i];
-        const uint8_t* src = lat_b + static_cast<size_t>(row) * kRowBytes + gl.off[i];
+    for (int i = 0; i < M; ++i) {
+        const int ci = c + kGatherWaves * (I0 + J0 + i);
+        const int row = max(s[i], 0);
+        const uint8_t* src = lat_b + static_cast<size_t>(row) * kRowBytes + gl.off[J0 + i];
         const uint32_t m0v = __builtin_amdgcn_readfirstlane(lds_base + ci * kWave * 16);
         asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off"
                      :: "s"(m0v), "v"(src) : "memory");
@@ -159,12 +184,27 @@ typedef __bf16 v4bf_t __attribute__((ext_vector_type(4)));
 
 // ---- QK waves
 
-// S partial of one tile over column half DH for 32 heads: lane l supplies key l % 32 of
-// the tile as A operand (columns 288 DH + 16 ks + 8 (l / 32) .. + 7 of its row) and
-// holds the matching query columns of head l % 32 as B operand; element r of the result
-// is S[key 8 (r / 4) + 4 (l / 32) + r % 4][head l % 32].
+struct QkState {
+    float m_ref;     // reference logit of this lane's head (log2 units), -inf until set
+    float m_max;     // largest logit seen
+    float l_run;     // sum of this lane's numerators
+    bool over;       // a logit above m_ref + kRefSpan
+};
+
+// Phase 1 of a QK wave: the S partial of tile ti over column half DH for 32 heads, with the
+// softmax numerators of the tile completed in the previous step formed between its
+// matrix-core instructions and published as the P operand.
+//   S: lane l supplies key l % 32 of the tile as A operand (columns 288 DH + 16 ks +
+//   8 (l / 32) .. + 7 of its row) and holds the matching query columns of head l % 32 as B
+//   operand; element r of the result is S[key 8 (r / 4) + 4 (l / 32) + r % 4][head l % 32].
+//   The operand reads run nine K-steps ahead of the matrix cores (LDS latency), and the
+//   order -- one instruction, the read nine steps ahead, one piece of the softmax -- is
+//   pinned, so no instruction waits for a read issued just before it.
+//   Numerators: exp2(logit - m_ref) as bf16.  Before any usable key every logit is -inf
+//   and the numerators are 0 whatever the reference.
 template <int DH>
-__device__ __forceinline__ v16f qk_half(const v8bf (&qreg)[kKs], const uint8_t* kb, int lane) {
+__device__ __forceinline__ v16f qk_tile(const v8bf (&qreg)[kKs], const uint8_t* kb, int lane,
+                                        const float (&v)[8], float mx, QkState& st, int hh, bool fixed) {
     int lo = lane;
     asm volatile("" : "+v"(lo));
     const int r = lo & 31;
@@ -180,6 +220,8 @@ __device__ __forceinline__ v16f qk_half(const v8bf (&qreg)[kKs], const uint8_t* 
         const int c0 = 36 * DH + 2 * ks;
         return reinterpret_cast<const v8bf*>(row + 128 * (c0 >> 3) + off[(c0 & 7) >> 1]);
     };
+    st.over = st.over || (!fixed && mx > st.m_ref + kRefSpan);
+    const float mref = st.m_ref == -INFINITY ? 0.f : st.m_ref;
     v16f acc;
 #pragma unroll
     for (int i = 0; i < 16; ++i) acc[i] = 0.f;
@@ -187,25 +229,31 @@ __device__ __forceinline__ v16f qk_half(const v8bf (&qreg)[kKs], const uint8_t* 
     v8bf a[kPre];
 #pragma unroll
     for (int ks = 0; ks < kPre; ++ks) a[ks] = *addr(ks);
+    __builtin_amdgcn_sched_barrier(0);
+    float p[8];
+    float psum = 0.f;
 #pragma unroll
     for (int ks = 0; ks < kKs; ++ks) {
         acc = mfma_bf16_32x32x16(a[ks % kPre], qreg[ks], acc);
         if (ks + kPre < kKs) a[ks % kPre] = *addr(ks + kPre);
+        if (ks < 8) {
+            p[ks] = exp2_num(v[ks] - mref);
+            psum += p[ks];
+        } else if (ks == 8) {
+            v8s pk;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) pk[e] = static_cast<short>(f32_to_bf16(p[e]));
+            *reinterpret_cast<v8s*>(&s_p[hh][DH][lane][0]) = pk;
+        }
+        __builtin_amdgcn_sched_barrier(0);
     }
+    st.l_run += psum;
     return acc;
 }
 
-struct QkState {
-    float m_ref;     // reference logit of this lane's head (log2 units), -inf until set
-    float m_max;     // largest logit seen
-    float l_run;     // sum of this lane's numerators
-    bool over;       // a logit above m_ref + kRefSpan
-};
-
-// Phase-1 tail: the partner's half of S (its 16 keys) and, while no reference is set, the
-// partial logit of the first usable key of the tile (for every head of the half).
+// Phase-1 tail: the partner's half of S (its 16 keys) to LDS.
 template <int DH>
-__device__ __forceinline__ void qk_send(const v16f& acc, int hh, int lane, bool want_ref, int ref_key) {
+__device__ __forceinline__ void qk_send(const v16f& acc, int hh, int lane) {
     constexpr int kOther = 1 - DH;
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
@@ -216,66 +264,38 @@ __device__ __forceinline__ void qk_send(const v16f& acc, int hh, int lane, bool 
         v.w = acc[8 * kOther + 4 * j + 3];
         *reinterpret_cast<float4*>(&s_half[hh][kOther][j][lane][0]) = v;
     }
-    if (want_ref) {
-        // key ref_key is element r = 4 (key / 8) + key % 4 of the lanes with l / 32 = (key / 4) & 1
-        const int rk = 4 * (ref_key >> 3) + (ref_key & 3);
-        float v = acc[0];
-#pragma unroll
-        for (int i = 1; i < 16; ++i) v = (i == rk) ? acc[i] : v;
-        if ((lane >> 5) == ((ref_key >> 2) & 1)) s_ref[hh][DH][lane & 31] = v;
-    }
 }
 
-// Phase 2: this wave's 16 keys of S complete, softmax numerators, P published.  The lane
-// holds keys 16 DH + 8 (s / 4) + 4 (l / 32) + s % 4, s = 0..7, of head l % 32 -- exactly
-// K-slot s of the P operand for K-step DH of the PV product.
-//   first_max  (step 0, tile 0 usable) the reference is the tile's largest logit: each
-//              wave posts the maximum of its 16 keys, and after one extra barrier (which
-//              the PV waves pass as well) takes the larger of the two;
-//   want_ref   (a later first usable tile) the reference is the logit of the tile's first
-//              usable key, the sum of the two halves' partials.
+// Phase 2: this wave's 16 keys of S complete (the partner's half added), in log2 units,
+// -inf at unusable slots; returns the lane's maximum.  The lane holds keys
+// 16 DH + 8 (s / 4) + 4 (l / 32) + s % 4, s = 0..7, of head l % 32 -- exactly K-slot s of
+// the P operand for K-step DH of the PV product.
 template <int DH>
-__device__ __forceinline__ void qk_finish(v16f& acc, QkState& st, int hh, int lane, uint32_t tmask,
-                                          bool first_max, bool want_ref, float scale_log2, bool fixed) {
+__device__ __forceinline__ float qk_complete(const v16f& acc, int hh, int lane, uint32_t tmask,
+                                             float scale_log2, float (&v)[8]) {
+    const int g = lane >> 5;
+    float mx = -INFINITY;
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
-        const float4 v = *reinterpret_cast<const float4*>(&s_half[hh][DH][j][lane][0]);
-        acc[8 * DH + 4 * j + 0] += v.x;
-        acc[8 * DH + 4 * j + 1] += v.y;
-        acc[8 * DH + 4 * j + 2] += v.z;
-        acc[8 * DH + 4 * j + 3] += v.w;
-    }
-    const int g = lane >> 5;
-    float v[8];
-    float mx = -INFINITY;
-    if (tmask == 0xffffffffu) {                           // every slot usable (uniform)
+        const float4 h = *reinterpret_cast<const float4*>(&s_half[hh][DH][j][lane][0]);
+        const float hv[4] = {h.x, h.y, h.z, h.w};
 #pragma unroll
-        for (int s = 0; s < 8; ++s) {
-            v[s] = acc[8 * DH + s] * scale_log2;
-            mx = fmaxf(mx, v[s]);
-        }
-    } else {
-#pragma unroll
-        for (int s = 0; s < 8; ++s) {
-            const int key = 16 * DH + 8 * (s >> 2) + 4 * g + (s & 3);
+        for (int e = 0; e < 4; ++e) {
+            const int s = 4 * j + e;
+            const int key = 16 * DH + 8 * j + 4 * g + e;
             const bool ok = (tmask >> key) & 1u;
-            v[s] = ok ? acc[8 * DH + s] * scale_log2 : -INFINITY;
+            v[s] = ok ? (acc[8 * DH + s] + hv[e]) * scale_log2 : -INFINITY;
             mx = fmaxf(mx, v[s]);
         }
     }
-    if (first_max) {
-        const float m2 = max_xor32(mx);
-        if (lane < 32) s_ref[hh][DH][lane] = m2;
-        lds_barrier();                                     // C: the extra step-0 barrier
-        st.m_ref = fmaxf(s_ref[hh][0][lane & 31], s_ref[hh][1][lane & 31]);
-    } else if (want_ref) {
-        st.m_ref = (s_ref[hh][0][lane & 31] + s_ref[hh][1][lane & 31]) * scale_log2;
-    }
-    if (!fixed) {
-        st.m_max = fmaxf(st.m_max, mx);
-        st.over = st.over || mx > st.m_ref + kRefSpan;
-    }
-    // no usable key seen yet: every logit so far is -inf, any finite reference gives 0
+    return mx;
+}
+
+// The numerators alone (the step after the last tile).
+template <int DH>
+__device__ __forceinline__ void qk_numerators(const float (&v)[8], float mx, QkState& st, int hh,
+                                              int lane, bool fixed) {
+    st.over = st.over || (!fixed && mx > st.m_ref + kRefSpan);
     const float mref = st.m_ref == -INFINITY ? 0.f : st.m_ref;
     float psum = 0.f;
     v8s pk;
@@ -436,75 +456,78 @@ void mla_decode32_kernel(const uint16_t* __restrict__ q, const uint8_t* __restri
         for (int w = 0; w < kWaves; ++w) redo |= s_redo[w];
         return redo != 0;
     };
-    // Tiles in flight while tile ti is used: ti + 1 and ti + 2 (at step 0 only tile 1: tiles
-    // 2 and 3 follow the queries through buffers 2 and 3 and go out after barrier B(0)).
-    auto later_tiles = [&](int ti) { return ti == 0 ? min(1, n_tiles - 1) : min(2, n_tiles - 1 - ti); };
-    // A(ti): the PV waves wait for their loads of tile ti (the QK waves load no tiles)
-    auto step_begin = [&](int ti) {
-        if (!qk_wave && ti < n_tiles) wait_tile(later_tiles(ti));
-        lds_barrier();
-    };
-    auto step_gathers = [&](int ti, const GatherLane& gl) {   // PV waves, after B(ti): tile ti's buffer is free
-        if (ti == 0) {
-            for (int tj = 2; tj <= 3; ++tj)
-                if (tj < n_tiles) gather_tile(lat_b, tj, wave - 4, gl);
-        } else if (ti + 3 < n_tiles) {
-            gather_tile(lat_b, ti + 3, wave - 4, gl);
-        }
-    };
-    const bool tile0_usable = n_tiles > 0 && s_tmask[0] != 0u;
+    // The softmax reference comes from the first tile with a usable slot (uniform).
+    int ref_tile = -1;
+    for (int i = n_tiles - 1; i >= 0; --i)
+        if (s_tmask[i] != 0u) ref_tile = i;
 
     // The two roles run separate code with the same barrier sequence (the slot barrier,
-    // A and B per step for n_tiles + 1 steps plus C at step 0 of a first pass with a usable
-    // first tile, the recompute decision, an optional second pass, the staging barrier),
-    // so their registers -- queries and S for the QK waves, output accumulators and V
-    // operands for the PV waves -- are never live at the same time.  The PV waves issue and
-    // wait for every tile's gathers; the QK waves see the tiles through barrier A.
+    // A and B per step for n_tiles + 1 steps, the recompute decision, an optional second
+    // pass, the staging barrier), so their registers -- queries and S for the QK waves,
+    // output accumulators and V operands for the PV waves -- are never live at the same
+    // time.  The PV waves issue and wait for every tile's gathers; the QK waves see the
+    // tiles through barrier A.
     if (qk_wave) {
         v8bf qreg[kKs];
         const uint16_t* qrow = q + (static_cast<size_t>(row) * H_total + head0 + 32 * hh + (lane & 31)) * kDq +
                                288 * dh + 8 * (lane >> 5);
+        const GatherLane<kPvLoads, kQkLoads> glq = gather_lane<kPvLoads, kQkLoads>(wave, lane);
         QkState qs;
         qs.m_ref = -INFINITY;
         qs.m_max = -INFINITY;
         qs.over = false;
-        auto qk_pass = [&](bool fixed) {
-            bool ref_set = fixed;
+        // Step ti: A(ti); QK(ti) with the numerators of tile ti-1 formed between its
+        // matrix-core instructions, the partner's half of S(ti) out; B(ti); S(ti) completed.
+        // Step n_tiles forms the last tile's numerators only.
+        auto qk_pass = [&](auto dhc, bool fixed) {
+            constexpr int DH = decltype(dhc)::value;
+            bool ref_known = fixed;
             qs.l_run = 0.f;
             if (!fixed) load_q(qrow, wave);
+            float v[8];                                               // S of the completed tile
+#pragma unroll
+            for (int s = 0; s < 8; ++s) v[s] = -INFINITY;
+            float vmx = -INFINITY;
             for (int ti = 0; ti <= n_tiles; ++ti) {
                 if (ti == 0) wait_vmcnt<0>();                         // this wave's queries
-                step_begin(ti);
+                else wait_tile_qk(ti, n_tiles);
+                lds_barrier();                                        // A(ti)
                 if (ti == 0 && !fixed) {
-                    // this wave's queries, landed with tile 0 (its own loads: no barrier needed)
+                    // this wave's queries, landed by its own loads (no barrier needed)
                     const uint8_t* qs_lds = q_stage(wave) + 16 * lane;
 #pragma unroll
                     for (int ks = 0; ks < kKs; ++ks) qreg[ks] = *reinterpret_cast<const v8bf*>(qs_lds + ks * 1024);
                 }
-                const uint32_t tmask = ti < n_tiles ? s_tmask[ti] : 0u;
-                // reference still unset and this tile usable (uniform over the workgroup)
-                const bool first_max = !ref_set && ti == 0 && tmask != 0u;
-                const bool want_ref = !ref_set && ti > 0 && tmask != 0u;
-                const int ref_key = want_ref ? __builtin_ctz(tmask) : 0;
-                v16f sacc;
+                if (!ref_known && ref_tile >= 0 && ti == ref_tile + 1) {
+                    qs.m_ref = fmaxf(s_ref[hh][0][lane & 31], s_ref[hh][1][lane & 31]);
+                    ref_known = true;
+                }
                 if (ti < n_tiles) {
-                    if (dh == 0) {
-                        sacc = qk_half<0>(qreg, tile_buf(ti), lane);
-                        qk_send<0>(sacc, hh, lane, want_ref, ref_key);
-                    } else {
-                        sacc = qk_half<1>(qreg, tile_buf(ti), lane);
-                        qk_send<1>(sacc, hh, lane, want_ref, ref_key);
+                    const v16f sacc = qk_tile<DH>(qreg, tile_buf(ti), lane, v, vmx, qs, hh, fixed);
+                    qk_send<DH>(sacc, hh, lane);
+                    lds_barrier();                                    // B(ti)
+                    vmx = qk_complete<DH>(sacc, hh, lane, s_tmask[ti], scale_log2, v);
+                    qs.m_max = fmaxf(qs.m_max, vmx);
+                    if (!ref_known && ti == ref_tile) {
+                        // the reference: the largest logit of this tile, over both halves
+                        const float m2 = max_xor32(vmx);
+                        if (lane < 32) s_ref[hh][DH][lane] = m2;
                     }
+                    // this wave's share of a later tile, into a buffer released at A(ti)
+                    if (ti == 0) {
+                        for (int tj = 2; tj <= 3; ++tj)
+                            if (tj < n_tiles) gather_tile<0, kQkLoads>(lat_b, tj, wave, glq);
+                    } else if (ti + 3 < n_tiles) {
+                        gather_tile<0, kQkLoads>(lat_b, ti + 3, wave, glq);
+                    }
+                } else {
+                    qk_numerators<DH>(v, vmx, qs, hh, lane, fixed);
+                    lds_barrier();                                    // B(ti)
                 }
-                lds_barrier();                                        // B(ti)
-                if (ti < n_tiles) {
-                    if (dh == 0) qk_finish<0>(sacc, qs, hh, lane, tmask, first_max, want_ref, scale_log2, fixed);
-                    else qk_finish<1>(sacc, qs, hh, lane, tmask, first_max, want_ref, scale_log2, fixed);
-                }
-                ref_set = ref_set || first_max || want_ref;
             }
         };
-        qk_pass(false);
+        if (dh == 0) qk_pass(IntConst<0>{}, false);
+        else qk_pass(IntConst<1>{}, false);
         // a head past its reference span: redo the split with the split's maximum as the
         // reference (a uniform decision: every wave reads the same flags)
         redo_flags(qs.over);
@@ -516,7 +539,8 @@ void mla_decode32_kernel(const uint16_t* __restrict__ q, const uint8_t* __restri
         if (any_redo()) {
             qs.m_ref = fmaxf(s_m[hh][0][lane & 31], s_m[hh][1][lane & 31]);
             __syncthreads();      // every wave has read the flags and maxima
-            qk_pass(true);
+            if (dh == 0) qk_pass(IntConst<0>{}, true);
+            else qk_pass(IntConst<1>{}, true);
         }
         // numerator sums and references per head for the normalisation and the lse
         const float l = qs.l_run + from_xor32(qs.l_run, lane);
@@ -528,6 +552,9 @@ void mla_decode32_kernel(const uint16_t* __restrict__ q, const uint8_t* __restri
     } else {
         PvState pv;
         const int c = wave - 4;
+        // Step ti: A(ti) (own loads of tile ti landed); the gathers of tile ti+3 into the
+        // buffer of tile ti-1; B(ti); PV(ti-1) from the V operands held since step ti-1 and
+        // P(ti-1), published at B(ti); then the V operands of tile ti into the same registers.
         auto pv_pass = [&](bool fixed) {
             const VAddr va = v_addr(c, lane);
 #pragma unroll
@@ -536,12 +563,20 @@ void mla_decode32_kernel(const uint16_t* __restrict__ q, const uint8_t* __restri
                 for (int ct = 0; ct < 4; ++ct)
 #pragma unroll
                     for (int i = 0; i < 16; ++i) pv.acc[h2][ct][i] = 0.f;
-            const GatherLane gl = gather_lane(c, lane);
-            if (n_tiles > 0) gather_tile(lat_b, 0, c, gl);
-            if (n_tiles > 1) gather_tile(lat_b, 1, c, gl);
+            const GatherLane<0, kGatherLoads> gl = gather_lane<0, kGatherLoads>(c, lane);
+            if (n_tiles > 0) gather_tile<0, kGatherLoads>(lat_b, 0, c, gl);
+            if (n_tiles > 1) gather_tile<0, kGatherLoads>(lat_b, 1, c, gl);
             v8bf vop[2][4];                                           // V operands of the previous tile
             for (int ti = 0; ti <= n_tiles; ++ti) {
-                step_begin(ti);
+                wait_tile_pv(ti, n_tiles);
+                lds_barrier();                                        // A(ti)
+                if (ti >= 1 && ti + 3 < n_tiles) gather_tile<0, kPvLoads>(lat_b, ti + 3, c, gl);
+                lds_barrier();                                        // B(ti)
+                if (ti == 0) {
+                    // buffers 2 and 3 held the queries until the QK waves' reads of step 0
+                    for (int tj = 2; tj <= 3; ++tj)
+                        if (tj < n_tiles) gather_tile<0, kPvLoads>(lat_b, tj, c, gl);
+                }
                 if (ti > 0) {
                     v8bf pop[2][2];                                   // P(ti - 1) operands [kk][hh]
 #pragma unroll
@@ -552,9 +587,6 @@ void mla_decode32_kernel(const uint16_t* __restrict__ q, const uint8_t* __restri
                     pv_tile(pv, vop, pop);
                 }
                 if (ti < n_tiles) load_v(vop, tile_buf(ti), va);
-                lds_barrier();                                        // B(ti)
-                step_gathers(ti, gl);
-                if (!fixed && ti == 0 && tile0_usable) lds_barrier();  // C
             }
         };
         pv_pass(false);

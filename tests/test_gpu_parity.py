@@ -560,6 +560,56 @@ def test_layer_step_deterministic(dsa):
     assert torch.equal(o1, o2)
 
 
+GRAPH_CASES = [
+    ("decode_split", _small("decode_v32", name="graph_decode", B=8, Lmax=9000, lens="ragged:3000:9000",
+                            seed=311)),
+    ("decode_long_rows", _small("decode_long", name="graph_long", B=2, Lmax=40000, seed=312)),
+    ("prefill_mha", _small("prefill_chunk", name="graph_mha", T=300, Lmax=300, H=4, k=64, seed=313)),
+]
+
+
+@pytest.mark.parametrize("name,cfg", GRAPH_CASES, ids=[c[0] for c in GRAPH_CASES])
+def test_layer_step_graph_replay(dsa, name, cfg):
+    """The whole step captured in one HIP graph, the way the benchmark can replay it: every
+    replay, with eager work and synchronisations between replays, reproduces the eager
+    step bit for bit (scores, selection, output, lse).  The outputs are overwritten
+    before each replay, so a replay that skipped a kernel would be caught."""
+    _say(f"[graph] {name}")
+    c = S.make_case(cfg)
+    d = _dev(c)
+    if cfg.form == "latent":
+        step = dsa.LayerStep(d["q_i"], d["q_scale"], d["w"], d["k_i"], d["k_scale"], d["lens"],
+                             cfg.sm_scale_i, cfg.k, d["q"], cfg.sm_scale, latent=d["latent"],
+                             Dv=cfg.Dv, want_idx=True, want_scores=True)
+    else:
+        step = dsa.LayerStep(d["q_i"], d["q_scale"], d["w"], d["k_i"], d["k_scale"], d["lens"],
+                             cfg.sm_scale_i, cfg.k, d["q"], cfg.sm_scale, k=d["k"], v=d["v"],
+                             want_idx=True, want_scores=True)
+    out, lse = step()
+    torch.cuda.synchronize()
+    ref = [t.clone() for t in (step.scores, step.idx, out, lse)]
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    for r in range(3):
+        step.scores.fill_(7.0)
+        step.idx.fill_(-7)
+        step.out.fill_(3.0)
+        step.lse.fill_(5.0)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for got, want, what in zip((step.scores, step.idx, step.out, step.lse), ref,
+                                   ("scores", "idx", "out", "lse")):
+            assert torch.equal(got, want), f"replay {r}: {what} differs from the eager step"
+
+
 @pytest.mark.parametrize("T,H,k", [(200, 2, 48), (130, 3, 130), (64, 1, 1)])
 def test_sparse_mla_prefill_blocks(dsa, orc, T, H, k):
     """Several 128-row query blocks and 64-key blocks, ragged tails, k >= T (dense causal)
