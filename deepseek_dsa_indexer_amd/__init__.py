@@ -16,12 +16,15 @@ The computation lives in ``libdsa_amd.so`` (HIP kernels behind the C ABI of
         (the library's fixed per-device scratch instead of a workspace; at most
          NOALLOC_SCRATCH_BYTES of it)
 
+    diag_fp8_mfma_dots(a, b)                                             -> (fp8, bf16)
+        (diagnostic: 128-code FP8 dot products on both matrix-core forms)
+
 Build the library with ``python -m deepseek_dsa_indexer_amd.build``.
 """
-from ._native import (NOALLOC_SCRATCH_BYTES, DSAError, LayerStep, index_scores, indexer_prep,
-                      library_path, load, profile_begin, profile_end, sparse_mla_decode,
-                      sparse_mla_prefill, topk)
+from ._native import (NOALLOC_SCRATCH_BYTES, DSAError, LayerStep, diag_fp8_mfma_dots, index_scores,
+                      indexer_prep, library_path, load, profile_begin, profile_end,
+                      sparse_mla_decode, sparse_mla_prefill, topk)
 
-__all__ = ["NOALLOC_SCRATCH_BYTES", "DSAError", "LayerStep", "index_scores", "indexer_prep",
-           "library_path", "load", "profile_begin", "profile_end", "sparse_mla_decode",
-           "sparse_mla_prefill", "topk"]
+__all__ = ["NOALLOC_SCRATCH_BYTES", "DSAError", "LayerStep", "diag_fp8_mfma_dots", "index_scores",
+           "indexer_prep", "library_path", "load", "profile_begin", "profile_end",
+           "sparse_mla_decode", "sparse_mla_prefill", "topk"]

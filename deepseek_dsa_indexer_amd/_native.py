@@ -26,7 +26,7 @@ EXPORTED = ["dsa_last_error", "dsa_version", "dsa_indexer_prep", "dsa_index_scor
             "dsa_topk", "dsa_sparse_mla_decode_workspace_bytes", "dsa_sparse_mla_decode",
             "dsa_sparse_mla_prefill_workspace_bytes", "dsa_sparse_mla_prefill",
             "dsa_layer_step_workspace_bytes", "dsa_layer_step", "dsa_layer_step_noalloc",
-            "dsa_profile_begin", "dsa_profile_end"]
+            "dsa_profile_begin", "dsa_profile_end", "dsa_diag_fp8_mfma_dots"]
 NOALLOC_SCRATCH_BYTES = 64 << 20     # DSA_NOALLOC_SCRATCH_BYTES
 PHASES = ("index_scores", "topk", "attention", "combine")
 
@@ -93,9 +93,11 @@ def load():
     lib.dsa_layer_step_noalloc.argtypes = [ctypes.POINTER(LayerArgs), P]
     lib.dsa_profile_begin.argtypes = [I]
     lib.dsa_profile_end.argtypes = [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(I)]
+    lib.dsa_diag_fp8_mfma_dots.argtypes = [P, P, I, P, P, P]
     for fn in ("dsa_indexer_prep", "dsa_index_scores", "dsa_topk", "dsa_sparse_mla_decode",
                "dsa_sparse_mla_prefill",
-               "dsa_layer_step", "dsa_layer_step_noalloc", "dsa_profile_begin", "dsa_profile_end"):
+               "dsa_layer_step", "dsa_layer_step_noalloc", "dsa_profile_begin", "dsa_profile_end",
+               "dsa_diag_fp8_mfma_dots"):
         getattr(lib, fn).restype = I
     _lib = lib
     return lib
@@ -274,6 +276,23 @@ def profile_end() -> dict:
     cnt = (ctypes.c_int * 4)()
     _check(load().dsa_profile_end(ms, cnt))
     return {name: (ms[i], cnt[i]) for i, name in enumerate(PHASES)}
+
+
+def diag_fp8_mfma_dots(a, b):
+    """Diagnostic: dot products of the 128-code FP8 rows a[p] . b[p] (uint8 [n,128] device
+    tensors, n a multiple of 16) on the FP8 and on the bf16 matrix-core forms.
+    Returns (out_fp8, out_bf16), float32 [n]."""
+    for t, n in ((a, "a"), (b, "b")):
+        if t.dtype != torch.uint8 or t.dim() != 2 or t.shape[1] != 128 or not t.is_contiguous():
+            raise ValueError(f"{n}: need a contiguous uint8 [n, 128] tensor")
+    if a.shape != b.shape:
+        raise ValueError("a and b differ in shape")
+    n = a.shape[0]
+    out8 = torch.empty(n, dtype=torch.float32, device=a.device)
+    outb = torch.empty(n, dtype=torch.float32, device=a.device)
+    _check(load().dsa_diag_fp8_mfma_dots(a.data_ptr(), b.data_ptr(), n, out8.data_ptr(),
+                                         outb.data_ptr(), _stream(a.device)))
+    return out8, outb
 
 
 class LayerStep:

@@ -468,4 +468,16 @@ dsa_status dsa_layer_step_noalloc(const dsa_layer_args* a, hipStream_t stream) {
     return dsa_layer_step(a, ws, kStaticScratchBytes, stream);
 }
 
+dsa_status dsa_diag_fp8_mfma_dots(const uint8_t* a, const uint8_t* b, int n, float* out_fp8,
+                                  float* out_bf16, hipStream_t stream) {
+    DSA_REQUIRE(a && b && out_fp8 && out_bf16, DSA_ERR_NULL, "diag fp8 dots: NULL pointer");
+    DSA_REQUIRE(n >= 16 && n % 16 == 0 && n <= (1 << 24), DSA_ERR_SHAPE,
+                "diag fp8 dots: n=%d must be a positive multiple of 16 up to 2^24", n);
+    DSA_REQUIRE(aligned16(a) && aligned16(b) && aligned16(out_fp8) && aligned16(out_bf16), DSA_ERR_ALIGN,
+                "diag fp8 dots: pointers must be 16-byte aligned");
+    const hipError_t e = dsa::launch_diag_fp8_dots(a, b, n, out_fp8, out_bf16, stream);
+    DSA_REQUIRE(e == hipSuccess, DSA_ERR_HIP, "diag fp8 dots: %s", hipGetErrorString(e));
+    return DSA_OK;
+}
+
 }  // extern "C"

@@ -127,6 +127,10 @@ hipError_t launch_mla_decode32(const void* q, const void* latent, const int32_t*
 // Matrix-core path of the MHA prefill form (bf16, Dqk = 192, Dv = 128).
 bool mha_prefill_mfma_supported(int Dqk, int Dv, int bf16);
 size_t mha_prefill_workspace_bytes(int B, int T);
+// Diagnostic: n (a multiple of 16) dot products of 128 FP8 codes, row p of a with row p
+// of b, on the FP8 and on the bf16 matrix-core forms.
+hipError_t launch_diag_fp8_dots(const uint8_t* a, const uint8_t* b, int n, float* out_fp8,
+                                float* out_bf16, hipStream_t stream);
 hipError_t launch_mha_prefill_mfma(const void* q, const void* k, const void* v, const int32_t* idx,
                                    int B, int T, int H, int topk, float sm_scale, void* out,
                                    float* lse, void* ws, hipStream_t stream);

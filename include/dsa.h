@@ -274,6 +274,19 @@ dsa_status dsa_layer_step_noalloc(const dsa_layer_args* a, hipStream_t stream);
 dsa_status dsa_profile_begin(int max_steps);
 dsa_status dsa_profile_end(double* ms_total, int* counts);
 
+/*
+ * Diagnostic: the precision of the two matrix-core forms of the indexer contraction.
+ *   Row p of a and row p of b (n rows each, 128 FP8 e4m3fn codes per row, device
+ *   memory, 16-byte aligned) give one dot product per row pair; out_fp8[p] is it as the
+ *   gfx950 FP8 matrix-core instruction (v_mfma_f32_16x16x128_f8f6f4) computes it,
+ *   out_bf16[p] as the bf16 form over the codes widened exactly (the form the index
+ *   kernels use).  The pairs are those of the score box of "dsa-indexer.excalidraw"
+ *   (q_j . k_s per head, before the ReLU and the scales).  n must be a positive
+ *   multiple of 16 up to 2^24.  Enqueues one kernel; outputs valid after a sync.
+ */
+dsa_status dsa_diag_fp8_mfma_dots(const uint8_t* a, const uint8_t* b, int n, float* out_fp8,
+                                  float* out_bf16, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -49,6 +49,14 @@ def test_index_scores_validation(lib):
     assert lib.dsa_index_scores(q, p, p, p, p, p, 1, 1, 64, 128, 16, 1.0, p, None) == 4
 
 
+def test_diag_fp8_dots_validation(lib):
+    p = _fake()
+    assert lib.dsa_diag_fp8_mfma_dots(None, p, 16, p, p, None) == 1
+    assert lib.dsa_diag_fp8_mfma_dots(p, p, 15, p, p, None) == 2
+    assert lib.dsa_diag_fp8_mfma_dots(p, p, 0, p, p, None) == 2
+    assert lib.dsa_diag_fp8_mfma_dots(_fake(0x10008), p, 16, p, p, None) == 4
+
+
 def test_topk_validation(lib):
     p = _fake()
     assert lib.dsa_topk(p, p, 1, 1, 16, 0, p, None, 0, None) == 2
