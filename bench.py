@@ -38,7 +38,8 @@ BF16_PEAK_TFLOPS = 2500.0        # MI355X dense bf16 MFMA, published
 FP8_PEAK_TFLOPS = 5000.0         # MI355X dense FP8 MFMA, published
 METRIC = "DSA decode layer-steps/s and indexer keys scored/s; % of HBM/MFMA roofline"
 ATTN_SOURCE = os.path.join(ROOT, "deepseek_dsa_indexer_amd", "csrc", "sparse_mla_decode32.hip")
-ATTN_FP8_SOURCE = os.path.join(ROOT, "deepseek_dsa_indexer_amd", "csrc", "sparse_attn.hip")
+ATTN_FP8_SOURCE = os.path.join(ROOT, "deepseek_dsa_indexer_amd", "csrc", "sparse_mla_decode32_fp8.hip")
+ATTN_GENERIC_SOURCE = os.path.join(ROOT, "deepseek_dsa_indexer_amd", "csrc", "sparse_attn.hip")
 INDEX_SOURCE = os.path.join(ROOT, "deepseek_dsa_indexer_amd", "csrc", "index_scores.hip")
 PREFILL_SOURCE = os.path.join(ROOT, "deepseek_dsa_indexer_amd", "csrc", "sparse_mha_prefill.hip")
 
@@ -78,6 +79,24 @@ def algorithmic_costs(cfg, lens, latent_form="bf16"):
         att_flops = sel * 2 * cfg.H * (cfg.Dqk + cfg.Dv)
     return dict(keys=keys, selected=sel, index_bytes=idx_bytes, index_flops=idx_flops,
                 attention_bytes=att_bytes, attention_flops=att_flops)
+
+
+def latent_32x32_kernel(cfg, fp8_rows: bool) -> bool:
+    """Whether the library's latent attention plan takes its 32x32x16 kernel for this
+    workload: 64 heads per workgroup, enough key splits to give 256 workgroups, tiles of
+    32 bf16 rows (at most 16 per split) or 64 FP8 rows (at most 8), and all of them in one
+    wave of at most 256 workgroups (mla_plan in sparse_attn.hip)."""
+    if cfg.H not in (64, 128) or cfg.Dv != 512:
+        return False
+    rows = cfg.B * cfg.T
+    parts = cfg.H // 64
+    kt, tmax = (64, 8) if fp8_rows else (32, 16)
+    n_tiles = -(-cfg.k // kt)
+    wg = rows * parts
+    s = 1 if wg >= 256 else -(-256 // wg)
+    s = max(min(s, 16), -(-n_tiles // tmax))
+    s = max(1, min(s, n_tiles))
+    return wg * s <= 256
 
 
 def read_traffic(kernel: str, workload: str, source: str):
@@ -329,12 +348,14 @@ def measure(D, S, cfg, steps: int, warmup: int, sets: int, latent: str, graph: b
     idx_tfs = costs["index_flops"] / (idx_launch_ms * 1e-3) / 1e12
     workload = cfg.name + ("-fp8" if fp8_lat else "")
     if cfg.form == "latent":
-        if fp8_lat:
-            kernel, tkey, src = "mla_decode_mfma_kernel", "sparse_mla_decode", ATTN_FP8_SOURCE
+        tkey = "sparse_mla_decode"
+        if latent_32x32_kernel(cfg, fp8_lat):
+            kernel, src = (("mla_decode32_fp8_kernel", ATTN_FP8_SOURCE) if fp8_lat
+                           else ("mla_decode32_kernel", ATTN_SOURCE))
         else:
-            kernel, tkey, src = "mla_decode32_kernel", "sparse_mla_decode", ATTN_SOURCE
+            kernel, src = "mla_decode_mfma_kernel", ATTN_GENERIC_SOURCE
         if cfg.H not in (64, 128) or cfg.Dv != 512:
-            kernel, src = "sparse_attn_generic_kernel", ATTN_FP8_SOURCE
+            kernel, src = "sparse_attn_generic_kernel", ATTN_GENERIC_SOURCE
     else:
         kernel, tkey, src = "mha_prefill_mfma_kernel", "sparse_mha_prefill", PREFILL_SOURCE
     traffic = read_traffic(tkey, workload, src)

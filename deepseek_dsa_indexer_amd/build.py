@@ -17,7 +17,8 @@ OUT = os.path.join(PKG, "libdsa_amd.so")
 BUILD_DIR = os.path.join(ROOT, "_build")
 
 SOURCES = ["indexer_prep.hip", "index_scores.hip", "topk.hip", "sparse_attn.hip",
-           "sparse_mla_decode32.hip", "sparse_mha_prefill.hip", "diag_fp8_mfma.hip",
+           "sparse_mla_decode32.hip", "sparse_mla_decode32_fp8.hip", "sparse_mha_prefill.hip",
+           "diag_fp8_mfma.hip",
            "dsa_abi.cpp"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

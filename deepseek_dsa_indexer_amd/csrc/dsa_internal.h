@@ -124,6 +124,16 @@ hipError_t launch_mla_decode32(const void* q, const void* latent, const int32_t*
                                int tiles_per_split, int n_splits, float scale_log2, void* out,
                                float* lse, void* part_o, float* part_lse, hipStream_t stream);
 
+// The same for latent rows in the 656-byte FP8 form (sparse_mla_decode32_fp8.hip): tiles of
+// mla_decode32_fp8_tile_rows() slots, at most mla_decode32_fp8_max_tiles() per split;
+// partials and the combine as above.
+int mla_decode32_fp8_max_tiles();
+int mla_decode32_fp8_tile_rows();
+hipError_t launch_mla_decode32_fp8(const void* q, const void* latent, const int32_t* idx,
+                                   const int32_t* len, int rows, int T, int H, int Lmax, int k, int m,
+                                   int tiles_per_split, int n_splits, float scale_log2, void* out,
+                                   float* lse, void* part_o, float* part_lse, hipStream_t stream);
+
 // Matrix-core path of the MHA prefill form (bf16, Dqk = 192, Dv = 128).
 bool mha_prefill_mfma_supported(int Dqk, int Dv, int bf16);
 size_t mha_prefill_workspace_bytes(int B, int T);

@@ -896,10 +896,33 @@ struct MlaPlan {
     int parts;        // head parts per row
     int splits;       // key splits per row
     bool k32;         // the 32x32x16 kernel (sparse_mla_decode32.hip)
+    bool k32f8;       // its FP8-row form (sparse_mla_decode32_fp8.hip)
+    int tile_rows;    // slots per tile of the chosen kernel
 };
 MlaPlan mla_plan(int rows, int H, int k, int type) {
     MlaPlan p;
     p.k32 = false;
+    p.k32f8 = false;
+    p.tile_rows = kKt;
+    if (type == kLatFp8 && (H == 64 || H == 128)) {
+        // the 32x32x16 kernel over FP8 rows: 64-slot tiles, same split rule (one wave of at
+        // most 256 workgroups, else the 16x16 kernel below)
+        const int kt = mla_decode32_fp8_tile_rows();
+        const int tmax = mla_decode32_fp8_max_tiles();
+        const int n_tiles = (k + kt - 1) / kt;
+        p.parts = H / 64;
+        p.nht = 4;
+        const int wg = rows * p.parts;
+        int s = wg >= 256 ? 1 : (256 + wg - 1) / wg;
+        s = min(s, kMaxSplits);
+        s = max(s, (n_tiles + tmax - 1) / tmax);
+        p.splits = max(1, min(s, n_tiles));
+        if (static_cast<long long>(wg) * p.splits <= 256 && n_tiles <= tmax * kMaxSplits) {
+            p.k32f8 = true;
+            p.tile_rows = kt;
+            return p;
+        }
+    }
     if (type == kLatBf16 && mla_decode32_supported(H, k)) {
         // the 32x32x16 kernel: 64 heads per workgroup, enough key splits to give every CU
         // a workgroup, at most mla_decode32_max_tiles() tiles per split -- when that fits
@@ -943,7 +966,7 @@ hipError_t launch_mla_decode_mfma(const void* q, const void* latent, const int32
     const int rows = B * T;
     const MlaPlan plan = mla_plan(rows, H, k, type);
     const int s = plan.splits;
-    const int n_tiles = (k + kKt - 1) / kKt;
+    const int n_tiles = (k + plan.tile_rows - 1) / plan.tile_rows;
     const int tps = (n_tiles + s - 1) / s;
     uint16_t* part_o = static_cast<uint16_t*>(ws);
     float* part_lse = s > 1 ? reinterpret_cast<float*>(part_o + static_cast<size_t>(rows) * s * H * kDv)
@@ -953,9 +976,11 @@ hipError_t launch_mla_decode_mfma(const void* q, const void* latent, const int32
     auto lp = static_cast<const uint8_t*>(latent);
     auto op = static_cast<uint16_t*>(out);
     const bool f8 = type == kLatFp8;
-    if (plan.k32) {
-        hipError_t e = launch_mla_decode32(q, latent, idx, len, rows, T, H, Lmax, k, m, tps, s,
-                                           scale_log2, out, lse, part_o, part_lse, stream);
+    if (plan.k32 || plan.k32f8) {
+        hipError_t e = plan.k32 ? launch_mla_decode32(q, latent, idx, len, rows, T, H, Lmax, k, m, tps, s,
+                                                      scale_log2, out, lse, part_o, part_lse, stream)
+                                : launch_mla_decode32_fp8(q, latent, idx, len, rows, T, H, Lmax, k, m, tps, s,
+                                                          scale_log2, out, lse, part_o, part_lse, stream);
         if (e != hipSuccess || s == 1) return e;
         const int parts = (H * (kDv / kCombCols) + 255) / 256;
         return launch_kernel(kPhaseCombine, mla_combine_kernel, dim3(rows * parts), dim3(256), 0, stream,
