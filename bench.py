@@ -119,6 +119,27 @@ def read_traffic(kernel: str, workload: str, source: str):
         return None
 
 
+def read_rocprof_avg_ms(kernels, workload: str, source: str):
+    """Average duration of the kernel named ``kernels`` (a name, or a tuple of names, up to
+    the template arguments) in the committed
+    rocprofv3 kernel-trace summary profiles/kernels_<workload>.txt; None when absent or
+    when the summary was taken on a different kernel source."""
+    path = os.path.join(ROOT, "profiles", f"kernels_{workload}.txt")
+    if not os.path.exists(path):
+        return None
+    src = os.path.basename(source)
+    ok = False
+    for line in open(path):
+        if line.startswith("# kernel sources"):
+            ok = f"{src} {_sha(source)}" in line
+        elif ok and not line.startswith("#"):
+            name = line.split("calls=")[0].strip()
+            if any(name == k or name.startswith(k + "<") for k in
+                   ((kernels,) if isinstance(kernels, str) else kernels)):
+                return float(line.split("avg_ns=")[1].split()[0]) * 1e-6
+    return None
+
+
 def cpu_baseline(cfg, n_seqs: int, min_seconds: float = 10.0, latent_form: str = "bf16"):
     """The oracle, untuned, on a bounded sample of the same workload, scaled to a step.
 
@@ -375,6 +396,16 @@ def measure(D, S, cfg, steps: int, warmup: int, sets: int, latent: str, graph: b
     roofline.update({"traffic": traffic, "kernel": kernel, "avg_launch_ms": round(att_launch_ms, 5),
                      "timing": "HIP start/stop events recorded by each launch's dispatch "
                                "(hipExtLaunchKernel), averaged over the profiled steps"})
+    # the same kernel's average in the committed rocprofv3 summary (per-dispatch timestamps
+    # under the profiler), and the fraction it gives
+    rp_ms = read_rocprof_avg_ms(kernel, workload, src)
+    if rp_ms is not None:
+        per_s = (costs["attention_flops"] / (BF16_PEAK_TFLOPS * 1e12) if mfma_bound
+                 else costs["attention_bytes"] / (HBM_PEAK_GBS * 1e9))
+        roofline.update({"rocprof_avg_launch_ms": round(rp_ms, 5),
+                         "frac_at_rocprof_avg": round(per_s / (rp_ms * 1e-3), 4)})
+    idx_rp_ms = read_rocprof_avg_ms(("index_scores_kernel", "index_scores_decode_kernel"),
+                                    workload, INDEX_SOURCE)
     # the step's floor: each phase at the larger of its HBM time and its matrix-core time at
     # the peak of its own data type (the indexer's FP8 products, the attention's bf16)
     t_roof = (max(costs["index_bytes"] / (HBM_PEAK_GBS * 1e9), costs["index_flops"] / (FP8_PEAK_TFLOPS * 1e12)) +
@@ -416,7 +447,8 @@ def measure(D, S, cfg, steps: int, warmup: int, sets: int, latent: str, graph: b
                          "mfma_frac_of_bf16_peak": round(idx_tfs / BF16_PEAK_TFLOPS, 4),
                          "mfma_frac_of_fp8_peak": round(idx_tfs / FP8_PEAK_TFLOPS, 4),
                          "keys_per_s": round(costs["keys"] / (idx_launch_ms * 1e-3), 1),
-                         "traffic": read_traffic("index_scores", workload, INDEX_SOURCE)},
+                         "traffic": read_traffic("index_scores", workload, INDEX_SOURCE),
+                         "rocprof_avg_launch_ms": (round(idx_rp_ms, 5) if idx_rp_ms else None)},
         "roofline": roofline,
     }
     if with_prep:

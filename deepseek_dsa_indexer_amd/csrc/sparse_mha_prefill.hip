@@ -17,7 +17,7 @@
 //   load  K [64 x 192] and V [64 x 128] bf16 rows and the block's selection-mask words
 //         of the 256 rows into LDS with direct global->LDS loads, in a three-stage
 //         ring (two blocks in flight while one is computed), 16-byte chunks
-//         XOR-swizzled per row;
+//         XOR-swizzled per row (swz_k, swz_v);
 //   QK    S^T = K . Q^T per 32-key group (keys as MFMA rows, the wave's 32 queries as 12
 //         B operands in registers), so lane l holds query row l % 32 and keys
 //         32 kg + 8 (r / 4) + 4 (l / 32) + r % 4;
@@ -71,7 +71,18 @@ __shared__ __attribute__((aligned(16))) uint8_t m_stage[kStages * kStageBytes];
 
 typedef __bf16 v4bf_m __attribute__((ext_vector_type(4)));
 
-__device__ __forceinline__ int swz8(int row, int chunk) { return chunk ^ (row & 7); }
+// LDS swizzles, chosen so that the operand reads are free of bank conflicts (64 banks of
+// 4 bytes; a 16-byte read serves 16 lanes per pass, an 8-byte read 32 lanes):
+//   K rows (384 B = 24 chunks of 16 bytes): chunk c of key row r sits at c ^ ((r >> 1) & 7),
+//     inside its aligned group of 8.  A QK operand read takes one chunk of 16 consecutive
+//     rows; rows are 96 dwords apart, so rows of one parity share bank alignment and the
+//     XOR gives the 8 rows of each parity distinct 16-byte bank groups.
+//   V rows (256 B = 16 chunks = 4 groups of 4): group g of row r sits at g ^ (r & 3).  A
+//     transpose read takes one group (32 columns) of 4 consecutive rows per 16 lanes, and
+//     rows are 64 dwords apart (all bank-aligned): the XOR puts the 4 rows in distinct
+//     quarters of the banks.
+__device__ __forceinline__ int swz_k(int row, int chunk) { return chunk ^ ((row >> 1) & 7); }
+__device__ __forceinline__ int swz_v(int row, int chunk) { return chunk ^ ((row & 3) << 2); }
 
 __device__ __forceinline__ void dma16(const uint8_t* src, uint32_t lds_addr) {
     const uint32_t m0v = __builtin_amdgcn_readfirstlane(lds_addr);
@@ -81,6 +92,25 @@ __device__ __forceinline__ void dma16(const uint8_t* src, uint32_t lds_addr) {
 __device__ __forceinline__ void dma4(const uint32_t* src, uint32_t lds_addr) {
     const uint32_t m0v = __builtin_amdgcn_readfirstlane(lds_addr);
     asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dword %1, off" :: "s"(m0v), "v"(src) : "memory");
+}
+
+// A wave-uniform pointer, in scalar registers (the scalar-base loads below need it there).
+__device__ __forceinline__ const uint8_t* sgpr_ptr(const void* p) {
+    const uint64_t a = reinterpret_cast<uint64_t>(p);
+    const uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(a));
+    const uint32_t hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(a >> 32));
+    return reinterpret_cast<const uint8_t*>((static_cast<uint64_t>(hi) << 32) | lo);
+}
+
+// The same with a wave-uniform 64-bit base in scalar registers and a 32-bit per-lane offset.
+__device__ __forceinline__ void dma16_s(const uint8_t* sbase, uint32_t voff, uint32_t lds_addr) {
+    const uint32_t m0v = __builtin_amdgcn_readfirstlane(lds_addr);
+    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2" :: "s"(m0v), "v"(voff), "s"(sbase) : "memory");
+}
+
+__device__ __forceinline__ void dma4_s(const uint8_t* sbase, uint32_t voff, uint32_t lds_addr) {
+    const uint32_t m0v = __builtin_amdgcn_readfirstlane(lds_addr);
+    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dword %1, %2" :: "s"(m0v), "v"(voff), "s"(sbase) : "memory");
 }
 
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
@@ -108,7 +138,7 @@ __device__ __forceinline__ void load_block(const uint8_t* kbase, const uint8_t* 
             const int key = c / kKChunks;
             const int phys = c - key * kKChunks;
             const int s = min(s0 + key, T - 1);
-            const uint8_t* src = kbase + (static_cast<size_t>(s) * H + h) * kKRow + swz8(key, phys) * 16;
+            const uint8_t* src = kbase + (static_cast<size_t>(s) * H + h) * kKRow + swz_k(key, phys) * 16;
             dma16(src, kl + ci * 1024);
         } else {
             const int cv = ci - kKLoads;
@@ -116,10 +146,62 @@ __device__ __forceinline__ void load_block(const uint8_t* kbase, const uint8_t* 
             const int key = c / kVChunks;
             const int phys = c - key * kVChunks;
             const int s = min(s0 + key, T - 1);
-            const uint8_t* src = vbase + (static_cast<size_t>(s) * H + h) * kVRow + swz8(key, phys) * 16;
+            const uint8_t* src = vbase + (static_cast<size_t>(s) * H + h) * kVRow + swz_v(key, phys) * 16;
             dma16(src, vl + cv * 1024);
         }
     }
+}
+
+// Per-lane byte offsets of a wave's block loads relative to the block's first key row,
+// the same for every block (wave w issues loads w, w + 8, w + 16 of K and w, w + 8 of V,
+// each lane one 16-byte chunk, and one mask dword).  Blocks wholly inside the chunk
+// (s0 + 64 <= T) need no clamp and use them with a scalar base; the last, partial block
+// takes the clamped loads above.
+constexpr int kKPerWave = kKLoads / kMhaWaves;       // 3
+constexpr int kVPerWave = kVLoads / kMhaWaves;       // 2
+static_assert(kKLoads % kMhaWaves == 0 && kVLoads % kMhaWaves == 0, "K and V loads split evenly");
+struct MhaDma {
+    uint32_t k[kKPerWave];
+    uint32_t v[kVPerWave];
+    uint32_t m;
+};
+
+__device__ __forceinline__ MhaDma mha_dma(int t0, int T, int H, int words, int wave, int lane) {
+    MhaDma d;
+#pragma unroll
+    for (int i = 0; i < kKPerWave; ++i) {
+        const int c = (wave + kMhaWaves * i) * kWave + lane;
+        const int key = c / kKChunks;
+        const int phys = c - key * kKChunks;
+        d.k[i] = static_cast<uint32_t>(key * H * kKRow + swz_k(key, phys) * 16);
+        asm volatile("" : "+v"(d.k[i]));
+    }
+#pragma unroll
+    for (int i = 0; i < kVPerWave; ++i) {
+        const int c = (wave + kMhaWaves * i) * kWave + lane;
+        const int key = c / kVChunks;
+        const int phys = c - key * kVChunks;
+        d.v[i] = static_cast<uint32_t>(key * H * kVRow + swz_v(key, phys) * 16);
+        asm volatile("" : "+v"(d.v[i]));
+    }
+    const int row = min(t0 + 32 * wave + (lane >> 1), T - 1);
+    d.m = static_cast<uint32_t>((row * words + (lane & 1)) * 4);
+    asm volatile("" : "+v"(d.m));
+    return d;
+}
+
+// load_block for a block with s0 + 64 <= T.
+__device__ __forceinline__ void load_block_full(const uint8_t* kbase, const uint8_t* vbase,
+                                                const uint32_t* mask_b, int H, int h, int s0,
+                                                uint8_t* st, int wave, const MhaDma& d) {
+    const uint32_t kl = lds_addr(st), vl = kl + kKBytes;
+    dma4_s(sgpr_ptr(mask_b + (s0 >> 5)), d.m, vl + kVBytes + wave * kWave * 4);
+    const uint8_t* kb = sgpr_ptr(kbase + (static_cast<size_t>(s0) * H + h) * kKRow);
+    const uint8_t* vb = sgpr_ptr(vbase + (static_cast<size_t>(s0) * H + h) * kVRow);
+#pragma unroll
+    for (int i = 0; i < kKPerWave; ++i) dma16_s(kb, d.k[i], kl + (wave + kMhaWaves * i) * 1024);
+#pragma unroll
+    for (int i = 0; i < kVPerWave; ++i) dma16_s(vb, d.v[i], vl + (wave + kMhaWaves * i) * 1024);
 }
 
 __device__ __forceinline__ void lds_sync() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
@@ -131,16 +213,53 @@ struct MhaState {
     bool over;
 };
 
-__device__ __forceinline__ void mha_block(MhaState& st, const uint8_t* stage, int t_row, int s0,
-                                          float scale_log2, int wave, int lane, bool fixed) {
-    const uint8_t* kb = stage;
-    const uint8_t* vb = stage + kKBytes;
-    const uint32_t* mk = reinterpret_cast<const uint32_t*>(stage + kKBytes + kVBytes);
-    int lo = lane;
-    asm volatile("" : "+v"(lo));
-    const int hf = lo >> 5;
-    const int r32 = lo & 31;
-    const uint2 mw = *reinterpret_cast<const uint2*>(mk + 2 * (32 * wave + r32));
+// Lane-invariant LDS byte offsets within a stage, computed once per workgroup (each block
+// then adds only its stage base; the rest of a K read's address is an instruction
+// immediate).
+//   K: key 32 kg + r32, 16-byte chunk 2 ks + hf at position (2 ks + hf) ^ z, z = (r32 >> 1)
+//      & 7 (= (key >> 1) & 7); for ks = 4 j + i that is 8 j + ((2 i + hf) ^ z), so koff[i] =
+//      384 r32 + 16 ((2 i + hf) ^ z) and the read of (ks, kg) is koff[ks % 4] + 12288 kg +
+//      128 (ks / 4).
+//   V: key 32 kg + 16 ks + 8 e4 + sv, sv = 4 hf + m / 4 (key & 3 = m / 4), chunk 4 dg + c0,
+//      c0 = 2 ch + (m % 4) / 2, at position 4 (dg ^ m / 4) + c0, so voff[dg] = 256 sv +
+//      64 (dg ^ m / 4) + 16 c0 + 8 (m % 2) and the read of (dg, kg, ks, e4) is voff[dg] +
+//      256 (32 kg + 16 ks + 8 e4).
+//   mask: the two words of row 32 wave + r32.
+struct MhaLane {
+    uint32_t koff[4];
+    uint32_t voff[4];
+    uint32_t moff;
+    int hf, r32;
+};
+
+__device__ __forceinline__ MhaLane mha_lane(int wave, int lane) {
+    MhaLane ml;
+    ml.hf = lane >> 5;
+    ml.r32 = lane & 31;
+    const int s = (ml.r32 >> 1) & 7;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        ml.koff[i] = static_cast<uint32_t>(kKRow * ml.r32 + 16 * ((2 * i + ml.hf) ^ s));
+        asm volatile("" : "+v"(ml.koff[i]));      // kept, not recomputed per block
+    }
+    const int m = lane & 15;
+    const int ch = (lane >> 4) & 1;
+    const int sv = 4 * ml.hf + (m >> 2);
+    const int c0 = 2 * ch + ((m & 3) >> 1);
+#pragma unroll
+    for (int dg = 0; dg < 4; ++dg) {
+        ml.voff[dg] = static_cast<uint32_t>(kKBytes + kVRow * sv + 64 * (dg ^ (m >> 2)) + 16 * c0 + 8 * (m & 1));
+        asm volatile("" : "+v"(ml.voff[dg]));
+    }
+    ml.moff = static_cast<uint32_t>(kKBytes + kVBytes + 8 * (32 * wave + ml.r32));
+    asm volatile("" : "+v"(ml.moff));
+    return ml;
+}
+
+__device__ __forceinline__ void mha_block(MhaState& st, const uint8_t* stage, const MhaLane& ml, int t_row,
+                                          int s0, float scale_log2, bool fixed) {
+    const int hf = ml.hf;
+    const uint2 mw = *reinterpret_cast<const uint2*>(stage + ml.moff);
 
     // ---- S^T = K . Q^T for the two 32-key groups: independent accumulation chains
     v16f sacc[2];
@@ -152,8 +271,7 @@ __device__ __forceinline__ void mha_block(MhaState& st, const uint8_t* stage, in
     for (int ks = 0; ks < kDqk / 16; ++ks) {
 #pragma unroll
         for (int kg = 0; kg < 2; ++kg) {
-            const int key = 32 * kg + r32;
-            const v8bf a = *reinterpret_cast<const v8bf*>(kb + key * kKRow + swz8(key, 2 * ks + hf) * 16);
+            const v8bf a = *reinterpret_cast<const v8bf*>(stage + ml.koff[ks & 3] + 32 * kKRow * kg + 128 * (ks >> 2));
             sacc[kg] = mfma_bf16_32x32x16(a, st.qreg[ks], sacc[kg]);
         }
     }
@@ -168,8 +286,12 @@ __device__ __forceinline__ void mha_block(MhaState& st, const uint8_t* stage, in
         const uint32_t word = ((kg ? mw.y : mw.x) & vis) >> (4 * hf);
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-            const bool ok = (word >> (8 * (r >> 2) + (r & 3))) & 1u;
-            const float v = ok ? sacc[kg][r] * scale_log2 : -INFINITY;
+            // all ones where the key is usable, else zero (a sign-extended one-bit field),
+            // then one bitwise select between the scaled logit and -inf
+            const int bit = 8 * (r >> 2) + (r & 3);
+            const uint32_t keep = static_cast<uint32_t>(static_cast<int32_t>(word << (31 - bit)) >> 31);
+            const float v = __uint_as_float((__float_as_uint(sacc[kg][r] * scale_log2) & keep) |
+                                            (0xff800000u & ~keep));
             sacc[kg][r] = v;
             mx = fmaxf(mx, v);
         }
@@ -197,11 +319,8 @@ __device__ __forceinline__ void mha_block(MhaState& st, const uint8_t* stage, in
     // ---- O += P . V.  V operand of (kg, ks), lane l: column 32 dg + l % 32, keys
     // 32 kg + 16 ks + 8 e4 + 4 hf + 0..3 (e4 = 0, 1), two transpose reads: lane m of a
     // 16-lane group supplies row key0 + m / 4, columns d0 + 4 (m % 4) .. + 3.
-    const int ch = (lo >> 4) & 1;
-    const int m = lo & 15;
 #pragma unroll
     for (int dg = 0; dg < kDvM / 32; ++dg) {
-        const int chunk = 4 * dg + 2 * ch + ((m & 3) >> 1);
 #pragma unroll
         for (int kg = 0; kg < 2; ++kg)
 #pragma unroll
@@ -209,10 +328,9 @@ __device__ __forceinline__ void mha_block(MhaState& st, const uint8_t* stage, in
                 v4bf_m half[2];
 #pragma unroll
                 for (int e4 = 0; e4 < 2; ++e4) {
-                    const int key = 32 * kg + 16 * ks + 8 * e4 + 4 * hf + (m >> 2);
-                    const int off = key * kVRow + swz8(key, chunk) * 16 + (m & 1) * 8;
+                    const uint8_t* src = stage + ml.voff[dg] + kVRow * (32 * kg + 16 * ks + 8 * e4);
                     half[e4] = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
-                        (__attribute__((address_space(3))) v4bf_m*)(vb + off));
+                        (__attribute__((address_space(3))) v4bf_m*)(src));
                 }
                 const v8bf vop = v8bf{half[0][0], half[0][1], half[0][2], half[0][3],
                                       half[1][0], half[1][1], half[1][2], half[1][3]};
@@ -269,21 +387,30 @@ void mha_prefill_mfma_kernel(const uint16_t* __restrict__ q, const uint16_t* __r
     // compiler's wait for them (it cannot see the direct-to-LDS loads) is the only
     // full drain, at the first block.
     auto stage = [&](int j) { return m_stage + (j % kStages) * kStageBytes; };
+    const MhaLane ml = mha_lane(wave, lane);
+    const MhaDma dma = mha_dma(t0, T, H, words, wave, lane);
+    // the per-lane offsets are 32-bit: key rows up to 64 H apart, mask rows up to T words
+    const bool offsets32 = static_cast<long long>(kKB) * H * kKRow < (1ll << 31) &&
+                           static_cast<long long>(T) * words * 4 < (1ll << 31);
     auto sweep = [&](bool fixed) {
 #pragma unroll
         for (int dg = 0; dg < kDvM / 32; ++dg)
 #pragma unroll
             for (int r = 0; r < 16; ++r) st.o[dg][r] = 0.f;
         st.l_run = 0.f;
-        load_block(kbase, vbase, mask_b, words, t0, T, H, h, 0, stage(0), wave, lane);
-        if (nblocks > 1) load_block(kbase, vbase, mask_b, words, t0, T, H, h, kKB, stage(1), wave, lane);
+        auto issue = [&](int j) {
+            const int s0 = j * kKB;
+            if (s0 + kKB <= T && offsets32) load_block_full(kbase, vbase, mask_b, H, h, s0, stage(j), wave, dma);
+            else load_block(kbase, vbase, mask_b, words, t0, T, H, h, s0, stage(j), wave, lane);
+        };
+        issue(0);
+        if (nblocks > 1) issue(1);
         for (int j = 0; j < nblocks; ++j) {
             if (j + 1 < nblocks) asm volatile("s_waitcnt vmcnt(%0)" :: "n"(kDmaPerBlock) : "memory");
             else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
             lds_sync();
-            if (j + 2 < nblocks)
-                load_block(kbase, vbase, mask_b, words, t0, T, H, h, (j + 2) * kKB, stage(j + 2), wave, lane);
-            mha_block(st, stage(j), t_row, j * kKB, scale_log2, wave, lane, fixed);
+            if (j + 2 < nblocks) issue(j + 2);
+            mha_block(st, stage(j), ml, t_row, j * kKB, scale_log2, fixed);
         }
     };
     sweep(false);
