@@ -126,12 +126,16 @@ __device__ __forceinline__ void wait_tile_qk(int t, int n_tiles) {
 }
 
 // LDS layout of a tile: row r (1152 bytes = 72 chunks of 16 bytes) keeps its chunk c at
-// chunk position c ^ swz(r), swz(r) = (r >> 1) & 7.  Rows are 288 dwords apart, which is 32
-// banks, so rows of one parity share a half of the 64 banks; within it the XOR gives the 8
-// rows of each parity among any 16 consecutive rows distinct 4-bank groups, and 16-lane
-// reads of one chunk over 16 consecutive rows are free of bank conflicts.  (The XOR stays
+// chunk position c ^ swz(r), swz(r) = 4 ((r >> 1) & 1) + ((r >> 2) & 3), a bijection of
+// (r >> 1) & 7.  Rows are 288 dwords apart, which is 32 banks, so rows of one parity share
+// a half of the 64 banks; within it the XOR gives the 8 rows of each parity among any 16
+// consecutive rows distinct 4-bank groups, so 16-lane reads of one chunk over 16
+// consecutive rows (the QK operands) are free of bank conflicts.  The V transpose reads
+// take, per 32-lane pass, one aligned group of 4 chunks from 4 consecutive rows 4 i ..
+// 4 i + 3: bit 2 of swz, ((r >> 1) & 1), puts rows 4 i and 4 i + 2 (and 4 i + 1, 4 i + 3) in
+// different bank quarters, so those reads are conflict-free as well.  (The XOR stays
 // inside each aligned group of 8 chunks, so the rope chunks 64..71 stay in place.)
-__device__ __forceinline__ int swz(int r) { return (r >> 1) & 7; }
+__device__ __forceinline__ int swz(int r) { return (((r >> 1) & 1) << 2) | ((r >> 2) & 3); }
 
 // Direct global->LDS loads of a tile: 36 wave-wide 1 KB loads ci = c + 4 i (wave position
 // c = 0..3, i = 0..8); lane l of load ci fetches 16-byte chunk q = 64 ci + l of the tile,
@@ -358,7 +362,7 @@ __device__ __forceinline__ VAddr v_addr(int c, int lane) {
     va.base = (4 * g + e) * kRowBytes + 8 * (j & 1) + 16 * 16 * c;
 #pragma unroll
     for (int qh = 0; qh < 2; ++qh) {
-        // the lane's keys 16 kk + 8 qh + 4 g + e share swz = (4 qh + 2 g + e / 2) & 7
+        // the lane's keys 16 kk + 8 qh + 4 g + e share swz (it depends on bits 1..3 of the row)
         const int x = swz(8 * qh + 4 * g + e);
         va.t[qh][0] = 16 * ((0 + low) ^ x);
         va.t[qh][1] = 16 * ((4 + low) ^ x);

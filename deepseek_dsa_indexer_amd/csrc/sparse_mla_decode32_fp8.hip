@@ -93,10 +93,16 @@ template <int N> struct IntConst { static constexpr int value = N; };
 __device__ __forceinline__ uint8_t* tile_buf(int ti) { return s_tile + (ti % kBufs) * kTileBytes; }
 __device__ __forceinline__ float* scale_tab(int ti, int blk) { return &s_scale[ti & (kScaleBufs - 1)][blk][0]; }
 
-// Byte offset of tile row r: groups of 16 rows, each followed by 128 bytes of padding, so
-// that rows r and r + 16 (656-byte rows are 36 banks apart; rows 16 apart would meet) lie
-// 32 banks apart and a 32-lane read of one column over 32 rows is free of conflicts.
-__device__ __forceinline__ int row_off(int r) { return ((r >> 4) * kGroupChunks + (r & 15) * kRowChunks) * 16; }
+// Tile layout: groups of 16 rows, each followed by 128 bytes of padding; within a group,
+// row r sits at position kpos(r) = 8 (r / 8) + 2 (r % 4) + (r / 4) % 2, 656 bytes apart.
+// With 64 banks of 4 bytes, position p starts 9 p (mod 16) 16-byte bank groups in, so the
+// 16 rows of a group fill the 16 groups once: a 16-byte read of one column over 16 rows
+// (QK operands, 16 lanes per pass) is free of conflicts.  The PV transpose reads take 32
+// bytes of one column from rows {0, 1, 2, 3, 8, 9, 10, 11} (or the other eight) per 32-lane
+// pass; those rows sit at even (odd) positions, whose 32-byte runs tile the 64 banks.
+__device__ __forceinline__ int kpos(int r) { return 8 * (r >> 3) + 2 * (r & 3) + ((r >> 2) & 1); }
+__device__ __forceinline__ int kslot(int p) { return 8 * (p >> 3) + 4 * (p & 1) + ((p & 7) >> 1); }
+__device__ __forceinline__ int row_off(int r) { return ((r >> 4) * kGroupChunks + kpos(r & 15) * kRowChunks) * 16; }
 
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() { asm volatile("s_waitcnt vmcnt(%0)" :: "n"(N) : "memory"); }
@@ -136,7 +142,7 @@ __device__ __forceinline__ GatherLane<I0, N> gather_lane(int c, int lane) {
             const int grp = p / kGroupChunks;
             const int w = p - grp * kGroupChunks;
             const bool data = w < 16 * kRowChunks;
-            gl.key[i] = p >= kTileChunks ? -1 : data ? 16 * grp + w / kRowChunks : 0;
+            gl.key[i] = p >= kTileChunks ? -1 : data ? 16 * grp + kslot(w / kRowChunks) : 0;
             gl.off[i] = data ? (w % kRowChunks) * 16 : 0;
         } else {
             gl.key[i] = lane;
@@ -185,9 +191,11 @@ struct QkState {
 
 // K-step order of a QK wave for one 32-row half kb of the tile: the two rope steps (into
 // the total), then latent block 2 dh (steps 0..7) and block 2 dh + 1 (steps 8..15), each
-// its own chain.  The lane supplies row 32 kb + l % 32, columns 8 (l / 32) .. + 7 of the
-// step: codes at byte 256 dh + 16 ks + 8 (l / 32), or rope values at byte 528 + 64 dh +
-// 32 (ks - 16) + 16 (l / 32).
+// its own chain.  The lane supplies row 32 kb + l % 32 and eight columns of the step:
+// codes at byte 256 dh + 32 (ks / 2) + 16 (l / 32) + 8 (ks % 2) (the two steps of a pair
+// come from one 16-byte read; the block's columns are a permutation of its 128, the
+// queries' K-steps use the same one), or rope values at byte 528 + 64 dh + 32 (ks - 16) +
+// 16 (l / 32).
 __device__ __forceinline__ constexpr int qk_order(int n) { return n < 2 ? 16 + n : n - 2; }
 
 // Phase 1 of a QK wave: the numerators of the tile completed in the previous step,
@@ -206,16 +214,19 @@ __device__ __forceinline__ void qk_tile(float (&own)[2][8], const v8bf (&qreg)[k
     const int g = lo >> 5;
     st.over = st.over || (!fixed && mx > st.m_ref + kRefSpan);
     const float mref = st.m_ref == -INFINITY ? 0.f : st.m_ref;
-    auto raw_at = [&](int kb, int ks) -> int4 {
+    // One 16-byte read per unit: units 0, 1 of a half are the two rope steps, units 2 + m the
+    // code K-steps 2 m and 2 m + 1 (bytes 256 dh + 32 m + 16 g: codes 0..7 for step 2 m,
+    // 8..15 for step 2 m + 1 -- the queries use the same column order).
+    auto unit_of = [](int n) { const int m = n % kKs; return (kKs / 2 + 1) * (n / kKs) + (m < 2 ? m : 2 + (m - 2) / 2); };
+    auto unit_read = [&](int u) -> int4 {
+        const int kb = u / (kKs / 2 + 1);
+        const int k = u % (kKs / 2 + 1);
         const uint8_t* row = kb_lds + row_off(32 * kb + r);
-        if (ks < 16) {
-            const uint2 c = *reinterpret_cast<const uint2*>(row + 256 * DH + 16 * ks + 8 * g);
-            return int4{static_cast<int>(c.x), static_cast<int>(c.y), 0, 0};
-        }
-        return *reinterpret_cast<const int4*>(row + kRopeOff + 64 * DH + 32 * (ks - 16) + 16 * g);
+        if (k < 2) return *reinterpret_cast<const int4*>(row + kRopeOff + 64 * DH + 32 * k + 16 * g);
+        return *reinterpret_cast<const int4*>(row + 256 * DH + 32 * (k - 2) + 16 * g);
     };
     auto op = [&](int ks, const int4& w) -> v8bf {
-        if (ks < 16) return fp8x8_to_bf16(w.x, w.y);
+        if (ks < 16) return (ks & 1) ? fp8x8_to_bf16(w.z, w.w) : fp8x8_to_bf16(w.x, w.y);
         return __builtin_bit_cast(v8bf, w);
     };
     // acc += scale (of the lane's 16 rows: 32 kb + 8 j + 4 g + 0..3) * blk
@@ -230,10 +241,11 @@ __device__ __forceinline__ void qk_tile(float (&own)[2][8], const v8bf (&qreg)[k
         }
     };
     constexpr int kN = 2 * kKs;           // K-steps of both halves
-    constexpr int kPre = 6;               // operand reads in flight (LDS latency)
+    constexpr int kUnits = 2 * (kKs / 2 + 1);   // 20 reads per tile
+    constexpr int kPre = 4;               // read units in flight (LDS latency)
     int4 raw[kPre];
 #pragma unroll
-    for (int n = 0; n < kPre; ++n) raw[n] = raw_at(n / kKs, qk_order(n % kKs));
+    for (int u = 0; u < kPre; ++u) raw[u] = unit_read(u);
     // numerators of the previous tile first, while the first operand reads are in flight
     // (the previous logits are then dead during the chains: registers are scarce here)
     float psum = 0.f;
@@ -255,8 +267,10 @@ __device__ __forceinline__ void qk_tile(float (&own)[2][8], const v8bf (&qreg)[k
         const int kb = n / kKs;
         const int m = n % kKs;
         const int ks = qk_order(m);
-        const v8bf a = op(ks, raw[n % kPre]);
-        if (n + kPre < kN) raw[n % kPre] = raw_at((n + kPre) / kKs, qk_order((n + kPre) % kKs));
+        const int u = unit_of(n);
+        const v8bf a = op(ks, raw[u % kPre]);
+        // the unit's last step: its slot takes the read kPre units ahead
+        if ((m < 2 || (ks & 1)) && u + kPre < kUnits) raw[u % kPre] = unit_read(u + kPre);
         if (m < 2) {
             acc = mfma_bf16_32x32x16(a, qreg[ks], m == 0 ? v16f{} : acc);
         } else if (m < 10) {
@@ -353,7 +367,7 @@ __device__ __forceinline__ int v_base(int c, int lane) {
     const int m = lo & 15;
     const int e = m >> 1;
     const int g = G >> 1;
-    return (8 * (e >> 2) + 4 * g + (e & 3)) * kRow + 128 * c + 16 * (G & 1) + 8 * (m & 1);
+    return (8 * (e >> 2) + 2 * (e & 3) + g) * kRow + 128 * c + 16 * (G & 1) + 8 * (m & 1);   // kpos of row 8 (e >> 2) + 4 g + (e & 3)
 }
 __device__ __forceinline__ void load_codes(v2i_t (&vc)[4][4], const uint8_t* kb_lds, int vb) {
 #pragma unroll
@@ -461,14 +475,16 @@ void mla_decode32_fp8_kernel(const uint16_t* __restrict__ q, const uint8_t* __re
         if (s_tmask[i] != 0ull) ref_tile = i;
 
     if (qk_wave) {
-        // queries of head 32 hh + l % 32: K-step ks < 16 holds columns 256 dh + 16 ks + 8 (l / 32)
-        // .. + 7, ks >= 16 rope columns 512 + 32 dh + 16 (ks - 16) + 8 (l / 32) .. + 7
+        // queries of head 32 hh + l % 32, in the column order of the code reads: K-step ks < 16
+        // holds columns 256 dh + 32 (ks / 2) + 16 (l / 32) + 8 (ks % 2) .. + 7, ks >= 16 rope
+        // columns 512 + 32 dh + 16 (ks - 16) + 8 (l / 32) .. + 7
         v8bf qreg[kKs];
-        const uint16_t* qrow = q + (static_cast<size_t>(row) * H_total + head0 + 32 * hh + (lane & 31)) * kDq +
-                               8 * (lane >> 5);
+        const uint16_t* qrow = q + (static_cast<size_t>(row) * H_total + head0 + 32 * hh + (lane & 31)) * kDq;
+        const int gq = lane >> 5;
 #pragma unroll
         for (int ks = 0; ks < kKs; ++ks)
-            qreg[ks] = *reinterpret_cast<const v8bf*>(qrow + (ks < 16 ? 256 * dh + 16 * ks : 512 + 32 * dh + 16 * (ks - 16)));
+            qreg[ks] = *reinterpret_cast<const v8bf*>(
+                qrow + (ks < 16 ? 256 * dh + 32 * (ks >> 1) + 16 * gq + 8 * (ks & 1) : 512 + 32 * dh + 16 * (ks - 16) + 8 * gq));
         // wait for them here, with the wait instruction the compiler tracks (vmcnt(0)), so
         // that it places no wait for them inside the tile loop, where it would also drain
         // this wave's gathers
