@@ -50,10 +50,15 @@ constexpr int kChunk = 64;          // keys per wave iteration (4 MFMA column ti
 constexpr int kMaxHeads = 64;       // indexer heads (4 MFMA row tiles)
 constexpr int kMaxSeqPerThread = 16; // numbered decode launches: up to 4096 sequences
 
-// Query operands of one row from its [64 heads][128 bytes] LDS copy: lane l, head group
-// hg takes head 32 hg + l % 32, dims 64 hf + 8 ks .. + 7; heads past H and bytes past D
-// are zero.  Weights: element r of head group hg belongs to head 32 hg + 8 (r / 4) +
-// 4 hf + r % 4.
+// LDS copy of a query row: [64 heads][128 bytes], the 16-byte chunk c of head h stored at
+// chunk position c ^ qswz(h).  Head rows are 32 banks apart, so without the XOR a 16-lane
+// read of one chunk over 16 heads would meet only two 4-bank groups (8-way conflicts);
+// with it the heads of each parity take distinct groups.
+__device__ __forceinline__ int qswz(int h) { return (h >> 1) & 7; }
+
+// Query operands of one row from its LDS copy: lane l, head group hg takes head 32 hg +
+// l % 32, dims 64 hf + 8 ks .. + 7; heads past H and bytes past D are zero.  Weights:
+// element r of head group hg belongs to head 32 hg + 8 (r / 4) + 4 hf + r % 4.
 template <int D>
 __device__ __forceinline__ void load_queries(const uint8_t* sq, const float* swf, int H, int lane,
                                              v8bf (&qa)[2][8], float (&wf)[2][16]) {
@@ -64,7 +69,7 @@ __device__ __forceinline__ void load_queries(const uint8_t* sq, const float* swf
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             const int byte = 64 * hf + 16 * j;
-            const uint4 v = *reinterpret_cast<const uint4*>(sq + h * 128 + byte);
+            const uint4 v = *reinterpret_cast<const uint4*>(sq + h * 128 + 16 * ((4 * hf + j) ^ qswz(h)));
             const int mk = (h < H && byte < D) ? -1 : 0;
             qa[hg][2 * j] = fp8x8_to_bf16(static_cast<int>(v.x) & mk, static_cast<int>(v.y) & mk);
             qa[hg][2 * j + 1] = fp8x8_to_bf16(static_cast<int>(v.z) & mk, static_cast<int>(v.w) & mk);
@@ -239,7 +244,7 @@ void index_scores_kernel(const uint8_t* __restrict__ q, const float* __restrict_
         const int r = i / (kMaxHeads * 8);
         const int h = (i / 8) % kMaxHeads;
         const int c16 = i % 8;
-        *reinterpret_cast<uint4*>(&s_q[r][h * 128 + c16 * 16]) = qok[u] ? qv[u] : uint4{0u, 0u, 0u, 0u};
+        *reinterpret_cast<uint4*>(&s_q[r][h * 128 + 16 * (c16 ^ qswz(h))]) = qok[u] ? qv[u] : uint4{0u, 0u, 0u, 0u};
     }
     if (wr < QR) s_wf[wr][wh] = (wr < nrows && wh < H) ? wv * qsv * sm_scale : 0.f;
     __syncthreads();
@@ -375,13 +380,16 @@ void index_scores_decode_kernel(const uint8_t* __restrict__ q, const float* __re
         dma4(lds_addr(slot + kChunk * 128), ks_ptr + min(kb + lane, Lmax - 1));
     };
 
-    // ---- the query row (wave w brings bytes [2048 w, 2048 w + 2048) of [64 heads][128]),
-    // the head weights (wave 0) and q scales (wave 1), then the first two chunks
+    // ---- the query row (wave w brings LDS bytes [2048 w, 2048 w + 2048) of [64 heads][128]:
+    // chunk position p of head h holds chunk p ^ qswz(h)), the head weights (wave 0) and q
+    // scales (wave 1), then the first two chunks
     const uint8_t* qrow = q + static_cast<size_t>(b) * H * D;
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
         const int o = 2048 * wave + 1024 * i + 16 * lane;
-        const int h = min(o >> 7, H - 1), byte = o & 127;   // heads past H, bytes past D: masked on read
+        const int hq = o >> 7;
+        const int h = min(hq, H - 1);                         // heads past H, bytes past D: masked on read
+        const int byte = 16 * (((o & 127) >> 4) ^ qswz(hq));
         dma16(lds_addr(s_q + 2048 * wave + 1024 * i), qrow + h * D + (byte < D ? byte : 0));
     }
     if (wave == 0) dma4(lds_addr(s_w), w + static_cast<size_t>(b) * H + min(lane, H - 1));
