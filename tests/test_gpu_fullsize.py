@@ -39,9 +39,9 @@ def _np(t):
 
 @pytest.mark.parametrize("name,latent_form", [("decode_v32", "bf16"), ("decode_long", "bf16"),
                                                ("decode_ragged", "bf16"), ("decode_v32", "fp8"),
-                                               ("decode_ragged", "fp8")],
+                                               ("decode_long", "fp8"), ("decode_ragged", "fp8")],
                          ids=["decode_v32", "decode_long", "decode_ragged", "decode_v32-fp8",
-                              "decode_ragged-fp8"])
+                              "decode_long-fp8", "decode_ragged-fp8"])
 def test_fullsize_decode(dsa, orc, name, latent_form):
     cfg = S.CONFIGS[name]
     _say(f"[fullsize] {name} ({latent_form} latent): generating inputs")
