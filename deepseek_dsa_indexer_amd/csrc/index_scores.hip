@@ -455,12 +455,20 @@ hipError_t launch_d(const IndexScoresArgs& a, hipStream_t stream) {
 }
 
 // Key chunks per wave: enough waves to cover every SIMD twice (2048 waves), then longer
-// streams per wave (up to 8 chunks) so the block's query and weight set-up is amortised.
+// streams per wave (up to 8 chunks) so the block's query and weight set-up is amortised --
+// but at most 4 when full-length 8-chunk blocks would take more than one round of the
+// 512 resident workgroups (two per CU): the blocks of many unequal sequences then do not
+// fill the last round, and shorter blocks shorten that tail (64 sequences of 1024..65536
+// positions: 67.2 -> 64.1 us; 8 sequences of 131072 fill exactly one round of 8-chunk
+// blocks: 32.9 against 33.5 us with 4).
+constexpr long long kResidentBlocks = 512;
 template <int D>
 hipError_t launch_rows(const IndexScoresArgs& a, hipStream_t stream) {
     if (a.T >= 2) return launch_d<D, 2, 4>(a, stream);
     const long long total_chunks = static_cast<long long>(a.B) * ((a.Lmax + kChunk - 1) / kChunk);
-    const int chunks = static_cast<int>(std::min<long long>(8, std::max<long long>(2, total_chunks / 2048)));
+    const long long blocks8 = static_cast<long long>(a.B) * ((a.Lmax + kWaves * kChunk * 8 - 1) / (kWaves * kChunk * 8));
+    const long long cap = blocks8 > kResidentBlocks ? 4 : 8;
+    const int chunks = static_cast<int>(std::min<long long>(cap, std::max<long long>(2, total_chunks / 2048)));
     // short streams (two chunks per wave) gain nothing from the deeper LDS pipeline and
     // pay its longer issue sequence: measured 12.4 vs 10.9 us at B=32, L=8192; at
     // B=8, L=131072 (eight chunks per wave) the LDS form is ahead
