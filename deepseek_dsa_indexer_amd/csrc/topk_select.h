@@ -9,7 +9,9 @@
 // the keys rather than fixed key bits (fixed top bits put scores that share an exponent
 // into a handful of bins), so one or two levels usually isolate the threshold.  The loop
 // ends when the range holds exactly the number of keys still needed or shrinks to one
-// key value.  A final compaction hands out, in index order, every key above the range
+// key value; when the bin of the k-th key holds at most kSelCand keys, they are instead
+// gathered into LDS and one wave ranks them, which gives that key's exact value in place
+// of further histogram levels.  A final compaction hands out, in index order, every key above the range
 // plus the first `need` keys inside it, using one block-wide prefix sum; equal keys
 // therefore resolve towards the smaller index.
 #pragma once
@@ -23,6 +25,7 @@ constexpr int kSelBinBits = 11;
 constexpr int kSelPerThread = 4;
 constexpr int kSelMaxIters = 4;                      // register-held block iterations
 constexpr uint32_t kNoKey = 0u;                      // no element (float bits of -NaN)
+constexpr int kSelCand = 64;                         // bin sizes resolved by ranking
 
 template <int NT>
 struct SelectShared {
@@ -33,6 +36,9 @@ struct SelectShared {
     uint32_t bin;
     uint32_t need;
     uint32_t bin_count;
+    uint32_t cand[kSelCand];          // the keys of a small threshold bin
+    uint32_t cand_n;
+    uint32_t tau;                     // their need-th largest value
 };
 
 __device__ __forceinline__ uint32_t score_key(float f) {
@@ -181,6 +187,7 @@ __device__ __forceinline__ void block_select(Keys<NT, REG, Src>& ks, int k, Sele
     kmax = wave_max_u32(kmax);
     if (lane == 0) { sh.red[0][wave] = kmin; sh.red[1][wave] = kmax; }
     for (int i = threadIdx.x; i < kSelBins; i += NT) sh.hist[0][i] = 0;
+    if (threadIdx.x == 0) sh.cand_n = 0;
     __syncthreads();
     uint32_t lo = sh.red[0][0], hi = sh.red[1][0];
 #pragma unroll
@@ -238,6 +245,35 @@ __device__ __forceinline__ void block_select(Keys<NT, REG, Src>& ks, int k, Sele
         lo = new_lo;
         ++level;
         if (count == need) break;                       // the whole class is selected
+        if (count <= static_cast<uint32_t>(kSelCand) && hi != lo) {
+            // A small bin: gather its keys (order does not matter) and let wave 0 rank
+            // them.  Key x is the need-th largest iff (keys > x) < need <= (keys >= x);
+            // the range becomes [x, x] with need - (keys > x) of its copies still needed,
+            // exactly what further levels would reach.  (cand_n was zeroed before the
+            // level's first barrier; sh.tau / sh.need are read after the next barrier.)
+            ks.visit_all([&](uint32_t key, int, bool ok) {
+                if (ok && key >= lo && key <= hi) sh.cand[atomicAdd(&sh.cand_n, 1u)] = key;
+            });
+            __syncthreads();
+            if (wave == 0) {
+                const int m = static_cast<int>(count);
+                const uint32_t x = lane < m ? sh.cand[lane] : 0u;
+                uint32_t gt = 0, ge = 0;
+                for (int j = 0; j < m; ++j) {
+                    const uint32_t y = sh.cand[j];
+                    gt += y > x;
+                    ge += y >= x;
+                }
+                if (lane < m && gt < need && need <= ge) {   // lanes holding that value agree
+                    sh.tau = x;
+                    sh.need = need - gt;
+                }
+            }
+            __syncthreads();
+            lo = hi = sh.tau;
+            need = sh.need;
+            break;
+        }
         // sh.bin / sh.need are rewritten only after the next level's two barriers
     }
 
