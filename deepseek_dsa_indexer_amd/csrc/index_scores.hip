@@ -83,6 +83,15 @@ __device__ __forceinline__ void load_queries(const uint8_t* sq, const float* swf
     }
 }
 
+// max(x, 0) as one instruction.  fmaxf(x, 0.f) compiles to two here: the compiler first
+// quiets a possible signalling NaN (v_max_f32 x, x, x) because it cannot tell that the
+// matrix-core result is canonical; the dot products of finite codes are never NaN.
+__device__ __forceinline__ float relu(float x) {
+    float y;
+    asm("v_max_f32 %0, 0, %1" : "=v"(y) : "v"(x));
+    return y;
+}
+
 // Head sum of one 64-key chunk for one query row: kr[kg][j] is lane l's 16-byte piece j
 // of key 32 kg + l % 32 (bytes 64 hf + 16 j .. + 15).  Returns, in lane l, the score of
 // key (chunk + l) before its key scale.
@@ -108,7 +117,7 @@ __device__ __forceinline__ float chunk_scores(const v8bf (&qa)[2][8], const floa
 #pragma unroll
         for (int hg = 0; hg < 2; ++hg)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) acc += wf[hg][r] * fmaxf(d[hg][r], 0.f);
+            for (int r = 0; r < 16; ++r) acc += wf[hg][r] * relu(d[hg][r]);
         tot[kg] = sum_xor32(acc);
     }
     return (lane & 32) ? tot[1] : tot[0];
@@ -464,7 +473,11 @@ hipError_t launch_d(const IndexScoresArgs& a, hipStream_t stream) {
 constexpr long long kResidentBlocks = 512;
 template <int D>
 hipError_t launch_rows(const IndexScoresArgs& a, hipStream_t stream) {
-    if (a.T >= 2) return launch_d<D, 2, 4>(a, stream);
+    // Several query rows (prefill): one row per wave and 8-chunk streams.  Two rows per wave
+    // halve the key loads from L2 but need 419 registers (one wave per SIMD, accumulators
+    // read back through AGPRs); one row fits two waves per SIMD (prefill chunk of 8192
+    // rows: 837 -> 789 us).
+    if (a.T >= 2) return launch_d<D, 1, 8>(a, stream);
     const long long total_chunks = static_cast<long long>(a.B) * ((a.Lmax + kChunk - 1) / kChunk);
     const long long blocks8 = static_cast<long long>(a.B) * ((a.Lmax + kWaves * kChunk * 8 - 1) / (kWaves * kChunk * 8));
     const long long cap = blocks8 > kResidentBlocks ? 4 : 8;
