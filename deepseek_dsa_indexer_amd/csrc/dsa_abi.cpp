@@ -134,7 +134,8 @@ size_t latent_ws(int B, int T, int H, int Dv, int Dr, int k, dsa_dtype dt) {
 }
 
 dsa_status check_mha_args(const void* q, const void* k, const void* v, const int32_t* idx, int B,
-                          int T, int H, int Dqk, int Dv, int topk, dsa_dtype dt, const void* out) {
+                          int T, int H, int Dqk, int Dv, int topk, float sm_scale, dsa_dtype dt,
+                          const void* out) {
     DSA_REQUIRE(q && k && v && idx && out, DSA_ERR_NULL, "sparse_mla_prefill: NULL pointer");
     DSA_REQUIRE(dt == DSA_F32 || dt == DSA_BF16, DSA_ERR_DTYPE, "sparse_mla_prefill: bad dtype %d",
                 static_cast<int>(dt));
@@ -146,7 +147,7 @@ dsa_status check_mha_args(const void* q, const void* k, const void* v, const int
                 "sparse_mla_prefill: B*T*H too large");
     DSA_REQUIRE(aligned16(q) && aligned16(k) && aligned16(v) && aligned16(idx) && aligned16(out),
                 DSA_ERR_ALIGN, "sparse_mla_prefill: pointers must be 16-byte aligned");
-    if (!dsa::mha_prefill_mfma_supported(Dqk, Dv, dt == DSA_BF16))
+    if (!dsa::mha_prefill_mfma_path(Dqk, Dv, dt == DSA_BF16, sm_scale))
         DSA_REQUIRE(sizeof(float) * (static_cast<size_t>(Dqk) + topk) <= kGenericLdsLimit, DSA_ERR_SHAPE,
                     "sparse_mla_prefill: k=%d too large for this shape", topk);
     return DSA_OK;
@@ -155,7 +156,7 @@ dsa_status check_mha_args(const void* q, const void* k, const void* v, const int
 dsa_status launch_mha(const void* q, const void* k, const void* v, const int32_t* idx, int B, int T,
                       int H, int Dqk, int Dv, int topk, float sm_scale, dsa_dtype dt, void* out,
                       float* lse, void* ws, hipStream_t stream) {
-    if (dsa::mha_prefill_mfma_supported(Dqk, Dv, dt == DSA_BF16))
+    if (dsa::mha_prefill_mfma_path(Dqk, Dv, dt == DSA_BF16, sm_scale))
         return hip_status(dsa::launch_mha_prefill_mfma(q, k, v, idx, B, T, H, topk, sm_scale, out, lse,
                                                        ws, stream),
                           "sparse_mla_prefill");
@@ -370,7 +371,7 @@ dsa_status dsa_sparse_mla_prefill(const void* q, const void* k, const void* v, c
                                   int B, int T, int H, int Dqk, int Dv, int topk, float sm_scale,
                                   dsa_dtype dt, void* out, float* lse, void* ws, size_t ws_bytes,
                                   hipStream_t stream) {
-    dsa_status st = check_mha_args(q, k, v, idx, B, T, H, Dqk, Dv, topk, dt, out);
+    dsa_status st = check_mha_args(q, k, v, idx, B, T, H, Dqk, Dv, topk, sm_scale, dt, out);
     if (st != DSA_OK) return st;
     DSA_REQUIRE(lse == nullptr || aligned16(lse), DSA_ERR_ALIGN, "sparse_mla_prefill: lse alignment");
     const size_t need = mha_ws(B, T, H, Dqk, Dv, topk, dt);
@@ -419,7 +420,7 @@ dsa_status dsa_layer_step(const dsa_layer_args* a, void* ws, size_t ws_bytes, hi
         DSA_REQUIRE(a->Lmax == a->T, DSA_ERR_SHAPE,
                     "layer step (MHA form): the chunk starts at 0, so Lmax must equal T");
         st = check_mha_args(a->q, a->k, a->v, a->len, a->B, a->T, a->H, a->Dqk, a->Dv, a->topk,
-                            a->dtype, a->out);
+                            a->sm_scale, a->dtype, a->out);
     }
     if (st != DSA_OK) return st;
     DSA_REQUIRE(a->lse == nullptr || aligned16(a->lse), DSA_ERR_ALIGN, "layer step: lse alignment");

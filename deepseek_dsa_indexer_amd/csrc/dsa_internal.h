@@ -136,6 +136,8 @@ hipError_t launch_mla_decode32_fp8(const void* q, const void* latent, const int3
 
 // Matrix-core path of the MHA prefill form (bf16, Dqk = 192, Dv = 128).
 bool mha_prefill_mfma_supported(int Dqk, int Dv, int bf16);
+// the matrix-core prefill path: a supported shape and a finite, positive softmax scale
+bool mha_prefill_mfma_path(int Dqk, int Dv, int bf16, float sm_scale);
 size_t mha_prefill_workspace_bytes(int B, int T);
 // Diagnostic: n (a multiple of 16) dot products of 128 FP8 codes, row p of a with row p
 // of b, on the FP8 and on the bf16 matrix-core forms.

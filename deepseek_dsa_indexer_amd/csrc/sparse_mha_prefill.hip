@@ -287,16 +287,17 @@ __device__ __forceinline__ void mha_block(MhaState& st, const uint8_t* stage, co
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
             // all ones where the key is usable, else zero (a sign-extended one-bit field),
-            // then one bitwise select between the scaled logit and -inf
+            // then one bitwise select between the (unscaled) logit and -inf
             const int bit = 8 * (r >> 2) + (r & 3);
             const uint32_t keep = static_cast<uint32_t>(static_cast<int32_t>(word << (31 - bit)) >> 31);
-            const float v = __uint_as_float((__float_as_uint(sacc[kg][r] * scale_log2) & keep) |
-                                            (0xff800000u & ~keep));
+            const float v = __uint_as_float((__float_as_uint(sacc[kg][r]) & keep) | (0xff800000u & ~keep));
             sacc[kg][r] = v;
             mx = fmaxf(mx, v);
         }
     }
-    mx = max_xor32(mx);
+    // the logits stay unscaled: the maximum is scaled once (the scale is positive, so it
+    // commutes with the maximum) and each numerator takes one fma before its exp2
+    mx = max_xor32(mx) * scale_log2;
     if (!fixed) {
         if (st.m_ref == -INFINITY) st.m_ref = mx;       // first block with a usable key
         st.m_max = fmaxf(st.m_max, mx);
@@ -310,7 +311,7 @@ __device__ __forceinline__ void mha_block(MhaState& st, const uint8_t* stage, co
     for (int kg = 0; kg < 2; ++kg)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-            const float p = exp2_num(sacc[kg][r] - mref);
+            const float p = exp2_num(fmaf(sacc[kg][r], scale_log2, -mref));
             psum += p;
             pk[kg][r >> 3][r & 7] = static_cast<short>(f32_to_bf16(p));
         }
@@ -476,6 +477,11 @@ void select_mask_kernel(const int32_t* __restrict__ idx, int T, int k, uint32_t*
 }  // namespace
 
 bool mha_prefill_mfma_supported(int Dqk, int Dv, int bf16) { return bf16 && Dqk == kDqk && Dv == kDvM; }
+// The kernel takes each block's maximum over the unscaled logits and scales it once, which
+// needs a positive scale (NaN fails both comparisons).
+bool mha_prefill_mfma_path(int Dqk, int Dv, int bf16, float sm_scale) {
+    return mha_prefill_mfma_supported(Dqk, Dv, bf16) && sm_scale > 0.f && sm_scale < INFINITY;
+}
 
 size_t mha_prefill_workspace_bytes(int B, int T) {
     return static_cast<size_t>(B) * T * ((T + 31) / 32) * sizeof(uint32_t) + 256;

@@ -177,8 +177,10 @@ dsa_status dsa_sparse_mla_decode(const void* q, const void* latent, const int32_
  *   out  [B,T,H,Dv] (same dtype), lse [B,T,H] f32 or NULL.
  * Supported: dtype F32 or BF16, Dqk <= 1024, Dv <= 1024 (the vector-ALU path keeps all
  * topk logits in LDS: 4 (Dqk + topk) <= 65536 bytes); the bf16 shape Dqk = 192, Dv = 128
- * runs on the matrix-core path, which needs a workspace for the per-row selection bit
- * mask (B * T * ceil(T / 32) words; dsa_sparse_mla_prefill_workspace_bytes()).
+ * with a finite sm_scale > 0 runs on the matrix-core path, which needs a workspace for the
+ * per-row selection bit mask (B * T * ceil(T / 32) words;
+ * dsa_sparse_mla_prefill_workspace_bytes(), sized for that path); any other scale takes
+ * the vector-ALU path and its LDS bound on topk.
  */
 size_t dsa_sparse_mla_prefill_workspace_bytes(int B, int T, int H, int Dqk, int Dv, int topk,
                                               dsa_dtype dt);

@@ -610,6 +610,28 @@ def test_layer_step_graph_replay(dsa, name, cfg):
             assert torch.equal(got, want), f"replay {r}: {what} differs from the eager step"
 
 
+@pytest.mark.parametrize("sm", [0.0, -0.07])
+def test_sparse_mla_prefill_nonpositive_scale(dsa, orc, sm):
+    """The matrix-core prefill shape (bf16, qk 192 / v 128) with a zero or negative softmax
+    scale: served by the vector-ALU kernel (the matrix-core one scales each block's maximum
+    after taking it, which needs a positive scale), still against the oracle."""
+    _say(f"[sparse_mla_prefill bf16] scale {sm}")
+    rng = np.random.default_rng(41)
+    B, T, H, Dqk, Dv, k = 1, 40, 2, 192, 128, 16
+    q = S.to_bf16_bits(rng.standard_normal((B, T, H, Dqk), dtype=np.float32))
+    kk = S.to_bf16_bits(rng.standard_normal((B, T, H, Dqk), dtype=np.float32))
+    v = S.to_bf16_bits(rng.standard_normal((B, T, H, Dv), dtype=np.float32))
+    idx = np.full((B, T, k), -1, np.int32)
+    for t in range(T):
+        m = min(k, t + 1)
+        idx[0, t, :m] = rng.choice(t + 1, size=m, replace=False)
+    tt = lambda a: torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).cuda()
+    out, lse = dsa.sparse_mla_prefill(tt(q), tt(kk), tt(v), torch.from_numpy(idx).cuda(), sm)
+    torch.cuda.synchronize()
+    ro, rl = orc.sparse_mha_prefill(q, kk, v, idx, sm)
+    check_attention(_np_out(out), lse.cpu().numpy(), ro, rl, "bf16")
+
+
 @pytest.mark.parametrize("T,H,k", [(200, 2, 48), (130, 3, 130), (64, 1, 1)])
 def test_sparse_mla_prefill_blocks(dsa, orc, T, H, k):
     """Several 128-row query blocks and 64-key blocks, ragged tails, k >= T (dense causal)
