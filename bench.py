@@ -8,7 +8,9 @@ Inputs are seeded synthetic tensors of the configuration's shapes, resident in H
 before the timed region; several independent input sets are cycled so that the
 256 MB Infinity Cache cannot serve a step from the previous one.
 
-The timed steps are eager calls of dsa_layer_step (the library enqueueing each kernel);
+Before each workload's W warm-up steps, its steps run untimed for --ramp-seconds (0.3 s)
+so that the GPU's clocks have left the idle state that input generation leaves them in;
+the timed steps are eager calls of dsa_layer_step (the library enqueueing each kernel);
 the same steps replayed from one HIP graph per input set are timed as well and reported
 as graph_ms_per_step (``--graph`` makes them the headline).
 
@@ -35,6 +37,7 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0            # MI355X HBM3E, published
 BF16_PEAK_TFLOPS = 2500.0        # MI355X dense bf16 MFMA, published
+RAMP_S = 0.3                     # untimed steps before each workload's warm-up (seconds)
 FP8_PEAK_TFLOPS = 5000.0         # MI355X dense FP8 MFMA, published
 METRIC = "DSA decode layer-steps/s and indexer keys scored/s; % of HBM/MFMA roofline"
 ATTN_SOURCE = os.path.join(ROOT, "deepseek_dsa_indexer_amd", "csrc", "sparse_mla_decode32.hip")
@@ -278,7 +281,7 @@ DEFAULT_SETS = {"tiny": 2, "decode_v32": 4, "decode_long": 2, "decode_ragged": 2
 
 
 def measure(D, S, cfg, steps: int, warmup: int, sets: int, latent: str, graph: bool = False,
-            with_prep: bool = True) -> dict:
+            with_prep: bool = True, ramp_s: float = RAMP_S) -> dict:
     """Time `steps` layer steps of one workload (inputs resident on the GPU, `sets` input
     sets cycled), then the same steps again with per-kernel HIP events, and return the
     figures of one JSON object."""
@@ -314,6 +317,19 @@ def measure(D, S, cfg, steps: int, warmup: int, sets: int, latent: str, graph: b
             run_list[i % len(run_list)]()
         torch.cuda.synchronize()
         return time.perf_counter() - t0
+
+    # The GPU idles while the inputs are generated on the host, and its clocks take several
+    # milliseconds of load to come back: the first windows after such a pause measured 5-15 %
+    # slower than the steady state.  So the steps run untimed for ramp_s seconds first (the
+    # driver-sized W warm-up steps alone are a fraction of a millisecond).
+    t_ramp = time.perf_counter()
+    n_ramp = 0
+    while time.perf_counter() - t_ramp < ramp_s:
+        step_objs[n_ramp % len(step_objs)]()
+        n_ramp += 1
+        if n_ramp % 32 == 0:
+            torch.cuda.synchronize()
+    torch.cuda.synchronize()
 
     # eager launches (one C call per step, the library enqueueing each kernel) and the same
     # steps replayed from one HIP graph per input set (the launch sequence captured once)
@@ -422,6 +438,7 @@ def measure(D, S, cfg, steps: int, warmup: int, sets: int, latent: str, graph: b
         "unit": "layer-steps/s",
         "steps": steps,
         "warmup": warmup,
+        "gpu_ramp_s": ramp_s,
         "ms_per_step": round(ms_per_step, 5),
         "eager_ms_per_step": round(1e3 * dt_eager / steps, 5),
         "graph_ms_per_step": round(1e3 * dt_graph / steps, 5),
@@ -465,6 +482,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--ramp-seconds", type=float, default=RAMP_S,
+                    help="untimed steps before the warm-up, to bring the GPU clocks out of idle")
     ap.add_argument("--config", default="decode_v32", help="the headline workload")
     ap.add_argument("--only", action="store_true", help="measure the headline workload only")
     ap.add_argument("--sets", type=int, default=0,
@@ -513,7 +532,8 @@ def main():
         print("--latent fp8 applies to the latent (decode) workloads only", file=sys.stderr)
         sys.exit(2)
     sets = args.sets or DEFAULT_SETS.get(cfg.name, 4)
-    head = measure(D, S, cfg, args.steps, args.warmup, sets, args.latent, graph=args.graph)
+    head = measure(D, S, cfg, args.steps, args.warmup, sets, args.latent, graph=args.graph,
+                   ramp_s=args.ramp_seconds)
     result = {
         "metric": METRIC,
         "value": head["value"],
@@ -542,7 +562,7 @@ def main():
             steps = min(args.steps, 50) if ocfg.T == 1 else min(args.steps, 10)
             warm = min(args.warmup, 5)
             others[name] = measure(D, S, ocfg, steps, warm, DEFAULT_SETS.get(name, 2), lat,
-                                   graph=args.graph, with_prep=False)
+                                   graph=args.graph, with_prep=False, ramp_s=args.ramp_seconds)
         result["other_workloads"] = others
     print(json.dumps(result))
 
