@@ -396,6 +396,10 @@ LAYER_CASES = [
     # rows of 8192 positions with k = 2000: the last tile of the selection is partly unused
     ("k2000_l8192", _small("decode_v32", name="fk", B=2, Lmax=8192, k=2000, lens="ragged:7000:8192",
                            seed=210)),
+    # four query rows per sequence on the 32x32x16 attention kernel (eight rows: 16 splits
+    # each): causal rows, some with fewer visible positions than k
+    ("t4_rows", _small("decode_v32", name="tf", B=2, T=4, Lmax=5000, lens="ragged:1000:5000",
+                       seed=216)),
 ]
 
 
