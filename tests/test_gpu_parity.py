@@ -214,21 +214,29 @@ def test_sparse_mla_decode_mfma(dsa, orc, name, B, T, Lmax, lens, k, H):
     check_attention(_np_out(out), lse.cpu().numpy(), ro, rl, "bf16")
 
 
-def test_sparse_mla_decode_logit_spread(dsa, orc):
+# (B, k): two rows run the 32x32x16 kernels (sparse_mla_decode32*.hip); forty rows are more
+# workgroups than one wave of 256 and run mla_decode_mfma_kernel (sparse_attn.hip)
+# (B, k, slot of the late boosted key): the slot lies in the second or a later tile of its
+# split under either plan (4 tiles of 32 slots per split for B = 2; 3 per split for B = 40)
+SPREAD_SHAPES = [(2, 2048, 200), (40, 512, 250)]
+
+
+@pytest.mark.parametrize("B,k,late", SPREAD_SHAPES, ids=[f"B{b}" for b, _, _ in SPREAD_SHAPES])
+def test_sparse_mla_decode_logit_spread(dsa, orc, B, k, late):
     """Logits far above the rest of a split: in row 0 one key selected late in a split
     scores about 100 (log2 units) above everything before it for head 5 (the split is
     then recomputed from its true maximum); in row 1 such a key comes first, so every
     later probability of head 9 underflows relative to it.  The boost sits in the rope
     columns, so the outputs keep the magnitude of ordinary value rows."""
-    _say("[sparse_mla_decode bf16] logit spread")
+    _say(f"[sparse_mla_decode bf16] logit spread, B={B} k={k}")
     rng = np.random.default_rng(11)
-    B, T, H, Lmax, k = 2, 1, 128, 3000, 2048
-    lens = np.array([3000, 3000], np.int32)
+    T, H, Lmax = 1, 128, 3000
+    lens = np.full(B, 3000, np.int32)
     qf = rng.standard_normal((B, T, H, 576), dtype=np.float32)
     latf = rng.standard_normal((B, Lmax, 576), dtype=np.float32)
     idx = _random_idx(rng, B, T, k, lens, invisible=False)
     qf = (S.to_bf16_bits(qf).astype(np.uint32) << 16).view(np.float32)   # bf16 values
-    latf[0, idx[0, 0, 200], 512:] = 16.0 * qf[0, 0, 5, 512:]      # exact in bf16
+    latf[0, idx[0, 0, late], 512:] = 16.0 * qf[0, 0, 5, 512:]     # exact in bf16
     latf[1, idx[1, 0, 3], 512:] = 16.0 * qf[1, 0, 9, 512:]
     q = S.to_bf16_bits(qf)
     lat = S.to_bf16_bits(latf)
@@ -242,22 +250,23 @@ def test_sparse_mla_decode_logit_spread(dsa, orc):
     check_attention(_np_out(out), lse.cpu().numpy(), ro, rl, "bf16")
 
 
-def test_sparse_mla_decode_fp8_logit_spread(dsa, orc):
+@pytest.mark.parametrize("B,k,late", SPREAD_SHAPES, ids=[f"B{b}" for b, _, _ in SPREAD_SHAPES])
+def test_sparse_mla_decode_fp8_logit_spread(dsa, orc, B, k, late):
     """FP8 latent rows with logits far above the rest of a split: one selected row's bf16
     rope columns are 16x the query's rope part of one head, so its logit lies about 100
     log2 units above the others -- late in a split in row 0 (the split is recomputed from
     its true maximum, with FP8 gathers and block-scaled numerators), first in row 1."""
-    _say("[sparse_mla_decode fp8 latent] logit spread")
+    _say(f"[sparse_mla_decode fp8 latent] logit spread, B={B} k={k}")
     rng = np.random.default_rng(12)
-    B, T, H, Lmax, k = 2, 1, 128, 3000, 2048
-    lens = np.array([3000, 3000], np.int32)
+    T, H, Lmax = 1, 128, 3000
+    lens = np.full(B, 3000, np.int32)
     qf = rng.standard_normal((B, T, H, 576), dtype=np.float32)
     qf = (S.to_bf16_bits(qf).astype(np.uint32) << 16).view(np.float32)   # bf16 values
     x = rng.standard_normal((B, Lmax, 576), dtype=np.float32)
     f = np.exp2(rng.uniform(-5, 0, size=(B, Lmax, 4))).astype(np.float32)
     x[..., :512] *= np.repeat(f, 128, axis=-1)
     idx = _random_idx(rng, B, T, k, lens, invisible=False)
-    x[0, idx[0, 0, 200], 512:] = 16.0 * qf[0, 0, 5, 512:]      # exact in bf16
+    x[0, idx[0, 0, late], 512:] = 16.0 * qf[0, 0, 5, 512:]     # exact in bf16
     x[1, idx[1, 0, 3], 512:] = 16.0 * qf[1, 0, 9, 512:]
     q = S.to_bf16_bits(qf)
     lat = S.pack_latent_fp8(x)
