@@ -41,8 +41,9 @@
 // issues them while the other role's matrix-core chain runs.  Four buffers: tile i+3 goes
 // into the buffer of tile i-1 while tiles i+1 and i+2 are in flight.  Step n_tiles forms
 // the last tile's numerators and runs its PV.  The queries reach the QK waves through LDS
-// (direct loads into buffers 2 and 3, read at step 0 before tiles 2 and 3 go out after
-// B(0)), so the compiler's own waits for register loads never drain the gathers.
+// (direct loads into buffers 2 and 3, read by each QK wave before A(0), so that the PV
+// waves' share of tiles 2 and 3 goes out in phase 1 of step 0), so the compiler's own
+// waits for register loads never drain the gathers.
 // Softmax without a running rescale: each head's numerators are exp2(logit - m_ref), where
 // m_ref is the largest logit of the split's first tile with a usable slot (posted by both
 // column-half waves in phase 2 of that tile's step, read in the next step), so that tile's
@@ -495,13 +496,14 @@ void mla_decode32_kernel(const uint16_t* __restrict__ q, const uint8_t* __restri
             for (int ti = 0; ti <= n_tiles; ++ti) {
                 if (ti == 0) wait_vmcnt<0>();                         // this wave's queries
                 else wait_tile_qk(ti, n_tiles);
-                lds_barrier();                                        // A(ti)
                 if (ti == 0 && !fixed) {
-                    // this wave's queries, landed by its own loads (no barrier needed)
+                    // this wave's queries, landed by its own loads (no barrier needed); read
+                    // before A(0), so that A(0) frees buffers 2 and 3 for tiles 2 and 3
                     const uint8_t* qs_lds = q_stage(wave) + 16 * lane;
 #pragma unroll
                     for (int ks = 0; ks < kKs; ++ks) qreg[ks] = *reinterpret_cast<const v8bf*>(qs_lds + ks * 1024);
                 }
+                lds_barrier();                                        // A(ti): LDS reads done first
                 if (!ref_known && ref_tile >= 0 && ti == ref_tile + 1) {
                     qs.m_ref = fmaxf(s_ref[hh][0][lane & 31], s_ref[hh][1][lane & 31]);
                     ref_known = true;
@@ -575,12 +577,12 @@ void mla_decode32_kernel(const uint16_t* __restrict__ q, const uint8_t* __restri
                 wait_tile_pv(ti, n_tiles);
                 lds_barrier();                                        // A(ti)
                 if (ti >= 1 && ti + 3 < n_tiles) gather_tile<0, kPvLoads>(lat_b, ti + 3, c, gl);
-                lds_barrier();                                        // B(ti)
                 if (ti == 0) {
-                    // buffers 2 and 3 held the queries until the QK waves' reads of step 0
+                    // buffers 2 and 3 held the queries until the QK waves' reads, done before A(0)
                     for (int tj = 2; tj <= 3; ++tj)
                         if (tj < n_tiles) gather_tile<0, kPvLoads>(lat_b, tj, c, gl);
                 }
+                lds_barrier();                                        // B(ti)
                 if (ti > 0) {
                     v8bf pop[2][2];                                   // P(ti - 1) operands [kk][hh]
 #pragma unroll
