@@ -416,6 +416,10 @@ FP8_LAYER_CASES = [
     ("decode_small", _small("decode_v32", name="ds8", B=3, Lmax=4100, seed=212)),
     ("ragged_small_t3", _small("decode_ragged", name="rs8", B=5, T=3, Lmax=6000,
                                lens="ragged:1024:6000", seed=215)),
+    # four causal query rows per sequence on the 32x32x16 FP8-row kernel (eight rows, 16
+    # splits), some rows with fewer visible positions than k
+    ("t4_rows", _small("decode_v32", name="tf8", B=2, T=4, Lmax=5000, lens="ragged:1000:5000",
+                       seed=218)),
 ]
 
 
@@ -472,6 +476,10 @@ COMPRESSED_CASES = [
     # more than 16384 visible entries: the two-stage top-k, two rows per sequence
     ("long_t2_m4", _small("decode_long", name="cp4", B=2, T=2, Lmax=20000,
                           lens="ragged:70000:80000", seed=504), 4),
+    # FP8 latent rows: the 32x32x16 FP8 kernel (first) and the 16x16x32 one (second)
+    ("prefill_t64_m4_fp8", _small("decode_v32", name="cp5", B=1, T=64, Lmax=64, k=8, seed=505), 4),
+    ("ragged_t3_m2_fp8", _small("decode_ragged", name="cp6", B=4, T=3, Lmax=3000,
+                                lens="ragged:1024:6000", seed=506), 2),
 ]
 
 
@@ -481,7 +489,7 @@ def test_layer_step_compressed_entries(dsa, orc, name, cfg, m):
     entry e iff e < (pos + 1) / m; rows with no entry get -1 slots, a zero output and
     lse = -inf."""
     _say(f"[layer_step compressed] {name} m={m}")
-    c = S.make_case(cfg, compress=m)
+    c = S.make_case(cfg, compress=m, latent_form="fp8" if name.endswith("_fp8") else "bf16")
     d = _dev(c)
     step = dsa.LayerStep(d["q_i"], d["q_scale"], d["w"], d["k_i"], d["k_scale"], d["lens"],
                          cfg.sm_scale_i, cfg.k, d["q"], cfg.sm_scale, latent=d["latent"],
