@@ -58,12 +58,6 @@ __device__ __forceinline__ int n_visible(int len, int T, int t, int Lmax, int m)
     return m == 1 ? min(len, Lmax) - T + t + 1 : min((len - T + t + 1) / m, Lmax);
 }
 
-// Order-preserving map of a float onto an unsigned key: larger float -> larger key.
-__device__ __forceinline__ uint32_t float_key(float f) {
-    uint32_t u = __float_as_uint(f);
-    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-}
-
 // 16x16x128 FP8 (OCP e4m3fn) matrix-core product, fp32 accumulate.
 // Lane l supplies row (l % 16) of A and column (l % 16) of B, 32 bytes each; the four
 // lane groups (l / 16) cover disjoint quarters of K.  Output lane l holds rows
@@ -132,10 +126,7 @@ __device__ __forceinline__ float sum_xor16(float v) {
 __device__ __forceinline__ float sum_xor32(float v) {
     uint32_t a, b; pair32(__float_as_uint(v), a, b); return __uint_as_float(a) + __uint_as_float(b);
 }
-// The value of lane l ^ 16 (l ^ 32); `lane` is this lane's index in the wave.
-__device__ __forceinline__ float from_xor16(float v, int lane) {
-    uint32_t a, b; pair16(__float_as_uint(v), a, b); return __uint_as_float((lane & 16) ? a : b);
-}
+// The value of lane l ^ 32; `lane` is this lane's index in the wave.
 __device__ __forceinline__ float from_xor32(float v, int lane) {
     uint32_t a, b; pair32(__float_as_uint(v), a, b); return __uint_as_float((lane & 32) ? a : b);
 }
