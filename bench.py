@@ -320,8 +320,8 @@ def measure(D, S, cfg, steps: int, warmup: int, sets: int, latent: str, graph: b
 
     # The GPU idles while the inputs are generated on the host, and its clocks take several
     # milliseconds of load to come back: the first windows after such a pause measured 5-15 %
-    # slower than the steady state.  So the steps run untimed for ramp_s seconds first (the
-    # driver-sized W warm-up steps alone are a fraction of a millisecond).
+    # slower than the steady state.  So the steps run untimed for ramp_s seconds first (a
+    # handful of warm-up steps alone lasts a fraction of a millisecond).
     t_ramp = time.perf_counter()
     n_ramp = 0
     while time.perf_counter() - t_ramp < ramp_s:
